@@ -1,0 +1,174 @@
+/*
+ * dspark.h - C ABI of the DSpark draft / verify / confidence hot path on gfx950.
+ *
+ * Pages cited (titles as published):
+ *   [P1] "大模型推理加速的系统级工程：DeepSeek V4-Pro DSpark 推测解码方案深度解析与开源工具链
+ *        DeepSpec" (Best Partners TV, 2026-06-30)
+ *   [P2] "DeepSeek 开源 DSpark，一个可将大语言模型推理速度提升高达 85% 的新框架" (VentureBeat,
+ *        Chinese translation)
+ *   [P3] "DSpark Speculative Decoding" (concept note)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory     Every array argument is DEVICE memory owned by the caller, row-major with the
+ *            last dimension contiguous. The library allocates nothing: scratch comes from
+ *            the caller's workspace `ws` of at least `dspark_*_workspace_bytes(...)` bytes
+ *            (any alignment the HIP allocator returns; 256-byte alignment is assumed).
+ * Streams    `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work and
+ *            return without synchronising. Calls on distinct workspaces may run concurrently;
+ *            the library keeps no mutable global state.
+ * Errors     Every call returns a status. Host-detected errors (bad sizes, NULL required
+ *            pointers, a workspace that is too small, caps exceeded) enqueue nothing and leave
+ *            all outputs untouched. DSPARK_ERR_HIP reports a failed kernel launch.
+ *            dspark_last_error() returns a per-thread text describing the last failure.
+ * Device     Faults in device-resident data cannot be reported synchronously; they produce
+ * data       sentinels instead: a token id outside [0, V) gives token -1 (and n = -1 in
+ *            verify), a logit row that is entirely -inf gives token -1, uniforms are clamped
+ *            into [0, 1 - 2^-24]. NaN logits are undefined behaviour.
+ * Dtypes     Logits, uniforms, confidences and speeds are fp32; tokens, lengths and offsets
+ *            are int32. Markov factors are fp32 (DSPARK_F32) or bf16 (DSPARK_BF16).
+ * Sampling   One host uniform per draw; the token is the inverse CDF in token-id order,
+ *            x = min { v : F(v) > u }.
+ * Caps       1 <= gamma <= 64; 1 <= r <= 1024; 1 <= V < 2^31 with B*gamma*V < 2^40;
+ *            scheduler R*gamma <= 16384 and R <= Bmax <= 2^20.
+ * Results    Deterministic: two calls on the same inputs give bit-identical outputs (no float
+ *            atomics; every reduction has a fixed order).
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DSPARK_OK = 0,
+    DSPARK_ERR_INVALID_ARG = 1,
+    DSPARK_ERR_WORKSPACE = 2,
+    DSPARK_ERR_UNSUPPORTED = 3,
+    DSPARK_ERR_HIP = 4
+};
+
+enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
+
+enum { DSPARK_SCHED_GLOBAL = 0, DSPARK_SCHED_EARLY_STOP = 1 };
+
+/* Static text of a status code. */
+const char* dspark_status_string(int status);
+
+/* Per-thread description of the last non-OK status returned on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int dspark_version(void);
+
+/*
+ * Markov-head sequential draft.
+ * [P3] "Semi-Autoregressive Generation": x_k ~ p_k(v) proportional to exp(U_k(v) + B_k(v))
+ * with the low-rank Markov bias B_k = W1[x_{k-1}] W2 (rank r); [P1] section
+ * "DSpark 架构设计：半自回归生成与马尔可夫修正": the head conditions only on the previous token
+ * and runs left to right. Position 1 conditions on the context token x0.
+ *
+ *   U       [B][gamma][V]  fp32 base logits from the parallel backbone (read only)
+ *   W1      [V][r]         Markov factor, dtype w_dtype (read only)
+ *   W2      [r][V]         Markov factor, dtype w_dtype (read only)
+ *   x0      [B]            int32 last committed token of each request
+ *   u       [B][gamma]     fp32 host uniforms, one per draw
+ *   x_out   [B][gamma]     int32 draft tokens (required)
+ *   q_out   [B][gamma]     fp32 p_k(x_k)                      (nullable)
+ *   lse_out [B][gamma]     fp32 logsumexp(U_k + B_k)          (nullable)
+ *   Ld_out  [B][gamma][V]  fp32 draft logits U_k + B_k        (nullable)
+ * Steps run in order on `stream` without host round trips; step k reads x_{k-1} from x_out.
+ */
+size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma);
+int dspark_markov_draft(int B, int V, int r, int gamma,
+                        const float* U, const void* W1, const void* W2, int w_dtype,
+                        const int32_t* x0, const float* u,
+                        int32_t* x_out, float* q_out, float* lse_out, float* Ld_out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Lossless rejection-sampling verification.
+ * [P1] section "大模型推理的显存瓶颈与推测解码的演进逻辑" and [P3] intro: keep the longest accepted
+ * prefix, resample at the first rejection, add a bonus token when all are kept. Rule (the
+ * speculative sampling papers [P2] points to in "为什么推测解码很重要"): x_k is kept when
+ * u_acc < p_t(x_k) / p_d(x_k) (tested as log u < log p_t(x) - log p_d(x); p_d(x) = 0 keeps iff
+ * p_t(x) > 0); at the first rejection z ~ max(0, p_t - p_d) normalised (p_t if that mass is
+ * zero); otherwise z ~ p_t at position len+1. [P1] section "极致的工程实现与内核优化": target
+ * rows are flattened without padding.
+ *
+ *   Ld      [B][gamma][V]  fp32 draft logits (row k = position k+1)
+ *   Lt      [rows][V]      fp32 flattened target logits: request b owns rows
+ *                          t_off[b] .. t_off[b] + len[b]; row t_off[b] + i is position i+1
+ *   t_off   [B+1]          int32 row offsets (nullable: b * (gamma + 1))
+ *   len     [B]            int32 verify lengths in [0, gamma] (nullable: gamma)
+ *   x       [B][gamma]     int32 draft tokens
+ *   ld_lse  [B][gamma]     fp32 logsumexp of the Ld rows, e.g. lse_out of the draft
+ *                          (nullable: computed here)
+ *   u_acc   [B][gamma]     fp32 acceptance uniforms
+ *   u_fin   [B]            fp32 uniform of the residual or bonus draw
+ *   n_acc_out [B]          int32 accepted count n_b (-1: a verified draft token was invalid)
+ *   y_out   [B][gamma+1]   int32 emitted tokens x_1..x_n, z, then -1
+ *   lse_d_out [B][gamma]   fp32 lse of the Ld rows            (nullable; NaN beyond len)
+ *   lse_t_out [B][gamma+1] fp32 lse of the target rows        (nullable; NaN beyond len+1)
+ * A len outside [0, gamma] or t_off rows outside Lt are device-data faults: the request is
+ * skipped with n = -1 and y all -1 (t_off must be non-decreasing; Lt must hold t_off[B] rows).
+ */
+size_t dspark_verify_workspace_bytes(int B, int V, int gamma);
+int dspark_verify(int B, int V, int gamma,
+                  const float* Ld, const float* Lt, const int32_t* t_off, const int32_t* len,
+                  const int32_t* x, const float* ld_lse, const float* u_acc, const float* u_fin,
+                  int32_t* n_acc_out, int32_t* y_out, float* lse_d_out, float* lse_t_out,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * TV soft labels c*_k = 1 - 1/2 ||p_d - p_t||_1 = sum_v min(p_d(v), p_t(v)).
+ * [P3] "Confidence-Scheduled Verification" (label of the confidence head); [P1] section
+ * "硬件感知与置信度自适应调度机制" (analytic acceptance rate from the total variation distance).
+ *
+ *   Ld, Lt, t_off, len   as in dspark_verify
+ *   lse_d   [B][gamma]   fp32 (nullable: computed)
+ *   lse_t   [B][gamma+1] fp32 (nullable: computed)
+ *   cstar_out [B][gamma] fp32 c* for k < len[b]; NaN for k >= len[b]
+ */
+size_t dspark_tv_labels_workspace_bytes(int B, int V, int gamma);
+int dspark_tv_labels(int B, int V, int gamma,
+                     const float* Ld, const float* Lt, const int32_t* t_off, const int32_t* len,
+                     const float* lse_d, const float* lse_t, float* cstar_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Hardware-aware prefix scheduler.
+ * [P1] section "硬件感知与置信度自适应调度机制" and [P3] "Confidence-Scheduled Verification":
+ * per-position temperature calibration c' = 1 / (1 + ((1-c)/c)^(1/T_k)); prefix survival
+ * a_{r,j} = prod_{i<=j} c'_{r,i}; all R*gamma candidates ranked by a descending (ties:
+ * position ascending, then request ascending); Theta(n) = (R + sum of the top-n a) *
+ * SPS(R + n) for n = 0 .. min(R*gamma, Bmax - R); GLOBAL takes the smallest argmax,
+ * EARLY_STOP the first n with Theta(n+1) <= Theta(n); len[r] counts request r's candidates
+ * among the top n (a prefix of its block).
+ *
+ *   conf    [R][gamma]  fp32 conditional confidences c in [0, 1]
+ *   temp    [gamma]     fp32 per-position temperatures > 0 (nullable: no scaling)
+ *   sps     [Bmax+1]    fp32 engine steps/s at B total verify tokens
+ *   mode    DSPARK_SCHED_GLOBAL or DSPARK_SCHED_EARLY_STOP
+ *   len_out   [R]       int32 verify lengths
+ *   t_off_out [R+1]     int32 exclusive scan of len + 1 (nullable)
+ *   K_out     [1]       int32 total verify tokens R + n* (nullable)
+ *   theta_out [1]       fp32 Theta(n*) (nullable)
+ *   a_out   [R][gamma]  fp32 prefix survival (nullable)
+ * Runs as one workgroup; the ranking key keeps 32 mantissa bits of each fp64 a.
+ */
+size_t dspark_schedule_workspace_bytes(int R, int gamma, int Bmax);
+int dspark_schedule(int R, int gamma, const float* conf, const float* temp,
+                    const float* sps, int Bmax, int mode,
+                    int32_t* len_out, int32_t* t_off_out, int32_t* K_out, float* theta_out,
+                    float* a_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,50 @@
+"""fp64 CPU oracle for the DSpark draft / verify / confidence path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or link this
+package; only the tests, the package smoke check and the benchmark's CPU-baseline leg
+use it. It shares no code with the HIP library: the two meet only in the seeded input
+generators of ``synth``.
+
+Everything is plain numpy in float64, request by request and row by row, with no
+blocking, fusion or reordering beyond the definitions it follows. bf16 inputs are
+decoded exactly (bits << 16) and fp32 inputs are widened exactly.
+
+Pages cited (titles as published):
+
+* [P1] "大模型推理加速的系统级工程：DeepSeek V4-Pro DSpark 推测解码方案深度解析与开源工具链
+  DeepSpec" (Best Partners TV, 2026-06-30).
+* [P2] "DeepSeek 开源 DSpark，一个可将大语言模型推理速度提升高达 85% 的新框架"
+  (VentureBeat article, Chinese translation).
+* [P3] "DSpark Speculative Decoding" (concept note).
+
+Functions and what pins them (all pins live in ``tests/test_oracle_*.py``):
+
+* ``markov_draft`` - [P3] "Semi-Autoregressive Generation" (p_k formula, Markov bias
+  B = W1[x_{k-1}] W2). Pinned by rational-weight distributions with integer CDFs, a
+  one-hot Markov bias with exact expected tokens, a permutation chain, a dominant logit,
+  logsumexp against scipy and a chi-squared test of the sampler.
+* ``verify`` - [P1] "大模型推理的显存瓶颈与推测解码的演进逻辑" (rejection sampling) and [P3]
+  intro (longest prefix + bonus). Pinned by p_d = p_t, zero target mass on a draft token,
+  len = 0, and chi-squared losslessness (single position and multi-round joint).
+* ``tv_labels`` - [P3] "Confidence-Scheduled Verification" (c* = 1 - 1/2 ||p_d - p_t||_1).
+  Pinned by exact rational arithmetic, the two-point closed form, identical and disjoint
+  rows, and the Monte-Carlo acceptance rate of ``verify``.
+* ``temperature_scale``, ``prefix_survival``, ``schedule``, ``brute_force_schedule`` -
+  [P1] "硬件感知与置信度自适应调度机制" and [P3] "Confidence-Scheduled Verification"
+  (a_{r,j} = prod c, Theta = tau * SPS(B)). Pinned by brute-force enumeration, the
+  constant-SPS and zero-SPS closed forms, early-stop = global for a smooth curve, a
+  step-shaped curve with known answers, and exact temperature values.
+"""
+from .numerics import decode_factor, clamp_uniform, softmax_row, inverse_cdf
+from .draft import markov_draft
+from .verify import verify, accept_test
+from .tv import tv_labels, tv_row_pair
+from .schedule import (temperature_scale, prefix_survival, schedule, brute_force_schedule,
+                       theta_curve, GLOBAL, EARLY_STOP)
+
+__all__ = [
+    "decode_factor", "clamp_uniform", "softmax_row", "inverse_cdf", "markov_draft",
+    "verify", "accept_test", "tv_labels", "tv_row_pair", "temperature_scale",
+    "prefix_survival", "schedule", "brute_force_schedule", "theta_curve", "GLOBAL",
+    "EARLY_STOP",
+]
