@@ -1,0 +1,221 @@
+"""Benchmark of the DSpark hot path on one MI355X.
+
+One step is one pass of the whole path over one batch: Markov-head draft (gamma sequential
+vocabulary sweeps) -> prefix-survival scheduler -> rejection-sampling verify of the scheduled
+prefixes -> TV labels. Inputs are seeded synthetic tensors resident in HBM before timing;
+the target logits stand in for the target model's forward and are generated ahead of time.
+
+Each step is captured once into a HIP graph and replayed. Before every replay a 512 MB
+buffer is overwritten so the 256 MB Infinity Cache no longer holds the Markov factors (the
+target forward that precedes drafting does the same in serving); the flush is outside the
+per-step events, which bracket exactly the replay on the replay stream.
+
+Prints one JSON line. value = (drafted + verified tokens per step) / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Markov-head draft tokens/s + verified tokens/s at V=151936; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    "single": 2,   # single-request draft, B=1, V=151936, r=256, gamma=7
+    "batched": 3,  # batched draft, B=64, V=151936, gamma=16
+    "round": 5,    # full round, B=512, V=129280, gamma=16
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="single")
+    ap.add_argument("--no-flush", action="store_true", help="keep the Infinity Cache warm")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="extra eager steps with no timing (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+def build_inputs(cfg: int):
+    import synth
+    c = synth.config(cfg)
+    base = [synth.base_rows(c, b) for b in range(c.B)]
+    U = np.stack([r[: c.gamma] for r in base])
+    Lt = np.stack([synth.target_rows(c, b, base[b]) for b in range(c.B)]).reshape(-1, c.V)
+    del base
+    w1, w2 = synth.factors(c)
+    u_acc, u_fin = synth.verify_uniforms(c)
+    return c, dict(U=U, W1=w1, W2=w2, x0=synth.x0(c), u=synth.draft_uniforms(c), Lt=Lt,
+                   conf=synth.confidences(c), temp=synth.temperatures(c.gamma),
+                   sps=synth.sps_table(4096), u_acc=u_acc, u_fin=u_fin)
+
+
+def to_dev(a, torch, device):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def draft_bytes_per_launch(c) -> float:
+    """Algorithmic HBM bytes of one draft step: W2 read, U_k read, W1 rows, L_d write, outputs."""
+    sw = 2 if c.w_dtype == "bf16" else 4
+    return c.r * c.V * sw + c.B * c.V * 4 + c.B * c.r * sw + c.B * c.V * 4 + c.B * 12
+
+
+def cpu_baseline(c, inp, seconds: float) -> dict:
+    """The fp64 oracle on the same step, single-threaded, repeated for about `seconds`."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    reqs = list(range(min(c.B, 2)))       # a bounded sample of requests
+    G, V = c.gamma, c.V
+    tokens = 0
+    t0 = time.perf_counter()
+    steps = 0
+    with threadpool_limits(limits=1):
+        while True:
+            d = oracle.markov_draft(inp["U"][reqs], inp["W1"], inp["W2"], inp["x0"][reqs],
+                                    inp["u"][reqs], c.w_dtype, want_logits=True)
+            s = oracle.schedule(inp["conf"][reqs], inp["temp"], inp["sps"], 4096)
+            Lt = inp["Lt"].reshape(c.B, G + 1, V)[reqs].reshape(-1, V)
+            oracle.verify(d["L"], Lt, d["x"], inp["u_acc"][reqs], inp["u_fin"][reqs],
+                          length=s["len"])
+            oracle.tv_labels(d["L"], Lt, length=s["len"])
+            tokens += len(reqs) * G + int(s["len"].sum())
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or el * (steps + 1) / steps > 30.0:
+                break
+    return dict(value=tokens / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{steps} oracle steps over requests {reqs} of the same workload "
+                       f"(draft + schedule + verify + TV, fp64, one thread), {el:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps(dict(error="this benchmark runs on exactly one GPU; "
+                                    "multi-GPU figures are not produced", n_gpus=args.gpus)))
+        sys.exit(2)
+    import torch
+    import draft_sampling_verification_head_amd as dspark
+
+    device = torch.device("cuda:0")
+    cfg = WORKLOADS[args.workload]
+    c, inp = build_inputs(cfg)
+    t = {k: to_dev(v, torch, device) for k, v in inp.items()}
+    B, G, V = c.B, c.gamma, c.V
+    Bmax = 4096
+
+    out_d = dict(x=torch.empty((B, G), dtype=torch.int32, device=device),
+                 q=torch.empty((B, G), dtype=torch.float32, device=device),
+                 lse=torch.empty((B, G), dtype=torch.float32, device=device),
+                 L=torch.empty((B, G, V), dtype=torch.float32, device=device))
+    out_s = dict(len=torch.empty(B, dtype=torch.int32, device=device),
+                 t_off=torch.empty(B + 1, dtype=torch.int32, device=device),
+                 K=torch.empty(1, dtype=torch.int32, device=device),
+                 theta=torch.empty(1, dtype=torch.float32, device=device))
+    out_v = dict(n=torch.empty(B, dtype=torch.int32, device=device),
+                 y=torch.empty((B, G + 1), dtype=torch.int32, device=device),
+                 lse_d=torch.empty((B, G), dtype=torch.float32, device=device),
+                 lse_t=torch.empty((B, G + 1), dtype=torch.float32, device=device))
+    cstar = torch.empty((B, G), dtype=torch.float32, device=device)
+
+    def draft():
+        dspark.markov_draft(t["U"], t["W1"], t["W2"], t["x0"], t["u"], out=out_d)
+
+    def rest():
+        dspark.schedule(t["conf"], t["sps"], Bmax, temp=t["temp"], out=out_s)
+        dspark.verify(out_d["L"], t["Lt"], out_d["x"], t["u_acc"], t["u_fin"],
+                      length=out_s["len"], ld_lse=out_d["lse"], out=out_v)
+        dspark.tv_labels(out_d["L"], t["Lt"], length=out_s["len"], lse_d=out_v["lse_d"],
+                         lse_t=out_v["lse_t"], out=cstar)
+
+    def step():
+        draft()
+        rest()
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+
+    # capture one step and the draft alone
+    g_step, g_draft = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g_step):
+        step()
+    with torch.cuda.graph(g_draft):
+        draft()
+    torch.cuda.synchronize()
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+    verified = int(out_s["len"].sum().item())
+    drafted = B * G
+
+    def timed(graph, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            if not args.no_flush:
+                flush.fill_(i & 0xFF)
+            ev[i][0].record()
+            graph.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    for _ in range(args.warmup):
+        g_step.replay()
+    ms = timed(g_step, args.steps)
+    ms_draft = timed(g_draft, args.steps)
+    torch.cuda.synchronize()
+
+    ms_step = float(np.mean(ms))
+    value = (drafted + verified) / (ms_step * 1e-3)
+    launch_us = float(np.mean(ms_draft)) * 1e3 / G          # one fused draft step per launch
+    bytes_launch = draft_bytes_per_launch(c)
+    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+    res = dict(
+        metric=METRIC, value=value, unit="tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload=f"{c.name}: draft + schedule + verify + TV labels per step",
+                    B=B, V=V, r=c.r, gamma=G, factors=c.w_dtype, sps="1/(0.02+1e-5 B)",
+                    Bmax=Bmax, mall_flush=not args.no_flush, graph_replay=True),
+        drafted_per_step=drafted, verified_per_step=verified,
+        draft_tok_s=drafted / (float(np.mean(ms_draft)) * 1e-3),
+        ms_per_step_p10_p90=[float(np.percentile(ms, 10)), float(np.percentile(ms, 90))],
+        roofline=dict(bound="hbm", kernel="draft_sweep_gemv (fused select)",
+                      achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=None,
+                      bytes_per_launch=bytes_launch, launch_us=launch_us),
+    )
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,7 @@
+"""DSpark draft / verify / confidence hot path for MI355X (gfx950).
+
+The compute lives in libdspark.so (hand-written HIP kernels behind the C ABI of
+include/dspark.h); this package only builds it and binds it for torch tensors.
+"""
+from .binding import (markov_draft, verify, tv_labels, schedule, load, DsparkError,  # noqa: F401
+                      F32, BF16, GLOBAL, EARLY_STOP)

@@ -1,0 +1,252 @@
+"""ctypes binding of libdspark.so (the C ABI in include/dspark.h).
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are checked, their
+device pointers and the current HIP stream are handed to the library, and outputs and
+workspaces are allocated with torch. Every step of the computation runs in the library's
+kernels; there is no fallback, and loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdspark.so")
+
+OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+GLOBAL, EARLY_STOP = 0, 1
+
+# every symbol include/dspark.h declares
+EXPORTS = (
+    "dspark_status_string", "dspark_last_error", "dspark_version",
+    "dspark_markov_draft_workspace_bytes", "dspark_markov_draft",
+    "dspark_verify_workspace_bytes", "dspark_verify",
+    "dspark_tv_labels_workspace_bytes", "dspark_tv_labels",
+    "dspark_schedule_workspace_bytes", "dspark_schedule",
+)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+
+_SIGS = {
+    "dspark_status_string": (ctypes.c_char_p, [_I]),
+    "dspark_last_error": (ctypes.c_char_p, []),
+    "dspark_version": (_I, []),
+    "dspark_markov_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_verify_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dspark_verify": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_tv_labels_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dspark_tv_labels": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_schedule_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dspark_schedule": (_I, [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+def load(path: str | None = None):
+    """Load libdspark.so once; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            p = path or LIB_PATH
+            if not os.path.exists(p):
+                raise RuntimeError(f"{p} is missing: build it with "
+                                   "`python -m draft_sampling_verification_head_amd.build`")
+            lib = ctypes.CDLL(p)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        lib = load()
+        raise DsparkError(status, where, lib.dspark_last_error().decode())
+
+
+# ----------------------------------------------------------------------------- torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device, tag: str = ""):
+    """A cached, zero-filled-once uint8 device buffer of at least nbytes (reused across calls;
+    the library returns it to a reusable state after every call)."""
+    torch = _torch()
+    key = (str(device), tag)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+# ----------------------------------------------------------------------------- entry points
+def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=False,
+                 out=None, stream=None):
+    """dspark_markov_draft. U [B][gamma][V] fp32, W1 [V][r], W2 [r][V] (fp32 or bf16),
+    x0 [B] int32, u [B][gamma] fp32. Returns dict x, q, lse, L (None when not asked)."""
+    torch = _torch()
+    lib = load()
+    B, G, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    wdt = {torch.float32: F32, torch.bfloat16: BF16}.get(W1.dtype)
+    if wdt is None:
+        raise TypeError("W1/W2 must be float32 or bfloat16")
+    _need(U, "U", torch.float32, (B, G, V), dev)
+    _need(W1, "W1", W1.dtype, (V, r), dev)
+    _need(W2, "W2", W1.dtype, (r, V), dev)
+    _need(x0, "x0", torch.int32, (B,), dev)
+    _need(u, "u", torch.float32, (B, G), dev)
+    o = out or {}
+    x = o.get("x") if o.get("x") is not None else torch.empty((B, G), dtype=torch.int32, device=dev)
+    q = o.get("q") if o.get("q") is not None else (torch.empty((B, G), dtype=torch.float32, device=dev) if want_q else None)
+    lse = o.get("lse") if o.get("lse") is not None else (torch.empty((B, G), dtype=torch.float32, device=dev) if want_lse else None)
+    L = o.get("L") if o.get("L") is not None else (torch.empty((B, G, V), dtype=torch.float32, device=dev) if want_logits else None)
+    nbytes = lib.dspark_markov_draft_workspace_bytes(B, V, r, G)
+    ws = workspace(nbytes, dev, "draft")
+    st = lib.dspark_markov_draft(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(x0), _ptr(u),
+                                 _ptr(x), _ptr(q), _ptr(lse), _ptr(L), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    _check(st, "dspark_markov_draft")
+    return dict(x=x, q=q, lse=lse, L=L)
+
+
+def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, want_lse=False,
+           out=None, stream=None):
+    """dspark_verify. Ld [B][gamma][V], Lt [rows][V] fp32; x, u_acc [B][gamma]; u_fin [B].
+    Returns dict n [B], y [B][gamma+1] (and lse_d, lse_t when want_lse)."""
+    torch = _torch()
+    lib = load()
+    B, G, V = Ld.shape
+    dev = Ld.device
+    _need(Ld, "Ld", torch.float32, (B, G, V), dev)
+    if Lt.dim() != 2 or Lt.shape[1] != V:
+        raise ValueError("Lt must be [rows][V]")
+    _need(Lt, "Lt", torch.float32, tuple(Lt.shape), dev)
+    _need(x, "x", torch.int32, (B, G), dev)
+    _need(u_acc, "u_acc", torch.float32, (B, G), dev)
+    _need(u_fin, "u_fin", torch.float32, (B,), dev)
+    if t_off is not None:
+        _need(t_off, "t_off", torch.int32, (B + 1,), dev)
+    if length is not None:
+        _need(length, "length", torch.int32, (B,), dev)
+    if ld_lse is not None:
+        _need(ld_lse, "ld_lse", torch.float32, (B, G), dev)
+    o = out or {}
+    n = o.get("n") if o.get("n") is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    y = o.get("y") if o.get("y") is not None else torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    lse_d, lse_t = o.get("lse_d"), o.get("lse_t")
+    if want_lse and lse_d is None:
+        lse_d = torch.empty((B, G), dtype=torch.float32, device=dev)
+    if want_lse and lse_t is None:
+        lse_t = torch.empty((B, G + 1), dtype=torch.float32, device=dev)
+    if lse_d is not None:
+        _need(lse_d, "lse_d", torch.float32, (B, G), dev)
+    if lse_t is not None:
+        _need(lse_t, "lse_t", torch.float32, (B, G + 1), dev)
+    nbytes = lib.dspark_verify_workspace_bytes(B, V, G)
+    ws = workspace(nbytes, dev, "verify")
+    st = lib.dspark_verify(B, V, G, _ptr(Ld), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
+                           _ptr(length), _ptr(x), _ptr(ld_lse), _ptr(u_acc), _ptr(u_fin),
+                           _ptr(n), _ptr(y), _ptr(lse_d), _ptr(lse_t), _ptr(ws), ws.numel(),
+                           _stream(stream))
+    _check(st, "dspark_verify")
+    return dict(n=n, y=y, lse_d=lse_d, lse_t=lse_t)
+
+
+def tv_labels(Ld, Lt, *, t_off=None, length=None, lse_d=None, lse_t=None, out=None, stream=None):
+    """dspark_tv_labels. Returns c* [B][gamma] (NaN beyond each request's length)."""
+    torch = _torch()
+    lib = load()
+    B, G, V = Ld.shape
+    dev = Ld.device
+    _need(Ld, "Ld", torch.float32, (B, G, V), dev)
+    if Lt.dim() != 2 or Lt.shape[1] != V:
+        raise ValueError("Lt must be [rows][V]")
+    _need(Lt, "Lt", torch.float32, tuple(Lt.shape), dev)
+    if t_off is not None:
+        _need(t_off, "t_off", torch.int32, (B + 1,), dev)
+    if length is not None:
+        _need(length, "length", torch.int32, (B,), dev)
+    if lse_d is not None:
+        _need(lse_d, "lse_d", torch.float32, (B, G), dev)
+    if lse_t is not None:
+        _need(lse_t, "lse_t", torch.float32, (B, G + 1), dev)
+    c = out if out is not None else torch.empty((B, G), dtype=torch.float32, device=dev)
+    nbytes = lib.dspark_tv_labels_workspace_bytes(B, V, G)
+    ws = workspace(nbytes, dev, "tv")
+    st = lib.dspark_tv_labels(B, V, G, _ptr(Ld), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
+                              _ptr(length), _ptr(lse_d), _ptr(lse_t), _ptr(c), _ptr(ws),
+                              ws.numel(), _stream(stream))
+    _check(st, "dspark_tv_labels")
+    return c
+
+
+def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None, stream=None):
+    """dspark_schedule. conf [R][gamma] fp32, sps [Bmax+1] fp32, temp [gamma] fp32 or None.
+    Returns dict len [R], t_off [R+1], K [1], theta [1] (and a [R][gamma] when want_a)."""
+    torch = _torch()
+    lib = load()
+    R, G = conf.shape
+    dev = conf.device
+    _need(conf, "conf", torch.float32, (R, G), dev)
+    _need(sps, "sps", torch.float32, (Bmax + 1,), dev)
+    if temp is not None:
+        _need(temp, "temp", torch.float32, (G,), dev)
+    o = out or {}
+    length = o.get("len") if o.get("len") is not None else torch.empty((R,), dtype=torch.int32, device=dev)
+    t_off = o.get("t_off") if o.get("t_off") is not None else torch.empty((R + 1,), dtype=torch.int32, device=dev)
+    K = o.get("K") if o.get("K") is not None else torch.empty((1,), dtype=torch.int32, device=dev)
+    theta = o.get("theta") if o.get("theta") is not None else torch.empty((1,), dtype=torch.float32, device=dev)
+    a = torch.empty((R, G), dtype=torch.float32, device=dev) if want_a else None
+    st = lib.dspark_schedule(R, G, _ptr(conf), _ptr(temp), _ptr(sps), int(Bmax), int(mode),
+                             _ptr(length), _ptr(t_off), _ptr(K), _ptr(theta), _ptr(a), None, 0,
+                             _stream(stream))
+    _check(st, "dspark_schedule")
+    return dict(len=length, t_off=t_off, K=K, theta=theta, a=a)

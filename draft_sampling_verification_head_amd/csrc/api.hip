@@ -1,0 +1,269 @@
+// C-ABI host layer of libdspark: argument validation, workspace carving, kernel launches.
+//
+// Every check here runs before any HIP call, so a rejected call enqueues nothing and leaves
+// the outputs untouched. Launch failures come back as DSPARK_ERR_HIP.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dspark.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return DSPARK_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(DSPARK_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Carves consecutive aligned regions out of the caller's workspace.
+struct Carver {
+    char* base;
+    size_t used = 0;
+    explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+    template <typename T>
+    T* take(size_t count) {
+        T* p = reinterpret_cast<T*>(base + used);
+        used += align_up(count * sizeof(T));
+        return p;
+    }
+};
+
+constexpr long long kMaxElems = 1LL << 40;
+
+constexpr int kMaxB = 1 << 24;         // keeps every 1-D grid below 2^31 workgroups
+
+bool common_sizes_ok(int B, int V, int gamma) {
+    return B >= 1 && B <= kMaxB && V >= 1 && gamma >= 1 && gamma <= 64 &&
+           static_cast<long long>(B) * gamma * V < kMaxElems;
+}
+
+int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
+
+// sizes of the draft workspace regions
+size_t draft_part_count(int B, int V) {
+    return static_cast<size_t>(B) * ceil_div(V, dspark::draft_tile_cols());
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_status_string(int status) {
+    switch (status) {
+        case DSPARK_OK: return "ok";
+        case DSPARK_ERR_INVALID_ARG: return "invalid argument";
+        case DSPARK_ERR_WORKSPACE: return "workspace too small";
+        case DSPARK_ERR_UNSUPPORTED: return "size outside the supported caps";
+        case DSPARK_ERR_HIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+const char* dspark_last_error(void) { return g_last_error; }
+
+int dspark_version(void) { return 10000; }
+
+// ----------------------------------------------------------------------------- draft
+size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma) {
+    (void)r;
+    (void)gamma;
+    if (B < 1 || V < 1) return 0;
+    return align_up(dspark::draft_counter_count(B) * sizeof(unsigned int)) +
+           align_up(draft_part_count(B, V) * sizeof(float2)) +
+           align_up(static_cast<size_t>(B) * V * sizeof(float));
+}
+
+int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const void* W1,
+                        const void* W2, int w_dtype, const int32_t* x0, const float* u,
+                        int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, void* ws,
+                        size_t ws_bytes, void* stream) {
+    if (B < 1 || V < 1 || gamma < 1 || r < 1)
+        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: B=%d V=%d r=%d gamma=%d must be >= 1",
+                    B, V, r, gamma);
+    if (gamma > 64 || r > 1024 || !common_sizes_ok(B, V, gamma))
+        return fail(DSPARK_ERR_UNSUPPORTED, "markov_draft: gamma=%d r=%d B*gamma*V outside caps",
+                    gamma, r);
+    if (w_dtype != DSPARK_F32 && w_dtype != DSPARK_BF16)
+        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: unknown w_dtype %d", w_dtype);
+    if (!U || !W1 || !W2 || !x0 || !u || !x_out)
+        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: a required pointer is NULL");
+    const size_t need = dspark_markov_draft_workspace_bytes(B, V, r, gamma);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "markov_draft: workspace %zu bytes, need %zu", ws_bytes,
+                    need);
+    Carver c(ws);
+    const int nblk = ceil_div(V, dspark::draft_tile_cols());
+    unsigned int* counters = c.take<unsigned int>(dspark::draft_counter_count(B));
+    float2* part = c.take<float2>(draft_part_count(B, V));
+    float* lbuf = c.take<float>(static_cast<size_t>(B) * V);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int k = 0; k < gamma; ++k) {
+        dspark::DraftStep s;
+        s.B = B; s.V = V; s.r = r; s.gamma = gamma; s.k = k; s.w_dtype = w_dtype;
+        s.U = U; s.W1 = W1; s.W2 = W2;
+        s.prev = (k == 0) ? x0 : x_out + (k - 1);
+        s.prev_stride = (k == 0) ? 1 : gamma;
+        if (Ld_out) {
+            s.L = Ld_out + static_cast<long long>(k) * V;
+            s.L_bstride = static_cast<long long>(gamma) * V;
+        } else {
+            s.L = lbuf;
+            s.L_bstride = V;
+        }
+        s.part = part; s.nblk = nblk; s.counters = counters;
+        s.u = u; s.x_out = x_out; s.q_out = q_out; s.lse_out = lse_out;
+        const hipError_t e = dspark::launch_draft_step(s, st);
+        if (e != hipSuccess) return hip_fail(e, "markov_draft");
+    }
+    return ok();
+}
+
+// ----------------------------------------------------------------------------- verify / TV
+namespace {
+
+int check_rows(const char* who, int B, int V, int gamma, const float* Ld, const float* Lt,
+               int Lt_rows, const int32_t* t_off) {
+    if (B < 1 || V < 1 || gamma < 1)
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: B=%d V=%d gamma=%d must be >= 1", who, B, V, gamma);
+    if (!common_sizes_ok(B, V, gamma))
+        return fail(DSPARK_ERR_UNSUPPORTED, "%s: gamma=%d or B*gamma*V outside caps", who, gamma);
+    if (!Ld || !Lt) return fail(DSPARK_ERR_INVALID_ARG, "%s: Ld / Lt is NULL", who);
+    if (Lt_rows < 1) return fail(DSPARK_ERR_INVALID_ARG, "%s: Lt_rows=%d", who, Lt_rows);
+    if (!t_off && static_cast<long long>(Lt_rows) < static_cast<long long>(B) * (gamma + 1))
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: padded layout needs %lld target rows, got %d",
+                    who, static_cast<long long>(B) * (gamma + 1), Lt_rows);
+    return DSPARK_OK;
+}
+
+size_t lse_bytes(int B, int gamma) {
+    return align_up(static_cast<size_t>(B) * (gamma + 1) * sizeof(float)) +
+           align_up(static_cast<size_t>(B) * gamma * sizeof(float));
+}
+
+}  // namespace
+
+size_t dspark_verify_workspace_bytes(int B, int V, int gamma) {
+    if (B < 1 || V < 1 || gamma < 1) return 0;
+    const size_t nchunk = ceil_div(V, dspark::verify_chunk_elems());
+    return lse_bytes(B, gamma) + align_up(static_cast<size_t>(B) * nchunk * sizeof(float));
+}
+
+int dspark_verify(int B, int V, int gamma, const float* Ld, const float* Lt, int Lt_rows,
+                  const int32_t* t_off, const int32_t* len, const int32_t* x, const float* ld_lse,
+                  const float* u_acc, const float* u_fin, int32_t* n_acc_out, int32_t* y_out,
+                  float* lse_d_out, float* lse_t_out, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_rows("verify", B, V, gamma, Ld, Lt, Lt_rows, t_off);
+    if (rc != DSPARK_OK) return rc;
+    if (!x || !u_acc || !u_fin || !n_acc_out || !y_out)
+        return fail(DSPARK_ERR_INVALID_ARG, "verify: a required pointer is NULL");
+    const size_t need = dspark_verify_workspace_bytes(B, V, gamma);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "verify: workspace %zu bytes, need %zu", ws_bytes, need);
+    Carver c(ws);
+    float* lt_ws = c.take<float>(static_cast<size_t>(B) * (gamma + 1));
+    float* ld_ws = c.take<float>(static_cast<size_t>(B) * gamma);
+    const int nchunk = ceil_div(V, dspark::verify_chunk_elems());
+    float* chunk = c.take<float>(static_cast<size_t>(B) * nchunk);
+    float* lse_t = lse_t_out ? lse_t_out : lt_ws;
+    float* lse_d = lse_d_out ? lse_d_out : ld_ws;
+    dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = dspark::launch_row_lse(rs, ld_lse, lse_d, lse_t, st);
+    if (e != hipSuccess) return hip_fail(e, "verify/row_lse");
+    e = dspark::launch_verify_finish(rs, x, lse_d, lse_t, u_acc, u_fin, chunk, nchunk, n_acc_out,
+                                     y_out, st);
+    if (e != hipSuccess) return hip_fail(e, "verify/finish");
+    return ok();
+}
+
+size_t dspark_tv_labels_workspace_bytes(int B, int V, int gamma) {
+    if (B < 1 || V < 1 || gamma < 1) return 0;
+    return lse_bytes(B, gamma);
+}
+
+int dspark_tv_labels(int B, int V, int gamma, const float* Ld, const float* Lt, int Lt_rows,
+                     const int32_t* t_off, const int32_t* len, const float* lse_d,
+                     const float* lse_t, float* cstar_out, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int rc = check_rows("tv_labels", B, V, gamma, Ld, Lt, Lt_rows, t_off);
+    if (rc != DSPARK_OK) return rc;
+    if (!cstar_out) return fail(DSPARK_ERR_INVALID_ARG, "tv_labels: cstar_out is NULL");
+    const bool need_lse = !lse_d || !lse_t;
+    if (need_lse) {
+        const size_t need = dspark_tv_labels_workspace_bytes(B, V, gamma);
+        if (!ws || ws_bytes < need)
+            return fail(DSPARK_ERR_WORKSPACE, "tv_labels: workspace %zu bytes, need %zu",
+                        ws_bytes, need);
+    }
+    dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const float* ld = lse_d;
+    const float* lt = lse_t;
+    if (need_lse) {
+        Carver c(ws);
+        float* lt_ws = c.take<float>(static_cast<size_t>(B) * (gamma + 1));
+        float* ld_ws = c.take<float>(static_cast<size_t>(B) * gamma);
+        // computes every row whose lse is missing; a given lse_d is copied through
+        const hipError_t e = dspark::launch_row_lse(rs, lse_d, ld_ws, lt_ws, st);
+        if (e != hipSuccess) return hip_fail(e, "tv_labels/row_lse");
+        ld = ld_ws;
+        if (!lse_t) lt = lt_ws;
+    }
+    const hipError_t e = dspark::launch_tv(rs, ld, lt, cstar_out, st);
+    if (e != hipSuccess) return hip_fail(e, "tv_labels");
+    return ok();
+}
+
+// ----------------------------------------------------------------------------- schedule
+size_t dspark_schedule_workspace_bytes(int R, int gamma, int Bmax) {
+    (void)R;
+    (void)gamma;
+    (void)Bmax;
+    return 0;
+}
+
+int dspark_schedule(int R, int gamma, const float* conf, const float* temp, const float* sps,
+                    int Bmax, int mode, int32_t* len_out, int32_t* t_off_out, int32_t* K_out,
+                    float* theta_out, float* a_out, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (R < 1 || gamma < 1)
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: R=%d gamma=%d must be >= 1", R, gamma);
+    if (gamma > 64 || static_cast<long long>(R) * gamma > dspark::schedule_max_candidates())
+        return fail(DSPARK_ERR_UNSUPPORTED, "schedule: R*gamma=%lld exceeds %d (or gamma > 64)",
+                    static_cast<long long>(R) * gamma, dspark::schedule_max_candidates());
+    if (Bmax < R || Bmax > (1 << 20))
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: need R <= Bmax <= 2^20 (R=%d Bmax=%d)", R,
+                    Bmax);
+    if (mode != DSPARK_SCHED_GLOBAL && mode != DSPARK_SCHED_EARLY_STOP)
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: unknown mode %d", mode);
+    if (!conf || !sps || !len_out)
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: conf / sps / len_out is NULL");
+    const hipError_t e = dspark::launch_schedule(R, gamma, conf, temp, sps, Bmax, mode, len_out,
+                                                 t_off_out, K_out, theta_out, a_out,
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "schedule");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+// Hardware-aware prefix scheduler kernel (gfx950), one workgroup.
+//
+// [P1] "大模型推理加速的系统级工程：DeepSeek V4-Pro DSpark 推测解码方案深度解析与开源工具链
+// DeepSpec" (Best Partners TV), section "硬件感知与置信度自适应调度机制", and [P3] "DSpark
+// Speculative Decoding", section "Confidence-Scheduled Verification":
+//   c'_{r,j} = 1 / (1 + ((1 - c)/c)^(1/T_j))      per-position temperature (order preserving)
+//   a_{r,j}  = prod_{i<=j} c'_{r,i}                 prefix survival
+//   rank all candidates by a (descending), add them one by one and keep the batch size n
+//   that maximises Theta(n) = (R + sum of the top-n a) * SPS(R + n) (global search), or stop
+//   at the first n where Theta stops rising (early stopping).
+//
+// Layout: one 64-bit key per candidate in LDS, key = (~a_bits[63:20]) << 20 | j << 14 | r,
+// so an ascending sort gives a descending, then position ascending, then request ascending.
+// The kept 44 bits of the fp64 a (sign, exponent, 32 mantissa bits) carry the sums.
+// Lengths come from one cut key: request r keeps its candidates whose key is below the key
+// at rank n*. Because a is non-increasing along a block and ties rank earlier positions
+// first, that set is a prefix of every block.
+#include "common.h"
+#include "kernels.h"
+
+namespace dspark {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kMaxCand = 16384;            // 128 KB of keys in LDS
+constexpr unsigned long long kMask44 = (1ull << 44) - 1ull;
+
+__device__ __forceinline__ double scaled_conf(float c, const float* temp, int j) {
+    const double cd = static_cast<double>(c);
+    if (!(cd > 0.0)) return 0.0;          // also NaN
+    if (cd >= 1.0) return 1.0;
+    if (!temp) return cd;
+    double T = static_cast<double>(temp[j]);
+    if (!(T > 0.0)) T = 1.0;
+    return 1.0 / (1.0 + pow((1.0 - cd) / cd, 1.0 / T));
+}
+
+__device__ __forceinline__ unsigned long long make_key(double a, int j, int r) {
+    const unsigned long long q = static_cast<unsigned long long>(__double_as_longlong(a)) >> 20;
+    return (((~q) & kMask44) << 20) | (static_cast<unsigned long long>(j) << 14) |
+           static_cast<unsigned long long>(r);
+}
+
+__device__ __forceinline__ double key_value(unsigned long long key) {
+    const unsigned long long q = (~(key >> 20)) & kMask44;
+    return __longlong_as_double(static_cast<long long>(q << 20));
+}
+
+struct Best {
+    double theta;
+    int n;
+};
+
+__device__ __forceinline__ Best better(Best a, Best b) {
+    // larger Theta wins; equal Theta -> smaller n. NaN Theta never wins.
+    if (b.theta > a.theta || (b.theta == a.theta && b.n < a.n) || (a.theta != a.theta)) return b;
+    return a;
+}
+
+__global__ __launch_bounds__(kThreads)
+void schedule_kernel(int R, int G, const float* __restrict__ conf, const float* __restrict__ temp,
+                     const float* __restrict__ sps, int Bmax, int mode, int npad,
+                     int32_t* __restrict__ len_out, int32_t* __restrict__ t_off_out,
+                     int32_t* __restrict__ K_out, float* __restrict__ theta_out,
+                     float* __restrict__ a_out) {
+    __shared__ unsigned long long keys[kMaxCand];
+    __shared__ double dscr[kThreads / kWave + 1];
+    __shared__ int iscr[kThreads / kWave + 1];
+    __shared__ double bth[kThreads / kWave];
+    __shared__ int bn[kThreads / kWave];
+    __shared__ int s_nstar;
+    __shared__ double s_theta;
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int N = R * G;
+
+    // 1. temperature, prefix products, keys
+    for (int r = tid; r < R; r += kThreads) {
+        double a = 1.0;
+        for (int j = 0; j < G; ++j) {
+            a *= scaled_conf(conf[static_cast<long long>(r) * G + j], temp, j);
+            keys[r * G + j] = make_key(a, j, r);
+            if (a_out) a_out[static_cast<long long>(r) * G + j] = static_cast<float>(a);
+        }
+    }
+    for (int i = N + tid; i < npad; i += kThreads) keys[i] = ~0ull;
+    __syncthreads();
+
+    // 2. bitonic sort, ascending
+    for (int kk = 2; kk <= npad; kk <<= 1) {
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            for (int i = tid; i < npad; i += kThreads) {
+                const int ixj = i ^ jj;
+                if (ixj > i) {
+                    const unsigned long long x = keys[i], y = keys[ixj];
+                    const bool up = (i & kk) == 0;
+                    if ((x > y) == up) {
+                        keys[i] = y;
+                        keys[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 3. prefix sums of the ranked a, Theta(n) for n = 0..nmax
+    const int nmax = min(N, Bmax - R);
+    const int E = (npad + kThreads - 1) / kThreads;     // ranks per thread
+    const int p0 = tid * E;
+    double local = 0.0;
+    for (int e = 0; e < E; ++e) {
+        const int p = p0 + e;
+        if (p < N) local += key_value(keys[p]);
+    }
+    double tot;
+    const double S0 = block_excl_scan<kThreads>(local, dscr, &tot);   // S(p0)
+
+    Best best{-INFINITY, INT32_MAX};
+    int first_drop = INT32_MAX;
+    {
+        double S = S0;
+        double th_prev = 0.0;
+        bool have_prev = false;
+        if (p0 <= nmax) {
+            th_prev = (static_cast<double>(R) + S) * static_cast<double>(sps[R + p0]);
+            have_prev = true;
+            best = better(best, Best{th_prev, p0});
+        }
+        for (int e = 0; e < E; ++e) {
+            const int n = p0 + e + 1;
+            if (n > nmax) break;
+            S += key_value(keys[n - 1]);
+            const double th = (static_cast<double>(R) + S) * static_cast<double>(sps[R + n]);
+            if (have_prev && th <= th_prev && first_drop == INT32_MAX) first_drop = n - 1;
+            best = better(best, Best{th, n});
+            th_prev = th;
+            have_prev = true;
+        }
+    }
+    // block reductions
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        Best other{__shfl_xor(best.theta, o, kWave), __shfl_xor(best.n, o, kWave)};
+        best = better(best, other);
+    }
+    if (lane == 0) {
+        bth[wave] = best.theta;
+        bn[wave] = best.n;
+    }
+    const int drop = block_min_int<kThreads>(first_drop, iscr);   // contains a barrier
+    if (tid == 0) {
+        Best bb{bth[0], bn[0]};
+        for (int w = 1; w < kThreads / kWave; ++w) bb = better(bb, Best{bth[w], bn[w]});
+        int nstar;
+        if (mode == 1)
+            nstar = (drop == INT32_MAX) ? nmax : drop;
+        else
+            nstar = (bb.n == INT32_MAX) ? 0 : bb.n;
+        s_nstar = nstar;
+    }
+    __syncthreads();
+    const int nstar = s_nstar;
+
+    // Theta(n*) from the thread whose range ends at n*
+    {
+        const bool mine = (nstar == 0) ? (tid == 0) : (nstar > p0 && nstar <= p0 + E);
+        if (mine) {
+            double S = S0;
+            for (int n = p0 + 1; n <= nstar; ++n) S += key_value(keys[n - 1]);
+            if (nstar == 0) S = 0.0;
+            s_theta = (static_cast<double>(R) + S) * static_cast<double>(sps[R + nstar]);
+        }
+    }
+    const unsigned long long cut = (nstar < npad) ? keys[nstar] : ~0ull;
+    __syncthreads();
+
+    // 4. lengths: candidates ranked above the cut (recomputed keys are bit-identical)
+    for (int r = tid; r < R; r += kThreads) {
+        double a = 1.0;
+        int cnt = 0;
+        for (int j = 0; j < G; ++j) {
+            a *= scaled_conf(conf[static_cast<long long>(r) * G + j], temp, j);
+            cnt += make_key(a, j, r) < cut;
+        }
+        len_out[r] = cnt;
+    }
+
+    // 5. offsets: exclusive scan of len + 1
+    if (t_off_out) {
+        int run = 0;
+        for (int base = 0; base < R; base += kThreads) {
+            const int r = base + tid;
+            const int v = (r < R) ? len_out[r] + 1 : 0;   // written by this same thread above
+            int total;
+            const int ex = block_excl_scan<kThreads>(v, iscr, &total);
+            if (r < R) t_off_out[r] = run + ex;
+            run += total;
+        }
+        if (tid == 0) t_off_out[R] = run;
+    }
+    if (tid == 0) {
+        if (K_out) *K_out = R + nstar;
+        if (theta_out) *theta_out = static_cast<float>(s_theta);
+    }
+}
+
+}  // namespace
+
+int schedule_max_candidates() { return kMaxCand; }
+
+hipError_t launch_schedule(int R, int gamma, const float* conf, const float* temp,
+                           const float* sps, int Bmax, int mode, int32_t* len_out,
+                           int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out,
+                           hipStream_t st) {
+    int npad = 1;
+    while (npad < R * gamma) npad <<= 1;
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, st, R, gamma, conf, temp, sps,
+                       Bmax, mode, npad, len_out, t_off_out, K_out, theta_out, a_out);
+    return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -13,7 +13,9 @@
  * Memory     Every array argument is DEVICE memory owned by the caller, row-major with the
  *            last dimension contiguous. The library allocates nothing: scratch comes from
  *            the caller's workspace `ws` of at least `dspark_*_workspace_bytes(...)` bytes
- *            (any alignment the HIP allocator returns; 256-byte alignment is assumed).
+ *            (256-byte aligned, as the HIP allocator returns). A workspace must be
+ *            zero-filled once before its first use; every call leaves it reusable, so one
+ *            workspace serves any later call whose size it covers (not concurrent ones).
  * Streams    `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work and
  *            return without synchronising. Calls on distinct workspaces may run concurrently;
  *            the library keeps no mutable global state.
@@ -29,7 +31,8 @@
  *            are int32. Markov factors are fp32 (DSPARK_F32) or bf16 (DSPARK_BF16).
  * Sampling   One host uniform per draw; the token is the inverse CDF in token-id order,
  *            x = min { v : F(v) > u }.
- * Caps       1 <= gamma <= 64; 1 <= r <= 1024; 1 <= V < 2^31 with B*gamma*V < 2^40;
+ * Caps       1 <= B <= 2^24; 1 <= gamma <= 64; 1 <= r <= 1024; 1 <= V < 2^31 with
+ *            B*gamma*V < 2^40;
  *            scheduler R*gamma <= 16384 and R <= Bmax <= 2^20.
  * Results    Deterministic: two calls on the same inputs give bit-identical outputs (no float
  *            atomics; every reduction has a fixed order).
@@ -101,8 +104,9 @@ int dspark_markov_draft(int B, int V, int r, int gamma,
  * rows are flattened without padding.
  *
  *   Ld      [B][gamma][V]  fp32 draft logits (row k = position k+1)
- *   Lt      [rows][V]      fp32 flattened target logits: request b owns rows
+ *   Lt      [Lt_rows][V]   fp32 flattened target logits: request b owns rows
  *                          t_off[b] .. t_off[b] + len[b]; row t_off[b] + i is position i+1
+ *   Lt_rows                number of rows Lt holds (>= B*(gamma+1) when t_off is NULL)
  *   t_off   [B+1]          int32 row offsets (nullable: b * (gamma + 1))
  *   len     [B]            int32 verify lengths in [0, gamma] (nullable: gamma)
  *   x       [B][gamma]     int32 draft tokens
@@ -114,12 +118,13 @@ int dspark_markov_draft(int B, int V, int r, int gamma,
  *   y_out   [B][gamma+1]   int32 emitted tokens x_1..x_n, z, then -1
  *   lse_d_out [B][gamma]   fp32 lse of the Ld rows            (nullable; NaN beyond len)
  *   lse_t_out [B][gamma+1] fp32 lse of the target rows        (nullable; NaN beyond len+1)
- * A len outside [0, gamma] or t_off rows outside Lt are device-data faults: the request is
- * skipped with n = -1 and y all -1 (t_off must be non-decreasing; Lt must hold t_off[B] rows).
+ * A len outside [0, gamma], or rows t_off[b] .. t_off[b] + len[b] not inside [0, Lt_rows), is
+ * a device-data fault: that request gets n = -1 and y all -1 and is otherwise skipped.
  */
 size_t dspark_verify_workspace_bytes(int B, int V, int gamma);
 int dspark_verify(int B, int V, int gamma,
-                  const float* Ld, const float* Lt, const int32_t* t_off, const int32_t* len,
+                  const float* Ld, const float* Lt, int Lt_rows,
+                  const int32_t* t_off, const int32_t* len,
                   const int32_t* x, const float* ld_lse, const float* u_acc, const float* u_fin,
                   int32_t* n_acc_out, int32_t* y_out, float* lse_d_out, float* lse_t_out,
                   void* ws, size_t ws_bytes, void* stream);
@@ -129,14 +134,15 @@ int dspark_verify(int B, int V, int gamma,
  * [P3] "Confidence-Scheduled Verification" (label of the confidence head); [P1] section
  * "硬件感知与置信度自适应调度机制" (analytic acceptance rate from the total variation distance).
  *
- *   Ld, Lt, t_off, len   as in dspark_verify
+ *   Ld, Lt, Lt_rows, t_off, len   as in dspark_verify (a faulty request gets NaN labels)
  *   lse_d   [B][gamma]   fp32 (nullable: computed)
  *   lse_t   [B][gamma+1] fp32 (nullable: computed)
  *   cstar_out [B][gamma] fp32 c* for k < len[b]; NaN for k >= len[b]
  */
 size_t dspark_tv_labels_workspace_bytes(int B, int V, int gamma);
 int dspark_tv_labels(int B, int V, int gamma,
-                     const float* Ld, const float* Lt, const int32_t* t_off, const int32_t* len,
+                     const float* Ld, const float* Lt, int Lt_rows,
+                     const int32_t* t_off, const int32_t* len,
                      const float* lse_d, const float* lse_t, float* cstar_out,
                      void* ws, size_t ws_bytes, void* stream);
 

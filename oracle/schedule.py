@@ -27,22 +27,27 @@ EARLY_STOP = 1
 
 
 def temperature_scale(c, T=None) -> np.ndarray:
-    """c' = 1 / (1 + ((1 - c)/c)^(1/T_k)) per position; c = 0 -> 0, c = 1 -> 1."""
+    """c' = 1 / (1 + ((1 - c)/c)^(1/T_k)) per position; c = 0 -> 0, c = 1 -> 1.
+
+    Inputs outside the confidence range are clamped into [0, 1] (NaN counts as 0) and a
+    temperature that is not positive counts as 1; T = None leaves c unscaled.
+    """
     c = np.asarray(c, dtype=np.float32).astype(np.float64)
-    if T is None:
-        return c.copy()
-    T = np.asarray(T, dtype=np.float32).astype(np.float64)
-    out = np.empty_like(c)
     R, G = c.shape
+    Tk = None if T is None else np.asarray(T, dtype=np.float32).astype(np.float64)
+    out = np.empty_like(c)
     for r in range(R):
         for k in range(G):
             ck = c[r, k]
-            if ck <= 0.0:
+            if not ck > 0.0:
                 out[r, k] = 0.0
             elif ck >= 1.0:
                 out[r, k] = 1.0
+            elif Tk is None:
+                out[r, k] = ck
             else:
-                out[r, k] = 1.0 / (1.0 + ((1.0 - ck) / ck) ** (1.0 / T[k]))
+                t = Tk[k] if Tk[k] > 0.0 else 1.0
+                out[r, k] = 1.0 / (1.0 + ((1.0 - ck) / ck) ** (1.0 / t))
     return out
 
 

@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports what include/dspark.h declares, and rejects bad calls
+on the host before any HIP call (these run without a GPU; no compute is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from draft_sampling_verification_head_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu(), reason="host error paths are exercised where no GPU exists")
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.dspark_version() == 10000
+    for s in range(5):
+        assert lib.dspark_status_string(s)
+    assert lib.dspark_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    B, V, r, G = 64, 151936, 256, 16
+    nblk = -(-V // 512)
+    need = lib.dspark_markov_draft_workspace_bytes(B, V, r, G)
+    assert need >= B * nblk * 8 + B * V * 4
+    assert lib.dspark_markov_draft_workspace_bytes(0, V, r, G) == 0
+    assert lib.dspark_verify_workspace_bytes(256, V, 16) >= 256 * 33 * 4
+    assert lib.dspark_tv_labels_workspace_bytes(256, V, 16) >= 256 * 33 * 4
+    assert lib.dspark_schedule_workspace_bytes(512, 16, 4096) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _draft(lib, B=2, V=64, r=4, G=3, wdt=0, ws=FAKE, wsb=1 << 30, U=FAKE, x_out=FAKE):
+    return lib.dspark_markov_draft(B, V, r, G, U, FAKE, FAKE, wdt, FAKE, FAKE, x_out, None,
+                                   None, None, ws, wsb, None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), binding.ERR_INVALID_ARG),
+    (dict(V=0), binding.ERR_INVALID_ARG),
+    (dict(r=0), binding.ERR_INVALID_ARG),
+    (dict(G=0), binding.ERR_INVALID_ARG),
+    (dict(G=65), binding.ERR_UNSUPPORTED),
+    (dict(r=1025), binding.ERR_UNSUPPORTED),
+    (dict(B=1 << 20, V=1 << 20, G=2), binding.ERR_UNSUPPORTED),
+    (dict(wdt=7), binding.ERR_INVALID_ARG),
+    (dict(U=None), binding.ERR_INVALID_ARG),
+    (dict(x_out=None), binding.ERR_INVALID_ARG),
+    (dict(ws=None), binding.ERR_WORKSPACE),
+    (dict(wsb=100), binding.ERR_WORKSPACE),
+])
+def test_draft_rejects(lib, kw, status):
+    assert _draft(lib, **kw) == status
+    assert lib.dspark_last_error()
+
+
+def _verify(lib, B=2, V=64, G=3, Ld=FAKE, Lt_rows=8, t_off=None, x=FAKE, y=FAKE, ws=FAKE,
+            wsb=1 << 30):
+    return lib.dspark_verify(B, V, G, Ld, FAKE, Lt_rows, t_off, None, x, None, FAKE, FAKE, FAKE,
+                             y, None, None, ws, wsb, None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), binding.ERR_INVALID_ARG),
+    (dict(G=65), binding.ERR_UNSUPPORTED),
+    (dict(Ld=None), binding.ERR_INVALID_ARG),
+    (dict(Lt_rows=0), binding.ERR_INVALID_ARG),
+    (dict(Lt_rows=7), binding.ERR_INVALID_ARG),       # padded layout needs B*(G+1) = 8 rows
+    (dict(x=None), binding.ERR_INVALID_ARG),
+    (dict(y=None), binding.ERR_INVALID_ARG),
+    (dict(ws=None), binding.ERR_WORKSPACE),
+    (dict(wsb=4), binding.ERR_WORKSPACE),
+])
+def test_verify_rejects(lib, kw, status):
+    assert _verify(lib, **kw) == status
+
+
+@cpu_only
+def test_tv_rejects(lib):
+    assert lib.dspark_tv_labels(2, 64, 3, FAKE, FAKE, 8, None, None, None, None, None, FAKE,
+                                1 << 20, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_tv_labels(2, 64, 3, FAKE, FAKE, 8, None, None, None, None, FAKE, None,
+                                0, None) == binding.ERR_WORKSPACE
+
+
+@cpu_only
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 10, 0), binding.ERR_INVALID_ARG),
+    ((4, 0, 10, 0), binding.ERR_INVALID_ARG),
+    ((4, 65, 1000, 0), binding.ERR_UNSUPPORTED),
+    ((2048, 16, 4096, 0), binding.ERR_UNSUPPORTED),   # 32768 candidates
+    ((8, 4, 7, 0), binding.ERR_INVALID_ARG),          # Bmax < R
+    ((8, 4, 40, 2), binding.ERR_INVALID_ARG),         # unknown mode
+])
+def test_schedule_rejects(lib, args, status):
+    R, G, Bmax, mode = args
+    assert lib.dspark_schedule(R, G, FAKE, None, FAKE, Bmax, mode, FAKE, None, None, None, None,
+                               None, 0, None) == status
+
+
+@cpu_only
+def test_schedule_null_required(lib):
+    assert lib.dspark_schedule(4, 4, None, None, FAKE, 40, 0, FAKE, None, None, None, None, None,
+                               0, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_schedule(4, 4, FAKE, None, FAKE, 40, 0, None, None, None, None, None, None,
+                               0, None) == binding.ERR_INVALID_ARG
+
+
+def test_binding_refuses_missing_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load(str(tmp_path / "nope.so"))

@@ -1,0 +1,152 @@
+"""GPU parity of dspark_markov_draft against the fp64 oracle (called through the C ABI)."""
+import numpy as np
+import pytest
+import scipy.stats
+import torch
+
+import oracle
+import synth
+import draft_sampling_verification_head_amd as dspark
+from parity import check_draft, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_draft(d, want_logits=True):
+    out = dspark.markov_draft(dev(d["U"]), dev(d["W1"]), dev(d["W2"]), dev(d["x0"]),
+                              dev(d["u"]), want_logits=want_logits)
+    torch.cuda.synchronize()
+    return {k: (host(v) if v is not None else None) for k, v in out.items()}
+
+
+def test_cfg1_tiny_fp32_exact(gpu):
+    c = synth.config(1)
+    d = synth.draft_inputs(c)
+    g = run_draft(d)
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], c.w_dtype, g["x"], g["q"],
+                      g["lse"], range(c.B), gL=g["L"])
+    assert rep.ties == 0 and rep.compared == c.B * c.gamma
+
+
+@pytest.mark.parametrize("B,V,r,G,wdt", [
+    (3, 1000, 17, 5, "f32"),      # V % 8 != 0: guarded loads, ragged last tile
+    (5, 4099, 64, 3, "bf16"),
+    (1, 513, 8, 9, "bf16"),       # one column into the second tile
+    (2, 2056, 256, 4, "bf16"),
+    (9, 3000, 32, 2, "f32"),      # two request groups, the second ragged
+    (4, 1, 3, 3, "f32"),          # a single-token vocabulary
+    (2, 4096, 1024, 2, "bf16"),   # rank at its cap
+    (1, 777, 5, 64, "f32"),       # gamma at its cap
+])
+def test_ragged_shapes(gpu, B, V, r, G, wdt):
+    c = synth.custom(920 + B + V % 97, B=B, V=V, r=r, gamma=G, w_dtype=wdt, w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    g = run_draft(d)
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], wdt, g["x"], g["q"], g["lse"],
+                      range(B), gL=g["L"])
+    assert rep.ties <= 1
+
+
+def test_w1_zero_is_independent_sampling(gpu):
+    c = synth.custom(930, B=6, V=3001, r=16, gamma=5, w_dtype="bf16")
+    d = synth.draft_inputs(c)
+    d["W1"] = np.zeros_like(d["W1"])
+    a = run_draft(d)
+    d2 = dict(d, x0=((d["x0"] + 11) % c.V).astype(np.int32))
+    b = run_draft(d2)
+    assert np.array_equal(a["x"], b["x"])
+    check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", a["x"], a["q"], a["lse"],
+                range(c.B))
+
+
+def test_permutation_chain_closed_form(gpu):
+    g = np.random.default_rng(7)
+    B, G, V, r = 8, 6, 5000, 16
+    perm = g.permutation(V)[:r]
+    W1 = np.zeros((V, r), np.float32)
+    W1[np.arange(V), np.arange(V) % r] = 50.0
+    W2 = np.zeros((r, V), np.float32)
+    W2[np.arange(r), perm] = 1.0
+    d = dict(U=(0.1 * g.standard_normal((B, G, V))).astype(np.float32), W1=W1, W2=W2,
+             x0=g.integers(0, V, size=B).astype(np.int32),
+             u=g.uniform(1e-3, 1 - 2 ** -24, size=(B, G)).astype(np.float32))
+    out = run_draft(d, want_logits=False)
+    for b in range(B):
+        prev = d["x0"][b]
+        for k in range(G):
+            prev = perm[prev % r]
+            assert out["x"][b, k] == prev
+
+
+def test_cfg2_single_request_full(gpu):
+    c = synth.config(2)
+    d = synth.draft_inputs(c)
+    g = run_draft(d)
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], c.w_dtype, g["x"], g["q"],
+                      g["lse"], range(c.B), gL=g["L"])
+    assert rep.compared + rep.ties + rep.skipped == c.gamma
+    assert rep.ties <= 1
+
+
+def test_cfg3_batched_sampled(gpu):
+    c = synth.config(3)
+    d = synth.draft_inputs(c)
+    g = run_draft(d)
+    reqs = [0, 1, 17, 31, 32, 50, 63]
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], c.w_dtype, g["x"], g["q"],
+                      g["lse"], reqs, gL=g["L"])
+    assert rep.ties <= 2
+    assert np.all((g["x"] >= 0) & (g["x"] < c.V))
+    assert np.all((g["q"] > 0) & (g["q"] <= 1))
+
+
+def test_determinism_bitwise(gpu):
+    c = synth.custom(931, B=16, V=20000, r=256, gamma=4)
+    d = synth.draft_inputs(c)
+    a = run_draft(d)
+    b = run_draft(d)
+    for k in ("x", "q", "lse", "L"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+
+
+def test_sentinels(gpu):
+    c = synth.custom(932, B=3, V=600, r=8, gamma=4, w_dtype="f32")
+    d = synth.draft_inputs(c)
+    d["x0"][0] = c.V + 5
+    d["x0"][1] = -3
+    d["U"][2, 2, :] = -np.inf
+    g = run_draft(d)
+    assert np.all(g["x"][0] == -1) and np.all(g["x"][1] == -1)
+    assert g["x"][2, 0] >= 0 and g["x"][2, 1] >= 0
+    assert np.all(g["x"][2, 2:] == -1)
+    assert g["lse"][2, 2] == -np.inf and g["q"][2, 2] == 0.0
+    ref = oracle.markov_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "f32")
+    assert np.array_equal(ref["x"], g["x"])
+
+
+def test_uniform_edges(gpu):
+    c = synth.custom(933, B=4, V=2500, r=8, gamma=3, w_dtype="f32")
+    d = synth.draft_inputs(c)
+    d["u"][0, :] = 0.0
+    d["u"][1, :] = 1.0            # clamped to 1 - 2^-24
+    d["u"][2, :] = np.nextafter(np.float32(1.0), np.float32(0.0))
+    g = run_draft(d)
+    check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "f32", g["x"], g["q"], g["lse"],
+                range(c.B))
+
+
+def test_sampler_chi_squared(gpu):
+    """2^18 requests drafting one token from the same context: the law of x_1 is
+    softmax(U_1 + W1[x0] W2), compared by a chi-squared test."""
+    N, V, r = 1 << 18, 12, 3
+    g = np.random.default_rng(44)
+    U1 = (0.7 * g.standard_normal(V)).astype(np.float32)
+    W1 = (0.5 * g.standard_normal((V, r))).astype(np.float32)
+    W2 = (0.5 * g.standard_normal((r, V))).astype(np.float32)
+    x0 = np.full(N, 5, np.int32)
+    U = torch.from_numpy(U1).cuda().expand(N, 1, V).contiguous()
+    u = torch.from_numpy(synth.uniforms(synth.rng(934, 0), (N, 1))).cuda()
+    out = dspark.markov_draft(U, dev(W1), dev(W2), dev(x0), u, want_q=False, want_lse=False)
+    counts = np.bincount(host(out["x"])[:, 0], minlength=V).astype(float)
+    p = oracle.softmax_row(U1.astype(np.float64) + W1[5].astype(np.float64) @ W2.astype(np.float64))[0]
+    assert scipy.stats.chisquare(counts, N * p).pvalue > 1e-3

@@ -108,3 +108,11 @@ def test_invariants_on_workload_shape():
             # selected set is the global top-n and is prefix-closed per request
             top = {(r, j) for _, j, r in res["ranked"][: res["n"]]}
             assert top == {(r, j) for r in range(96) for j in range(res["len"][r])}
+
+
+def test_out_of_range_confidences_are_clamped():
+    c = np.array([[1.5, -0.2, np.nan, 0.7]], np.float32)
+    out = oracle.temperature_scale(c, np.array([2.0, 2.0, 2.0, -1.0], np.float32))
+    assert list(out[0, :3]) == [1.0, 0.0, 0.0]
+    assert out[0, 3] == pytest.approx(float(np.float32(0.7)), rel=1e-15)   # T <= 0 counts as 1
+    np.testing.assert_array_equal(oracle.temperature_scale(c)[0, :3], [1.0, 0.0, 0.0])
