@@ -114,13 +114,13 @@ _ws_cache: dict = {}
 
 
 def workspace(nbytes: int, device, tag: str = ""):
-    """A cached, zero-filled-once uint8 device buffer of at least nbytes (reused across calls;
-    the library returns it to a reusable state after every call)."""
+    """A cached uint8 device buffer of at least nbytes, reused by later calls of the same kind
+    (calls are stream-ordered on one stream, so they never overlap)."""
     torch = _torch()
     key = (str(device), tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -245,8 +245,9 @@ def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None,
     K = o.get("K") if o.get("K") is not None else torch.empty((1,), dtype=torch.int32, device=dev)
     theta = o.get("theta") if o.get("theta") is not None else torch.empty((1,), dtype=torch.float32, device=dev)
     a = torch.empty((R, G), dtype=torch.float32, device=dev) if want_a else None
+    ws = workspace(lib.dspark_schedule_workspace_bytes(R, G, int(Bmax)), dev, "schedule")
     st = lib.dspark_schedule(R, G, _ptr(conf), _ptr(temp), _ptr(sps), int(Bmax), int(mode),
-                             _ptr(length), _ptr(t_off), _ptr(K), _ptr(theta), _ptr(a), None, 0,
-                             _stream(stream))
+                             _ptr(length), _ptr(t_off), _ptr(K), _ptr(theta), _ptr(a), _ptr(ws),
+                             ws.numel(), _stream(stream))
     _check(st, "dspark_schedule")
     return dict(len=length, t_off=t_off, K=K, theta=theta, a=a)

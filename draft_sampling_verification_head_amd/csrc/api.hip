@@ -88,9 +88,8 @@ size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma) {
     (void)r;
     (void)gamma;
     if (B < 1 || V < 1) return 0;
-    return align_up(dspark::draft_counter_count(B) * sizeof(unsigned int)) +
-           align_up(draft_part_count(B, V) * sizeof(float2)) +
-           align_up(static_cast<size_t>(B) * V * sizeof(float));
+    return 2 * align_up(draft_part_count(B, V) * sizeof(float2)) +
+           2 * align_up(static_cast<size_t>(B) * V * sizeof(float));
 }
 
 int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const void* W1,
@@ -112,41 +111,35 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
         return fail(DSPARK_ERR_WORKSPACE, "markov_draft: workspace %zu bytes, need %zu", ws_bytes,
                     need);
     Carver c(ws);
-    const int nblk = ceil_div(V, dspark::draft_tile_cols());
-    unsigned int* counters = c.take<unsigned int>(dspark::draft_counter_count(B));
-    float2* part = c.take<float2>(draft_part_count(B, V));
-    float* lbuf = c.take<float>(static_cast<size_t>(B) * V);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    for (int k = 0; k < gamma; ++k) {
-        dspark::DraftStep s;
-        s.B = B; s.V = V; s.r = r; s.gamma = gamma; s.k = k; s.w_dtype = w_dtype;
-        s.U = U; s.W1 = W1; s.W2 = W2;
-        s.prev = (k == 0) ? x0 : x_out + (k - 1);
-        s.prev_stride = (k == 0) ? 1 : gamma;
-        if (Ld_out) {
-            s.L = Ld_out + static_cast<long long>(k) * V;
-            s.L_bstride = static_cast<long long>(gamma) * V;
-        } else {
-            s.L = lbuf;
-            s.L_bstride = V;
-        }
-        s.part = part; s.nblk = nblk; s.counters = counters;
-        s.u = u; s.x_out = x_out; s.q_out = q_out; s.lse_out = lse_out;
-        const hipError_t e = dspark::launch_draft_step(s, st);
-        if (e != hipSuccess) return hip_fail(e, "markov_draft");
-    }
+    dspark::DraftCall dc;
+    dc.B = B; dc.V = V; dc.r = r; dc.gamma = gamma; dc.w_dtype = w_dtype;
+    dc.nblk = ceil_div(V, dspark::draft_tile_cols());
+    dc.U = U; dc.W1 = W1; dc.W2 = W2; dc.x0 = x0; dc.u = u;
+    dc.x_out = x_out; dc.q_out = q_out; dc.lse_out = lse_out;
+    dc.part[0] = c.take<float2>(draft_part_count(B, V));
+    dc.part[1] = c.take<float2>(draft_part_count(B, V));
+    float* lbuf[2] = {c.take<float>(static_cast<size_t>(B) * V),
+                      c.take<float>(static_cast<size_t>(B) * V)};
+    for (int k = 0; k < gamma; ++k)
+        dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
+    dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
+    const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "markov_draft");
     return ok();
 }
 
 // ----------------------------------------------------------------------------- verify / TV
 namespace {
 
+long long row_chunks(int V) { return ceil_div(V, dspark::verify_chunk_elems()); }
+
 int check_rows(const char* who, int B, int V, int gamma, const float* Ld, const float* Lt,
                int Lt_rows, const int32_t* t_off) {
     if (B < 1 || V < 1 || gamma < 1)
         return fail(DSPARK_ERR_INVALID_ARG, "%s: B=%d V=%d gamma=%d must be >= 1", who, B, V, gamma);
-    if (!common_sizes_ok(B, V, gamma))
-        return fail(DSPARK_ERR_UNSUPPORTED, "%s: gamma=%d or B*gamma*V outside caps", who, gamma);
+    if (!common_sizes_ok(B, V, gamma) ||
+        row_chunks(V) * (2 * gamma + 1) * static_cast<long long>(B) > INT32_MAX)
+        return fail(DSPARK_ERR_UNSUPPORTED, "%s: B=%d gamma=%d V=%d outside caps", who, B, gamma, V);
     if (!Ld || !Lt) return fail(DSPARK_ERR_INVALID_ARG, "%s: Ld / Lt is NULL", who);
     if (Lt_rows < 1) return fail(DSPARK_ERR_INVALID_ARG, "%s: Lt_rows=%d", who, Lt_rows);
     if (!t_off && static_cast<long long>(Lt_rows) < static_cast<long long>(B) * (gamma + 1))
@@ -155,17 +148,17 @@ int check_rows(const char* who, int B, int V, int gamma, const float* Ld, const 
     return DSPARK_OK;
 }
 
-size_t lse_bytes(int B, int gamma) {
-    return align_up(static_cast<size_t>(B) * (gamma + 1) * sizeof(float)) +
-           align_up(static_cast<size_t>(B) * gamma * sizeof(float));
+size_t part_bytes(int B, int V, int gamma) {
+    return align_up(static_cast<size_t>(B) * (2 * gamma + 1) * row_chunks(V) * sizeof(float2));
 }
 
 }  // namespace
 
 size_t dspark_verify_workspace_bytes(int B, int V, int gamma) {
     if (B < 1 || V < 1 || gamma < 1) return 0;
-    const size_t nchunk = ceil_div(V, dspark::verify_chunk_elems());
-    return lse_bytes(B, gamma) + align_up(static_cast<size_t>(B) * nchunk * sizeof(float));
+    return part_bytes(B, V, gamma) +
+           align_up(static_cast<size_t>(B) * row_chunks(V) * sizeof(float)) +
+           align_up(static_cast<size_t>(B) * dspark::verify_state_bytes());
 }
 
 int dspark_verify(int B, int V, int gamma, const float* Ld, const float* Lt, int Lt_rows,
@@ -180,25 +173,23 @@ int dspark_verify(int B, int V, int gamma, const float* Ld, const float* Lt, int
     if (!ws || ws_bytes < need)
         return fail(DSPARK_ERR_WORKSPACE, "verify: workspace %zu bytes, need %zu", ws_bytes, need);
     Carver c(ws);
-    float* lt_ws = c.take<float>(static_cast<size_t>(B) * (gamma + 1));
-    float* ld_ws = c.take<float>(static_cast<size_t>(B) * gamma);
-    const int nchunk = ceil_div(V, dspark::verify_chunk_elems());
-    float* chunk = c.take<float>(static_cast<size_t>(B) * nchunk);
-    float* lse_t = lse_t_out ? lse_t_out : lt_ws;
-    float* lse_d = lse_d_out ? lse_d_out : ld_ws;
+    float2* part = c.take<float2>(static_cast<size_t>(B) * (2 * gamma + 1) * row_chunks(V));
+    float* csum = c.take<float>(static_cast<size_t>(B) * row_chunks(V));
+    char* state = c.take<char>(static_cast<size_t>(B) * dspark::verify_state_bytes());
     dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = dspark::launch_row_lse(rs, ld_lse, lse_d, lse_t, st);
-    if (e != hipSuccess) return hip_fail(e, "verify/row_lse");
-    e = dspark::launch_verify_finish(rs, x, lse_d, lse_t, u_acc, u_fin, chunk, nchunk, n_acc_out,
-                                     y_out, st);
-    if (e != hipSuccess) return hip_fail(e, "verify/finish");
+    hipError_t e = dspark::launch_row_stats(rs, ld_lse, part, st);
+    if (e != hipSuccess) return hip_fail(e, "verify/row_stats");
+    e = dspark::launch_verify(rs, x, part, ld_lse, u_acc, u_fin, lse_d_out, lse_t_out, csum,
+                              state, n_acc_out, y_out, st);
+    if (e != hipSuccess) return hip_fail(e, "verify");
     return ok();
 }
 
 size_t dspark_tv_labels_workspace_bytes(int B, int V, int gamma) {
     if (B < 1 || V < 1 || gamma < 1) return 0;
-    return lse_bytes(B, gamma);
+    return part_bytes(B, V, gamma) +
+           align_up(static_cast<size_t>(B) * gamma * row_chunks(V) * sizeof(float));
 }
 
 int dspark_tv_labels(int B, int V, int gamma, const float* Ld, const float* Lt, int Lt_rows,
@@ -208,45 +199,35 @@ int dspark_tv_labels(int B, int V, int gamma, const float* Ld, const float* Lt, 
     int rc = check_rows("tv_labels", B, V, gamma, Ld, Lt, Lt_rows, t_off);
     if (rc != DSPARK_OK) return rc;
     if (!cstar_out) return fail(DSPARK_ERR_INVALID_ARG, "tv_labels: cstar_out is NULL");
-    const bool need_lse = !lse_d || !lse_t;
-    if (need_lse) {
-        const size_t need = dspark_tv_labels_workspace_bytes(B, V, gamma);
-        if (!ws || ws_bytes < need)
-            return fail(DSPARK_ERR_WORKSPACE, "tv_labels: workspace %zu bytes, need %zu",
-                        ws_bytes, need);
-    }
+    const size_t need = dspark_tv_labels_workspace_bytes(B, V, gamma);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "tv_labels: workspace %zu bytes, need %zu", ws_bytes,
+                    need);
+    Carver c(ws);
+    float2* part = c.take<float2>(static_cast<size_t>(B) * (2 * gamma + 1) * row_chunks(V));
+    float* psum = c.take<float>(static_cast<size_t>(B) * gamma * row_chunks(V));
     dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const float* ld = lse_d;
-    const float* lt = lse_t;
-    if (need_lse) {
-        Carver c(ws);
-        float* lt_ws = c.take<float>(static_cast<size_t>(B) * (gamma + 1));
-        float* ld_ws = c.take<float>(static_cast<size_t>(B) * gamma);
-        // computes every row whose lse is missing; a given lse_d is copied through
-        const hipError_t e = dspark::launch_row_lse(rs, lse_d, ld_ws, lt_ws, st);
-        if (e != hipSuccess) return hip_fail(e, "tv_labels/row_lse");
-        ld = ld_ws;
-        if (!lse_t) lt = lt_ws;
+    if (!lse_d || !lse_t) {
+        // partials of every row whose lse is missing (draft rows only when lse_d is missing)
+        const hipError_t e = dspark::launch_row_stats(rs, lse_d, part, st);
+        if (e != hipSuccess) return hip_fail(e, "tv_labels/row_stats");
     }
-    const hipError_t e = dspark::launch_tv(rs, ld, lt, cstar_out, st);
+    const hipError_t e = dspark::launch_tv(rs, lse_d, lse_t, part, psum, cstar_out, st);
     if (e != hipSuccess) return hip_fail(e, "tv_labels");
     return ok();
 }
 
 // ----------------------------------------------------------------------------- schedule
 size_t dspark_schedule_workspace_bytes(int R, int gamma, int Bmax) {
-    (void)R;
-    (void)gamma;
     (void)Bmax;
-    return 0;
+    if (R < 1 || gamma < 1) return 0;
+    return align_up(static_cast<size_t>(R) * gamma * sizeof(double));
 }
 
 int dspark_schedule(int R, int gamma, const float* conf, const float* temp, const float* sps,
                     int Bmax, int mode, int32_t* len_out, int32_t* t_off_out, int32_t* K_out,
                     float* theta_out, float* a_out, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (R < 1 || gamma < 1)
         return fail(DSPARK_ERR_INVALID_ARG, "schedule: R=%d gamma=%d must be >= 1", R, gamma);
     if (gamma > 64 || static_cast<long long>(R) * gamma > dspark::schedule_max_candidates())
@@ -259,8 +240,12 @@ int dspark_schedule(int R, int gamma, const float* conf, const float* temp, cons
         return fail(DSPARK_ERR_INVALID_ARG, "schedule: unknown mode %d", mode);
     if (!conf || !sps || !len_out)
         return fail(DSPARK_ERR_INVALID_ARG, "schedule: conf / sps / len_out is NULL");
+    const size_t need = dspark_schedule_workspace_bytes(R, gamma, Bmax);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "schedule: workspace %zu bytes, need %zu", ws_bytes, need);
     const hipError_t e = dspark::launch_schedule(R, gamma, conf, temp, sps, Bmax, mode, len_out,
                                                  t_off_out, K_out, theta_out, a_out,
+                                                 static_cast<double*>(ws),
                                                  static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "schedule");
     return ok();

@@ -7,17 +7,21 @@
 // 推测解码方案深度解析与开源工具链 DeepSpec"; [P3] = the concept note "DSpark Speculative
 // Decoding".)
 //
-// One draft step:
-//   sweep  - grid (vocabulary tiles of 512 columns, request groups of up to 8). Gathers
-//            W1[x_{k-1}] into LDS, streams the tile's W2 columns once for the whole group
-//            (each lane 8 consecutive columns, waves split the rank), adds U_k, writes the
-//            logits row segment and the tile's (max, sum exp(l - max)) partial.
-//   select - one wave per request. Merges the partials in tile order into (m, Z),
-//            lse = m + log Z, finds the tile holding the inverse-CDF point u * Z and rescans
-//            that tile's stored logits for x_k = min { v : F(v) > u }.
-// Up to 8 requests the select runs inside the sweep's last workgroup (one launch per step);
-// larger batches launch it separately. Step k+1 reads x_k from device memory, so the gamma
-// steps are enqueued back to back with no host round trip.
+// A draft of gamma positions is gamma + 1 launches, all on one stream:
+//   step k  - 1-D grid over (request group of up to 8, vocabulary tile of 512 columns), tile
+//             fastest. Each workgroup first draws x_{k-1} itself from step k-1's tile
+//             partials and stored logits (every workgroup of the step computes the same
+//             token; workgroup 0 also writes it out), gathers W1[x_{k-1}] into LDS, streams
+//             the tile's W2 columns once for the whole group, adds U_k and writes the logits
+//             row segment and the tile's (max, sum exp(l - max)) partial. Each lane owns 8
+//             consecutive columns (one 16-byte bf16 load per W2 row); the 16 waves split the
+//             rank with 8 rows of loads in flight each. Step 0 takes x_0 from the caller.
+//   select  - draws x_{gamma-1} from the last step's partials, one wave per request.
+// The draw: (m, Z) merged from the partials in tile order, lse = m + log Z, the first tile
+// whose running mass exceeds u * Z, then the first column of that tile whose running mass
+// exceeds the remainder: x = min { v : F(v) > u } (inverse CDF in token order). Rounding
+// that leaves the point past the end falls back to the last positive column. Results cross
+// workgroups only at kernel boundaries, so no workgroup needs a device-scope fence.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,163 +29,334 @@ namespace dspark {
 
 namespace {
 
-constexpr int kSweepThreads = 512;                 // 8 waves
+constexpr int kSweepThreads = 1024;                // 16 waves
 constexpr int kSweepWaves = kSweepThreads / kWave;
 constexpr int kColsPerLane = 8;
 constexpr int kTileCols = kWave * kColsPerLane;    // 512 vocabulary columns per tile
-static_assert(kTileCols == kSweepThreads, "one output column per thread in the epilogue");
+static_assert(kTileCols * 2 == kSweepThreads, "epilogue: one column per thread of the first half");
 
-constexpr int kSelThreads = 256;                 // 4 requests per workgroup, one per wave
+constexpr int kSelThreads = 256;                   // 4 requests per workgroup, one per wave
+constexpr int kSelRegTiles = 8;                    // tiles per lane kept in registers
 
-// Eight consecutive factor elements as fp32. VEC: the eight are in bounds and 16-byte
-// aligned (V % 8 == 0); otherwise each element is guarded by `avail` (elements left).
-template <bool VEC>
-__device__ __forceinline__ void load8(const float* p, long long avail, float (&o)[8]) {
-    if (VEC) {
-        float4 a = *reinterpret_cast<const float4*>(p);
-        float4 b = *reinterpret_cast<const float4*>(p + 4);
+// Eight consecutive factor elements of one W2 row.
+template <typename WT>
+struct Seg;
+
+template <>
+struct Seg<uint16_t> {
+    uint4 v;
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        v = *reinterpret_cast<const uint4*>(p);
+    }
+    __device__ __forceinline__ void load_guarded(const uint16_t* p, long long avail) {
+        uint32_t t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (e < avail) ? static_cast<uint32_t>(p[e]) : 0u;
+        v = make_uint4(t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16),
+                       t[6] | (t[7] << 16));
+    }
+    __device__ __forceinline__ void to_f32(float (&o)[8]) const {
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+        o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
+        o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
+    }
+};
+
+template <>
+struct Seg<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void load_guarded(const float* p, long long avail) {
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (e < avail) ? p[e] : 0.0f;
+        a = make_float4(t[0], t[1], t[2], t[3]);
+        b = make_float4(t[4], t[5], t[6], t[7]);
+    }
+    __device__ __forceinline__ void to_f32(float (&o)[8]) const {
         o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
         o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (e < avail) ? p[e] : 0.0f;
     }
-}
-
-template <bool VEC>
-__device__ __forceinline__ void load8(const uint16_t* p, long long avail, float (&o)[8]) {
-    if (VEC) {
-        uint4 a = *reinterpret_cast<const uint4*>(p);
-        o[0] = __uint_as_float(a.x << 16); o[1] = __uint_as_float(a.x & 0xffff0000u);
-        o[2] = __uint_as_float(a.y << 16); o[3] = __uint_as_float(a.y & 0xffff0000u);
-        o[4] = __uint_as_float(a.z << 16); o[5] = __uint_as_float(a.z & 0xffff0000u);
-        o[6] = __uint_as_float(a.w << 16); o[7] = __uint_as_float(a.w & 0xffff0000u);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (e < avail) ? to_f32(p[e]) : 0.0f;
-    }
-}
+};
 
 __device__ __forceinline__ float tile_mass(float2 p, float m) {
     return (p.x == -INFINITY) ? 0.0f : p.y * __expf(p.x - m);
 }
 
-// ----------------------------------------------------------------------------- select
-// One wave draws one request's token from its tile partials and stored logits row:
-// (m, Z) merged in tile order, lse = m + log Z, the first tile whose running mass exceeds
-// u * Z, then the first column of that tile whose running mass exceeds the remainder.
-// Rounding that leaves the point past the end falls back to the last positive column.
-__device__ void select_wave(int V, const float2* __restrict__ P, int nblk,
-                            const float* __restrict__ row, float u, int32_t* x_o, float* q_o,
-                            float* lse_o) {
+// Where a draw writes its results (nothing when `write` is false).
+struct DrawOut {
+    int32_t* x;
+    float* q;
+    float* lse;
+    bool write;
+};
+
+__device__ __forceinline__ void put(const DrawOut& o, int tok, float q, float lse) {
+    *o.x = tok;
+    if (o.q) *o.q = q;
+    if (o.lse) *o.lse = lse;
+}
+
+// ----------------------------------------------------------------------------- wave draw
+// In-tile rescan: lane owns 8 consecutive columns of `tile`.
+__device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__ row, int tile,
+                                                float m, float lse, float tprime,
+                                                const DrawOut& o) {
     const int lane = threadIdx.x & (kWave - 1);
-    float m = -INFINITY;
-    for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, P[i].x);
-    m = wave_max(m);
-    if (m == -INFINITY) {                 // invalid previous token or an all -inf row
-        if (lane == 0) {
-            *x_o = -1;
-            if (q_o) *q_o = 0.0f;
-            if (lse_o) *lse_o = -INFINITY;
-        }
-        return;
-    }
-    float z = 0.0f;
-    for (int i = lane; i < nblk; i += kWave) z += tile_mass(P[i], m);
-    const float Z = wave_sum(z);
-    const float lse = m + __logf(Z);
-    const float target = clamp_uniform(u) * Z;
-
-    int found = -1;
-    float tprime = INFINITY, run = 0.0f;
-    for (int base = 0; base < nblk; base += kWave) {
-        const int i = base + lane;
-        const float v = (i < nblk) ? tile_mass(P[i], m) : 0.0f;
-        const float incl = wave_incl_scan(v);
-        float excl = __shfl_up(incl, 1, kWave);
-        if (lane == 0) excl = 0.0f;
-        const unsigned long long hit = __ballot((i < nblk) && (v > 0.0f) && (run + incl > target));
-        if (hit) {
-            const int f = __ffsll(static_cast<long long>(hit)) - 1;
-            found = base + f;
-            tprime = target - (run + __shfl(excl, f, kWave));
-            break;
-        }
-        run += __shfl(incl, kWave - 1, kWave);
-    }
-    if (found < 0) {
-        int last = -1;
-        for (int i = lane; i < nblk; i += kWave)
-            if (tile_mass(P[i], m) > 0.0f) last = i;
-        found = wave_max_int(last);
-        tprime = INFINITY;
-    }
-
-    const long long c0 = static_cast<long long>(found) * kTileCols + lane * kColsPerLane;
-    float e[kColsPerLane];
+    const long long c0 = static_cast<long long>(tile) * kTileCols + lane * kColsPerLane;
+    float lv[kColsPerLane], e[kColsPerLane];
     float local = 0.0f;
 #pragma unroll
+    for (int j = 0; j < kColsPerLane; ++j) lv[j] = (c0 + j < V) ? row[c0 + j] : -INFINITY;
+#pragma unroll
     for (int j = 0; j < kColsPerLane; ++j) {
-        const long long c = c0 + j;
-        const float l = (c < V) ? row[c] : -INFINITY;
-        e[j] = (l == -INFINITY) ? 0.0f : __expf(l - m);
+        e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
         local += e[j];
     }
     const float incl = wave_incl_scan(local);
-    float run2 = __shfl_up(incl, 1, kWave);
-    if (lane == 0) run2 = 0.0f;
-    int hitc = INT32_MAX, lastpos = -1;
+    float run = __shfl_up(incl, 1, kWave);
+    if (lane == 0) run = 0.0f;
+    int hit = INT32_MAX, lastpos = -1;
 #pragma unroll
     for (int j = 0; j < kColsPerLane; ++j) {
-        run2 += e[j];
+        run += e[j];
         if (e[j] > 0.0f) {
             lastpos = static_cast<int>(c0 + j);
-            if (hitc == INT32_MAX && run2 > tprime) hitc = static_cast<int>(c0 + j);
+            if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(c0 + j);
         }
     }
-    int tok = wave_min_int(hitc);
+    int tok = wave_min_int(hit);
     if (tok == INT32_MAX) tok = wave_max_int(lastpos);
-    if (lane == 0) {
-        *x_o = tok;
-        if (q_o) *q_o = (tok >= 0) ? __expf(row[tok] - lse) : 0.0f;
-        if (lse_o) *lse_o = lse;
-    }
+    const int rel = tok - tile * kTileCols;
+    const int owner = rel / kColsPerLane, jj = rel - owner * kColsPerLane;
+    float mine = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kColsPerLane; ++j)
+        if (j == jj) mine = lv[j];
+    const float lx = __shfl(mine, owner, kWave);
+    if (o.write && lane == 0) put(o, tok, __expf(lx - lse), lse);
+    return tok;
 }
 
-// ----------------------------------------------------------------------------- sweep
-// FUSED: the last workgroup of a request group to finish (counted with a device-scope
-// atomic after a release fence) also runs the select, one wave per request, so a step is a
-// single launch. Its counter is reset before it returns, so counters stay zero between
-// launches.
-template <typename WT, int BT, bool VEC, bool FUSED>
-__global__ __launch_bounds__(kSweepThreads)
-void draft_sweep_gemv(int B, int V, int r, int gamma, int k,
-                      const float* __restrict__ U, const WT* __restrict__ W1,
-                      const WT* __restrict__ W2, const int32_t* __restrict__ prev,
-                      int prev_stride, float* __restrict__ L, long long L_bstride,
-                      float2* __restrict__ part, int nblk, unsigned int* __restrict__ counters,
-                      const float* __restrict__ u, int32_t* __restrict__ x_out,
-                      float* __restrict__ q_out, float* __restrict__ lse_out) {
+// One wave draws one request's token; returns it (-1 for a dead request) in every lane.
+__device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
+                         const float* __restrict__ row, float u, const DrawOut& o) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float m = -INFINITY;
+    float Z, lse, target;
+    int found = -1;
+    float tprime = INFINITY;
+    if (nblk <= kWave * kSelRegTiles) {
+        // register form: lane l holds tiles [8l, 8l + 8)
+        float2 p[kSelRegTiles];
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) {
+            const int i = lane * kSelRegTiles + t;
+            p[t] = (i < nblk) ? P[i] : make_float2(-INFINITY, 0.0f);
+        }
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) m = fmaxf(m, p[t].x);
+        m = wave_max(m);
+        if (m == -INFINITY) {
+            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
+            return -1;
+        }
+        float mass[kSelRegTiles];
+        float local = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) {
+            mass[t] = tile_mass(p[t], m);
+            local += mass[t];
+        }
+        Z = wave_sum(local);
+        lse = m + __logf(Z);
+        target = clamp_uniform(u) * Z;
+        const float incl = wave_incl_scan(local);
+        float run = __shfl_up(incl, 1, kWave);
+        if (lane == 0) run = 0.0f;
+        int hit = INT32_MAX, last = -1;
+        float before = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) {
+            const float nr = run + mass[t];
+            if (mass[t] > 0.0f) {
+                last = lane * kSelRegTiles + t;
+                if (hit == INT32_MAX && nr > target) {
+                    hit = lane * kSelRegTiles + t;
+                    before = run;
+                }
+            }
+            run = nr;
+        }
+        found = wave_min_int(hit);
+        if (found == INT32_MAX) {
+            found = wave_max_int(last);
+        } else {
+            tprime = target - __shfl(before, found / kSelRegTiles, kWave);
+        }
+    } else {
+        // loop form for vocabularies with more than 512 tiles
+        for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, P[i].x);
+        m = wave_max(m);
+        if (m == -INFINITY) {
+            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
+            return -1;
+        }
+        float z = 0.0f;
+        for (int i = lane; i < nblk; i += kWave) z += tile_mass(P[i], m);
+        Z = wave_sum(z);
+        lse = m + __logf(Z);
+        target = clamp_uniform(u) * Z;
+        float run = 0.0f;
+        for (int base = 0; base < nblk; base += kWave) {
+            const int i = base + lane;
+            const float v = (i < nblk) ? tile_mass(P[i], m) : 0.0f;
+            const float incl = wave_incl_scan(v);
+            float excl = __shfl_up(incl, 1, kWave);
+            if (lane == 0) excl = 0.0f;
+            const unsigned long long hit =
+                __ballot((i < nblk) && (v > 0.0f) && (run + incl > target));
+            if (hit) {
+                const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                found = base + f;
+                tprime = target - (run + __shfl(excl, f, kWave));
+                break;
+            }
+            run += __shfl(incl, kWave - 1, kWave);
+        }
+        if (found < 0) {
+            int last = -1;
+            for (int i = lane; i < nblk; i += kWave)
+                if (tile_mass(P[i], m) > 0.0f) last = i;
+            found = wave_max_int(last);
+        }
+    }
+    return rescan_tile_wave(V, row, found, m, lse, tprime, o);
+}
+
+// ----------------------------------------------------------------------------- block draw
+// The same draw spread over a whole 1024-thread workgroup (one request per workgroup):
+// thread i holds tile i (nblk <= 1024), then column i of the chosen tile. Returns the token
+// in every thread.
+__device__ int draw_block(int V, const float2* __restrict__ P, int nblk,
+                          const float* __restrict__ row, float u, const DrawOut& o,
+                          float* fscr, int* iscr, float* s_before, int* s_tok) {
+    const int tid = threadIdx.x;
+    const float2 p = (tid < nblk) ? P[tid] : make_float2(-INFINITY, 0.0f);
+    const float m = block_max<kSweepThreads>(p.x, fscr);
+    if (m == -INFINITY) {
+        if (o.write && tid == 0) put(o, -1, 0.0f, -INFINITY);
+        return -1;
+    }
+    const float mass = tile_mass(p, m);
+    float Z;
+    const float ex = block_excl_scan<kSweepThreads>(mass, fscr, &Z);
+    const float lse = m + __logf(Z);
+    const float target = clamp_uniform(u) * Z;
+    int found = block_min_int<kSweepThreads>(
+        (tid < nblk && mass > 0.0f && ex + mass > target) ? tid : INT32_MAX, iscr);
+    float tprime = INFINITY;
+    if (found == INT32_MAX) {
+        found = block_max_int<kSweepThreads>((tid < nblk && mass > 0.0f) ? tid : -1, iscr);
+    } else {
+        if (tid == found) *s_before = ex;
+        __syncthreads();
+        tprime = target - *s_before;
+    }
+    // rescan: thread t < 512 owns column t of the tile
+    const long long c = static_cast<long long>(found) * kTileCols + tid;
+    const bool mine = tid < kTileCols && c < V;
+    const float l = mine ? row[c] : -INFINITY;
+    const float e = (l == -INFINITY) ? 0.0f : __expf(l - m);
+    float tot;
+    const float ex2 = block_excl_scan<kSweepThreads>(e, fscr, &tot);
+    int tok = block_min_int<kSweepThreads>(
+        (e > 0.0f && ex2 + e > tprime) ? static_cast<int>(c) : INT32_MAX, iscr);
+    if (tok == INT32_MAX)
+        tok = block_max_int<kSweepThreads>(e > 0.0f ? static_cast<int>(c) : -1, iscr);
+    if (static_cast<long long>(tok) == c && mine) {
+        *s_tok = tok;
+        if (o.write) put(o, tok, __expf(l - lse), lse);
+    }
+    return tok;
+}
+
+// ----------------------------------------------------------------------------- step kernel
+struct StepArgs {
+    int B, V, r, gamma, k, nblk;
+    const float* U;
+    const void* W1;
+    const void* W2;
+    const int32_t* x0;
+    const float* u;
+    int32_t* x_out;
+    float* q_out;
+    float* lse_out;
+    float* L;                 // this step's logits: L + b * L_bstride
+    const float* Lprev;       // the previous step's logits, same stride
+    long long L_bstride;
+    float2* part;             // this step's partials [B][nblk]
+    const float2* part_prev;  // the previous step's partials
+};
+
+template <typename WT, int BT, bool VEC>
+__global__ __launch_bounds__(kSweepThreads, (BT <= 2 ? 8 : 4))
+void draft_step_gemv(StepArgs a) {
+    constexpr int RB = !VEC ? 2 : (sizeof(WT) == 2 ? 8 : 4);   // W2 rows in flight per wave
     extern __shared__ float smem[];
     float* h = smem;                       // [BT][r] gathered W1 rows
-    float* red = smem + BT * r;            // [kSweepWaves][kTileCols] cross-wave partials
+    float* red = smem + BT * a.r;          // [kSweepWaves][kTileCols] cross-wave partials
     __shared__ float scratch[kSweepWaves + 1];
+    __shared__ int iscr[kSweepWaves + 1];
+    __shared__ float s_before;
     __shared__ int tok[BT];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int blk = static_cast<int>(blockIdx.x % static_cast<unsigned>(nblk));   // vocab tile
-    const int grp = static_cast<int>(blockIdx.x / static_cast<unsigned>(nblk));   // request group
+    const int blk = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.nblk));   // vocab tile
+    const int grp = static_cast<int>(blockIdx.x / static_cast<unsigned>(a.nblk));   // req group
     const int b0 = grp * BT;
+    const int V = a.V, r = a.r;
+    const WT* W1 = static_cast<const WT*>(a.W1);
+    const WT* W2 = static_cast<const WT*>(a.W2);
 
-    if (tid < BT) {
-        const int b = b0 + tid;
-        int t = -1;
-        if (b < B) {
-            t = prev[static_cast<long long>(b) * prev_stride];
-            if (t < 0 || t >= V) t = -1;   // out-of-range previous token: sentinel request
+    // 1. previous token of every request in the group
+    if (a.k == 0) {
+        if (tid < BT) {
+            const int b = b0 + tid;
+            int t = -1;
+            if (b < a.B) {
+                t = a.x0[b];
+                if (t < 0 || t >= V) t = -1;   // out-of-range context token: dead request
+            }
+            tok[tid] = t;
         }
-        tok[tid] = t;
+    } else if (BT == 1) {
+        if (b0 < a.B) {
+            const long long o = static_cast<long long>(b0) * a.gamma + (a.k - 1);
+            const DrawOut out{a.x_out + o, a.q_out ? a.q_out + o : nullptr,
+                              a.lse_out ? a.lse_out + o : nullptr, blk == 0};
+            const int t = draw_block(V, a.part_prev + static_cast<long long>(b0) * a.nblk, a.nblk,
+                                     a.Lprev + b0 * a.L_bstride, a.u[o], out, scratch, iscr,
+                                     &s_before, &tok[0]);
+            if (t < 0 && tid == 0) tok[0] = -1;
+        } else if (tid == 0) {
+            tok[0] = -1;
+        }
+    } else if (wave < BT) {
+        const int b = b0 + wave;
+        int t = -1;
+        if (b < a.B) {
+            const long long o = static_cast<long long>(b) * a.gamma + (a.k - 1);
+            const DrawOut out{a.x_out + o, a.q_out ? a.q_out + o : nullptr,
+                              a.lse_out ? a.lse_out + o : nullptr, blk == 0};
+            t = draw_wave(V, a.part_prev + static_cast<long long>(b) * a.nblk, a.nblk,
+                          a.Lprev + b * a.L_bstride, a.u[o], out);
+        }
+        if (lane == 0) tok[wave] = t;
     }
     __syncthreads();
     for (int i = tid; i < BT * r; i += kSweepThreads) {
@@ -189,78 +364,81 @@ void draft_sweep_gemv(int B, int V, int r, int gamma, int k,
         const int t = tok[bi];
         h[i] = (t >= 0) ? to_f32(W1[static_cast<long long>(t) * r + j]) : 0.0f;
     }
+    // U_k of this thread's epilogue column, fetched before the sweep
+    const bool owner = tid < kTileCols;
+    const long long col = static_cast<long long>(blk) * kTileCols + tid;
+    float uk[BT];
+#pragma unroll
+    for (int bi = 0; bi < BT; ++bi) {
+        const int b = b0 + bi;
+        uk[bi] = (owner && b < a.B && col < V)
+                     ? a.U[(static_cast<long long>(b) * a.gamma + a.k) * V + col] : 0.0f;
+    }
     __syncthreads();
 
-    // projection: lane owns 8 consecutive columns, waves split the rank dimension
+    // 2. projection: lane owns 8 consecutive columns; wave w owns rank rows [jb, je)
     const long long col0 = static_cast<long long>(blk) * kTileCols + lane * kColsPerLane;
     const long long avail = static_cast<long long>(V) - col0;
+    const int rpw = (r + kSweepWaves - 1) / kSweepWaves;
+    const int jb = wave * rpw, je = min(r, jb + rpw);
     float acc[BT][kColsPerLane];
 #pragma unroll
     for (int bi = 0; bi < BT; ++bi)
 #pragma unroll
         for (int e = 0; e < kColsPerLane; ++e) acc[bi][e] = 0.0f;
-    if (avail > 0) {
+    if (avail > 0 && jb < je) {
         const WT* wp = W2 + col0;
-#pragma unroll 4
-        for (int j = wave; j < r; j += kSweepWaves) {
-            float w[kColsPerLane];
-            load8<VEC>(wp + static_cast<long long>(j) * V, avail, w);
+        for (int j0 = jb; j0 < je; j0 += RB) {
+            Seg<WT> seg[RB];
 #pragma unroll
-            for (int bi = 0; bi < BT; ++bi) {
-                const float hv = h[bi * r + j];
+            for (int t = 0; t < RB; ++t) {
+                const long long j = min(j0 + t, je - 1);     // clamped: always a valid row
+                if (VEC)
+                    seg[t].load(wp + j * V);
+                else
+                    seg[t].load_guarded(wp + j * V, avail);
+            }
 #pragma unroll
-                for (int e = 0; e < kColsPerLane; ++e) acc[bi][e] = fmaf(hv, w[e], acc[bi][e]);
+            for (int t = 0; t < RB; ++t) {
+                const int j = j0 + t;
+                const float on = (j < je) ? 1.0f : 0.0f;     // rows past je add nothing
+                float w[kColsPerLane];
+                seg[t].to_f32(w);
+#pragma unroll
+                for (int bi = 0; bi < BT; ++bi) {
+                    const float hv = on * h[bi * r + min(j, je - 1)];
+#pragma unroll
+                    for (int e = 0; e < kColsPerLane; ++e) acc[bi][e] = fmaf(hv, w[e], acc[bi][e]);
+                }
             }
         }
     }
 
-    // epilogue per request: fixed-order cross-wave sum, + U_k, logits store, tile partial
-    const long long col = static_cast<long long>(blk) * kTileCols + tid;
+    // 3. epilogue per request: fixed-order cross-wave sum, + U_k, logits store, tile partial
 #pragma unroll
     for (int bi = 0; bi < BT; ++bi) {
         const int b = b0 + bi;
-#pragma unroll
-        for (int e = 0; e < kColsPerLane; ++e)
-            red[wave * kTileCols + lane * kColsPerLane + e] = acc[bi][e];
+        float4* dst = reinterpret_cast<float4*>(red + wave * kTileCols + lane * kColsPerLane);
+        dst[0] = make_float4(acc[bi][0], acc[bi][1], acc[bi][2], acc[bi][3]);
+        dst[1] = make_float4(acc[bi][4], acc[bi][5], acc[bi][6], acc[bi][7]);
         __syncthreads();
-        const bool live = (b < B) && (tok[bi] >= 0);
+        const bool live = (b < a.B) && (tok[bi] >= 0);
         float l = -INFINITY;
-        if (live && col < V) {
+        if (owner && live && col < V) {
             float s = 0.0f;
 #pragma unroll
             for (int w = 0; w < kSweepWaves; ++w) s += red[w * kTileCols + tid];
-            l = U[(static_cast<long long>(b) * gamma + k) * V + col] + s;
+            l = uk[bi] + s;
         }
-        if (b < B && col < V) L[b * L_bstride + col] = l;
+        if (owner && b < a.B && col < V) a.L[b * a.L_bstride + col] = l;
         const float m = block_max<kSweepThreads>(l, scratch);   // also fences `red` reuse
         const float ex = (l == -INFINITY) ? 0.0f : __expf(l - m);
         const float s = block_sum<kSweepThreads>(ex, scratch);
-        if (tid == 0 && b < B) part[static_cast<long long>(b) * nblk + blk] = make_float2(m, s);
-    }
-
-    if (FUSED) {
-        __threadfence();                   // release this workgroup's logits and partials
-        __syncthreads();
-        if (tid == 0) {
-            const unsigned int done = atomicAdd(&counters[grp], 1u);
-            s_last = (done == static_cast<unsigned int>(nblk) - 1u);
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();                   // acquire the other workgroups' results
-        if (tid == 0) counters[grp] = 0u;
-        if (wave < BT) {
-            const int b = b0 + wave;
-            if (b < B) {
-                const long long o = static_cast<long long>(b) * gamma + k;
-                select_wave(V, part + static_cast<long long>(b) * nblk, nblk, L + b * L_bstride,
-                            u[o], x_out + o, q_out ? q_out + o : nullptr,
-                            lse_out ? lse_out + o : nullptr);
-            }
-        }
+        if (tid == 0 && b < a.B) a.part[static_cast<long long>(b) * a.nblk + blk] = make_float2(m, s);
     }
 }
 
+// Draw of the last position: one wave per request.
 __global__ __launch_bounds__(kSelThreads)
 void draft_select(int B, int V, int gamma, int k, const float2* __restrict__ part, int nblk,
                   const float* __restrict__ L, long long L_bstride, const float* __restrict__ u,
@@ -269,54 +447,57 @@ void draft_select(int B, int V, int gamma, int k, const float2* __restrict__ par
     const int b = blockIdx.x * (kSelThreads / kWave) + threadIdx.x / kWave;
     if (b >= B) return;
     const long long o = static_cast<long long>(b) * gamma + k;
-    select_wave(V, part + static_cast<long long>(b) * nblk, nblk, L + b * L_bstride, u[o],
-                x_out + o, q_out ? q_out + o : nullptr, lse_out ? lse_out + o : nullptr);
+    const DrawOut out{x_out + o, q_out ? q_out + o : nullptr, lse_out ? lse_out + o : nullptr,
+                      true};
+    draw_wave(V, part + static_cast<long long>(b) * nblk, nblk, L + b * L_bstride, u[o], out);
 }
 
-template <typename WT, int BT, bool FUSED>
-hipError_t launch_sweep_bt(const DraftStep& s, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(s.nblk) * ((s.B + BT - 1) / BT));   // 1-D: tile fastest
-    const size_t smem = (static_cast<size_t>(BT) * s.r + kSweepWaves * kTileCols) * sizeof(float);
-    const bool vec = (s.V % kColsPerLane) == 0 &&
-                     (reinterpret_cast<uintptr_t>(s.W2) % 16) == 0;
-#define DSPARK_SWEEP_ARGS                                                                     \
-    s.B, s.V, s.r, s.gamma, s.k, s.U, static_cast<const WT*>(s.W1),                             \
-        static_cast<const WT*>(s.W2), s.prev, s.prev_stride, s.L, s.L_bstride, s.part, s.nblk,  \
-        s.counters, s.u, s.x_out, s.q_out, s.lse_out
+template <typename WT, int BT>
+hipError_t launch_step_bt(const StepArgs& a, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(a.nblk) * ((a.B + BT - 1) / BT));   // 1-D: tile fastest
+    const size_t smem = (static_cast<size_t>(BT) * a.r + kSweepWaves * kTileCols) * sizeof(float);
+    const bool vec = (a.V % kColsPerLane) == 0 && (reinterpret_cast<uintptr_t>(a.W2) % 16) == 0;
     if (vec)
-        hipLaunchKernelGGL((draft_sweep_gemv<WT, BT, true, FUSED>), grid, dim3(kSweepThreads),
-                           smem, st, DSPARK_SWEEP_ARGS);
+        hipLaunchKernelGGL((draft_step_gemv<WT, BT, true>), grid, dim3(kSweepThreads), smem, st, a);
     else
-        hipLaunchKernelGGL((draft_sweep_gemv<WT, BT, false, FUSED>), grid, dim3(kSweepThreads),
-                           smem, st, DSPARK_SWEEP_ARGS);
-#undef DSPARK_SWEEP_ARGS
+        hipLaunchKernelGGL((draft_step_gemv<WT, BT, false>), grid, dim3(kSweepThreads), smem, st, a);
     return hipGetLastError();
 }
 
 template <typename WT>
-hipError_t launch_step_w(const DraftStep& s, hipStream_t st) {
-    // small batches: one fused launch per step, all requests of the batch in one group
-    if (s.B == 1) return launch_sweep_bt<WT, 1, true>(s, st);
-    if (s.B == 2) return launch_sweep_bt<WT, 2, true>(s, st);
-    if (s.B <= 4) return launch_sweep_bt<WT, 4, true>(s, st);
-    if (s.B <= 8) return launch_sweep_bt<WT, 8, true>(s, st);
-    hipError_t e = launch_sweep_bt<WT, 8, false>(s, st);
-    if (e != hipSuccess) return e;
-    const int waves = kSelThreads / kWave;
-    hipLaunchKernelGGL(draft_select, dim3((s.B + waves - 1) / waves), dim3(kSelThreads), 0, st,
-                       s.B, s.V, s.gamma, s.k, s.part, s.nblk, s.L, s.L_bstride, s.u, s.x_out,
-                       s.q_out, s.lse_out);
-    return hipGetLastError();
+hipError_t launch_step_w(const StepArgs& a, hipStream_t st) {
+    if (a.B == 1) return launch_step_bt<WT, 1>(a, st);
+    if (a.B == 2) return launch_step_bt<WT, 2>(a, st);
+    if (a.B <= 4) return launch_step_bt<WT, 4>(a, st);
+    return launch_step_bt<WT, 8>(a, st);
 }
 
 }  // namespace
 
 int draft_tile_cols() { return kTileCols; }
 
-int draft_counter_count(int B) { return (B + 7) / 8; }
-
-hipError_t launch_draft_step(const DraftStep& s, hipStream_t st) {
-    return (s.w_dtype == 1) ? launch_step_w<uint16_t>(s, st) : launch_step_w<float>(s, st);
+hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
+    StepArgs a;
+    a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma; a.nblk = c.nblk;
+    a.U = c.U; a.W1 = c.W1; a.W2 = c.W2; a.x0 = c.x0; a.u = c.u;
+    a.x_out = c.x_out; a.q_out = c.q_out; a.lse_out = c.lse_out;
+    a.L_bstride = c.L_bstride;
+    for (int k = 0; k < c.gamma; ++k) {
+        a.k = k;
+        a.L = c.L[k];
+        a.Lprev = k ? c.L[k - 1] : nullptr;
+        a.part = c.part[k & 1];
+        a.part_prev = c.part[(k + 1) & 1];
+        const hipError_t e = (c.w_dtype == 1) ? launch_step_w<uint16_t>(a, st)
+                                              : launch_step_w<float>(a, st);
+        if (e != hipSuccess) return e;
+    }
+    const int k = c.gamma - 1;
+    const int waves = kSelThreads / kWave;
+    hipLaunchKernelGGL(draft_select, dim3((c.B + waves - 1) / waves), dim3(kSelThreads), 0, st,
+                       c.B, c.V, c.gamma, k, static_cast<const float2*>(c.part[k & 1]), c.nblk,
+                       c.L[k], c.L_bstride, c.u, c.x_out, c.q_out, c.lse_out);
+    return hipGetLastError();
 }
 
 }  // namespace dspark

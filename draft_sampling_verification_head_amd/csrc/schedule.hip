@@ -14,7 +14,8 @@
 // The kept 44 bits of the fp64 a (sign, exponent, 32 mantissa bits) carry the sums.
 // Lengths come from one cut key: request r keeps its candidates whose key is below the key
 // at rank n*. Because a is non-increasing along a block and ties rank earlier positions
-// first, that set is a prefix of every block.
+// first, that set is a prefix of every block. The fp64 prefix products are kept in the
+// caller's workspace between the ranking and the counting.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,7 +23,6 @@ namespace dspark {
 
 namespace {
 
-constexpr int kThreads = 1024;
 constexpr int kMaxCand = 16384;            // 128 KB of keys in LDS
 constexpr unsigned long long kMask44 = (1ull << 44) - 1ull;
 
@@ -58,12 +58,13 @@ __device__ __forceinline__ Best better(Best a, Best b) {
     return a;
 }
 
+template <int kThreads>
 __global__ __launch_bounds__(kThreads)
 void schedule_kernel(int R, int G, const float* __restrict__ conf, const float* __restrict__ temp,
                      const float* __restrict__ sps, int Bmax, int mode, int npad,
                      int32_t* __restrict__ len_out, int32_t* __restrict__ t_off_out,
                      int32_t* __restrict__ K_out, float* __restrict__ theta_out,
-                     float* __restrict__ a_out) {
+                     float* __restrict__ a_out, double* __restrict__ a_ws) {
     __shared__ unsigned long long keys[kMaxCand];
     __shared__ double dscr[kThreads / kWave + 1];
     __shared__ int iscr[kThreads / kWave + 1];
@@ -75,19 +76,25 @@ void schedule_kernel(int R, int G, const float* __restrict__ conf, const float* 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int N = R * G;
 
-    // 1. temperature, prefix products, keys
+    // 1. temperature-scaled confidences, one candidate per thread (fp64 bits parked in keys)
+    for (int i = tid; i < N; i += kThreads)
+        keys[i] = static_cast<unsigned long long>(__double_as_longlong(scaled_conf(conf[i], temp, i % G)));
+    for (int i = N + tid; i < npad; i += kThreads) keys[i] = ~0ull;
+    __syncthreads();
+    // 2. prefix products along each block, then the ranking keys
     for (int r = tid; r < R; r += kThreads) {
         double a = 1.0;
         for (int j = 0; j < G; ++j) {
-            a *= scaled_conf(conf[static_cast<long long>(r) * G + j], temp, j);
-            keys[r * G + j] = make_key(a, j, r);
-            if (a_out) a_out[static_cast<long long>(r) * G + j] = static_cast<float>(a);
+            const int i = r * G + j;
+            a *= __longlong_as_double(static_cast<long long>(keys[i]));
+            a_ws[i] = a;
+            keys[i] = make_key(a, j, r);
+            if (a_out) a_out[i] = static_cast<float>(a);
         }
     }
-    for (int i = N + tid; i < npad; i += kThreads) keys[i] = ~0ull;
     __syncthreads();
 
-    // 2. bitonic sort, ascending
+    // 3. bitonic sort, ascending
     for (int kk = 2; kk <= npad; kk <<= 1) {
         for (int jj = kk >> 1; jj > 0; jj >>= 1) {
             for (int i = tid; i < npad; i += kThreads) {
@@ -105,7 +112,7 @@ void schedule_kernel(int R, int G, const float* __restrict__ conf, const float* 
         }
     }
 
-    // 3. prefix sums of the ranked a, Theta(n) for n = 0..nmax
+    // 4. prefix sums of the ranked a, Theta(n) for n = 0..nmax
     const int nmax = min(N, Bmax - R);
     const int E = (npad + kThreads - 1) / kThreads;     // ranks per thread
     const int p0 = tid * E;
@@ -176,18 +183,14 @@ void schedule_kernel(int R, int G, const float* __restrict__ conf, const float* 
     const unsigned long long cut = (nstar < npad) ? keys[nstar] : ~0ull;
     __syncthreads();
 
-    // 4. lengths: candidates ranked above the cut (recomputed keys are bit-identical)
+    // 5. lengths: candidates ranked above the cut (a_ws rows were written by this thread)
     for (int r = tid; r < R; r += kThreads) {
-        double a = 1.0;
         int cnt = 0;
-        for (int j = 0; j < G; ++j) {
-            a *= scaled_conf(conf[static_cast<long long>(r) * G + j], temp, j);
-            cnt += make_key(a, j, r) < cut;
-        }
+        for (int j = 0; j < G; ++j) cnt += make_key(a_ws[r * G + j], j, r) < cut;
         len_out[r] = cnt;
     }
 
-    // 5. offsets: exclusive scan of len + 1
+    // 6. offsets: exclusive scan of len + 1
     if (t_off_out) {
         int run = 0;
         for (int base = 0; base < R; base += kThreads) {
@@ -213,11 +216,17 @@ int schedule_max_candidates() { return kMaxCand; }
 hipError_t launch_schedule(int R, int gamma, const float* conf, const float* temp,
                            const float* sps, int Bmax, int mode, int32_t* len_out,
                            int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out,
-                           hipStream_t st) {
+                           double* a_ws, hipStream_t st) {
     int npad = 1;
     while (npad < R * gamma) npad <<= 1;
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, st, R, gamma, conf, temp, sps,
-                       Bmax, mode, npad, len_out, t_off_out, K_out, theta_out, a_out);
+    if (npad <= 2048 && R <= 2048)
+        hipLaunchKernelGGL(schedule_kernel<256>, dim3(1), dim3(256), 0, st, R, gamma, conf, temp,
+                           sps, Bmax, mode, npad, len_out, t_off_out, K_out, theta_out, a_out,
+                           a_ws);
+    else
+        hipLaunchKernelGGL(schedule_kernel<1024>, dim3(1), dim3(1024), 0, st, R, gamma, conf,
+                           temp, sps, Bmax, mode, npad, len_out, t_off_out, K_out, theta_out,
+                           a_out, a_ws);
     return hipGetLastError();
 }
 

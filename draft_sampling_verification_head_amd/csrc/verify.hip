@@ -3,16 +3,24 @@
 // [P1] = "大模型推理加速的系统级工程：DeepSeek V4-Pro DSpark 推测解码方案深度解析与开源工具链
 // DeepSpec" (Best Partners TV); [P3] = "DSpark Speculative Decoding" (concept note).
 //
-// row_lse        - [P1] section "大模型推理的显存瓶颈与推测解码的演进逻辑": the accept test needs
-//                  normalised probabilities, so every verified row gets its logsumexp in one
-//                  HBM pass (online max / sum-exp, float4 loads, one workgroup per row).
-// verify_finish  - one workgroup per request: gathers p_d(x_k), p_t(x_k), tests
-//                  log u < log p_t - log p_d for all k in one wave, takes the first rejection
-//                  from a ballot, then draws the residual max(0, p_t - p_d) (or the bonus
-//                  p_t row, [P3] intro) by inverse CDF: chunk sums in id order, chunk search,
-//                  in-chunk rescan.
-// tv             - [P3] "Confidence-Scheduled Verification": c* = sum_v min(p_d, p_t), computed
-//                  as sum_v exp(min(l_d - lse_d, l_t - lse_t)) (one exp per element).
+// Every vocabulary row is cut into chunks of 8192 logits, one workgroup per chunk, so even a
+// single request spreads over the whole chip and every pass is one HBM sweep. Per-row
+// results are combined by the next kernel on the stream (kernel boundaries order the
+// writes; no workgroup needs a device-scope fence).
+//
+// row_stats      - [P1] section "大模型推理的显存瓶颈与推测解码的演进逻辑": the acceptance test needs
+//                  normalised probabilities; every verified row gets chunk (max, sum exp)
+//                  partials.
+// verify_chunks  - per request and chunk: merges the row partials into lse (chunk order),
+//                  runs the acceptance test of every verified position
+//                  (log u < log p_t(x) - log p_d(x); first rejection from a ballot) and sums the
+//                  chunk's mass under the final law: the residual max(0, p_t - p_d) at the first
+//                  rejection, or the bonus row p_t when all are kept ([P3] intro). Chunk 0 also
+//                  publishes n and the normalisers.
+// verify_select  - per request: finds the chunk holding u * total in chunk order and rescans
+//                  it in token order for the emitted token.
+// tv_chunks / tv_merge - [P3] "Confidence-Scheduled Verification": c* = sum_v min(p_d, p_t),
+//                  summed per chunk as exp(min(l_d - lse_d, l_t - lse_t)), then in chunk order.
 // Target rows are flattened with per-request offsets ([P1] section "极致的工程实现与内核优化").
 #include "common.h"
 #include "kernels.h"
@@ -21,11 +29,10 @@ namespace dspark {
 
 namespace {
 
-constexpr int kLseThreads = 256;
-constexpr int kFinThreads = 1024;
-constexpr int kFinPerThread = 4;
-constexpr int kChunk = kFinThreads * kFinPerThread;
-constexpr int kTvThreads = 256;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kPer = 32;                      // logits per thread per chunk
+constexpr int kChunk = kThreads * kPer;       // 8192 logits (32 KB) per workgroup
 
 struct ReqRows {
     int ell;
@@ -42,7 +49,56 @@ __device__ __forceinline__ ReqRows request_rows(const RowSet& rs, int b) {
     return q;
 }
 
-// (max, sum exp(x - max)) pairs; combination is symmetric, so butterflies are exact.
+__device__ __forceinline__ float qnan() { return __int_as_float(0x7fc00000); }
+
+// Chunk c of a row in the sweep layout: thread t holds float4 granules t + kThreads*g.
+template <bool VEC4>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int c, int V,
+                                           float (&x)[kPer]) {
+    const long long base = static_cast<long long>(c) * kChunk;
+    const int t = threadIdx.x;
+    if (VEC4) {
+        const float4* r4 = reinterpret_cast<const float4*>(row + base);
+#pragma unroll
+        for (int g = 0; g < kPer / 4; ++g) {
+            const long long i = static_cast<long long>(t) + kThreads * g;
+            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (base + 4 * i < V) v = r4[i];        // V % 4 == 0: a granule is in or out
+            x[4 * g] = v.x; x[4 * g + 1] = v.y; x[4 * g + 2] = v.z; x[4 * g + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < kPer / 4; ++g)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const long long v = base + 4 * (static_cast<long long>(t) + kThreads * g) + w;
+                x[4 * g + w] = (v < V) ? row[v] : -INFINITY;
+            }
+    }
+}
+
+// Chunk c in the rescan layout: thread t owns the kPer consecutive logits starting at
+// c*kChunk + kPer*t, so a block scan runs in token-id order.
+template <bool VEC4>
+__device__ __forceinline__ void load_chunk_contig(const float* __restrict__ row, int c, int V,
+                                                  float (&x)[kPer]) {
+    const long long base =
+        static_cast<long long>(c) * kChunk + static_cast<long long>(kPer) * threadIdx.x;
+    if (VEC4) {
+        const float4* r4 = reinterpret_cast<const float4*>(row + base);
+#pragma unroll
+        for (int g = 0; g < kPer / 4; ++g) {
+            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (base + 4 * g < V) v = r4[g];
+            x[4 * g] = v.x; x[4 * g + 1] = v.y; x[4 * g + 2] = v.z; x[4 * g + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) x[e] = (base + e < V) ? row[base + e] : -INFINITY;
+    }
+}
+
+// (max, sum exp(x - max)) pairs; the combination is symmetric, so butterflies are exact.
 __device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s2) {
     const float mm = fmaxf(m, m2);
     if (mm == -INFINITY) {
@@ -54,87 +110,84 @@ __device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s
     m = mm;
 }
 
-__device__ __forceinline__ void ms_push4(float& m, float& s, float a, float b, float c, float d) {
-    const float cm = fmaxf(fmaxf(a, b), fmaxf(c, d));
-    if (cm == -INFINITY) return;
-    if (cm > m) {
-        s = (m == -INFINITY) ? 0.0f : s * __expf(m - cm);
-        m = cm;
-    }
-    s += (__expf(a - m) + __expf(b - m)) + (__expf(c - m) + __expf(d - m));
-}
-
-template <bool VEC4>
-__device__ float row_logsumexp(const float* __restrict__ row, int V) {
-    __shared__ float ms[2][kLseThreads / kWave];
-    float m = -INFINITY, s = 0.0f;
-    const int tid = threadIdx.x;
-    if (VEC4) {
-        const float4* r4 = reinterpret_cast<const float4*>(row);
-        const int n4 = V >> 2;
-        for (int i = tid; i < n4; i += kLseThreads) {
-            const float4 x = r4[i];
-            ms_push4(m, s, x.x, x.y, x.z, x.w);
-        }
-    } else {
-        for (long long base = static_cast<long long>(tid) * 4; base < V; base += 4LL * kLseThreads) {
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (base + e < V) ? row[base + e] : -INFINITY;
-            ms_push4(m, s, x[0], x[1], x[2], x[3]);
-        }
-    }
+__device__ __forceinline__ void block_ms(float& m, float& s, float (*sm)[kWaves]) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
         ms_combine(m, s, m2, s2);
     }
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     if (lane == 0) {
-        ms[0][wave] = m;
-        ms[1][wave] = s;
+        sm[0][wave] = m;
+        sm[1][wave] = s;
     }
     __syncthreads();
-    m = ms[0][0];
-    s = ms[1][0];
+    m = sm[0][0];
+    s = sm[1][0];
 #pragma unroll
-    for (int w = 1; w < kLseThreads / kWave; ++w) ms_combine(m, s, ms[0][w], ms[1][w]);
-    return (m == -INFINITY) ? -INFINITY : m + __logf(s);
+    for (int w = 1; w < kWaves; ++w) ms_combine(m, s, sm[0][w], sm[1][w]);
+    __syncthreads();
 }
 
+// lse of one row from its chunk partials, merged by one wave (max first, then the scaled
+// sums in lane-strided order and a butterfly); the same value in every lane.
+__device__ __forceinline__ float merge_lse_wave(const float2* __restrict__ P, int nch) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float mm = -INFINITY;
+    for (int i = lane; i < nch; i += kWave) mm = fmaxf(mm, P[i].x);
+    mm = wave_max(mm);
+    if (mm == -INFINITY) return -INFINITY;
+    float ss = 0.0f;
+    for (int i = lane; i < nch; i += kWave)
+        ss += (P[i].x == -INFINITY) ? 0.0f : P[i].y * __expf(P[i].x - mm);
+    ss = wave_sum(ss);
+    return mm + __logf(ss);
+}
+
+// Row slots of a request: slot s <= gamma is target row s, slot gamma+1+k is draft row k.
+__device__ __forceinline__ const float2* slot_part(const float2* part, int b, int slot, int G,
+                                                   int nch) {
+    return part + (static_cast<long long>(b) * (2 * G + 1) + slot) * nch;
+}
+
+// ----------------------------------------------------------------------------- row_stats
 template <bool VEC4>
-__global__ __launch_bounds__(kLseThreads)
-void row_lse_kernel(RowSet rs, const float* __restrict__ lse_d_in, float* __restrict__ lse_d,
-                    float* __restrict__ lse_t) {
-    const int G = rs.gamma;
-    const int slot = static_cast<int>(blockIdx.x % static_cast<unsigned>(2 * G + 1));
-    const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(2 * G + 1));
+__global__ __launch_bounds__(kThreads)
+void row_stats_kernel(RowSet rs, int nch, const float* __restrict__ lse_d_in,
+                      float2* __restrict__ part) {
+    __shared__ float sm[2][kWaves];
+    const int G = rs.gamma, S = 2 * G + 1;
+    const int c = static_cast<int>(blockIdx.x % static_cast<unsigned>(nch));
+    const long long rowid = blockIdx.x / static_cast<unsigned>(nch);        // b * S + slot
+    const int slot = static_cast<int>(rowid % S);
+    const int b = static_cast<int>(rowid / S);
     const ReqRows q = request_rows(rs, b);
     const float* row;
-    float* out;
     bool valid;
     if (slot <= G) {
-        out = lse_t + static_cast<long long>(b) * (G + 1) + slot;
         valid = q.ok && slot <= q.ell;
         row = rs.Lt + (q.off + slot) * rs.V;
     } else {
         const int k = slot - G - 1;
-        out = lse_d + static_cast<long long>(b) * G + k;
-        valid = q.ok && k < q.ell;
+        valid = q.ok && k < q.ell && !lse_d_in;
         row = rs.Ld + (static_cast<long long>(b) * G + k) * rs.V;
-        if (valid && lse_d_in) {
-            if (threadIdx.x == 0) *out = lse_d_in[static_cast<long long>(b) * G + k];
-            return;
-        }
     }
-    if (!valid) {
-        if (threadIdx.x == 0) *out = __int_as_float(0x7fc00000);
-        return;
+    if (!valid) return;
+    float x[kPer];
+    load_chunk<VEC4>(row, c, rs.V, x);
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) m = fmaxf(m, x[e]);
+    float s = 0.0f;
+    if (m != -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) s += __expf(x[e] - m);
     }
-    const float lse = row_logsumexp<VEC4>(row, rs.V);
-    if (threadIdx.x == 0) *out = lse;
+    block_ms(m, s, sm);
+    if (threadIdx.x == 0) part[rowid * nch + c] = make_float2(m, s);
 }
 
+// ----------------------------------------------------------------------------- verify
 // Weights of the final draw: p_t (bonus, or residual with zero mass) or max(0, p_t - p_d).
 struct FinalRow {
     const float* lt;
@@ -151,45 +204,63 @@ struct FinalRow {
 };
 
 template <bool VEC4>
-__device__ __forceinline__ void weights4(const FinalRow& fr, long long v0, int V, float (&w)[4]) {
-    if (VEC4 && v0 + 4 <= V) {
-        const float4 t = *reinterpret_cast<const float4*>(fr.lt + v0);
-        float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (fr.residual) d = *reinterpret_cast<const float4*>(fr.ld + v0);
-        w[0] = fr.weight(t.x, d.x);
-        w[1] = fr.weight(t.y, d.y);
-        w[2] = fr.weight(t.z, d.z);
-        w[3] = fr.weight(t.w, d.w);
-    } else {
+__device__ __forceinline__ float chunk_mass(const FinalRow& fr, int c, int V) {
+    float t[kPer], d[kPer];
+    load_chunk<VEC4>(fr.lt, c, V, t);
+    if (fr.residual) load_chunk<VEC4>(fr.ld, c, V, d);
+    float s = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const long long v = v0 + e;
-            w[e] = (v < V) ? fr.weight(fr.lt[v], fr.residual ? fr.ld[v] : 0.0f) : 0.0f;
-        }
-    }
+    for (int e = 0; e < kPer; ++e) s += fr.weight(t[e], fr.residual ? d[e] : 0.0f);
+    return s;
 }
 
-template <bool VEC4>
-__global__ __launch_bounds__(kFinThreads)
-void verify_finish_kernel(RowSet rs, const int32_t* __restrict__ x, const float* __restrict__ lse_d,
-                          const float* __restrict__ lse_t, const float* __restrict__ u_acc,
-                          const float* __restrict__ u_fin, float* __restrict__ chunk_ws,
-                          int nchunk, int32_t* __restrict__ n_out, int32_t* __restrict__ y_out) {
-    __shared__ float fscr[kFinThreads / kWave + 1];
-    __shared__ int iscr[kFinThreads / kWave + 1];
-    __shared__ int s_n, s_bad, s_found;
-    __shared__ float s_tprime, s_total;
+// Per-request state handed from verify_chunks (chunk 0) to verify_select.
+struct ReqState {
+    int n;          // accepted count, -1 for a faulty request
+    int residual;   // 1: residual draw at position n+1, 0: p_t draw
+    float lse_t, lse_d;
+};
 
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads)
+void verify_chunks_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
+                          const float2* __restrict__ part, const float* __restrict__ lse_d_in,
+                          const float* __restrict__ u_acc, float* __restrict__ lse_d_out,
+                          float* __restrict__ lse_t_out, float* __restrict__ csum,
+                          ReqState* __restrict__ state) {
+    __shared__ float fscr[kWaves + 1];
+    __shared__ float s_lt[65], s_ld[64];
+    __shared__ int s_n, s_bad;
+
+    const int c = static_cast<int>(blockIdx.x % static_cast<unsigned>(nch));
+    const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(nch));
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int G = rs.gamma, V = rs.V;
-    int32_t* y = y_out + static_cast<long long>(b) * (G + 1);
     const ReqRows q = request_rows(rs, b);
     if (!q.ok) {
-        for (int i = tid; i <= G; i += kFinThreads) y[i] = -1;
-        if (tid == 0) n_out[b] = -1;
+        if (c == 0 && tid == 0) state[b] = ReqState{-1, 0, 0.0f, 0.0f};
+        if (c == 0) {
+            for (int i = tid; i <= G; i += kThreads) {
+                if (lse_t_out) lse_t_out[static_cast<long long>(b) * (G + 1) + i] = qnan();
+                if (lse_d_out && i < G) lse_d_out[static_cast<long long>(b) * G + i] = qnan();
+            }
+        }
         return;
     }
+    // normalisers of the verified rows: each wave merges the partials of some rows
+    for (int slot = wave; slot <= q.ell; slot += kWaves) {
+        const float v = merge_lse_wave(slot_part(part, b, slot, G, nch), nch);
+        if (lane == 0) s_lt[slot] = v;
+    }
+    for (int k = wave; k < q.ell; k += kWaves) {
+        float v;
+        if (lse_d_in)
+            v = lse_d_in[static_cast<long long>(b) * G + k];
+        else
+            v = merge_lse_wave(slot_part(part, b, G + 1 + k, G, nch), nch);
+        if (lane == 0) s_ld[k] = v;
+    }
+    __syncthreads();
 
     // acceptance test for every verified position in one wave (gamma <= 64)
     if (wave == 0) {
@@ -202,8 +273,7 @@ void verify_finish_kernel(RowSet rs, const int32_t* __restrict__ x, const float*
             } else {
                 const float ltx = rs.Lt[(q.off + k) * V + xk];
                 const float ldx = rs.Ld[(static_cast<long long>(b) * G + k) * V + xk];
-                const float lst = lse_t[static_cast<long long>(b) * (G + 1) + k];
-                const float lsd = lse_d[static_cast<long long>(b) * G + k];
+                const float lst = s_lt[k], lsd = s_ld[k];
                 const float lpt = (lst == -INFINITY) ? -INFINITY : ltx - lst;
                 const float lpd = (lsd == -INFINITY) ? -INFINITY : ldx - lsd;
                 bool acc;
@@ -222,175 +292,258 @@ void verify_finish_kernel(RowSet rs, const int32_t* __restrict__ x, const float*
         }
     }
     __syncthreads();
-    if (s_bad) {
-        for (int i = tid; i <= G; i += kFinThreads) y[i] = -1;
+    const int n = s_n;
+    if (c == 0) {
+        for (int i = tid; i <= G; i += kThreads) {
+            if (lse_t_out)
+                lse_t_out[static_cast<long long>(b) * (G + 1) + i] = (i <= q.ell) ? s_lt[i] : qnan();
+            if (lse_d_out && i < G)
+                lse_d_out[static_cast<long long>(b) * G + i] = (i < q.ell) ? s_ld[i] : qnan();
+        }
+        if (tid == 0)
+            state[b] = s_bad ? ReqState{-1, 0, 0.0f, 0.0f}
+                             : ReqState{n, n < q.ell ? 1 : 0, s_lt[n], n < q.ell ? s_ld[n] : 0.0f};
+    }
+    if (s_bad) return;
+    FinalRow fr;
+    fr.lt = rs.Lt + (q.off + n) * V;
+    fr.lse_t = s_lt[n];
+    fr.residual = n < q.ell;
+    fr.ld = fr.residual ? rs.Ld + (static_cast<long long>(b) * G + n) * V : nullptr;
+    fr.lse_d = fr.residual ? s_ld[n] : 0.0f;
+    const float s = block_sum<kThreads>(chunk_mass<VEC4>(fr, c, V), fscr);
+    if (tid == 0) csum[static_cast<long long>(b) * nch + c] = s;
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads)
+void verify_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
+                          const float* __restrict__ u_fin, float* __restrict__ csum,
+                          const ReqState* __restrict__ state, int32_t* __restrict__ n_out,
+                          int32_t* __restrict__ y_out) {
+    __shared__ float fscr[kWaves + 1];
+    __shared__ int iscr[kWaves + 1];
+    __shared__ int s_found;
+    __shared__ float s_tprime, s_total;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int G = rs.gamma, V = rs.V;
+    int32_t* y = y_out + static_cast<long long>(b) * (G + 1);
+    const ReqState st = state[b];
+    if (st.n < 0) {
+        for (int i = tid; i <= G; i += kThreads) y[i] = -1;
         if (tid == 0) n_out[b] = -1;
         return;
     }
-    const int n = s_n;
-
+    const ReqRows q = request_rows(rs, b);
+    const int n = st.n;
     FinalRow fr;
-    if (n < q.ell) {
-        fr.lt = rs.Lt + (q.off + n) * V;
-        fr.ld = rs.Ld + (static_cast<long long>(b) * G + n) * V;
-        fr.lse_t = lse_t[static_cast<long long>(b) * (G + 1) + n];
-        fr.lse_d = lse_d[static_cast<long long>(b) * G + n];
-        fr.residual = 1;
-    } else {
-        fr.lt = rs.Lt + (q.off + q.ell) * V;
-        fr.ld = nullptr;
-        fr.lse_t = lse_t[static_cast<long long>(b) * (G + 1) + q.ell];
-        fr.lse_d = 0.0f;
-        fr.residual = 0;
-    }
+    fr.lt = rs.Lt + (q.off + n) * V;
+    fr.lse_t = st.lse_t;
+    fr.residual = st.residual;
+    fr.ld = fr.residual ? rs.Ld + (static_cast<long long>(b) * G + n) * V : nullptr;
+    fr.lse_d = st.lse_d;
+    float* cs = csum + static_cast<long long>(b) * nch;
     const float uf = clamp_uniform(u_fin[b]);
-    float* cs = chunk_ws + static_cast<long long>(b) * nchunk;
 
     for (int pass = 0; pass < 2; ++pass) {
-        for (int c = 0; c < nchunk; ++c) {
-            float w[4];
-            weights4<VEC4>(fr, static_cast<long long>(c) * kChunk + tid * kFinPerThread, V, w);
-            const float s = block_sum<kFinThreads>((w[0] + w[1]) + (w[2] + w[3]), fscr);
-            if (tid == 0) cs[c] = s;
-        }
-        if (tid == 0) {
+        // chunk totals in chunk order by one wave: lane-strided sums then a butterfly give the
+        // total; the search walks the chunks in order with per-lane running sums
+        if (tid < kWave) {
             float tot = 0.0f;
-            for (int c = 0; c < nchunk; ++c) tot += cs[c];
+            for (int i = tid; i < nch; i += kWave) tot += cs[i];
+            tot = wave_sum(tot);
             const float target = uf * tot;
             int found = -1;
-            float tprime = INFINITY;
-            if (tot > 0.0f) {
-                float run = 0.0f;
-                for (int c = 0; c < nchunk; ++c) {
-                    const float nr = run + cs[c];
-                    if (cs[c] > 0.0f && nr > target) {
-                        found = c;
-                        tprime = target - run;
-                        break;
-                    }
-                    run = nr;
+            float tprime = INFINITY, run = 0.0f;
+            for (int base = 0; base < nch && found < 0; base += kWave) {
+                const int i = base + tid;
+                const float v = (i < nch) ? cs[i] : 0.0f;
+                const float incl = wave_incl_scan(v);
+                float excl = __shfl_up(incl, 1, kWave);
+                if (tid == 0) excl = 0.0f;
+                const unsigned long long hit =
+                    __ballot((i < nch) && (v > 0.0f) && (run + incl > target));
+                if (hit) {
+                    const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                    found = base + f;
+                    tprime = target - (run + __shfl(excl, f, kWave));
                 }
-                if (found < 0)       // rounding left the target past the end
-                    for (int c = nchunk - 1; c >= 0; --c)
-                        if (cs[c] > 0.0f) { found = c; break; }
+                run += __shfl(incl, kWave - 1, kWave);
             }
-            s_found = found;
-            s_tprime = tprime;
-            s_total = tot;
+            if (found < 0 && tot > 0.0f) {      // rounding left the target past the end
+                int last = -1;
+                for (int i = tid; i < nch; i += kWave)
+                    if (cs[i] > 0.0f) last = i;
+                found = wave_max_int(last);
+                tprime = INFINITY;
+            }
+            if (tid == 0) {
+                s_found = found;
+                s_tprime = tprime;
+                s_total = tot;
+            }
         }
         __syncthreads();
         if (s_total > 0.0f || !fr.residual) break;
-        fr.residual = 0;           // residual mass rounded to zero: draw from p_t instead
+        // residual mass rounded to zero: draw from p_t of the same target row instead
+        fr.residual = 0;
+        for (int i = 0; i < nch; ++i) {
+            const float s = block_sum<kThreads>(chunk_mass<VEC4>(fr, i, V), fscr);
+            if (tid == 0) cs[i] = s;
+        }
         __syncthreads();
     }
 
     int z = -1;
     const int found = s_found;
     if (found >= 0) {
-        const long long v0 = static_cast<long long>(found) * kChunk + tid * kFinPerThread;
-        float w[4];
-        weights4<VEC4>(fr, v0, V, w);
+        float t[kPer], d[kPer];
+        load_chunk_contig<VEC4>(fr.lt, found, V, t);
+        if (fr.residual) load_chunk_contig<VEC4>(fr.ld, found, V, d);
+        float w[kPer];
+        float local = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            w[e] = fr.weight(t[e], fr.residual ? d[e] : 0.0f);
+            local += w[e];
+        }
         float tot;
-        const float ex = block_excl_scan<kFinThreads>((w[0] + w[1]) + (w[2] + w[3]), fscr, &tot);
+        const float ex = block_excl_scan<kThreads>(local, fscr, &tot);
         const float tprime = s_tprime;
+        const long long v0 =
+            static_cast<long long>(found) * kChunk + static_cast<long long>(kPer) * tid;
         int hit = INT32_MAX, lastpos = -1;
         float run = ex;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < kPer; ++e) {
             run += w[e];
             if (w[e] > 0.0f) {
                 lastpos = static_cast<int>(v0 + e);
                 if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(v0 + e);
             }
         }
-        z = block_min_int<kFinThreads>(hit, iscr);
-        if (z == INT32_MAX) z = block_max_int<kFinThreads>(lastpos, iscr);
+        z = block_min_int<kThreads>(hit, iscr);
+        if (z == INT32_MAX) z = block_max_int<kThreads>(lastpos, iscr);
     }
-    for (int i = tid; i <= G; i += kFinThreads)
+    for (int i = tid; i <= G; i += kThreads)
         y[i] = (i < n) ? x[static_cast<long long>(b) * G + i] : (i == n ? z : -1);
     if (tid == 0) n_out[b] = n;
 }
 
+// ----------------------------------------------------------------------------- TV labels
+// lse_d / lse_t given, or merged here from row partials.
 template <bool VEC4>
-__global__ __launch_bounds__(kTvThreads)
-void tv_kernel(RowSet rs, const float* __restrict__ lse_d, const float* __restrict__ lse_t,
-               float* __restrict__ cstar) {
-    __shared__ float fscr[kTvThreads / kWave + 1];
+__global__ __launch_bounds__(kThreads)
+void tv_chunks_kernel(RowSet rs, int nch, const float* __restrict__ lse_d,
+                      const float* __restrict__ lse_t, const float2* __restrict__ part,
+                      float* __restrict__ psum) {
+    __shared__ float fscr[kWaves + 1];
+    __shared__ float s_lse[2];
     const int G = rs.gamma, V = rs.V, tid = threadIdx.x;
-    const int k = static_cast<int>(blockIdx.x % static_cast<unsigned>(G));
-    const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(G));
+    const int c = static_cast<int>(blockIdx.x % static_cast<unsigned>(nch));
+    const long long pair = blockIdx.x / static_cast<unsigned>(nch);          // b * G + k
+    const int k = static_cast<int>(pair % G);
+    const int b = static_cast<int>(pair / G);
     const ReqRows q = request_rows(rs, b);
-    float* out = cstar + static_cast<long long>(b) * G + k;
-    if (!q.ok || k >= q.ell) {
-        if (tid == 0) *out = __int_as_float(0x7fc00000);
-        return;
+    if (!q.ok || k >= q.ell) return;
+    if (tid < 2 * kWave) {
+        const int w = tid / kWave;   // 0: draft row k, 1: target row k
+        float v;
+        if (w == 0)
+            v = lse_d ? lse_d[pair] : merge_lse_wave(slot_part(part, b, G + 1 + k, G, nch), nch);
+        else
+            v = lse_t ? lse_t[static_cast<long long>(b) * (G + 1) + k]
+                      : merge_lse_wave(slot_part(part, b, k, G, nch), nch);
+        if ((tid & (kWave - 1)) == 0) s_lse[w] = v;
     }
-    const float a = lse_d[static_cast<long long>(b) * G + k];
-    const float c = lse_t[static_cast<long long>(b) * (G + 1) + k];
-    if (a == -INFINITY || c == -INFINITY) {     // a zero distribution shares no mass
-        if (tid == 0) *out = 0.0f;
-        return;
-    }
-    const float* ld = rs.Ld + (static_cast<long long>(b) * G + k) * V;
-    const float* lt = rs.Lt + (q.off + k) * V;
+    __syncthreads();
+    const float a = s_lse[0], cc = s_lse[1];
     float s = 0.0f;
-    if (VEC4) {
-        const float4* d4 = reinterpret_cast<const float4*>(ld);
-        const float4* t4 = reinterpret_cast<const float4*>(lt);
-        for (int i = tid; i < (V >> 2); i += kTvThreads) {
-            const float4 d = d4[i], t = t4[i];
-            s += (__expf(fminf(d.x - a, t.x - c)) + __expf(fminf(d.y - a, t.y - c))) +
-                 (__expf(fminf(d.z - a, t.z - c)) + __expf(fminf(d.w - a, t.w - c)));
-        }
-    } else {
-        for (int v = tid; v < V; v += kTvThreads) s += __expf(fminf(ld[v] - a, lt[v] - c));
+    if (a != -INFINITY && cc != -INFINITY) {     // a zero distribution shares no mass
+        float ld[kPer], lt[kPer];
+        load_chunk<VEC4>(rs.Ld + pair * V, c, V, ld);
+        load_chunk<VEC4>(rs.Lt + (q.off + k) * V, c, V, lt);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) s += __expf(fminf(ld[e] - a, lt[e] - cc));
     }
-    s = block_sum<kTvThreads>(s, fscr);
-    if (tid == 0) *out = s;
+    s = block_sum<kThreads>(s, fscr);
+    if (tid == 0) psum[pair * nch + c] = s;
+}
+
+__global__ __launch_bounds__(kThreads)
+void tv_merge_kernel(RowSet rs, int nch, const float* __restrict__ psum,
+                     float* __restrict__ cstar) {
+    const int G = rs.gamma;
+    const long long pair = static_cast<long long>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    if (pair >= static_cast<long long>(rs.B) * G) return;
+    const int k = static_cast<int>(pair % G);
+    const int b = static_cast<int>(pair / G);
+    const ReqRows q = request_rows(rs, b);
+    const int lane = threadIdx.x & (kWave - 1);
+    float s = 0.0f;
+    const bool live = q.ok && k < q.ell;
+    if (live)
+        for (int i = lane; i < nch; i += kWave) s += psum[pair * nch + i];
+    s = wave_sum(s);
+    if (lane == 0) cstar[pair] = live ? s : qnan();
 }
 
 }  // namespace
 
 int verify_chunk_elems() { return kChunk; }
+size_t verify_state_bytes() { return sizeof(ReqState); }
 
 static bool rows_vec4(const RowSet& rs) {
     return (rs.V % 4) == 0 && (reinterpret_cast<uintptr_t>(rs.Ld) % 16) == 0 &&
            (reinterpret_cast<uintptr_t>(rs.Lt) % 16) == 0;
 }
 
-hipError_t launch_row_lse(const RowSet& rs, const float* lse_d_in, float* lse_d, float* lse_t,
-                          hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(2 * rs.gamma + 1) * rs.B);
-    if (rows_vec4(rs))
-        hipLaunchKernelGGL(row_lse_kernel<true>, grid, dim3(kLseThreads), 0, st, rs, lse_d_in,
-                           lse_d, lse_t);
-    else
-        hipLaunchKernelGGL(row_lse_kernel<false>, grid, dim3(kLseThreads), 0, st, rs, lse_d_in,
-                           lse_d, lse_t);
+static int nchunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+#define DSPARK_LAUNCH_VEC4(kernel, grid, ...)                                              \
+    do {                                                                                    \
+        if (rows_vec4(rs))                                                                  \
+            hipLaunchKernelGGL(kernel<true>, grid, dim3(kThreads), 0, st, __VA_ARGS__);     \
+        else                                                                                \
+            hipLaunchKernelGGL(kernel<false>, grid, dim3(kThreads), 0, st, __VA_ARGS__);    \
+    } while (0)
+
+hipError_t launch_row_stats(const RowSet& rs, const float* lse_d_in, float2* part,
+                            hipStream_t st) {
+    const int nch = nchunks(rs.V);
+    const dim3 grid(static_cast<unsigned>(nch) * (2 * rs.gamma + 1) * rs.B);
+    DSPARK_LAUNCH_VEC4(row_stats_kernel, grid, rs, nch, lse_d_in, part);
     return hipGetLastError();
 }
 
-hipError_t launch_verify_finish(const RowSet& rs, const int32_t* x, const float* lse_d,
-                                const float* lse_t, const float* u_acc, const float* u_fin,
-                                float* chunk_ws, int nchunk, int32_t* n_out, int32_t* y_out,
-                                hipStream_t st) {
-    if (rows_vec4(rs))
-        hipLaunchKernelGGL(verify_finish_kernel<true>, dim3(rs.B), dim3(kFinThreads), 0, st, rs, x,
-                           lse_d, lse_t, u_acc, u_fin, chunk_ws, nchunk, n_out, y_out);
-    else
-        hipLaunchKernelGGL(verify_finish_kernel<false>, dim3(rs.B), dim3(kFinThreads), 0, st, rs, x,
-                           lse_d, lse_t, u_acc, u_fin, chunk_ws, nchunk, n_out, y_out);
+hipError_t launch_verify(const RowSet& rs, const int32_t* x, const float2* part,
+                         const float* lse_d_in, const float* u_acc, const float* u_fin,
+                         float* lse_d_out, float* lse_t_out, float* csum, void* state,
+                         int32_t* n_out, int32_t* y_out, hipStream_t st) {
+    const int nch = nchunks(rs.V);
+    ReqState* rstate = static_cast<ReqState*>(state);
+    DSPARK_LAUNCH_VEC4(verify_chunks_kernel, dim3(static_cast<unsigned>(nch) * rs.B), rs, nch, x,
+                       part, lse_d_in, u_acc, lse_d_out, lse_t_out, csum, rstate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DSPARK_LAUNCH_VEC4(verify_select_kernel, dim3(rs.B), rs, nch, x, u_fin, csum, rstate, n_out,
+                       y_out);
     return hipGetLastError();
 }
 
-hipError_t launch_tv(const RowSet& rs, const float* lse_d, const float* lse_t, float* cstar,
-                     hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(rs.gamma) * rs.B);
-    if (rows_vec4(rs))
-        hipLaunchKernelGGL(tv_kernel<true>, grid, dim3(kTvThreads), 0, st, rs, lse_d, lse_t, cstar);
-    else
-        hipLaunchKernelGGL(tv_kernel<false>, grid, dim3(kTvThreads), 0, st, rs, lse_d, lse_t, cstar);
+hipError_t launch_tv(const RowSet& rs, const float* lse_d, const float* lse_t,
+                     const float2* part, float* psum, float* cstar, hipStream_t st) {
+    const int nch = nchunks(rs.V);
+    DSPARK_LAUNCH_VEC4(tv_chunks_kernel, dim3(static_cast<unsigned>(nch) * rs.gamma * rs.B), rs,
+                       nch, lse_d, lse_t, part, psum);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long pairs = static_cast<long long>(rs.B) * rs.gamma;
+    hipLaunchKernelGGL(tv_merge_kernel, dim3(static_cast<unsigned>((pairs + kWaves - 1) / kWaves)),
+                       dim3(kThreads), 0, st, rs, nch, psum, cstar);
     return hipGetLastError();
 }
+
+#undef DSPARK_LAUNCH_VEC4
 
 }  // namespace dspark

@@ -13,9 +13,9 @@
  * Memory     Every array argument is DEVICE memory owned by the caller, row-major with the
  *            last dimension contiguous. The library allocates nothing: scratch comes from
  *            the caller's workspace `ws` of at least `dspark_*_workspace_bytes(...)` bytes
- *            (256-byte aligned, as the HIP allocator returns). A workspace must be
- *            zero-filled once before its first use; every call leaves it reusable, so one
- *            workspace serves any later call whose size it covers (not concurrent ones).
+ *            (256-byte aligned, as the HIP allocator returns). Its contents need no
+ *            preparation; a call owns it until the call's work on `stream` has finished, so
+ *            calls that may overlap need distinct workspaces.
  * Streams    `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work and
  *            return without synchronising. Calls on distinct workspaces may run concurrently;
  *            the library keeps no mutable global state.
@@ -165,7 +165,8 @@ int dspark_tv_labels(int B, int V, int gamma,
  *   K_out     [1]       int32 total verify tokens R + n* (nullable)
  *   theta_out [1]       fp32 Theta(n*) (nullable)
  *   a_out   [R][gamma]  fp32 prefix survival (nullable)
- * Runs as one workgroup; the ranking key keeps 32 mantissa bits of each fp64 a.
+ * Runs as one workgroup; the ranking key keeps 32 mantissa bits of each fp64 a. The
+ * workspace holds the fp64 prefix products (R * gamma * 8 bytes).
  */
 size_t dspark_schedule_workspace_bytes(int R, int gamma, int Bmax);
 int dspark_schedule(int R, int gamma, const float* conf, const float* temp,

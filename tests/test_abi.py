@@ -56,7 +56,7 @@ def test_workspace_sizes(lib):
     assert lib.dspark_markov_draft_workspace_bytes(0, V, r, G) == 0
     assert lib.dspark_verify_workspace_bytes(256, V, 16) >= 256 * 33 * 4
     assert lib.dspark_tv_labels_workspace_bytes(256, V, 16) >= 256 * 33 * 4
-    assert lib.dspark_schedule_workspace_bytes(512, 16, 4096) == 0
+    assert lib.dspark_schedule_workspace_bytes(512, 16, 4096) >= 512 * 16 * 8
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
@@ -129,15 +129,17 @@ def test_tv_rejects(lib):
 def test_schedule_rejects(lib, args, status):
     R, G, Bmax, mode = args
     assert lib.dspark_schedule(R, G, FAKE, None, FAKE, Bmax, mode, FAKE, None, None, None, None,
-                               None, 0, None) == status
+                               FAKE, 1 << 30, None) == status
 
 
 @cpu_only
 def test_schedule_null_required(lib):
-    assert lib.dspark_schedule(4, 4, None, None, FAKE, 40, 0, FAKE, None, None, None, None, None,
-                               0, None) == binding.ERR_INVALID_ARG
-    assert lib.dspark_schedule(4, 4, FAKE, None, FAKE, 40, 0, None, None, None, None, None, None,
-                               0, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_schedule(4, 4, None, None, FAKE, 40, 0, FAKE, None, None, None, None, FAKE,
+                               1 << 30, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_schedule(4, 4, FAKE, None, FAKE, 40, 0, None, None, None, None, None, FAKE,
+                               1 << 30, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_schedule(4, 4, FAKE, None, FAKE, 40, 0, FAKE, None, None, None, None, FAKE,
+                               8, None) == binding.ERR_WORKSPACE
 
 
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):

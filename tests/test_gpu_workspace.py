@@ -1,0 +1,59 @@
+"""Workspaces need no preparation: every entry point gives oracle-matching results when its
+workspace holds arbitrary bytes left by earlier calls of other shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import draft_sampling_verification_head_amd as dspark
+from draft_sampling_verification_head_amd import binding
+from parity import check_draft, check_verify, dev, host, PROB_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _poison(tag, nbytes, seed):
+    buf = binding.workspace(nbytes, torch.device("cuda:0"), tag)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    buf.copy_(torch.randint(0, 256, (buf.numel(),), dtype=torch.uint8, device="cuda", generator=g))
+    torch.cuda.synchronize()
+
+
+def test_poisoned_workspaces(gpu):
+    lib = binding.load()
+    for seed, (B, V, G) in enumerate([(3, 9000, 3), (6, 20000, 5), (2, 8192, 2)]):
+        c = synth.custom(980 + seed, B=B, V=V, r=16, gamma=G, w_dtype="bf16", tnoise=0.7)
+        d = synth.draft_inputs(c)
+        _poison("draft", lib.dspark_markov_draft_workspace_bytes(B, V, 16, G) + 4096, seed)
+        out = dspark.markov_draft(dev(d["U"]), dev(d["W1"]), dev(d["W2"]), dev(d["x0"]),
+                                  dev(d["u"]), want_logits=True)
+        g = {k: host(v) for k, v in out.items()}
+        check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
+                    range(B), gL=g["L"])
+
+        Ld = synth.draft_logits_all(c)
+        Lt_pad = synth.target_padded_all(c)
+        lengths = np.array([(b * 7 + seed) % (G + 1) for b in range(B)], np.int32)
+        t_off = np.concatenate([[0], np.cumsum(lengths + 1)]).astype(np.int32)
+        Lt = np.concatenate([Lt_pad[b, : lengths[b] + 1] for b in range(B)])
+        x = np.array([[oracle.inverse_cdf(oracle.softmax_row(Ld[b, k])[0], 0.37) for k in range(G)]
+                      for b in range(B)], np.int32)
+        u_acc, u_fin = synth.verify_uniforms(c)
+        _poison("verify", lib.dspark_verify_workspace_bytes(B, V, G) + 4096, seed + 10)
+        v = dspark.verify(dev(Ld), dev(Lt), dev(x), dev(u_acc), dev(u_fin), t_off=dev(t_off),
+                          length=dev(lengths))
+        check_verify(Ld, Lt, x, u_acc, u_fin, t_off, lengths, host(v["n"]), host(v["y"]), range(B))
+        _poison("tv", lib.dspark_tv_labels_workspace_bytes(B, V, G) + 4096, seed + 20)
+        cs = host(dspark.tv_labels(dev(Ld), dev(Lt), t_off=dev(t_off), length=dev(lengths)))
+        ref = oracle.tv_labels(Ld, Lt, t_off=t_off, length=lengths)
+        fin = np.isfinite(ref)
+        assert np.array_equal(fin, np.isfinite(cs))
+        assert np.max(np.abs(cs[fin] - ref[fin]), initial=0.0) < PROB_TOL
+
+        conf = synth.confidences(c)
+        sps = synth.sps_table(64, b=1e-3)
+        _poison("schedule", lib.dspark_schedule_workspace_bytes(B, G, 64) + 4096, seed + 30)
+        s = dspark.schedule(dev(conf), dev(sps), 64, temp=dev(synth.temperatures(G)))
+        ref = oracle.schedule(conf, synth.temperatures(G), sps, 64)
+        assert np.array_equal(host(s["len"]), ref["len"])
