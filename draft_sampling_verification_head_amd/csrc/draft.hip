@@ -15,7 +15,8 @@
 //             the tile's W2 columns once for the whole group, adds U_k and writes the logits
 //             row segment and the tile's (max, sum exp(l - max)) partial. Each lane owns 8
 //             consecutive columns (one 16-byte bf16 load per W2 row); the 16 waves split the
-//             rank with 8 rows of loads in flight each. Step 0 takes x_0 from the caller.
+//             rank with 4 rows of loads in flight each, and waves that do not draw start their
+//             first rows before the draw. Step 0 takes x_0 from the caller.
 //   select  - draws x_{gamma-1} from the last step's partials, one wave per request.
 // The draw: (m, Z) merged from the partials in tile order, lse = m + log Z, the first tile
 // whose running mass exceeds u * Z, then the first column of that tile whose running mass
@@ -238,53 +239,6 @@ __device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
     return rescan_tile_wave(V, row, found, m, lse, tprime, o);
 }
 
-// ----------------------------------------------------------------------------- block draw
-// The same draw spread over a whole 1024-thread workgroup (one request per workgroup):
-// thread i holds tile i (nblk <= 1024), then column i of the chosen tile. Returns the token
-// in every thread.
-__device__ int draw_block(int V, const float2* __restrict__ P, int nblk,
-                          const float* __restrict__ row, float u, const DrawOut& o,
-                          float* fscr, int* iscr, float* s_before, int* s_tok) {
-    const int tid = threadIdx.x;
-    const float2 p = (tid < nblk) ? P[tid] : make_float2(-INFINITY, 0.0f);
-    const float m = block_max<kSweepThreads>(p.x, fscr);
-    if (m == -INFINITY) {
-        if (o.write && tid == 0) put(o, -1, 0.0f, -INFINITY);
-        return -1;
-    }
-    const float mass = tile_mass(p, m);
-    float Z;
-    const float ex = block_excl_scan<kSweepThreads>(mass, fscr, &Z);
-    const float lse = m + __logf(Z);
-    const float target = clamp_uniform(u) * Z;
-    int found = block_min_int<kSweepThreads>(
-        (tid < nblk && mass > 0.0f && ex + mass > target) ? tid : INT32_MAX, iscr);
-    float tprime = INFINITY;
-    if (found == INT32_MAX) {
-        found = block_max_int<kSweepThreads>((tid < nblk && mass > 0.0f) ? tid : -1, iscr);
-    } else {
-        if (tid == found) *s_before = ex;
-        __syncthreads();
-        tprime = target - *s_before;
-    }
-    // rescan: thread t < 512 owns column t of the tile
-    const long long c = static_cast<long long>(found) * kTileCols + tid;
-    const bool mine = tid < kTileCols && c < V;
-    const float l = mine ? row[c] : -INFINITY;
-    const float e = (l == -INFINITY) ? 0.0f : __expf(l - m);
-    float tot;
-    const float ex2 = block_excl_scan<kSweepThreads>(e, fscr, &tot);
-    int tok = block_min_int<kSweepThreads>(
-        (e > 0.0f && ex2 + e > tprime) ? static_cast<int>(c) : INT32_MAX, iscr);
-    if (tok == INT32_MAX)
-        tok = block_max_int<kSweepThreads>(e > 0.0f ? static_cast<int>(c) : -1, iscr);
-    if (static_cast<long long>(tok) == c && mine) {
-        *s_tok = tok;
-        if (o.write) put(o, tok, __expf(l - lse), lse);
-    }
-    return tok;
-}
-
 // ----------------------------------------------------------------------------- step kernel
 struct StepArgs {
     int B, V, r, gamma, k, nblk;
@@ -304,15 +258,15 @@ struct StepArgs {
 };
 
 template <typename WT, int BT, bool VEC>
-__global__ __launch_bounds__(kSweepThreads, (BT <= 2 ? 8 : 4))
+__global__ __launch_bounds__(kSweepThreads, (BT == 1 ? 8 : (BT == 2 ? 6 : 4)))
 void draft_step_gemv(StepArgs a) {
-    constexpr int RB = !VEC ? 2 : (sizeof(WT) == 2 ? 8 : 4);   // W2 rows in flight per wave
+    // 16 bytes per lane and 4 bf16 rows in flight per wave keep a single request's kernel at
+    // 64 VGPRs, so two 16-wave workgroups fit per CU and every tile is resident at once.
+    constexpr int RB = (!VEC || sizeof(WT) == 4) ? 2 : 4;
     extern __shared__ float smem[];
     float* h = smem;                       // [BT][r] gathered W1 rows
     float* red = smem + BT * a.r;          // [kSweepWaves][kTileCols] cross-wave partials
     __shared__ float scratch[kSweepWaves + 1];
-    __shared__ int iscr[kSweepWaves + 1];
-    __shared__ float s_before;
     __shared__ int tok[BT];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -323,7 +277,26 @@ void draft_step_gemv(StepArgs a) {
     const WT* W1 = static_cast<const WT*>(a.W1);
     const WT* W2 = static_cast<const WT*>(a.W2);
 
-    // 1. previous token of every request in the group
+    // lane owns 8 consecutive columns; wave w owns rank rows [jb, je)
+    const long long col0 = static_cast<long long>(blk) * kTileCols + lane * kColsPerLane;
+    const long long avail = static_cast<long long>(V) - col0;
+    const int rpw = (r + kSweepWaves - 1) / kSweepWaves;
+    const int jb = wave * rpw, je = min(r, jb + rpw);
+    const WT* wp = W2 + col0;
+    Seg<WT> seg[RB];
+    const bool streams = avail > 0 && jb < je;
+
+    // 1. previous token of every request in the group. Waves that do not draw issue their
+    //    first W2 rows meanwhile (W2 does not depend on the token).
+    const bool drawing = a.k > 0 && wave < BT;
+    const bool preloaded = !drawing && streams;
+    if (preloaded) {
+#pragma unroll
+        for (int t = 0; t < RB; ++t) {
+            const long long j = min(jb + t, je - 1);
+            if (VEC) seg[t].load(wp + j * V); else seg[t].load_guarded(wp + j * V, avail);
+        }
+    }
     if (a.k == 0) {
         if (tid < BT) {
             const int b = b0 + tid;
@@ -334,19 +307,7 @@ void draft_step_gemv(StepArgs a) {
             }
             tok[tid] = t;
         }
-    } else if (BT == 1) {
-        if (b0 < a.B) {
-            const long long o = static_cast<long long>(b0) * a.gamma + (a.k - 1);
-            const DrawOut out{a.x_out + o, a.q_out ? a.q_out + o : nullptr,
-                              a.lse_out ? a.lse_out + o : nullptr, blk == 0};
-            const int t = draw_block(V, a.part_prev + static_cast<long long>(b0) * a.nblk, a.nblk,
-                                     a.Lprev + b0 * a.L_bstride, a.u[o], out, scratch, iscr,
-                                     &s_before, &tok[0]);
-            if (t < 0 && tid == 0) tok[0] = -1;
-        } else if (tid == 0) {
-            tok[0] = -1;
-        }
-    } else if (wave < BT) {
+    } else if (drawing) {
         const int b = b0 + wave;
         int t = -1;
         if (b < a.B) {
@@ -376,27 +337,20 @@ void draft_step_gemv(StepArgs a) {
     }
     __syncthreads();
 
-    // 2. projection: lane owns 8 consecutive columns; wave w owns rank rows [jb, je)
-    const long long col0 = static_cast<long long>(blk) * kTileCols + lane * kColsPerLane;
-    const long long avail = static_cast<long long>(V) - col0;
-    const int rpw = (r + kSweepWaves - 1) / kSweepWaves;
-    const int jb = wave * rpw, je = min(r, jb + rpw);
+    // 2. projection, fp32 accumulation in row order
     float acc[BT][kColsPerLane];
 #pragma unroll
     for (int bi = 0; bi < BT; ++bi)
 #pragma unroll
         for (int e = 0; e < kColsPerLane; ++e) acc[bi][e] = 0.0f;
-    if (avail > 0 && jb < je) {
-        const WT* wp = W2 + col0;
+    if (streams) {
         for (int j0 = jb; j0 < je; j0 += RB) {
-            Seg<WT> seg[RB];
+            if (!(preloaded && j0 == jb)) {
 #pragma unroll
-            for (int t = 0; t < RB; ++t) {
-                const long long j = min(j0 + t, je - 1);     // clamped: always a valid row
-                if (VEC)
-                    seg[t].load(wp + j * V);
-                else
-                    seg[t].load_guarded(wp + j * V, avail);
+                for (int t = 0; t < RB; ++t) {
+                    const long long j = min(j0 + t, je - 1);     // clamped: always a valid row
+                    if (VEC) seg[t].load(wp + j * V); else seg[t].load_guarded(wp + j * V, avail);
+                }
             }
 #pragma unroll
             for (int t = 0; t < RB; ++t) {
