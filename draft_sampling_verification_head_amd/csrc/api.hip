@@ -61,7 +61,7 @@ int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b
 
 // sizes of the draft workspace regions
 size_t draft_part_count(int B, int V) {
-    return static_cast<size_t>(B) * ceil_div(V, dspark::draft_tile_cols());
+    return static_cast<size_t>(B) * dspark::draft_part_tiles(V);
 }
 
 }  // namespace
@@ -113,7 +113,6 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
     Carver c(ws);
     dspark::DraftCall dc;
     dc.B = B; dc.V = V; dc.r = r; dc.gamma = gamma; dc.w_dtype = w_dtype;
-    dc.nblk = ceil_div(V, dspark::draft_tile_cols());
     dc.U = U; dc.W1 = W1; dc.W2 = W2; dc.x0 = x0; dc.u = u;
     dc.x_out = x_out; dc.q_out = q_out; dc.lse_out = lse_out;
     dc.part[0] = c.take<float2>(draft_part_count(B, V));

@@ -24,6 +24,7 @@
 // that leaves the point past the end falls back to the last positive column. Results cross
 // workgroups only at kernel boundaries, so no workgroup needs a device-scope fence.
 #include "common.h"
+#include "draw.h"
 #include "kernels.h"
 
 namespace dspark {
@@ -36,8 +37,6 @@ constexpr int kColsPerLane = 8;
 constexpr int kTileCols = kWave * kColsPerLane;    // 512 vocabulary columns per tile
 static_assert(kTileCols * 2 == kSweepThreads, "epilogue: one column per thread of the first half");
 
-constexpr int kSelThreads = 256;                   // 4 requests per workgroup, one per wave
-constexpr int kSelRegTiles = 8;                    // tiles per lane kept in registers
 
 // Eight consecutive factor elements of one W2 row.
 template <typename WT>
@@ -83,161 +82,6 @@ struct Seg<float> {
         o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
     }
 };
-
-__device__ __forceinline__ float tile_mass(float2 p, float m) {
-    return (p.x == -INFINITY) ? 0.0f : p.y * __expf(p.x - m);
-}
-
-// Where a draw writes its results (nothing when `write` is false).
-struct DrawOut {
-    int32_t* x;
-    float* q;
-    float* lse;
-    bool write;
-};
-
-__device__ __forceinline__ void put(const DrawOut& o, int tok, float q, float lse) {
-    *o.x = tok;
-    if (o.q) *o.q = q;
-    if (o.lse) *o.lse = lse;
-}
-
-// ----------------------------------------------------------------------------- wave draw
-// In-tile rescan: lane owns 8 consecutive columns of `tile`.
-__device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__ row, int tile,
-                                                float m, float lse, float tprime,
-                                                const DrawOut& o) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const long long c0 = static_cast<long long>(tile) * kTileCols + lane * kColsPerLane;
-    float lv[kColsPerLane], e[kColsPerLane];
-    float local = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kColsPerLane; ++j) lv[j] = (c0 + j < V) ? row[c0 + j] : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kColsPerLane; ++j) {
-        e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
-        local += e[j];
-    }
-    const float incl = wave_incl_scan(local);
-    float run = __shfl_up(incl, 1, kWave);
-    if (lane == 0) run = 0.0f;
-    int hit = INT32_MAX, lastpos = -1;
-#pragma unroll
-    for (int j = 0; j < kColsPerLane; ++j) {
-        run += e[j];
-        if (e[j] > 0.0f) {
-            lastpos = static_cast<int>(c0 + j);
-            if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(c0 + j);
-        }
-    }
-    int tok = wave_min_int(hit);
-    if (tok == INT32_MAX) tok = wave_max_int(lastpos);
-    const int rel = tok - tile * kTileCols;
-    const int owner = rel / kColsPerLane, jj = rel - owner * kColsPerLane;
-    float mine = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kColsPerLane; ++j)
-        if (j == jj) mine = lv[j];
-    const float lx = __shfl(mine, owner, kWave);
-    if (o.write && lane == 0) put(o, tok, __expf(lx - lse), lse);
-    return tok;
-}
-
-// One wave draws one request's token; returns it (-1 for a dead request) in every lane.
-__device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
-                         const float* __restrict__ row, float u, const DrawOut& o) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float m = -INFINITY;
-    float Z, lse, target;
-    int found = -1;
-    float tprime = INFINITY;
-    if (nblk <= kWave * kSelRegTiles) {
-        // register form: lane l holds tiles [8l, 8l + 8)
-        float2 p[kSelRegTiles];
-#pragma unroll
-        for (int t = 0; t < kSelRegTiles; ++t) {
-            const int i = lane * kSelRegTiles + t;
-            p[t] = (i < nblk) ? P[i] : make_float2(-INFINITY, 0.0f);
-        }
-#pragma unroll
-        for (int t = 0; t < kSelRegTiles; ++t) m = fmaxf(m, p[t].x);
-        m = wave_max(m);
-        if (m == -INFINITY) {
-            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
-            return -1;
-        }
-        float mass[kSelRegTiles];
-        float local = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kSelRegTiles; ++t) {
-            mass[t] = tile_mass(p[t], m);
-            local += mass[t];
-        }
-        Z = wave_sum(local);
-        lse = m + __logf(Z);
-        target = clamp_uniform(u) * Z;
-        const float incl = wave_incl_scan(local);
-        float run = __shfl_up(incl, 1, kWave);
-        if (lane == 0) run = 0.0f;
-        int hit = INT32_MAX, last = -1;
-        float before = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kSelRegTiles; ++t) {
-            const float nr = run + mass[t];
-            if (mass[t] > 0.0f) {
-                last = lane * kSelRegTiles + t;
-                if (hit == INT32_MAX && nr > target) {
-                    hit = lane * kSelRegTiles + t;
-                    before = run;
-                }
-            }
-            run = nr;
-        }
-        found = wave_min_int(hit);
-        if (found == INT32_MAX) {
-            found = wave_max_int(last);
-        } else {
-            tprime = target - __shfl(before, found / kSelRegTiles, kWave);
-        }
-    } else {
-        // loop form for vocabularies with more than 512 tiles
-        for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, P[i].x);
-        m = wave_max(m);
-        if (m == -INFINITY) {
-            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
-            return -1;
-        }
-        float z = 0.0f;
-        for (int i = lane; i < nblk; i += kWave) z += tile_mass(P[i], m);
-        Z = wave_sum(z);
-        lse = m + __logf(Z);
-        target = clamp_uniform(u) * Z;
-        float run = 0.0f;
-        for (int base = 0; base < nblk; base += kWave) {
-            const int i = base + lane;
-            const float v = (i < nblk) ? tile_mass(P[i], m) : 0.0f;
-            const float incl = wave_incl_scan(v);
-            float excl = __shfl_up(incl, 1, kWave);
-            if (lane == 0) excl = 0.0f;
-            const unsigned long long hit =
-                __ballot((i < nblk) && (v > 0.0f) && (run + incl > target));
-            if (hit) {
-                const int f = __ffsll(static_cast<long long>(hit)) - 1;
-                found = base + f;
-                tprime = target - (run + __shfl(excl, f, kWave));
-                break;
-            }
-            run += __shfl(incl, kWave - 1, kWave);
-        }
-        if (found < 0) {
-            int last = -1;
-            for (int i = lane; i < nblk; i += kWave)
-                if (tile_mass(P[i], m) > 0.0f) last = i;
-            found = wave_max_int(last);
-        }
-    }
-    return rescan_tile_wave(V, row, found, m, lse, tprime, o);
-}
 
 // ----------------------------------------------------------------------------- step kernel
 struct StepArgs {
@@ -314,7 +158,7 @@ void draft_step_gemv(StepArgs a) {
             const long long o = static_cast<long long>(b) * a.gamma + (a.k - 1);
             const DrawOut out{a.x_out + o, a.q_out ? a.q_out + o : nullptr,
                               a.lse_out ? a.lse_out + o : nullptr, blk == 0};
-            t = draw_wave(V, a.part_prev + static_cast<long long>(b) * a.nblk, a.nblk,
+            t = draw_wave<kTileCols>(V, a.part_prev + static_cast<long long>(b) * a.nblk, a.nblk,
                           a.Lprev + b * a.L_bstride, a.u[o], out);
         }
         if (lane == 0) tok[wave] = t;
@@ -392,20 +236,6 @@ void draft_step_gemv(StepArgs a) {
     }
 }
 
-// Draw of the last position: one wave per request.
-__global__ __launch_bounds__(kSelThreads)
-void draft_select(int B, int V, int gamma, int k, const float2* __restrict__ part, int nblk,
-                  const float* __restrict__ L, long long L_bstride, const float* __restrict__ u,
-                  int32_t* __restrict__ x_out, float* __restrict__ q_out,
-                  float* __restrict__ lse_out) {
-    const int b = blockIdx.x * (kSelThreads / kWave) + threadIdx.x / kWave;
-    if (b >= B) return;
-    const long long o = static_cast<long long>(b) * gamma + k;
-    const DrawOut out{x_out + o, q_out ? q_out + o : nullptr, lse_out ? lse_out + o : nullptr,
-                      true};
-    draw_wave(V, part + static_cast<long long>(b) * nblk, nblk, L + b * L_bstride, u[o], out);
-}
-
 template <typename WT, int BT>
 hipError_t launch_step_bt(const StepArgs& a, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(a.nblk) * ((a.B + BT - 1) / BT));   // 1-D: tile fastest
@@ -428,11 +258,15 @@ hipError_t launch_step_w(const StepArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int draft_tile_cols() { return kTileCols; }
+int draft_part_tiles(int V) {
+    const int t = kTileCols < draft_mfma_tile_cols() ? kTileCols : draft_mfma_tile_cols();
+    return (V + t - 1) / t;
+}
 
 hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
+    if (draft_mfma_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2)) return launch_draft_mfma(c, st);
     StepArgs a;
-    a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma; a.nblk = c.nblk;
+    a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma; a.nblk = (c.V + kTileCols - 1) / kTileCols;
     a.U = c.U; a.W1 = c.W1; a.W2 = c.W2; a.x0 = c.x0; a.u = c.u;
     a.x_out = c.x_out; a.q_out = c.q_out; a.lse_out = c.lse_out;
     a.L_bstride = c.L_bstride;
@@ -448,8 +282,8 @@ hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
     }
     const int k = c.gamma - 1;
     const int waves = kSelThreads / kWave;
-    hipLaunchKernelGGL(draft_select, dim3((c.B + waves - 1) / waves), dim3(kSelThreads), 0, st,
-                       c.B, c.V, c.gamma, k, static_cast<const float2*>(c.part[k & 1]), c.nblk,
+    hipLaunchKernelGGL(draft_select<kTileCols>, dim3((c.B + waves - 1) / waves), dim3(kSelThreads), 0, st,
+                       c.B, c.V, c.gamma, k, static_cast<const float2*>(c.part[k & 1]), a.nblk,
                        c.L[k], c.L_bstride, c.u, c.x_out, c.q_out, c.lse_out);
     return hipGetLastError();
 }

@@ -1,0 +1,199 @@
+// Inverse-CDF draw from vocabulary-tile partials, shared by the draft kernels.
+//
+// [P3] "DSpark Speculative Decoding", section "Semi-Autoregressive Generation": x_k is a sample
+// of softmax(U_k + B_k). With one host uniform u per draw the sample is the inverse CDF taken
+// in token order, x = min { v : F(v) > u }. A step kernel leaves, per request and vocabulary
+// tile of TC columns, the tile's (max, sum exp(l - max)) and the logits row itself; a draw
+// merges the partials in tile order into (m, Z), lse = m + log Z, finds the first tile whose
+// running mass exceeds u * Z and rescans that tile's logits in token order. Rounding that
+// leaves the point past the end takes the last column with positive mass.
+// ([P3] = the concept note "DSpark Speculative Decoding".)
+#pragma once
+
+#include "common.h"
+
+namespace dspark {
+
+constexpr int kSelThreads = 256;      // draw kernels: 4 requests per workgroup, one per wave
+
+// Tile partials per lane a draw keeps in registers: enough for a 2^18-token vocabulary at
+// either tile width (512 tiles of 512 columns, 1024 tiles of 256 columns).
+template <int TC>
+struct RegTiles {
+    static constexpr int value = TC >= 512 ? 8 : 16;
+};
+
+__device__ __forceinline__ float tile_mass(float2 p, float m) {
+    return (p.x == -INFINITY) ? 0.0f : p.y * __expf(p.x - m);
+}
+
+// Where a draw writes its results (nothing when `write` is false).
+struct DrawOut {
+    int32_t* x;
+    float* q;
+    float* lse;
+    bool write;
+};
+
+__device__ __forceinline__ void put(const DrawOut& o, int tok, float q, float lse) {
+    *o.x = tok;
+    if (o.q) *o.q = q;
+    if (o.lse) *o.lse = lse;
+}
+
+// In-tile rescan: lane owns TC/64 consecutive columns of `tile`.
+template <int TC>
+__device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__ row, int tile,
+                                                float m, float lse, float tprime,
+                                                const DrawOut& o) {
+    constexpr int CPL = TC / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long c0 = static_cast<long long>(tile) * TC + lane * CPL;
+    float lv[CPL], e[CPL];
+    float local = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) lv[j] = (c0 + j < V) ? row[c0 + j] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
+        local += e[j];
+    }
+    const float incl = wave_incl_scan(local);
+    float run = __shfl_up(incl, 1, kWave);
+    if (lane == 0) run = 0.0f;
+    int hit = INT32_MAX, lastpos = -1;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        run += e[j];
+        if (e[j] > 0.0f) {
+            lastpos = static_cast<int>(c0 + j);
+            if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(c0 + j);
+        }
+    }
+    int tok = wave_min_int(hit);
+    if (tok == INT32_MAX) tok = wave_max_int(lastpos);
+    const int rel = tok - tile * TC;
+    const int owner = rel / CPL, jj = rel - owner * CPL;
+    float mine = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+        if (j == jj) mine = lv[j];
+    const float lx = __shfl(mine, owner, kWave);
+    if (o.write && lane == 0) put(o, tok, __expf(lx - lse), lse);
+    return tok;
+}
+
+// One wave draws one request's token; returns it (-1 for a dead request) in every lane.
+template <int TC>
+__device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
+                         const float* __restrict__ row, float u, const DrawOut& o) {
+    constexpr int kSelRegTiles = RegTiles<TC>::value;
+    const int lane = threadIdx.x & (kWave - 1);
+    float m = -INFINITY;
+    float Z, lse, target;
+    int found = -1;
+    float tprime = INFINITY;
+    if (nblk <= kWave * kSelRegTiles) {
+        // register form: lane l holds tiles [l * kSelRegTiles, (l + 1) * kSelRegTiles)
+        float2 p[kSelRegTiles];
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) {
+            const int i = lane * kSelRegTiles + t;
+            p[t] = (i < nblk) ? P[i] : make_float2(-INFINITY, 0.0f);
+        }
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) m = fmaxf(m, p[t].x);
+        m = wave_max(m);
+        if (m == -INFINITY) {
+            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
+            return -1;
+        }
+        float mass[kSelRegTiles];
+        float local = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) {
+            mass[t] = tile_mass(p[t], m);
+            local += mass[t];
+        }
+        Z = wave_sum(local);
+        lse = m + __logf(Z);
+        target = clamp_uniform(u) * Z;
+        const float incl = wave_incl_scan(local);
+        float run = __shfl_up(incl, 1, kWave);
+        if (lane == 0) run = 0.0f;
+        int hit = INT32_MAX, last = -1;
+        float before = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kSelRegTiles; ++t) {
+            const float nr = run + mass[t];
+            if (mass[t] > 0.0f) {
+                last = lane * kSelRegTiles + t;
+                if (hit == INT32_MAX && nr > target) {
+                    hit = lane * kSelRegTiles + t;
+                    before = run;
+                }
+            }
+            run = nr;
+        }
+        found = wave_min_int(hit);
+        if (found == INT32_MAX) {
+            found = wave_max_int(last);
+        } else {
+            tprime = target - __shfl(before, found / kSelRegTiles, kWave);
+        }
+    } else {
+        // loop form for vocabularies with more tiles than the registers hold
+        for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, P[i].x);
+        m = wave_max(m);
+        if (m == -INFINITY) {
+            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
+            return -1;
+        }
+        float z = 0.0f;
+        for (int i = lane; i < nblk; i += kWave) z += tile_mass(P[i], m);
+        Z = wave_sum(z);
+        lse = m + __logf(Z);
+        target = clamp_uniform(u) * Z;
+        float run = 0.0f;
+        for (int base = 0; base < nblk; base += kWave) {
+            const int i = base + lane;
+            const float v = (i < nblk) ? tile_mass(P[i], m) : 0.0f;
+            const float incl = wave_incl_scan(v);
+            float excl = __shfl_up(incl, 1, kWave);
+            if (lane == 0) excl = 0.0f;
+            const unsigned long long hit =
+                __ballot((i < nblk) && (v > 0.0f) && (run + incl > target));
+            if (hit) {
+                const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                found = base + f;
+                tprime = target - (run + __shfl(excl, f, kWave));
+                break;
+            }
+            run += __shfl(incl, kWave - 1, kWave);
+        }
+        if (found < 0) {
+            int last = -1;
+            for (int i = lane; i < nblk; i += kWave)
+                if (tile_mass(P[i], m) > 0.0f) last = i;
+            found = wave_max_int(last);
+        }
+    }
+    return rescan_tile_wave<TC>(V, row, found, m, lse, tprime, o);
+}
+
+// Draw of position k for every request, one wave per request; partials of TC-column tiles.
+template <int TC>
+__global__ __launch_bounds__(kSelThreads)
+void draft_select(int B, int V, int gamma, int k, const float2* __restrict__ part, int nblk,
+                  const float* __restrict__ L, long long L_bstride, const float* __restrict__ u,
+                  int32_t* __restrict__ x_out, float* __restrict__ q_out,
+                  float* __restrict__ lse_out) {
+    const int b = blockIdx.x * (kSelThreads / kWave) + threadIdx.x / kWave;
+    if (b >= B) return;
+    const long long o = static_cast<long long>(b) * gamma + k;
+    const DrawOut out{x_out + o, q_out ? q_out + o : nullptr, lse_out ? lse_out + o : nullptr,
+                      true};
+    draw_wave<TC>(V, part + static_cast<long long>(b) * nblk, nblk, L + b * L_bstride, u[o], out);
+}
+
+}  // namespace dspark

@@ -9,7 +9,7 @@ namespace dspark {
 
 // ---------------------------------------------------------------- draft
 struct DraftCall {
-    int B, V, r, gamma, w_dtype, nblk;
+    int B, V, r, gamma, w_dtype;
     const float* U;
     const void* W1;
     const void* W2;
@@ -20,11 +20,17 @@ struct DraftCall {
     float* lse_out;
     float* L[64];             // logits rows of step k: L[k] + b * L_bstride
     long long L_bstride;
-    float2* part[2];          // tile partials [B][nblk] of even / odd steps
+    float2* part[2];          // tile partials [B][draft_part_tiles(V)] of even / odd steps
 };
 
-int draft_tile_cols();
+// Vocabulary tiles per request the partial buffers must hold (the finest tiling in use).
+int draft_part_tiles(int V);
 hipError_t launch_draft(const DraftCall& c, hipStream_t st);
+
+// Batched path on bf16 MFMA (draft_mfma.hip), chosen by launch_draft when it applies.
+bool draft_mfma_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
+int draft_mfma_tile_cols();
+hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st);
 
 // ---------------------------------------------------------------- verify / TV
 struct RowSet {               // the draft and target rows of a verify batch

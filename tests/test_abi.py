@@ -50,9 +50,9 @@ def test_status_strings_and_version(lib):
 
 def test_workspace_sizes(lib):
     B, V, r, G = 64, 151936, 256, 16
-    nblk = -(-V // 512)
+    ntiles = -(-V // 256)
     need = lib.dspark_markov_draft_workspace_bytes(B, V, r, G)
-    assert need >= B * nblk * 8 + B * V * 4
+    assert need >= 2 * B * ntiles * 8 + 2 * B * V * 4
     assert lib.dspark_markov_draft_workspace_bytes(0, V, r, G) == 0
     assert lib.dspark_verify_workspace_bytes(256, V, 16) >= 256 * 33 * 4
     assert lib.dspark_tv_labels_workspace_bytes(256, V, 16) >= 256 * 33 * 4

@@ -47,6 +47,23 @@ def test_ragged_shapes(gpu, B, V, r, G, wdt):
     assert rep.ties <= 1
 
 
+@pytest.mark.parametrize("B,V,r,G", [
+    (9, 4104, 16, 3),       # one ragged request group, V not a multiple of the 256-column tile
+    (65, 2056, 248, 2),     # two request groups; rank padded to the 16-row chunk
+    (130, 3000, 64, 3),     # three groups, last one ragged
+    (64, 8192, 256, 2),     # exact tiles
+])
+def test_batched_mfma_shapes(gpu, B, V, r, G):
+    c = synth.custom(935 + B, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    g = run_draft(d)
+    reqs = sorted({0, 1, B // 2, B - 2, B - 1})
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
+                      reqs, gL=g["L"])
+    assert rep.ties <= 1
+    assert np.all((g["x"] >= 0) & (g["x"] < V))
+
+
 def test_w1_zero_is_independent_sampling(gpu):
     c = synth.custom(930, B=6, V=3001, r=16, gamma=5, w_dtype="bf16")
     d = synth.draft_inputs(c)
