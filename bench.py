@@ -29,10 +29,12 @@ METRIC = "Markov-head draft tokens/s + verified tokens/s at V=151936; % HBM/MFMA
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
-    "single": 2,   # single-request draft, B=1, V=151936, r=256, gamma=7
+    "single": 2,   # single-request draft, B=1, V=151936, r=256, gamma=7 (the headline line)
     "batched": 3,  # batched draft, B=64, V=151936, gamma=16
+    "verify": 4,   # batched verify + TV labels, B=256, V=151936, gamma=16
     "round": 5,    # full round, B=512, V=129280, gamma=16
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -75,7 +77,7 @@ def draft_bytes_per_launch(c) -> float:
     return c.r * c.V * sw + c.B * c.V * 4 + c.B * c.r * sw + c.B * c.V * 4 + c.B * 12
 
 
-def cpu_baseline(c, inp, seconds: float) -> dict:
+def cpu_baseline(c, inp, seconds: float, verify_only: bool = False) -> dict:
     """The fp64 oracle on the same step, single-threaded, repeated for about `seconds`."""
     from threadpoolctl import threadpool_limits
     import oracle
@@ -87,21 +89,30 @@ def cpu_baseline(c, inp, seconds: float) -> dict:
     steps = 0
     with threadpool_limits(limits=1):
         while True:
-            d = oracle.markov_draft(inp["U"][reqs], inp["W1"], inp["W2"], inp["x0"][reqs],
-                                    inp["u"][reqs], c.w_dtype, want_logits=True)
-            s = oracle.schedule(inp["conf"][reqs], inp["temp"], inp["sps"], 4096)
             Lt = inp["Lt"].reshape(c.B, G + 1, V)[reqs].reshape(-1, V)
-            oracle.verify(d["L"], Lt, d["x"], inp["u_acc"][reqs], inp["u_fin"][reqs],
-                          length=s["len"])
-            oracle.tv_labels(d["L"], Lt, length=s["len"])
-            tokens += len(reqs) * G + int(s["len"].sum())
+            if verify_only:
+                Ld = inp["U"][reqs]
+                x = np.array([[oracle.inverse_cdf(oracle.softmax_row(Ld[i, k])[0], 0.5)
+                               for k in range(G)] for i in range(len(reqs))])
+                oracle.verify(Ld, Lt, x, inp["u_acc"][reqs], inp["u_fin"][reqs])
+                oracle.tv_labels(Ld, Lt)
+                tokens += len(reqs) * G
+            else:
+                d = oracle.markov_draft(inp["U"][reqs], inp["W1"], inp["W2"], inp["x0"][reqs],
+                                        inp["u"][reqs], c.w_dtype, want_logits=True)
+                s = oracle.schedule(inp["conf"][reqs], inp["temp"], inp["sps"], 4096)
+                oracle.verify(d["L"], Lt, d["x"], inp["u_acc"][reqs], inp["u_fin"][reqs],
+                              length=s["len"])
+                oracle.tv_labels(d["L"], Lt, length=s["len"])
+                tokens += len(reqs) * G + int(s["len"].sum())
             steps += 1
             el = time.perf_counter() - t0
             if el >= seconds or el * (steps + 1) / steps > 30.0:
                 break
     return dict(value=tokens / el, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{steps} oracle steps over requests {reqs} of the same workload "
-                       f"(draft + schedule + verify + TV, fp64, one thread), {el:.1f} s")
+                       f"({'verify + TV' if verify_only else 'draft + schedule + verify + TV'}, "
+                       f"fp64, one thread), {el:.1f} s")
 
 
 def main():
@@ -115,6 +126,7 @@ def main():
 
     device = torch.device("cuda:0")
     cfg = WORKLOADS[args.workload]
+    verify_only = args.workload == "verify"
     c, inp = build_inputs(cfg)
     t = {k: to_dev(v, torch, device) for k, v in inp.items()}
     B, G, V = c.B, c.gamma, c.V
@@ -134,19 +146,38 @@ def main():
                  lse_t=torch.empty((B, G + 1), dtype=torch.float32, device=device))
     cstar = torch.empty((B, G), dtype=torch.float32, device=device)
 
+    if verify_only:
+        # draft logits are the inputs; draft tokens x ~ p_d are drawn once, before timing, with
+        # the library's own sampler (a zero Markov bias leaves softmax(L_d) unchanged)
+        out_d["L"].copy_(t["U"])
+        zw1 = torch.zeros((V, 1), dtype=torch.float32, device=device)
+        zw2 = torch.zeros((1, V), dtype=torch.float32, device=device)
+        dspark.markov_draft(t["U"], zw1, zw2, t["x0"], t["u"], out=dict(x=out_d["x"]))
+        torch.cuda.synchronize()
+
     def draft():
         dspark.markov_draft(t["U"], t["W1"], t["W2"], t["x0"], t["u"], out=out_d)
 
-    def rest():
+    def schedule():
         dspark.schedule(t["conf"], t["sps"], Bmax, temp=t["temp"], out=out_s)
-        dspark.verify(out_d["L"], t["Lt"], out_d["x"], t["u_acc"], t["u_fin"],
-                      length=out_s["len"], ld_lse=out_d["lse"], out=out_v)
-        dspark.tv_labels(out_d["L"], t["Lt"], length=out_s["len"], lse_d=out_v["lse_d"],
-                         lse_t=out_v["lse_t"], out=cstar)
+
+    def verify():
+        if verify_only:
+            dspark.verify(out_d["L"], t["Lt"], out_d["x"], t["u_acc"], t["u_fin"], out=out_v)
+        else:
+            dspark.verify(out_d["L"], t["Lt"], out_d["x"], t["u_acc"], t["u_fin"],
+                          length=out_s["len"], ld_lse=out_d["lse"], out=out_v)
+
+    def tv():
+        dspark.tv_labels(out_d["L"], t["Lt"], length=None if verify_only else out_s["len"],
+                         lse_d=out_v["lse_d"], lse_t=out_v["lse_t"], out=cstar)
+
+    parts = dict(verify=verify, tv=tv) if verify_only else dict(draft=draft, schedule=schedule,
+                                                               verify=verify, tv=tv)
 
     def step():
-        draft()
-        rest()
+        for fn in parts.values():
+            fn()
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -155,25 +186,28 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # capture one step and the draft alone
-    g_step, g_draft = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    # capture one step, and each part on its own
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         step()
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
+    g_step = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_step):
         step()
-    with torch.cuda.graph(g_draft):
-        draft()
+    g_parts = {}
+    for name, fn in parts.items():
+        g_parts[name] = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_parts[name]):
+            fn()
     torch.cuda.synchronize()
 
     # reading 512 MB evicts the factors from the 256 MB Infinity Cache without leaving dirty
     # lines behind (a write-based flush would make the first draft step pay the write-back)
     flush = torch.ones(128 << 20, dtype=torch.float32, device=device)
-    verified = int(out_s["len"].sum().item())
-    drafted = B * G
+    verified = B * G if verify_only else int(out_s["len"].sum().item())
+    drafted = 0 if verify_only else B * G
 
     def timed(graph, n):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -190,32 +224,53 @@ def main():
 
     for _ in range(args.warmup):
         g_step.replay()
+    torch.cuda.synchronize()
     ms = timed(g_step, args.steps)
-    ms_draft = timed(g_draft, args.steps)
+    ms_parts = {name: float(np.mean(timed(g, args.steps))) for name, g in g_parts.items()}
     torch.cuda.synchronize()
 
     ms_step = float(np.mean(ms))
     value = (drafted + verified) / (ms_step * 1e-3)
-    launch_us = float(np.mean(ms_draft)) * 1e3 / G          # one fused draft step per launch
-    bytes_launch = draft_bytes_per_launch(c)
-    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+    if verify_only:
+        # dominant work: one HBM sweep over every draft and target row, plus the final rows
+        bytes_call = B * (2 * G + 1) * V * 4 + B * 2 * V * 4
+        launch_us = ms_parts["verify"] * 1e3
+        roof = dict(bound="hbm", kernel="dspark_verify (row_stats + verify_chunks + verify_select)",
+                    achieved=bytes_call / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS, traffic=None, bytes_per_launch=bytes_call,
+                    launch_us=launch_us)
+    else:
+        launch_us = ms_parts["draft"] * 1e3 / G        # one draft step (and draw) per position
+        bytes_launch = draft_bytes_per_launch(c)
+        mfma = B > 8 and c.w_dtype == "bf16"
+        roof = dict(bound="hbm",
+                    kernel="draft_step_mfma + draft_select" if mfma else "draft_step_gemv",
+                    achieved=bytes_launch / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
+                    unit="GB/s")
+        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS, traffic=None,
+                    bytes_per_launch=bytes_launch, launch_us=launch_us)
+        if mfma:
+            tflops = 2.0 * B * c.r * V / (launch_us * 1e-6) / 1e12
+            roof["mfma"] = dict(achieved=tflops, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                                frac=tflops / MFMA_BF16_PEAK_TFLOPS)
+    what = "verify + TV labels" if verify_only else "draft + schedule + verify + TV labels"
     res = dict(
         metric=METRIC, value=value, unit="tokens/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="f32", data="synthetic",
-        config=dict(workload=f"{c.name}: draft + schedule + verify + TV labels per step",
-                    B=B, V=V, r=c.r, gamma=G, factors=c.w_dtype, sps="1/(0.02+1e-5 B)",
-                    Bmax=Bmax, mall_flush=not args.no_flush, graph_replay=True),
+        config=dict(workload=f"{c.name}: {what} per step", B=B, V=V, r=c.r, gamma=G,
+                    factors=c.w_dtype, sps="1/(0.02+1e-5 B)", Bmax=Bmax,
+                    mall_flush=not args.no_flush, graph_replay=True),
         drafted_per_step=drafted, verified_per_step=verified,
-        draft_tok_s=drafted / (float(np.mean(ms_draft)) * 1e-3),
+        breakdown_us={k: v * 1e3 for k, v in ms_parts.items()},
         ms_per_step_p10_p90=[float(np.percentile(ms, 10)), float(np.percentile(ms, 90))],
-        roofline=dict(bound="hbm", kernel="draft_sweep_gemv (fused select)",
-                      achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=None,
-                      bytes_per_launch=bytes_launch, launch_us=launch_us),
+        roofline=roof,
     )
+    if not verify_only:
+        res["draft_tok_s"] = drafted / (ms_parts["draft"] * 1e-3)
+    res["verified_tok_s"] = verified / (ms_parts["verify"] * 1e-3)
     if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_seconds, verify_only)
     print(json.dumps(res), flush=True)
 
 
