@@ -35,6 +35,33 @@ WORKLOADS = {
     "round": 5,    # full round, B=512, V=129280, gamma=16
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
+
+# HBM bytes per dispatch of a dominant kernel, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# WRITE_SIZE) of this benchmark, each scaled by the same counter on a kernel of known size
+# in the same run (the 512 MB flush read: fetch scale 1.9996; its fill: write scale 1.0).
+# A figure holds only for the kernel sources it was measured with.
+MEASURED_TRAFFIC = {
+    ("single", "draft_step_gemv"): dict(
+        bytes=79281052.0,
+        profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
+        sources={"draft.hip": "00feb01c6db9ffaa05974bf39e3f95d1476d01bef333d04b8f7b519855a5ce9f",
+                 "draw.h": "68a13dee38665bffbf47caea15375a90352debe18a3fe1aff59075732b46e18b",
+                 "common.h": "739a5e62ecf98417fbae5c9345a0180ded0f8e56c092c2fffa7484408e8627f4"}),
+}
+
+
+def measured_traffic(workload: str, kernel: str):
+    """Counter-measured bytes per dispatch, or None if absent or the sources have changed."""
+    import hashlib
+    rec = MEASURED_TRAFFIC.get((workload, kernel))
+    if rec is None:
+        return None
+    for name, digest in rec["sources"].items():
+        with open(os.path.join(CSRC, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return rec["bytes"]
 
 
 def parse():
@@ -247,7 +274,8 @@ def main():
                     kernel="draft_step_mfma + draft_select" if mfma else "draft_step_gemv",
                     achieved=bytes_launch / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
                     unit="GB/s")
-        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS, traffic=None,
+        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS,
+                    traffic=measured_traffic(args.workload, roof["kernel"]),
                     bytes_per_launch=bytes_launch, launch_us=launch_us)
         if mfma:
             tflops = 2.0 * B * c.r * V / (launch_us * 1e-6) / 1e12
