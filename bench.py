@@ -98,8 +98,8 @@ def to_dev(a, torch, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def draft_bytes_per_launch(c) -> float:
-    """Algorithmic HBM bytes of one draft step: W2 read, U_k read, W1 rows, L_d write, outputs."""
+def draft_bytes_per_position(c) -> float:
+    """Algorithmic HBM bytes of one draft position: W2 read, U_k read, W1 rows, L_d write, outputs."""
     sw = 2 if c.w_dtype == "bf16" else 4
     return c.r * c.V * sw + c.B * c.V * 4 + c.B * c.r * sw + c.B * c.V * 4 + c.B * 12
 
@@ -267,17 +267,24 @@ def main():
         roof.update(frac=roof["achieved"] / HBM_PEAK_GBS, traffic=None, bytes_per_launch=bytes_call,
                     launch_us=launch_us)
     else:
-        launch_us = ms_parts["draft"] * 1e3 / G        # one draft step (and draw) per position
-        bytes_launch = draft_bytes_per_launch(c)
-        mfma = B > 8 and c.w_dtype == "bf16"
-        roof = dict(bound="hbm",
-                    kernel="draft_step_mfma + draft_select" if mfma else "draft_step_gemv",
-                    achieved=bytes_launch / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
-                    unit="GB/s")
+        path = dspark.markov_draft_path(B, t["W1"], t["W2"])
+        per_pos = draft_bytes_per_position(c)            # algorithmic bytes of one position
+        if path == "resident":
+            # one launch draws all gamma positions (W2 read once, then held in registers); the
+            # timed call also holds the tiny counter-reset kernel that precedes it
+            kernel, units, launch_us = "draft_resident", G, ms_parts["draft"] * 1e3
+        else:
+            # one step kernel per position; the per-position time also carries the draws
+            kernel = "draft_step_mfma + draft_select" if path == "mfma" else "draft_step_gemv"
+            units, launch_us = 1, ms_parts["draft"] * 1e3 / G
+        bytes_launch = per_pos * units
+        roof = dict(bound="hbm", kernel=kernel, achieved=bytes_launch / (launch_us * 1e-6) / 1e9,
+                    peak=HBM_PEAK_GBS, unit="GB/s")
         roof.update(frac=roof["achieved"] / HBM_PEAK_GBS,
-                    traffic=measured_traffic(args.workload, roof["kernel"]),
-                    bytes_per_launch=bytes_launch, launch_us=launch_us)
-        if mfma:
+                    traffic=measured_traffic(args.workload, kernel),
+                    bytes_per_launch=bytes_launch, positions_per_launch=units,
+                    launch_us=launch_us, draft_path=path)
+        if path == "mfma":
             tflops = 2.0 * B * c.r * V / (launch_us * 1e-6) / 1e12
             roof["mfma"] = dict(achieved=tflops, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                 frac=tflops / MFMA_BF16_PEAK_TFLOPS)

@@ -16,12 +16,13 @@ LIB_PATH = os.path.join(PKG, "libdspark.so")
 
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(5)
 F32, BF16 = 0, 1
+PATH_NAMES = {0: "sweep", 1: "mfma", 2: "resident"}
 GLOBAL, EARLY_STOP = 0, 1
 
 # every symbol include/dspark.h declares
 EXPORTS = (
     "dspark_status_string", "dspark_last_error", "dspark_version",
-    "dspark_markov_draft_workspace_bytes", "dspark_markov_draft",
+    "dspark_markov_draft_path", "dspark_markov_draft_workspace_bytes", "dspark_markov_draft",
     "dspark_verify_workspace_bytes", "dspark_verify",
     "dspark_tv_labels_workspace_bytes", "dspark_tv_labels",
     "dspark_schedule_workspace_bytes", "dspark_schedule",
@@ -35,6 +36,7 @@ _SIGS = {
     "dspark_status_string": (ctypes.c_char_p, [_I]),
     "dspark_last_error": (ctypes.c_char_p, []),
     "dspark_version": (_I, []),
+    "dspark_markov_draft_path": (_I, [_I, _I, _I, _I, _P, _P]),
     "dspark_markov_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_verify_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -126,6 +128,15 @@ def workspace(nbytes: int, device, tag: str = ""):
 
 
 # ----------------------------------------------------------------------------- entry points
+def markov_draft_path(B: int, W1, W2) -> str:
+    """Which kernel path markov_draft takes for B requests with these factors on the
+    current device: "sweep", "mfma" or "resident" (see dspark_markov_draft_path)."""
+    torch = _torch()
+    V, r = W1.shape
+    wdt = BF16 if W1.dtype == torch.bfloat16 else F32
+    return PATH_NAMES[load().dspark_markov_draft_path(B, V, r, wdt, _ptr(W1), _ptr(W2))]
+
+
 def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=False,
                  out=None, stream=None):
     """dspark_markov_draft. U [B][gamma][V] fp32, W1 [V][r], W2 [r][V] (fp32 or bf16),

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 
-SOURCES = ["api.hip", "draft.hip", "draft_mfma.hip", "verify.hip", "schedule.hip"]
+SOURCES = ["api.hip", "draft.hip", "draft_mfma.hip", "draft_resident.hip", "verify.hip",
+           "schedule.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -1,0 +1,321 @@
+// Single-request Markov-head draft with W2 held in registers across all positions (gfx950).
+//
+// [P3] "DSpark Speculative Decoding", section "Semi-Autoregressive Generation": position k
+// samples x_k from softmax(U_k + B_k) with B_k = W1[x_{k-1}] W2 (rank r), one position after
+// the other. For a single request each position is a GEMV whose only large operand, W2
+// (r x V bf16, 77.8 MB at r = 256, V = 151936), is the same at every position. The chip's
+// vector register files hold 128 MB, so one persistent launch reads W2 from HBM once and
+// keeps it in registers for all gamma positions. Each position then moves only U_k, the
+// logits row and one W1 row. ([P3] = the concept note "DSpark Speculative Decoding".)
+//
+// Layout. One workgroup of 8 waves per CU, G = ceil(V / 640) workgroups (238 at
+// V = 151936), all resident at once. Workgroup g owns the 640 columns starting at 640g.
+//   - Wave w owns the rank group [32w, 32w + 32).
+//   - Lane l owns the 10 consecutive columns starting at 640g + 10l.
+// Each register holds two consecutive ranks of one column as bf16, 160 registers per
+// lane. The load phase reads each 1280-byte W2 row segment with 16-byte coalesced loads
+// into LDS, and each lane then picks its columns out of it. The products use v_dot2
+// (bf16 x bf16 pairs into fp32). The 8
+// rank-group partial sums of a column meet in LDS and are added in wave order.
+//
+// Positions are separated by a grid barrier. Arrivals go to 16 agent-scope counters in the
+// workspace, one per 128-byte line, so that the increments do not serialise on one
+// address. Everything other workgroups read is written with device-scope (sc1) stores, and
+// each thread waits for its own stores before the arrival increment. No L2 write-back fence
+// is used, because that costs tens of microseconds per barrier on this part.
+//
+// After a barrier, wave 0 of every workgroup draws x_k from the published tile partials
+// and logits. It merges the G partials in tile order and rescans the chosen 640-column tile
+// in token order. The workgroup then stages W1[x_k] in LDS for the next position.
+// Workgroup 0 writes x_k, q_k and lse_k. The spin on the counters is bounded. A workgroup that gives up returns, so the
+// launch always drains. If workgroup 0 gives up, it writes the -1 sentinel into the
+// positions it could not draw.
+#include "common.h"
+#include "draw.h"
+#include "kernels.h"
+
+namespace dspark {
+
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRThreads = 512;                            // 8 waves
+constexpr int kRWaves = kRThreads / kWave;
+constexpr int kGroupRanks = 32;                           // ranks per wave
+constexpr int kResMaxRank = kRWaves * kGroupRanks;        // 256
+constexpr int kLaneCols = 10;                             // consecutive columns per lane
+constexpr int kResTileCols = kWave * kLaneCols;           // 640 columns per workgroup
+constexpr int kStageRows = 8;                             // W2 rows per wave per staging round
+constexpr int kChunks = kResTileCols / 8;                 // 16-byte chunks per row segment
+constexpr int kStageLoads = kStageRows * kChunks / kWave; // uint4 loads per lane per round
+constexpr size_t kResLds = static_cast<size_t>(kRWaves) * kStageRows * kResTileCols * 2;
+static_assert(kStageLoads * kWave == kStageRows * kChunks, "staging rounds cover whole rows");
+static_assert(kResLds >= sizeof(float) * kRWaves * kResTileCols, "sums fit in the staging area");
+constexpr int kCounters = 16;                             // arrival counters
+constexpr int kCounterStride = 32;                        // uint32 per counter (128 bytes)
+constexpr unsigned kSpinMax = 1u << 20;                   // bounded wait, about a second
+static_assert(kResTileCols == 640 && kRThreads + 128 == kResTileCols, "epilogue ownership");
+
+struct ResArgs {
+    int V, r, gamma, G;
+    const float* U;           // [gamma][V]
+    const uint16_t* W1;       // [V][r] bf16 bits
+    const uint16_t* W2;       // [r][V] bf16 bits
+    const int32_t* x0;
+    const float* u;           // [gamma]
+    int32_t* x_out;
+    float* q_out;
+    float* lse_out;
+    float* L[64];             // logits row of position k
+    float2* part[2];          // [G] tile partials of even / odd positions
+    unsigned* sync;           // kCounters arrival counters, kCounterStride apart, zero at launch
+};
+
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t h, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, h), acc, false);
+}
+
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every store this thread issued has been acknowledged at device scope.
+__device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+__global__ __launch_bounds__(kRThreads, 1)
+void draft_resident(ResArgs a) {
+    __shared__ uint4 lds[kResLds / sizeof(uint4)];         // W2 staging, then rank-group sums
+    __shared__ float2 wpart[kRWaves];
+    __shared__ uint32_t hs[kResMaxRank / 2];               // W1[x] as bf16 pairs
+    __shared__ int stok;
+    __shared__ int gave_up;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int V = a.V, r = a.r;
+    const long long c0 = static_cast<long long>(blockIdx.x) * kResTileCols;
+
+    // 1. W2 slice: w[i][m] = (W2[32w + 2m][c + i], W2[32w + 2m + 1][c + i]), c = 640g + 10l. Each wave
+    //    issues all of its 32 rows at once as 16-byte coalesced loads of the workgroup's
+    //    1280-byte row segments (V % 8 == 0), then passes them through LDS in 4 rounds of 8
+    //    rows, and every lane picks its 10 columns out of each row as 5 aligned 4-byte words.
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds) + wave * (kStageRows * kResTileCols);
+    uint32_t w[kLaneCols][kGroupRanks / 2];
+    constexpr int kRounds = kGroupRanks / kStageRows;
+    uint4 v[kRounds][kStageLoads];                         // all of the lane's loads in flight
+#pragma unroll
+    for (int rho = 0; rho < kRounds; ++rho)
+#pragma unroll
+        for (int n = 0; n < kStageLoads; ++n) {
+            const int i = lane + kWave * n, t = i / kChunks, ch = i - t * kChunks;
+            const int row = kGroupRanks * wave + kStageRows * rho + t;
+            const long long col = c0 + 8 * ch;
+            v[rho][n] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < r && col < V)
+                v[rho][n] = *reinterpret_cast<const uint4*>(a.W2 + static_cast<long long>(row) * V + col);
+        }
+#pragma unroll
+    for (int rho = 0; rho < kRounds; ++rho) {
+#pragma unroll
+        for (int n = 0; n < kStageLoads; ++n) {
+            const int i = lane + kWave * n, t = i / kChunks, ch = i - t * kChunks;
+            *reinterpret_cast<uint4*>(stage + t * kResTileCols + 8 * ch) = v[rho][n];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kStageRows; t += 2) {
+            const uint32_t* r0p = reinterpret_cast<const uint32_t*>(stage + t * kResTileCols + kLaneCols * lane);
+            const uint32_t* r1p = reinterpret_cast<const uint32_t*>(stage + (t + 1) * kResTileCols + kLaneCols * lane);
+            const int m = (kStageRows / 2) * rho + t / 2;
+#pragma unroll
+            for (int i = 0; i < kLaneCols / 2; ++i) {
+                const uint32_t r0 = r0p[i], r1 = r1p[i];
+                w[2 * i][m] = (r0 & 0xffffu) | (r1 << 16);
+                w[2 * i + 1][m] = (r0 >> 16) | (r1 & 0xffff0000u);
+            }
+        }
+        __syncthreads();
+    }
+    float (*red)[kResTileCols] = reinterpret_cast<float (*)[kResTileCols]>(lds);   // reuses the staging area
+
+    // epilogue columns of this thread: c0 + tid, and c0 + 512 + tid for tid < 128
+    const long long e1 = c0 + tid, e2 = c0 + kRThreads + tid;
+    const bool own2 = tid < kResTileCols - kRThreads;
+    if (tid == 0) {
+        int t = a.x0[0];
+        stok = (t >= 0 && t < V) ? t : -1;                 // dead request: -inf logits
+        gave_up = 0;
+    }
+    __syncthreads();
+    int k = 0;
+    for (; k < a.gamma; ++k) {
+        const float u1 = (e1 < V) ? a.U[static_cast<long long>(k) * V + e1] : 0.0f;
+        const float u2 = (own2 && e2 < V) ? a.U[static_cast<long long>(k) * V + e2] : 0.0f;
+        const int tok = stok;
+        // 2. h = W1[x_{k-1}] into LDS (r % 8 == 0: whole 8-rank segments)
+        if (tid < kResMaxRank / 8) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (tok >= 0 && 8 * tid < r)
+                v = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tok) * r + 8 * tid);
+            reinterpret_cast<uint4*>(hs)[tid] = v;
+        }
+        __syncthreads();
+        // 3. projection from registers: this wave's 32 ranks of the lane's 10 columns
+        uint32_t hv[kGroupRanks / 2];
+#pragma unroll
+        for (int m = 0; m < kGroupRanks / 2; ++m) hv[m] = hs[(kGroupRanks / 2) * wave + m];
+        float acc[kLaneCols];
+#pragma unroll
+        for (int i = 0; i < kLaneCols; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int m = 0; m < kGroupRanks / 2; ++m) s = dot2(w[i][m], hv[m], s);
+            acc[i] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < kLaneCols / 2; ++i)
+            reinterpret_cast<float2*>(&red[wave][kLaneCols * lane])[i] = make_float2(acc[2 * i], acc[2 * i + 1]);
+        __syncthreads();
+        // 4. logits (rank groups added in wave order), logits row, tile partial
+        const bool live = tok >= 0;
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kRWaves; ++g) s1 += red[g][tid];
+        if (own2) {
+#pragma unroll
+            for (int g = 0; g < kRWaves; ++g) s2 += red[g][kRThreads + tid];
+        }
+        const float l1 = (live && e1 < V) ? u1 + s1 : -INFINITY;
+        const float l2 = (live && own2 && e2 < V) ? u2 + s2 : -INFINITY;
+        float* Lk = a.L[k];
+        if (e1 < V) store_coherent(Lk + e1, l1);
+        if (own2 && e2 < V) store_coherent(Lk + e2, l2);
+        const float mw = wave_max(fmaxf(l1, l2));
+        const float ew = (mw == -INFINITY) ? 0.0f
+                         : ((l1 == -INFINITY ? 0.0f : __expf(l1 - mw)) +
+                            (l2 == -INFINITY ? 0.0f : __expf(l2 - mw)));
+        const float sw = wave_sum(ew);
+        if (lane == 0) wpart[wave] = make_float2(mw, sw);
+        __syncthreads();
+        if (tid == 0) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < kRWaves; ++i) m = fmaxf(m, wpart[i].x);
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kRWaves; ++i) s += tile_mass(wpart[i], m);
+            store_coherent(a.part[k & 1] + blockIdx.x, make_float2(m, s));
+        }
+        // 5. grid barrier: own stores acknowledged, arrive, wait for the counters' sum
+        drain_stores();
+        __syncthreads();
+        if (wave == 0) {
+            if (lane == 0)
+                __hip_atomic_fetch_add(a.sync + (blockIdx.x % kCounters) * kCounterStride, 1u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned target = static_cast<unsigned>(a.G) * static_cast<unsigned>(k + 1);
+            unsigned n = 0;
+            while (true) {
+                unsigned v = (lane < kCounters)
+                                 ? __hip_atomic_load(a.sync + lane * kCounterStride, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0u;
+#pragma unroll
+                for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);   // same in every lane
+                if (v >= target) break;
+                if (++n > kSpinMax) {
+                    if (lane == 0) gave_up = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            // 6. draw x_k from the published partials and logits
+            if (!gave_up) {
+                const DrawOut out{a.x_out + k, a.q_out ? a.q_out + k : nullptr,
+                                  a.lse_out ? a.lse_out + k : nullptr, blockIdx.x == 0};
+                const int t = draw_wave<kResTileCols, true>(V, a.part[k & 1], a.G, Lk, a.u[k], out);
+                if (lane == 0) stok = t;
+            }
+        }
+        __syncthreads();
+        if (gave_up) break;
+        // the partial buffer of k + 2 reuses this one: no workgroup writes it before every
+        // workgroup has passed the barrier of position k + 1, i.e. finished this draw
+    }
+    if (gave_up && blockIdx.x == 0 && tid == 0) {
+        for (int i = k; i < a.gamma; ++i) {
+            a.x_out[i] = -1;
+            if (a.q_out) a.q_out[i] = 0.0f;
+            if (a.lse_out) a.lse_out[i] = -INFINITY;
+        }
+    }
+}
+
+__global__ void zero_counters(unsigned* sync) {
+    if (threadIdx.x < kCounters) sync[threadIdx.x * kCounterStride] = 0u;
+}
+
+struct DeviceFit {
+    int cus = -1;
+    int occupancy = -1;
+};
+
+DeviceFit device_fit() {
+    thread_local DeviceFit cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DeviceFit{};
+    DeviceFit& f = cache[dev];
+    if (f.cus < 0) {
+        int cus = 0, occ = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, draft_resident, kRThreads, 0) !=
+                hipSuccess)
+            return DeviceFit{};
+        f.cus = cus;
+        f.occupancy = occ;
+    }
+    return f;
+}
+
+}  // namespace
+
+int draft_resident_tile_cols() { return kResTileCols; }
+
+size_t draft_resident_sync_bytes() { return kCounters * kCounterStride * sizeof(unsigned); }
+
+bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
+    if (B != 1 || w_dtype != 1 || r > kResMaxRank || (r % 8) != 0 || (V % 8) != 0) return false;
+    if ((reinterpret_cast<uintptr_t>(W1) % 16) != 0 || (reinterpret_cast<uintptr_t>(W2) % 16) != 0)
+        return false;
+    const DeviceFit f = device_fit();
+    const long long G = (static_cast<long long>(V) + kResTileCols - 1) / kResTileCols;
+    return f.cus > 0 && f.occupancy >= 1 && G <= f.cus;
+}
+
+hipError_t launch_draft_resident(const DraftCall& c, unsigned* sync, hipStream_t st) {
+    ResArgs a;
+    a.V = c.V; a.r = c.r; a.gamma = c.gamma;
+    a.G = (c.V + kResTileCols - 1) / kResTileCols;
+    a.U = c.U;
+    a.W1 = static_cast<const uint16_t*>(c.W1);
+    a.W2 = static_cast<const uint16_t*>(c.W2);
+    a.x0 = c.x0; a.u = c.u;
+    a.x_out = c.x_out; a.q_out = c.q_out; a.lse_out = c.lse_out;
+    for (int k = 0; k < c.gamma; ++k) a.L[k] = c.L[k];
+    a.part[0] = c.part[0];
+    a.part[1] = c.part[1];
+    a.sync = sync;
+    hipLaunchKernelGGL(zero_counters, dim3(1), dim3(64), 0, st, sync);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(draft_resident, dim3(a.G), dim3(kRThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -23,6 +23,22 @@ struct RegTiles {
     static constexpr int value = TC >= 512 ? 8 : 16;
 };
 
+// Loads of partials and logits. COHERENT = device-scope loads that bypass the per-XCD L2
+// copies, for data another workgroup wrote earlier in the same launch.
+template <bool COHERENT>
+__device__ __forceinline__ float2 load_part(const float2* p) {
+    if (!COHERENT) return *p;
+    const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_bit_cast(float2, v);
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ float load_logit(const float* p) {
+    if (!COHERENT) return *p;
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float tile_mass(float2 p, float m) {
     return (p.x == -INFINITY) ? 0.0f : p.y * __expf(p.x - m);
 }
@@ -42,7 +58,7 @@ __device__ __forceinline__ void put(const DrawOut& o, int tok, float q, float ls
 }
 
 // In-tile rescan: lane owns TC/64 consecutive columns of `tile`.
-template <int TC>
+template <int TC, bool COHERENT = false>
 __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__ row, int tile,
                                                 float m, float lse, float tprime,
                                                 const DrawOut& o) {
@@ -52,7 +68,7 @@ __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__
     float lv[CPL], e[CPL];
     float local = 0.0f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) lv[j] = (c0 + j < V) ? row[c0 + j] : -INFINITY;
+    for (int j = 0; j < CPL; ++j) lv[j] = (c0 + j < V) ? load_logit<COHERENT>(row + c0 + j) : -INFINITY;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
@@ -84,7 +100,7 @@ __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__
 }
 
 // One wave draws one request's token; returns it (-1 for a dead request) in every lane.
-template <int TC>
+template <int TC, bool COHERENT = false>
 __device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
                          const float* __restrict__ row, float u, const DrawOut& o) {
     constexpr int kSelRegTiles = RegTiles<TC>::value;
@@ -99,7 +115,7 @@ __device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
 #pragma unroll
         for (int t = 0; t < kSelRegTiles; ++t) {
             const int i = lane * kSelRegTiles + t;
-            p[t] = (i < nblk) ? P[i] : make_float2(-INFINITY, 0.0f);
+            p[t] = (i < nblk) ? load_part<COHERENT>(P + i) : make_float2(-INFINITY, 0.0f);
         }
 #pragma unroll
         for (int t = 0; t < kSelRegTiles; ++t) m = fmaxf(m, p[t].x);
@@ -143,21 +159,21 @@ __device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
         }
     } else {
         // loop form for vocabularies with more tiles than the registers hold
-        for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, P[i].x);
+        for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, load_part<COHERENT>(P + i).x);
         m = wave_max(m);
         if (m == -INFINITY) {
             if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
             return -1;
         }
         float z = 0.0f;
-        for (int i = lane; i < nblk; i += kWave) z += tile_mass(P[i], m);
+        for (int i = lane; i < nblk; i += kWave) z += tile_mass(load_part<COHERENT>(P + i), m);
         Z = wave_sum(z);
         lse = m + __logf(Z);
         target = clamp_uniform(u) * Z;
         float run = 0.0f;
         for (int base = 0; base < nblk; base += kWave) {
             const int i = base + lane;
-            const float v = (i < nblk) ? tile_mass(P[i], m) : 0.0f;
+            const float v = (i < nblk) ? tile_mass(load_part<COHERENT>(P + i), m) : 0.0f;
             const float incl = wave_incl_scan(v);
             float excl = __shfl_up(incl, 1, kWave);
             if (lane == 0) excl = 0.0f;
@@ -174,11 +190,11 @@ __device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
         if (found < 0) {
             int last = -1;
             for (int i = lane; i < nblk; i += kWave)
-                if (tile_mass(P[i], m) > 0.0f) last = i;
+                if (tile_mass(load_part<COHERENT>(P + i), m) > 0.0f) last = i;
             found = wave_max_int(last);
         }
     }
-    return rescan_tile_wave<TC>(V, row, found, m, lse, tprime, o);
+    return rescan_tile_wave<TC, COHERENT>(V, row, found, m, lse, tprime, o);
 }
 
 // Draw of position k for every request, one wave per request; partials of TC-column tiles.

@@ -84,8 +84,25 @@ int dspark_version(void);
  *   q_out   [B][gamma]     fp32 p_k(x_k)                      (nullable)
  *   lse_out [B][gamma]     fp32 logsumexp(U_k + B_k)          (nullable)
  *   Ld_out  [B][gamma][V]  fp32 draft logits U_k + B_k        (nullable)
- * Steps run in order on `stream` without host round trips; step k reads x_{k-1} from x_out.
+ * Positions run in order on `stream` without host round trips. Three kernel paths compute
+ * this same function (dspark_markov_draft_path tells which one a call takes); each is
+ * deterministic, and they differ from one another only in fp32 rounding order:
+ *   DSPARK_PATH_SWEEP     one vocabulary sweep per position (B <= 8, or fp32 factors).
+ *   DSPARK_PATH_MFMA      one bf16 MFMA projection per position (B > 8, bf16 factors).
+ *   DSPARK_PATH_RESIDENT  one launch for all positions, W2 held in registers across the GPU
+ *                         (B = 1, bf16, r <= 256 and r % 8 == 0, V % 8 == 0, 16-byte aligned
+ *                         factors, ceil(V / 640) <= compute units). Its workgroups must all be
+ *                         resident at once and meet at a grid barrier after every position.
+ *                         If other work keeps compute units busy for about a second, a
+ *                         barrier gives up, and the positions not yet drawn get token -1,
+ *                         q = 0 and lse = -inf. Draft calls on other streams of the same
+ *                         device must not overlap a call that takes this path.
  */
+enum { DSPARK_PATH_SWEEP = 0, DSPARK_PATH_MFMA = 1, DSPARK_PATH_RESIDENT = 2 };
+
+/* The path dspark_markov_draft takes for these arguments on the current device. */
+int dspark_markov_draft_path(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
+
 size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma);
 int dspark_markov_draft(int B, int V, int r, int gamma,
                         const float* U, const void* W1, const void* W2, int w_dtype,

@@ -62,6 +62,19 @@ def test_workspace_sizes(lib):
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
 
 
+def test_draft_path_host_rules(lib):
+    """Path choices that depend on sizes, dtype and alignment only (no device query)."""
+    lib.dspark_markov_draft_path.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
+    odd = ctypes.c_void_p(0x1002)                 # not 16-byte aligned
+    assert lib.dspark_markov_draft_path(64, 151936, 256, 1, FAKE, FAKE) == 1     # bf16 MFMA
+    assert lib.dspark_markov_draft_path(64, 151936, 256, 0, FAKE, FAKE) == 0     # fp32: sweep
+    assert lib.dspark_markov_draft_path(8, 151936, 256, 1, FAKE, FAKE) == 0      # B <= 8
+    assert lib.dspark_markov_draft_path(64, 151936, 256, 1, odd, FAKE) == 0      # misaligned
+    assert lib.dspark_markov_draft_path(1, 151936, 256, 0, FAKE, FAKE) == 0      # fp32, B = 1
+    assert lib.dspark_markov_draft_path(1, 151936, 260, 1, FAKE, FAKE) == 0      # r > 256
+    assert lib.dspark_markov_draft_path(1, 151937, 256, 1, FAKE, FAKE) == 0      # V % 8 != 0
+
+
 def _draft(lib, B=2, V=64, r=4, G=3, wdt=0, ws=FAKE, wsb=1 << 30, U=FAKE, x_out=FAKE):
     return lib.dspark_markov_draft(B, V, r, G, U, FAKE, FAKE, wdt, FAKE, FAKE, x_out, None,
                                    None, None, ws, wsb, None)

@@ -41,6 +41,7 @@ def test_cfg1_tiny_fp32_exact(gpu):
 def test_ragged_shapes(gpu, B, V, r, G, wdt):
     c = synth.custom(920 + B + V % 97, B=B, V=V, r=r, gamma=G, w_dtype=wdt, w_sigma=0.3)
     d = synth.draft_inputs(c)
+    assert dspark.markov_draft_path(B, dev(d["W1"]), dev(d["W2"])) == "sweep"
     g = run_draft(d)
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], wdt, g["x"], g["q"], g["lse"],
                       range(B), gL=g["L"])
@@ -56,12 +57,66 @@ def test_ragged_shapes(gpu, B, V, r, G, wdt):
 def test_batched_mfma_shapes(gpu, B, V, r, G):
     c = synth.custom(935 + B, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
+    assert dspark.markov_draft_path(B, dev(d["W1"]), dev(d["W2"])) == "mfma"
     g = run_draft(d)
     reqs = sorted({0, 1, B // 2, B - 2, B - 1})
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
                       reqs, gL=g["L"])
     assert rep.ties <= 1
     assert np.all((g["x"] >= 0) & (g["x"] < V))
+
+
+@pytest.mark.parametrize("V,r,G", [
+    (8, 8, 3),              # one 16-byte chunk: one workgroup, one live lane
+    (640, 256, 5),          # exactly one 640-column workgroup tile
+    (1288, 64, 7),          # two full tiles and a ragged third
+    (20000, 248, 16),       # rank not a multiple of the 32-rank lane group
+    (151936, 256, 64),      # full vocabulary, gamma at its cap
+])
+def test_single_request_bf16_shapes(gpu, V, r, G):
+    """One bf16 request: the single-launch path with W2 held in registers."""
+    c = synth.custom(940 + V % 89, B=1, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    assert dspark.markov_draft_path(1, dev(d["W1"]), dev(d["W2"])) == "resident"
+    g = run_draft(d)
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"],
+                      g["lse"], [0], gL=g["L"])
+    assert rep.ties <= 1
+    assert rep.compared + rep.ties + rep.skipped == G
+
+
+def test_single_request_bf16_permutation_chain(gpu):
+    """Closed form through the single-request path: W1[x] = 50 e_{x mod r}, W2 a partial
+    permutation, so x_k = perm[x_{k-1} mod r] whatever the uniforms."""
+    g = np.random.default_rng(8)
+    G, V, r = 12, 6000, 16
+    perm = g.permutation(V)[:r]
+    W1 = np.zeros((V, r), np.float32)
+    W1[np.arange(V), np.arange(V) % r] = 50.0
+    W2 = np.zeros((r, V), np.float32)
+    W2[np.arange(r), perm] = 1.0
+    d = dict(U=(0.1 * g.standard_normal((1, G, V))).astype(np.float32),
+             W1=synth.f32_to_bf16_bits(W1), W2=synth.f32_to_bf16_bits(W2),
+             x0=np.array([4321], np.int32),
+             u=g.uniform(1e-3, 1 - 2 ** -24, size=(1, G)).astype(np.float32))
+    out = run_draft(d, want_logits=False)
+    prev = 4321
+    for k in range(G):
+        prev = perm[prev % r]
+        assert out["x"][0, k] == prev
+
+
+def test_single_request_bf16_sentinels(gpu):
+    c = synth.custom(936, B=1, V=3000, r=32, gamma=5)
+    d = synth.draft_inputs(c)
+    d["U"][0, 2, :] = -np.inf                  # position 3 has no mass: -1 from there on
+    g = run_draft(d)
+    ref = oracle.markov_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16")
+    assert np.array_equal(ref["x"], g["x"])
+    assert np.all(g["x"][0, 2:] == -1) and g["lse"][0, 2] == -np.inf and g["q"][0, 2] == 0.0
+    d["x0"][0] = c.V + 7                       # out-of-range context token: all -1
+    g = run_draft(d)
+    assert np.all(g["x"] == -1)
 
 
 def test_w1_zero_is_independent_sampling(gpu):
