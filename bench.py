@@ -42,6 +42,12 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # in the same run (the 512 MB flush read: fetch scale 1.9996; its fill: write scale 1.0).
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
+    ("single", "draft_resident"): dict(
+        bytes=87223243.0,
+        profile="profiles/draft_resident_single_request_B1_V151936.md",
+        sources={"draft_resident.hip": "682bcf714d79396666e448c71696e1dbf3b865c181e549572ed41b30490585c3",
+                 "draw.h": "12a3facce0ee750fa340bb90c5245304d707a343b6ba4cb89f46436ecf8b4f09",
+                 "common.h": "739a5e62ecf98417fbae5c9345a0180ded0f8e56c092c2fffa7484408e8627f4"}),
     ("single", "draft_step_gemv"): dict(
         bytes=79281052.0,
         profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
