@@ -92,11 +92,10 @@ int dspark_markov_draft_path(int B, int V, int r, int w_dtype, const void* W1, c
 
 size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma) {
     (void)r;
-    (void)gamma;
-    if (B < 1 || V < 1) return 0;
+    if (B < 1 || V < 1 || gamma < 1) return 0;
     return 2 * align_up(draft_part_count(B, V) * sizeof(float2)) +
            2 * align_up(static_cast<size_t>(B) * V * sizeof(float)) +
-           align_up(dspark::draft_resident_sync_bytes());
+           align_up(dspark::draft_resident_slot_bytes(V, gamma));
 }
 
 int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const void* W1,
@@ -129,7 +128,7 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
     for (int k = 0; k < gamma; ++k)
         dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
     dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
-    dc.sync = c.take<unsigned>(dspark::draft_resident_sync_bytes() / sizeof(unsigned));
+    dc.slots = c.take<float2>(dspark::draft_resident_slot_bytes(V, gamma) / sizeof(float2));
     const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "markov_draft");
     return ok();

@@ -80,6 +80,75 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// ---------------------------------------------------------------- wave level, DPP forms
+// For code in which all 64 lanes are active. Reductions run a butterfly inside each row of
+// 16 lanes on DPP (quad xor 1, quad xor 2, half-row mirror, row mirror), which leaves the
+// row result in every lane of the row, then read the four row results out with v_readlane
+// and combine them in row order, so every lane returns the same value. The scan is the
+// Hillis-Steele prefix inside each row (row_shr 1, 2, 4, 8) followed by the row_bcast 15 and
+// 31 steps that carry row totals forward. All orders are fixed, so results are reproducible.
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL, ROW_MASK, BOUND_ZERO>(__float_as_int(v)));
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+template <class Op>
+__device__ __forceinline__ float wave_reduce_dpp(float v, Op op) {
+    v = op(v, dpp_f<0xB1>(v));     // quad_perm [1,0,3,2]
+    v = op(v, dpp_f<0x4E>(v));     // quad_perm [2,3,0,1]
+    v = op(v, dpp_f<0x141>(v));    // row_half_mirror
+    v = op(v, dpp_f<0x140>(v));    // row_mirror
+    return op(op(readlane_f(v, 0), readlane_f(v, 16)), op(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+template <class Op>
+__device__ __forceinline__ int wave_reduce_dpp(int v, Op op) {
+    v = op(v, dpp_i<0xB1>(v));
+    v = op(v, dpp_i<0x4E>(v));
+    v = op(v, dpp_i<0x141>(v));
+    v = op(v, dpp_i<0x140>(v));
+    return op(op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+              op(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpSum { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpMinI { __device__ int operator()(int a, int b) const { return min(a, b); } };
+struct OpMaxI { __device__ int operator()(int a, int b) const { return max(a, b); } };
+
+__device__ __forceinline__ float wave_max_dpp(float v) { return wave_reduce_dpp(v, OpMax{}); }
+__device__ __forceinline__ float wave_sum_dpp(float v) { return wave_reduce_dpp(v, OpSum{}); }
+__device__ __forceinline__ int wave_min_int_dpp(int v) { return wave_reduce_dpp(v, OpMinI{}); }
+__device__ __forceinline__ int wave_max_int_dpp(int v) { return wave_reduce_dpp(v, OpMaxI{}); }
+
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ float wave_incl_scan_dpp(float v) {
+    v += dpp_f<0x111, 0xF, true>(v);   // row_shr 1, zero at the row start
+    v += dpp_f<0x112, 0xF, true>(v);   // row_shr 2
+    v += dpp_f<0x114, 0xF, true>(v);   // row_shr 4
+    v += dpp_f<0x118, 0xF, true>(v);   // row_shr 8
+    v += dpp_f<0x142, 0xA>(v);         // row_bcast 15 into rows 1 and 3
+    v += dpp_f<0x143, 0xC>(v);         // row_bcast 31 into rows 2 and 3
+    return v;
+}
+
+// Value of the previous lane (0 in lane 0): turns an inclusive scan into an exclusive one.
+__device__ __forceinline__ float wave_shr1_dpp(float v) { return dpp_f<0x138, 0xF, true>(v); }
+
+// v from a lane index that is the same in every lane.
+__device__ __forceinline__ float wave_bcast(float v, int lane) {
+    return readlane_f(v, __builtin_amdgcn_readfirstlane(lane));
+}
+
 // ---------------------------------------------------------------- block level
 // `scratch` must hold at least NT/64 + 1 elements; callers may reuse it right after.
 template <int NT>

@@ -265,7 +265,7 @@ int draft_part_tiles(int V) {
 
 hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
     if (draft_resident_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2))
-        return launch_draft_resident(c, c.sync, st);
+        return launch_draft_resident(c, st);
     if (draft_mfma_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2)) return launch_draft_mfma(c, st);
     StepArgs a;
     a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma; a.nblk = (c.V + kTileCols - 1) / kTileCols;

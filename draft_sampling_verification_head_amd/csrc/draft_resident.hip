@@ -15,21 +15,24 @@
 // Each register holds two consecutive ranks of one column as bf16, 160 registers per
 // lane. The load phase reads each 1280-byte W2 row segment with 16-byte coalesced loads
 // into LDS, and each lane then picks its columns out of it. The products use v_dot2
-// (bf16 x bf16 pairs into fp32). The 8
-// rank-group partial sums of a column meet in LDS and are added in wave order.
+// (bf16 x bf16 pairs into fp32). The 8 rank-group partial sums of a column meet in LDS and
+// are added in wave order.
 //
-// Positions are separated by a grid barrier. Arrivals go to 16 agent-scope counters in the
-// workspace, one per 128-byte line, so that the increments do not serialise on one
-// address. Everything other workgroups read is written with device-scope (sc1) stores, and
-// each thread waits for its own stores before the arrival increment. No L2 write-back fence
-// is used, because that costs tens of microseconds per barrier on this part.
-//
-// After a barrier, wave 0 of every workgroup draws x_k from the published tile partials
-// and logits. It merges the G partials in tile order and rescans the chosen 640-column tile
-// in token order. The workgroup then stages W1[x_k] in LDS for the next position.
-// Workgroup 0 writes x_k, q_k and lse_k. The spin on the counters is bounded. A workgroup that gives up returns, so the
-// launch always drains. If workgroup 0 gives up, it writes the -1 sentinel into the
-// positions it could not draw.
+// Positions meet through their tile partials, with no separate barrier:
+//   - A one-block kernel fills the per-position partial slots with a sentinel before the
+//     launch.
+//   - At position k every workgroup writes its 640 logits with device-scope (sc1) stores,
+//     waits for them (s_waitcnt), then publishes its tile's (max, sum exp) into slot
+//     [k][g] with one 8-byte device-scope store.
+//   - Wave 0 of every workgroup polls the G slots of position k until none holds the
+//     sentinel, and then draws x_k from those partials (in tile order), rescanning the
+//     chosen 640-column tile in token order with device-scope loads.
+// Seeing a workgroup's partial therefore guarantees that its logits are visible. A
+// workgroup publishes position k+1 only after it has finished drawing x_k, so the
+// ping-pong logits rows are never overwritten while another workgroup still reads them.
+// No L2 write-back fence is used, because that costs tens of microseconds per position on
+// this part. Polling is bounded: a workgroup that gives up stops, so the launch always
+// drains, and workgroup 0 then writes the -1 sentinel into the positions it could not draw.
 #include "common.h"
 #include "draw.h"
 #include "kernels.h"
@@ -50,11 +53,12 @@ constexpr int kStageRows = 8;                             // W2 rows per wave pe
 constexpr int kChunks = kResTileCols / 8;                 // 16-byte chunks per row segment
 constexpr int kStageLoads = kStageRows * kChunks / kWave; // uint4 loads per lane per round
 constexpr size_t kResLds = static_cast<size_t>(kRWaves) * kStageRows * kResTileCols * 2;
+constexpr int kPartRegs = RegTiles<kResTileCols>::value;  // partials per lane in the draw
+constexpr int kMaxTiles = kWave * kPartRegs;              // 512 workgroups at most
+constexpr unsigned kSpinMax = 1u << 20;                   // bounded wait, about a second
+constexpr unsigned long long kEmpty = ~0ull;              // sentinel: both halves NaN
 static_assert(kStageLoads * kWave == kStageRows * kChunks, "staging rounds cover whole rows");
 static_assert(kResLds >= sizeof(float) * kRWaves * kResTileCols, "sums fit in the staging area");
-constexpr int kCounters = 16;                             // arrival counters
-constexpr int kCounterStride = 32;                        // uint32 per counter (128 bytes)
-constexpr unsigned kSpinMax = 1u << 20;                   // bounded wait, about a second
 static_assert(kResTileCols == 640 && kRThreads + 128 == kResTileCols, "epilogue ownership");
 
 struct ResArgs {
@@ -68,8 +72,7 @@ struct ResArgs {
     float* q_out;
     float* lse_out;
     float* L[64];             // logits row of position k
-    float2* part[2];          // [G] tile partials of even / odd positions
-    unsigned* sync;           // kCounters arrival counters, kCounterStride apart, zero at launch
+    float2* slots;            // [gamma][G] tile partials, kEmpty until published
 };
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t h, float acc) {
@@ -87,6 +90,11 @@ __device__ __forceinline__ void store_coherent(float2* p, float2 v) {
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ unsigned long long load_slot(const float2* p) {
+    return __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Waits until every store this thread issued has been acknowledged at device scope.
 __device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -100,11 +108,24 @@ void draft_resident(ResArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int V = a.V, r = a.r;
     const long long c0 = static_cast<long long>(blockIdx.x) * kResTileCols;
+    // epilogue columns of this thread: c0 + tid, and c0 + 512 + tid for tid < 128
+    const long long e1 = c0 + tid, e2 = c0 + kRThreads + tid;
+    const bool own2 = tid < kResTileCols - kRThreads;
 
-    // 1. W2 slice: w[i][m] = (W2[32w + 2m][c + i], W2[32w + 2m + 1][c + i]), c = 640g + 10l. Each wave
-    //    issues all of its 32 rows at once as 16-byte coalesced loads of the workgroup's
-    //    1280-byte row segments (V % 8 == 0), then passes them through LDS in 4 rounds of 8
-    //    rows, and every lane picks its 10 columns out of each row as 5 aligned 4-byte words.
+    // 0. what position 0 needs besides W2, issued first: U_0 and the W1 row of x_0
+    int tok0 = a.x0[0];
+    if (tok0 < 0 || tok0 >= V) tok0 = -1;                  // dead request: -inf logits
+    float u1 = (e1 < V) ? a.U[e1] : 0.0f;
+    float u2 = (own2 && e2 < V) ? a.U[e2] : 0.0f;
+    uint4 h0 = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < kResMaxRank / 8 && tok0 >= 0 && 8 * tid < r)
+        h0 = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tok0) * r + 8 * tid);
+
+    // 1. W2 slice: w[i][m] = (W2[32w + 2m][c + i], W2[32w + 2m + 1][c + i]), c = 640g + 10l.
+    //    Each wave issues all of its 32 rows at once as 16-byte coalesced loads of the
+    //    workgroup's 1280-byte row segments (V % 8 == 0), then passes them through LDS in 4
+    //    rounds of 8 rows, and every lane picks its 10 columns out of each row as 5 aligned
+    //    4-byte words.
     uint16_t* stage = reinterpret_cast<uint16_t*>(lds) + wave * (kStageRows * kResTileCols);
     uint32_t w[kLaneCols][kGroupRanks / 2];
     constexpr int kRounds = kGroupRanks / kStageRows;
@@ -120,6 +141,7 @@ void draft_resident(ResArgs a) {
             if (row < r && col < V)
                 v[rho][n] = *reinterpret_cast<const uint4*>(a.W2 + static_cast<long long>(row) * V + col);
         }
+    if (tid < kResMaxRank / 8) reinterpret_cast<uint4*>(hs)[tid] = h0;
 #pragma unroll
     for (int rho = 0; rho < kRounds; ++rho) {
 #pragma unroll
@@ -144,29 +166,12 @@ void draft_resident(ResArgs a) {
     }
     float (*red)[kResTileCols] = reinterpret_cast<float (*)[kResTileCols]>(lds);   // reuses the staging area
 
-    // epilogue columns of this thread: c0 + tid, and c0 + 512 + tid for tid < 128
-    const long long e1 = c0 + tid, e2 = c0 + kRThreads + tid;
-    const bool own2 = tid < kResTileCols - kRThreads;
-    if (tid == 0) {
-        int t = a.x0[0];
-        stok = (t >= 0 && t < V) ? t : -1;                 // dead request: -inf logits
-        gave_up = 0;
-    }
-    __syncthreads();
+    if (tid == 0) gave_up = 0;
+    int tok = tok0;
     int k = 0;
     for (; k < a.gamma; ++k) {
-        const float u1 = (e1 < V) ? a.U[static_cast<long long>(k) * V + e1] : 0.0f;
-        const float u2 = (own2 && e2 < V) ? a.U[static_cast<long long>(k) * V + e2] : 0.0f;
-        const int tok = stok;
-        // 2. h = W1[x_{k-1}] into LDS (r % 8 == 0: whole 8-rank segments)
-        if (tid < kResMaxRank / 8) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (tok >= 0 && 8 * tid < r)
-                v = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tok) * r + 8 * tid);
-            reinterpret_cast<uint4*>(hs)[tid] = v;
-        }
-        __syncthreads();
-        // 3. projection from registers: this wave's 32 ranks of the lane's 10 columns
+        // 2. projection from registers: this wave's 32 ranks of the lane's 10 columns, with
+        //    h = W1[x_{k-1}] from LDS (staged before the last workgroup barrier)
         uint32_t hv[kGroupRanks / 2];
 #pragma unroll
         for (int m = 0; m < kGroupRanks / 2; ++m) hv[m] = hs[(kGroupRanks / 2) * wave + m];
@@ -182,7 +187,7 @@ void draft_resident(ResArgs a) {
         for (int i = 0; i < kLaneCols / 2; ++i)
             reinterpret_cast<float2*>(&red[wave][kLaneCols * lane])[i] = make_float2(acc[2 * i], acc[2 * i + 1]);
         __syncthreads();
-        // 4. logits (rank groups added in wave order), logits row, tile partial
+        // 3. logits (rank groups added in wave order), logits row, tile partial
         const bool live = tok >= 0;
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
@@ -196,13 +201,15 @@ void draft_resident(ResArgs a) {
         float* Lk = a.L[k];
         if (e1 < V) store_coherent(Lk + e1, l1);
         if (own2 && e2 < V) store_coherent(Lk + e2, l2);
-        const float mw = wave_max(fmaxf(l1, l2));
+        const float mw = wave_max_dpp(fmaxf(l1, l2));
         const float ew = (mw == -INFINITY) ? 0.0f
                          : ((l1 == -INFINITY ? 0.0f : __expf(l1 - mw)) +
                             (l2 == -INFINITY ? 0.0f : __expf(l2 - mw)));
-        const float sw = wave_sum(ew);
+        const float sw = wave_sum_dpp(ew);
         if (lane == 0) wpart[wave] = make_float2(mw, sw);
+        drain_stores();                                    // this thread's logits are visible
         __syncthreads();
+        float2* slot = a.slots + static_cast<long long>(k) * a.G;
         if (tid == 0) {
             float m = -INFINITY;
 #pragma unroll
@@ -210,43 +217,53 @@ void draft_resident(ResArgs a) {
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < kRWaves; ++i) s += tile_mass(wpart[i], m);
-            store_coherent(a.part[k & 1] + blockIdx.x, make_float2(m, s));
+            store_coherent(slot + blockIdx.x, make_float2(m, s));   // publishes the tile
         }
-        // 5. grid barrier: own stores acknowledged, arrive, wait for the counters' sum
-        drain_stores();
-        __syncthreads();
+        // U_{k+1} goes out now, so it is in flight while the partials arrive
+        if (k + 1 < a.gamma) {
+            const long long o = static_cast<long long>(k + 1) * V;
+            u1 = (e1 < V) ? a.U[o + e1] : 0.0f;
+            u2 = (own2 && e2 < V) ? a.U[o + e2] : 0.0f;
+        }
+        // 4. wave 0: wait for every tile partial of position k, draw x_k, stage W1[x_k]
         if (wave == 0) {
-            if (lane == 0)
-                __hip_atomic_fetch_add(a.sync + (blockIdx.x % kCounters) * kCounterStride, 1u,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const unsigned target = static_cast<unsigned>(a.G) * static_cast<unsigned>(k + 1);
+            float2 p[kPartRegs];
             unsigned n = 0;
             while (true) {
-                unsigned v = (lane < kCounters)
-                                 ? __hip_atomic_load(a.sync + lane * kCounterStride, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)
-                                 : 0u;
+                bool missing = false;
 #pragma unroll
-                for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);   // same in every lane
-                if (v >= target) break;
+                for (int t = 0; t < kPartRegs; ++t) {
+                    const int i = lane * kPartRegs + t;
+                    unsigned long long bits = 0ull;
+                    if (i < a.G) {
+                        bits = load_slot(slot + i);
+                        missing |= bits == kEmpty;
+                    }
+                    p[t] = (i < a.G) ? __builtin_bit_cast(float2, bits) : make_float2(-INFINITY, 0.0f);
+                }
+                if (!__any(missing)) break;
                 if (++n > kSpinMax) {
                     if (lane == 0) gave_up = 1;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
-            // 6. draw x_k from the published partials and logits
             if (!gave_up) {
                 const DrawOut out{a.x_out + k, a.q_out ? a.q_out + k : nullptr,
                                   a.lse_out ? a.lse_out + k : nullptr, blockIdx.x == 0};
-                const int t = draw_wave<kResTileCols, true>(V, a.part[k & 1], a.G, Lk, a.u[k], out);
+                const int t = draw_regs<kResTileCols, true>(V, p, Lk, a.u[k], out);
                 if (lane == 0) stok = t;
+                if (k + 1 < a.gamma && lane < kResMaxRank / 8) {
+                    uint4 hn = make_uint4(0u, 0u, 0u, 0u);
+                    if (t >= 0 && 8 * lane < r)
+                        hn = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(t) * r + 8 * lane);
+                    reinterpret_cast<uint4*>(hs)[lane] = hn;
+                }
             }
         }
         __syncthreads();
         if (gave_up) break;
-        // the partial buffer of k + 2 reuses this one: no workgroup writes it before every
-        // workgroup has passed the barrier of position k + 1, i.e. finished this draw
+        tok = stok;
     }
     if (gave_up && blockIdx.x == 0 && tid == 0) {
         for (int i = k; i < a.gamma; ++i) {
@@ -257,8 +274,9 @@ void draft_resident(ResArgs a) {
     }
 }
 
-__global__ void zero_counters(unsigned* sync) {
-    if (threadIdx.x < kCounters) sync[threadIdx.x * kCounterStride] = 0u;
+__global__ void clear_slots(unsigned long long* slots, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) slots[i] = kEmpty;
 }
 
 struct DeviceFit {
@@ -283,35 +301,37 @@ DeviceFit device_fit() {
     return f;
 }
 
+int tiles_of(int V) { return (V + kResTileCols - 1) / kResTileCols; }
+
 }  // namespace
 
-int draft_resident_tile_cols() { return kResTileCols; }
-
-size_t draft_resident_sync_bytes() { return kCounters * kCounterStride * sizeof(unsigned); }
+size_t draft_resident_slot_bytes(int V, int gamma) {
+    return static_cast<size_t>(gamma) * tiles_of(V) * sizeof(float2);
+}
 
 bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
     if (B != 1 || w_dtype != 1 || r > kResMaxRank || (r % 8) != 0 || (V % 8) != 0) return false;
     if ((reinterpret_cast<uintptr_t>(W1) % 16) != 0 || (reinterpret_cast<uintptr_t>(W2) % 16) != 0)
         return false;
     const DeviceFit f = device_fit();
-    const long long G = (static_cast<long long>(V) + kResTileCols - 1) / kResTileCols;
-    return f.cus > 0 && f.occupancy >= 1 && G <= f.cus;
+    const int G = tiles_of(V);
+    return f.cus > 0 && f.occupancy >= 1 && G <= f.cus && G <= kMaxTiles;
 }
 
-hipError_t launch_draft_resident(const DraftCall& c, unsigned* sync, hipStream_t st) {
+hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {
     ResArgs a;
     a.V = c.V; a.r = c.r; a.gamma = c.gamma;
-    a.G = (c.V + kResTileCols - 1) / kResTileCols;
+    a.G = tiles_of(c.V);
     a.U = c.U;
     a.W1 = static_cast<const uint16_t*>(c.W1);
     a.W2 = static_cast<const uint16_t*>(c.W2);
     a.x0 = c.x0; a.u = c.u;
     a.x_out = c.x_out; a.q_out = c.q_out; a.lse_out = c.lse_out;
     for (int k = 0; k < c.gamma; ++k) a.L[k] = c.L[k];
-    a.part[0] = c.part[0];
-    a.part[1] = c.part[1];
-    a.sync = sync;
-    hipLaunchKernelGGL(zero_counters, dim3(1), dim3(64), 0, st, sync);
+    a.slots = c.slots;
+    const int n = c.gamma * a.G;
+    hipLaunchKernelGGL(clear_slots, dim3((n + 255) / 256), dim3(256), 0, st,
+                       reinterpret_cast<unsigned long long*>(c.slots), n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(draft_resident, dim3(a.G), dim3(kRThreads), 0, st, a);

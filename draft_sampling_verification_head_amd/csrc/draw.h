@@ -57,7 +57,8 @@ __device__ __forceinline__ void put(const DrawOut& o, int tok, float q, float ls
     if (o.lse) *o.lse = lse;
 }
 
-// In-tile rescan: lane owns TC/64 consecutive columns of `tile`.
+// In-tile rescan: lane owns TC/64 consecutive columns of `tile`. The draw functions run with
+// all 64 lanes of the wave active (their wave-level steps are DPP forms).
 template <int TC, bool COHERENT = false>
 __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__ row, int tile,
                                                 float m, float lse, float tprime,
@@ -74,9 +75,8 @@ __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__
         e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
         local += e[j];
     }
-    const float incl = wave_incl_scan(local);
-    float run = __shfl_up(incl, 1, kWave);
-    if (lane == 0) run = 0.0f;
+    const float incl = wave_incl_scan_dpp(local);
+    float run = wave_shr1_dpp(incl);
     int hit = INT32_MAX, lastpos = -1;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -86,17 +86,69 @@ __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__
             if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(c0 + j);
         }
     }
-    int tok = wave_min_int(hit);
-    if (tok == INT32_MAX) tok = wave_max_int(lastpos);
+    int tok = wave_min_int_dpp(hit);
+    if (tok == INT32_MAX) tok = wave_max_int_dpp(lastpos);
     const int rel = tok - tile * TC;
     const int owner = rel / CPL, jj = rel - owner * CPL;
     float mine = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
         if (j == jj) mine = lv[j];
-    const float lx = __shfl(mine, owner, kWave);
+    const float lx = wave_bcast(mine, owner);
     if (o.write && lane == 0) put(o, tok, __expf(lx - lse), lse);
     return tok;
+}
+
+// The draw from tile partials already in registers: lane l holds tiles
+// [l * RegTiles, (l + 1) * RegTiles), absent tiles as (-inf, 0). Returns the token (-1 for a
+// request with no mass) in every lane; `row` is read only for the in-tile rescan.
+template <int TC, bool COHERENT = false>
+__device__ int draw_regs(int V, const float2 (&p)[RegTiles<TC>::value],
+                         const float* __restrict__ row, float u, const DrawOut& o) {
+    constexpr int kSelRegTiles = RegTiles<TC>::value;
+    const int lane = threadIdx.x & (kWave - 1);
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kSelRegTiles; ++t) m = fmaxf(m, p[t].x);
+    m = wave_max_dpp(m);
+    if (m == -INFINITY) {
+        if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
+        return -1;
+    }
+    float mass[kSelRegTiles];
+    float local = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kSelRegTiles; ++t) {
+        mass[t] = tile_mass(p[t], m);
+        local += mass[t];
+    }
+    const float Z = wave_sum_dpp(local);
+    const float lse = m + __logf(Z);
+    const float target = clamp_uniform(u) * Z;
+    const float incl = wave_incl_scan_dpp(local);
+    float run = wave_shr1_dpp(incl);
+    int hit = INT32_MAX, last = -1;
+    float before = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kSelRegTiles; ++t) {
+        const float nr = run + mass[t];
+        if (mass[t] > 0.0f) {
+            last = lane * kSelRegTiles + t;
+            if (hit == INT32_MAX && nr > target) {
+                hit = lane * kSelRegTiles + t;
+                before = run;
+            }
+        }
+        run = nr;
+    }
+    int found = wave_min_int_dpp(hit);
+    float tprime = INFINITY;
+    if (found == INT32_MAX) {
+        found = wave_max_int_dpp(last);
+    } else {
+        tprime = target - wave_bcast(before, found / kSelRegTiles);
+    }
+    return rescan_tile_wave<TC, COHERENT>(V, row, found, m, lse, tprime, o);
 }
 
 // One wave draws one request's token; returns it (-1 for a dead request) in every lane.
@@ -105,10 +157,6 @@ __device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
                          const float* __restrict__ row, float u, const DrawOut& o) {
     constexpr int kSelRegTiles = RegTiles<TC>::value;
     const int lane = threadIdx.x & (kWave - 1);
-    float m = -INFINITY;
-    float Z, lse, target;
-    int found = -1;
-    float tprime = INFINITY;
     if (nblk <= kWave * kSelRegTiles) {
         // register form: lane l holds tiles [l * kSelRegTiles, (l + 1) * kSelRegTiles)
         float2 p[kSelRegTiles];
@@ -117,82 +165,44 @@ __device__ int draw_wave(int V, const float2* __restrict__ P, int nblk,
             const int i = lane * kSelRegTiles + t;
             p[t] = (i < nblk) ? load_part<COHERENT>(P + i) : make_float2(-INFINITY, 0.0f);
         }
-#pragma unroll
-        for (int t = 0; t < kSelRegTiles; ++t) m = fmaxf(m, p[t].x);
-        m = wave_max(m);
-        if (m == -INFINITY) {
-            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
-            return -1;
+        return draw_regs<TC, COHERENT>(V, p, row, u, o);
+    }
+    // loop form for vocabularies with more tiles than the registers hold
+    float m = -INFINITY;
+    for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, load_part<COHERENT>(P + i).x);
+    m = wave_max(m);
+    if (m == -INFINITY) {
+        if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
+        return -1;
+    }
+    float z = 0.0f;
+    for (int i = lane; i < nblk; i += kWave) z += tile_mass(load_part<COHERENT>(P + i), m);
+    const float Z = wave_sum(z);
+    const float lse = m + __logf(Z);
+    const float target = clamp_uniform(u) * Z;
+    int found = -1;
+    float tprime = INFINITY;
+    float run = 0.0f;
+    for (int base = 0; base < nblk; base += kWave) {
+        const int i = base + lane;
+        const float v = (i < nblk) ? tile_mass(load_part<COHERENT>(P + i), m) : 0.0f;
+        const float incl = wave_incl_scan(v);
+        float excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 0.0f;
+        const unsigned long long hit = __ballot((i < nblk) && (v > 0.0f) && (run + incl > target));
+        if (hit) {
+            const int f = __ffsll(static_cast<long long>(hit)) - 1;
+            found = base + f;
+            tprime = target - (run + __shfl(excl, f, kWave));
+            break;
         }
-        float mass[kSelRegTiles];
-        float local = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kSelRegTiles; ++t) {
-            mass[t] = tile_mass(p[t], m);
-            local += mass[t];
-        }
-        Z = wave_sum(local);
-        lse = m + __logf(Z);
-        target = clamp_uniform(u) * Z;
-        const float incl = wave_incl_scan(local);
-        float run = __shfl_up(incl, 1, kWave);
-        if (lane == 0) run = 0.0f;
-        int hit = INT32_MAX, last = -1;
-        float before = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kSelRegTiles; ++t) {
-            const float nr = run + mass[t];
-            if (mass[t] > 0.0f) {
-                last = lane * kSelRegTiles + t;
-                if (hit == INT32_MAX && nr > target) {
-                    hit = lane * kSelRegTiles + t;
-                    before = run;
-                }
-            }
-            run = nr;
-        }
-        found = wave_min_int(hit);
-        if (found == INT32_MAX) {
-            found = wave_max_int(last);
-        } else {
-            tprime = target - __shfl(before, found / kSelRegTiles, kWave);
-        }
-    } else {
-        // loop form for vocabularies with more tiles than the registers hold
-        for (int i = lane; i < nblk; i += kWave) m = fmaxf(m, load_part<COHERENT>(P + i).x);
-        m = wave_max(m);
-        if (m == -INFINITY) {
-            if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
-            return -1;
-        }
-        float z = 0.0f;
-        for (int i = lane; i < nblk; i += kWave) z += tile_mass(load_part<COHERENT>(P + i), m);
-        Z = wave_sum(z);
-        lse = m + __logf(Z);
-        target = clamp_uniform(u) * Z;
-        float run = 0.0f;
-        for (int base = 0; base < nblk; base += kWave) {
-            const int i = base + lane;
-            const float v = (i < nblk) ? tile_mass(load_part<COHERENT>(P + i), m) : 0.0f;
-            const float incl = wave_incl_scan(v);
-            float excl = __shfl_up(incl, 1, kWave);
-            if (lane == 0) excl = 0.0f;
-            const unsigned long long hit =
-                __ballot((i < nblk) && (v > 0.0f) && (run + incl > target));
-            if (hit) {
-                const int f = __ffsll(static_cast<long long>(hit)) - 1;
-                found = base + f;
-                tprime = target - (run + __shfl(excl, f, kWave));
-                break;
-            }
-            run += __shfl(incl, kWave - 1, kWave);
-        }
-        if (found < 0) {
-            int last = -1;
-            for (int i = lane; i < nblk; i += kWave)
-                if (tile_mass(load_part<COHERENT>(P + i), m) > 0.0f) last = i;
-            found = wave_max_int(last);
-        }
+        run += __shfl(incl, kWave - 1, kWave);
+    }
+    if (found < 0) {
+        int last = -1;
+        for (int i = lane; i < nblk; i += kWave)
+            if (tile_mass(load_part<COHERENT>(P + i), m) > 0.0f) last = i;
+        found = wave_max_int(last);
     }
     return rescan_tile_wave<TC, COHERENT>(V, row, found, m, lse, tprime, o);
 }

@@ -21,7 +21,7 @@ struct DraftCall {
     float* L[64];             // logits rows of step k: L[k] + b * L_bstride
     long long L_bstride;
     float2* part[2];          // tile partials [B][draft_part_tiles(V)] of even / odd steps
-    unsigned* sync;           // draft_resident_sync_bytes() of workspace (single-launch barrier)
+    float2* slots;            // draft_resident_slot_bytes(V, gamma) of workspace (single launch)
 };
 
 // Vocabulary tiles per request the partial buffers must hold (the finest tiling in use).
@@ -37,8 +37,8 @@ hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st);
 // launch_draft when it applies: one launch covers all gamma positions.
 bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
 int draft_resident_tile_cols();
-size_t draft_resident_sync_bytes();
-hipError_t launch_draft_resident(const DraftCall& c, unsigned* sync, hipStream_t st);
+size_t draft_resident_slot_bytes(int V, int gamma);
+hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st);
 
 // ---------------------------------------------------------------- verify / TV
 struct RowSet {               // the draft and target rows of a verify batch
