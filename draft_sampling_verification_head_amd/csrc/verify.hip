@@ -129,18 +129,21 @@ __device__ __forceinline__ void block_ms(float& m, float& s, float (*sm)[kWaves]
     __syncthreads();
 }
 
-// lse of one row from its chunk partials, merged by one wave (max first, then the scaled
-// sums in lane-strided order and a butterfly); the same value in every lane.
+// lse of one row from its chunk partials, merged by one wave with all lanes active (max
+// first, then the scaled sums in lane-strided order and a fixed-order wave sum); the same
+// value in every lane.
 __device__ __forceinline__ float merge_lse_wave(const float2* __restrict__ P, int nch) {
     const int lane = threadIdx.x & (kWave - 1);
     float mm = -INFINITY;
-    for (int i = lane; i < nch; i += kWave) mm = fmaxf(mm, P[i].x);
-    mm = wave_max(mm);
+    float2 p0 = make_float2(-INFINITY, 0.0f);
+    if (lane < nch) p0 = P[lane];
+    for (int i = lane + kWave; i < nch; i += kWave) mm = fmaxf(mm, P[i].x);
+    mm = wave_max_dpp(fmaxf(mm, p0.x));
     if (mm == -INFINITY) return -INFINITY;
-    float ss = 0.0f;
-    for (int i = lane; i < nch; i += kWave)
+    float ss = (p0.x == -INFINITY) ? 0.0f : p0.y * __expf(p0.x - mm);
+    for (int i = lane + kWave; i < nch; i += kWave)
         ss += (P[i].x == -INFINITY) ? 0.0f : P[i].y * __expf(P[i].x - mm);
-    ss = wave_sum(ss);
+    ss = wave_sum_dpp(ss);
     return mm + __logf(ss);
 }
 
@@ -351,30 +354,29 @@ void verify_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
         if (tid < kWave) {
             float tot = 0.0f;
             for (int i = tid; i < nch; i += kWave) tot += cs[i];
-            tot = wave_sum(tot);
+            tot = wave_sum_dpp(tot);
             const float target = uf * tot;
             int found = -1;
             float tprime = INFINITY, run = 0.0f;
             for (int base = 0; base < nch && found < 0; base += kWave) {
                 const int i = base + tid;
                 const float v = (i < nch) ? cs[i] : 0.0f;
-                const float incl = wave_incl_scan(v);
-                float excl = __shfl_up(incl, 1, kWave);
-                if (tid == 0) excl = 0.0f;
+                const float incl = wave_incl_scan_dpp(v);
+                const float excl = wave_shr1_dpp(incl);
                 const unsigned long long hit =
                     __ballot((i < nch) && (v > 0.0f) && (run + incl > target));
                 if (hit) {
                     const int f = __ffsll(static_cast<long long>(hit)) - 1;
                     found = base + f;
-                    tprime = target - (run + __shfl(excl, f, kWave));
+                    tprime = target - (run + wave_bcast(excl, f));
                 }
-                run += __shfl(incl, kWave - 1, kWave);
+                run += wave_bcast(incl, kWave - 1);
             }
             if (found < 0 && tot > 0.0f) {      // rounding left the target past the end
                 int last = -1;
                 for (int i = tid; i < nch; i += kWave)
                     if (cs[i] > 0.0f) last = i;
-                found = wave_max_int(last);
+                found = wave_max_int_dpp(last);
                 tprime = INFINITY;
             }
             if (tid == 0) {
@@ -484,7 +486,7 @@ void tv_merge_kernel(RowSet rs, int nch, const float* __restrict__ psum,
     const bool live = q.ok && k < q.ell;
     if (live)
         for (int i = lane; i < nch; i += kWave) s += psum[pair * nch + i];
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
     if (lane == 0) cstar[pair] = live ? s : qnan();
 }
 

@@ -59,6 +59,7 @@ def test_brute_force_tiny(gpu):
 @pytest.mark.parametrize("R,G,Bmax", [
     (1, 1, 1), (1, 1, 2), (3, 5, 3), (1024, 16, 20000), (16384, 1, 20000), (256, 64, 5000),
     (700, 7, 2100), (1, 64, 100),
+    (4, 16, 200), (8, 8, 9), (5, 13, 200),   # 64 and 65 candidates: both sides of the one-wave path
 ])
 def test_shapes_and_caps(gpu, R, G, Bmax):
     c = synth.custom(960 + R % 101, B=R, V=8, r=1, gamma=G)
