@@ -6,14 +6,23 @@
 // "DSpark Speculative Decoding".)
 //
 // Used when a batch is large enough for the product to be a dense GEMM (B > 8 requests,
-// bf16 factors). Workgroup = 64 requests x 256 vocabulary columns, 8 waves; wave w owns
-// columns [32w, 32w + 32) and both 32-request halves, accumulating with
-// v_mfma_f32_32x32x16_bf16 in fp32. The gathered W1 rows (A operand, rank-contiguous) sit in
-// LDS for the whole workgroup; W2 (B operand) streams through LDS in 16-row chunks, double
-// buffered, in its natural [r][V] layout, and each lane picks its 8 rank values of one
-// column with 2-byte LDS reads. The epilogue adds U_k, stores the logits and reduces each
-// request row of the tile to a (max, sum exp) partial for the draw. Workgroups are mapped so
-// that the request groups of one vocabulary tile run on the same XCD (shared L2).
+// bf16 factors). Workgroup = 64 requests x 256 vocabulary columns, 8 waves that run
+// independently after the W1 rows of the 64 requests (the A operand, rank-contiguous) are
+// gathered into LDS:
+//   - Wave w owns columns [32w, 32w + 32) and both 32-request halves, accumulating
+//     v_mfma_f32_32x32x16_bf16 in fp32.
+//   - Its B operand streams from HBM as one 16-byte load per lane per 16-rank chunk (W2's
+//     natural [r][V] layout). Each chunk passes through a wave-private LDS area that turns
+//     it into the fragment layout, so no workgroup barrier is needed. Two chunks stay in
+//     flight per wave.
+//   - U_k for the wave's 64 x 32 tile is loaded first, together with the first chunks.
+// The epilogue adds U_k, stores the logits, and reduces each request row to (max, sum exp):
+//   - a 31-step reduce-scatter butterfly across the 32 lanes of a half-wave (ds_swizzle for
+//     lane distance 16, then DPP row rotate, half-row mirror and quad swaps), after which
+//     lane l32 holds one row;
+//   - the 8 waves' row results are then merged in wave order through LDS.
+// Workgroups are mapped so that the request groups of one vocabulary tile run on the same
+// XCD (shared L2).
 #include "common.h"
 #include "draw.h"
 #include "kernels.h"
@@ -23,7 +32,6 @@ namespace dspark {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMT = 64;                 // requests per workgroup
@@ -31,9 +39,13 @@ constexpr int kNT = 256;                // vocabulary columns per workgroup
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kKC = 16;                 // rank rows per W2 chunk (one MFMA k-step)
-constexpr int kWS = kNT + 4;            // W2 chunk row stride (bf16), padded against bank conflicts
 constexpr int kHPad = 8;                // H row padding (bf16)
+constexpr int kWS = 40;                 // row stride (bf16) of a wave's W2 chunk in LDS
 constexpr int kXcds = 8;
+constexpr int kPF = 2;                  // W2 chunks in flight per wave
+constexpr int kMaxRank = 256;           // rank the A operand staging covers
+constexpr int kHSeg = kMT * kMaxRank / 8 / kThreads;   // 16-byte W1 segments per thread
+static_assert(kHSeg * kThreads * 8 == kMT * kMaxRank, "W1 gather covers 64 rows of rank kMaxRank");
 static_assert(kWaves * 32 == kNT, "one 32-column MFMA tile per wave");
 
 struct MfmaArgs {
@@ -48,12 +60,46 @@ struct MfmaArgs {
     float2* part;             // [B][ntiles] (max, sum exp) per request and tile
 };
 
-__global__ __launch_bounds__(kThreads, 2)
+// Row of accumulator element v of half-tile h, for the lane half hf = lane / 32.
+__device__ __forceinline__ int acc_row(int h, int v, int hf) {
+    return 32 * h + 8 * (v / 4) + 4 * hf + (v % 4);
+}
+
+__device__ __forceinline__ float swz_xor16(float v) {   // lane ^ 16 within each 32 lanes
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+// Reduce-scatter across the 32 lanes of a half-wave: x[rho] is this lane's value of row
+// index rho; the result is row index (lane & 31) reduced over the 32 lanes. Each step keeps
+// the upper half of the values when the lane's bit is set and receives the partner's copy
+// of the kept half; the partner of every step agrees with the lane on all bits handled
+// before and differs on the current one.
+template <class Op>
+__device__ __forceinline__ float reduce_scatter32(const float (&x)[32], Op op) {
+    const int l = threadIdx.x & 31;
+    float a16[16], a8[8], a4[4], a2[2];
+    const bool b4 = l & 16, b3 = l & 8, b2 = l & 4, b1 = l & 2, b0 = l & 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        a16[i] = op(b4 ? x[i + 16] : x[i], swz_xor16(b4 ? x[i] : x[i + 16]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)                                     // row_ror 8: lane ^ 8
+        a8[i] = op(b3 ? a16[i + 8] : a16[i], dpp_f<0x128>(b3 ? a16[i] : a16[i + 8]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)                                     // half-row mirror
+        a4[i] = op(b2 ? a8[i + 4] : a8[i], dpp_f<0x141>(b2 ? a8[i] : a8[i + 4]));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)                                     // quad lane ^ 2
+        a2[i] = op(b1 ? a4[i + 2] : a4[i], dpp_f<0x4E>(b1 ? a4[i] : a4[i + 2]));
+    return op(b0 ? a2[1] : a2[0], dpp_f<0xB1>(b0 ? a2[0] : a2[1]));  // quad lane ^ 1
+}
+
+__global__ __launch_bounds__(kThreads, 4)      // 4 waves per SIMD: two workgroups per CU
 void draft_step_mfma(MfmaArgs a) {
     extern __shared__ uint16_t sm16[];
     const int HS = a.rp + kHPad;
     uint16_t* Hs = sm16;                              // [kMT][HS] gathered W1 rows
-    uint16_t* Ws = sm16 + kMT * HS;                   // [2][kKC][kWS] W2 chunks
+    uint16_t* Ws = sm16 + kMT * HS;                   // [kWaves][kKC][kWS] W2 chunk per wave
     __shared__ float red[kWaves][kMT];
     __shared__ float rowmax[kMT];
     __shared__ int stok[kMT];
@@ -65,7 +111,42 @@ void draft_step_mfma(MfmaArgs a) {
     if (tile >= a.ntiles) return;
     const int m0 = mg * kMT;
     const long long n0 = static_cast<long long>(tile) * kNT;
+    const int hf = lane >> 5, l32 = lane & 31;
+    const long long col = n0 + wave * 32 + l32;
+    const bool colok = col < a.V;
 
+    // 1. loads that do not depend on the tokens: U_k of the wave's tile, first W2 chunks.
+    //    B fragment of chunk c: ranks 16c + 8hf .. +8 of column `col`, two per register.
+    // 32-bit element offsets from workgroup-uniform bases (the host checks they fit)
+    const float* Ub = a.U + (static_cast<long long>(m0) * a.gamma + a.k) * a.V;
+    const uint32_t urow = static_cast<uint32_t>(a.gamma) * static_cast<uint32_t>(a.V);
+    const uint32_t c32 = static_cast<uint32_t>(col);
+    float lv[32];                                      // U_k, then the logits
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = acc_row(h, v, hf);
+            lv[16 * h + v] = (colok && m0 + i < a.B) ? Ub[static_cast<uint32_t>(i) * urow + c32] : 0.0f;
+        }
+    // W2 chunk c as one 16-byte load per lane: rank 16c + lane / 4, 8 columns starting at
+    // 32w + 8 (lane % 4)
+    const uint32_t V32 = static_cast<uint32_t>(a.V);
+    const int wq = lane >> 2, wcol = (lane & 3) * 8;
+    const long long gcol = n0 + wave * 32 + wcol;
+    auto load_w = [&](int c) {
+        const int kk = kKC * c + wq;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (kk < a.r && gcol < a.V)
+            v = *reinterpret_cast<const uint4*>(a.W2 + (static_cast<uint32_t>(kk) * V32 + static_cast<uint32_t>(gcol)));
+        return v;
+    };
+    const int nkc = a.rp / kKC;
+    uint4 gq[kPF];
+#pragma unroll
+    for (int d = 0; d < kPF; ++d) gq[d] = (d < nkc) ? load_w(d) : make_uint4(0u, 0u, 0u, 0u);
+
+    // 2. tokens and the gathered W1 rows (A operand: zero beyond r and for dead / absent requests)
     if (tid < kMT) {
         const int b = m0 + tid;
         int t = -1;
@@ -76,117 +157,94 @@ void draft_step_mfma(MfmaArgs a) {
         stok[tid] = t;
     }
     __syncthreads();
-    // A operand: the gathered W1 rows, zero beyond r and for dead / absent requests
-    const int segs = a.rp / 8;
-    for (int s = tid; s < kMT * segs; s += kThreads) {
-        const int i = s / segs, c = (s % segs) * 8;
-        const int t = stok[i];
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (t >= 0 && c < a.r) v = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(t) * a.r + c);
-        *reinterpret_cast<uint4*>(Hs + i * HS + c) = v;
+    const int segs = a.rp / 8;                         // rp <= 256: at most kHSeg per thread
+#pragma unroll
+    for (int q = 0; q < kHSeg; ++q) {
+        const int s = tid + q * kThreads;
+        if (s < kMT * segs) {
+            const int i = s / segs, c = (s % segs) * 8;
+            const int t = stok[i];
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (t >= 0 && c < a.r) v = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(t) * a.r + c);
+            *reinterpret_cast<uint4*>(Hs + i * HS + c) = v;
+        }
     }
-    // W2 chunk kc -> registers: thread t holds row t/32, columns 8*(t%32) .. +8
-    const int wrow = tid >> 5, wcol = (tid & 31) * 8;
-    auto load_chunk = [&](int kc) {
-        const int kk = kc * kKC + wrow;
-        const long long col = n0 + wcol;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (kk < a.r && col < a.V) v = *reinterpret_cast<const uint4*>(a.W2 + static_cast<long long>(kk) * a.V + col);
-        return v;
-    };
-    auto store_chunk = [&](int buf, uint4 v) {
-        uint16_t* dst = Ws + (buf * kKC + wrow) * kWS + wcol;
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
-        reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
-    };
-    store_chunk(0, load_chunk(0));
     __syncthreads();
 
+    // 3. K loop, wave-local: kPF chunks in flight in a statically indexed register ring; each
+    //    chunk passes through the wave's own LDS area (row-major, 16 ranks x 32 columns) to
+    //    become the B fragment (ranks 8hf .. 8hf+7 of column l32). LDS accesses of one wave
+    //    execute in order, so no barrier is needed.
+    uint16_t* ws = Ws + wave * (kKC * kWS);
     f32x16 acc0 = {}, acc1 = {};
-    const int nkc = a.rp / kKC;
-    const int half = lane >> 5, l32 = lane & 31;
-    for (int kc = 0; kc < nkc; ++kc) {
-        const int cur = kc & 1;
-        uint4 nxt = make_uint4(0u, 0u, 0u, 0u);
-        if (kc + 1 < nkc) nxt = load_chunk(kc + 1);   // in flight during the MFMAs
-        // B fragment: column 32*wave + l32, rank rows 8*half .. +8 of the chunk
-        const uint16_t* wc = Ws + (cur * kKC + 8 * half) * kWS + wave * 32 + l32;
-        s16x8 bv;
+    for (int kc0 = 0; kc0 < nkc; kc0 += kPF) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = static_cast<short>(wc[e * kWS]);
-        const bf16x8 bfrag = __builtin_bit_cast(bf16x8, bv);
-        // A fragments: request rows l32 and 32 + l32, the same 8 rank values
-        const int kofs = kc * kKC + 8 * half;
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Hs + l32 * HS + kofs));
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Hs + (32 + l32) * HS + kofs));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfrag, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfrag, acc1, 0, 0, 0);
-        if (kc + 1 < nkc) store_chunk(cur ^ 1, nxt);
-        __syncthreads();
+        for (int d = 0; d < kPF; ++d) {
+            const int kc = kc0 + d;
+            if (kc < nkc) {
+                const uint4 g = gq[d];
+                if (kc + kPF < nkc) gq[d] = load_w(kc + kPF);
+                uint2* dst = reinterpret_cast<uint2*>(ws + wq * kWS + wcol);
+                dst[0] = make_uint2(g.x, g.y);
+                dst[1] = make_uint2(g.z, g.w);
+                const uint16_t* src = ws + (8 * hf) * kWS + l32;
+                uint32_t bv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bv[e] = static_cast<uint32_t>(src[(2 * e) * kWS]) |
+                            (static_cast<uint32_t>(src[(2 * e + 1) * kWS]) << 16);
+                const bf16x8 bfrag = __builtin_bit_cast(bf16x8, make_uint4(bv[0], bv[1], bv[2], bv[3]));
+                const int kofs = kc * kKC + 8 * hf;
+                const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Hs + l32 * HS + kofs));
+                const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Hs + (32 + l32) * HS + kofs));
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfrag, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfrag, acc1, 0, 0, 0);
+            }
+        }
     }
 
-    // epilogue: element v of the accumulator of half-tile h is request row
-    // 32h + 8(v/4) + 4*half + v%4, column 32*wave + l32
-    const long long col = n0 + wave * 32 + l32;
-    const bool colok = col < a.V;
-    float lv[32];
+    // 4. epilogue: logits, stores, per-row (max, sum exp) over the workgroup's 256 columns
+    float* Lb = a.L + static_cast<long long>(m0) * a.L_bstride;
+    const uint32_t lrow = static_cast<uint32_t>(a.L_bstride);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int i = 32 * h + 8 * (v / 4) + 4 * half + (v % 4);
+            const int i = acc_row(h, v, hf);
             const int b = m0 + i;
             const bool live = colok && b < a.B && stok[i] >= 0;
             const float accv = h ? acc1[v] : acc0[v];
-            lv[16 * h + v] = live ? a.U[(static_cast<long long>(b) * a.gamma + a.k) * a.V + col] + accv
-                                  : -INFINITY;
+            lv[16 * h + v] = live ? lv[16 * h + v] + accv : -INFINITY;
+            if (colok && b < a.B) Lb[static_cast<uint32_t>(i) * lrow + c32] = lv[16 * h + v];
         }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = 32 * h + 8 * (v / 4) + 4 * half + (v % 4);
-            const int b = m0 + i;
-            if (colok && b < a.B) a.L[b * a.L_bstride + col] = lv[16 * h + v];
-        }
-    // per request row: max over the tile (lanes of a half, then waves in order)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float m = lv[16 * h + v];
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-            if (l32 == 0) red[wave][32 * h + 8 * (v / 4) + 4 * half + (v % 4)] = m;
-        }
+    const int myrow = acc_row(l32 >> 4, l32 & 15, hf);  // row index l32 of this lane's half
+    float m = reduce_scatter32(lv, OpMax{});
+    red[wave][myrow] = m;
     __syncthreads();
     if (tid < kMT) {
-        float m = red[0][tid];
+        float mm = red[0][tid];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][tid]);
-        rowmax[tid] = m;
+        for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, red[w][tid]);
+        rowmax[tid] = mm;
     }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int i = 32 * h + 8 * (v / 4) + 4 * half + (v % 4);
-            const float m = rowmax[i];
             const float x = lv[16 * h + v];
-            float e = (x == -INFINITY) ? 0.0f : __expf(x - m);
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) e += __shfl_xor(e, o, kWave);
-            if (l32 == 0) red[wave][i] = e;
+            lv[16 * h + v] = (x == -INFINITY) ? 0.0f : __expf(x - rowmax[acc_row(h, v, hf)]);
         }
+    const float s = reduce_scatter32(lv, OpSum{});
+    red[wave][myrow] = s;
     __syncthreads();
     if (tid < kMT) {
         const int b = m0 + tid;
         if (b < a.B) {
-            float s = red[0][tid];
+            float ss = red[0][tid];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) s += red[w][tid];
-            a.part[static_cast<long long>(b) * a.ntiles + tile] = make_float2(rowmax[tid], s);
+            for (int w = 1; w < kWaves; ++w) ss += red[w][tid];
+            a.part[static_cast<long long>(b) * a.ntiles + tile] = make_float2(rowmax[tid], ss);
         }
     }
 }
@@ -196,7 +254,10 @@ void draft_step_mfma(MfmaArgs a) {
 int draft_mfma_tile_cols() { return kNT; }
 
 bool draft_mfma_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
-    return w_dtype == 1 && B > 8 && r <= 256 && (r % 8) == 0 && (V % 8) == 0 &&
+    // element offsets inside W2 and inside 64 requests' rows of U / L_d stay below 2^32
+    const long long span = static_cast<long long>(kMT) * 64 * V;   // gamma <= 64
+    return w_dtype == 1 && B > 8 && r <= kMaxRank && (r % 8) == 0 && (V % 8) == 0 &&
+           static_cast<long long>(kMaxRank) * V < (1LL << 32) && span < (1LL << 32) &&
            (reinterpret_cast<uintptr_t>(W1) % 16) == 0 && (reinterpret_cast<uintptr_t>(W2) % 16) == 0;
 }
 
@@ -213,7 +274,7 @@ hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st) {
     a.L_bstride = c.L_bstride;
     const unsigned grid_tiles = static_cast<unsigned>((a.ntiles + kXcds - 1) / kXcds * kXcds);
     const dim3 grid(grid_tiles * a.mgroups);
-    const size_t smem = (static_cast<size_t>(kMT) * (a.rp + kHPad) + 2 * kKC * kWS) * sizeof(uint16_t);
+    const size_t smem = (static_cast<size_t>(kMT) * (a.rp + kHPad) + kWaves * kKC * kWS) * sizeof(uint16_t);
     const int waves = kSelThreads / kWave;
     for (int k = 0; k < c.gamma; ++k) {
         if (k > 0) {
