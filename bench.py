@@ -43,11 +43,11 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
     ("single", "draft_resident"): dict(
-        bytes=87223243.0,
+        bytes=87291618.0,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
-        sources={"draft_resident.hip": "682bcf714d79396666e448c71696e1dbf3b865c181e549572ed41b30490585c3",
-                 "draw.h": "12a3facce0ee750fa340bb90c5245304d707a343b6ba4cb89f46436ecf8b4f09",
-                 "common.h": "739a5e62ecf98417fbae5c9345a0180ded0f8e56c092c2fffa7484408e8627f4"}),
+        sources={"draft_resident.hip": "bca35370d74d6723c8eca0d01c55009e66855f4e33f82bef3537403917327cf1",
+                 "draw.h": "1176839c2edc2f5bb830cb6cd198946f040c954242ee8c435ee65da753590588",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("single", "draft_step_gemv"): dict(
         bytes=79281052.0,
         profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
