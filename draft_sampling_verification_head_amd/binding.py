@@ -24,6 +24,7 @@ EXPORTS = (
     "dspark_status_string", "dspark_last_error", "dspark_version",
     "dspark_markov_draft_path", "dspark_markov_draft_workspace_bytes", "dspark_markov_draft",
     "dspark_verify_workspace_bytes", "dspark_verify",
+    "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
     "dspark_tv_labels_workspace_bytes", "dspark_tv_labels",
     "dspark_schedule_workspace_bytes", "dspark_schedule",
 )
@@ -41,6 +42,8 @@ _SIGS = {
     "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_verify_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_verify": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_verify_tv_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dspark_verify_tv": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_tv_labels_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_tv_labels": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_schedule_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -169,9 +172,10 @@ def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=Fa
 
 
 def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, want_lse=False,
-           out=None, stream=None):
-    """dspark_verify. Ld [B][gamma][V], Lt [rows][V] fp32; x, u_acc [B][gamma]; u_fin [B].
-    Returns dict n [B], y [B][gamma+1] (and lse_d, lse_t when want_lse)."""
+           out=None, stream=None, with_tv=False):
+    """dspark_verify (dspark_verify_tv when with_tv). Ld [B][gamma][V], Lt [rows][V] fp32;
+    x, u_acc [B][gamma]; u_fin [B]. Returns dict n [B], y [B][gamma+1] (and lse_d, lse_t when
+    want_lse; cstar [B][gamma] when with_tv)."""
     torch = _torch()
     lib = load()
     B, G, V = Ld.shape
@@ -201,6 +205,17 @@ def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, wan
         _need(lse_d, "lse_d", torch.float32, (B, G), dev)
     if lse_t is not None:
         _need(lse_t, "lse_t", torch.float32, (B, G + 1), dev)
+    if with_tv:
+        cstar = o.get("cstar") if o.get("cstar") is not None else torch.empty((B, G), dtype=torch.float32, device=dev)
+        _need(cstar, "cstar", torch.float32, (B, G), dev)
+        nbytes = lib.dspark_verify_tv_workspace_bytes(B, V, G)
+        ws = workspace(nbytes, dev, "verify_tv")
+        st = lib.dspark_verify_tv(B, V, G, _ptr(Ld), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
+                                  _ptr(length), _ptr(x), _ptr(ld_lse), _ptr(u_acc), _ptr(u_fin),
+                                  _ptr(n), _ptr(y), _ptr(lse_d), _ptr(lse_t), _ptr(cstar),
+                                  _ptr(ws), ws.numel(), _stream(stream))
+        _check(st, "dspark_verify_tv")
+        return dict(n=n, y=y, lse_d=lse_d, lse_t=lse_t, cstar=cstar)
     nbytes = lib.dspark_verify_workspace_bytes(B, V, G)
     ws = workspace(nbytes, dev, "verify")
     st = lib.dspark_verify(B, V, G, _ptr(Ld), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),

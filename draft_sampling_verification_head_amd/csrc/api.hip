@@ -192,6 +192,40 @@ int dspark_verify(int B, int V, int gamma, const float* Ld, const float* Lt, int
     return ok();
 }
 
+size_t dspark_verify_tv_workspace_bytes(int B, int V, int gamma) {
+    if (B < 1 || V < 1 || gamma < 1) return 0;
+    return dspark_verify_workspace_bytes(B, V, gamma) +
+           align_up(static_cast<size_t>(B) * gamma * row_chunks(V) * sizeof(float));
+}
+
+int dspark_verify_tv(int B, int V, int gamma, const float* Ld, const float* Lt, int Lt_rows,
+                     const int32_t* t_off, const int32_t* len, const int32_t* x,
+                     const float* ld_lse, const float* u_acc, const float* u_fin,
+                     int32_t* n_acc_out, int32_t* y_out, float* lse_d_out, float* lse_t_out,
+                     float* cstar_out, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_rows("verify_tv", B, V, gamma, Ld, Lt, Lt_rows, t_off);
+    if (rc != DSPARK_OK) return rc;
+    if (!x || !u_acc || !u_fin || !n_acc_out || !y_out || !cstar_out)
+        return fail(DSPARK_ERR_INVALID_ARG, "verify_tv: a required pointer is NULL");
+    const size_t need = dspark_verify_tv_workspace_bytes(B, V, gamma);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "verify_tv: workspace %zu bytes, need %zu", ws_bytes,
+                    need);
+    Carver c(ws);
+    float2* part = c.take<float2>(static_cast<size_t>(B) * (2 * gamma + 1) * row_chunks(V));
+    float* csum = c.take<float>(static_cast<size_t>(B) * row_chunks(V));
+    char* state = c.take<char>(static_cast<size_t>(B) * dspark::verify_state_bytes());
+    float* psum = c.take<float>(static_cast<size_t>(B) * gamma * row_chunks(V));
+    dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = dspark::launch_row_stats(rs, ld_lse, part, st);
+    if (e != hipSuccess) return hip_fail(e, "verify_tv/row_stats");
+    e = dspark::launch_verify_tv(rs, x, part, ld_lse, u_acc, u_fin, lse_d_out, lse_t_out, csum,
+                                 state, psum, n_acc_out, y_out, cstar_out, st);
+    if (e != hipSuccess) return hip_fail(e, "verify_tv");
+    return ok();
+}
+
 size_t dspark_tv_labels_workspace_bytes(int B, int V, int gamma) {
     if (B < 1 || V < 1 || gamma < 1) return 0;
     return part_bytes(B, V, gamma) +

@@ -65,6 +65,14 @@ hipError_t launch_verify(const RowSet& rs, const int32_t* x, const float2* part,
                          float* lse_d_out, float* lse_t_out, float* csum, void* state,
                          int32_t* n_out, int32_t* y_out, hipStream_t st);
 
+// Verify and TV labels together, after launch_row_stats: two launches instead of four.
+// psum: [B][gamma][nch].
+hipError_t launch_verify_tv(const RowSet& rs, const int32_t* x, const float2* part,
+                            const float* lse_d_in, const float* u_acc, const float* u_fin,
+                            float* lse_d_out, float* lse_t_out, float* csum, void* state,
+                            float* psum, int32_t* n_out, int32_t* y_out, float* cstar,
+                            hipStream_t st);
+
 // TV labels; normalisers from lse_d / lse_t when given, else merged from `part`.
 // psum: [B][gamma][nch].
 hipError_t launch_tv(const RowSet& rs, const float* lse_d, const float* lse_t,

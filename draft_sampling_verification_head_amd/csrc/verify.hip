@@ -225,18 +225,17 @@ struct ReqState {
 };
 
 template <bool VEC4>
-__global__ __launch_bounds__(kThreads)
-void verify_chunks_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
-                          const float2* __restrict__ part, const float* __restrict__ lse_d_in,
-                          const float* __restrict__ u_acc, float* __restrict__ lse_d_out,
-                          float* __restrict__ lse_t_out, float* __restrict__ csum,
-                          ReqState* __restrict__ state) {
+__device__ __forceinline__ void verify_chunks_body(const RowSet& rs, int nch, const int32_t* __restrict__ x,
+                                   const float2* __restrict__ part, const float* __restrict__ lse_d_in,
+                                   const float* __restrict__ u_acc, float* __restrict__ lse_d_out,
+                                   float* __restrict__ lse_t_out, float* __restrict__ csum,
+                                   ReqState* __restrict__ state, unsigned blk) {
     __shared__ float fscr[kWaves + 1];
     __shared__ float s_lt[65], s_ld[64];
     __shared__ int s_n, s_bad;
 
-    const int c = static_cast<int>(blockIdx.x % static_cast<unsigned>(nch));
-    const int b = static_cast<int>(blockIdx.x / static_cast<unsigned>(nch));
+    const int c = static_cast<int>(blk % static_cast<unsigned>(nch));
+    const int b = static_cast<int>(blk / static_cast<unsigned>(nch));
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int G = rs.gamma, V = rs.V;
     const ReqRows q = request_rows(rs, b);
@@ -320,15 +319,25 @@ void verify_chunks_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
 
 template <bool VEC4>
 __global__ __launch_bounds__(kThreads)
-void verify_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
-                          const float* __restrict__ u_fin, float* __restrict__ csum,
-                          const ReqState* __restrict__ state, int32_t* __restrict__ n_out,
-                          int32_t* __restrict__ y_out) {
+void verify_chunks_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
+                          const float2* __restrict__ part, const float* __restrict__ lse_d_in,
+                          const float* __restrict__ u_acc, float* __restrict__ lse_d_out,
+                          float* __restrict__ lse_t_out, float* __restrict__ csum,
+                          ReqState* __restrict__ state) {
+    verify_chunks_body<VEC4>(rs, nch, x, part, lse_d_in, u_acc, lse_d_out, lse_t_out, csum, state,
+                             blockIdx.x);
+}
+
+template <bool VEC4>
+__device__ __forceinline__ void verify_select_body(const RowSet& rs, int nch, const int32_t* __restrict__ x,
+                                   const float* __restrict__ u_fin, float* __restrict__ csum,
+                                   const ReqState* __restrict__ state, int32_t* __restrict__ n_out,
+                                   int32_t* __restrict__ y_out, int b) {
     __shared__ float fscr[kWaves + 1];
     __shared__ int iscr[kWaves + 1];
     __shared__ int s_found;
     __shared__ float s_tprime, s_total;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int tid = threadIdx.x;
     const int G = rs.gamma, V = rs.V;
     int32_t* y = y_out + static_cast<long long>(b) * (G + 1);
     const ReqState st = state[b];
@@ -432,18 +441,26 @@ void verify_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
     if (tid == 0) n_out[b] = n;
 }
 
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads)
+void verify_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
+                          const float* __restrict__ u_fin, float* __restrict__ csum,
+                          const ReqState* __restrict__ state, int32_t* __restrict__ n_out,
+                          int32_t* __restrict__ y_out) {
+    verify_select_body<VEC4>(rs, nch, x, u_fin, csum, state, n_out, y_out, blockIdx.x);
+}
+
 // ----------------------------------------------------------------------------- TV labels
 // lse_d / lse_t given, or merged here from row partials.
 template <bool VEC4>
-__global__ __launch_bounds__(kThreads)
-void tv_chunks_kernel(RowSet rs, int nch, const float* __restrict__ lse_d,
-                      const float* __restrict__ lse_t, const float2* __restrict__ part,
-                      float* __restrict__ psum) {
+__device__ __forceinline__ void tv_chunks_body(const RowSet& rs, int nch, const float* __restrict__ lse_d,
+                               const float* __restrict__ lse_t, const float2* __restrict__ part,
+                               float* __restrict__ psum, unsigned blk) {
     __shared__ float fscr[kWaves + 1];
     __shared__ float s_lse[2];
     const int G = rs.gamma, V = rs.V, tid = threadIdx.x;
-    const int c = static_cast<int>(blockIdx.x % static_cast<unsigned>(nch));
-    const long long pair = blockIdx.x / static_cast<unsigned>(nch);          // b * G + k
+    const int c = static_cast<int>(blk % static_cast<unsigned>(nch));
+    const long long pair = blk / static_cast<unsigned>(nch);                 // b * G + k
     const int k = static_cast<int>(pair % G);
     const int b = static_cast<int>(pair / G);
     const ReqRows q = request_rows(rs, b);
@@ -472,11 +489,18 @@ void tv_chunks_kernel(RowSet rs, int nch, const float* __restrict__ lse_d,
     if (tid == 0) psum[pair * nch + c] = s;
 }
 
+template <bool VEC4>
 __global__ __launch_bounds__(kThreads)
-void tv_merge_kernel(RowSet rs, int nch, const float* __restrict__ psum,
-                     float* __restrict__ cstar) {
+void tv_chunks_kernel(RowSet rs, int nch, const float* __restrict__ lse_d,
+                      const float* __restrict__ lse_t, const float2* __restrict__ part,
+                      float* __restrict__ psum) {
+    tv_chunks_body<VEC4>(rs, nch, lse_d, lse_t, part, psum, blockIdx.x);
+}
+
+__device__ __forceinline__ void tv_merge_body(const RowSet& rs, int nch, const float* __restrict__ psum,
+                              float* __restrict__ cstar, unsigned blk) {
     const int G = rs.gamma;
-    const long long pair = static_cast<long long>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    const long long pair = static_cast<long long>(blk) * kWaves + threadIdx.x / kWave;
     if (pair >= static_cast<long long>(rs.B) * G) return;
     const int k = static_cast<int>(pair % G);
     const int b = static_cast<int>(pair / G);
@@ -488,6 +512,44 @@ void tv_merge_kernel(RowSet rs, int nch, const float* __restrict__ psum,
         for (int i = lane; i < nch; i += kWave) s += psum[pair * nch + i];
     s = wave_sum_dpp(s);
     if (lane == 0) cstar[pair] = live ? s : qnan();
+}
+
+__global__ __launch_bounds__(kThreads)
+void tv_merge_kernel(RowSet rs, int nch, const float* __restrict__ psum,
+                     float* __restrict__ cstar) {
+    tv_merge_body(rs, nch, psum, cstar, blockIdx.x);
+}
+
+// ----------------------------------------------------------------------------- verify + TV
+// One launch for the verify chunk pass and the TV chunk pass (first nch*B workgroups verify,
+// the rest sum min(p_d, p_t) per row pair and chunk), one for the final draws and the TV
+// merges (first B workgroups draw, the rest merge four row pairs each).
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads)
+void verify_tv_chunks_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
+                             const float2* __restrict__ part, const float* __restrict__ lse_d_in,
+                             const float* __restrict__ u_acc, float* __restrict__ lse_d_out,
+                             float* __restrict__ lse_t_out, float* __restrict__ csum,
+                             ReqState* __restrict__ state, float* __restrict__ psum,
+                             unsigned nverify) {
+    if (blockIdx.x < nverify)
+        verify_chunks_body<VEC4>(rs, nch, x, part, lse_d_in, u_acc, lse_d_out, lse_t_out, csum,
+                                 state, blockIdx.x);
+    else
+        tv_chunks_body<VEC4>(rs, nch, lse_d_in, nullptr, part, psum, blockIdx.x - nverify);
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads)
+void verify_tv_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
+                             const float* __restrict__ u_fin, float* __restrict__ csum,
+                             const ReqState* __restrict__ state, int32_t* __restrict__ n_out,
+                             int32_t* __restrict__ y_out, const float* __restrict__ psum,
+                             float* __restrict__ cstar) {
+    if (blockIdx.x < static_cast<unsigned>(rs.B))
+        verify_select_body<VEC4>(rs, nch, x, u_fin, csum, state, n_out, y_out, blockIdx.x);
+    else
+        tv_merge_body(rs, nch, psum, cstar, blockIdx.x - rs.B);
 }
 
 }  // namespace
@@ -530,6 +592,26 @@ hipError_t launch_verify(const RowSet& rs, const int32_t* x, const float2* part,
     if (e != hipSuccess) return e;
     DSPARK_LAUNCH_VEC4(verify_select_kernel, dim3(rs.B), rs, nch, x, u_fin, csum, rstate, n_out,
                        y_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify_tv(const RowSet& rs, const int32_t* x, const float2* part,
+                            const float* lse_d_in, const float* u_acc, const float* u_fin,
+                            float* lse_d_out, float* lse_t_out, float* csum, void* state,
+                            float* psum, int32_t* n_out, int32_t* y_out, float* cstar,
+                            hipStream_t st) {
+    const int nch = nchunks(rs.V);
+    ReqState* rstate = static_cast<ReqState*>(state);
+    const unsigned nverify = static_cast<unsigned>(nch) * rs.B;
+    const unsigned ntv = static_cast<unsigned>(nch) * rs.gamma * rs.B;
+    DSPARK_LAUNCH_VEC4(verify_tv_chunks_kernel, dim3(nverify + ntv), rs, nch, x, part, lse_d_in,
+                       u_acc, lse_d_out, lse_t_out, csum, rstate, psum, nverify);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long pairs = static_cast<long long>(rs.B) * rs.gamma;
+    const unsigned nmerge = static_cast<unsigned>((pairs + kWaves - 1) / kWaves);
+    DSPARK_LAUNCH_VEC4(verify_tv_select_kernel, dim3(static_cast<unsigned>(rs.B) + nmerge), rs, nch,
+                       x, u_fin, csum, rstate, n_out, y_out, psum, cstar);
     return hipGetLastError();
 }
 

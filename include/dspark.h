@@ -164,6 +164,22 @@ int dspark_tv_labels(int B, int V, int gamma,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Verify and TV labels in one call: the same results as dspark_verify followed by
+ * dspark_tv_labels on the same rows, in fewer launches (the TV chunk sums run beside the
+ * acceptance pass, the TV merges beside the final draws). Arguments as in dspark_verify,
+ * plus cstar_out [B][gamma] fp32 (required) as in dspark_tv_labels. The normalisers of
+ * both come from the same row partials, so c* equals what dspark_tv_labels computes from
+ * this call's lse_d / lse_t.
+ */
+size_t dspark_verify_tv_workspace_bytes(int B, int V, int gamma);
+int dspark_verify_tv(int B, int V, int gamma,
+                     const float* Ld, const float* Lt, int Lt_rows,
+                     const int32_t* t_off, const int32_t* len, const int32_t* x,
+                     const float* ld_lse, const float* u_acc, const float* u_fin,
+                     int32_t* n_acc_out, int32_t* y_out, float* lse_d_out, float* lse_t_out,
+                     float* cstar_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Hardware-aware prefix scheduler.
  * [P1] section "硬件感知与置信度自适应调度机制" and [P3] "Confidence-Scheduled Verification":
  * per-position temperature calibration c' = 1 / (1 + ((1-c)/c)^(1/T_k)); prefix survival

@@ -131,6 +131,17 @@ def test_tv_rejects(lib):
 
 
 @cpu_only
+def test_verify_tv_rejects(lib):
+    args = (2, 64, 3, FAKE, FAKE, 8, None, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert lib.dspark_verify_tv(*args, None, FAKE, 1 << 30, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_verify_tv(*args, FAKE, FAKE, 4, None) == binding.ERR_WORKSPACE
+    need = lib.dspark_verify_tv_workspace_bytes(2, 64, 3)
+    assert need > lib.dspark_verify_workspace_bytes(2, 64, 3)
+    bad = (2, 64, 65) + args[3:]
+    assert lib.dspark_verify_tv(*bad, FAKE, FAKE, 1 << 30, None) == binding.ERR_UNSUPPORTED
+
+
+@cpu_only
 @pytest.mark.parametrize("args,status", [
     ((0, 4, 10, 0), binding.ERR_INVALID_ARG),
     ((4, 0, 10, 0), binding.ERR_INVALID_ARG),

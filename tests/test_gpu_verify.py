@@ -116,6 +116,48 @@ def test_ld_lse_input_matches_computed(gpu):
     assert np.max(np.abs(c1 - c2)) < 1e-6
 
 
+def run_verify_tv(inp, ld_lse=None):
+    t = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    out = dspark.verify(t["Ld"], t["Lt"], t["x"], t["u_acc"], t["u_fin"], t_off=t["t_off"],
+                        length=t["length"], ld_lse=ld_lse, want_lse=True, with_tv=True)
+    torch.cuda.synchronize()
+    return {k: (host(v) if v is not None else None) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("B,V,G,flat,given", [
+    (4, 1024, 4, False, False),
+    (7, 1000, 5, True, False),      # V % 4 != 0
+    (5, 9000, 3, True, True),       # several chunks, draft normalisers supplied
+    (1, 151936, 7, True, True),     # one request at the full vocabulary
+])
+def test_verify_tv_matches_separate_calls(gpu, B, V, G, flat, given):
+    """dspark_verify_tv gives bit-identical tokens, normalisers and c* to dspark_verify
+    followed by dspark_tv_labels on that verify's normalisers, and c* within tolerance of the
+    oracle."""
+    c = synth.custom(950 + V % 83, B=B, V=V, r=1, gamma=G, w_dtype="f32", tnoise=0.8)
+    g = np.random.default_rng(V + B)
+    lengths = g.integers(0, G + 1, size=B) if flat else None
+    if flat:
+        lengths[0] = G
+    inp = verify_inputs(c, lengths, flat)
+    ld_lse = None
+    if given:
+        ld_lse = dev(np.array([[oracle.softmax_row(inp["Ld"][i, k])[1] for k in range(G)]
+                               for i in range(B)], np.float32))
+    a = run_verify(inp, want_lse=True, ld_lse=ld_lse)
+    tv = run_tv(inp, lse_d=dev(a["lse_d"]) if not given else ld_lse, lse_t=dev(a["lse_t"]))
+    f = run_verify_tv(inp, ld_lse=ld_lse)
+    for k in ("n", "y", "lse_d", "lse_t"):
+        assert np.array_equal(a[k].view(np.uint8), f[k].view(np.uint8)), k
+    assert np.array_equal(np.isnan(tv), np.isnan(f["cstar"]))
+    fin = ~np.isnan(tv)
+    assert np.array_equal(tv[fin], f["cstar"][fin])
+    rep = check_verify(inp["Ld"], inp["Lt"], inp["x"], inp["u_acc"], inp["u_fin"], inp["t_off"],
+                       inp["length"], f["n"], f["y"], range(B))
+    assert rep.accept_ties + rep.final_ties <= 1
+    check_tv(inp, f["cstar"], range(B))
+
+
 def test_device_data_faults(gpu):
     c = synth.custom(947, B=4, V=700, r=1, gamma=3, w_dtype="f32")
     lengths = np.array([3, 2, 1, 3])
