@@ -18,6 +18,7 @@ OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 PATH_NAMES = {0: "sweep", 1: "mfma", 2: "resident"}
 GLOBAL, EARLY_STOP = 0, 1
+STS_NLL, STS_ECE = 0, 1
 
 # every symbol include/dspark.h declares
 EXPORTS = (
@@ -27,6 +28,7 @@ EXPORTS = (
     "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
     "dspark_tv_labels_workspace_bytes", "dspark_tv_labels",
     "dspark_schedule_workspace_bytes", "dspark_schedule",
+    "dspark_sts_fit_workspace_bytes", "dspark_sts_fit",
 )
 
 _P = ctypes.c_void_p
@@ -48,6 +50,8 @@ _SIGS = {
     "dspark_tv_labels": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_schedule_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_schedule": (_I, [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_sts_fit_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dspark_sts_fit": (_I, [_I, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
 }
 
 _lib = None
@@ -277,3 +281,31 @@ def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None,
                              ws.numel(), _stream(stream))
     _check(st, "dspark_schedule")
     return dict(len=length, t_off=t_off, K=K, theta=theta, a=a)
+
+
+def sts_fit(conf, n_acc, grid, *, length=None, bins=15, objective=STS_NLL, want_obj=False,
+            stream=None):
+    """dspark_sts_fit. conf [N][gamma] fp32, n_acc [N] int32 (and length [N] int32) from
+    verify, grid [n_grid] fp32. Returns dict T, ece_before, ece_after [gamma] (and obj
+    [gamma][n_grid] when want_obj)."""
+    torch = _torch()
+    lib = load()
+    N, G = conf.shape
+    dev = conf.device
+    _need(conf, "conf", torch.float32, (N, G), dev)
+    _need(n_acc, "n_acc", torch.int32, (N,), dev)
+    if length is not None:
+        _need(length, "length", torch.int32, (N,), dev)
+    nT = grid.shape[0]
+    _need(grid, "grid", torch.float32, (nT,), dev)
+    T = torch.empty(G, dtype=torch.float32, device=dev)
+    eb = torch.empty(G, dtype=torch.float32, device=dev)
+    ea = torch.empty(G, dtype=torch.float32, device=dev)
+    obj = torch.empty((G, nT), dtype=torch.float32, device=dev) if want_obj else None
+    nbytes = lib.dspark_sts_fit_workspace_bytes(N, G, nT)
+    ws = workspace(nbytes, dev, "sts")
+    st = lib.dspark_sts_fit(N, G, _ptr(conf), _ptr(n_acc), _ptr(length), _ptr(grid), nT, bins,
+                            objective, _ptr(T), _ptr(eb), _ptr(ea), _ptr(obj), _ptr(ws),
+                            ws.numel(), _stream(stream))
+    _check(st, "dspark_sts_fit")
+    return dict(T=T, ece_before=eb, ece_after=ea, obj=obj)

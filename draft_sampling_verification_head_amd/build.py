@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 
 SOURCES = ["api.hip", "draft.hip", "draft_mfma.hip", "draft_resident.hip", "verify.hip",
-           "schedule.hip"]
+           "schedule.hip", "sts.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -291,4 +291,42 @@ int dspark_schedule(int R, int gamma, const float* conf, const float* temp, cons
     return ok();
 }
 
+// ----------------------------------------------------------------------------- STS fit
+size_t dspark_sts_fit_workspace_bytes(int N, int gamma, int n_grid) {
+    if (N < 1 || gamma < 1 || n_grid < 1) return 0;
+    const size_t cells = static_cast<size_t>(N) * gamma;
+    return align_up(cells * sizeof(float)) + align_up(cells) +
+           align_up(dspark::sts_stats_bytes(gamma, n_grid));
+}
+
+int dspark_sts_fit(int N, int gamma, const float* conf, const int32_t* n_acc, const int32_t* len,
+                   const float* grid, int n_grid, int bins, int objective, float* T_out,
+                   float* ece_before, float* ece_after, float* obj_out, void* ws, size_t ws_bytes,
+                   void* stream) {
+    if (N < 1 || gamma < 1 || n_grid < 1 || bins < 1)
+        return fail(DSPARK_ERR_INVALID_ARG, "sts_fit: N=%d gamma=%d n_grid=%d bins=%d must be >= 1",
+                    N, gamma, n_grid, bins);
+    if (gamma > 64 || n_grid > 4096 || bins > dspark::sts_max_bins() ||
+        static_cast<long long>(N) * gamma >= (1LL << 31))
+        return fail(DSPARK_ERR_UNSUPPORTED, "sts_fit: gamma=%d n_grid=%d bins=%d N*gamma outside caps",
+                    gamma, n_grid, bins);
+    if (objective != DSPARK_STS_NLL && objective != DSPARK_STS_ECE)
+        return fail(DSPARK_ERR_INVALID_ARG, "sts_fit: unknown objective %d", objective);
+    if (!conf || !n_acc || !grid || !T_out || !ece_before || !ece_after)
+        return fail(DSPARK_ERR_INVALID_ARG, "sts_fit: a required pointer is NULL");
+    const size_t need = dspark_sts_fit_workspace_bytes(N, gamma, n_grid);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "sts_fit: workspace %zu bytes, need %zu", ws_bytes, need);
+    Carver c(ws);
+    const size_t cells = static_cast<size_t>(N) * gamma;
+    float* ct = c.take<float>(cells);
+    int8_t* ot = c.take<int8_t>(cells);
+    double* stats = c.take<double>(dspark::sts_stats_bytes(gamma, n_grid) / sizeof(double));
+    const hipError_t e = dspark::launch_sts_fit(N, gamma, conf, n_acc, len, grid, n_grid, bins,
+                                                objective, ct, ot, stats, T_out, ece_before,
+                                                ece_after, obj_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sts_fit");
+    return ok();
+}
+
 }  // extern "C"

@@ -85,4 +85,12 @@ hipError_t launch_schedule(int R, int gamma, const float* conf, const float* tem
                            int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out,
                            double* a_ws, hipStream_t st);
 
+// ---------------------------------------------------------------- STS fit
+int sts_max_bins();
+size_t sts_stats_bytes(int gamma, int n_grid);
+hipError_t launch_sts_fit(int N, int G, const float* conf, const int32_t* n_acc,
+                          const int32_t* len, const float* grid, int nT, int bins, int objective,
+                          float* ct, int8_t* ot, double* stats, float* T_out, float* ece_before,
+                          float* ece_after, float* obj_out, hipStream_t st);
+
 }  // namespace dspark

@@ -207,6 +207,36 @@ int dspark_schedule(int R, int gamma, const float* conf, const float* temp,
                     int32_t* len_out, int32_t* t_off_out, int32_t* K_out, float* theta_out,
                     float* a_out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Sequential temperature scaling (STS) fit.
+ * [P1] section "硬件感知与置信度自适应调度机制": the confidence head's scores are calibrated
+ * with one temperature per candidate position, each chosen by a one-dimensional grid search
+ * on validation data (the expected calibration error, ECE, is the figure of merit; the
+ * scaling keeps the scores' order). [P3] "Confidence-Scheduled Verification": c_k estimates
+ * P(position k accepted | its prefix accepted).
+ *
+ *   conf    [N][gamma] fp32 raw scores of N validation requests
+ *   n_acc   [N] int32 accepted counts from dspark_verify (negative: request ignored)
+ *   len     [N] int32 verify lengths (nullable -> gamma)
+ *   grid    [n_grid] fp32 candidate temperatures (a value <= 0 counts as 1)
+ *   bins    number of equal-width ECE bins on [0, 1], 1 <= bins <= 16
+ *   objective  DSPARK_STS_NLL: binary negative log-likelihood of the observed outcomes
+ *              (probabilities floored at 1e-12); DSPARK_STS_ECE: the ECE itself
+ *   T_out   [gamma] fp32 the first grid value minimising the objective
+ *   ece_before / ece_after [gamma] fp32 ECE at T = 1 and at T_out
+ *   obj_out [gamma][n_grid] fp32 the objective at every grid value (nullable)
+ * Outcomes: positions k < n_acc were accepted, position n_acc was rejected when
+ * n_acc < len, later positions were not observed. Calibrated score:
+ * sigmoid(logit(c) / T) in fp64. Caps: 1 <= N, N * gamma < 2^31, 1 <= gamma <= 64,
+ * 1 <= n_grid <= 4096.
+ */
+enum { DSPARK_STS_NLL = 0, DSPARK_STS_ECE = 1 };
+size_t dspark_sts_fit_workspace_bytes(int N, int gamma, int n_grid);
+int dspark_sts_fit(int N, int gamma, const float* conf, const int32_t* n_acc, const int32_t* len,
+                   const float* grid, int n_grid, int bins, int objective,
+                   float* T_out, float* ece_before, float* ece_after, float* obj_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,13 @@ Functions and what pins them (all pins live in ``tests/test_oracle_*.py``):
   (a_{r,j} = prod c, Theta = tau * SPS(B)). Pinned by brute-force enumeration, the
   constant-SPS and zero-SPS closed forms, early-stop = global for a smooth curve, a
   step-shaped curve with known answers, and exact temperature values.
+* ``outcomes``, ``scale``, ``nll``, ``ece``, ``sts_fit`` - [P1] "硬件感知与置信度自适应调度机制"
+  (sequential temperature scaling: a per-position 1-D grid search, order preserving, judged
+  by the expected calibration error) and [P3] "Confidence-Scheduled Verification" (c_k is
+  the acceptance probability given the prefix). Pinned by the outcome pattern of verify's
+  results, a hand-computed ECE, the closed-form NLL optimum logit(c)/logit(p) for a single
+  score, recovery of the temperature that generated Bernoulli outcomes, T = 1 leaving the
+  ECE unchanged, and order preservation.
 """
 from .numerics import decode_factor, clamp_uniform, softmax_row, inverse_cdf
 from .draft import markov_draft
@@ -41,6 +48,7 @@ from .verify import verify, accept_test
 from .tv import tv_labels, tv_row_pair
 from .schedule import (temperature_scale, prefix_survival, schedule, brute_force_schedule,
                        theta_curve, GLOBAL, EARLY_STOP)
+from . import sts
 
 __all__ = [
     "decode_factor", "clamp_uniform", "softmax_row", "inverse_cdf", "markov_draft",

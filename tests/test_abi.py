@@ -166,6 +166,29 @@ def test_schedule_null_required(lib):
                                8, None) == binding.ERR_WORKSPACE
 
 
+@cpu_only
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 8, 15, 0), binding.ERR_INVALID_ARG),
+    ((16, 65, 8, 15, 0), binding.ERR_UNSUPPORTED),
+    ((16, 4, 8, 17, 0), binding.ERR_UNSUPPORTED),     # more bins than the kernel keeps
+    ((16, 4, 5000, 15, 0), binding.ERR_UNSUPPORTED),
+    ((16, 4, 8, 15, 2), binding.ERR_INVALID_ARG),     # unknown objective
+])
+def test_sts_rejects(lib, args, status):
+    N, G, nT, bins, obj = args
+    assert lib.dspark_sts_fit(N, G, FAKE, FAKE, None, FAKE, nT, bins, obj, FAKE, FAKE, FAKE, None,
+                              FAKE, 1 << 30, None) == status
+
+
+@cpu_only
+def test_sts_null_and_workspace(lib):
+    assert lib.dspark_sts_fit(16, 4, None, FAKE, None, FAKE, 8, 15, 0, FAKE, FAKE, FAKE, None,
+                              FAKE, 1 << 30, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_sts_fit(16, 4, FAKE, FAKE, None, FAKE, 8, 15, 0, FAKE, FAKE, FAKE, None,
+                              FAKE, 8, None) == binding.ERR_WORKSPACE
+    assert lib.dspark_sts_fit_workspace_bytes(16, 4, 8) >= 16 * 4 * 5
+
+
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
