@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="single")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["sts"], default="single")
     ap.add_argument("--no-flush", action="store_true", help="keep the Infinity Cache warm")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -148,6 +148,50 @@ def cpu_baseline(c, inp, seconds: float, verify_only: bool = False) -> dict:
                        f"fp64, one thread), {el:.1f} s")
 
 
+def bench_sts(args, torch, dspark, device):
+    """Timing of the per-position temperature fit (STS) on synthetic validation pairs:
+    N = 65536 requests, gamma = 16, 64 grid temperatures, 15 bins, NLL objective. Scores
+    are Beta(6, 2); verification of a block stops at its first rejection, position k being
+    accepted with probability sigmoid(logit(c) / T_k), T_k from 0.6 to 2.4."""
+    from oracle import sts as oracle_sts
+    g = np.random.default_rng(2024)
+    N, G, nT, bins = 65536, 16, 64, 15
+    conf = g.beta(6, 2, size=(N, G)).astype(np.float32)
+    T_true = np.linspace(0.6, 2.4, G)
+    q = np.stack([1.0 / (1.0 + ((1.0 - conf[:, k].astype(np.float64)) / conf[:, k]) ** (1.0 / T_true[k]))
+                  for k in range(G)], axis=1)
+    acc = g.random((N, G)) < q
+    n_acc = np.where(acc.all(axis=1), G, np.argmin(acc, axis=1)).astype(np.int32)
+    grid = np.linspace(0.3, 3.0, nT).astype(np.float32)
+    tc, tn, tg = (torch.from_numpy(a).to(device) for a in (conf, n_acc, grid))
+    for _ in range(max(1, args.warmup)):
+        dspark.sts_fit(tc, tn, tg, bins=bins)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record()
+        out = dspark.sts_fit(tc, tn, tg, bins=bins)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    res = dict(metric="STS per-position temperature fit: validation pairs per second",
+               value=N * G / (ms * 1e-3), unit="pairs/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="f64", data="synthetic",
+               config=dict(workload="STS fit", N=N, gamma=G, grid=nT, bins=bins, objective="nll"),
+               T=[round(float(v), 4) for v in out["T"].cpu()],
+               ece_before=float(out["ece_before"].mean()), ece_after=float(out["ece_after"].mean()))
+    if args.cpu_seconds > 0:
+        import time
+        t0 = time.perf_counter()
+        oracle_sts.sts_fit(conf[:4096], n_acc[:4096], None, grid, bins=bins)
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=4096 * G / el, unit="pairs/s", cores=1, kind="oracle",
+                                   sample=f"the fp64 oracle fit on the first 4096 requests, {el:.1f} s")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -158,6 +202,8 @@ def main():
     import draft_sampling_verification_head_amd as dspark
 
     device = torch.device("cuda:0")
+    if args.workload == "sts":
+        return bench_sts(args, torch, dspark, device)
     cfg = WORKLOADS[args.workload]
     verify_only = args.workload == "verify"
     c, inp = build_inputs(cfg)

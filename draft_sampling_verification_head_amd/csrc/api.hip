@@ -262,7 +262,8 @@ int dspark_tv_labels(int B, int V, int gamma, const float* Ld, const float* Lt, 
 size_t dspark_schedule_workspace_bytes(int R, int gamma, int Bmax) {
     (void)Bmax;
     if (R < 1 || gamma < 1) return 0;
-    return align_up(static_cast<size_t>(R) * gamma * sizeof(double));
+    // row keys, ranked keys, ranks
+    return align_up(static_cast<size_t>(R) * gamma * (2 * sizeof(double) + sizeof(int32_t)));
 }
 
 int dspark_schedule(int R, int gamma, const float* conf, const float* temp, const float* sps,

@@ -9,13 +9,13 @@
 //   that maximises Theta(n) = (R + sum of the top-n a) * SPS(R + n) (global search), or stop
 //   at the first n where Theta stops rising (early stopping).
 //
-// Layout: one 64-bit key per candidate in LDS, key = (~a_bits[63:20]) << 20 | j << 14 | r,
-// so an ascending sort gives a descending, then position ascending, then request ascending.
-// The kept 44 bits of the fp64 a (sign, exponent, 32 mantissa bits) carry the sums.
-// Lengths come from one cut key: request r keeps its candidates whose key is below the key
-// at rank n*. Because a is non-increasing along a block and ties rank earlier positions
-// first, that set is a prefix of every block. The fp64 prefix products are kept in the
-// caller's workspace between the ranking and the counting.
+// Ranking: one 64-bit key per candidate, key = (~a_bits[63:20]) << 20 | j << 14 | r, so that
+// ascending keys mean descending a, then position ascending, then request ascending. The kept
+// 44 bits of the fp64 a (sign, exponent, 32 mantissa bits) carry the sums. Lengths come from
+// one cut key: request r keeps its candidates whose key is below the key at rank n*; since
+// a is non-increasing along a block and ties rank earlier positions first, that set is a
+// prefix of every block. Up to 64 candidates run in one wave (schedule_small_kernel); more
+// run as a rank pass over many workgroups followed by one pick workgroup.
 #include "common.h"
 #include "kernels.h"
 
@@ -56,157 +56,6 @@ __device__ __forceinline__ Best better(Best a, Best b) {
     // larger Theta wins; equal Theta -> smaller n. NaN Theta never wins.
     if (b.theta > a.theta || (b.theta == a.theta && b.n < a.n) || (a.theta != a.theta)) return b;
     return a;
-}
-
-template <int kThreads>
-__global__ __launch_bounds__(kThreads)
-void schedule_kernel(int R, int G, const float* __restrict__ conf, const float* __restrict__ temp,
-                     const float* __restrict__ sps, int Bmax, int mode, int npad,
-                     int32_t* __restrict__ len_out, int32_t* __restrict__ t_off_out,
-                     int32_t* __restrict__ K_out, float* __restrict__ theta_out,
-                     float* __restrict__ a_out, double* __restrict__ a_ws) {
-    __shared__ unsigned long long keys[kMaxCand];
-    __shared__ double dscr[kThreads / kWave + 1];
-    __shared__ int iscr[kThreads / kWave + 1];
-    __shared__ double bth[kThreads / kWave];
-    __shared__ int bn[kThreads / kWave];
-    __shared__ int s_nstar;
-    __shared__ double s_theta;
-
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int N = R * G;
-
-    // 1. temperature-scaled confidences, one candidate per thread (fp64 bits parked in keys)
-    for (int i = tid; i < N; i += kThreads)
-        keys[i] = static_cast<unsigned long long>(__double_as_longlong(scaled_conf(conf[i], temp, i % G)));
-    for (int i = N + tid; i < npad; i += kThreads) keys[i] = ~0ull;
-    __syncthreads();
-    // 2. prefix products along each block, then the ranking keys
-    for (int r = tid; r < R; r += kThreads) {
-        double a = 1.0;
-        for (int j = 0; j < G; ++j) {
-            const int i = r * G + j;
-            a *= __longlong_as_double(static_cast<long long>(keys[i]));
-            a_ws[i] = a;
-            keys[i] = make_key(a, j, r);
-            if (a_out) a_out[i] = static_cast<float>(a);
-        }
-    }
-    __syncthreads();
-
-    // 3. bitonic sort, ascending
-    for (int kk = 2; kk <= npad; kk <<= 1) {
-        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < npad; i += kThreads) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const unsigned long long x = keys[i], y = keys[ixj];
-                    const bool up = (i & kk) == 0;
-                    if ((x > y) == up) {
-                        keys[i] = y;
-                        keys[ixj] = x;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-
-    // 4. prefix sums of the ranked a, Theta(n) for n = 0..nmax
-    const int nmax = min(N, Bmax - R);
-    const int E = (npad + kThreads - 1) / kThreads;     // ranks per thread
-    const int p0 = tid * E;
-    double local = 0.0;
-    for (int e = 0; e < E; ++e) {
-        const int p = p0 + e;
-        if (p < N) local += key_value(keys[p]);
-    }
-    double tot;
-    const double S0 = block_excl_scan<kThreads>(local, dscr, &tot);   // S(p0)
-
-    Best best{-INFINITY, INT32_MAX};
-    int first_drop = INT32_MAX;
-    {
-        double S = S0;
-        double th_prev = 0.0;
-        bool have_prev = false;
-        if (p0 <= nmax) {
-            th_prev = (static_cast<double>(R) + S) * static_cast<double>(sps[R + p0]);
-            have_prev = true;
-            best = better(best, Best{th_prev, p0});
-        }
-        for (int e = 0; e < E; ++e) {
-            const int n = p0 + e + 1;
-            if (n > nmax) break;
-            S += key_value(keys[n - 1]);
-            const double th = (static_cast<double>(R) + S) * static_cast<double>(sps[R + n]);
-            if (have_prev && th <= th_prev && first_drop == INT32_MAX) first_drop = n - 1;
-            best = better(best, Best{th, n});
-            th_prev = th;
-            have_prev = true;
-        }
-    }
-    // block reductions
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        Best other{__shfl_xor(best.theta, o, kWave), __shfl_xor(best.n, o, kWave)};
-        best = better(best, other);
-    }
-    if (lane == 0) {
-        bth[wave] = best.theta;
-        bn[wave] = best.n;
-    }
-    const int drop = block_min_int<kThreads>(first_drop, iscr);   // contains a barrier
-    if (tid == 0) {
-        Best bb{bth[0], bn[0]};
-        for (int w = 1; w < kThreads / kWave; ++w) bb = better(bb, Best{bth[w], bn[w]});
-        int nstar;
-        if (mode == 1)
-            nstar = (drop == INT32_MAX) ? nmax : drop;
-        else
-            nstar = (bb.n == INT32_MAX) ? 0 : bb.n;
-        s_nstar = nstar;
-    }
-    __syncthreads();
-    const int nstar = s_nstar;
-
-    // Theta(n*) from the thread whose range ends at n*
-    {
-        const bool mine = (nstar == 0) ? (tid == 0) : (nstar > p0 && nstar <= p0 + E);
-        if (mine) {
-            double S = S0;
-            for (int n = p0 + 1; n <= nstar; ++n) S += key_value(keys[n - 1]);
-            if (nstar == 0) S = 0.0;
-            s_theta = (static_cast<double>(R) + S) * static_cast<double>(sps[R + nstar]);
-        }
-    }
-    const unsigned long long cut = (nstar < npad) ? keys[nstar] : ~0ull;
-    __syncthreads();
-
-    // 5. lengths: candidates ranked above the cut (a_ws rows were written by this thread)
-    for (int r = tid; r < R; r += kThreads) {
-        int cnt = 0;
-        for (int j = 0; j < G; ++j) cnt += make_key(a_ws[r * G + j], j, r) < cut;
-        len_out[r] = cnt;
-    }
-
-    // 6. offsets: exclusive scan of len + 1
-    if (t_off_out) {
-        int run = 0;
-        for (int base = 0; base < R; base += kThreads) {
-            const int r = base + tid;
-            const int v = (r < R) ? len_out[r] + 1 : 0;   // written by this same thread above
-            int total;
-            const int ex = block_excl_scan<kThreads>(v, iscr, &total);
-            if (r < R) t_off_out[r] = run + ex;
-            run += total;
-        }
-        if (tid == 0) t_off_out[R] = run;
-    }
-    if (tid == 0) {
-        if (K_out) *K_out = R + nstar;
-        if (theta_out) *theta_out = static_cast<float>(s_theta);
-    }
 }
 
 // One wave for up to 64 candidates (a few short requests): every candidate sits in a lane,
@@ -300,6 +149,229 @@ void schedule_small_kernel(int R, int G, const float* __restrict__ conf,
     }
 }
 
+// ---------------------------------------------------------------- many candidates
+// Along a request's block the keys increase strictly (a is non-increasing in j and ties
+// rank the earlier position first), so a candidate's rank is the sum over requests of a
+// binary search in that request's row of keys. schedule_rank_kernel: every workgroup loads
+// all keys into LDS and ranks 16 candidates, 16 threads per candidate splitting the
+// requests; the ranked keys are scattered into sorted order (the keys themselves come from a
+// one-thread-per-request kernel before). schedule_pick_kernel: one
+// workgroup scans the ranked values into S(n), evaluates Theta, finds n* and counts each
+// request's candidates ranked before n*.
+constexpr int kRankThreads = 256;
+constexpr int kRankSplit = 16;                              // threads per candidate
+constexpr int kRankPerBlock = kRankThreads / kRankSplit;
+
+// keys of every candidate: the temperature-scaled confidences in parallel (one thread per
+// candidate), then the prefix products of each request in position order (one thread per
+// request, as the oracle multiplies). A workgroup covers whole requests.
+__global__ __launch_bounds__(kRankThreads)
+void schedule_keys_kernel(int R, int G, const float* __restrict__ conf,
+                          const float* __restrict__ temp, float* __restrict__ a_out,
+                          unsigned long long* __restrict__ row_keys) {
+    __shared__ double cs[kRankThreads];
+    const int per = kRankThreads / G;                        // requests per workgroup
+    const int rb = blockIdx.x * per;
+    const int tid = threadIdx.x;
+    const int i = rb * G + tid;
+    if (tid < per * G && i < R * G) cs[tid] = scaled_conf(conf[i], temp, tid % G);
+    __syncthreads();
+    const int r = rb + tid;
+    if (tid < per && r < R) {
+        double a = 1.0;
+        for (int j = 0; j < G; ++j) {
+            a *= cs[tid * G + j];
+            const int k = r * G + j;
+            row_keys[k] = make_key(a, j, r);
+            if (a_out) a_out[k] = static_cast<float>(a);
+        }
+    }
+}
+
+// number of keys of one row (strictly increasing, length G <= 64) below `key`
+__device__ __forceinline__ int count_below(const unsigned long long* row, int G,
+                                           unsigned long long key) {
+    int lo = 0;
+#pragma unroll
+    for (int step = 64; step > 0; step >>= 1) {           // branch-free: always an in-row read
+        const unsigned long long v = row[min(lo + step, G) - 1];
+        lo += (lo + step <= G && v < key) ? step : 0;
+    }
+    return lo;
+}
+
+__host__ __device__ inline int rank_stride(int R, int G) {
+    return (static_cast<long long>(R) * (G + 1) <= kMaxCand) ? G + 1 : G;
+}
+
+// Rows sit in LDS at a stride of G + 1 keys when that fits, and the 16 threads of a
+// candidate take interleaved requests, so their reads fall on different banks.
+__global__ __launch_bounds__(kRankThreads)
+void schedule_rank_kernel(int R, int G, const unsigned long long* __restrict__ row_keys,
+                          unsigned long long* __restrict__ sorted_keys,
+                          int32_t* __restrict__ ranks) {
+    extern __shared__ unsigned long long keys[];             // R rows at stride S
+    const int tid = threadIdx.x;
+    const int N = R * G;
+    const int S = rank_stride(R, G);
+    constexpr int kBatch = 8;                                 // loads in flight per thread
+    for (int i0 = tid; i0 < N; i0 += kBatch * kRankThreads) {
+        unsigned long long v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int i = i0 + q * kRankThreads;
+            v[q] = (i < N) ? row_keys[i] : 0ull;
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int i = i0 + q * kRankThreads;
+            if (i < N) {
+                const int r = i / G;
+                keys[static_cast<long long>(r) * S + (i - r * G)] = v[q];
+            }
+        }
+    }
+    __syncthreads();
+    const int cand = blockIdx.x * kRankPerBlock + tid / kRankSplit, part = tid % kRankSplit;
+    if (cand >= N) return;                                   // whole groups leave together
+    const unsigned long long key = row_keys[cand];
+    int cnt = 0;
+    int r = part;
+    for (; r + 3 * kRankSplit < R; r += 4 * kRankSplit) {    // four independent searches
+        const int c0 = count_below(keys + static_cast<long long>(r) * S, G, key);
+        const int c1 = count_below(keys + static_cast<long long>(r + kRankSplit) * S, G, key);
+        const int c2 = count_below(keys + static_cast<long long>(r + 2 * kRankSplit) * S, G, key);
+        const int c3 = count_below(keys + static_cast<long long>(r + 3 * kRankSplit) * S, G, key);
+        cnt += (c0 + c1) + (c2 + c3);
+    }
+    for (; r < R; r += kRankSplit) cnt += count_below(keys + static_cast<long long>(r) * S, G, key);
+#pragma unroll
+    for (int o = 1; o < kRankSplit; o <<= 1) cnt += __shfl_xor(cnt, o, kWave);
+    if (part == 0) {
+        sorted_keys[cnt] = key;
+        ranks[cand] = cnt;
+    }
+}
+
+constexpr int kPickThreads = 1024;
+constexpr int kPickMaxE = kMaxCand / kPickThreads;            // ranks per thread at the cap
+
+__global__ __launch_bounds__(kPickThreads)
+void schedule_pick_kernel(int R, int G, const float* __restrict__ sps, int Bmax, int mode,
+                          const int32_t* __restrict__ ranks,
+                          const unsigned long long* __restrict__ sorted_keys,
+                          int32_t* __restrict__ len_out, int32_t* __restrict__ t_off_out,
+                          int32_t* __restrict__ K_out, float* __restrict__ theta_out) {
+    __shared__ double dscr[kPickThreads / kWave + 1];
+    __shared__ int iscr[kPickThreads / kWave + 1];
+    __shared__ double bth[kPickThreads / kWave];
+    __shared__ int bn[kPickThreads / kWave];
+    __shared__ int s_nstar;
+    __shared__ double s_theta;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int N = R * G;
+    const int nmax = min(N, Bmax - R);
+    const int E = (N + kPickThreads - 1) / kPickThreads;     // ranks per thread (<= 16)
+    const int p0 = tid * E;
+    double val[kPickMaxE], spv[kPickMaxE + 1];                // loads issued together
+#pragma unroll
+    for (int e = 0; e < kPickMaxE; ++e) {
+        const int p = p0 + e;
+        val[e] = (e < E && p < N) ? key_value(sorted_keys[p]) : 0.0;
+    }
+#pragma unroll
+    for (int e = 0; e <= kPickMaxE; ++e) {
+        const int n = p0 + e;
+        spv[e] = (e <= E && n <= nmax) ? static_cast<double>(sps[R + n]) : 0.0;
+    }
+    double local = 0.0;
+#pragma unroll
+    for (int e = 0; e < kPickMaxE; ++e) local += val[e];
+    double tot;
+    const double S0 = block_excl_scan<kPickThreads>(local, dscr, &tot);   // S(p0)
+    Best best{-INFINITY, INT32_MAX};
+    int first_drop = INT32_MAX;
+    {
+        double S = S0, th_prev = 0.0;
+        bool have_prev = false;
+        if (p0 <= nmax) {
+            th_prev = (static_cast<double>(R) + S) * spv[0];
+            have_prev = true;
+            best = better(best, Best{th_prev, p0});
+        }
+#pragma unroll
+        for (int e = 0; e < kPickMaxE; ++e) {
+            const int n = p0 + e + 1;
+            if (e < E && n <= nmax) {
+                S += val[e];
+                const double th = (static_cast<double>(R) + S) * spv[e + 1];
+                if (have_prev && th <= th_prev && first_drop == INT32_MAX) first_drop = n - 1;
+                best = better(best, Best{th, n});
+                th_prev = th;
+                have_prev = true;
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        Best other{__shfl_xor(best.theta, o, kWave), __shfl_xor(best.n, o, kWave)};
+        best = better(best, other);
+    }
+    if (lane == 0) {
+        bth[wave] = best.theta;
+        bn[wave] = best.n;
+    }
+    const int drop = block_min_int<kPickThreads>(first_drop, iscr);   // contains a barrier
+    if (tid == 0) {
+        Best bb{bth[0], bn[0]};
+        for (int w = 1; w < kPickThreads / kWave; ++w) bb = better(bb, Best{bth[w], bn[w]});
+        s_nstar = (mode == 1) ? ((drop == INT32_MAX) ? nmax : drop)
+                              : ((bb.n == INT32_MAX) ? 0 : bb.n);
+    }
+    __syncthreads();
+    const int nstar = s_nstar;
+    {
+        const bool mine = (nstar == 0) ? (tid == 0) : (nstar > p0 && nstar <= p0 + E);
+        if (mine) {
+            double S = S0;
+#pragma unroll
+            for (int e = 0; e < kPickMaxE; ++e)
+                if (p0 + e + 1 <= nstar) S += val[e];
+            if (nstar == 0) S = 0.0;
+            s_theta = (static_cast<double>(R) + S) * static_cast<double>(sps[R + nstar]);
+        }
+    }
+    __syncthreads();
+    // lengths: candidates of request r below the cut (a prefix of its row)
+    int run = 0;
+    for (int base = 0; base < R; base += kPickThreads) {
+        const int r = base + tid;
+        int cnt = 0;
+        if (r < R) {                                          // ranks of the block, loaded together
+            const int32_t* rk = ranks + static_cast<long long>(r) * G;
+            for (int j0 = 0; j0 < G; j0 += 16) {
+                int rv[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) rv[q] = (j0 + q < G) ? rk[j0 + q] : INT32_MAX;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) cnt += rv[q] < nstar;
+            }
+            len_out[r] = cnt;
+        }
+        if (t_off_out) {
+            int total;
+            const int ex = block_excl_scan<kPickThreads>((r < R) ? cnt + 1 : 0, iscr, &total);
+            if (r < R) t_off_out[r] = run + ex;
+            run += total;
+        }
+    }
+    if (tid == 0) {
+        if (t_off_out) t_off_out[R] = run;
+        if (K_out) *K_out = R + nstar;
+        if (theta_out) *theta_out = static_cast<float>(s_theta);
+    }
+}
+
 }  // namespace
 
 int schedule_max_candidates() { return kMaxCand; }
@@ -313,16 +385,22 @@ hipError_t launch_schedule(int R, int gamma, const float* conf, const float* tem
                            sps, Bmax, mode, len_out, t_off_out, K_out, theta_out, a_out);
         return hipGetLastError();
     }
-    int npad = 1;
-    while (npad < R * gamma) npad <<= 1;
-    if (npad <= 2048 && R <= 2048)
-        hipLaunchKernelGGL(schedule_kernel<256>, dim3(1), dim3(256), 0, st, R, gamma, conf, temp,
-                           sps, Bmax, mode, npad, len_out, t_off_out, K_out, theta_out, a_out,
-                           a_ws);
-    else
-        hipLaunchKernelGGL(schedule_kernel<1024>, dim3(1), dim3(1024), 0, st, R, gamma, conf,
-                           temp, sps, Bmax, mode, npad, len_out, t_off_out, K_out, theta_out,
-                           a_out, a_ws);
+    const int N = R * gamma;
+    unsigned long long* row_keys = reinterpret_cast<unsigned long long*>(a_ws);
+    unsigned long long* sorted_keys = row_keys + N;
+    int32_t* ranks = reinterpret_cast<int32_t*>(sorted_keys + N);
+    const int per = kRankThreads / gamma;
+    hipLaunchKernelGGL(schedule_keys_kernel, dim3((R + per - 1) / per), dim3(kRankThreads), 0, st, R,
+                       gamma, conf, temp, a_out, row_keys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = static_cast<size_t>(R) * rank_stride(R, gamma) * sizeof(unsigned long long);
+    hipLaunchKernelGGL(schedule_rank_kernel, dim3((N + kRankPerBlock - 1) / kRankPerBlock),
+                       dim3(kRankThreads), lds, st, R, gamma, row_keys, sorted_keys, ranks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(schedule_pick_kernel, dim3(1), dim3(kPickThreads), 0, st, R, gamma, sps, Bmax,
+                       mode, ranks, sorted_keys, len_out, t_off_out, K_out, theta_out);
     return hipGetLastError();
 }
 
