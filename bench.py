@@ -335,7 +335,8 @@ def main():
             kernel, units, launch_us = "draft_resident", G, ms_parts["draft"] * 1e3
         else:
             # one step kernel per position; the per-position time also carries the draws
-            kernel = "draft_step_mfma + draft_select" if path == "mfma" else "draft_step_gemv"
+            kernel = {"mfma": "draft_step_mfma + draft_select",
+                      "slab": "draft_slab_step + draft_slab_select"}.get(path, "draft_step_gemv")
             units, launch_us = 1, ms_parts["draft"] * 1e3 / G
         bytes_launch = per_pos * units
         roof = dict(bound="hbm", kernel=kernel, achieved=bytes_launch / (launch_us * 1e-6) / 1e9,
@@ -344,7 +345,7 @@ def main():
                     traffic=measured_traffic(args.workload, kernel),
                     bytes_per_launch=bytes_launch, positions_per_launch=units,
                     launch_us=launch_us, draft_path=path)
-        if path == "mfma":
+        if path in ("mfma", "slab"):
             tflops = 2.0 * B * c.r * V / (launch_us * 1e-6) / 1e12
             roof["mfma"] = dict(achieved=tflops, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                 frac=tflops / MFMA_BF16_PEAK_TFLOPS)

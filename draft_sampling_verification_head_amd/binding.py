@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libdspark.so")
 
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(5)
 F32, BF16 = 0, 1
-PATH_NAMES = {0: "sweep", 1: "mfma", 2: "resident"}
+PATH_NAMES = {0: "sweep", 1: "mfma", 2: "resident", 3: "slab"}
 GLOBAL, EARLY_STOP = 0, 1
 STS_NLL, STS_ECE = 0, 1
 

@@ -86,6 +86,7 @@ int dspark_version(void) { return 10000; }
 // ----------------------------------------------------------------------------- draft
 int dspark_markov_draft_path(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
     if (dspark::draft_resident_ok(B, V, r, w_dtype, W1, W2)) return DSPARK_PATH_RESIDENT;
+    if (dspark::draft_slab_ok(B, V, r, w_dtype, W1, W2)) return DSPARK_PATH_SLAB;
     if (dspark::draft_mfma_ok(B, V, r, w_dtype, W1, W2)) return DSPARK_PATH_MFMA;
     return DSPARK_PATH_SWEEP;
 }
@@ -128,6 +129,7 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
     for (int k = 0; k < gamma; ++k)
         dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
     dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
+    dc.L_out = Ld_out != nullptr;
     dc.slots = c.take<float2>(dspark::draft_resident_slot_bytes(V, gamma) / sizeof(float2));
     const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "markov_draft");

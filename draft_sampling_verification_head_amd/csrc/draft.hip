@@ -260,12 +260,17 @@ hipError_t launch_step_w(const StepArgs& a, hipStream_t st) {
 
 int draft_part_tiles(int V) {
     const int t = kTileCols < draft_mfma_tile_cols() ? kTileCols : draft_mfma_tile_cols();
-    return (V + t - 1) / t;
+    const int n = (V + t - 1) / t;
+    const int ns = draft_slab_tiles(V);
+    return n > ns ? n : ns;
 }
 
 hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; };
     if (draft_resident_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2))
         return launch_draft_resident(c, st);
+    if (draft_slab_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2) && al16(c.U) && (!c.L_out || al16(c.L[0])))
+        return launch_draft_slab(c, st);
     if (draft_mfma_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2)) return launch_draft_mfma(c, st);
     StepArgs a;
     a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma; a.nblk = (c.V + kTileCols - 1) / kTileCols;

@@ -1,0 +1,454 @@
+// Batched Markov-head draft with each vocabulary slab of W2 held in registers (gfx950).
+//
+// [P3] "DSpark Speculative Decoding", section "Semi-Autoregressive Generation": the bias of
+// position k is B_k = W1[x_{k-1}] W2 for every request, one [B x r] * [r x V] product per step
+// (rank r = 256), added to the backbone logits U_k; x_k is drawn from softmax(U_k + B_k).
+// ([P3] = the concept note "DSpark Speculative Decoding".)
+//
+// Step kernel (draft_slab_step), one launch per draft position:
+//   - One workgroup of 8 waves per vocabulary slab of 128 * NT columns. Wave w owns the
+//     16 * NT columns of its "wave tile" and keeps W2 for those columns, all ranks, in
+//     registers as MFMA A fragments of W2^T (v_mfma_f32_16x16x32_bf16: 16 columns x 32 ranks
+//     per fragment, NT * 8 fragments). W2 is read from HBM once per launch, staged through a
+//     wave-private LDS area that turns rank-major rows into rank-contiguous fragments.
+//   - The batch then streams through the slab in groups of 16 requests. A group's U_k rows
+//     (16 x 128 NT floats) and gathered W1 rows (16 x 256 bf16) arrive in LDS by direct
+//     global-to-LDS loads, issued two groups ahead into one of three buffers, so HBM keeps
+//     two groups in flight while the current one is multiplied.
+//   - Per group and wave: NT * r/32 MFMAs give the bias for 16 requests x 16 * NT columns;
+//     the epilogue adds U_k, optionally stores the logits, and reduces each request's
+//     columns of the wave tile to (max, sum exp(l - max)), the tile partial the draw uses.
+// Draw kernel (draft_slab_select), one wave per request: merges the request's tile partials
+// in tile order, picks the tile that holds the inverse-CDF point, and recomputes that tile's
+// logits with the same MFMA sequence on the same operands. A fragment column of the MFMA
+// result depends only on that column's operands, so the recomputed logits are bit-identical
+// to the step's and the logits never need to be written to memory.
+#include "common.h"
+#include "draw.h"
+#include "kernels.h"
+
+namespace dspark {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* gbl_ptr;
+
+constexpr int kSlabWaves = 8;
+constexpr int kSlabThreads = kSlabWaves * kWave;
+constexpr int kGrp = 16;                 // requests per group (MFMA N)
+constexpr int kKS = 8;                   // rank chunks of 32 (r <= 256)
+constexpr int kMaxRank = kKS * 32;
+constexpr int kMaxNT = 5;                // 16-column MFMA tiles per wave
+constexpr int kHRow = kMaxRank * 2;      // bytes of one gathered W1 row in LDS
+constexpr int kHBuf = kGrp * kHRow;      // 8 KB
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kSelRegs = 32;             // tile partials per lane in the draw (2048 tiles)
+
+template <int NT> struct Slab {
+    static constexpr int WC = 16 * NT;                // columns of a wave tile
+    static constexpr int SW = kSlabWaves * WC;        // columns of a slab
+    static constexpr int UBuf = kGrp * SW * 4;        // one group's U_k slice, bytes
+    static constexpr int Pitch = 32 * NT + 8;         // staged W2 rank row, bytes
+    static constexpr int Stage = 32 * Pitch;          // one wave's staging area, bytes
+};
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at l + 16 l
+// (the LDS base must be wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds((gbl_ptr)(g), (lds_ptr)(l), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), expcnt not waited on (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without a memory fence: the direct-to-LDS loads are ordered by the
+// explicit vmcnt waits, and the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// W2 fragments of one wave tile (columns cw .. cw + 16 NT), all r ranks: fragment [t][s]
+// holds, in lane l, ranks 32 s + 8 (l / 16) .. + 8 of column cw + 16 t + l % 16. Ranks >= r
+// and columns >= V are zero. Rank rows are loaded as 16-byte pieces, PF chunks of 32 ranks
+// in flight, and transposed through the wave-private LDS area `stg` (NSTG slots of
+// Slab<NT>::Stage bytes; chunk s uses slot s % NSTG).
+template <int NT, int PF, int NSTG>
+__device__ __forceinline__ void load_w2_frags(bf16x8 (&w2f)[NT][kKS], const uint16_t* __restrict__ W2,
+                                              int V, int r, int ks, long long cw, char* stg) {
+    constexpr int CH = 2 * NT;                      // 16-byte pieces per rank row
+    constexpr int P = Slab<NT>::Pitch;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t V32 = static_cast<uint32_t>(V);
+    uint4 g[PF][NT];
+    auto issue = [&](int s, uint4 (&dst)[NT]) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int q = j * kWave + lane, rho = q / CH, cc = q - rho * CH;
+            const int rank = 32 * s + rho;
+            const long long col = cw + 8 * cc;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (rank < r && col < V)
+                v = *reinterpret_cast<const uint4*>(W2 + (static_cast<uint32_t>(rank) * V32 + static_cast<uint32_t>(col)));
+            dst[j] = v;
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < PF; ++d)
+        if (d < ks) issue(d, g[d]);
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+        if (s < ks) {
+            char* slot = stg + (s % NSTG) * Slab<NT>::Stage;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int q = j * kWave + lane, rho = q / CH, cc = q - rho * CH;
+                uint2* dst = reinterpret_cast<uint2*>(slot + rho * P + 16 * cc);
+                dst[0] = make_uint2(g[s % PF][j].x, g[s % PF][j].y);
+                dst[1] = make_uint2(g[s % PF][j].z, g[s % PF][j].w);
+            }
+            if (s + PF < ks) issue(s + PF, g[s % PF]);
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(slot + (8 * (lane >> 4)) * P) + (lane & 15);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                uint32_t bv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bv[e] = static_cast<uint32_t>(src[(2 * e) * (P / 2) + 16 * t]) |
+                            (static_cast<uint32_t>(src[(2 * e + 1) * (P / 2) + 16 * t]) << 16);
+                w2f[t][s] = __builtin_bit_cast(bf16x8, make_uint4(bv[0], bv[1], bv[2], bv[3]));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) w2f[t][s] = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+        }
+    }
+}
+
+__device__ __forceinline__ float swz_xor16(float v) {   // lane ^ 16 within each 32 lanes
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+struct SlabArgs {
+    int B, V, r, ks, gamma, k, ntw;
+    const float* U;           // [B][gamma][V]
+    const uint16_t* W1;       // [V][r] bf16
+    const uint16_t* W2;       // [r][V] bf16
+    const int32_t* tok;       // x_{k-1}: tok[b * tok_stride]
+    int tok_stride;
+    float* L;                 // logits rows L + b * L_bstride, or null (not stored)
+    long long L_bstride;
+    float2* part;             // [B][ntw] (max, sum exp) per request and wave tile
+};
+
+// LDS: [U0][U1][H0][H1][U2][H2][tokens]; the W2 staging areas overlay U2 + H2, which the
+// first two groups do not use.
+template <int NT>
+__device__ __forceinline__ int ubuf_off(int i) {
+    constexpr int UB = Slab<NT>::UBuf;
+    return i == 0 ? 0 : (i == 1 ? UB : 2 * UB + 2 * kHBuf);
+}
+template <int NT>
+__device__ __forceinline__ int hbuf_off(int i) {
+    constexpr int UB = Slab<NT>::UBuf;
+    return i == 0 ? 2 * UB : (i == 1 ? 2 * UB + kHBuf : 3 * UB + 2 * kHBuf);
+}
+
+template <int NT>
+__global__ __launch_bounds__(kSlabThreads)
+void draft_slab_step(SlabArgs a) {
+    using S = Slab<NT>;
+    static_assert(kSlabWaves * S::Stage <= S::UBuf + kHBuf, "W2 staging fits in U2 + H2");
+    extern __shared__ __align__(16) char sm[];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int slab = blockIdx.x;
+    const long long cw = static_cast<long long>(slab) * S::SW + wave * S::WC;
+    const int ng = (a.B + kGrp - 1) / kGrp;
+    int* stok = reinterpret_cast<int*>(sm + 3 * S::UBuf + 3 * kHBuf);
+
+    for (int b = tid; b < a.B; b += kSlabThreads) {
+        const int t = a.tok[static_cast<long long>(b) * a.tok_stride];
+        stok[b] = (t >= 0 && t < a.V) ? t : -1;       // dead request: no bias, -inf logits
+    }
+    __syncthreads();
+
+    // Loads of group g into buffer i, NT + 1 direct-to-LDS instructions per wave, every lane
+    // active (addresses of absent requests / columns / ranks are clamped to valid memory;
+    // the epilogue masks those values), so each wave issues exactly NT + 1 of them.
+    //  U: wave w fills tiles w NT .. w NT + NT - 1 of the slab, 1 KB each ([16 req][16 col]);
+    //     lane l loads request l / 4, 4-column chunk (l % 4) ^ ((l / 16) % 4), an XOR swizzle
+    //     that makes the epilogue's reads bank-conflict free.
+    //  H: wave w fills rows 2w, 2w + 1 (512 bytes each); lane l loads 16-byte piece
+    //     (l % 32) ^ (row % 16) of the row, again a swizzle for the fragment reads.
+    const int u_rq = lane >> 2, u_ch = (lane & 3) ^ ((lane >> 4) & 3);
+    const int h_row = 2 * wave + (lane >> 5), h_piece = (lane & 31) ^ (h_row & 15);
+    auto issue = [&](int g, int i) {
+        const int m0 = g * kGrp;
+        const int b = min(m0 + u_rq, a.B - 1);
+        const float* urow = a.U + (static_cast<long long>(b) * a.gamma + a.k) * a.V;
+        char* ub = sm + ubuf_off<NT>(i);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            long long col = cw + 16 * t + 4 * u_ch;
+            if (col >= a.V) col = 0;
+            lds_dma16(urow + col, ub + (wave * NT + t) * 1024);
+        }
+        int tk = (m0 + h_row < a.B) ? stok[m0 + h_row] : -1;
+        if (tk < 0) tk = 0;
+        const int piece = (8 * h_piece < a.r) ? h_piece : 0;
+        lds_dma16(a.W1 + static_cast<long long>(tk) * a.r + 8 * piece, sm + hbuf_off<NT>(i) + wave * 1024);
+    };
+
+    issue(0, 0);
+    if (ng > 1) issue(1, 1);
+    bf16x8 w2f[NT][kKS];
+    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, a.ks, cw, sm + 2 * S::UBuf + 2 * kHBuf + wave * S::Stage);
+
+    const int rq = lane & 15, cg = lane >> 4;
+    const int upos = 4 * rq + (cg ^ ((rq >> 2) & 3));  // this lane's 16 bytes of a U tile
+    for (int g = 0; g < ng; ++g) {
+        const int i = g % 3;
+        // group g's loads have landed once at most the NT + 1 loads of group g + 1 are
+        // outstanding (vector memory loads complete in order); the barrier then makes every
+        // wave's loads visible and frees buffer (g + 2) % 3, last read in group g - 1
+        if (g + 1 < ng) wait_vm_lgkm<NT + 1>();
+        else wait_vm_lgkm<0>();
+        bare_barrier();
+        if (g + 2 < ng) issue(g + 2, (g + 2) % 3);
+
+        const char* H = sm + hbuf_off<NT>(i);
+        f32x4 acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < kKS; ++s) {
+            if (s < a.ks) {
+                const int piece = (4 * s + cg) ^ rq;
+                const bf16x8 hf = *reinterpret_cast<const bf16x8*>(H + rq * kHRow + 16 * piece);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
+            }
+        }
+
+        // epilogue: lane holds request rq, columns 4 cg .. 4 cg + 3 of each of its NT tiles
+        const int b = g * kGrp + rq;
+        const bool live = b < a.B && stok[b] >= 0;
+        const char* Ub = sm + ubuf_off<NT>(i);
+        float lv[NT][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float4 u4 = *reinterpret_cast<const float4*>(Ub + (wave * NT + t) * 1024 + 16 * upos);
+            const long long col = cw + 16 * t + 4 * cg;
+            const bool ok = live && col < a.V;
+            lv[t][0] = ok ? u4.x + acc[t][0] : -INFINITY;
+            lv[t][1] = ok ? u4.y + acc[t][1] : -INFINITY;
+            lv[t][2] = ok ? u4.z + acc[t][2] : -INFINITY;
+            lv[t][3] = ok ? u4.w + acc[t][3] : -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, lv[t][v]);
+            if (a.L && b < a.B && col < a.V)
+                *reinterpret_cast<float4*>(a.L + b * a.L_bstride + col) =
+                    make_float4(lv[t][0], lv[t][1], lv[t][2], lv[t][3]);
+        }
+        mx = fmaxf(mx, swz_xor16(mx));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        float sum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                sum += (lv[t][v] == -INFINITY) ? 0.0f : __expf(lv[t][v] - mx);
+        sum += swz_xor16(sum);
+        sum += __shfl_xor(sum, 32, kWave);
+        if (lane < kGrp && b < a.B)
+            a.part[static_cast<long long>(b) * a.ntw + slab * kSlabWaves + wave] = make_float2(mx, sum);
+    }
+}
+
+struct SlabSelArgs {
+    int B, V, r, ks, gamma, k, ntw;
+    const float* U;
+    const uint16_t* W1;
+    const uint16_t* W2;
+    const int32_t* tok;       // x_{k-1}
+    int tok_stride;
+    const float2* part;
+    const float* u;           // [B][gamma]
+    int32_t* x_out;
+    float* q_out;
+    float* lse_out;
+};
+
+// One wave (one workgroup) per request: tile pick from the partials, MFMA recompute of that
+// tile's logits, in-tile rescan. Every W2 load of the tile is in flight at once (one LDS
+// staging slot per rank chunk), and the W1 row is fetched before the merge.
+template <int NT>
+__global__ __launch_bounds__(kWave)
+void draft_slab_select(SlabSelArgs a) {
+    using S = Slab<NT>;
+    constexpr int CPL = (S::WC + kWave - 1) / kWave;
+    __shared__ __align__(16) char stg[kKS * S::Stage];
+    __shared__ float rowv[S::WC];
+    const int lane = threadIdx.x;
+    const int b = blockIdx.x;
+    const long long o = static_cast<long long>(b) * a.gamma + a.k;
+    const DrawOut out{a.x_out + o, a.q_out ? a.q_out + o : nullptr,
+                      a.lse_out ? a.lse_out + o : nullptr, true};
+    const int rq = lane & 15, cg = lane >> 4;
+
+    // the W1 row of the previous token in every one of the 16 request columns of the B
+    // operand (only used when the request has mass, which implies a valid token)
+    int tk = a.tok[static_cast<long long>(b) * a.tok_stride];
+    if (tk < 0 || tk >= a.V) tk = 0;
+    uint4 hv[kKS];
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+        const int rank = 32 * s + 8 * cg;
+        hv[s] = make_uint4(0u, 0u, 0u, 0u);
+        if (s < a.ks && rank < a.r) hv[s] = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
+    }
+    // lane l holds tiles [32 l, 32 l + 32): 16 loads of two partials each
+    float2 p[kSelRegs];
+    const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw);
+#pragma unroll
+    for (int t = 0; t < kSelRegs / 2; ++t) {
+        const int i = lane * kSelRegs + 2 * t;        // ntw is a multiple of 8: pairs are whole
+        float4 v = make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+        if (i < a.ntw) v = P4[i / 2];
+        p[2 * t] = make_float2(v.x, v.y);
+        p[2 * t + 1] = make_float2(v.z, v.w);
+    }
+    const TilePick tp = pick_tile<kSelRegs>(p, a.u[o]);
+    if (tp.tile < 0) {
+        if (lane == 0) put(out, -1, 0.0f, -INFINITY);
+        return;
+    }
+    const long long cw = static_cast<long long>(tp.tile) * S::WC;
+    const float* urow = a.U + (static_cast<long long>(b) * a.gamma + a.k) * a.V;
+    float4 u4[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const long long col = cw + 16 * t + 4 * cg;
+        u4[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (rq == 0 && col < a.V) u4[t] = *reinterpret_cast<const float4*>(urow + col);
+    }
+    bf16x8 w2f[NT][kKS];
+    load_w2_frags<NT, kKS, kKS>(w2f, a.W2, a.V, a.r, a.ks, cw, stg);
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+        if (s < a.ks) {
+            const bf16x8 hf = __builtin_bit_cast(bf16x8, hv[s]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
+        }
+    }
+    if (rq == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const bool ok = cw + 16 * t + 4 * cg < a.V;
+            float* rv = &rowv[16 * t + 4 * cg];
+            rv[0] = ok ? u4[t].x + acc[t][0] : -INFINITY;
+            rv[1] = ok ? u4[t].y + acc[t][1] : -INFINITY;
+            rv[2] = ok ? u4[t].z + acc[t][2] : -INFINITY;
+            rv[3] = ok ? u4[t].w + acc[t][3] : -INFINITY;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): the row is in LDS
+    __builtin_amdgcn_wave_barrier();
+    float lv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lane * CPL + j;
+        lv[j] = (c < S::WC) ? rowv[c] : -INFINITY;
+    }
+    rescan_values<CPL>(lv, cw + lane * CPL, static_cast<int>(cw), tp.m, tp.lse, tp.tprime, out);
+}
+
+int slab_nt(int V) {
+    const int nt = (V + 32767) / 32768;               // keeps the slab count <= 256
+    return nt < 1 ? 1 : (nt > kMaxNT ? kMaxNT : nt);
+}
+
+int slab_count(int V) {
+    const int sw = kSlabWaves * 16 * slab_nt(V);
+    return (V + sw - 1) / sw;
+}
+
+size_t slab_lds_bytes(int nt, int B) {
+    return 3 * static_cast<size_t>(kGrp) * kSlabWaves * 16 * nt * 4 + 3 * kHBuf + 4 * static_cast<size_t>(B);
+}
+
+template <int NT>
+hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
+    SlabArgs a;
+    a.B = c.B; a.V = c.V; a.r = c.r; a.ks = (c.r + 31) / 32; a.gamma = c.gamma;
+    a.ntw = draft_slab_tiles(c.V);
+    a.U = c.U;
+    a.W1 = static_cast<const uint16_t*>(c.W1);
+    a.W2 = static_cast<const uint16_t*>(c.W2);
+    a.L_bstride = c.L_bstride;
+    SlabSelArgs s;
+    s.B = c.B; s.V = c.V; s.r = c.r; s.ks = a.ks; s.gamma = c.gamma; s.ntw = a.ntw;
+    s.U = c.U; s.W1 = a.W1; s.W2 = a.W2; s.u = c.u;
+    s.x_out = c.x_out; s.q_out = c.q_out; s.lse_out = c.lse_out;
+    const size_t smem = slab_lds_bytes(NT, c.B);
+    const dim3 grid(static_cast<unsigned>(slab_count(c.V)));
+    const dim3 sgrid(static_cast<unsigned>(c.B));
+    for (int k = 0; k < c.gamma; ++k) {
+        a.k = k;
+        a.tok = k ? c.x_out + (k - 1) : c.x0;
+        a.tok_stride = k ? c.gamma : 1;
+        a.L = c.L_out ? c.L[k] : nullptr;
+        a.part = c.part[k & 1];
+        hipLaunchKernelGGL(draft_slab_step<NT>, grid, dim3(kSlabThreads), smem, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        s.k = k;
+        s.tok = a.tok;
+        s.tok_stride = a.tok_stride;
+        s.part = a.part;
+        hipLaunchKernelGGL(draft_slab_select<NT>, sgrid, dim3(kWave), 0, st, s);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+int draft_slab_tiles(int V) { return slab_count(V) * kSlabWaves; }
+
+bool draft_slab_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
+    if (w_dtype != 1 || B <= 8 || r > kMaxRank || (r % 8) != 0 || (V % 8) != 0) return false;
+    if (draft_slab_tiles(V) > kWave * kSelRegs) return false;     // the draw keeps every partial in registers
+    if (slab_lds_bytes(slab_nt(V), B) > static_cast<size_t>(kLdsBytes)) return false;
+    if (static_cast<long long>(kMaxRank) * V >= (1LL << 32)) return false;
+    return (reinterpret_cast<uintptr_t>(W1) % 16) == 0 && (reinterpret_cast<uintptr_t>(W2) % 16) == 0;
+}
+
+hipError_t launch_draft_slab(const DraftCall& c, hipStream_t st) {
+    switch (slab_nt(c.V)) {
+        case 1: return launch_nt<1>(c, st);
+        case 2: return launch_nt<2>(c, st);
+        case 3: return launch_nt<3>(c, st);
+        case 4: return launch_nt<4>(c, st);
+        default: return launch_nt<5>(c, st);
+    }
+}
+
+}  // namespace dspark

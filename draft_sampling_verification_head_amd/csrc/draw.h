@@ -57,19 +57,18 @@ __device__ __forceinline__ void put(const DrawOut& o, int tok, float q, float ls
     if (o.lse) *o.lse = lse;
 }
 
-// In-tile rescan: lane owns TC/64 consecutive columns of `tile`. The draw functions run with
-// all 64 lanes of the wave active (their wave-level steps are DPP forms).
-template <int TC, bool COHERENT = false>
-__device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__ row, int tile,
-                                                float m, float lse, float tprime,
-                                                const DrawOut& o) {
-    constexpr int CPL = TC / kWave;
+// In-tile rescan over values already in registers: lane owns CPL consecutive columns
+// starting at c0 (absent columns as -inf), in token order across lanes. tprime is the mass
+// still to cover inside the tile (INFINITY: take the last column with positive mass). The
+// draw functions run with all 64 lanes of the wave active (their wave-level steps are DPP
+// forms).
+template <int CPL>
+__device__ __forceinline__ int rescan_values(const float (&lv)[CPL], long long c0, int tile_c0,
+                                             float m, float lse, float tprime,
+                                             const DrawOut& o) {
     const int lane = threadIdx.x & (kWave - 1);
-    const long long c0 = static_cast<long long>(tile) * TC + lane * CPL;
-    float lv[CPL], e[CPL];
+    float e[CPL];
     float local = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) lv[j] = (c0 + j < V) ? load_logit<COHERENT>(row + c0 + j) : -INFINITY;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
@@ -88,7 +87,7 @@ __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__
     }
     int tok = wave_min_int_dpp(hit);
     if (tok == INT32_MAX) tok = wave_max_int_dpp(lastpos);
-    const int rel = tok - tile * TC;
+    const int rel = tok - tile_c0;
     const int owner = rel / CPL, jj = rel - owner * CPL;
     float mine = 0.0f;
 #pragma unroll
@@ -99,56 +98,95 @@ __device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__
     return tok;
 }
 
-// The draw from tile partials already in registers: lane l holds tiles
-// [l * RegTiles, (l + 1) * RegTiles), absent tiles as (-inf, 0). Returns the token (-1 for a
-// request with no mass) in every lane; `row` is read only for the in-tile rescan.
+// In-tile rescan of logits in memory: lane owns TC/64 consecutive columns of `tile`.
 template <int TC, bool COHERENT = false>
-__device__ int draw_regs(int V, const float2 (&p)[RegTiles<TC>::value],
-                         const float* __restrict__ row, float u, const DrawOut& o) {
-    constexpr int kSelRegTiles = RegTiles<TC>::value;
+__device__ __forceinline__ int rescan_tile_wave(int V, const float* __restrict__ row, int tile,
+                                                float m, float lse, float tprime,
+                                                const DrawOut& o) {
+    constexpr int CPL = TC / kWave;
     const int lane = threadIdx.x & (kWave - 1);
+    const long long c0 = static_cast<long long>(tile) * TC + lane * CPL;
+    float lv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) lv[j] = (c0 + j < V) ? load_logit<COHERENT>(row + c0 + j) : -INFINITY;
+    return rescan_values<CPL>(lv, c0, tile * TC, m, lse, tprime, o);
+}
+
+// Result of merging one request's tile partials: the normaliser and the tile that holds
+// the inverse-CDF point. tile < 0: the request has no mass.
+struct TilePick {
+    int tile;
+    float m, lse, tprime;
+};
+
+// Merge of NREG tile partials per lane (lane l holds tiles [l * NREG, (l + 1) * NREG),
+// absent tiles as (-inf, 0)) in tile order, and the search for the first tile whose running
+// mass exceeds u * Z.
+template <int NREG>
+__device__ __forceinline__ TilePick pick_tile(const float2 (&p)[NREG], float u) {
+    const int lane = threadIdx.x & (kWave - 1);
+    TilePick r;
     float m = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < kSelRegTiles; ++t) m = fmaxf(m, p[t].x);
+    for (int t = 0; t < NREG; ++t) m = fmaxf(m, p[t].x);
     m = wave_max_dpp(m);
+    r.m = m;
     if (m == -INFINITY) {
-        if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
-        return -1;
+        r.tile = -1;
+        r.lse = -INFINITY;
+        r.tprime = INFINITY;
+        return r;
     }
-    float mass[kSelRegTiles];
+    float mass[NREG];
     float local = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kSelRegTiles; ++t) {
+    for (int t = 0; t < NREG; ++t) {
         mass[t] = tile_mass(p[t], m);
         local += mass[t];
     }
     const float Z = wave_sum_dpp(local);
-    const float lse = m + __logf(Z);
+    r.lse = m + __logf(Z);
     const float target = clamp_uniform(u) * Z;
     const float incl = wave_incl_scan_dpp(local);
     float run = wave_shr1_dpp(incl);
     int hit = INT32_MAX, last = -1;
     float before = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kSelRegTiles; ++t) {
+    for (int t = 0; t < NREG; ++t) {
         const float nr = run + mass[t];
         if (mass[t] > 0.0f) {
-            last = lane * kSelRegTiles + t;
+            last = lane * NREG + t;
             if (hit == INT32_MAX && nr > target) {
-                hit = lane * kSelRegTiles + t;
+                hit = lane * NREG + t;
                 before = run;
             }
         }
         run = nr;
     }
     int found = wave_min_int_dpp(hit);
-    float tprime = INFINITY;
+    r.tprime = INFINITY;
     if (found == INT32_MAX) {
         found = wave_max_int_dpp(last);
     } else {
-        tprime = target - wave_bcast(before, found / kSelRegTiles);
+        r.tprime = target - wave_bcast(before, found / NREG);
     }
-    return rescan_tile_wave<TC, COHERENT>(V, row, found, m, lse, tprime, o);
+    r.tile = found;
+    return r;
+}
+
+// The draw from tile partials already in registers: lane l holds tiles
+// [l * RegTiles, (l + 1) * RegTiles), absent tiles as (-inf, 0). Returns the token (-1 for a
+// request with no mass) in every lane; `row` is read only for the in-tile rescan.
+template <int TC, bool COHERENT = false>
+__device__ int draw_regs(int V, const float2 (&p)[RegTiles<TC>::value],
+                         const float* __restrict__ row, float u, const DrawOut& o) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const TilePick tp = pick_tile<RegTiles<TC>::value>(p, u);
+    if (tp.tile < 0) {
+        if (o.write && lane == 0) put(o, -1, 0.0f, -INFINITY);
+        return -1;
+    }
+    return rescan_tile_wave<TC, COHERENT>(V, row, tp.tile, tp.m, tp.lse, tp.tprime, o);
 }
 
 // One wave draws one request's token; returns it (-1 for a dead request) in every lane.

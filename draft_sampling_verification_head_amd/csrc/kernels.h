@@ -20,6 +20,7 @@ struct DraftCall {
     float* lse_out;
     float* L[64];             // logits rows of step k: L[k] + b * L_bstride
     long long L_bstride;
+    bool L_out;               // L[k] is the caller's output (else workspace the path may skip)
     float2* part[2];          // tile partials [B][draft_part_tiles(V)] of even / odd steps
     float2* slots;            // draft_resident_slot_bytes(V, gamma) of workspace (single launch)
 };
@@ -32,6 +33,12 @@ hipError_t launch_draft(const DraftCall& c, hipStream_t st);
 bool draft_mfma_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
 int draft_mfma_tile_cols();
 hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st);
+
+// Batched path with each vocabulary slab of W2 in registers (draft_slab.hip), chosen by
+// launch_draft when it applies and U (and the caller's logits output) are 16-byte aligned.
+bool draft_slab_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
+int draft_slab_tiles(int V);
+hipError_t launch_draft_slab(const DraftCall& c, hipStream_t st);
 
 // Single-request path with W2 resident in registers (draft_resident.hip), chosen by
 // launch_draft when it applies: one launch covers all gamma positions.

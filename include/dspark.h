@@ -84,11 +84,19 @@ int dspark_version(void);
  *   q_out   [B][gamma]     fp32 p_k(x_k)                      (nullable)
  *   lse_out [B][gamma]     fp32 logsumexp(U_k + B_k)          (nullable)
  *   Ld_out  [B][gamma][V]  fp32 draft logits U_k + B_k        (nullable)
- * Positions run in order on `stream` without host round trips. Three kernel paths compute
+ * Positions run in order on `stream` without host round trips. Four kernel paths compute
  * this same function (dspark_markov_draft_path tells which one a call takes); each is
  * deterministic, and they differ from one another only in fp32 rounding order:
  *   DSPARK_PATH_SWEEP     one vocabulary sweep per position (B <= 8, or fp32 factors).
- *   DSPARK_PATH_MFMA      one bf16 MFMA projection per position (B > 8, bf16 factors).
+ *   DSPARK_PATH_SLAB      per position, one bf16 MFMA launch in which every workgroup keeps
+ *                         its vocabulary slab of W2 in registers and streams the batch
+ *                         through it, and one draw launch that recomputes the chosen tile's
+ *                         logits instead of reading them (B > 8, bf16, r <= 256 and
+ *                         r % 8 == 0, V % 8 == 0, V <= 163840, B <= 4096 at V > 131072,
+ *                         16-byte aligned W1, W2, U and Ld_out). Logits reach memory only
+ *                         when Ld_out is given.
+ *   DSPARK_PATH_MFMA      one bf16 MFMA projection per position (B > 8, bf16 factors, where
+ *                         the slab path does not apply).
  *   DSPARK_PATH_RESIDENT  one launch for all positions, W2 held in registers across the GPU
  *                         (B = 1, bf16, r <= 256 and r % 8 == 0, V % 8 == 0, 16-byte aligned
  *                         factors, ceil(V / 640) <= compute units). Its workgroups must all be
@@ -98,7 +106,7 @@ int dspark_version(void);
  *                         q = 0 and lse = -inf. Draft calls on other streams of the same
  *                         device must not overlap a call that takes this path.
  */
-enum { DSPARK_PATH_SWEEP = 0, DSPARK_PATH_MFMA = 1, DSPARK_PATH_RESIDENT = 2 };
+enum { DSPARK_PATH_SWEEP = 0, DSPARK_PATH_MFMA = 1, DSPARK_PATH_RESIDENT = 2, DSPARK_PATH_SLAB = 3 };
 
 /* The path dspark_markov_draft takes for these arguments on the current device. */
 int dspark_markov_draft_path(int B, int V, int r, int w_dtype, const void* W1, const void* W2);

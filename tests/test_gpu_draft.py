@@ -49,15 +49,36 @@ def test_ragged_shapes(gpu, B, V, r, G, wdt):
 
 
 @pytest.mark.parametrize("B,V,r,G", [
-    (9, 4104, 16, 3),       # one ragged request group, V not a multiple of the 256-column tile
-    (65, 2056, 248, 2),     # two request groups; rank padded to the 16-row chunk
-    (130, 3000, 64, 3),     # three groups, last one ragged
-    (64, 8192, 256, 2),     # exact tiles
+    (9, 163848, 16, 3),     # one ragged request group, V past the slab path's cap
+    (65, 164000, 248, 2),   # two request groups; rank padded to the 16-row chunk
 ])
 def test_batched_mfma_shapes(gpu, B, V, r, G):
     c = synth.custom(935 + B, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
     assert dspark.markov_draft_path(B, dev(d["W1"]), dev(d["W2"])) == "mfma"
+    g = run_draft(d)
+    reqs = sorted({0, 1, B // 2, B - 2, B - 1})
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
+                      reqs, gL=g["L"])
+    assert rep.ties <= 1
+    assert np.all((g["x"] >= 0) & (g["x"] < V))
+
+
+@pytest.mark.parametrize("B,V,r,G", [
+    (9, 4104, 16, 3),       # one ragged request group of 16, one slab tile past V
+    (65, 2056, 248, 2),     # five groups, the last ragged; rank padded to the 32-rank chunk
+    (130, 3000, 64, 3),     # two MFMA rank chunks
+    (64, 8192, 256, 2),     # exact slabs
+    (20, 40000, 256, 2),    # two 16-column tiles per wave
+    (33, 70000, 128, 3),    # three
+    (17, 129280, 256, 2),   # four
+    (40, 151936, 256, 2),   # five, the full vocabulary
+])
+def test_batched_slab_shapes(gpu, B, V, r, G):
+    """bf16 batches: W2 slabs in registers, draws that recompute the chosen tile."""
+    c = synth.custom(955 + B, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    assert dspark.markov_draft_path(B, dev(d["W1"]), dev(d["W2"])) == "slab"
     g = run_draft(d)
     reqs = sorted({0, 1, B // 2, B - 2, B - 1})
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
@@ -83,6 +104,79 @@ def test_single_request_bf16_shapes(gpu, V, r, G):
                       g["lse"], [0], gL=g["L"])
     assert rep.ties <= 1
     assert rep.compared + rep.ties + rep.skipped == G
+
+
+def test_slab_logits_output_is_optional(gpu):
+    """The slab path's draws do not read the logits: the same tokens, probabilities and
+    normalisers with and without the logits output, and the stored logits match the
+    oracle's."""
+    c = synth.custom(961, B=24, V=30000, r=256, gamma=4, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    a = run_draft(d, want_logits=True)
+    b = run_draft(d, want_logits=False)
+    for k in ("x", "q", "lse"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", a["x"], a["q"], a["lse"],
+                [0, 11, 23], gL=a["L"])
+
+
+def test_slab_permutation_chain_and_sentinels(gpu):
+    """Closed form through the slab path (W1[x] = 50 e_{x mod r}, W2 a partial permutation:
+    x_k = perm[x_{k-1} mod r]), with dead requests: an out-of-range context token gives -1
+    everywhere, a row of -inf from its position on."""
+    g = np.random.default_rng(9)
+    B, G, V, r = 21, 6, 9000, 16
+    perm = g.permutation(V)[:r]
+    W1 = np.zeros((V, r), np.float32)
+    W1[np.arange(V), np.arange(V) % r] = 50.0
+    W2 = np.zeros((r, V), np.float32)
+    W2[np.arange(r), perm] = 1.0
+    x0 = g.integers(0, V, size=B).astype(np.int32)
+    x0[3] = V + 2
+    x0[17] = -1
+    U = (0.1 * g.standard_normal((B, G, V))).astype(np.float32)
+    U[8, 2, :] = -np.inf
+    d = dict(U=U, W1=synth.f32_to_bf16_bits(W1), W2=synth.f32_to_bf16_bits(W2), x0=x0,
+             u=g.uniform(1e-3, 1 - 2 ** -24, size=(B, G)).astype(np.float32))
+    assert dspark.markov_draft_path(B, dev(d["W1"]), dev(d["W2"])) == "slab"
+    out = run_draft(d, want_logits=False)
+    for b in range(B):
+        if b in (3, 17):
+            assert np.all(out["x"][b] == -1)
+            assert np.all(out["lse"][b] == -np.inf) and np.all(out["q"][b] == 0.0)
+            continue
+        prev = x0[b]
+        for k in range(G):
+            if b == 8 and k >= 2:
+                assert out["x"][b, k] == -1
+                continue
+            prev = perm[prev % r]
+            assert out["x"][b, k] == prev
+            assert 0.99 < out["q"][b, k] <= 1.0
+
+
+def test_slab_max_batch(gpu):
+    """The slab path at its batch cap on the full vocabulary (4096 requests, V = 151936), one
+    position; sampled requests against the oracle. U is generated on the device (seeded) and
+    the sampled rows are copied back for the oracle."""
+    B, V, r = 4096, 151936, 256
+    c = synth.custom(962, B=2, V=V, r=r, gamma=1, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    gen = torch.Generator(device="cuda").manual_seed(962)
+    U = torch.randn((B, 1, V), generator=gen, device="cuda") * 3.0
+    x0 = torch.randint(0, V, (B,), generator=gen, device="cuda", dtype=torch.int32)
+    u = torch.rand((B, 1), generator=gen, device="cuda").clamp_(max=1 - 2 ** -24)
+    W1, W2 = dev(d["W1"]), dev(d["W2"])
+    assert dspark.markov_draft_path(B, W1, W2) == "slab"
+    out = dspark.markov_draft(U, W1, W2, x0, u)
+    torch.cuda.synchronize()
+    reqs = [0, 1, 2047, 4094, 4095]
+    idx = torch.tensor(reqs, device="cuda")
+    rep = check_draft(host(U[idx]), d["W1"], d["W2"], host(x0[idx]), host(u[idx]), "bf16",
+                      host(out["x"][idx]), host(out["q"][idx]), host(out["lse"][idx]),
+                      range(len(reqs)))
+    assert rep.ties <= 1
+    assert bool(((out["x"] >= 0) & (out["x"] < V)).all())
 
 
 def test_single_request_bf16_permutation_chain(gpu):
