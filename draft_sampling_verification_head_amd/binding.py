@@ -26,6 +26,7 @@ EXPORTS = (
     "dspark_markov_draft_path", "dspark_markov_draft_workspace_bytes", "dspark_markov_draft",
     "dspark_verify_workspace_bytes", "dspark_verify",
     "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
+    "dspark_verify_markov_workspace_bytes", "dspark_verify_markov",
     "dspark_tv_labels_workspace_bytes", "dspark_tv_labels",
     "dspark_schedule_workspace_bytes", "dspark_schedule",
     "dspark_sts_fit_workspace_bytes", "dspark_sts_fit",
@@ -46,6 +47,9 @@ _SIGS = {
     "dspark_verify": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_verify_tv_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_verify_tv": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_verify_markov_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "dspark_verify_markov": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_tv_labels_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_tv_labels": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_schedule_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -137,7 +141,7 @@ def workspace(nbytes: int, device, tag: str = ""):
 # ----------------------------------------------------------------------------- entry points
 def markov_draft_path(B: int, W1, W2) -> str:
     """Which kernel path markov_draft takes for B requests with these factors on the
-    current device: "sweep", "mfma" or "resident" (see dspark_markov_draft_path)."""
+    current device: "sweep", "slab", "mfma" or "resident" (see dspark_markov_draft_path)."""
     torch = _torch()
     V, r = W1.shape
     wdt = BF16 if W1.dtype == torch.bfloat16 else F32
@@ -228,6 +232,50 @@ def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, wan
                            _stream(stream))
     _check(st, "dspark_verify")
     return dict(n=n, y=y, lse_d=lse_d, lse_t=lse_t)
+
+
+def verify_markov(U, W1, W2, x0, x, ld_lse, Lt, u_acc, u_fin, *, t_off=None, length=None,
+                  out=None, stream=None):
+    """dspark_verify_markov: verify + TV labels with the draft logits rebuilt from U, W1, W2
+    (bf16 factors). U [B][gamma][V] fp32, x0 [B], x [B][gamma] int32, ld_lse [B][gamma] from the
+    draft, Lt [rows][V] fp32, u_acc [B][gamma], u_fin [B]. Returns dict n, y, lse_t, cstar."""
+    torch = _torch()
+    lib = load()
+    B, G, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    if W1.dtype != torch.bfloat16:
+        raise TypeError("verify_markov needs bfloat16 factors")
+    _need(U, "U", torch.float32, (B, G, V), dev)
+    _need(W1, "W1", torch.bfloat16, (V, r), dev)
+    _need(W2, "W2", torch.bfloat16, (r, V), dev)
+    _need(x0, "x0", torch.int32, (B,), dev)
+    _need(x, "x", torch.int32, (B, G), dev)
+    _need(ld_lse, "ld_lse", torch.float32, (B, G), dev)
+    if Lt.dim() != 2 or Lt.shape[1] != V:
+        raise ValueError("Lt must be [rows][V]")
+    _need(Lt, "Lt", torch.float32, tuple(Lt.shape), dev)
+    _need(u_acc, "u_acc", torch.float32, (B, G), dev)
+    _need(u_fin, "u_fin", torch.float32, (B,), dev)
+    if t_off is not None:
+        _need(t_off, "t_off", torch.int32, (B + 1,), dev)
+    if length is not None:
+        _need(length, "length", torch.int32, (B,), dev)
+    o = out or {}
+    n = o.get("n") if o.get("n") is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    y = o.get("y") if o.get("y") is not None else torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    lse_t = o.get("lse_t") if o.get("lse_t") is not None else torch.empty((B, G + 1), dtype=torch.float32, device=dev)
+    cstar = o.get("cstar") if o.get("cstar") is not None else torch.empty((B, G), dtype=torch.float32, device=dev)
+    _need(lse_t, "lse_t", torch.float32, (B, G + 1), dev)
+    _need(cstar, "cstar", torch.float32, (B, G), dev)
+    nbytes = lib.dspark_verify_markov_workspace_bytes(B, V, r, G)
+    ws = workspace(nbytes, dev, "verify_markov")
+    st = lib.dspark_verify_markov(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), BF16, _ptr(x0), _ptr(x),
+                                  _ptr(ld_lse), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
+                                  _ptr(length), _ptr(u_acc), _ptr(u_fin), _ptr(n), _ptr(y),
+                                  _ptr(lse_t), _ptr(cstar), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "dspark_verify_markov")
+    return dict(n=n, y=y, lse_t=lse_t, cstar=cstar)
 
 
 def tv_labels(Ld, Lt, *, t_off=None, length=None, lse_d=None, lse_t=None, out=None, stream=None):

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 
-SOURCES = ["api.hip", "draft.hip", "draft_mfma.hip", "draft_resident.hip", "draft_slab.hip", "verify.hip",
+SOURCES = ["api.hip", "draft.hip", "draft_mfma.hip", "draft_resident.hip", "draft_slab.hip", "verify.hip", "verify_markov.hip",
            "schedule.hip", "sts.hip"]
 ARCH = "gfx950"
 

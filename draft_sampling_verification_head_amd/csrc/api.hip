@@ -228,6 +228,57 @@ int dspark_verify_tv(int B, int V, int gamma, const float* Ld, const float* Lt, 
     return ok();
 }
 
+size_t dspark_verify_markov_workspace_bytes(int B, int V, int r, int gamma) {
+    (void)r;
+    if (B < 1 || V < 1 || gamma < 1) return 0;
+    const size_t rows = static_cast<size_t>(B) * gamma;
+    return part_bytes(B, V, gamma) + align_up((static_cast<size_t>(B) + 1) * sizeof(int32_t)) +
+           align_up(8 * rows * sizeof(int32_t)) +
+           align_up(static_cast<size_t>(B) * (gamma + 1) * sizeof(float)) +
+           align_up(rows * dspark::verify_markov_tiles(V) * sizeof(float2)) +
+           align_up(rows * sizeof(float));
+}
+
+int dspark_verify_markov(int B, int V, int r, int gamma, const float* U, const void* W1,
+                         const void* W2, int w_dtype, const int32_t* x0, const int32_t* x,
+                         const float* ld_lse, const float* Lt, int Lt_rows, const int32_t* t_off,
+                         const int32_t* len, const float* u_acc, const float* u_fin,
+                         int32_t* n_acc_out, int32_t* y_out, float* lse_t_out, float* cstar_out,
+                         void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_rows("verify_markov", B, V, gamma, Lt, Lt, Lt_rows, t_off);
+    if (rc != DSPARK_OK) return rc;
+    if (r < 1) return fail(DSPARK_ERR_INVALID_ARG, "verify_markov: r=%d must be >= 1", r);
+    if (w_dtype != DSPARK_BF16 || !dspark::verify_markov_ok(V, r))
+        return fail(DSPARK_ERR_UNSUPPORTED,
+                    "verify_markov: needs bf16 factors, r <= 256 with r %% 8 == 0, V %% 8 == 0 and "
+                    "V <= 163840 (w_dtype=%d r=%d V=%d)", w_dtype, r, V);
+    if (!U || !W1 || !W2 || !x0 || !x || !ld_lse || !u_acc || !u_fin || !n_acc_out || !y_out)
+        return fail(DSPARK_ERR_INVALID_ARG, "verify_markov: a required pointer is NULL");
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; };
+    if (!al16(U) || !al16(W1) || !al16(W2) || !al16(Lt))
+        return fail(DSPARK_ERR_INVALID_ARG, "verify_markov: U, W1, W2 and Lt must be 16-byte aligned");
+    const size_t need = dspark_verify_markov_workspace_bytes(B, V, r, gamma);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "verify_markov: workspace %zu bytes, need %zu", ws_bytes,
+                    need);
+    Carver c(ws);
+    const size_t rows = static_cast<size_t>(B) * gamma;
+    dspark::VerifyMarkovCall vc;
+    vc.rs = dspark::RowSet{B, V, gamma, Lt, Lt, Lt_rows, t_off, len};
+    vc.r = r; vc.U = U; vc.W1 = W1; vc.W2 = W2; vc.x0 = x0; vc.x = x; vc.ld_lse = ld_lse;
+    vc.u_acc = u_acc; vc.u_fin = u_fin; vc.n_out = n_acc_out; vc.y_out = y_out;
+    vc.lse_t_out = lse_t_out; vc.cstar = cstar_out;
+    vc.part_t = c.take<float2>(static_cast<size_t>(B) * (2 * gamma + 1) * row_chunks(V));
+    vc.d_off = c.take<int32_t>(static_cast<size_t>(B) + 1);
+    vc.rec = c.take<int32_t>(8 * rows);
+    vc.lse_t = c.take<float>(static_cast<size_t>(B) * (gamma + 1));
+    vc.tvpart = c.take<float2>(rows * dspark::verify_markov_tiles(V));
+    vc.ldx = c.take<float>(rows);
+    const hipError_t e = dspark::launch_verify_markov(vc, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "verify_markov");
+    return ok();
+}
+
 size_t dspark_tv_labels_workspace_bytes(int B, int V, int gamma) {
     if (B < 1 || V < 1 || gamma < 1) return 0;
     return part_bytes(B, V, gamma) +

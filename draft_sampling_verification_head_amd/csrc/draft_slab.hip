@@ -26,117 +26,18 @@
 #include "common.h"
 #include "draw.h"
 #include "kernels.h"
+#include "slab.h"
 
 namespace dspark {
 
 namespace {
+using namespace slab;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(1))) void* gbl_ptr;
-
-constexpr int kSlabWaves = 8;
-constexpr int kSlabThreads = kSlabWaves * kWave;
 constexpr int kGrp = 16;                 // requests per group (MFMA N)
-constexpr int kKS = 8;                   // rank chunks of 32 (r <= 256)
-constexpr int kMaxRank = kKS * 32;
-constexpr int kMaxNT = 5;                // 16-column MFMA tiles per wave
-constexpr int kHRow = kMaxRank * 2;      // bytes of one gathered W1 row in LDS
-constexpr int kHBuf = kGrp * kHRow;      // 8 KB
-constexpr int kLdsBytes = 160 * 1024;
-constexpr int kSelRegs = 32;             // tile partials per lane in the draw (2048 tiles)
+constexpr int kHBuf = kGrp * kHRow;      // 8 KB of gathered W1 rows per group
 
-template <int NT> struct Slab {
-    static constexpr int WC = 16 * NT;                // columns of a wave tile
-    static constexpr int SW = kSlabWaves * WC;        // columns of a slab
-    static constexpr int UBuf = kGrp * SW * 4;        // one group's U_k slice, bytes
-    static constexpr int Pitch = 32 * NT + 8;         // staged W2 rank row, bytes
-    static constexpr int Stage = 32 * Pitch;          // one wave's staging area, bytes
-};
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at l + 16 l
-// (the LDS base must be wave-uniform).
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds((gbl_ptr)(g), (lds_ptr)(l), 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0), expcnt not waited on (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// Workgroup barrier without a memory fence: the direct-to-LDS loads are ordered by the
-// explicit vmcnt waits, and the empty asm statements keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void bare_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// W2 fragments of one wave tile (columns cw .. cw + 16 NT), all r ranks: fragment [t][s]
-// holds, in lane l, ranks 32 s + 8 (l / 16) .. + 8 of column cw + 16 t + l % 16. Ranks >= r
-// and columns >= V are zero. Rank rows are loaded as 16-byte pieces, PF chunks of 32 ranks
-// in flight, and transposed through the wave-private LDS area `stg` (NSTG slots of
-// Slab<NT>::Stage bytes; chunk s uses slot s % NSTG).
-template <int NT, int PF, int NSTG>
-__device__ __forceinline__ void load_w2_frags(bf16x8 (&w2f)[NT][kKS], const uint16_t* __restrict__ W2,
-                                              int V, int r, int ks, long long cw, char* stg) {
-    constexpr int CH = 2 * NT;                      // 16-byte pieces per rank row
-    constexpr int P = Slab<NT>::Pitch;
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t V32 = static_cast<uint32_t>(V);
-    uint4 g[PF][NT];
-    auto issue = [&](int s, uint4 (&dst)[NT]) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int q = j * kWave + lane, rho = q / CH, cc = q - rho * CH;
-            const int rank = 32 * s + rho;
-            const long long col = cw + 8 * cc;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (rank < r && col < V)
-                v = *reinterpret_cast<const uint4*>(W2 + (static_cast<uint32_t>(rank) * V32 + static_cast<uint32_t>(col)));
-            dst[j] = v;
-        }
-    };
-#pragma unroll
-    for (int d = 0; d < PF; ++d)
-        if (d < ks) issue(d, g[d]);
-#pragma unroll
-    for (int s = 0; s < kKS; ++s) {
-        if (s < ks) {
-            char* slot = stg + (s % NSTG) * Slab<NT>::Stage;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int q = j * kWave + lane, rho = q / CH, cc = q - rho * CH;
-                uint2* dst = reinterpret_cast<uint2*>(slot + rho * P + 16 * cc);
-                dst[0] = make_uint2(g[s % PF][j].x, g[s % PF][j].y);
-                dst[1] = make_uint2(g[s % PF][j].z, g[s % PF][j].w);
-            }
-            if (s + PF < ks) issue(s + PF, g[s % PF]);
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(slot + (8 * (lane >> 4)) * P) + (lane & 15);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                uint32_t bv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    bv[e] = static_cast<uint32_t>(src[(2 * e) * (P / 2) + 16 * t]) |
-                            (static_cast<uint32_t>(src[(2 * e + 1) * (P / 2) + 16 * t]) << 16);
-                w2f[t][s] = __builtin_bit_cast(bf16x8, make_uint4(bv[0], bv[1], bv[2], bv[3]));
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) w2f[t][s] = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
-        }
-    }
-}
-
-__device__ __forceinline__ float swz_xor16(float v) {   // lane ^ 16 within each 32 lanes
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-}
+template <int NT>
+constexpr int ubuf_bytes() { return kGrp * Slab<NT>::SW * 4; }   // one group's U_k slice
 
 struct SlabArgs {
     int B, V, r, ks, gamma, k, ntw;
@@ -154,12 +55,12 @@ struct SlabArgs {
 // first two groups do not use.
 template <int NT>
 __device__ __forceinline__ int ubuf_off(int i) {
-    constexpr int UB = Slab<NT>::UBuf;
+    constexpr int UB = ubuf_bytes<NT>();
     return i == 0 ? 0 : (i == 1 ? UB : 2 * UB + 2 * kHBuf);
 }
 template <int NT>
 __device__ __forceinline__ int hbuf_off(int i) {
-    constexpr int UB = Slab<NT>::UBuf;
+    constexpr int UB = ubuf_bytes<NT>();
     return i == 0 ? 2 * UB : (i == 1 ? 2 * UB + kHBuf : 3 * UB + 2 * kHBuf);
 }
 
@@ -167,13 +68,14 @@ template <int NT>
 __global__ __launch_bounds__(kSlabThreads)
 void draft_slab_step(SlabArgs a) {
     using S = Slab<NT>;
-    static_assert(kSlabWaves * S::Stage <= S::UBuf + kHBuf, "W2 staging fits in U2 + H2");
+    constexpr int UB = ubuf_bytes<NT>();
+    static_assert(kSlabWaves * S::Stage <= UB + kHBuf, "W2 staging fits in U2 + H2");
     extern __shared__ __align__(16) char sm[];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int slab = blockIdx.x;
     const long long cw = static_cast<long long>(slab) * S::SW + wave * S::WC;
     const int ng = (a.B + kGrp - 1) / kGrp;
-    int* stok = reinterpret_cast<int*>(sm + 3 * S::UBuf + 3 * kHBuf);
+    int* stok = reinterpret_cast<int*>(sm + 3 * UB + 3 * kHBuf);
 
     for (int b = tid; b < a.B; b += kSlabThreads) {
         const int t = a.tok[static_cast<long long>(b) * a.tok_stride];
@@ -211,7 +113,7 @@ void draft_slab_step(SlabArgs a) {
     issue(0, 0);
     if (ng > 1) issue(1, 1);
     bf16x8 w2f[NT][kKS];
-    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, a.ks, cw, sm + 2 * S::UBuf + 2 * kHBuf + wave * S::Stage);
+    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, a.ks, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
 
     const int rq = lane & 15, cg = lane >> 4;
     const int upos = 4 * rq + (cg ^ ((rq >> 2) & 3));  // this lane's 16 bytes of a U tile
@@ -377,16 +279,6 @@ void draft_slab_select(SlabSelArgs a) {
         lv[j] = (c < S::WC) ? rowv[c] : -INFINITY;
     }
     rescan_values<CPL>(lv, cw + lane * CPL, static_cast<int>(cw), tp.m, tp.lse, tp.tprime, out);
-}
-
-int slab_nt(int V) {
-    const int nt = (V + 32767) / 32768;               // keeps the slab count <= 256
-    return nt < 1 ? 1 : (nt > kMaxNT ? kMaxNT : nt);
-}
-
-int slab_count(int V) {
-    const int sw = kSlabWaves * 16 * slab_nt(V);
-    return (V + sw - 1) / sw;
 }
 
 size_t slab_lds_bytes(int nt, int B) {

@@ -57,23 +57,16 @@ __device__ __forceinline__ void put(const DrawOut& o, int tok, float q, float ls
     if (o.lse) *o.lse = lse;
 }
 
-// In-tile rescan over values already in registers: lane owns CPL consecutive columns
-// starting at c0 (absent columns as -inf), in token order across lanes. tprime is the mass
-// still to cover inside the tile (INFINITY: take the last column with positive mass). The
-// draw functions run with all 64 lanes of the wave active (their wave-level steps are DPP
-// forms).
+// In-tile search over weights already in registers: lane owns CPL consecutive columns
+// starting at c0, in token order across lanes. Returns the first column whose running weight
+// exceeds tprime, or (rounding left the point past the end; tprime = INFINITY asks for it)
+// the last column with positive weight; -1 when no column has weight. Runs with all 64
+// lanes of the wave active (the wave-level steps are DPP forms).
 template <int CPL>
-__device__ __forceinline__ int rescan_values(const float (&lv)[CPL], long long c0, int tile_c0,
-                                             float m, float lse, float tprime,
-                                             const DrawOut& o) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float e[CPL];
+__device__ __forceinline__ int scan_pick(const float (&e)[CPL], long long c0, float tprime) {
     float local = 0.0f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
-        local += e[j];
-    }
+    for (int j = 0; j < CPL; ++j) local += e[j];
     const float incl = wave_incl_scan_dpp(local);
     float run = wave_shr1_dpp(incl);
     int hit = INT32_MAX, lastpos = -1;
@@ -85,8 +78,21 @@ __device__ __forceinline__ int rescan_values(const float (&lv)[CPL], long long c
             if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(c0 + j);
         }
     }
-    int tok = wave_min_int_dpp(hit);
-    if (tok == INT32_MAX) tok = wave_max_int_dpp(lastpos);
+    const int tok = wave_min_int_dpp(hit);
+    return tok == INT32_MAX ? wave_max_int_dpp(lastpos) : tok;
+}
+
+// In-tile rescan over logits already in registers (same lane layout, absent columns as
+// -inf): weights exp(l - m), then scan_pick; writes the token, p(token) and lse.
+template <int CPL>
+__device__ __forceinline__ int rescan_values(const float (&lv)[CPL], long long c0, int tile_c0,
+                                             float m, float lse, float tprime,
+                                             const DrawOut& o) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float e[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - m);
+    const int tok = scan_pick<CPL>(e, c0, tprime);
     const int rel = tok - tile_c0;
     const int owner = rel / CPL, jj = rel - owner * CPL;
     float mine = 0.0f;
@@ -119,12 +125,51 @@ struct TilePick {
     float m, lse, tprime;
 };
 
+// Search of NREG tile masses per lane (lane l holds tiles [l * NREG, (l + 1) * NREG)) in
+// tile order for the first tile whose running mass exceeds `target`; `local` is the lane's
+// own sum. tprime is the mass still to cover inside the found tile; INFINITY when rounding
+// left the target past the end and the last tile with mass is taken. tile = -1: no mass.
+struct MassPick {
+    int tile;
+    float tprime;
+};
+
+template <int NREG>
+__device__ __forceinline__ MassPick search_mass(const float (&mass)[NREG], float local, float target) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float incl = wave_incl_scan_dpp(local);
+    float run = wave_shr1_dpp(incl);
+    int hit = INT32_MAX, last = -1;
+    float before = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NREG; ++t) {
+        const float nr = run + mass[t];
+        if (mass[t] > 0.0f) {
+            last = lane * NREG + t;
+            if (hit == INT32_MAX && nr > target) {
+                hit = lane * NREG + t;
+                before = run;
+            }
+        }
+        run = nr;
+    }
+    MassPick r;
+    const int found = wave_min_int_dpp(hit);
+    if (found == INT32_MAX) {
+        r.tile = wave_max_int_dpp(last);
+        r.tprime = INFINITY;
+    } else {
+        r.tile = found;
+        r.tprime = target - wave_bcast(before, found / NREG);
+    }
+    return r;
+}
+
 // Merge of NREG tile partials per lane (lane l holds tiles [l * NREG, (l + 1) * NREG),
 // absent tiles as (-inf, 0)) in tile order, and the search for the first tile whose running
 // mass exceeds u * Z.
 template <int NREG>
 __device__ __forceinline__ TilePick pick_tile(const float2 (&p)[NREG], float u) {
-    const int lane = threadIdx.x & (kWave - 1);
     TilePick r;
     float m = -INFINITY;
 #pragma unroll
@@ -146,31 +191,9 @@ __device__ __forceinline__ TilePick pick_tile(const float2 (&p)[NREG], float u) 
     }
     const float Z = wave_sum_dpp(local);
     r.lse = m + __logf(Z);
-    const float target = clamp_uniform(u) * Z;
-    const float incl = wave_incl_scan_dpp(local);
-    float run = wave_shr1_dpp(incl);
-    int hit = INT32_MAX, last = -1;
-    float before = 0.0f;
-#pragma unroll
-    for (int t = 0; t < NREG; ++t) {
-        const float nr = run + mass[t];
-        if (mass[t] > 0.0f) {
-            last = lane * NREG + t;
-            if (hit == INT32_MAX && nr > target) {
-                hit = lane * NREG + t;
-                before = run;
-            }
-        }
-        run = nr;
-    }
-    int found = wave_min_int_dpp(hit);
-    r.tprime = INFINITY;
-    if (found == INT32_MAX) {
-        found = wave_max_int_dpp(last);
-    } else {
-        r.tprime = target - wave_bcast(before, found / NREG);
-    }
-    r.tile = found;
+    const MassPick mp = search_mass<NREG>(mass, local, clamp_uniform(u) * Z);
+    r.tile = mp.tile;
+    r.tprime = mp.tprime;
     return r;
 }
 

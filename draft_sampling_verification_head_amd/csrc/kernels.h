@@ -85,6 +85,34 @@ hipError_t launch_verify_tv(const RowSet& rs, const int32_t* x, const float2* pa
 hipError_t launch_tv(const RowSet& rs, const float* lse_d, const float* lse_t,
                      const float2* part, float* psum, float* cstar, hipStream_t st);
 
+// Verify + TV labels with the draft logits rebuilt from the Markov factors
+// (verify_markov.hip). Workspace regions are carved by the host layer.
+struct VerifyMarkovCall {
+    RowSet rs;                // Ld unused (set to Lt)
+    int r;
+    const float* U;
+    const void* W1;
+    const void* W2;
+    const int32_t* x0;
+    const int32_t* x;
+    const float* ld_lse;
+    const float* u_acc;
+    const float* u_fin;
+    int32_t* n_out;
+    int32_t* y_out;
+    float* lse_t_out;
+    float* cstar;
+    float2* part_t;           // [B][2 gamma + 1][chunks] row partials
+    int32_t* d_off;           // [B + 1]
+    int32_t* rec;             // [8][B gamma]
+    float* lse_t;             // [B][gamma + 1]
+    float2* tvpart;           // [B gamma][verify_markov_tiles(V)]
+    float* ldx;               // [B gamma]
+};
+int verify_markov_tiles(int V);
+bool verify_markov_ok(int V, int r);
+hipError_t launch_verify_markov(const VerifyMarkovCall& c, hipStream_t st);
+
 // ---------------------------------------------------------------- schedule
 int schedule_max_candidates();
 hipError_t launch_schedule(int R, int gamma, const float* conf, const float* temp,

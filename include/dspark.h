@@ -188,6 +188,38 @@ int dspark_verify_tv(int B, int V, int gamma,
                      float* cstar_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Verify and TV labels with the draft logits rebuilt from the Markov factors, so that the
+ * draft call need not write them (Ld_out NULL). [P3] "Semi-Autoregressive Generation":
+ * L_d[b, k] = U[b, k] + W1[x_{k-1}] W2 with x_{-1} = x0; the acceptance test, residual and
+ * bonus draws ([P1] section "大模型推理的显存瓶颈与推测解码的演进逻辑") and the labels ([P3]
+ * "Confidence-Scheduled Verification") are those of dspark_verify_tv. Only the verified
+ * rows (k < len[b]) are rebuilt, with the same bf16 MFMA arithmetic as the slab draft path,
+ * whose logits they reproduce bit for bit.
+ *
+ *   U, W1, W2, w_dtype, x0   the draft call's inputs (bf16 factors only; r <= 256 with
+ *                            r % 8 == 0, V % 8 == 0, V <= 163840; U, W1, W2, Lt 16-byte
+ *                            aligned)
+ *   x       [B][gamma]       int32 draft tokens
+ *   ld_lse  [B][gamma]       fp32 draft normalisers from the draft call (required)
+ *   Lt, Lt_rows, t_off, len, u_acc, u_fin   as in dspark_verify
+ *   n_acc_out, y_out         as in dspark_verify
+ *   lse_t_out [B][gamma+1]   fp32 lse of the target rows (nullable; NaN beyond len+1)
+ *   cstar_out [B][gamma]     fp32 c* for k < len[b], NaN beyond (nullable)
+ * Faulty requests (len or offsets out of range, a token outside [0, V), or an invalid x0
+ * with len > 0) get n = -1, y all -1 and NaN labels. Up to rounding order (the final draw
+ * sums masses over 16 NT-column tiles instead of 8192-logit chunks) the results equal
+ * dspark_verify_tv on the draft's own logits; the acceptance decisions are identical.
+ */
+size_t dspark_verify_markov_workspace_bytes(int B, int V, int r, int gamma);
+int dspark_verify_markov(int B, int V, int r, int gamma,
+                         const float* U, const void* W1, const void* W2, int w_dtype,
+                         const int32_t* x0, const int32_t* x, const float* ld_lse,
+                         const float* Lt, int Lt_rows, const int32_t* t_off, const int32_t* len,
+                         const float* u_acc, const float* u_fin,
+                         int32_t* n_acc_out, int32_t* y_out, float* lse_t_out, float* cstar_out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Hardware-aware prefix scheduler.
  * [P1] section "硬件感知与置信度自适应调度机制" and [P3] "Confidence-Scheduled Verification":
  * per-position temperature calibration c' = 1 / (1 + ((1-c)/c)^(1/T_k)); prefix survival

@@ -145,6 +145,40 @@ def test_verify_tv_rejects(lib):
     assert lib.dspark_verify_tv(*bad, FAKE, FAKE, 1 << 30, None) == binding.ERR_UNSUPPORTED
 
 
+def _vm(lib, B=2, V=64, r=8, G=3, wdt=1, U=FAKE, ld_lse=FAKE, Lt=FAKE, ws=FAKE, wsb=1 << 30):
+    return lib.dspark_verify_markov(B, V, r, G, U, FAKE, FAKE, wdt, FAKE, FAKE, ld_lse, Lt, 8, None,
+                                    None, FAKE, FAKE, FAKE, FAKE, None, None, ws, wsb, None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), binding.ERR_INVALID_ARG),
+    (dict(G=65), binding.ERR_UNSUPPORTED),
+    (dict(wdt=0), binding.ERR_UNSUPPORTED),            # fp32 factors
+    (dict(r=264), binding.ERR_UNSUPPORTED),            # rank past the register slabs
+    (dict(r=12), binding.ERR_UNSUPPORTED),             # r % 8 != 0
+    (dict(V=68), binding.ERR_UNSUPPORTED),             # V % 8 != 0
+    (dict(V=163848), binding.ERR_UNSUPPORTED),         # more than 2048 wave tiles
+    (dict(r=0), binding.ERR_INVALID_ARG),
+    (dict(U=None), binding.ERR_INVALID_ARG),
+    (dict(ld_lse=None), binding.ERR_INVALID_ARG),      # the draft's normalisers are required
+    (dict(U=ctypes.c_void_p(0x1004)), binding.ERR_INVALID_ARG),   # not 16-byte aligned
+    (dict(ws=None), binding.ERR_WORKSPACE),
+    (dict(wsb=16), binding.ERR_WORKSPACE),
+])
+def test_verify_markov_rejects(lib, kw, status):
+    assert _vm(lib, **kw) == status
+    assert lib.dspark_last_error()
+
+
+def test_verify_markov_workspace(lib):
+    B, V, r, G = 512, 129280, 256, 16
+    need = lib.dspark_verify_markov_workspace_bytes(B, V, r, G)
+    tiles = -(-V // 512) * 8                       # 16-column tiles x 4 per wave, 8 waves
+    assert need >= B * G * tiles * 8               # wave-tile partials of every verified row
+    assert lib.dspark_verify_markov_workspace_bytes(0, V, r, G) == 0
+
+
 @cpu_only
 @pytest.mark.parametrize("args,status", [
     ((0, 4, 10, 0), binding.ERR_INVALID_ARG),
