@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="keep the Infinity Cache warm")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--materialised-logits", action="store_true",
+                    help="draft writes its logits and verify reads them, also where the verify "
+                         "could rebuild them from the Markov factors")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="extra eager steps with no timing (for rocprofv3 runs)")
     return ap.parse_args()
@@ -104,10 +107,12 @@ def to_dev(a, torch, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def draft_bytes_per_position(c) -> float:
-    """Algorithmic HBM bytes of one draft position: W2 read, U_k read, W1 rows, L_d write, outputs."""
+def draft_bytes_per_position(c, logits_written: bool = True) -> float:
+    """Algorithmic HBM bytes of one draft position: W2 read, U_k read, W1 rows, L_d write (when
+    the logits are written), outputs."""
     sw = 2 if c.w_dtype == "bf16" else 4
-    return c.r * c.V * sw + c.B * c.V * 4 + c.B * c.r * sw + c.B * c.V * 4 + c.B * 12
+    return (c.r * c.V * sw + c.B * c.V * 4 + c.B * c.r * sw + c.B * 12 +
+            (c.B * c.V * 4 if logits_written else 0))
 
 
 def cpu_baseline(c, inp, seconds: float, verify_only: bool = False) -> dict:
@@ -218,10 +223,16 @@ def main():
     B, G, V = c.B, c.gamma, c.V
     Bmax = 4096
 
+    # where the draft takes the slab path, verify rebuilds the draft logits from the Markov
+    # factors (dspark_verify_markov) and the draft does not write them
+    # (at V > 131072 the rebuilding pass holds five 16-column tiles of W2 per wave, which
+    # does not fit its registers without spills, and writing the logits is faster there)
+    rebuild = (not verify_only and not args.materialised_logits and V <= 131072 and
+               dspark.markov_draft_path(B, t["W1"], t["W2"]) == "slab")
     out_d = dict(x=torch.empty((B, G), dtype=torch.int32, device=device),
                  q=torch.empty((B, G), dtype=torch.float32, device=device),
                  lse=torch.empty((B, G), dtype=torch.float32, device=device),
-                 L=torch.empty((B, G, V), dtype=torch.float32, device=device))
+                 L=None if rebuild else torch.empty((B, G, V), dtype=torch.float32, device=device))
     out_s = dict(len=torch.empty(B, dtype=torch.int32, device=device),
                  t_off=torch.empty(B + 1, dtype=torch.int32, device=device),
                  K=torch.empty(1, dtype=torch.int32, device=device),
@@ -248,8 +259,12 @@ def main():
         dspark.schedule(t["conf"], t["sps"], Bmax, temp=t["temp"], out=out_s)
 
     def verify():
-        # verify and TV labels in one call (dspark_verify_tv)
-        if verify_only:
+        # verify and TV labels in one call (dspark_verify_markov or dspark_verify_tv)
+        if rebuild:
+            dspark.verify_markov(t["U"], t["W1"], t["W2"], t["x0"], out_d["x"], out_d["lse"],
+                                 t["Lt"], t["u_acc"], t["u_fin"], t_off=out_s["t_off"],
+                                 length=out_s["len"], out=out_v)
+        elif verify_only:
             dspark.verify(out_d["L"], t["Lt"], out_d["x"], t["u_acc"], t["u_fin"], out=out_v,
                           with_tv=True)
         else:
@@ -328,7 +343,7 @@ def main():
                     launch_us=launch_us)
     else:
         path = dspark.markov_draft_path(B, t["W1"], t["W2"])
-        per_pos = draft_bytes_per_position(c)            # algorithmic bytes of one position
+        per_pos = draft_bytes_per_position(c, not rebuild)   # algorithmic bytes of one position
         if path == "resident":
             # one launch draws all gamma positions (W2 read once, then held in registers); the
             # timed call also holds the tiny counter-reset kernel that precedes it
@@ -356,7 +371,10 @@ def main():
         vs_baseline=None, dtype="f32", data="synthetic",
         config=dict(workload=f"{c.name}: {what} per step", B=B, V=V, r=c.r, gamma=G,
                     factors=c.w_dtype, sps="1/(0.02+1e-5 B)", Bmax=Bmax,
-                    mall_flush=not args.no_flush, graph_replay=True),
+                    mall_flush=not args.no_flush, graph_replay=True,
+                    draft_logits=("input" if verify_only else
+                                  "rebuilt by verify from the factors" if rebuild else
+                                  "written by the draft")),
         drafted_per_step=drafted, verified_per_step=verified,
         breakdown_us={k: v * 1e3 for k, v in ms_parts.items()},
         ms_per_step_p10_p90=[float(np.percentile(ms, 10)), float(np.percentile(ms, 90))],

@@ -36,11 +36,8 @@ using namespace slab;
 constexpr int kGrp = 16;                 // requests per group (MFMA N)
 constexpr int kHBuf = kGrp * kHRow;      // 8 KB of gathered W1 rows per group
 
-template <int NT>
-constexpr int ubuf_bytes() { return kGrp * Slab<NT>::SW * 4; }   // one group's U_k slice
-
 struct SlabArgs {
-    int B, V, r, ks, gamma, k, ntw;
+    int B, V, r, gamma, k, ntw;
     const float* U;           // [B][gamma][V]
     const uint16_t* W1;       // [V][r] bf16
     const uint16_t* W2;       // [r][V] bf16
@@ -51,31 +48,46 @@ struct SlabArgs {
     float2* part;             // [B][ntw] (max, sum exp) per request and wave tile
 };
 
-// LDS: [U0][U1][H0][H1][U2][H2][tokens]; the W2 staging areas overlay U2 + H2, which the
-// first two groups do not use.
+// LDS: [U0][U1][H0][H1][U2][H2][H3][tokens]. U slot i holds group g = i (mod 3), every wave's
+// own tiles (wave-private); H slot j holds group g = j (mod 4), shared by the waves. The W2
+// staging areas overlay U2 + H2 + H3, which are first written after the staging.
+template <int NT>
+constexpr int ubuf_bytes() { return kGrp * Slab<NT>::SW * 4; }   // one group's U_k slice
 template <int NT>
 __device__ __forceinline__ int ubuf_off(int i) {
     constexpr int UB = ubuf_bytes<NT>();
     return i == 0 ? 0 : (i == 1 ? UB : 2 * UB + 2 * kHBuf);
 }
 template <int NT>
-__device__ __forceinline__ int hbuf_off(int i) {
+__device__ __forceinline__ int hbuf_off(int j) {
     constexpr int UB = ubuf_bytes<NT>();
-    return i == 0 ? 2 * UB : (i == 1 ? 2 * UB + kHBuf : 3 * UB + 2 * kHBuf);
+    return j < 2 ? 2 * UB + j * kHBuf : 3 * UB + j * kHBuf;
 }
-
 template <int NT>
+constexpr int tok_off() { return 3 * ubuf_bytes<NT>() + 4 * kHBuf; }
+
+// Pipeline (per wave, three groups of loads in flight while a group is computed):
+//   wait for group g's loads; store group g - 1's results; copy this wave's U_k tiles of
+//   group g into registers (the wave's U slot is then free); barrier (group g's W1 rows are
+//   visible, every wave is done with group g - 1's W1 slot); issue group g + 3's loads into
+//   the freed slots; MFMA and epilogue of group g.
+// The stores of group g - 1 are issued before group g + 3's loads, so that the loads issued
+// after group g's are always the 2 (NT + 1) of groups g + 1 and g + 2 (plus stores that
+// precede them): vector memory loads complete in order, so once at most 2 (NT + 1)
+// operations are outstanding, group g's loads have landed.
+template <int NT, bool LOUT>
 __global__ __launch_bounds__(kSlabThreads)
 void draft_slab_step(SlabArgs a) {
     using S = Slab<NT>;
     constexpr int UB = ubuf_bytes<NT>();
-    static_assert(kSlabWaves * S::Stage <= UB + kHBuf, "W2 staging fits in U2 + H2");
+    constexpr int NL = NT + 1;                        // direct loads per wave and group
+    static_assert(kSlabWaves * S::Stage <= UB + 2 * kHBuf, "W2 staging fits in U2 + H2 + H3");
     extern __shared__ __align__(16) char sm[];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int slab = blockIdx.x;
     const long long cw = static_cast<long long>(slab) * S::SW + wave * S::WC;
     const int ng = (a.B + kGrp - 1) / kGrp;
-    int* stok = reinterpret_cast<int*>(sm + 3 * UB + 3 * kHBuf);
+    int* stok = reinterpret_cast<int*>(sm + tok_off<NT>());
 
     for (int b = tid; b < a.B; b += kSlabThreads) {
         const int t = a.tok[static_cast<long long>(b) * a.tok_stride];
@@ -83,85 +95,116 @@ void draft_slab_step(SlabArgs a) {
     }
     __syncthreads();
 
-    // Loads of group g into buffer i, NT + 1 direct-to-LDS instructions per wave, every lane
-    // active (addresses of absent requests / columns / ranks are clamped to valid memory;
-    // the epilogue masks those values), so each wave issues exactly NT + 1 of them.
-    //  U: wave w fills tiles w NT .. w NT + NT - 1 of the slab, 1 KB each ([16 req][16 col]);
+    // Loads of group g, NT + 1 direct-to-LDS instructions per wave, every lane active
+    // (addresses of absent requests / columns / ranks are clamped to valid memory; the
+    // epilogue masks those values), so each wave issues exactly NT + 1 of them.
+    //  U: wave w fills its tiles w NT .. w NT + NT - 1 of the slab, 1 KB each ([16 req][16 col]);
     //     lane l loads request l / 4, 4-column chunk (l % 4) ^ ((l / 16) % 4), an XOR swizzle
-    //     that makes the epilogue's reads bank-conflict free.
+    //     that makes the register copy's reads bank-conflict free.
     //  H: wave w fills rows 2w, 2w + 1 (512 bytes each); lane l loads 16-byte piece
     //     (l % 32) ^ (row % 16) of the row, again a swizzle for the fragment reads.
     const int u_rq = lane >> 2, u_ch = (lane & 3) ^ ((lane >> 4) & 3);
     const int h_row = 2 * wave + (lane >> 5), h_piece = (lane & 31) ^ (h_row & 15);
-    auto issue = [&](int g, int i) {
+    auto issue = [&](int g) {
         const int m0 = g * kGrp;
         const int b = min(m0 + u_rq, a.B - 1);
         const float* urow = a.U + (static_cast<long long>(b) * a.gamma + a.k) * a.V;
-        char* ub = sm + ubuf_off<NT>(i);
+        char* ub = sm + ubuf_off<NT>(g % 3) + wave * NT * 1024;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             long long col = cw + 16 * t + 4 * u_ch;
             if (col >= a.V) col = 0;
-            lds_dma16(urow + col, ub + (wave * NT + t) * 1024);
+            lds_dma16(urow + col, ub + t * 1024);
         }
         int tk = (m0 + h_row < a.B) ? stok[m0 + h_row] : -1;
         if (tk < 0) tk = 0;
         const int piece = (8 * h_piece < a.r) ? h_piece : 0;
-        lds_dma16(a.W1 + static_cast<long long>(tk) * a.r + 8 * piece, sm + hbuf_off<NT>(i) + wave * 1024);
+        lds_dma16(a.W1 + static_cast<long long>(tk) * a.r + 8 * piece, sm + hbuf_off<NT>(g & 3) + wave * 1024);
     };
 
-    issue(0, 0);
-    if (ng > 1) issue(1, 1);
+    issue(0);
+    if (ng > 1) issue(1);
     bf16x8 w2f[NT][kKS];
-    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, a.ks, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
+    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
+    wait_lgkm0();
+    __syncthreads();                                  // every wave is done with the staging area
+    if (ng > 2) issue(2);
 
     const int rq = lane & 15, cg = lane >> 4;
     const int upos = 4 * rq + (cg ^ ((rq >> 2) & 3));  // this lane's 16 bytes of a U tile
+    int pend_b = -1;                                   // request of the pending results
+    float2 pend_part = make_float2(0.0f, 0.0f);
+    float4 pend_l[LOUT ? NT : 1];
+    auto flush = [&]() {
+        if (pend_b < 0) return;
+        if (LOUT) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const long long col = cw + 16 * t + 4 * cg;
+                if (col < a.V) *reinterpret_cast<float4*>(a.L + pend_b * a.L_bstride + col) = pend_l[LOUT ? t : 0];
+            }
+        }
+        if (lane < kGrp)
+            a.part[static_cast<long long>(pend_b) * a.ntw + slab * kSlabWaves + wave] = pend_part;
+    };
     for (int g = 0; g < ng; ++g) {
-        const int i = g % 3;
-        // group g's loads have landed once at most the NT + 1 loads of group g + 1 are
-        // outstanding (vector memory loads complete in order); the barrier then makes every
-        // wave's loads visible and frees buffer (g + 2) % 3, last read in group g - 1
-        if (g + 1 < ng) wait_vm_lgkm<NT + 1>();
+        if (g + 2 < ng) wait_vm_lgkm<2 * NL>();
+        else if (g + 1 < ng) wait_vm_lgkm<NL>();
         else wait_vm_lgkm<0>();
+        flush();
+        float4 u4[NT];
+        const char* Ub = sm + ubuf_off<NT>(g % 3) + wave * NT * 1024;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) u4[t] = *reinterpret_cast<const float4*>(Ub + t * 1024 + 16 * upos);
+        wait_lgkm0();                                 // the U slot may be refilled
         bare_barrier();
-        if (g + 2 < ng) issue(g + 2, (g + 2) % 3);
+        if (g + 3 < ng) issue(g + 3);
 
-        const char* H = sm + hbuf_off<NT>(i);
+        const char* H = sm + hbuf_off<NT>(g & 3);
         f32x4 acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // B fragments one rank chunk ahead; the empty asm keeps the compiler from hoisting
+        // every chunk's fragment at once, which would not fit beside the W2 fragments
+        auto hfrag = [&](int s) {
+            const int piece = (4 * s + cg) ^ rq;
+            return *reinterpret_cast<const bf16x8*>(H + rq * kHRow + 16 * piece);
+        };
+        bf16x8 hf = hfrag(0);
 #pragma unroll
         for (int s = 0; s < kKS; ++s) {
-            if (s < a.ks) {
-                const int piece = (4 * s + cg) ^ rq;
-                const bf16x8 hf = *reinterpret_cast<const bf16x8*>(H + rq * kHRow + 16 * piece);
+            const bf16x8 hn = (s + 1 < kKS) ? hfrag(s + 1) : hf;
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
-            }
+            for (int t = 0; t < NT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
+            asm volatile("" ::: "memory");
+            hf = hn;
         }
 
-        // epilogue: lane holds request rq, columns 4 cg .. 4 cg + 3 of each of its NT tiles
+        // epilogue: lane holds request rq, columns 4 cg .. 4 cg + 3 of each of its NT tiles.
+        // Dead or absent requests and columns past V get -inf; when the whole wave is live
+        // and its tile lies inside the vocabulary (all but the last slab), no per-element
+        // masking is needed. exp(-inf - max) is 0, so only an all -inf row needs care.
         const int b = g * kGrp + rq;
         const bool live = b < a.B && stok[b] >= 0;
-        const char* Ub = sm + ubuf_off<NT>(i);
+        const bool fast = cw + S::WC <= a.V && __builtin_amdgcn_read_exec() == ~0ull &&
+                          __ballot(live) == ~0ull;
         float lv[NT][4];
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float4 u4 = *reinterpret_cast<const float4*>(Ub + (wave * NT + t) * 1024 + 16 * upos);
-            const long long col = cw + 16 * t + 4 * cg;
-            const bool ok = live && col < a.V;
-            lv[t][0] = ok ? u4.x + acc[t][0] : -INFINITY;
-            lv[t][1] = ok ? u4.y + acc[t][1] : -INFINITY;
-            lv[t][2] = ok ? u4.z + acc[t][2] : -INFINITY;
-            lv[t][3] = ok ? u4.w + acc[t][3] : -INFINITY;
+            lv[t][0] = u4[t].x + acc[t][0];
+            lv[t][1] = u4[t].y + acc[t][1];
+            lv[t][2] = u4[t].z + acc[t][2];
+            lv[t][3] = u4[t].w + acc[t][3];
+            if (!fast) {
+                const bool ok = live && cw + 16 * t + 4 * cg < a.V;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) lv[t][v] = ok ? lv[t][v] : -INFINITY;
+            }
 #pragma unroll
             for (int v = 0; v < 4; ++v) mx = fmaxf(mx, lv[t][v]);
-            if (a.L && b < a.B && col < a.V)
-                *reinterpret_cast<float4*>(a.L + b * a.L_bstride + col) =
-                    make_float4(lv[t][0], lv[t][1], lv[t][2], lv[t][3]);
+            if (LOUT) pend_l[LOUT ? t : 0] = make_float4(lv[t][0], lv[t][1], lv[t][2], lv[t][3]);
         }
         mx = fmaxf(mx, swz_xor16(mx));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
@@ -169,17 +212,18 @@ void draft_slab_step(SlabArgs a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                sum += (lv[t][v] == -INFINITY) ? 0.0f : __expf(lv[t][v] - mx);
+            for (int v = 0; v < 4; ++v) sum += __expf(lv[t][v] - mx);
         sum += swz_xor16(sum);
         sum += __shfl_xor(sum, 32, kWave);
-        if (lane < kGrp && b < a.B)
-            a.part[static_cast<long long>(b) * a.ntw + slab * kSlabWaves + wave] = make_float2(mx, sum);
+        if (mx == -INFINITY) sum = 0.0f;
+        pend_b = b < a.B ? b : -1;
+        pend_part = make_float2(mx, sum);
     }
+    flush();
 }
 
 struct SlabSelArgs {
-    int B, V, r, ks, gamma, k, ntw;
+    int B, V, r, gamma, k, ntw;
     const float* U;
     const uint16_t* W1;
     const uint16_t* W2;
@@ -218,7 +262,7 @@ void draft_slab_select(SlabSelArgs a) {
     for (int s = 0; s < kKS; ++s) {
         const int rank = 32 * s + 8 * cg;
         hv[s] = make_uint4(0u, 0u, 0u, 0u);
-        if (s < a.ks && rank < a.r) hv[s] = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
+        if (rank < a.r) hv[s] = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
     }
     // lane l holds tiles [32 l, 32 l + 32): 16 loads of two partials each
     float2 p[kSelRegs];
@@ -246,13 +290,13 @@ void draft_slab_select(SlabSelArgs a) {
         if (rq == 0 && col < a.V) u4[t] = *reinterpret_cast<const float4*>(urow + col);
     }
     bf16x8 w2f[NT][kKS];
-    load_w2_frags<NT, kKS, kKS>(w2f, a.W2, a.V, a.r, a.ks, cw, stg);
+    load_w2_frags<NT, kKS, kKS>(w2f, a.W2, a.V, a.r, cw, stg);
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
-        if (s < a.ks) {
+        {
             const bf16x8 hf = __builtin_bit_cast(bf16x8, hv[s]);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -282,20 +326,20 @@ void draft_slab_select(SlabSelArgs a) {
 }
 
 size_t slab_lds_bytes(int nt, int B) {
-    return 3 * static_cast<size_t>(kGrp) * kSlabWaves * 16 * nt * 4 + 3 * kHBuf + 4 * static_cast<size_t>(B);
+    return 3 * static_cast<size_t>(kGrp) * kSlabWaves * 16 * nt * 4 + 4 * kHBuf + 4 * static_cast<size_t>(B);
 }
 
 template <int NT>
 hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
     SlabArgs a;
-    a.B = c.B; a.V = c.V; a.r = c.r; a.ks = (c.r + 31) / 32; a.gamma = c.gamma;
+    a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma;
     a.ntw = draft_slab_tiles(c.V);
     a.U = c.U;
     a.W1 = static_cast<const uint16_t*>(c.W1);
     a.W2 = static_cast<const uint16_t*>(c.W2);
     a.L_bstride = c.L_bstride;
     SlabSelArgs s;
-    s.B = c.B; s.V = c.V; s.r = c.r; s.ks = a.ks; s.gamma = c.gamma; s.ntw = a.ntw;
+    s.B = c.B; s.V = c.V; s.r = c.r; s.gamma = c.gamma; s.ntw = a.ntw;
     s.U = c.U; s.W1 = a.W1; s.W2 = a.W2; s.u = c.u;
     s.x_out = c.x_out; s.q_out = c.q_out; s.lse_out = c.lse_out;
     const size_t smem = slab_lds_bytes(NT, c.B);
@@ -307,7 +351,10 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
         a.tok_stride = k ? c.gamma : 1;
         a.L = c.L_out ? c.L[k] : nullptr;
         a.part = c.part[k & 1];
-        hipLaunchKernelGGL(draft_slab_step<NT>, grid, dim3(kSlabThreads), smem, st, a);
+        if (c.L_out)
+            hipLaunchKernelGGL((draft_slab_step<NT, true>), grid, dim3(kSlabThreads), smem, st, a);
+        else
+            hipLaunchKernelGGL((draft_slab_step<NT, false>), grid, dim3(kSlabThreads), smem, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         s.k = k;

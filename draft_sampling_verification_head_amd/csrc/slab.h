@@ -18,8 +18,6 @@ namespace slab {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(1))) void* gbl_ptr;
 
 constexpr int kSlabWaves = 8;
 constexpr int kSlabThreads = kSlabWaves * kWave;
@@ -38,14 +36,28 @@ template <int NT> struct Slab {
 };
 
 // Global memory straight into LDS, 16 or 4 bytes per lane: lane l's bytes land at
-// l + 16 l (l + 4 l); the LDS base must be wave-uniform. Every lane of the wave must be
-// active, so that each call issues exactly one instruction (the vmcnt waits count them).
+// base + 16 l (base + 4 l); the LDS base must be wave-uniform. Every lane of the wave must
+// be active, so that each call issues exactly one instruction (the vmcnt waits count them).
+// The instruction is written as inline assembly on purpose: the compiler then does not
+// treat it as an LDS write, and so does not put a wait for every outstanding direct load in
+// front of each later LDS read (which would serialise the prefetch). The kernels order these
+// loads themselves with explicit vmcnt waits and barriers. M0, which holds the LDS base, is
+// used by nothing else in these kernels (no LDS-DMA builtins, no indexed register moves).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"     // m0 in the clobber lists below
+__device__ __forceinline__ uint32_t lds_addr(const void* l) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) char*)(l)));
+}
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds((gbl_ptr)(g), (lds_ptr)(l), 16, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(l))) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds((gbl_ptr)(g), (lds_ptr)(l), 4, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(l))) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), expcnt not waited on (gfx9 encoding).
 template <int N>
@@ -53,6 +65,9 @@ __device__ __forceinline__ void wait_vm_lgkm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Workgroup barrier without a memory fence: the direct-to-LDS loads are ordered by the
 // explicit vmcnt waits, and the empty asm statements keep the compiler from moving memory
@@ -63,14 +78,18 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// W2 fragments of one wave tile (columns cw .. cw + 16 NT), all r ranks: fragment [t][s]
-// holds, in lane l, ranks 32 s + 8 (l / 16) .. + 8 of column cw + 16 t + l % 16. Ranks >= r
-// and columns >= V are zero. Rank rows are loaded as 16-byte pieces, PF chunks of 32 ranks
-// in flight, and transposed through the wave-private LDS area `stg` (NSTG slots of
-// Slab<NT>::Stage bytes; chunk s uses slot s % NSTG).
+// W2 fragments of one wave tile (columns cw .. cw + 16 NT): fragment [t][s] holds, in lane
+// l, ranks 32 s + 8 (l / 16) .. + 8 of column cw + 16 t + l % 16. Ranks >= r and columns
+// >= V are zero, and so are the chunks s >= ks = ceil(r / 32), which are not loaded: every
+// caller then runs all kKS rank chunks whatever r is (a zero fragment adds exact zeros), so
+// the step kernels and the tile recomputations perform the same MFMA sequence. Rank rows are
+// loaded as 16-byte pieces, PF chunks of 32 ranks in flight, and transposed through the
+// wave-private LDS area `stg` (NSTG slots of Slab<NT>::Stage bytes; chunk s uses slot
+// s % NSTG).
 template <int NT, int PF, int NSTG>
 __device__ __forceinline__ void load_w2_frags(bf16x8 (&w2f)[NT][kKS], const uint16_t* __restrict__ W2,
-                                              int V, int r, int ks, long long cw, char* stg) {
+                                              int V, int r, long long cw, char* stg) {
+    const int ks = (r + 31) / 32;
     constexpr int CH = 2 * NT;                      // 16-byte pieces per rank row
     constexpr int P = Slab<NT>::Pitch;
     const int lane = threadIdx.x & (kWave - 1);
@@ -93,29 +112,30 @@ __device__ __forceinline__ void load_w2_frags(bf16x8 (&w2f)[NT][kKS], const uint
         if (d < ks) issue(d, g[d]);
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
-        if (s < ks) {
-            char* slot = stg + (s % NSTG) * Slab<NT>::Stage;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int q = j * kWave + lane, rho = q / CH, cc = q - rho * CH;
-                uint2* dst = reinterpret_cast<uint2*>(slot + rho * P + 16 * cc);
-                dst[0] = make_uint2(g[s % PF][j].x, g[s % PF][j].y);
-                dst[1] = make_uint2(g[s % PF][j].z, g[s % PF][j].w);
-            }
-            if (s + PF < ks) issue(s + PF, g[s % PF]);
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(slot + (8 * (lane >> 4)) * P) + (lane & 15);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                uint32_t bv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    bv[e] = static_cast<uint32_t>(src[(2 * e) * (P / 2) + 16 * t]) |
-                            (static_cast<uint32_t>(src[(2 * e + 1) * (P / 2) + 16 * t]) << 16);
-                w2f[t][s] = __builtin_bit_cast(bf16x8, make_uint4(bv[0], bv[1], bv[2], bv[3]));
-            }
-        } else {
+        if (s >= ks) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) w2f[t][s] = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+            continue;
+        }
+        char* slot = stg + (s % NSTG) * Slab<NT>::Stage;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int q = j * kWave + lane, rho = q / CH, cc = q - rho * CH;
+            uint2* dst = reinterpret_cast<uint2*>(slot + rho * P + 16 * cc);
+            dst[0] = make_uint2(g[s % PF][j].x, g[s % PF][j].y);
+            dst[1] = make_uint2(g[s % PF][j].z, g[s % PF][j].w);
+        }
+        if (s + PF < ks) issue(s + PF, g[s % PF]);
+        asm volatile("" ::: "memory");                // keeps later chunks' loads below
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(slot + (8 * (lane >> 4)) * P) + (lane & 15);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            uint32_t bv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bv[e] = static_cast<uint32_t>(src[(2 * e) * (P / 2) + 16 * t]) |
+                        (static_cast<uint32_t>(src[(2 * e + 1) * (P / 2) + 16 * t]) << 16);
+            w2f[t][s] = __builtin_bit_cast(bf16x8, make_uint4(bv[0], bv[1], bv[2], bv[3]));
         }
     }
 }

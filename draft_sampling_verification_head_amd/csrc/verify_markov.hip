@@ -119,7 +119,7 @@ void vm_rows(RowSet rs, int nch, const int32_t* __restrict__ x0, const int32_t* 
 
 // ----------------------------------------------------------------------------- vm_tv
 struct VmArgs {
-    int V, r, ks, ntw;
+    int V, r, ntw;
     long long cap;
     const float* U;
     const uint16_t* W1;
@@ -168,18 +168,25 @@ void vm_tv(VmArgs a) {
         char* ub = sm + i * Ly::Buf;
         char* lb = ub + Ly::UT;
         char* hb = ub + 2 * Ly::UT;
+        // the empty asm makes the column base opaque, so that the per-tile addresses are
+        // formed here instead of being hoisted out of the group loop (kept live, they would
+        // not fit beside the W2 fragments)
+        int cbase = static_cast<int>(cw) + (lane & 3);
+        asm volatile("" : "+v"(cbase));
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int h = 0; h < 2; ++h) {
+            const int rr = 4 * h + (lane >> 4);
+            const int c0 = cbase + 4 * (((lane >> 2) & 3) ^ h);
+            const float* up = a.U + static_cast<long long>(mt[kUrow * kRows + rr]) * a.V;
+            const float* tp = a.Lt + static_cast<long long>(mt[kTrow * kRows + rr]) * a.V;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rr = 4 * h + (lane >> 4);
-                const int gc = ((lane >> 2) & 3) ^ ((rr >> 2) & 3);
-                long long col = cw + 16 * t + 4 * gc + (lane & 3);
-                if (col >= a.V) col = 0;
+            for (int t = 0; t < NT; ++t) {
+                const int col = min(c0 + 16 * t, a.V - 1);   // past V: any valid element
                 const int off = ((wave * NT + t) * 2 + h) * 256;
-                lds_dma4(a.U + static_cast<long long>(mt[kUrow * kRows + rr]) * a.V + col, ub + off);
-                lds_dma4(a.Lt + static_cast<long long>(mt[kTrow * kRows + rr]) * a.V + col, lb + off);
+                lds_dma4(up + col, ub + off);
+                lds_dma4(tp + col, lb + off);
             }
+        }
         const int hrow = mt[kHrow * kRows + wave];
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
@@ -203,9 +210,20 @@ void vm_tv(VmArgs a) {
         issue(1, 1);
     }
     bf16x8 w2f[NT][kKS];
-    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, a.ks, cw, sm + 2 * Ly::Buf + wave * S::Stage);
+    load_w2_frags<NT, (NT > 4 ? 2 : 4), 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * Ly::Buf + wave * S::Stage);
 
     const int rq = lane & 15, cg = lane >> 4, rr = rq & 7;
+    // A group's results are stored at the top of the next group, before its loads, so that
+    // the wait below covers loads only (see draft_slab_step).
+    long long pend_j = -1;
+    float2 pend_part = make_float2(0.0f, 0.0f);
+    float pend_ldx = 0.0f;
+    bool pend_has_ldx = false;
+    auto flush = [&]() {
+        if (pend_j < 0) return;
+        if (cg == 0) a.part[pend_j * a.ntw + slab * kSlabWaves + wave] = pend_part;
+        if (pend_has_ldx) a.ldx[pend_j] = pend_ldx;
+    };
     for (int g = 0; g < ng; ++g) {
         const int i = g % 3;
         // group g's loads (and the records of group g + 2, issued before group g + 1's
@@ -213,6 +231,7 @@ void vm_tv(VmArgs a) {
         if (g + 1 < ng) wait_vm_lgkm<NL>();
         else wait_vm_lgkm<0>();
         bare_barrier();
+        flush();
         if (wave == 0 && g + 3 < ng) meta_issue(g + 3);   // slot of group g - 1, now free
         if (g + 2 < ng) issue(g + 2, (g + 2) % 3);
 
@@ -222,14 +241,23 @@ void vm_tv(VmArgs a) {
         f32x4 acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // B fragments one rank chunk ahead (request columns 8..15 repeat rows 0..7); the
+        // empty asm keeps the compiler from hoisting every chunk's fragment at once, which
+        // would not fit beside the W2 fragments
+        auto hfrag = [&](int s) {
+            const int p = (4 * s + cg) ^ rr;
+            return *reinterpret_cast<const bf16x8*>(H + rr * kHRow + 16 * p);
+        };
+        bf16x8 hf = hfrag(0);
 #pragma unroll
         for (int s = 0; s < kKS; ++s) {
-            if (s < a.ks) {
-                const int p = (4 * s + cg) ^ rr;     // request columns 8..15 repeat rows 0..7
-                const bf16x8 hf = *reinterpret_cast<const bf16x8*>(H + rr * kHRow + 16 * p);
+            {
+                const bf16x8 hn = (s + 1 < kKS) ? hfrag(s + 1) : hf;
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
+                asm volatile("" ::: "memory");
+                hf = hn;
             }
         }
 
@@ -241,6 +269,8 @@ void vm_tv(VmArgs a) {
         const int xk = mt[kXk * kRows + rr];
         const int pos = 16 * (rr & 3) + 4 * (cg ^ ((rr >> 2) & 3));
         float smin = 0.0f, sres = 0.0f;
+        bool has_ldx = false;
+        float ldx_v = 0.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int off = ((wave * NT + t) * 2 + (rr >> 2)) * 256 + 4 * pos;
@@ -257,22 +287,28 @@ void vm_tv(VmArgs a) {
                 const float pd = pexp(ld[v], lsd), pt = pexp(lt[v], lst);
                 smin += fminf(pd, pt);
                 sres += fmaxf(pt - pd, 0.0f);
-                if (valid && ok && xk == col + v) a.ldx[j] = ld[v];
+                if (valid && ok && xk == col + v) {
+                    has_ldx = true;
+                    ldx_v = ld[v];
+                }
             }
         }
         smin += swz_xor16(smin);
         smin += __shfl_xor(smin, 32, kWave);
         sres += swz_xor16(sres);
         sres += __shfl_xor(sres, 32, kWave);
-        if (valid && cg == 0)
-            a.part[j * a.ntw + slab * kSlabWaves + wave] = make_float2(smin, sres);
+        pend_j = valid ? j : -1;
+        pend_part = make_float2(smin, sres);
+        pend_ldx = ldx_v;
+        pend_has_ldx = has_ldx;
     }
+    flush();
 }
 
 // ----------------------------------------------------------------------------- vm_select
 struct SelArgs {
     RowSet rs;
-    int nch, r, ks, ntw;
+    int nch, r, ntw;
     const float* U;
     const uint16_t* W1;
     const uint16_t* W2;
@@ -398,7 +434,7 @@ void vm_select(SelArgs a) {
             for (int s = 0; s < kKS; ++s) {
                 const int rank = 32 * s + 8 * cg;
                 hv[s] = make_uint4(0u, 0u, 0u, 0u);
-                if (s < a.ks && rank < a.r)
+                if (rank < a.r)
                     hv[s] = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(hrow) * a.r + rank);
             }
             const float* urow = a.U + (static_cast<long long>(b) * G + n) * V;
@@ -414,13 +450,13 @@ void vm_select(SelArgs a) {
                 }
             }
             bf16x8 w2f[NT][kKS];
-            load_w2_frags<NT, kKS, kKS>(w2f, a.W2, V, a.r, a.ks, cw, stg);
+            load_w2_frags<NT, kKS, kKS>(w2f, a.W2, V, a.r, cw, stg);
             f32x4 acc[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < kKS; ++s) {
-                if (s < a.ks) {
+                {
                     const bf16x8 hf = __builtin_bit_cast(bf16x8, hv[s]);
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
@@ -548,14 +584,14 @@ hipError_t launch_nt(const VerifyMarkovCall& c, hipStream_t st) {
                        0, st, rs, nch, c.x0, c.x, c.ld_lse, c.part_t, c.d_off, c.rec, cap, c.lse_t);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     VmArgs v;
-    v.V = rs.V; v.r = c.r; v.ks = (c.r + 31) / 32; v.ntw = verify_markov_tiles(rs.V); v.cap = cap;
+    v.V = rs.V; v.r = c.r; v.ntw = verify_markov_tiles(rs.V); v.cap = cap;
     v.U = c.U; v.W1 = static_cast<const uint16_t*>(c.W1); v.W2 = static_cast<const uint16_t*>(c.W2);
     v.Lt = rs.Lt; v.rec = c.rec; v.nd = c.d_off + rs.B; v.part = c.tvpart; v.ldx = c.ldx;
     hipLaunchKernelGGL(vm_tv<NT>, dim3(static_cast<unsigned>(slab_count(rs.V))), dim3(kSlabThreads),
                        VmLds<NT>::Total, st, v);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     SelArgs s;
-    s.rs = rs; s.nch = nch; s.r = c.r; s.ks = v.ks; s.ntw = v.ntw;
+    s.rs = rs; s.nch = nch; s.r = c.r; s.ntw = v.ntw;
     s.U = c.U; s.W1 = v.W1; s.W2 = v.W2; s.x0 = c.x0; s.x = c.x; s.ld_lse = c.ld_lse;
     s.u_acc = c.u_acc; s.u_fin = c.u_fin; s.part_t = c.part_t; s.d_off = c.d_off; s.lse_t = c.lse_t;
     s.part = c.tvpart; s.ldx = c.ldx; s.n_out = c.n_out; s.y_out = c.y_out;

@@ -92,7 +92,8 @@ int dspark_version(void);
  *                         its vocabulary slab of W2 in registers and streams the batch
  *                         through it, and one draw launch that recomputes the chosen tile's
  *                         logits instead of reading them (B > 8, bf16, r <= 256 and
- *                         r % 8 == 0, V % 8 == 0, V <= 163840, B <= 4096 at V > 131072,
+ *                         r % 8 == 0, V % 8 == 0, V <= 163840, B <= 2048 at V > 131072 and
+ *                         B <= 8192 at V > 98304,
  *                         16-byte aligned W1, W2, U and Ld_out). Logits reach memory only
  *                         when Ld_out is given.
  *   DSPARK_PATH_MFMA      one bf16 MFMA projection per position (B > 8, bf16 factors, where

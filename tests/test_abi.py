@@ -67,8 +67,10 @@ def test_draft_path_host_rules(lib):
     lib.dspark_markov_draft_path.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
     odd = ctypes.c_void_p(0x1002)                 # not 16-byte aligned
     assert lib.dspark_markov_draft_path(64, 151936, 256, 1, FAKE, FAKE) == 3     # bf16 slab
-    assert lib.dspark_markov_draft_path(4096, 151936, 256, 1, FAKE, FAKE) == 3   # slab at its B cap
-    assert lib.dspark_markov_draft_path(4097, 151936, 256, 1, FAKE, FAKE) == 1   # MFMA beyond it
+    assert lib.dspark_markov_draft_path(2048, 151936, 256, 1, FAKE, FAKE) == 3   # slab at its B cap
+    assert lib.dspark_markov_draft_path(2049, 151936, 256, 1, FAKE, FAKE) == 1   # MFMA beyond it
+    assert lib.dspark_markov_draft_path(8192, 129280, 256, 1, FAKE, FAKE) == 3
+    assert lib.dspark_markov_draft_path(8193, 129280, 256, 1, FAKE, FAKE) == 1
     assert lib.dspark_markov_draft_path(64, 163848, 256, 1, FAKE, FAKE) == 1     # V past the slab cap
     assert lib.dspark_markov_draft_path(9, 2056, 16, 1, FAKE, FAKE) == 3
     assert lib.dspark_markov_draft_path(64, 151936, 256, 0, FAKE, FAKE) == 0     # fp32: sweep
