@@ -64,6 +64,12 @@ size_t draft_part_count(int B, int V) {
     return static_cast<size_t>(B) * dspark::draft_part_tiles(V);
 }
 
+// flags / slots of the one-launch draft forms (single request, or slab)
+size_t draft_slot_bytes(int V, int gamma) {
+    const size_t a = dspark::draft_resident_slot_bytes(V, gamma), b = dspark::draft_slab_flag_bytes(V, gamma);
+    return a > b ? a : b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,7 +102,7 @@ size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma) {
     if (B < 1 || V < 1 || gamma < 1) return 0;
     return 2 * align_up(draft_part_count(B, V) * sizeof(float2)) +
            2 * align_up(static_cast<size_t>(B) * V * sizeof(float)) +
-           align_up(dspark::draft_resident_slot_bytes(V, gamma));
+           align_up(draft_slot_bytes(V, gamma));
 }
 
 int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const void* W1,
@@ -130,7 +136,7 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
         dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
     dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
     dc.L_out = Ld_out != nullptr;
-    dc.slots = c.take<float2>(dspark::draft_resident_slot_bytes(V, gamma) / sizeof(float2));
+    dc.slots = c.take<float2>(draft_slot_bytes(V, gamma) / sizeof(float2));
     const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "markov_draft");
     return ok();

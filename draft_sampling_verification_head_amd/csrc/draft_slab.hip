@@ -5,24 +5,35 @@
 // (rank r = 256), added to the backbone logits U_k; x_k is drawn from softmax(U_k + B_k).
 // ([P3] = the concept note "DSpark Speculative Decoding".)
 //
-// Step kernel (draft_slab_step), one launch per draft position:
-//   - One workgroup of 8 waves per vocabulary slab of 128 * NT columns. Wave w owns the
-//     16 * NT columns of its "wave tile" and keeps W2 for those columns, all ranks, in
-//     registers as MFMA A fragments of W2^T (v_mfma_f32_16x16x32_bf16: 16 columns x 32 ranks
-//     per fragment, NT * 8 fragments). W2 is read from HBM once per launch, staged through a
-//     wave-private LDS area that turns rank-major rows into rank-contiguous fragments.
-//   - The batch then streams through the slab in groups of 16 requests. A group's U_k rows
-//     (16 x 128 NT floats) and gathered W1 rows (16 x 256 bf16) arrive in LDS by direct
-//     global-to-LDS loads, issued two groups ahead into one of three buffers, so HBM keeps
-//     two groups in flight while the current one is multiplied.
-//   - Per group and wave: NT * r/32 MFMAs give the bias for 16 requests x 16 * NT columns;
-//     the epilogue adds U_k, optionally stores the logits, and reduces each request's
-//     columns of the wave tile to (max, sum exp(l - max)), the tile partial the draw uses.
-// Draw kernel (draft_slab_select), one wave per request: merges the request's tile partials
-// in tile order, picks the tile that holds the inverse-CDF point, and recomputes that tile's
-// logits with the same MFMA sequence on the same operands. A fragment column of the MFMA
+// Stream (one position): one workgroup of 8 waves per vocabulary slab of 128 * NT columns.
+// Wave w owns the 16 * NT columns of its "wave tile" and keeps W2 for those columns, all
+// ranks, in registers as MFMA A fragments of W2^T (v_mfma_f32_16x16x32_bf16: 16 columns x 32
+// ranks per fragment, NT * 8 fragments), staged once through a wave-private LDS area that
+// turns rank-major rows into rank-contiguous fragments. The batch streams through the slab in
+// groups of 16 requests: U_k tiles and gathered W1 rows arrive in LDS by direct loads three
+// groups ahead, the MFMAs give the bias of 16 requests x 16 NT columns per wave, and the
+// epilogue adds U_k, optionally stores the logits, and reduces each request's columns of the
+// wave tile to (max, sum exp(l - max)), the tile partial the draw uses.
+//
+// Draw (one request): a two-level pick. The 8 wave-tile partials of each slab are merged in
+// tile order into a slab partial; the request's slab partials give the slab that holds the
+// inverse-CDF point, and that slab's 8 tile partials the tile. The chosen tile's logits are
+// then recomputed with the same MFMA sequence on the same operands. A column of an MFMA
 // result depends only on that column's operands, so the recomputed logits are bit-identical
-// to the step's and the logits never need to be written to memory.
+// to the stream's and the logits never need to be written to memory.
+//
+// Two launch shapes, which draw the same tokens bit for bit:
+//   - per position, a stream launch (draft_slab_step, which can also store the logits) and a
+//     draw launch (draft_slab_select, one wave per request, which merges the slab partials
+//     from the tile partials itself and loads the chosen tile's W2 fragments);
+//   - one persistent launch for all positions (draft_slab_resident) when the logits are not
+//     wanted and every slab workgroup fits on the device at once. W2 is loaded once per call;
+//     each position runs in three phases separated by flag barriers (as in the single-request
+//     resident draft): the stream, which also merges each group's slab partials through LDS
+//     and publishes them; the slab picks, each workgroup for its share of the requests; the
+//     draws, each by the wave that holds the chosen tile's W2 fragments in registers. Polling
+//     is bounded; a workgroup that gives up writes -1 tokens for its requests' remaining
+//     positions and stops, so the launch drains.
 #include "common.h"
 #include "draw.h"
 #include "kernels.h"
@@ -37,16 +48,25 @@ constexpr int kGrp = 16;                 // requests per group (MFMA N)
 constexpr int kHBuf = kGrp * kHRow;      // 8 KB of gathered W1 rows per group
 
 struct SlabArgs {
-    int B, V, r, gamma, k, ntw;
+    int B, V, r, gamma, ntw, G;
     const float* U;           // [B][gamma][V]
     const uint16_t* W1;       // [V][r] bf16
     const uint16_t* W2;       // [r][V] bf16
-    const int32_t* tok;       // x_{k-1}: tok[b * tok_stride]
-    int tok_stride;
-    float* L;                 // logits rows L + b * L_bstride, or null (not stored)
+    const int32_t* x0;        // [B]
+    const float* u;           // [B][gamma]
+    int32_t* x_out;           // [B][gamma]
+    float* q_out;
+    float* lse_out;
+    float* L;                 // step: logits rows of the position, L + b * L_bstride
     long long L_bstride;
     float2* part;             // [B][ntw] (max, sum exp) per request and wave tile
+    float2* spart;            // resident: [B][G] the same per request and slab (8 wave tiles)
+    unsigned long long* flags;   // resident: [3][gamma][G], kEmpty until published
+    float4* picks;            // resident: [B] (tile, max, lse, mass left in the tile)
 };
+
+constexpr unsigned kSpinMax = 1u << 20;             // bounded flag wait, about a second
+constexpr unsigned long long kEmpty = ~0ull;
 
 // LDS: [U0][U1][H0][H1][U2][H2][H3][tokens]. U slot i holds group g = i (mod 3), every wave's
 // own tiles (wave-private); H slot j holds group g = j (mod 4), shared by the waves. The W2
@@ -66,69 +86,99 @@ __device__ __forceinline__ int hbuf_off(int j) {
 template <int NT>
 constexpr int tok_off() { return 3 * ubuf_bytes<NT>() + 4 * kHBuf; }
 
-// Pipeline (per wave, three groups of loads in flight while a group is computed):
-//   wait for group g's loads; store group g - 1's results; copy this wave's U_k tiles of
-//   group g into registers (the wave's U slot is then free); barrier (group g's W1 rows are
-//   visible, every wave is done with group g - 1's W1 slot); issue group g + 3's loads into
-//   the freed slots; MFMA and epilogue of group g.
-// The stores of group g - 1 are issued before group g + 3's loads, so that the loads issued
-// after group g's are always the 2 (NT + 1) of groups g + 1 and g + 2 (plus stores that
-// precede them): vector memory loads complete in order, so once at most 2 (NT + 1)
-// operations are outstanding, group g's loads have landed.
-template <int NT, bool LOUT>
-__global__ __launch_bounds__(kSlabThreads)
-void draft_slab_step(SlabArgs a) {
+
+// Device-scope accesses for data that other workgroups of the same launch read or wrote.
+__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __builtin_bit_cast(unsigned long long, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_coherent(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long load_coherent(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads of group g of position k, NT + 1 direct-to-LDS instructions per wave, every lane
+// active (addresses of absent requests / columns / ranks are clamped to valid memory; the
+// epilogue masks those values), so each wave issues exactly NT + 1 of them.
+//  U: wave w fills its tiles w NT .. w NT + NT - 1 of the slab, 1 KB each ([16 req][16 col]);
+//     lane l loads request l / 4, 4-column chunk (l % 4) ^ ((l / 16) % 4), an XOR swizzle that
+//     makes the register copy's reads bank-conflict free.
+//  H: wave w fills rows 2w, 2w + 1 (512 bytes each); lane l loads 16-byte piece
+//     (l % 32) ^ (row % 16) of the row, again a swizzle for the fragment reads.
+// PARTS: 1 = the U loads only, 2 = the H load only, 3 = both.
+template <int NT, int PARTS = 3>
+__device__ __forceinline__ void issue_group(const SlabArgs& a, int k, int g, char* sm, const int* stok) {
     using S = Slab<NT>;
-    constexpr int UB = ubuf_bytes<NT>();
-    constexpr int NL = NT + 1;                        // direct loads per wave and group
-    static_assert(kSlabWaves * S::Stage <= UB + 2 * kHBuf, "W2 staging fits in U2 + H2 + H3");
-    extern __shared__ __align__(16) char sm[];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int slab = blockIdx.x;
-    const long long cw = static_cast<long long>(slab) * S::SW + wave * S::WC;
-    const int ng = (a.B + kGrp - 1) / kGrp;
-    int* stok = reinterpret_cast<int*>(sm + tok_off<NT>());
-
-    for (int b = tid; b < a.B; b += kSlabThreads) {
-        const int t = a.tok[static_cast<long long>(b) * a.tok_stride];
-        stok[b] = (t >= 0 && t < a.V) ? t : -1;       // dead request: no bias, -inf logits
-    }
-    __syncthreads();
-
-    // Loads of group g, NT + 1 direct-to-LDS instructions per wave, every lane active
-    // (addresses of absent requests / columns / ranks are clamped to valid memory; the
-    // epilogue masks those values), so each wave issues exactly NT + 1 of them.
-    //  U: wave w fills its tiles w NT .. w NT + NT - 1 of the slab, 1 KB each ([16 req][16 col]);
-    //     lane l loads request l / 4, 4-column chunk (l % 4) ^ ((l / 16) % 4), an XOR swizzle
-    //     that makes the register copy's reads bank-conflict free.
-    //  H: wave w fills rows 2w, 2w + 1 (512 bytes each); lane l loads 16-byte piece
-    //     (l % 32) ^ (row % 16) of the row, again a swizzle for the fragment reads.
+    const int lane = opaque_lane(), wave = threadIdx.x / kWave;
+    const long long cw = static_cast<long long>(blockIdx.x) * S::SW + wave * S::WC;
     const int u_rq = lane >> 2, u_ch = (lane & 3) ^ ((lane >> 4) & 3);
     const int h_row = 2 * wave + (lane >> 5), h_piece = (lane & 31) ^ (h_row & 15);
-    auto issue = [&](int g) {
-        const int m0 = g * kGrp;
-        const int b = min(m0 + u_rq, a.B - 1);
-        const float* urow = a.U + (static_cast<long long>(b) * a.gamma + a.k) * a.V;
-        char* ub = sm + ubuf_off<NT>(g % 3) + wave * NT * 1024;
+    const int m0 = g * kGrp;
+    const int b = min(m0 + u_rq, a.B - 1);
+    const float* urow = a.U + (static_cast<long long>(b) * a.gamma + k) * a.V;
+    const uint32_t ub = lds_addr(sm) + ubuf_off<NT>(g % 3) + wave * NT * 1024;
+    if (PARTS & 1) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             long long col = cw + 16 * t + 4 * u_ch;
             if (col >= a.V) col = 0;
             lds_dma16(urow + col, ub + t * 1024);
         }
-        int tk = (m0 + h_row < a.B) ? stok[m0 + h_row] : -1;
-        if (tk < 0) tk = 0;
-        const int piece = (8 * h_piece < a.r) ? h_piece : 0;
-        lds_dma16(a.W1 + static_cast<long long>(tk) * a.r + 8 * piece, sm + hbuf_off<NT>(g & 3) + wave * 1024);
-    };
+    }
+    if (!(PARTS & 2)) return;
+    int tk = (m0 + h_row < a.B) ? stok[m0 + h_row] : -1;
+    if (tk < 0) tk = 0;
+    const int piece = (8 * h_piece < a.r) ? h_piece : 0;
+    lds_dma16(a.W1 + static_cast<long long>(tk) * a.r + 8 * piece,
+              lds_addr(sm) + hbuf_off<NT>(g & 3) + wave * 1024);
+}
 
-    issue(0);
-    if (ng > 1) issue(1);
-    bf16x8 w2f[NT][kKS];
-    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
-    wait_lgkm0();
-    __syncthreads();                                  // every wave is done with the staging area
-    if (ng > 2) issue(2);
+// One position of the stream for this workgroup (slab): the tokens x_{k-1} of every request
+// are in stok (-1: dead request). The caller has issued the loads of the first groups:
+// `issued` whole groups (0 or 2), or with PRE the U loads of groups 0 .. min(ng, 3) - 1 (U
+// does not depend on the tokens), whose H loads are then issued here first.
+// Pipeline per wave, three groups of loads in flight while a group is computed: wait for
+// group g's loads; store group g - 1's results; copy this wave's U_k tiles of group g into
+// registers (the wave's U slot is then free); barrier (group g's W1 rows are visible, every
+// wave is done with group g - 1's W1 slot); issue group g + 3's loads; MFMA and epilogue of
+// group g. The stores of group g - 1 are issued before group g + 3's loads. Vector memory
+// operations complete in order, so group g's loads have landed once no more operations are
+// outstanding than were issued after group g's last load (the loads of later groups counted;
+// stores between them only make the wait longer): 2 (NT + 1) in the steady state, fewer in
+// the first groups and at the tail (after_group).
+template <int NT, bool LOUT, bool PRE>
+__device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, const bf16x8 (&w2f)[NT][kKS],
+                                            char* sm, const int* stok, int issued) {
+    using S = Slab<NT>;
+    constexpr int NL = NT + 1;                        // direct loads per wave and group
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int slab = blockIdx.x;
+    const long long cw = static_cast<long long>(slab) * S::SW + wave * S::WC;
+    const int ng = (a.B + kGrp - 1) / kGrp;
+
+    auto issue = [&](int g) { issue_group<NT>(a, k, g, sm, stok); };
+    const int npre = ng < 3 ? ng : 3;                 // groups issued before the loop
+    if (PRE) {
+        for (int g = 0; g < npre; ++g) issue_group<NT, 2>(a, k, g, sm, stok);
+    } else {
+        for (int g = issued; g < npre; ++g) issue(g);
+    }
+    // loads issued after group g's last load when group g is waited for
+    auto after_group = [&](int g) {
+        int n = 0;
+        if (g < 3) n += (npre - 1 - g) * (PRE ? 1 : NL);   // later groups of the prologue
+        for (int j = (g < 3 ? 0 : g - 2); j < g; ++j)       // groups j + 3 issued in loop j
+            if (j + 3 < ng) n += NL;
+        return n;
+    };
 
     const int rq = lane & 15, cg = lane >> 4;
     const int upos = 4 * rq + (cg ^ ((rq >> 2) & 3));  // this lane's 16 bytes of a U tile
@@ -144,12 +194,16 @@ void draft_slab_step(SlabArgs a) {
                 if (col < a.V) *reinterpret_cast<float4*>(a.L + pend_b * a.L_bstride + col) = pend_l[LOUT ? t : 0];
             }
         }
-        if (lane < kGrp)
-            a.part[static_cast<long long>(pend_b) * a.ntw + slab * kSlabWaves + wave] = pend_part;
+        if (lane < kGrp) a.part[static_cast<long long>(pend_b) * a.ntw + slab * kSlabWaves + wave] = pend_part;
     };
+
     for (int g = 0; g < ng; ++g) {
-        if (g + 2 < ng) wait_vm_lgkm<2 * NL>();
-        else if (g + 1 < ng) wait_vm_lgkm<NL>();
+        const int n = after_group(g);                 // wait-uniform: a scalar branch
+        if (n >= 2 * NL) wait_vm_lgkm<2 * NL>();
+        else if (n >= NL + 1) wait_vm_lgkm<NL + 1>();
+        else if (n >= NL) wait_vm_lgkm<NL>();
+        else if (n >= 2) wait_vm_lgkm<2>();
+        else if (n >= 1) wait_vm_lgkm<1>();
         else wait_vm_lgkm<0>();
         flush();
         float4 u4[NT];
@@ -166,9 +220,10 @@ void draft_slab_step(SlabArgs a) {
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         // B fragments one rank chunk ahead; the empty asm keeps the compiler from hoisting
         // every chunk's fragment at once, which would not fit beside the W2 fragments
+        const int hl = opaque_lane(), hrq = hl & 15, hcg = hl >> 4;
         auto hfrag = [&](int s) {
-            const int piece = (4 * s + cg) ^ rq;
-            return *reinterpret_cast<const bf16x8*>(H + rq * kHRow + 16 * piece);
+            const int piece = (4 * s + hcg) ^ hrq;
+            return *reinterpret_cast<const bf16x8*>(H + hrq * kHRow + 16 * piece);
         };
         bf16x8 hf = hfrag(0);
 #pragma unroll
@@ -222,66 +277,90 @@ void draft_slab_step(SlabArgs a) {
     flush();
 }
 
-struct SlabSelArgs {
-    int B, V, r, gamma, k, ntw;
-    const float* U;
-    const uint16_t* W1;
-    const uint16_t* W2;
-    const int32_t* tok;       // x_{k-1}
-    int tok_stride;
-    const float2* part;
-    const float* u;           // [B][gamma]
-    int32_t* x_out;
-    float* q_out;
-    float* lse_out;
-};
+// Draw of request b at position k, by one wave (all 64 lanes active), in three parts.
+//  slab_pick:      the slab (8 wave tiles) holding the inverse-CDF point, from the request's
+//                  slab partials, and the mass still to cover inside it. COH (resident): the
+//                  slab partials the stream merged, read at device scope; else merged here
+//                  from the tile partials (lane l holds tiles [32 l, 32 l + 32), that is slabs
+//                  [4 l, 4 l + 4)) with the same arithmetic.
+//  slab_walk:      the tile of that slab, from its 8 tile partials (walk_slab8).
+//  slab_recompute: that tile's logits rebuilt with the MFMA sequence of the stream, from the
+//                  tile's W2 fragments, the W1 row of x_{k-1} (tk, valid when the request has
+//                  mass) and U_k; then the in-tile rescan. `rowv` holds the tile's logits.
+// slab_finish writes the token (COH: at device scope), p(token) and lse.
+constexpr int kSlabRegs = kSelRegs / kSlabWaves;     // slabs per lane (256 slabs at most)
 
-// One wave (one workgroup) per request: tile pick from the partials, MFMA recompute of that
-// tile's logits, in-tile rescan. Every W2 load of the tile is in flight at once (one LDS
-// staging slot per rank chunk), and the W1 row is fetched before the merge.
-template <int NT>
-__global__ __launch_bounds__(kWave)
-void draft_slab_select(SlabSelArgs a) {
-    using S = Slab<NT>;
-    constexpr int CPL = (S::WC + kWave - 1) / kWave;
-    __shared__ __align__(16) char stg[kKS * S::Stage];
-    __shared__ float rowv[S::WC];
-    const int lane = threadIdx.x;
-    const int b = blockIdx.x;
-    const long long o = static_cast<long long>(b) * a.gamma + a.k;
-    const DrawOut out{a.x_out + o, a.q_out ? a.q_out + o : nullptr,
-                      a.lse_out ? a.lse_out + o : nullptr, true};
-    const int rq = lane & 15, cg = lane >> 4;
-
-    // the W1 row of the previous token in every one of the 16 request columns of the B
-    // operand (only used when the request has mass, which implies a valid token)
-    int tk = a.tok[static_cast<long long>(b) * a.tok_stride];
-    if (tk < 0 || tk >= a.V) tk = 0;
-    uint4 hv[kKS];
+template <bool COH>
+__device__ __forceinline__ TilePick slab_pick(const SlabArgs& a, int b, int k) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float u = a.u[static_cast<long long>(b) * a.gamma + k];
+    float2 sp[kSlabRegs];
+    if (COH) {
+        const float2* P = a.spart + static_cast<long long>(b) * a.G;
 #pragma unroll
-    for (int s = 0; s < kKS; ++s) {
-        const int rank = 32 * s + 8 * cg;
-        hv[s] = make_uint4(0u, 0u, 0u, 0u);
-        if (rank < a.r) hv[s] = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
+        for (int j = 0; j < kSlabRegs; ++j) {
+            const int i = lane * kSlabRegs + j;
+            sp[j] = (i < a.G) ? load_part<true>(P + i) : make_float2(-INFINITY, 0.0f);
+        }
+    } else {
+        const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw);
+#pragma unroll
+        for (int j = 0; j < kSlabRegs; ++j) {
+            float2 p[8];
+            const int i = lane * kSelRegs + 8 * j;    // first tile of slab 4 lane + j
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float4 v = make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+                if (i < a.ntw) v = P4[i / 2 + t];     // ntw is a multiple of 8: slabs are whole
+                p[2 * t] = make_float2(v.x, v.y);
+                p[2 * t + 1] = make_float2(v.z, v.w);
+            }
+            sp[j] = merge_slab8(p);
+        }
     }
-    // lane l holds tiles [32 l, 32 l + 32): 16 loads of two partials each
-    float2 p[kSelRegs];
-    const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw);
+    return pick_tile<kSlabRegs>(sp, u);
+}
+
+// The tile of slab `sl` for a request picked there (m, tprime from slab_pick): the global
+// tile index and the mass left inside it.
+__device__ __forceinline__ TilePick slab_walk(const SlabArgs& a, int b, int sl, const TilePick& tp) {
+    const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw +
+                                                       sl * kSlabWaves);
+    float2 p[8];
 #pragma unroll
-    for (int t = 0; t < kSelRegs / 2; ++t) {
-        const int i = lane * kSelRegs + 2 * t;        // ntw is a multiple of 8: pairs are whole
-        float4 v = make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
-        if (i < a.ntw) v = P4[i / 2];
+    for (int t = 0; t < 4; ++t) {
+        const float4 v = P4[t];
         p[2 * t] = make_float2(v.x, v.y);
         p[2 * t + 1] = make_float2(v.z, v.w);
     }
-    const TilePick tp = pick_tile<kSelRegs>(p, a.u[o]);
-    if (tp.tile < 0) {
-        if (lane == 0) put(out, -1, 0.0f, -INFINITY);
-        return;
-    }
+    const SlabWalk w = walk_slab8(p, tp.m, tp.tprime);
+    TilePick r = tp;
+    r.tile = w.w < 0 ? -1 : sl * kSlabWaves + w.w;
+    r.tprime = w.tprime;
+    return r;
+}
+
+template <bool COH>
+__device__ __forceinline__ void slab_finish(const SlabArgs& a, int b, int k, int tok, float q, float lse) {
+    if ((threadIdx.x & (kWave - 1)) != 0) return;
+    const long long o = static_cast<long long>(b) * a.gamma + k;
+    if (COH) store_coherent(a.x_out + o, tok);
+    else a.x_out[o] = tok;
+    if (a.q_out) a.q_out[o] = q;
+    if (a.lse_out) a.lse_out[o] = lse;
+}
+
+template <int NT, bool COH>
+__device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, int tk,
+                                               const TilePick& tp, const bf16x8 (&w2f)[NT][kKS],
+                                               float* rowv) {
+    using S = Slab<NT>;
+    constexpr int CPL = (S::WC + kWave - 1) / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rq = lane & 15, cg = lane >> 4;
+    if (tk < 0 || tk >= a.V) tk = 0;
     const long long cw = static_cast<long long>(tp.tile) * S::WC;
-    const float* urow = a.U + (static_cast<long long>(b) * a.gamma + a.k) * a.V;
+    const float* urow = a.U + (static_cast<long long>(b) * a.gamma + k) * a.V;
     float4 u4[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -289,32 +368,32 @@ void draft_slab_select(SlabSelArgs a) {
         u4[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (rq == 0 && col < a.V) u4[t] = *reinterpret_cast<const float4*>(urow + col);
     }
-    bf16x8 w2f[NT][kKS];
-    load_w2_frags<NT, kKS, kKS>(w2f, a.W2, a.V, a.r, cw, stg);
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
-        {
-            const bf16x8 hf = __builtin_bit_cast(bf16x8, hv[s]);
+        // the W1 row of the previous token in every one of the 16 request columns
+        const int rank = 32 * s + 8 * cg;
+        uint4 hv = make_uint4(0u, 0u, 0u, 0u);
+        if (rank < a.r) hv = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
+        const bf16x8 hf = __builtin_bit_cast(bf16x8, hv);
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
-        }
+        for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
     }
     if (rq == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const bool ok = cw + 16 * t + 4 * cg < a.V;
-            float* rv = &rowv[16 * t + 4 * cg];
+            float* rv = rowv + 16 * t + 4 * cg;
             rv[0] = ok ? u4[t].x + acc[t][0] : -INFINITY;
             rv[1] = ok ? u4[t].y + acc[t][1] : -INFINITY;
             rv[2] = ok ? u4[t].z + acc[t][2] : -INFINITY;
             rv[3] = ok ? u4[t].w + acc[t][3] : -INFINITY;
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): the row is in LDS
+    wait_lgkm0();                                     // the row is in LDS
     __builtin_amdgcn_wave_barrier();
     float lv[CPL];
 #pragma unroll
@@ -322,11 +401,255 @@ void draft_slab_select(SlabSelArgs a) {
         const int c = lane * CPL + j;
         lv[j] = (c < S::WC) ? rowv[c] : -INFINITY;
     }
-    rescan_values<CPL>(lv, cw + lane * CPL, static_cast<int>(cw), tp.m, tp.lse, tp.tprime, out);
+    const DrawOut none{nullptr, nullptr, nullptr, false};
+    const int tok = rescan_values<CPL>(lv, cw + lane * CPL, static_cast<int>(cw), tp.m, tp.lse,
+                                       tp.tprime, none);
+    const int rel = tok - static_cast<int>(cw), owner = rel / CPL, jj = rel - owner * CPL;
+    float mine = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+        if (j == jj) mine = lv[j];
+    const float lx = wave_bcast(mine, owner);
+    slab_finish<COH>(a, b, k, tok, __expf(lx - tp.lse), tp.lse);
+}
+
+// One position: stream launch (W2 staged once per launch; the logits stored when LOUT).
+template <int NT, bool LOUT>
+__global__ __launch_bounds__(kSlabThreads)
+void draft_slab_step(SlabArgs a, int k) {
+    using S = Slab<NT>;
+    constexpr int UB = ubuf_bytes<NT>();
+    static_assert(kSlabWaves * S::Stage <= UB + 2 * kHBuf, "W2 staging fits in U2 + H2 + H3");
+    extern __shared__ __align__(16) char sm[];
+    const int tid = threadIdx.x, wave = tid / kWave;
+    const long long cw = static_cast<long long>(blockIdx.x) * S::SW + wave * S::WC;
+    int* stok = reinterpret_cast<int*>(sm + tok_off<NT>());
+    const int32_t* tok = k ? a.x_out + (k - 1) : a.x0;
+    const long long stride = k ? a.gamma : 1;
+    for (int b = tid; b < a.B; b += kSlabThreads) {
+        const int t = tok[b * stride];
+        stok[b] = (t >= 0 && t < a.V) ? t : -1;       // dead request: no bias, -inf logits
+    }
+    __syncthreads();
+    // the first two groups' loads go out before the W2 staging (whose area they do not use)
+    const int ng = (a.B + kGrp - 1) / kGrp;
+    for (int g = 0; g < 2 && g < ng; ++g) issue_group<NT>(a, k, g, sm, stok);
+    bf16x8 w2f[NT][kKS];
+    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
+    wait_lgkm0();
+    __syncthreads();                                  // every wave is done with the staging area
+    slab_stream<NT, LOUT, false>(a, k, w2f, sm, stok, ng < 2 ? ng : 2);
+}
+
+// One position: draw launch, one workgroup (one wave) per request; every W2 load of the
+// chosen tile is in flight at once (one LDS staging slot per rank chunk).
+template <int NT>
+__global__ __launch_bounds__(kWave)
+void draft_slab_select(SlabArgs a, int k) {
+    using S = Slab<NT>;
+    __shared__ __align__(16) char stg[kKS * S::Stage];
+    __shared__ float rowv[S::WC];
+    const int b = blockIdx.x;
+    const int tk = k ? a.x_out[static_cast<long long>(b) * a.gamma + k - 1] : a.x0[b];
+    const TilePick sp = slab_pick<false>(a, b, k);
+    const TilePick tp = sp.tile < 0 ? sp : slab_walk(a, b, sp.tile, sp);
+    if (tp.tile < 0) {
+        slab_finish<false>(a, b, k, -1, 0.0f, -INFINITY);
+        return;
+    }
+    bf16x8 w2f[NT][kKS];
+    load_w2_frags<NT, kKS, kKS>(w2f, a.W2, a.V, a.r, static_cast<long long>(tp.tile) * S::WC, stg);
+    slab_recompute<NT, false>(a, b, k, tk, tp, w2f, rowv);
+}
+
+// All positions in one launch (see the file comment). Per position k three flag rows,
+// [f][k][g] for f = 0, 1, 2: workgroup g's partials, its tile picks, its tokens published.
+// The draw is split so that no workgroup needs a second copy of W2: workgroup g picks the
+// tiles of its share of the requests (b = g, g + G, ...), and the wave that holds a picked
+// tile in registers recomputes that tile's logits and draws the token.
+template <int NT>
+__global__ __launch_bounds__(kSlabThreads)
+void draft_slab_resident(SlabArgs a) {
+    using S = Slab<NT>;
+    constexpr int UB = ubuf_bytes<NT>();
+    static_assert(kSlabWaves * S::Stage <= UB + 2 * kHBuf, "W2 staging fits in U2 + H2 + H3");
+    extern __shared__ __align__(16) char sm[];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int slab = blockIdx.x, G = a.G;
+    // set by a wave whose flag wait ran out; after the tokens (the launch adds kResidentExtra)
+    volatile int& gave_up = *reinterpret_cast<int*>(sm + tok_off<NT>() + 4 * a.B);
+    const long long cw = static_cast<long long>(slab) * S::SW + wave * S::WC;
+    const int my_tile = slab * kSlabWaves + wave;
+    const int ng = (a.B + kGrp - 1) / kGrp, npre = ng < 3 ? ng : 3;
+    int* stok = reinterpret_cast<int*>(sm + tok_off<NT>());
+    // the draw's LDS lies in the W1 row slots H0 + H1, idle between streams (the U slots then
+    // hold the next position's first groups): each wave's logit row, then the picked slabs
+    float* rowv = reinterpret_cast<float*>(sm + 2 * UB) + wave * S::WC;
+    int* pslab = reinterpret_cast<int*>(sm + 2 * UB + kSlabWaves * S::WC * 4);
+    if (tid == 0) gave_up = 0;
+
+    bf16x8 w2f[NT][kKS];
+    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
+    wait_lgkm0();
+    __syncthreads();                                  // every wave is done with the staging area
+    // U loads of the first groups of a position (they do not depend on the tokens)
+    auto prefetch_u = [&](int kk) {
+        for (int g = 0; g < npre; ++g) issue_group<NT, 1>(a, kk, g, sm, stok);
+    };
+    prefetch_u(0);
+
+    auto flag_row = [&](int f, int k) { return a.flags + (static_cast<long long>(f) * a.gamma + k) * G; };
+    // every wave waits until all G flags of `row` are set; false after the spin bound
+    auto wait_flags = [&](const unsigned long long* row) {
+        for (unsigned n = 0;; ++n) {
+            bool missing = false;
+            for (int i = lane; i < G; i += kWave) missing |= load_coherent(row + i) == kEmpty;
+            if (!__any(missing)) return true;
+            if (n > kSpinMax) return false;
+            __builtin_amdgcn_s_sleep(1);
+        }
+    };
+    // publishes flag (f, k) of this workgroup once every thread's stores are visible
+    auto publish = [&](int f, int k) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) store_coherent(flag_row(f, k) + slab, 0ull);
+    };
+    int k = 0;
+    for (; k < a.gamma; ++k) {
+        // tokens x_{k-1} of every request: x0, or the previous position's draws
+        if (k > 0 && !wait_flags(flag_row(2, k - 1)) && lane == 0) gave_up = 1;
+        __syncthreads();                              // also: every wave is done with the draw LDS
+        if (gave_up) break;
+        for (int b = tid; b < a.B; b += kSlabThreads) {
+            const int t = k ? load_coherent(a.x_out + static_cast<long long>(b) * a.gamma + k - 1) : a.x0[b];
+            stok[b] = (t >= 0 && t < a.V) ? t : -1;
+        }
+        __syncthreads();
+        slab_stream<NT, false, true>(a, k, w2f, sm, stok, 0);
+        // slab partials of every request for this slab, merged from the tile partials this
+        // workgroup's waves stored (visible within the workgroup after the barrier)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int b = tid; b < a.B; b += kSlabThreads) {
+            const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw +
+                                                               slab * kSlabWaves);
+            float2 p[8];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float4 v = P4[t];
+                p[2 * t] = make_float2(v.x, v.y);
+                p[2 * t + 1] = make_float2(v.z, v.w);
+            }
+            store_coherent(a.spart + static_cast<long long>(b) * G + slab, merge_slab8(p));
+        }
+        publish(0, k);
+
+        // slab picks of this workgroup's requests, one wave per request
+        if (!wait_flags(flag_row(0, k)) && lane == 0) gave_up = 1;
+        __syncthreads();
+        if (gave_up) break;
+        for (int b = slab + G * wave; b < a.B; b += G * kSlabWaves) {
+            const TilePick tp = slab_pick<true>(a, b, k);
+            if (lane == 0) {
+                unsigned long long* rec = reinterpret_cast<unsigned long long*>(a.picks + b);
+                store_coherent(rec, __builtin_bit_cast(unsigned long long, make_float2(__int_as_float(tp.tile), tp.m)));
+                store_coherent(rec + 1, __builtin_bit_cast(unsigned long long, make_float2(tp.lse, tp.tprime)));
+            }
+            if (tp.tile < 0) slab_finish<true>(a, b, k, -1, 0.0f, -INFINITY);
+        }
+        publish(1, k);
+
+        // requests picked in this slab: every wave walks the slab's 8 tile partials (written
+        // by this workgroup), and the wave holding the chosen tile in registers draws. The
+        // picked slabs of all requests are staged in LDS after the waves' logit rows.
+        if (!wait_flags(flag_row(1, k)) && lane == 0) gave_up = 1;
+        for (int b = tid; b < a.B; b += kSlabThreads)
+            pslab[b] = static_cast<int>(load_coherent(reinterpret_cast<const unsigned long long*>(a.picks + b)));
+        __syncthreads();
+        if (gave_up) break;
+        for (int base = 0; base < a.B; base += kWave) {
+            const int b = base + lane;
+            unsigned long long hit = __ballot(b < a.B && pslab[min(b, a.B - 1)] == slab);
+            while (hit) {
+                const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                hit &= hit - 1;
+                const int bb = base + f;
+                const unsigned long long* rec = reinterpret_cast<const unsigned long long*>(a.picks + bb);
+                const float2 r0 = __builtin_bit_cast(float2, load_coherent(rec));
+                const float2 r1 = __builtin_bit_cast(float2, load_coherent(rec + 1));
+                TilePick sp;
+                sp.tile = slab;
+                sp.m = r0.y;
+                sp.lse = r1.x;
+                sp.tprime = r1.y;
+                const TilePick tp = slab_walk(a, bb, slab, sp);
+                if (tp.tile == my_tile) slab_recompute<NT, true>(a, bb, k, stok[bb], tp, w2f, rowv);
+                else if (tp.tile < 0 && wave == 0) slab_finish<true>(a, bb, k, -1, 0.0f, -INFINITY);
+            }
+        }
+        publish(2, k);
+        if (k + 1 < a.gamma) prefetch_u(k + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);                    // no load in flight at exit
+    if (gave_up) {                                    // this workgroup's requests: -1 from k on
+        for (long long i = tid; i < static_cast<long long>(a.B) * a.gamma; i += kSlabThreads) {
+            const int b = static_cast<int>(i / a.gamma), kk = static_cast<int>(i % a.gamma);
+            if (b % G != slab || kk < k) continue;
+            a.x_out[i] = -1;
+            if (a.q_out) a.q_out[i] = 0.0f;
+            if (a.lse_out) a.lse_out[i] = -INFINITY;
+        }
+    }
+}
+
+__global__ void clear_flags(unsigned long long* f, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) f[i] = kEmpty;
 }
 
 size_t slab_lds_bytes(int nt, int B) {
     return 3 * static_cast<size_t>(kGrp) * kSlabWaves * 16 * nt * 4 + 4 * kHBuf + 4 * static_cast<size_t>(B);
+}
+constexpr size_t kResidentExtra = 16;     // the resident launch's give-up word, after the tokens
+
+struct SlabFit {
+    int cus = -1;
+    int occupancy[kMaxNT + 1] = {-1, -1, -1, -1, -1, -1};
+};
+
+template <int NT>
+int resident_occupancy(size_t smem) {
+    int occ = 0;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_slab_resident<NT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, draft_slab_resident<NT>, kSlabThreads, smem) != hipSuccess)
+        return 0;
+    return occ;
+}
+
+// Whether every slab workgroup of the resident launch can be on the device at once (queried
+// with the largest LDS the path uses, so smaller batches fit as well).
+bool resident_fits(int V) {
+    thread_local SlabFit cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    SlabFit& f = cache[dev];
+    if (f.cus < 0 && hipDeviceGetAttribute(&f.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    const int nt = slab_nt(V);
+    if (f.occupancy[nt] < 0) {
+        const size_t smem = static_cast<size_t>(kLdsBytes);
+        switch (nt) {
+            case 1: f.occupancy[nt] = resident_occupancy<1>(smem); break;
+            case 2: f.occupancy[nt] = resident_occupancy<2>(smem); break;
+            case 3: f.occupancy[nt] = resident_occupancy<3>(smem); break;
+            case 4: f.occupancy[nt] = resident_occupancy<4>(smem); break;
+            default: f.occupancy[nt] = resident_occupancy<5>(smem); break;
+        }
+    }
+    return f.cus > 0 && f.occupancy[nt] >= 1 && slab_count(V) <= f.cus * f.occupancy[nt];
 }
 
 template <int NT>
@@ -334,34 +657,42 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
     SlabArgs a;
     a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma;
     a.ntw = draft_slab_tiles(c.V);
+    a.G = slab_count(c.V);
     a.U = c.U;
     a.W1 = static_cast<const uint16_t*>(c.W1);
     a.W2 = static_cast<const uint16_t*>(c.W2);
+    a.x0 = c.x0; a.u = c.u;
+    a.x_out = c.x_out; a.q_out = c.q_out; a.lse_out = c.lse_out;
+    a.L = nullptr;
     a.L_bstride = c.L_bstride;
-    SlabSelArgs s;
-    s.B = c.B; s.V = c.V; s.r = c.r; s.gamma = c.gamma; s.ntw = a.ntw;
-    s.U = c.U; s.W1 = a.W1; s.W2 = a.W2; s.u = c.u;
-    s.x_out = c.x_out; s.q_out = c.q_out; s.lse_out = c.lse_out;
+    a.flags = reinterpret_cast<unsigned long long*>(c.slots);
+    // resident: the second partial buffer holds the picks [B] and the slab partials [B][G]
+    a.picks = reinterpret_cast<float4*>(c.part[1]);
+    a.spart = c.part[1] + 2 * static_cast<long long>(c.B);
     const size_t smem = slab_lds_bytes(NT, c.B);
-    const dim3 grid(static_cast<unsigned>(slab_count(c.V)));
-    const dim3 sgrid(static_cast<unsigned>(c.B));
+    const dim3 grid(static_cast<unsigned>(a.G));
+    // the resident form also needs the draw's logit rows and the B picked slabs in H0 + H1
+    const bool lds_ok = smem + kResidentExtra <= static_cast<size_t>(kLdsBytes) &&
+                        kSlabWaves * Slab<NT>::WC * 4 + 4 * static_cast<size_t>(c.B) <= 2 * static_cast<size_t>(kHBuf);
+    if (!c.L_out && lds_ok && resident_fits(c.V)) {
+        const int n = 3 * c.gamma * a.G;
+        hipLaunchKernelGGL(clear_flags, dim3((n + 255) / 256), dim3(256), 0, st, a.flags, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        a.part = c.part[0];
+        hipLaunchKernelGGL(draft_slab_resident<NT>, grid, dim3(kSlabThreads), smem + kResidentExtra, st, a);
+        return hipGetLastError();
+    }
     for (int k = 0; k < c.gamma; ++k) {
-        a.k = k;
-        a.tok = k ? c.x_out + (k - 1) : c.x0;
-        a.tok_stride = k ? c.gamma : 1;
         a.L = c.L_out ? c.L[k] : nullptr;
         a.part = c.part[k & 1];
         if (c.L_out)
-            hipLaunchKernelGGL((draft_slab_step<NT, true>), grid, dim3(kSlabThreads), smem, st, a);
+            hipLaunchKernelGGL((draft_slab_step<NT, true>), grid, dim3(kSlabThreads), smem, st, a, k);
         else
-            hipLaunchKernelGGL((draft_slab_step<NT, false>), grid, dim3(kSlabThreads), smem, st, a);
+            hipLaunchKernelGGL((draft_slab_step<NT, false>), grid, dim3(kSlabThreads), smem, st, a, k);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        s.k = k;
-        s.tok = a.tok;
-        s.tok_stride = a.tok_stride;
-        s.part = a.part;
-        hipLaunchKernelGGL(draft_slab_select<NT>, sgrid, dim3(kWave), 0, st, s);
+        hipLaunchKernelGGL(draft_slab_select<NT>, dim3(static_cast<unsigned>(c.B)), dim3(kWave), 0, st, a, k);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -371,6 +702,10 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
 }  // namespace
 
 int draft_slab_tiles(int V) { return slab_count(V) * kSlabWaves; }
+
+size_t draft_slab_flag_bytes(int V, int gamma) {
+    return 3 * static_cast<size_t>(gamma) * slab_count(V) * sizeof(unsigned long long);
+}
 
 bool draft_slab_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
     if (w_dtype != 1 || B <= 8 || r > kMaxRank || (r % 8) != 0 || (V % 8) != 0) return false;

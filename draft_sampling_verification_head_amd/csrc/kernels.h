@@ -22,7 +22,7 @@ struct DraftCall {
     long long L_bstride;
     bool L_out;               // L[k] is the caller's output (else workspace the path may skip)
     float2* part[2];          // tile partials [B][draft_part_tiles(V)] of even / odd steps
-    float2* slots;            // draft_resident_slot_bytes(V, gamma) of workspace (single launch)
+    float2* slots;            // max(draft_resident_slot_bytes, draft_slab_flag_bytes) of workspace
 };
 
 // Vocabulary tiles per request the partial buffers must hold (the finest tiling in use).
@@ -38,6 +38,7 @@ hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st);
 // launch_draft when it applies and U (and the caller's logits output) are 16-byte aligned.
 bool draft_slab_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
 int draft_slab_tiles(int V);
+size_t draft_slab_flag_bytes(int V, int gamma);   // position flags of the one-launch form
 hipError_t launch_draft_slab(const DraftCall& c, hipStream_t st);
 
 // Single-request path with W2 resident in registers (draft_resident.hip), chosen by

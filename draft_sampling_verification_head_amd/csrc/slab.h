@@ -49,13 +49,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* l) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (const __attribute__((address_space(3))) char*)(l)));
 }
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+// The LDS address is a 32-bit byte offset (lds_addr of a __shared__ pointer plus an offset):
+// computing it as an integer keeps the compiler from materialising 64-bit generic pointers
+// into LDS, which it would otherwise hoist out of loops, one register pair per address.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t l) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(l))) : "memory", "m0");
+                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(l)) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t l) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_addr(l))) : "memory", "m0");
+                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(l)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -72,6 +75,15 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // Workgroup barrier without a memory fence: the direct-to-LDS loads are ordered by the
 // explicit vmcnt waits, and the empty asm statements keep the compiler from moving memory
 // accesses across the barrier.
+// The lane index made opaque to the optimiser: per-lane addresses derived from it are then
+// computed where they are used instead of being hoisted out of the loops around that use,
+// where each would hold a register for the whole loop.
+__device__ __forceinline__ int opaque_lane() {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();

@@ -157,7 +157,8 @@ void vm_tv(VmArgs a) {
     // row g * 8 + l % 8 (rows past the end repeat the last row; the epilogue masks them)
     auto meta_issue = [&](int g) {
         const int row = min(g * kRows + (lane & 7), nd - 1);
-        lds_dma4(a.rec + static_cast<long long>(lane >> 3) * a.cap + row, meta + (g & 3) * (kFields * kRows));
+        lds_dma4(a.rec + static_cast<long long>(lane >> 3) * a.cap + row,
+                 lds_addr(meta) + 4 * (g & 3) * (kFields * kRows));
     };
     // U and L_t slices of group g: per tile two 4-byte direct loads (rows 0-3, 4-7); lane l
     // of half h takes row 4h + l / 16, column group ((l / 4) % 4) ^ (row / 4) (a swizzle for
@@ -165,9 +166,9 @@ void vm_tv(VmArgs a) {
     // group, 16-byte piece p of the row at position p ^ w. Every lane issues every load.
     auto issue = [&](int g, int i) {
         const int* mt = meta + (g & 3) * (kFields * kRows);
-        char* ub = sm + i * Ly::Buf;
-        char* lb = ub + Ly::UT;
-        char* hb = ub + 2 * Ly::UT;
+        const uint32_t ub = lds_addr(sm) + i * Ly::Buf;
+        const uint32_t lb = ub + Ly::UT;
+        const uint32_t hb = ub + 2 * Ly::UT;
         // the empty asm makes the column base opaque, so that the per-tile addresses are
         // formed here instead of being hoisted out of the group loop (kept live, they would
         // not fit beside the W2 fragments)
