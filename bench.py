@@ -344,10 +344,12 @@ def main():
     else:
         path = dspark.markov_draft_path(B, t["W1"], t["W2"])
         per_pos = draft_bytes_per_position(c, not rebuild)   # algorithmic bytes of one position
-        if path == "resident":
+        one_launch = dspark.markov_draft_one_launch(B, t["W1"], t["W2"], want_logits=not rebuild)
+        if one_launch:
             # one launch draws all gamma positions (W2 read once, then held in registers); the
-            # timed call also holds the tiny counter-reset kernel that precedes it
-            kernel, units, launch_us = "draft_resident", G, ms_parts["draft"] * 1e3
+            # timed call also holds the tiny flag-reset kernel that precedes it
+            kernel = "draft_resident" if path == "resident" else "draft_slab_resident"
+            units, launch_us = G, ms_parts["draft"] * 1e3
         else:
             # one step kernel per position; the per-position time also carries the draws
             kernel = {"mfma": "draft_step_mfma + draft_select",

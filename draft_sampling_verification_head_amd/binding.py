@@ -23,7 +23,8 @@ STS_NLL, STS_ECE = 0, 1
 # every symbol include/dspark.h declares
 EXPORTS = (
     "dspark_status_string", "dspark_last_error", "dspark_version",
-    "dspark_markov_draft_path", "dspark_markov_draft_workspace_bytes", "dspark_markov_draft",
+    "dspark_markov_draft_path", "dspark_markov_draft_one_launch", "dspark_markov_draft_workspace_bytes",
+    "dspark_markov_draft",
     "dspark_verify_workspace_bytes", "dspark_verify",
     "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
     "dspark_verify_markov_workspace_bytes", "dspark_verify_markov",
@@ -41,6 +42,7 @@ _SIGS = {
     "dspark_last_error": (ctypes.c_char_p, []),
     "dspark_version": (_I, []),
     "dspark_markov_draft_path": (_I, [_I, _I, _I, _I, _P, _P]),
+    "dspark_markov_draft_one_launch": (_I, [_I, _I, _I, _I, _P, _P, _I]),
     "dspark_markov_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_verify_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -146,6 +148,14 @@ def markov_draft_path(B: int, W1, W2) -> str:
     V, r = W1.shape
     wdt = BF16 if W1.dtype == torch.bfloat16 else F32
     return PATH_NAMES[load().dspark_markov_draft_path(B, V, r, wdt, _ptr(W1), _ptr(W2))]
+
+
+def markov_draft_one_launch(B: int, W1, W2, want_logits: bool = False) -> bool:
+    """Whether markov_draft draws all positions in one launch (dspark_markov_draft_one_launch)."""
+    torch = _torch()
+    V, r = W1.shape
+    wdt = BF16 if W1.dtype == torch.bfloat16 else F32
+    return bool(load().dspark_markov_draft_one_launch(B, V, r, wdt, _ptr(W1), _ptr(W2), int(want_logits)))
 
 
 def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=False,

@@ -97,6 +97,13 @@ int dspark_markov_draft_path(int B, int V, int r, int w_dtype, const void* W1, c
     return DSPARK_PATH_SWEEP;
 }
 
+int dspark_markov_draft_one_launch(int B, int V, int r, int w_dtype, const void* W1, const void* W2,
+                                   int want_logits) {
+    const int p = dspark_markov_draft_path(B, V, r, w_dtype, W1, W2);
+    if (p == DSPARK_PATH_RESIDENT) return 1;
+    return p == DSPARK_PATH_SLAB && dspark::draft_slab_one_launch(B, V, want_logits != 0) ? 1 : 0;
+}
+
 size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma) {
     (void)r;
     if (B < 1 || V < 1 || gamma < 1) return 0;

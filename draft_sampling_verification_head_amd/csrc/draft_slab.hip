@@ -652,6 +652,20 @@ bool resident_fits(int V) {
     return f.cus > 0 && f.occupancy[nt] >= 1 && slab_count(V) <= f.cus * f.occupancy[nt];
 }
 
+}  // namespace
+
+// The persistent form: no logits output, its LDS (with the draw's logit rows and the B picked
+// slabs in H0 + H1) fits, and every slab workgroup can be on the device at once.
+bool draft_slab_one_launch(int B, int V, bool L_out) {
+    const int nt = slab_nt(V);
+    const size_t wc = 16 * static_cast<size_t>(nt);
+    const bool lds_ok = slab_lds_bytes(nt, B) + kResidentExtra <= static_cast<size_t>(kLdsBytes) &&
+                        kSlabWaves * wc * 4 + 4 * static_cast<size_t>(B) <= 2 * static_cast<size_t>(kHBuf);
+    return !L_out && lds_ok && resident_fits(V);
+}
+
+namespace {
+
 template <int NT>
 hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
     SlabArgs a;
@@ -671,10 +685,7 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
     a.spart = c.part[1] + 2 * static_cast<long long>(c.B);
     const size_t smem = slab_lds_bytes(NT, c.B);
     const dim3 grid(static_cast<unsigned>(a.G));
-    // the resident form also needs the draw's logit rows and the B picked slabs in H0 + H1
-    const bool lds_ok = smem + kResidentExtra <= static_cast<size_t>(kLdsBytes) &&
-                        kSlabWaves * Slab<NT>::WC * 4 + 4 * static_cast<size_t>(c.B) <= 2 * static_cast<size_t>(kHBuf);
-    if (!c.L_out && lds_ok && resident_fits(c.V)) {
+    if (draft_slab_one_launch(c.B, c.V, c.L_out)) {
         const int n = 3 * c.gamma * a.G;
         hipLaunchKernelGGL(clear_flags, dim3((n + 255) / 256), dim3(256), 0, st, a.flags, n);
         hipError_t e = hipGetLastError();

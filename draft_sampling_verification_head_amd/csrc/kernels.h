@@ -39,6 +39,7 @@ hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st);
 bool draft_slab_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
 int draft_slab_tiles(int V);
 size_t draft_slab_flag_bytes(int V, int gamma);   // position flags of the one-launch form
+bool draft_slab_one_launch(int B, int V, bool L_out);   // whether a slab call is that form
 hipError_t launch_draft_slab(const DraftCall& c, hipStream_t st);
 
 // Single-request path with W2 resident in registers (draft_resident.hip), chosen by

@@ -88,14 +88,19 @@ int dspark_version(void);
  * this same function (dspark_markov_draft_path tells which one a call takes); each is
  * deterministic, and they differ from one another only in fp32 rounding order:
  *   DSPARK_PATH_SWEEP     one vocabulary sweep per position (B <= 8, or fp32 factors).
- *   DSPARK_PATH_SLAB      per position, one bf16 MFMA launch in which every workgroup keeps
- *                         its vocabulary slab of W2 in registers and streams the batch
- *                         through it, and one draw launch that recomputes the chosen tile's
- *                         logits instead of reading them (B > 8, bf16, r <= 256 and
- *                         r % 8 == 0, V % 8 == 0, V <= 163840, B <= 2048 at V > 131072 and
- *                         B <= 8192 at V > 98304,
- *                         16-byte aligned W1, W2, U and Ld_out). Logits reach memory only
- *                         when Ld_out is given.
+ *   DSPARK_PATH_SLAB      every workgroup keeps its vocabulary slab of W2 in registers as
+ *                         bf16 MFMA operands and streams the batch through it; the draw
+ *                         recomputes the chosen tile's logits instead of reading them (B > 8,
+ *                         bf16, r <= 256 and r % 8 == 0, V % 8 == 0, V <= 163840, B <= 2048
+ *                         at V > 131072 and B <= 8192 at V > 98304, 16-byte aligned W1, W2,
+ *                         U and Ld_out). Logits reach memory only when Ld_out is given.
+ *                         Without Ld_out, and where the batch and every slab workgroup fit
+ *                         (dspark_markov_draft_one_launch), all positions run in one launch
+ *                         that holds W2 in registers throughout and separates positions by
+ *                         flag barriers, with the same give-up behaviour and the same
+ *                         restriction on overlapping draft calls as DSPARK_PATH_RESIDENT;
+ *                         otherwise each position is one stream launch and one draw launch.
+ *                         Both forms draw the same tokens bit for bit.
  *   DSPARK_PATH_MFMA      one bf16 MFMA projection per position (B > 8, bf16 factors, where
  *                         the slab path does not apply).
  *   DSPARK_PATH_RESIDENT  one launch for all positions, W2 held in registers across the GPU
@@ -111,6 +116,11 @@ enum { DSPARK_PATH_SWEEP = 0, DSPARK_PATH_MFMA = 1, DSPARK_PATH_RESIDENT = 2, DS
 
 /* The path dspark_markov_draft takes for these arguments on the current device. */
 int dspark_markov_draft_path(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
+
+/* 1 if dspark_markov_draft runs all positions in one launch for these arguments (a non-null
+ * Ld_out when want_logits != 0; U 16-byte aligned) on the current device, else 0. */
+int dspark_markov_draft_one_launch(int B, int V, int r, int w_dtype, const void* W1, const void* W2,
+                                   int want_logits);
 
 size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma);
 int dspark_markov_draft(int B, int V, int r, int gamma,

@@ -79,6 +79,12 @@ def test_draft_path_host_rules(lib):
     assert lib.dspark_markov_draft_path(1, 151936, 256, 0, FAKE, FAKE) == 0      # fp32, B = 1
     assert lib.dspark_markov_draft_path(1, 151936, 260, 1, FAKE, FAKE) == 0      # r > 256
     assert lib.dspark_markov_draft_path(1, 151937, 256, 1, FAKE, FAKE) == 0      # V % 8 != 0
+    # one launch for all positions: never with a logits output or off the resident / slab paths
+    f = lib.dspark_markov_draft_one_launch
+    f.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int]
+    assert f(64, 151936, 256, 1, FAKE, FAKE, 1) == 0
+    assert f(64, 151936, 256, 0, FAKE, FAKE, 0) == 0
+    assert f(2049, 151936, 256, 1, FAKE, FAKE, 0) == 0
 
 
 def _draft(lib, B=2, V=64, r=4, G=3, wdt=0, ws=FAKE, wsb=1 << 30, U=FAKE, x_out=FAKE):

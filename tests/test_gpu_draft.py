@@ -75,16 +75,25 @@ def test_batched_mfma_shapes(gpu, B, V, r, G):
     (40, 151936, 256, 2),   # five, the full vocabulary
 ])
 def test_batched_slab_shapes(gpu, B, V, r, G):
-    """bf16 batches: W2 slabs in registers, draws that recompute the chosen tile."""
+    """bf16 batches: W2 slabs in registers, draws that recompute the chosen tile. With the
+    logits output each position is a stream and a draw launch; without it one persistent
+    launch draws every position, and its tokens, probabilities and normalisers are the same
+    bit for bit."""
     c = synth.custom(955 + B, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
-    assert dspark.markov_draft_path(B, dev(d["W1"]), dev(d["W2"])) == "slab"
+    W1, W2 = dev(d["W1"]), dev(d["W2"])
+    assert dspark.markov_draft_path(B, W1, W2) == "slab"
+    assert dspark.markov_draft_one_launch(B, W1, W2)
+    assert not dspark.markov_draft_one_launch(B, W1, W2, want_logits=True)
     g = run_draft(d)
     reqs = sorted({0, 1, B // 2, B - 2, B - 1})
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
                       reqs, gL=g["L"])
     assert rep.ties <= 1
     assert np.all((g["x"] >= 0) & (g["x"] < V))
+    one = run_draft(d, want_logits=False)
+    for k in ("x", "q", "lse"):
+        assert np.array_equal(g[k].view(np.uint8), one[k].view(np.uint8)), k
 
 
 @pytest.mark.parametrize("V,r,G", [
@@ -108,10 +117,11 @@ def test_single_request_bf16_shapes(gpu, V, r, G):
 
 def test_slab_logits_output_is_optional(gpu):
     """The slab path's draws do not read the logits: the same tokens, probabilities and
-    normalisers with and without the logits output, and the stored logits match the
-    oracle's."""
+    normalisers with and without the logits output (per-position launches, then the
+    persistent launch), and the stored logits match the oracle's."""
     c = synth.custom(961, B=24, V=30000, r=256, gamma=4, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
+    assert dspark.markov_draft_one_launch(c.B, dev(d["W1"]), dev(d["W2"]))
     a = run_draft(d, want_logits=True)
     b = run_draft(d, want_logits=False)
     for k in ("x", "q", "lse"):
