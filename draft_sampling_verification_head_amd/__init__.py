@@ -4,4 +4,4 @@ The compute lives in libdspark.so (hand-written HIP kernels behind the C ABI of
 include/dspark.h); this package only builds it and binds it for torch tensors.
 """
 from .binding import (markov_draft, markov_draft_one_launch, markov_draft_path, verify, verify_markov,  # noqa: F401
-                      tv_labels, schedule, sts_fit, load, DsparkError, F32, BF16, GLOBAL, EARLY_STOP, STS_NLL, STS_ECE)
+                      tv_labels, schedule, schedule_lagged, ConfRing, sts_fit, load, DsparkError, F32, BF16, GLOBAL, EARLY_STOP, STS_NLL, STS_ECE)

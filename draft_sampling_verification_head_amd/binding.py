@@ -30,6 +30,7 @@ EXPORTS = (
     "dspark_verify_markov_workspace_bytes", "dspark_verify_markov",
     "dspark_tv_labels_workspace_bytes", "dspark_tv_labels",
     "dspark_schedule_workspace_bytes", "dspark_schedule",
+    "dspark_conf_ring_bytes", "dspark_conf_ring_init", "dspark_conf_ring_push", "dspark_schedule_lagged",
     "dspark_sts_fit_workspace_bytes", "dspark_sts_fit",
 )
 
@@ -56,6 +57,10 @@ _SIGS = {
     "dspark_tv_labels": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_schedule_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_schedule": (_I, [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_conf_ring_bytes": (_Z, [_I, _I]),
+    "dspark_conf_ring_init": (_I, [_I, _I, _P, _Z, _P]),
+    "dspark_conf_ring_push": (_I, [_I, _I, _P, _Z, _P, _P]),
+    "dspark_schedule_lagged": (_I, [_I, _I, _P, _Z, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_sts_fit_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_sts_fit": (_I, [_I, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
 }
@@ -316,6 +321,17 @@ def tv_labels(Ld, Lt, *, t_off=None, length=None, lse_d=None, lse_t=None, out=No
     return c
 
 
+def _schedule_outputs(R, G, dev, out, want_a):
+    torch = _torch()
+    o = out or {}
+    length = o.get("len") if o.get("len") is not None else torch.empty((R,), dtype=torch.int32, device=dev)
+    t_off = o.get("t_off") if o.get("t_off") is not None else torch.empty((R + 1,), dtype=torch.int32, device=dev)
+    K = o.get("K") if o.get("K") is not None else torch.empty((1,), dtype=torch.int32, device=dev)
+    theta = o.get("theta") if o.get("theta") is not None else torch.empty((1,), dtype=torch.float32, device=dev)
+    a = torch.empty((R, G), dtype=torch.float32, device=dev) if want_a else None
+    return dict(len=length, t_off=t_off, K=K, theta=theta, a=a)
+
+
 def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None, stream=None):
     """dspark_schedule. conf [R][gamma] fp32, sps [Bmax+1] fp32, temp [gamma] fp32 or None.
     Returns dict len [R], t_off [R+1], K [1], theta [1] (and a [R][gamma] when want_a)."""
@@ -327,18 +343,60 @@ def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None,
     _need(sps, "sps", torch.float32, (Bmax + 1,), dev)
     if temp is not None:
         _need(temp, "temp", torch.float32, (G,), dev)
-    o = out or {}
-    length = o.get("len") if o.get("len") is not None else torch.empty((R,), dtype=torch.int32, device=dev)
-    t_off = o.get("t_off") if o.get("t_off") is not None else torch.empty((R + 1,), dtype=torch.int32, device=dev)
-    K = o.get("K") if o.get("K") is not None else torch.empty((1,), dtype=torch.int32, device=dev)
-    theta = o.get("theta") if o.get("theta") is not None else torch.empty((1,), dtype=torch.float32, device=dev)
-    a = torch.empty((R, G), dtype=torch.float32, device=dev) if want_a else None
+    o = _schedule_outputs(R, G, dev, out, want_a)
     ws = workspace(lib.dspark_schedule_workspace_bytes(R, G, int(Bmax)), dev, "schedule")
     st = lib.dspark_schedule(R, G, _ptr(conf), _ptr(temp), _ptr(sps), int(Bmax), int(mode),
-                             _ptr(length), _ptr(t_off), _ptr(K), _ptr(theta), _ptr(a), _ptr(ws),
-                             ws.numel(), _stream(stream))
+                             _ptr(o["len"]), _ptr(o["t_off"]), _ptr(o["K"]), _ptr(o["theta"]),
+                             _ptr(o["a"]), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "dspark_schedule")
-    return dict(len=length, t_off=t_off, K=K, theta=theta, a=a)
+    return o
+
+
+class ConfRing:
+    """Two-step-lag confidence history (dspark_conf_ring_*): one device buffer holding a
+    round counter and three [R][gamma] fp32 slots, initialised to "no history" (all 1.0)."""
+
+    def __init__(self, R: int, gamma: int, device=None, stream=None):
+        torch = _torch()
+        self.R, self.gamma = int(R), int(gamma)
+        self.nbytes = int(load().dspark_conf_ring_bytes(self.R, self.gamma))
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device or "cuda")
+        self.reset(stream)
+
+    def reset(self, stream=None):
+        """dspark_conf_ring_init: counter 0, every slot 1.0."""
+        _check(load().dspark_conf_ring_init(self.R, self.gamma, _ptr(self.buf), self.nbytes,
+                                            _stream(stream)), "dspark_conf_ring_init")
+
+    def push(self, conf, stream=None):
+        """dspark_conf_ring_push: this round's confidences [R][gamma] fp32."""
+        torch = _torch()
+        _need(conf, "conf", torch.float32, (self.R, self.gamma), self.buf.device)
+        _check(load().dspark_conf_ring_push(self.R, self.gamma, _ptr(self.buf), self.nbytes,
+                                            _ptr(conf), _stream(stream)), "dspark_conf_ring_push")
+
+    def rounds(self) -> int:
+        """The device counter (pushes so far); synchronises with the device."""
+        return int(self.buf[:8].view(_torch().int64).item())
+
+
+def schedule_lagged(ring: ConfRing, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None,
+                    stream=None):
+    """dspark_schedule_lagged: dspark_schedule on the confidences pushed two rounds ago."""
+    torch = _torch()
+    lib = load()
+    R, G, dev = ring.R, ring.gamma, ring.buf.device
+    _need(sps, "sps", torch.float32, (Bmax + 1,), dev)
+    if temp is not None:
+        _need(temp, "temp", torch.float32, (G,), dev)
+    o = _schedule_outputs(R, G, dev, out, want_a)
+    ws = workspace(lib.dspark_schedule_workspace_bytes(R, G, int(Bmax)), dev, "schedule")
+    st = lib.dspark_schedule_lagged(R, G, _ptr(ring.buf), ring.nbytes, _ptr(temp), _ptr(sps),
+                                    int(Bmax), int(mode), _ptr(o["len"]), _ptr(o["t_off"]),
+                                    _ptr(o["K"]), _ptr(o["theta"]), _ptr(o["a"]), _ptr(ws),
+                                    ws.numel(), _stream(stream))
+    _check(st, "dspark_schedule_lagged")
+    return o
 
 
 def sts_fit(conf, n_acc, grid, *, length=None, bins=15, objective=STS_NLL, want_obj=False,

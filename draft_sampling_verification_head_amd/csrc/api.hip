@@ -332,30 +332,105 @@ size_t dspark_schedule_workspace_bytes(int R, int gamma, int Bmax) {
     return align_up(static_cast<size_t>(R) * gamma * (2 * sizeof(double) + sizeof(int32_t)));
 }
 
+namespace {
+
+// Shared checks and launch of dspark_schedule / dspark_schedule_lagged (ring_n: the ring's
+// counter, conf then the base of its slots).
+int schedule_call(const char* who, int R, int gamma, const float* conf, const long long* ring_n,
+                  const float* temp, const float* sps, int Bmax, int mode, int32_t* len_out,
+                  int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+    if (R < 1 || gamma < 1)
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: R=%d gamma=%d must be >= 1", who, R, gamma);
+    if (gamma > 64 || static_cast<long long>(R) * gamma > dspark::schedule_max_candidates())
+        return fail(DSPARK_ERR_UNSUPPORTED, "%s: R*gamma=%lld exceeds %d (or gamma > 64)", who,
+                    static_cast<long long>(R) * gamma, dspark::schedule_max_candidates());
+    if (Bmax < R || Bmax > (1 << 20))
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: need R <= Bmax <= 2^20 (R=%d Bmax=%d)", who, R,
+                    Bmax);
+    if (mode != DSPARK_SCHED_GLOBAL && mode != DSPARK_SCHED_EARLY_STOP)
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: unknown mode %d", who, mode);
+    if (!conf || !sps || !len_out)
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: conf / sps / len_out is NULL", who);
+    const size_t need = dspark_schedule_workspace_bytes(R, gamma, Bmax);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+    const hipError_t e = dspark::launch_schedule(R, gamma, conf, ring_n, temp, sps, Bmax, mode,
+                                                 len_out, t_off_out, K_out, theta_out, a_out,
+                                                 static_cast<double*>(ws),
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, who);
+    return ok();
+}
+
+// Ring layout: the round counter (int64) in the first 256 bytes, then three [R][gamma] slots.
+constexpr size_t kRingHeader = 256;
+
+int check_ring(const char* who, int R, int gamma, const void* ring, size_t ring_bytes) {
+    if (R < 1 || gamma < 1)
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: R=%d gamma=%d must be >= 1", who, R, gamma);
+    if (static_cast<long long>(R) * gamma > dspark::schedule_max_candidates())
+        return fail(DSPARK_ERR_UNSUPPORTED, "%s: R*gamma=%lld exceeds %d", who,
+                    static_cast<long long>(R) * gamma, dspark::schedule_max_candidates());
+    if (!ring || (reinterpret_cast<uintptr_t>(ring) % 8) != 0)
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: ring is NULL or not 8-byte aligned", who);
+    const size_t need = dspark_conf_ring_bytes(R, gamma);
+    if (ring_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "%s: ring %zu bytes, need %zu", who, ring_bytes, need);
+    return DSPARK_OK;
+}
+
+long long* ring_counter(const void* ring) {
+    return static_cast<long long*>(const_cast<void*>(ring));
+}
+float* ring_slots(const void* ring) {
+    return reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ring)) + kRingHeader);
+}
+
+}  // namespace
+
 int dspark_schedule(int R, int gamma, const float* conf, const float* temp, const float* sps,
                     int Bmax, int mode, int32_t* len_out, int32_t* t_off_out, int32_t* K_out,
                     float* theta_out, float* a_out, void* ws, size_t ws_bytes, void* stream) {
-    if (R < 1 || gamma < 1)
-        return fail(DSPARK_ERR_INVALID_ARG, "schedule: R=%d gamma=%d must be >= 1", R, gamma);
-    if (gamma > 64 || static_cast<long long>(R) * gamma > dspark::schedule_max_candidates())
-        return fail(DSPARK_ERR_UNSUPPORTED, "schedule: R*gamma=%lld exceeds %d (or gamma > 64)",
-                    static_cast<long long>(R) * gamma, dspark::schedule_max_candidates());
-    if (Bmax < R || Bmax > (1 << 20))
-        return fail(DSPARK_ERR_INVALID_ARG, "schedule: need R <= Bmax <= 2^20 (R=%d Bmax=%d)", R,
-                    Bmax);
-    if (mode != DSPARK_SCHED_GLOBAL && mode != DSPARK_SCHED_EARLY_STOP)
-        return fail(DSPARK_ERR_INVALID_ARG, "schedule: unknown mode %d", mode);
-    if (!conf || !sps || !len_out)
-        return fail(DSPARK_ERR_INVALID_ARG, "schedule: conf / sps / len_out is NULL");
-    const size_t need = dspark_schedule_workspace_bytes(R, gamma, Bmax);
-    if (!ws || ws_bytes < need)
-        return fail(DSPARK_ERR_WORKSPACE, "schedule: workspace %zu bytes, need %zu", ws_bytes, need);
-    const hipError_t e = dspark::launch_schedule(R, gamma, conf, temp, sps, Bmax, mode, len_out,
-                                                 t_off_out, K_out, theta_out, a_out,
-                                                 static_cast<double*>(ws),
-                                                 static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "schedule");
+    return schedule_call("schedule", R, gamma, conf, nullptr, temp, sps, Bmax, mode, len_out,
+                         t_off_out, K_out, theta_out, a_out, ws, ws_bytes, stream);
+}
+
+// ----------------------------------------------------------------------------- lag ring
+size_t dspark_conf_ring_bytes(int R, int gamma) {
+    if (R < 1 || gamma < 1) return 0;
+    return kRingHeader + 3 * static_cast<size_t>(R) * gamma * sizeof(float);
+}
+
+int dspark_conf_ring_init(int R, int gamma, void* ring, size_t ring_bytes, void* stream) {
+    const int st = check_ring("conf_ring_init", R, gamma, ring, ring_bytes);
+    if (st != DSPARK_OK) return st;
+    const hipError_t e = dspark::launch_conf_ring_init(ring_counter(ring), ring_slots(ring), R, gamma,
+                                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "conf_ring_init");
     return ok();
+}
+
+int dspark_conf_ring_push(int R, int gamma, void* ring, size_t ring_bytes, const float* conf,
+                          void* stream) {
+    const int st = check_ring("conf_ring_push", R, gamma, ring, ring_bytes);
+    if (st != DSPARK_OK) return st;
+    if (!conf) return fail(DSPARK_ERR_INVALID_ARG, "conf_ring_push: conf is NULL");
+    const hipError_t e = dspark::launch_conf_ring_push(ring_counter(ring), ring_slots(ring), conf, R,
+                                                       gamma, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "conf_ring_push");
+    return ok();
+}
+
+int dspark_schedule_lagged(int R, int gamma, const void* ring, size_t ring_bytes, const float* temp,
+                           const float* sps, int Bmax, int mode, int32_t* len_out,
+                           int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out,
+                           void* ws, size_t ws_bytes, void* stream) {
+    const int st = check_ring("schedule_lagged", R, gamma, ring, ring_bytes);
+    if (st != DSPARK_OK) return st;
+    return schedule_call("schedule_lagged", R, gamma, ring_slots(ring), ring_counter(ring), temp, sps,
+                         Bmax, mode, len_out, t_off_out, K_out, theta_out, a_out, ws, ws_bytes,
+                         stream);
 }
 
 // ----------------------------------------------------------------------------- STS fit

@@ -117,10 +117,15 @@ hipError_t launch_verify_markov(const VerifyMarkovCall& c, hipStream_t st);
 
 // ---------------------------------------------------------------- schedule
 int schedule_max_candidates();
-hipError_t launch_schedule(int R, int gamma, const float* conf, const float* temp,
-                           const float* sps, int Bmax, int mode, int32_t* len_out,
-                           int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out,
-                           double* a_ws, hipStream_t st);
+// conf: the confidences, or with ring_n the base of the three ring slots (the lagged slot is
+// resolved on the device from the counter).
+hipError_t launch_schedule(int R, int gamma, const float* conf, const long long* ring_n,
+                           const float* temp, const float* sps, int Bmax, int mode,
+                           int32_t* len_out, int32_t* t_off_out, int32_t* K_out, float* theta_out,
+                           float* a_out, double* a_ws, hipStream_t st);
+hipError_t launch_conf_ring_init(long long* ring_n, float* slots, int R, int gamma, hipStream_t st);
+hipError_t launch_conf_ring_push(long long* ring_n, float* slots, const float* conf, int R, int gamma,
+                                 hipStream_t st);
 
 // ---------------------------------------------------------------- STS fit
 int sts_max_bins();

@@ -16,6 +16,13 @@
 // a is non-increasing along a block and ties rank earlier positions first, that set is a
 // prefix of every block. Up to 64 candidates run in one wave (schedule_small_kernel); more
 // run as a rank pass over many workgroups followed by one pick workgroup.
+//
+// Two-step-lag confidences ([P1] same section, the asynchronous adaptation; [P3] same
+// section, the batch capacity predicted from confidences two steps old): a ring of three
+// [R][gamma] slots and a round counter n in device memory. A push stores the round's
+// confidences in slot n mod 3 and advances n; the lagged schedule reads slot (n - 2) mod 3,
+// the confidences pushed two rounds before the next push (all 1.0 until two pushes exist).
+// The slot is resolved on the device, so a captured round needs no host round trip.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,6 +32,13 @@ namespace {
 
 constexpr int kMaxCand = 16384;            // 128 KB of keys in LDS
 constexpr unsigned long long kMask44 = (1ull << 44) - 1ull;
+
+// The confidences a schedule reads: `conf`, or with a ring counter the lagged ring slot.
+__device__ __forceinline__ const float* lagged(const float* conf, const long long* ring_n, int R, int G) {
+    if (!ring_n) return conf;
+    const long long n = *ring_n;
+    return conf + ((n + 1) % 3) * static_cast<long long>(R) * G;   // (n - 2) mod 3 for n >= 0
+}
 
 __device__ __forceinline__ double scaled_conf(float c, const float* temp, int j) {
     const double cd = static_cast<double>(c);
@@ -65,11 +79,13 @@ __device__ __forceinline__ Best better(Best a, Best b) {
 constexpr int kSmallCand = kWave;
 
 __global__ __launch_bounds__(kWave)
-void schedule_small_kernel(int R, int G, const float* __restrict__ conf,
+void schedule_small_kernel(int R, int G, const float* __restrict__ conf_in,
+                           const long long* __restrict__ ring_n,
                            const float* __restrict__ temp, const float* __restrict__ sps,
                            int Bmax, int mode, int32_t* __restrict__ len_out,
                            int32_t* __restrict__ t_off_out, int32_t* __restrict__ K_out,
                            float* __restrict__ theta_out, float* __restrict__ a_out) {
+    const float* conf = lagged(conf_in, ring_n, R, G);
     __shared__ double cs[kSmallCand];
     __shared__ double sorted[kSmallCand];
     const int lane = threadIdx.x;
@@ -166,9 +182,11 @@ constexpr int kRankPerBlock = kRankThreads / kRankSplit;
 // candidate), then the prefix products of each request in position order (one thread per
 // request, as the oracle multiplies). A workgroup covers whole requests.
 __global__ __launch_bounds__(kRankThreads)
-void schedule_keys_kernel(int R, int G, const float* __restrict__ conf,
+void schedule_keys_kernel(int R, int G, const float* __restrict__ conf_in,
+                          const long long* __restrict__ ring_n,
                           const float* __restrict__ temp, float* __restrict__ a_out,
                           unsigned long long* __restrict__ row_keys) {
+    const float* conf = lagged(conf_in, ring_n, R, G);
     __shared__ double cs[kRankThreads];
     const int per = kRankThreads / G;                        // requests per workgroup
     const int rb = blockIdx.x * per;
@@ -372,17 +390,47 @@ void schedule_pick_kernel(int R, int G, const float* __restrict__ sps, int Bmax,
     }
 }
 
+// Ring set-up: counter 0, every slot 1.0 (no history yet: every position survives). One
+// workgroup; a fill kernel rather than a memset, so that it can sit in a captured graph.
+__global__ __launch_bounds__(1024)
+void conf_ring_init_kernel(long long* __restrict__ ring_n, float* __restrict__ slots, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) slots[i] = 1.0f;
+    if (threadIdx.x == 0) *ring_n = 0;
+}
+
+// Push: slot n mod 3 <- conf, then n <- n + 1 once every thread has read n.
+__global__ __launch_bounds__(1024)
+void conf_ring_push_kernel(long long* __restrict__ ring_n, float* __restrict__ slots,
+                           const float* __restrict__ conf, int per_slot) {
+    const long long n = *ring_n;
+    float* dst = slots + (n % 3) * static_cast<long long>(per_slot);
+    for (int i = threadIdx.x; i < per_slot; i += blockDim.x) dst[i] = conf[i];
+    __syncthreads();
+    if (threadIdx.x == 0) *ring_n = n + 1;
+}
+
 }  // namespace
 
 int schedule_max_candidates() { return kMaxCand; }
 
-hipError_t launch_schedule(int R, int gamma, const float* conf, const float* temp,
-                           const float* sps, int Bmax, int mode, int32_t* len_out,
-                           int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out,
-                           double* a_ws, hipStream_t st) {
+hipError_t launch_conf_ring_init(long long* ring_n, float* slots, int R, int gamma, hipStream_t st) {
+    hipLaunchKernelGGL(conf_ring_init_kernel, dim3(1), dim3(1024), 0, st, ring_n, slots, 3 * R * gamma);
+    return hipGetLastError();
+}
+
+hipError_t launch_conf_ring_push(long long* ring_n, float* slots, const float* conf, int R, int gamma,
+                                 hipStream_t st) {
+    hipLaunchKernelGGL(conf_ring_push_kernel, dim3(1), dim3(1024), 0, st, ring_n, slots, conf, R * gamma);
+    return hipGetLastError();
+}
+
+hipError_t launch_schedule(int R, int gamma, const float* conf, const long long* ring_n,
+                           const float* temp, const float* sps, int Bmax, int mode,
+                           int32_t* len_out, int32_t* t_off_out, int32_t* K_out, float* theta_out,
+                           float* a_out, double* a_ws, hipStream_t st) {
     if (R * gamma <= kSmallCand) {
-        hipLaunchKernelGGL(schedule_small_kernel, dim3(1), dim3(kWave), 0, st, R, gamma, conf, temp,
-                           sps, Bmax, mode, len_out, t_off_out, K_out, theta_out, a_out);
+        hipLaunchKernelGGL(schedule_small_kernel, dim3(1), dim3(kWave), 0, st, R, gamma, conf, ring_n,
+                           temp, sps, Bmax, mode, len_out, t_off_out, K_out, theta_out, a_out);
         return hipGetLastError();
     }
     const int N = R * gamma;
@@ -391,7 +439,7 @@ hipError_t launch_schedule(int R, int gamma, const float* conf, const float* tem
     int32_t* ranks = reinterpret_cast<int32_t*>(sorted_keys + N);
     const int per = kRankThreads / gamma;
     hipLaunchKernelGGL(schedule_keys_kernel, dim3((R + per - 1) / per), dim3(kRankThreads), 0, st, R,
-                       gamma, conf, temp, a_out, row_keys);
+                       gamma, conf, ring_n, temp, a_out, row_keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = static_cast<size_t>(R) * rank_stride(R, gamma) * sizeof(unsigned long long);

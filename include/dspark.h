@@ -259,6 +259,39 @@ int dspark_schedule(int R, int gamma, const float* conf, const float* temp,
                     float* a_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Two-step-lag schedule.
+ * [P1] section "硬件感知与置信度自适应调度机制" (the asynchronous adaptation): the verify
+ * lengths of step t are decided from the confidences predicted at step t - 2, which cannot
+ * carry information about the tokens being generated now, so the decision is lossless and
+ * its latency hides in the GPU pipeline (no host handshake, compatible with graph replay);
+ * [P3] "Confidence-Scheduled Verification": the batch capacity K is predicted from the
+ * confidences of two steps earlier.
+ *
+ * The history is a device buffer (`ring`, dspark_conf_ring_bytes(R, gamma) bytes, 8-byte
+ * aligned, owned by the caller): a round counter n and three [R][gamma] fp32 slots.
+ *   dspark_conf_ring_init    n = 0 and every slot 1.0 (no history: every position survives)
+ *   dspark_conf_ring_push    slot n mod 3 <- conf [R][gamma], then n <- n + 1
+ *   dspark_schedule_lagged   dspark_schedule on slot (n - 2) mod 3: the confidences pushed
+ *                            two pushes before the next one, i.e. at round t (n = t pushes
+ *                            so far, one per earlier round) those of round t - 2, and all
+ *                            1.0 for t < 2. Arguments and outputs as dspark_schedule.
+ * The slot is chosen on the device from n, so a round (lagged schedule, draft, verify, push)
+ * can be captured once and replayed without host synchronisation. Calls on one ring must be
+ * ordered (one stream, or events); a push must not overlap a lagged schedule on the same
+ * ring. Errors: INVALID_ARG for a NULL or misaligned ring or NULL conf, WORKSPACE when
+ * ring_bytes is too small, UNSUPPORTED past the scheduler's R * gamma cap.
+ */
+size_t dspark_conf_ring_bytes(int R, int gamma);
+int dspark_conf_ring_init(int R, int gamma, void* ring, size_t ring_bytes, void* stream);
+int dspark_conf_ring_push(int R, int gamma, void* ring, size_t ring_bytes, const float* conf,
+                          void* stream);
+int dspark_schedule_lagged(int R, int gamma, const void* ring, size_t ring_bytes,
+                           const float* temp, const float* sps, int Bmax, int mode,
+                           int32_t* len_out, int32_t* t_off_out, int32_t* K_out,
+                           float* theta_out, float* a_out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
  * Sequential temperature scaling (STS) fit.
  * [P1] section "硬件感知与置信度自适应调度机制": the confidence head's scores are calibrated
  * with one temperature per candidate position, each chosen by a one-dimensional grid search

@@ -34,6 +34,10 @@ Functions and what pins them (all pins live in ``tests/test_oracle_*.py``):
   (a_{r,j} = prod c, Theta = tau * SPS(B)). Pinned by brute-force enumeration, the
   constant-SPS and zero-SPS closed forms, early-stop = global for a smooth curve, a
   step-shaped curve with known answers, and exact temperature values.
+* ``lagged_confidences``, ``lagged_schedule`` - [P1] same section (the asynchronous
+  adaptation: step t is scheduled from the confidences of step t - 2) and [P3] same section.
+  Pinned by the no-history closed form (all ones: lengths from the SPS curve alone) and by
+  round t's schedule ignoring rounds t and t - 1 while following round t - 2.
 * ``outcomes``, ``scale``, ``nll``, ``ece``, ``sts_fit`` - [P1] "硬件感知与置信度自适应调度机制"
   (sequential temperature scaling: a per-position 1-D grid search, order preserving, judged
   by the expected calibration error) and [P3] "Confidence-Scheduled Verification" (c_k is
@@ -47,12 +51,13 @@ from .draft import markov_draft
 from .verify import verify, accept_test
 from .tv import tv_labels, tv_row_pair
 from .schedule import (temperature_scale, prefix_survival, schedule, brute_force_schedule,
-                       theta_curve, GLOBAL, EARLY_STOP)
+                       theta_curve, lagged_confidences, lagged_schedule, GLOBAL, EARLY_STOP)
 from . import sts
 
 __all__ = [
     "decode_factor", "clamp_uniform", "softmax_row", "inverse_cdf", "markov_draft",
     "verify", "accept_test", "tv_labels", "tv_row_pair", "temperature_scale",
-    "prefix_survival", "schedule", "brute_force_schedule", "theta_curve", "GLOBAL",
+    "prefix_survival", "schedule", "brute_force_schedule", "theta_curve", "lagged_confidences",
+    "lagged_schedule", "GLOBAL",
     "EARLY_STOP",
 ]

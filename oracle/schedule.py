@@ -113,6 +113,27 @@ def schedule(conf, temp, sps, Bmax: int, mode: int = GLOBAL) -> dict:
                 a=a, theta_curve=theta, ranked=ranked)
 
 
+def lagged_confidences(history, t: int, R: int, gamma: int) -> np.ndarray:
+    """The confidences the scheduler of round t reads under the two-step lag.
+
+    [P1] same section (the asynchronous adaptation): the verify length of step t is decided
+    from the confidence predictions made at step t - 2, so the decision cannot depend on the
+    tokens being generated now. [P3] same section: the batch capacity is predicted from the
+    confidences of two steps earlier. history[i] is the [R][gamma] array recorded at round i.
+    Reading: before two rounds have been recorded there is no history, and every position is
+    taken to survive (all ones).
+    """
+    if t >= 2:
+        return np.asarray(history[t - 2], dtype=np.float64)
+    return np.ones((R, gamma))
+
+
+def lagged_schedule(history, t: int, temp, sps, Bmax: int, mode: int = GLOBAL) -> dict:
+    """The schedule of round t from the confidences recorded at round t - 2."""
+    h0 = np.asarray(history[0])
+    return schedule(lagged_confidences(history, t, h0.shape[0], h0.shape[1]), temp, sps, Bmax, mode)
+
+
 def brute_force_schedule(conf, temp, sps, Bmax: int):
     """Maximum of Theta over every length vector l in {0..gamma}^R with R + sum(l) <= Bmax.
 

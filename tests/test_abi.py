@@ -212,6 +212,35 @@ def test_schedule_null_required(lib):
                                8, None) == binding.ERR_WORKSPACE
 
 
+def test_conf_ring_bytes(lib):
+    """Counter header (256 bytes) plus three [R][gamma] fp32 slots."""
+    assert lib.dspark_conf_ring_bytes(512, 16) == 256 + 3 * 512 * 16 * 4
+    assert lib.dspark_conf_ring_bytes(0, 16) == 0
+    assert lib.dspark_conf_ring_bytes(4, 0) == 0
+
+
+@cpu_only
+def test_conf_ring_rejects(lib):
+    n = lib.dspark_conf_ring_bytes(4, 4)
+    odd = ctypes.c_void_p(0x1004)
+    assert lib.dspark_conf_ring_init(4, 4, None, n, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_conf_ring_init(4, 4, odd, n, None) == binding.ERR_INVALID_ARG   # not 8-aligned
+    assert lib.dspark_conf_ring_init(4, 4, FAKE, n - 1, None) == binding.ERR_WORKSPACE
+    assert lib.dspark_conf_ring_init(0, 4, FAKE, n, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_conf_ring_init(2048, 16, FAKE, 1 << 30, None) == binding.ERR_UNSUPPORTED
+    assert lib.dspark_conf_ring_push(4, 4, FAKE, n, None, None) == binding.ERR_INVALID_ARG
+    assert lib.dspark_conf_ring_push(4, 4, FAKE, n - 1, FAKE, None) == binding.ERR_WORKSPACE
+    lag = lib.dspark_schedule_lagged
+    assert lag(4, 4, None, n, None, FAKE, 40, 0, FAKE, None, None, None, None, FAKE, 1 << 30,
+               None) == binding.ERR_INVALID_ARG
+    assert lag(4, 4, FAKE, n - 1, None, FAKE, 40, 0, FAKE, None, None, None, None, FAKE, 1 << 30,
+               None) == binding.ERR_WORKSPACE
+    assert lag(4, 4, FAKE, n, None, FAKE, 3, 0, FAKE, None, None, None, None, FAKE, 1 << 30,
+               None) == binding.ERR_INVALID_ARG                                  # Bmax < R
+    assert lag(4, 4, FAKE, n, None, FAKE, 40, 0, FAKE, None, None, None, None, FAKE, 8,
+               None) == binding.ERR_WORKSPACE                                    # schedule workspace
+
+
 @cpu_only
 @pytest.mark.parametrize("args,status", [
     ((0, 4, 8, 15, 0), binding.ERR_INVALID_ARG),

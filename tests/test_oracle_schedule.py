@@ -116,3 +116,42 @@ def test_out_of_range_confidences_are_clamped():
     assert list(out[0, :3]) == [1.0, 0.0, 0.0]
     assert out[0, 3] == pytest.approx(float(np.float32(0.7)), rel=1e-15)   # T <= 0 counts as 1
     np.testing.assert_array_equal(oracle.temperature_scale(c)[0, :3], [1.0, 0.0, 0.0])
+
+
+def test_lag_without_history_is_the_speed_curve_alone():
+    """Rounds 0 and 1 have no history: all ones, so a = 1 everywhere and
+    Theta(n) = (R + n) SPS(R + n). The ranking then takes position 0 of every request, then
+    position 1, ..., so len[r] = n* // R + (r < n* % R)."""
+    R, G, Bmax = 5, 4, 23
+    g = np.random.default_rng(31)
+    sps = g.uniform(0.5, 2.0, size=Bmax + 1).astype(np.float32)
+    history = [g.uniform(0.05, 0.95, size=(R, G)) for _ in range(2)]
+    n = np.arange(min(R * G, Bmax - R) + 1)
+    n_star = int(np.argmax((R + n) * sps[R + n].astype(np.float64)))
+    want = np.array([n_star // R + (r < n_star % R) for r in range(R)])
+    for t in (0, 1):
+        got = oracle.lagged_schedule(history, t, None, sps, Bmax)
+        assert got["n"] == n_star
+        assert np.array_equal(got["len"], want)
+
+
+def test_lag_reads_round_t_minus_2_only():
+    """Round t's schedule ignores what rounds t and t - 1 recorded (no leak of the tokens
+    being generated) and follows round t - 2."""
+    R, G, Bmax = 6, 5, 40
+    g = np.random.default_rng(32)
+    sps = (1.0 / (0.02 + 1e-3 * np.arange(Bmax + 1))).astype(np.float32)
+    history = [g.uniform(0.05, 0.99, size=(R, G)) for _ in range(6)]
+    for t in range(2, 6):
+        base = oracle.lagged_schedule(history, t, None, sps, Bmax)
+        noisy = [h.copy() for h in history]
+        noisy[t] = g.uniform(0.0, 1.0, size=(R, G))
+        noisy[t - 1] = g.uniform(0.0, 1.0, size=(R, G))
+        same = oracle.lagged_schedule(noisy, t, None, sps, Bmax)
+        assert np.array_equal(base["len"], same["len"]) and base["theta"] == same["theta"]
+        ref = oracle.schedule(history[t - 2], None, sps, Bmax)
+        assert np.array_equal(base["len"], ref["len"]) and base["theta"] == ref["theta"]
+        # a round t - 2 with every confidence at zero schedules nothing
+        zero = [h.copy() for h in history]
+        zero[t - 2] = np.zeros((R, G))
+        assert oracle.lagged_schedule(zero, t, None, sps, Bmax)["len"].sum() == 0
