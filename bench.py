@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["sts"], default="single")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["sts", "pipeline"], default="single")
     ap.add_argument("--no-flush", action="store_true", help="keep the Infinity Cache warm")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -204,6 +204,170 @@ def bench_sts(args, torch, dspark, device):
     print(json.dumps(res), flush=True)
 
 
+def bench_pipeline(args, torch, dspark, device):
+    """The asynchronous round on the round workload's shapes (B=512, V=129280, gamma=16):
+    [P1] "硬件感知与置信度自适应调度机制" (the asynchronous adaptation) and [P3]
+    "Confidence-Scheduled Verification". Step t is scheduled from the confidences of step
+    t - 2 (dspark_schedule_lagged over a dspark_conf_ring), so the schedule depends on
+    nothing this round produces and no host round trip is needed: the whole round (lagged
+    schedule, draft, verify + TV on the rebuilt draft logits, push of this round's
+    confidences) is one captured graph. Variants, each run as `steps` rounds back to back
+    with no host synchronisation between rounds (the Infinity Cache flushed before each
+    round, outside the round's events); the variants take turns over three passes and each
+    reports the median of its three per-pass means:
+      graph              the captured round, schedule before the draft (the `value`);
+      graph_overlapped   the captured round with the schedule on a second stream beside the
+                         draft;
+      eager              the same launches issued from the host each round;
+      eager_sync         the synchronous scheduler the pages contrast it with: the schedule
+                         uses this round's confidences, so it runs after the draft, and the
+                         host reads the verify batch size before it launches verify.
+    bubble_us = eager_sync - graph per round: the host handshake that the lag removes. The
+    same four variants also run on the first 32 requests (`small_batch`), where a round is
+    short and fixed per-round costs weigh more."""
+    c, inp = build_inputs(WORKLOADS["round"])
+    full = {k: to_dev(v, torch, device) for k, v in inp.items()}
+    G, V = c.gamma, c.V
+    Bmax = 4096
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=device)
+
+    def sequence(fn, n):
+        """n rounds back to back; each round's GPU span from events recorded after its flush
+        and after its last launch (no host synchronisation between rounds)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            if not args.no_flush:
+                flush.sum()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def measure(B):
+        """The four variants on the first B requests of the workload."""
+        t = dict(full)
+        for k in ("U", "x0", "u", "conf", "u_acc", "u_fin"):
+            t[k] = full[k][:B].contiguous()
+        t["Lt"] = full["Lt"][: B * (G + 1)]
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        out_d = dict(x=torch.empty((B, G), **i32), q=torch.empty((B, G), **f32),
+                     lse=torch.empty((B, G), **f32), L=None)
+        out_s = dict(len=torch.empty(B, **i32), t_off=torch.empty(B + 1, **i32),
+                     K=torch.empty(1, **i32), theta=torch.empty(1, **f32))
+        out_v = dict(n=torch.empty(B, **i32), y=torch.empty((B, G + 1), **i32),
+                     lse_t=torch.empty((B, G + 1), **f32), cstar=torch.empty((B, G), **f32))
+        ring = dspark.ConfRing(B, G, device=device)
+        side = torch.cuda.Stream(device=device)
+
+        def draft():
+            dspark.markov_draft(t["U"], t["W1"], t["W2"], t["x0"], t["u"], out=out_d)
+
+        def verify():
+            dspark.verify_markov(t["U"], t["W1"], t["W2"], t["x0"], out_d["x"], out_d["lse"],
+                                 t["Lt"], t["u_acc"], t["u_fin"], t_off=out_s["t_off"],
+                                 length=out_s["len"], out=out_v)
+
+        def round_async(overlap: bool):
+            main = torch.cuda.current_stream()
+            if overlap:
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    dspark.schedule_lagged(ring, t["sps"], Bmax, temp=t["temp"], out=out_s)
+                draft()
+                main.wait_stream(side)
+            else:
+                dspark.schedule_lagged(ring, t["sps"], Bmax, temp=t["temp"], out=out_s)
+                draft()
+            verify()
+            ring.push(t["conf"])
+
+        def round_sync():
+            draft()
+            dspark.schedule(t["conf"], t["sps"], Bmax, temp=t["temp"], out=out_s)
+            int(out_s["K"].item())                    # the host handshake
+            verify()
+
+        for _ in range(max(2, args.warmup)):
+            round_async(True)
+            round_async(False)
+            round_sync()
+        torch.cuda.synchronize()
+        graphs = {}
+        for name, overlap in (("graph", False), ("graph_overlapped", True)):
+            graphs[name] = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graphs[name]):
+                round_async(overlap)
+        torch.cuda.synchronize()
+        for _ in range(args.profile_steps):
+            graphs["graph"].replay()
+        for _ in range(args.warmup):
+            graphs["graph"].replay()
+        variants = dict(graph=graphs["graph"].replay,
+                        graph_overlapped=graphs["graph_overlapped"].replay,
+                        eager=lambda: round_async(False), eager_sync=round_sync)
+        runs = {name: [] for name in variants}
+        means = {name: [] for name in variants}
+        for _ in range(3):                            # variants interleaved, three passes
+            for name, fn in variants.items():
+                r = sequence(fn, args.steps)
+                runs[name] += r
+                means[name].append(float(np.mean(r)))
+        per_round = {k: float(np.median(v)) for k, v in means.items()}
+        pct = {k: [float(np.percentile(v, 10)), float(np.percentile(v, 90))] for k, v in runs.items()}
+        graphs["graph"].replay()
+        torch.cuda.synchronize()
+        verified = int(out_s["len"].sum().item())
+        return t, draft, per_round, pct, verified
+
+    B = c.B
+    small_B = 32
+    _, _, small_round, _, small_verified = measure(small_B)
+    t, draft, per_round, pct, verified = measure(B)
+    n = args.steps
+    # the draft alone (the dominant kernel), captured the same way
+    g_draft = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_draft):
+        draft()
+    draft_ms = float(np.mean(sequence(g_draft.replay, n)))
+    drafted = B * G
+    ms_round = per_round["graph"]
+    per_pos = draft_bytes_per_position(c, False)
+    one = dspark.markov_draft_one_launch(B, t["W1"], t["W2"])
+    kernel = "draft_slab_resident" if one else "draft_slab_step + draft_slab_select"
+    units = G if one else 1
+    launch_us = draft_ms * 1e3 / (1 if one else G)
+    achieved = per_pos * units / (launch_us * 1e-6) / 1e9
+    roof = dict(bound="hbm", kernel=kernel, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=achieved / HBM_PEAK_GBS, traffic=None, bytes_per_launch=per_pos * units,
+                positions_per_launch=units, launch_us=launch_us)
+    res = dict(
+        metric=METRIC, value=(drafted + verified) / (ms_round * 1e-3), unit="tokens/s", n_gpus=1,
+        steps=n, warmup=args.warmup, ms_per_step=ms_round, higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload=f"{c.name}: asynchronous rounds (two-step-lag schedule, one captured "
+                             "graph per round, rounds back to back)", B=B, V=V, r=c.r, gamma=G,
+                    factors=c.w_dtype, sps="1/(0.02+1e-5 B)", Bmax=Bmax,
+                    mall_flush=not args.no_flush, graph_replay=True,
+                    draft_logits="rebuilt by verify from the factors"),
+        drafted_per_step=drafted, verified_per_step=verified,
+        pipeline_ms_per_round=per_round,
+        pipeline_p10_p90=pct,
+        bubble_us=(per_round["eager_sync"] - ms_round) * 1e3,
+        small_batch=dict(B=small_B, ms_per_round=small_round,
+                         bubble_us=(small_round["eager_sync"] - small_round["graph"]) * 1e3,
+                         tokens_per_s=(small_B * G + small_verified) / (small_round["graph"] * 1e-3)),
+        draft_us=draft_ms * 1e3,
+        roofline=roof,
+    )
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_seconds, False)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -216,6 +380,8 @@ def main():
     device = torch.device("cuda:0")
     if args.workload == "sts":
         return bench_sts(args, torch, dspark, device)
+    if args.workload == "pipeline":
+        return bench_pipeline(args, torch, dspark, device)
     cfg = WORKLOADS[args.workload]
     verify_only = args.workload == "verify"
     c, inp = build_inputs(cfg)
