@@ -43,17 +43,18 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
     ("single", "draft_resident"): dict(
-        bytes=87291618.0,
+        bytes=87276875.8,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
         sources={"draft_resident.hip": "bca35370d74d6723c8eca0d01c55009e66855f4e33f82bef3537403917327cf1",
-                 "draw.h": "1176839c2edc2f5bb830cb6cd198946f040c954242ee8c435ee65da753590588",
+                 "draw.h": "c5d35c4890d54a93c797ec16ce7ce653347440b96762794e07ef01432d4d8b05",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
-    ("single", "draft_step_gemv"): dict(
-        bytes=79281052.0,
-        profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
-        sources={"draft.hip": "00feb01c6db9ffaa05974bf39e3f95d1476d01bef333d04b8f7b519855a5ce9f",
-                 "draw.h": "68a13dee38665bffbf47caea15375a90352debe18a3fe1aff59075732b46e18b",
-                 "common.h": "739a5e62ecf98417fbae5c9345a0180ded0f8e56c092c2fffa7484408e8627f4"}),
+    ("round", "draft_slab_resident"): dict(
+        bytes=4838332360.1,
+        profile="profiles/draft_slab_resident_round_B512_V129280.md",
+        sources={"draft_slab.hip": "11dc9f442b086fd296ba42dd29d510f7b9a3404b9d86ff6c8788b896f7fd93ea",
+                 "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
+                 "draw.h": "c5d35c4890d54a93c797ec16ce7ce653347440b96762794e07ef01432d4d8b05",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
 }
 
 
@@ -341,9 +342,10 @@ def bench_pipeline(args, torch, dspark, device):
     units = G if one else 1
     launch_us = draft_ms * 1e3 / (1 if one else G)
     achieved = per_pos * units / (launch_us * 1e-6) / 1e9
+    # the same kernel on the same shapes as the round workload: its counter record applies
     roof = dict(bound="hbm", kernel=kernel, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=achieved / HBM_PEAK_GBS, traffic=None, bytes_per_launch=per_pos * units,
-                positions_per_launch=units, launch_us=launch_us)
+                frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("round", kernel),
+                bytes_per_launch=per_pos * units, positions_per_launch=units, launch_us=launch_us)
     res = dict(
         metric=METRIC, value=(drafted + verified) / (ms_round * 1e-3), unit="tokens/s", n_gpus=1,
         steps=n, warmup=args.warmup, ms_per_step=ms_round, higher_is_better=True,
@@ -529,7 +531,7 @@ def main():
                     bytes_per_launch=bytes_launch, positions_per_launch=units,
                     launch_us=launch_us, draft_path=path)
         if path in ("mfma", "slab"):
-            tflops = 2.0 * B * c.r * V / (launch_us * 1e-6) / 1e12
+            tflops = 2.0 * B * c.r * V * units / (launch_us * 1e-6) / 1e12
             roof["mfma"] = dict(achieved=tflops, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                 frac=tflops / MFMA_BF16_PEAK_TFLOPS)
     what = "verify + TV labels" if verify_only else "draft + schedule + verify + TV labels"
