@@ -46,14 +46,14 @@ MEASURED_TRAFFIC = {
         bytes=87276875.8,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
         sources={"draft_resident.hip": "bca35370d74d6723c8eca0d01c55009e66855f4e33f82bef3537403917327cf1",
-                 "draw.h": "c5d35c4890d54a93c797ec16ce7ce653347440b96762794e07ef01432d4d8b05",
+                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
         bytes=4838332360.1,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
         sources={"draft_slab.hip": "11dc9f442b086fd296ba42dd29d510f7b9a3404b9d86ff6c8788b896f7fd93ea",
                  "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
-                 "draw.h": "c5d35c4890d54a93c797ec16ce7ce653347440b96762794e07ef01432d4d8b05",
+                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
 }
 

@@ -239,81 +239,6 @@ __device__ __forceinline__ SlabWalk walk_slab8(const float2 (&p)[8], float m, fl
     return r;
 }
 
-// pick_tile with the partials left in memory (P[0 .. ntw), tiles past ntw absent) and read
-// again in each of the three passes, CH at a time (CH loads in flight, 2 CH registers), instead
-// of all NREG held in registers: the same operations in the same order, so the result is
-// bit-identical to pick_tile<NREG> on the same partials.
-template <int NREG, int CH, bool COHERENT>
-__device__ __forceinline__ TilePick pick_tile_mem(const float2* __restrict__ P, int ntw, float u) {
-    static_assert(NREG % CH == 0, "whole chunks");
-    const int lane = threadIdx.x & (kWave - 1);
-    const int i0 = lane * NREG;
-    float2 v[CH];
-    auto load = [&](int c) {
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int i = i0 + c + j;
-            v[j] = (i < ntw) ? load_part<COHERENT>(P + i) : make_float2(-INFINITY, 0.0f);
-        }
-    };
-    TilePick r;
-    float m = -INFINITY;
-    for (int c = 0; c < NREG; c += CH) {
-        load(c);
-#pragma unroll
-        for (int j = 0; j < CH; ++j) m = fmaxf(m, v[j].x);
-        asm volatile("" : "+v"(m) :: "memory");       // the next chunk's loads wait for this one
-    }
-    m = wave_max_dpp(m);
-    r.m = m;
-    if (m == -INFINITY) {
-        r.tile = -1;
-        r.lse = -INFINITY;
-        r.tprime = INFINITY;
-        return r;
-    }
-    float local = 0.0f;
-    for (int c = 0; c < NREG; c += CH) {
-        load(c);
-#pragma unroll
-        for (int j = 0; j < CH; ++j) local += tile_mass(v[j], m);
-        asm volatile("" : "+v"(local) :: "memory");
-    }
-    const float Z = wave_sum_dpp(local);
-    r.lse = m + __logf(Z);
-    const float target = clamp_uniform(u) * Z;
-    const float incl = wave_incl_scan_dpp(local);
-    float run = wave_shr1_dpp(incl);
-    int hit = INT32_MAX, last = -1;
-    float before = 0.0f;
-    for (int c = 0; c < NREG; c += CH) {
-        load(c);
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const float mt = tile_mass(v[j], m);
-            const float nr = run + mt;
-            if (mt > 0.0f) {
-                last = i0 + c + j;
-                if (hit == INT32_MAX && nr > target) {
-                    hit = i0 + c + j;
-                    before = run;
-                }
-            }
-            run = nr;
-        }
-        asm volatile("" : "+v"(run) :: "memory");
-    }
-    const int found = wave_min_int_dpp(hit);
-    if (found == INT32_MAX) {
-        r.tile = wave_max_int_dpp(last);
-        r.tprime = INFINITY;
-    } else {
-        r.tile = found;
-        r.tprime = target - wave_bcast(before, found / NREG);
-    }
-    return r;
-}
-
 // The draw from tile partials already in registers: lane l holds tiles
 // [l * RegTiles, (l + 1) * RegTiles), absent tiles as (-inf, 0). Returns the token (-1 for a
 // request with no mass) in every lane; `row` is read only for the in-tile rescan.
