@@ -43,7 +43,8 @@ enum VmRec { kUrow = 0, kTrow, kHrow, kXk, kLsd, kLst, kRb, kRk };
 
 template <int NT>
 struct VmLds {
-    static constexpr int UT = kSlabWaves * NT * 2 * 256;   // one group's U (or L_t) slice
+    static constexpr int NTP = (NT + 1) / 2;                // 1 KB blocks per wave: 2 tiles x 8 rows
+    static constexpr int UT = kSlabWaves * NTP * 1024;      // one group's U (or L_t) slice
     static constexpr int HB = kRows * kHRow;                // the group's W1 rows, 4 KB
     static constexpr int Buf = 2 * UT + HB;
     static constexpr int Meta = 4 * kFields * kRows * 4;    // record ring, 4 groups
@@ -143,7 +144,7 @@ void vm_tv(VmArgs a) {
     using S = Slab<NT>;
     using Ly = VmLds<NT>;
     static_assert(kSlabWaves * S::Stage <= Ly::Buf, "W2 staging fits in buffer 2");
-    constexpr int NL = 4 * NT + 2;                    // direct loads per wave and group
+    constexpr int NL = 2 * Ly::NTP + 2;               // direct loads per wave and group
     extern __shared__ __align__(16) char sm[];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int slab = blockIdx.x;
@@ -160,33 +161,26 @@ void vm_tv(VmArgs a) {
         lds_dma4(a.rec + static_cast<long long>(lane >> 3) * a.cap + row,
                  lds_addr(meta) + 4 * (g & 3) * (kFields * kRows));
     };
-    // U and L_t slices of group g: per tile two 4-byte direct loads (rows 0-3, 4-7); lane l
-    // of half h takes row 4h + l / 16, column group ((l / 4) % 4) ^ (row / 4) (a swizzle for
-    // conflict-free epilogue reads), element l % 4. W1 rows: wave w loads row w of the
-    // group, 16-byte piece p of the row at position p ^ w. Every lane issues every load.
+    // U and L_t slices of group g: per pair of tiles one 16-byte direct load each, into a
+    // 1 KB block of 64 slots; slot l holds row l / 8, 4-column chunk (l % 8) ^ (l / 8) of the
+    // pair's 32 columns (a swizzle for conflict-free epilogue reads). Chunks past V load
+    // column 0 (the epilogue masks them). W1 rows: wave w loads row w of the group, 16-byte
+    // piece p of the row at position p ^ w. Every lane issues every load.
     auto issue = [&](int g, int i) {
         const int* mt = meta + (g & 3) * (kFields * kRows);
-        const uint32_t ub = lds_addr(sm) + i * Ly::Buf;
+        const uint32_t ub = lds_addr(sm) + i * Ly::Buf + wave * Ly::NTP * 1024;
         const uint32_t lb = ub + Ly::UT;
-        const uint32_t hb = ub + 2 * Ly::UT;
-        // the empty asm makes the column base opaque, so that the per-tile addresses are
-        // formed here instead of being hoisted out of the group loop (kept live, they would
-        // not fit beside the W2 fragments)
-        int cbase = static_cast<int>(cw) + (lane & 3);
-        asm volatile("" : "+v"(cbase));
+        const uint32_t hb = lds_addr(sm) + i * Ly::Buf + 2 * Ly::UT;
+        const int l = opaque_lane(), lr = l >> 3;
+        const int cbase = static_cast<int>(cw) + 4 * ((l & 7) ^ lr);
+        const float* up = a.U + static_cast<long long>(mt[kUrow * kRows + lr]) * a.V;
+        const float* tp = a.Lt + static_cast<long long>(mt[kTrow * kRows + lr]) * a.V;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int rr = 4 * h + (lane >> 4);
-            const int c0 = cbase + 4 * (((lane >> 2) & 3) ^ h);
-            const float* up = a.U + static_cast<long long>(mt[kUrow * kRows + rr]) * a.V;
-            const float* tp = a.Lt + static_cast<long long>(mt[kTrow * kRows + rr]) * a.V;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int col = min(c0 + 16 * t, a.V - 1);   // past V: any valid element
-                const int off = ((wave * NT + t) * 2 + h) * 256;
-                lds_dma4(up + col, ub + off);
-                lds_dma4(tp + col, lb + off);
-            }
+        for (int q = 0; q < Ly::NTP; ++q) {
+            int col = cbase + 32 * q;
+            if (col > a.V - 4) col = 0;
+            lds_dma16(up + col, ub + q * 1024);
+            lds_dma16(tp + col, lb + q * 1024);
         }
         const int hrow = mt[kHrow * kRows + wave];
 #pragma unroll
@@ -268,13 +262,13 @@ void vm_tv(VmArgs a) {
         const float lsd = __int_as_float(mt[kLsd * kRows + rr]);
         const float lst = __int_as_float(mt[kLst * kRows + rr]);
         const int xk = mt[kXk * kRows + rr];
-        const int pos = 16 * (rr & 3) + 4 * (cg ^ ((rr >> 2) & 3));
         float smin = 0.0f, sres = 0.0f;
         bool has_ldx = false;
         float ldx_v = 0.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int off = ((wave * NT + t) * 2 + (rr >> 2)) * 256 + 4 * pos;
+            const int c = ((t & 1) << 2) + cg;        // chunk of the tile pair t / 2
+            const int off = (wave * Ly::NTP + (t >> 1)) * 1024 + 16 * (rr * 8 + (c ^ rr));
             const float4 u4 = *reinterpret_cast<const float4*>(ub + off);
             const float4 t4 = *reinterpret_cast<const float4*>(lb + off);
             const long long col = cw + 16 * t + 4 * cg;
