@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--materialised-logits", action="store_true",
                     help="draft writes its logits and verify reads them, also where the verify "
                          "could rebuild them from the Markov factors")
+    ap.add_argument("--rebuilt-logits", action="store_true",
+                    help="verify rebuilds the draft logits from the Markov factors wherever the "
+                         "draft takes the slab path, also past V = 131072")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="extra eager steps with no timing (for rocprofv3 runs)")
     return ap.parse_args()
@@ -395,7 +398,8 @@ def main():
     # factors (dspark_verify_markov) and the draft does not write them
     # (at V > 131072 the rebuilding pass holds five 16-column tiles of W2 per wave, which
     # does not fit its registers without spills, and writing the logits is faster there)
-    rebuild = (not verify_only and not args.materialised_logits and V <= 131072 and
+    rebuild = (not verify_only and not args.materialised_logits and
+               (V <= 131072 or args.rebuilt_logits) and
                dspark.markov_draft_path(B, t["W1"], t["W2"]) == "slab")
     out_d = dict(x=torch.empty((B, G), dtype=torch.int32, device=device),
                  q=torch.empty((B, G), dtype=torch.float32, device=device),
