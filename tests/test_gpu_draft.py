@@ -165,11 +165,15 @@ def test_slab_permutation_chain_and_sentinels(gpu):
             assert 0.99 < out["q"][b, k] <= 1.0
 
 
-def test_slab_max_batch(gpu):
-    """The slab path at its batch cap on the full vocabulary (2048 requests, V = 151936), one
-    position; sampled requests against the oracle. U is generated on the device (seeded) and
-    the sampled rows are copied back for the oracle."""
-    B, V, r = 2048, 151936, 256
+@pytest.mark.parametrize("B,one_launch", [
+    (2044, True),     # the largest batch whose persistent launch fits in LDS at V = 151936
+    (2048, False),    # the slab path's cap: per-position launches
+])
+def test_slab_max_batch(gpu, B, one_launch):
+    """The slab path at its LDS limits on the full vocabulary (V = 151936), one position;
+    sampled requests against the oracle. U is generated on the device (seeded) and the
+    sampled rows are copied back for the oracle."""
+    V, r = 151936, 256
     c = synth.custom(962, B=2, V=V, r=r, gamma=1, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
     gen = torch.Generator(device="cuda").manual_seed(962)
@@ -178,9 +182,10 @@ def test_slab_max_batch(gpu):
     u = torch.rand((B, 1), generator=gen, device="cuda").clamp_(max=1 - 2 ** -24)
     W1, W2 = dev(d["W1"]), dev(d["W2"])
     assert dspark.markov_draft_path(B, W1, W2) == "slab"
+    assert dspark.markov_draft_one_launch(B, W1, W2) == one_launch
     out = dspark.markov_draft(U, W1, W2, x0, u)
     torch.cuda.synchronize()
-    reqs = [0, 1, 1023, 2046, 2047]
+    reqs = [0, 1, 1023, B - 2, B - 1]
     idx = torch.tensor(reqs, device="cuda")
     rep = check_draft(host(U[idx]), d["W1"], d["W2"], host(x0[idx]), host(u[idx]), "bf16",
                       host(out["x"][idx]), host(out["q"][idx]), host(out["lse"][idx]),
