@@ -16,10 +16,12 @@
 //   vm_scan   - offsets of each request's verified draft rows in a compact row list;
 //   vm_rows   - lse of the target rows, and one record per verified draft row (U row, target
 //               row, W1 row of the previous token, drafted token, both normalisers);
-//   vm_tv     - slab pass over the compact rows, 8 rows per group: U, L_t and W1 rows arrive
-//               in LDS by direct loads two groups ahead; per row and wave tile it leaves
+//   vm_tv     - slab pass over the compact rows: U, L_t and W1 rows arrive in LDS by direct
+//               loads ahead of the group being computed; per row and wave tile it leaves
 //               sum min(p_d, p_t) and sum max(0, p_t - p_d), and the draft logit of the
-//               drafted token;
+//               drafted token. Up to four 16-column tiles per wave (vm_tv16): groups of 16
+//               rows, the MFMA's full width, one group ahead; five tiles (vm_tv): groups of
+//               8 rows, two groups ahead, as five tiles of 16 rows do not fit in LDS twice;
 //   vm_select - per request: acceptance scan (same test as the materialised verify), TV labels
 //               (wave-tile sums in tile order), and the final draw: the residual from its
 //               wave-tile masses with the chosen tile recomputed by MFMA, or p_t (bonus, or a
@@ -271,6 +273,172 @@ void vm_tv(VmArgs a) {
             const int off = (wave * Ly::NTP + (t >> 1)) * 1024 + 16 * (rr * 8 + (c ^ rr));
             const float4 u4 = *reinterpret_cast<const float4*>(ub + off);
             const float4 t4 = *reinterpret_cast<const float4*>(lb + off);
+            const long long col = cw + 16 * t + 4 * cg;
+            const bool ok = col < a.V;
+            const float ld[4] = {ok ? u4.x + acc[t][0] : -INFINITY, ok ? u4.y + acc[t][1] : -INFINITY,
+                                 ok ? u4.z + acc[t][2] : -INFINITY, ok ? u4.w + acc[t][3] : -INFINITY};
+            const float lt[4] = {ok ? t4.x : -INFINITY, ok ? t4.y : -INFINITY,
+                                 ok ? t4.z : -INFINITY, ok ? t4.w : -INFINITY};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float pd = pexp(ld[v], lsd), pt = pexp(lt[v], lst);
+                smin += fminf(pd, pt);
+                sres += fmaxf(pt - pd, 0.0f);
+                if (valid && ok && xk == col + v) {
+                    has_ldx = true;
+                    ldx_v = ld[v];
+                }
+            }
+        }
+        smin += swz_xor16(smin);
+        smin += __shfl_xor(smin, 32, kWave);
+        sres += swz_xor16(sres);
+        sres += __shfl_xor(sres, 32, kWave);
+        pend_j = valid ? j : -1;
+        pend_part = make_float2(smin, sres);
+        pend_ldx = ldx_v;
+        pend_has_ldx = has_ldx;
+    }
+    flush();
+}
+
+// vm_tv for NT <= 4 with groups of 16 rows (the MFMA's N): lane (rq, cg) of the epilogue owns
+// row rq, columns 4 cg .. 4 cg + 3 of each tile, as in vm_tv, so the per-lane sums and their
+// reductions run in the same order and the outputs are bit-identical. Two LDS buffers: the
+// loads of group g + 1 are issued after the barrier of group g and land while it is computed.
+constexpr int kRows16 = 16;
+
+template <int NT>
+struct VmLds16 {
+    static constexpr int UT = kSlabWaves * NT * 1024;      // [wave][tile][16 rows][16 cols] fp32
+    static constexpr int HB = kRows16 * kHRow;             // the group's W1 rows, 8 KB
+    static constexpr int Buf = 2 * UT + HB;
+    static constexpr int Meta = 4 * kFields * kRows16 * 4; // record ring, 4 groups
+    static constexpr int Total = 2 * Buf + Meta;
+};
+
+template <int NT>
+__global__ __launch_bounds__(kSlabThreads)
+void vm_tv16(VmArgs a) {
+    using S = Slab<NT>;
+    using Ly = VmLds16<NT>;
+    static_assert(NT <= 4 && Ly::Total <= kLdsBytes, "two buffers of 16-row groups fit in LDS");
+    static_assert(kSlabWaves * S::Stage <= Ly::Buf, "W2 staging fits in buffer 1");
+    extern __shared__ __align__(16) char sm[];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int slab = blockIdx.x;
+    const long long cw = static_cast<long long>(slab) * S::SW + wave * S::WC;
+    const int nd = *a.nd;
+    const int ng = (nd + kRows16 - 1) / kRows16;
+    if (ng == 0) return;
+    int* meta = reinterpret_cast<int*>(sm + 2 * Ly::Buf);
+    // record ring slot: field f of row i of the group at [(i / 8) * 64 + f * 8 + i % 8]
+    auto fld = [](const int* mt, int f, int i) { return mt[(i >> 3) * 64 + f * 8 + (i & 7)]; };
+
+    // records of group g into ring slot g % 4 (wave 0 only), two 4-byte direct loads: lane l
+    // of load h takes field l / 8 of row 16 g + 8 h + l % 8 (rows past the end repeat the last)
+    auto meta_issue = [&](int g) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = min(g * kRows16 + 8 * h + (lane & 7), nd - 1);
+            lds_dma4(a.rec + static_cast<long long>(lane >> 3) * a.cap + row,
+                     lds_addr(meta) + 4 * ((g & 3) * (kFields * kRows16) + 64 * h));
+        }
+    };
+    // U and L_t tiles of group g as in the slab draft ([16 rows][16 cols] per tile, lane l
+    // loads row l / 4, 4-column chunk (l % 4) ^ ((l / 16) % 4)); W1 rows: wave w fills rows
+    // 2w, 2w + 1, lane l loads 16-byte piece (l % 32) ^ (row % 16). Every lane issues every
+    // load; chunks past V load column 0 (the epilogue masks them).
+    auto issue = [&](int g, int i) {
+        const int* mt = meta + (g & 3) * (kFields * kRows16);
+        const uint32_t ub = lds_addr(sm) + i * Ly::Buf + wave * NT * 1024;
+        const uint32_t lb = ub + Ly::UT;
+        const uint32_t hb = lds_addr(sm) + i * Ly::Buf + 2 * Ly::UT;
+        const int l = opaque_lane();
+        const int u_rq = l >> 2, u_ch = (l & 3) ^ ((l >> 4) & 3);
+        const float* up = a.U + static_cast<long long>(fld(mt, kUrow, u_rq)) * a.V;
+        const float* tp = a.Lt + static_cast<long long>(fld(mt, kTrow, u_rq)) * a.V;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            int col = static_cast<int>(cw) + 16 * t + 4 * u_ch;
+            if (col > a.V - 4) col = 0;
+            lds_dma16(up + col, ub + t * 1024);
+            lds_dma16(tp + col, lb + t * 1024);
+        }
+        const int h_row = 2 * wave + (l >> 5), h_piece = (l & 31) ^ (h_row & 15);
+        const int piece = (8 * h_piece < a.r) ? h_piece : 0;
+        lds_dma16(a.W1 + static_cast<long long>(fld(mt, kHrow, h_row)) * a.r + 8 * piece,
+                  hb + wave * 1024);
+    };
+
+    if (wave == 0) {
+        meta_issue(0);
+        if (ng > 1) meta_issue(1);
+    }
+    wait_vm_lgkm<0>();
+    __syncthreads();
+    issue(0, 0);
+    bf16x8 w2f[NT][kKS];
+    load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + Ly::Buf + wave * S::Stage);
+    wait_lgkm0();
+    __syncthreads();                                  // buffer 1 (the staging area) is free
+
+    const int rq = lane & 15, cg = lane >> 4;
+    const int upos = 4 * rq + (cg ^ ((rq >> 2) & 3));  // this lane's 16 bytes of a tile
+    long long pend_j = -1;
+    float2 pend_part = make_float2(0.0f, 0.0f);
+    float pend_ldx = 0.0f;
+    bool pend_has_ldx = false;
+    auto flush = [&]() {
+        if (pend_j < 0) return;
+        if (cg == 0) a.part[pend_j * a.ntw + slab * kSlabWaves + wave] = pend_part;
+        if (pend_has_ldx) a.ldx[pend_j] = pend_ldx;
+    };
+    for (int g = 0; g < ng; ++g) {
+        const int i = g & 1;
+        // group g's loads and the records of group g + 1 were issued in the previous
+        // iteration; nothing issued since is needed later than them
+        wait_vm_lgkm<0>();
+        bare_barrier();
+        flush();
+        if (wave == 0 && g + 2 < ng) meta_issue(g + 2);   // slot of group g - 2, now free
+        if (g + 1 < ng) issue(g + 1, i ^ 1);
+
+        const char* ub = sm + i * Ly::Buf + wave * NT * 1024;
+        const char* lb = ub + Ly::UT;
+        const char* H = sm + i * Ly::Buf + 2 * Ly::UT;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const int hl = opaque_lane(), hrq = hl & 15, hcg = hl >> 4;
+        auto hfrag = [&](int s) {
+            const int p = (4 * s + hcg) ^ hrq;
+            return *reinterpret_cast<const bf16x8*>(H + hrq * kHRow + 16 * p);
+        };
+        bf16x8 hf = hfrag(0);
+#pragma unroll
+        for (int s = 0; s < kKS; ++s) {
+            const bf16x8 hn = (s + 1 < kKS) ? hfrag(s + 1) : hf;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
+            asm volatile("" ::: "memory");
+            hf = hn;
+        }
+
+        const int* mt = meta + (g & 3) * (kFields * kRows16);
+        const long long j = static_cast<long long>(g) * kRows16 + rq;
+        const bool valid = j < nd;
+        const float lsd = __int_as_float(fld(mt, kLsd, rq));
+        const float lst = __int_as_float(fld(mt, kLst, rq));
+        const int xk = fld(mt, kXk, rq);
+        float smin = 0.0f, sres = 0.0f;
+        bool has_ldx = false;
+        float ldx_v = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float4 u4 = *reinterpret_cast<const float4*>(ub + t * 1024 + 16 * upos);
+            const float4 t4 = *reinterpret_cast<const float4*>(lb + t * 1024 + 16 * upos);
             const long long col = cw + 16 * t + 4 * cg;
             const bool ok = col < a.V;
             const float ld[4] = {ok ? u4.x + acc[t][0] : -INFINITY, ok ? u4.y + acc[t][1] : -INFINITY,
@@ -582,8 +750,12 @@ hipError_t launch_nt(const VerifyMarkovCall& c, hipStream_t st) {
     v.V = rs.V; v.r = c.r; v.ntw = verify_markov_tiles(rs.V); v.cap = cap;
     v.U = c.U; v.W1 = static_cast<const uint16_t*>(c.W1); v.W2 = static_cast<const uint16_t*>(c.W2);
     v.Lt = rs.Lt; v.rec = c.rec; v.nd = c.d_off + rs.B; v.part = c.tvpart; v.ldx = c.ldx;
-    hipLaunchKernelGGL(vm_tv<NT>, dim3(static_cast<unsigned>(slab_count(rs.V))), dim3(kSlabThreads),
-                       VmLds<NT>::Total, st, v);
+    if constexpr (NT <= 4)
+        hipLaunchKernelGGL(vm_tv16<NT>, dim3(static_cast<unsigned>(slab_count(rs.V))),
+                           dim3(kSlabThreads), VmLds16<NT>::Total, st, v);
+    else
+        hipLaunchKernelGGL(vm_tv<NT>, dim3(static_cast<unsigned>(slab_count(rs.V))), dim3(kSlabThreads),
+                           VmLds<NT>::Total, st, v);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     SelArgs s;
     s.rs = rs; s.nch = nch; s.r = c.r; s.ntw = v.ntw;
