@@ -51,7 +51,7 @@ MEASURED_TRAFFIC = {
     ("round", "draft_slab_resident"): dict(
         bytes=4838332360.1,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
-        sources={"draft_slab.hip": "11dc9f442b086fd296ba42dd29d510f7b9a3404b9d86ff6c8788b896f7fd93ea",
+        sources={"draft_slab.hip": "3275a338565d4c182952204e62fb4f961fbf876643d3026fe475f5b38d0f424e",
                  "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),

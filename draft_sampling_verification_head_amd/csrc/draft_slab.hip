@@ -62,7 +62,7 @@ struct SlabArgs {
     float2* part;             // [B][ntw] (max, sum exp) per request and wave tile
     float2* spart;            // resident: [B][G] the same per request and slab (8 wave tiles)
     unsigned long long* flags;   // resident: [3][gamma][G], kEmpty until published
-    float4* picks;            // resident: [B] (tile, max, lse, mass left in the tile)
+    float4* picks;            // resident: [B] (slab, max, lse, mass left in the slab)
 };
 
 constexpr unsigned kSpinMax = 1u << 20;             // bounded flag wait, about a second
@@ -463,10 +463,11 @@ void draft_slab_select(SlabArgs a, int k) {
 }
 
 // All positions in one launch (see the file comment). Per position k three flag rows,
-// [f][k][g] for f = 0, 1, 2: workgroup g's partials, its tile picks, its tokens published.
-// The draw is split so that no workgroup needs a second copy of W2: workgroup g picks the
-// tiles of its share of the requests (b = g, g + G, ...), and the wave that holds a picked
-// tile in registers recomputes that tile's logits and draws the token.
+// [f][k][g] for f = 0, 1, 2: workgroup g's slab partials, its slab picks, its tokens
+// published. The draw is split so that no workgroup needs a second copy of W2: workgroup g
+// picks the slab of its share of the requests (b = g, g + G, ...); the workgroup of a
+// picked slab walks its 8 tile partials, and the wave that holds the chosen tile in
+// registers recomputes that tile's logits and draws the token.
 template <int NT>
 __global__ __launch_bounds__(kSlabThreads)
 void draft_slab_resident(SlabArgs a) {
