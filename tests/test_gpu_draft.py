@@ -331,3 +331,30 @@ def test_sampler_chi_squared(gpu):
     counts = np.bincount(host(out["x"])[:, 0], minlength=V).astype(float)
     p = oracle.softmax_row(U1.astype(np.float64) + W1[5].astype(np.float64) @ W2.astype(np.float64))[0]
     assert scipy.stats.chisquare(counts, N * p).pvalue > 1e-3
+
+
+@pytest.mark.parametrize("B,V,r,G,wdt,want_logits", [
+    (4, 3000, 32, 7, "f32", True),          # vocabulary sweep
+    (1, 20000, 256, 9, "bf16", False),      # single-request resident launch
+    (40, 40000, 256, 6, "bf16", False),     # slab path, persistent launch
+    (40, 40000, 256, 6, "bf16", True),      # slab path, per-position launches
+])
+def test_resume_split_generation(gpu, B, V, r, G, wdt, want_logits):
+    """Resuming a generation: a gamma-position draft equals a g1-position draft followed by a
+    (gamma - g1)-position draft started from the last drafted token with the remaining U rows
+    and uniforms, bit for bit (position k depends only on U_k, x_{k-1}, u_k and the factors)."""
+    c = synth.custom(990 + B + G, B=B, V=V, r=r, gamma=G, w_dtype=wdt, w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    full = run_draft(d, want_logits=want_logits)
+    for g1 in (1, G // 2, G - 1):
+        a = dict(d, U=np.ascontiguousarray(d["U"][:, :g1]), u=np.ascontiguousarray(d["u"][:, :g1]))
+        first = run_draft(a, want_logits=want_logits)
+        b = dict(d, U=np.ascontiguousarray(d["U"][:, g1:]), u=np.ascontiguousarray(d["u"][:, g1:]),
+                 x0=np.ascontiguousarray(first["x"][:, -1]).astype(np.int32))
+        second = run_draft(b, want_logits=want_logits)
+        for k in ("x", "q", "lse"):
+            joined = np.concatenate([first[k], second[k]], axis=1)
+            assert np.array_equal(joined.view(np.uint8), full[k].view(np.uint8)), (g1, k)
+        if want_logits:
+            joined = np.concatenate([first["L"], second["L"]], axis=1)
+            assert np.array_equal(joined.view(np.uint8), full["L"].view(np.uint8)), g1
