@@ -278,66 +278,67 @@ __device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, const bf16
 }
 
 // Draw of request b at position k, by one wave (all 64 lanes active), in three parts.
-//  slab_pick:      the slab (8 wave tiles) holding the inverse-CDF point, from the request's
-//                  slab partials, and the mass still to cover inside it. COH (resident): the
-//                  slab partials the stream merged, read at device scope; else merged here
-//                  from the tile partials (lane l holds tiles [32 l, 32 l + 32), that is slabs
-//                  [4 l, 4 l + 4)) with the same arithmetic.
-//  slab_walk:      the tile of that slab, from its 8 tile partials (walk_slab8).
+//  slab pick:      the slab (8 wave tiles) holding the inverse-CDF point, from the request's
+//                  slab partials, and the mass still to cover inside it: merged from the tile
+//                  partials in registers (slab_pick_regs, lane l holds tiles [32 l, 32 l + 32),
+//                  that is slabs [4 l, 4 l + 4)), or the slab partials the persistent stream
+//                  merged with the same arithmetic (slab_pick_coherent, device scope).
+//  walk:           the tile of that slab, from its 8 tile partials (walk_pick, walk_slab8).
 //  slab_recompute: that tile's logits rebuilt with the MFMA sequence of the stream, from the
-//                  tile's W2 fragments, the W1 row of x_{k-1} (tk, valid when the request has
-//                  mass) and U_k; then the in-tile rescan. `rowv` holds the tile's logits.
+//                  tile's W2 fragments, the W1 row of x_{k-1} and U_k (recompute_loads); then
+//                  the in-tile rescan. `rowv` holds the tile's logits.
 // slab_finish writes the token (COH: at device scope), p(token) and lse.
 constexpr int kSlabRegs = kSelRegs / kSlabWaves;     // slabs per lane (256 slabs at most)
 
-template <bool COH>
-__device__ __forceinline__ TilePick slab_pick(const SlabArgs& a, int b, int k) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const float u = a.u[static_cast<long long>(b) * a.gamma + k];
+// The slab pick from tile partials in registers (lane l holds tiles [32 l, 32 l + 32)): the
+// slab partials merged per lane, then the pick over slabs.
+__device__ __forceinline__ TilePick slab_pick_regs(const float2 (&p)[kSelRegs], float u) {
     float2 sp[kSlabRegs];
-    if (COH) {
-        const float2* P = a.spart + static_cast<long long>(b) * a.G;
 #pragma unroll
-        for (int j = 0; j < kSlabRegs; ++j) {
-            const int i = lane * kSlabRegs + j;
-            sp[j] = (i < a.G) ? load_part<true>(P + i) : make_float2(-INFINITY, 0.0f);
-        }
-    } else {
-        const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw);
+    for (int j = 0; j < kSlabRegs; ++j) {
+        float2 q[8];
 #pragma unroll
-        for (int j = 0; j < kSlabRegs; ++j) {
-            float2 p[8];
-            const int i = lane * kSelRegs + 8 * j;    // first tile of slab 4 lane + j
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                float4 v = make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
-                if (i < a.ntw) v = P4[i / 2 + t];     // ntw is a multiple of 8: slabs are whole
-                p[2 * t] = make_float2(v.x, v.y);
-                p[2 * t + 1] = make_float2(v.z, v.w);
-            }
-            sp[j] = merge_slab8(p);
-        }
+        for (int w = 0; w < 8; ++w) q[w] = p[8 * j + w];
+        sp[j] = merge_slab8(q);
     }
     return pick_tile<kSlabRegs>(sp, u);
 }
 
-// The tile of slab `sl` for a request picked there (m, tprime from slab_pick): the global
+// The slab pick from the slab partials the persistent stream published (device scope).
+__device__ __forceinline__ TilePick slab_pick_coherent(const SlabArgs& a, int b, int k) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float2* P = a.spart + static_cast<long long>(b) * a.G;
+    float2 sp[kSlabRegs];
+#pragma unroll
+    for (int j = 0; j < kSlabRegs; ++j) {
+        const int i = lane * kSlabRegs + j;
+        sp[j] = (i < a.G) ? load_part<true>(P + i) : make_float2(-INFINITY, 0.0f);
+    }
+    return pick_tile<kSlabRegs>(sp, a.u[static_cast<long long>(b) * a.gamma + k]);
+}
+
+// The tile of the picked slab sp.tile from its 8 tile partials p8 (walk_slab8): the global
 // tile index and the mass left inside it.
-__device__ __forceinline__ TilePick slab_walk(const SlabArgs& a, int b, int sl, const TilePick& tp) {
+__device__ __forceinline__ TilePick walk_pick(const TilePick& sp, const float2 (&p8)[8]) {
+    const SlabWalk w = walk_slab8(p8, sp.m, sp.tprime);
+    TilePick r = sp;
+    r.tile = w.w < 0 ? -1 : sp.tile * kSlabWaves + w.w;
+    r.tprime = w.tprime;
+    return r;
+}
+
+// The same, with the 8 partials read from the tile partials in memory.
+__device__ __forceinline__ TilePick slab_walk(const SlabArgs& a, int b, const TilePick& sp) {
     const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw +
-                                                       sl * kSlabWaves);
-    float2 p[8];
+                                                       sp.tile * kSlabWaves);
+    float2 p8[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const float4 v = P4[t];
-        p[2 * t] = make_float2(v.x, v.y);
-        p[2 * t + 1] = make_float2(v.z, v.w);
+        p8[2 * t] = make_float2(v.x, v.y);
+        p8[2 * t + 1] = make_float2(v.z, v.w);
     }
-    const SlabWalk w = walk_slab8(p, tp.m, tp.tprime);
-    TilePick r = tp;
-    r.tile = w.w < 0 ? -1 : sl * kSlabWaves + w.w;
-    r.tprime = w.tprime;
-    return r;
+    return walk_pick(sp, p8);
 }
 
 template <bool COH>
@@ -350,33 +351,64 @@ __device__ __forceinline__ void slab_finish(const SlabArgs& a, int b, int k, int
     if (a.lse_out) a.lse_out[o] = lse;
 }
 
-template <int NT, bool COH>
+// The global operands of a tile's recompute, loaded before the MFMAs: U_k at the lane's
+// columns (lanes of request column 0) and the W1 row of the previous token (every column).
+template <int NT>
+struct RecomputeIn {
+    float4 u4[NT];
+    uint4 hv[kKS];
+};
+
+// HV: the W1 row too (else only U, and slab_recompute loads the row chunk by chunk, which
+// needs fewer registers beside a resident W2 slab).
+template <int NT, bool HV>
+__device__ __forceinline__ void recompute_loads(const SlabArgs& a, int b, int k, int tk, int tile,
+                                                RecomputeIn<NT>& in) {
+    using S = Slab<NT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rq = lane & 15, cg = lane >> 4;
+    if (tk < 0 || tk >= a.V) tk = 0;
+    const long long cw = static_cast<long long>(tile) * S::WC;
+    const float* urow = a.U + (static_cast<long long>(b) * a.gamma + k) * a.V;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const long long col = cw + 16 * t + 4 * cg;
+        in.u4[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (rq == 0 && col < a.V) in.u4[t] = *reinterpret_cast<const float4*>(urow + col);
+    }
+    if (!HV) return;
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+        const int rank = 32 * s + 8 * cg;
+        in.hv[s] = make_uint4(0u, 0u, 0u, 0u);
+        if (rank < a.r) in.hv[s] = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
+    }
+}
+
+template <int NT, bool COH, bool HV>
 __device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, int tk,
                                                const TilePick& tp, const bf16x8 (&w2f)[NT][kKS],
-                                               float* rowv) {
+                                               const RecomputeIn<NT>& in, float* rowv) {
     using S = Slab<NT>;
     constexpr int CPL = (S::WC + kWave - 1) / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int rq = lane & 15, cg = lane >> 4;
-    if (tk < 0 || tk >= a.V) tk = 0;
     const long long cw = static_cast<long long>(tp.tile) * S::WC;
-    const float* urow = a.U + (static_cast<long long>(b) * a.gamma + k) * a.V;
-    float4 u4[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const long long col = cw + 16 * t + 4 * cg;
-        u4[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (rq == 0 && col < a.V) u4[t] = *reinterpret_cast<const float4*>(urow + col);
-    }
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
         // the W1 row of the previous token in every one of the 16 request columns
-        const int rank = 32 * s + 8 * cg;
-        uint4 hv = make_uint4(0u, 0u, 0u, 0u);
-        if (rank < a.r) hv = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
+        uint4 hv;
+        if constexpr (HV) {
+            hv = in.hv[s];
+        } else {
+            const int rank = 32 * s + 8 * cg;
+            const int row = (tk < 0 || tk >= a.V) ? 0 : tk;
+            hv = make_uint4(0u, 0u, 0u, 0u);
+            if (rank < a.r) hv = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(row) * a.r + rank);
+        }
         const bf16x8 hf = __builtin_bit_cast(bf16x8, hv);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -387,10 +419,10 @@ __device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, 
         for (int t = 0; t < NT; ++t) {
             const bool ok = cw + 16 * t + 4 * cg < a.V;
             float* rv = rowv + 16 * t + 4 * cg;
-            rv[0] = ok ? u4[t].x + acc[t][0] : -INFINITY;
-            rv[1] = ok ? u4[t].y + acc[t][1] : -INFINITY;
-            rv[2] = ok ? u4[t].z + acc[t][2] : -INFINITY;
-            rv[3] = ok ? u4[t].w + acc[t][3] : -INFINITY;
+            rv[0] = ok ? in.u4[t].x + acc[t][0] : -INFINITY;
+            rv[1] = ok ? in.u4[t].y + acc[t][1] : -INFINITY;
+            rv[2] = ok ? in.u4[t].z + acc[t][2] : -INFINITY;
+            rv[3] = ok ? in.u4[t].w + acc[t][3] : -INFINITY;
         }
     }
     wait_lgkm0();                                     // the row is in LDS
@@ -450,16 +482,46 @@ void draft_slab_select(SlabArgs a, int k) {
     __shared__ __align__(16) char stg[kKS * S::Stage];
     __shared__ float rowv[S::WC];
     const int b = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     const int tk = k ? a.x_out[static_cast<long long>(b) * a.gamma + k - 1] : a.x0[b];
-    const TilePick sp = slab_pick<false>(a, b, k);
-    const TilePick tp = sp.tile < 0 ? sp : slab_walk(a, b, sp.tile, sp);
+    // the request's tile partials, lane l holding tiles [32 l, 32 l + 32) = slabs [4 l, 4 l + 4)
+    float2 p[kSelRegs];
+    const float4* P4 = reinterpret_cast<const float4*>(a.part + static_cast<long long>(b) * a.ntw);
+#pragma unroll
+    for (int t = 0; t < kSelRegs / 2; ++t) {
+        const int i = lane * kSelRegs + 2 * t;        // ntw is a multiple of 8: slabs are whole
+        float4 v = make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+        if (i < a.ntw) v = P4[i / 2];
+        p[2 * t] = make_float2(v.x, v.y);
+        p[2 * t + 1] = make_float2(v.z, v.w);
+    }
+    const TilePick sp = slab_pick_regs(p, a.u[static_cast<long long>(b) * a.gamma + k]);
+    if (sp.tile < 0) {
+        slab_finish<false>(a, b, k, -1, 0.0f, -INFINITY);
+        return;
+    }
+    // the picked slab's 8 tile partials, from the lane that holds them
+    const int owner = sp.tile / kSlabRegs, jj = sp.tile - owner * kSlabRegs;
+    float2 p8[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        float2 mine = p[w];
+#pragma unroll
+        for (int j = 1; j < kSlabRegs; ++j)
+            if (j == jj) mine = p[8 * j + w];
+        p8[w] = make_float2(wave_bcast(mine.x, owner), wave_bcast(mine.y, owner));
+    }
+    const TilePick tp = walk_pick(sp, p8);
     if (tp.tile < 0) {
         slab_finish<false>(a, b, k, -1, 0.0f, -INFINITY);
         return;
     }
+    // the recompute's U and W1 loads go out before the W2 fragments', so both are in flight
+    RecomputeIn<NT> in;
+    recompute_loads<NT, true>(a, b, k, tk, tp.tile, in);
     bf16x8 w2f[NT][kKS];
     load_w2_frags<NT, kKS, kKS>(w2f, a.W2, a.V, a.r, static_cast<long long>(tp.tile) * S::WC, stg);
-    slab_recompute<NT, false>(a, b, k, tk, tp, w2f, rowv);
+    slab_recompute<NT, false, true>(a, b, k, tk, tp, w2f, in, rowv);
 }
 
 // All positions in one launch (see the file comment). Per position k three flag rows,
@@ -551,7 +613,7 @@ void draft_slab_resident(SlabArgs a) {
         __syncthreads();
         if (gave_up) break;
         for (int b = slab + G * wave; b < a.B; b += G * kSlabWaves) {
-            const TilePick tp = slab_pick<true>(a, b, k);
+            const TilePick tp = slab_pick_coherent(a, b, k);
             if (lane == 0) {
                 unsigned long long* rec = reinterpret_cast<unsigned long long*>(a.picks + b);
                 store_coherent(rec, __builtin_bit_cast(unsigned long long, make_float2(__int_as_float(tp.tile), tp.m)));
@@ -584,8 +646,12 @@ void draft_slab_resident(SlabArgs a) {
                 sp.m = r0.y;
                 sp.lse = r1.x;
                 sp.tprime = r1.y;
-                const TilePick tp = slab_walk(a, bb, slab, sp);
-                if (tp.tile == my_tile) slab_recompute<NT, true>(a, bb, k, stok[bb], tp, w2f, rowv);
+                const TilePick tp = slab_walk(a, bb, sp);
+                if (tp.tile == my_tile) {
+                    RecomputeIn<NT> in;
+                    recompute_loads<NT, false>(a, bb, k, stok[bb], tp.tile, in);
+                    slab_recompute<NT, true, false>(a, bb, k, stok[bb], tp, w2f, in, rowv);
+                }
                 else if (tp.tile < 0 && wave == 0) slab_finish<true>(a, bb, k, -1, 0.0f, -INFINITY);
             }
         }
