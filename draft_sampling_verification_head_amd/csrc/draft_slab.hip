@@ -284,9 +284,10 @@ __device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, const bf16
 //                  that is slabs [4 l, 4 l + 4)), or the slab partials the persistent stream
 //                  merged with the same arithmetic (slab_pick_coherent, device scope).
 //  walk:           the tile of that slab, from its 8 tile partials (walk_pick, walk_slab8).
-//  slab_recompute: that tile's logits rebuilt with the MFMA sequence of the stream, from the
-//                  tile's W2 fragments, the W1 row of x_{k-1} and U_k (recompute_loads); then
-//                  the in-tile rescan. `rowv` holds the tile's logits.
+//  recompute:      that tile's logits rebuilt with the MFMA sequence of the stream, from the
+//                  tile's W2 fragments, the W1 row of x_{k-1} and U_k, then the in-tile
+//                  rescan: slab_recompute (the draw launch, operands from recompute_loads;
+//                  `rowv` holds the tile's logits) or batch_recompute (the persistent form).
 // slab_finish writes the token (COH: at device scope), p(token) and lse.
 constexpr int kSlabRegs = kSelRegs / kSlabWaves;     // slabs per lane (256 slabs at most)
 
@@ -359,9 +360,7 @@ struct RecomputeIn {
     uint4 hv[kKS];
 };
 
-// HV: the W1 row too (else only U, and slab_recompute loads the row chunk by chunk, which
-// needs fewer registers beside a resident W2 slab).
-template <int NT, bool HV>
+template <int NT>
 __device__ __forceinline__ void recompute_loads(const SlabArgs& a, int b, int k, int tk, int tile,
                                                 RecomputeIn<NT>& in) {
     using S = Slab<NT>;
@@ -376,7 +375,6 @@ __device__ __forceinline__ void recompute_loads(const SlabArgs& a, int b, int k,
         in.u4[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (rq == 0 && col < a.V) in.u4[t] = *reinterpret_cast<const float4*>(urow + col);
     }
-    if (!HV) return;
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
         const int rank = 32 * s + 8 * cg;
@@ -385,9 +383,9 @@ __device__ __forceinline__ void recompute_loads(const SlabArgs& a, int b, int k,
     }
 }
 
-template <int NT, bool COH, bool HV>
-__device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, int tk,
-                                               const TilePick& tp, const bf16x8 (&w2f)[NT][kKS],
+template <int NT>
+__device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, const TilePick& tp,
+                                               const bf16x8 (&w2f)[NT][kKS],
                                                const RecomputeIn<NT>& in, float* rowv) {
     using S = Slab<NT>;
     constexpr int CPL = (S::WC + kWave - 1) / kWave;
@@ -400,16 +398,7 @@ __device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, 
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
         // the W1 row of the previous token in every one of the 16 request columns
-        uint4 hv;
-        if constexpr (HV) {
-            hv = in.hv[s];
-        } else {
-            const int rank = 32 * s + 8 * cg;
-            const int row = (tk < 0 || tk >= a.V) ? 0 : tk;
-            hv = make_uint4(0u, 0u, 0u, 0u);
-            if (rank < a.r) hv = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(row) * a.r + rank);
-        }
-        const bf16x8 hf = __builtin_bit_cast(bf16x8, hv);
+        const bf16x8 hf = __builtin_bit_cast(bf16x8, in.hv[s]);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
@@ -442,7 +431,94 @@ __device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, 
     for (int j = 0; j < CPL; ++j)
         if (j == jj) mine = lv[j];
     const float lx = wave_bcast(mine, owner);
-    slab_finish<COH>(a, b, k, tok, __expf(lx - tp.lse), tp.lse);
+    slab_finish<false>(a, b, k, tok, __expf(lx - tp.lse), tp.lse);
+}
+
+// Draws of up to kBatch requests whose chosen tile is this wave's (the persistent form): one
+// MFMA pass rebuilds the tile for all of them, request j in B column j (a column of the
+// result depends only on its own operands, so each is bit-identical to the single-request
+// recompute), and the in-tile rescans follow one request at a time from `rowb`
+// ([kBatch][WC] floats of this wave's LDS). bb, pk: the requests and their picks (uniform);
+// `breq` (kBatch ints of this wave's LDS) hands each lane its column's request.
+constexpr int kBatch = 4;
+
+template <int NT>
+__device__ __forceinline__ void batch_recompute(const SlabArgs& a, int k, int n, const int (&bb)[kBatch],
+                                                const TilePick (&pk)[kBatch], const int* stok,
+                                                const bf16x8 (&w2f)[NT][kKS], float* rowb, int* breq) {
+    using S = Slab<NT>;
+    constexpr int CPL = (S::WC + kWave - 1) / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rq = lane & 15, cg = lane >> 4;
+    const int i = rq < n ? rq : 0;                    // request of this lane's B / C column
+    if (lane < kBatch) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (lane == j) breq[j] = bb[j];
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_wave_barrier();
+    const int rb = breq[i];
+    int tk = stok[rb];
+    if (tk < 0 || tk >= a.V) tk = 0;
+    const long long cw = static_cast<long long>(pk[0].tile) * S::WC;
+    const float* urow = a.U + (static_cast<long long>(rb) * a.gamma + k) * a.V;
+    float4 u4[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const long long col = cw + 16 * t + 4 * cg;
+        u4[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (rq < n && col < a.V) u4[t] = *reinterpret_cast<const float4*>(urow + col);
+    }
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+        // the W1 row of request i's previous token in column i
+        const int rank = 32 * s + 8 * cg;
+        uint4 hv = make_uint4(0u, 0u, 0u, 0u);
+        if (rank < a.r) hv = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(tk) * a.r + rank);
+        const bf16x8 hf = __builtin_bit_cast(bf16x8, hv);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2f[t][s], hf, acc[t], 0, 0, 0);
+    }
+    if (rq < n) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const bool ok = cw + 16 * t + 4 * cg < a.V;
+            float* rv = rowb + rq * S::WC + 16 * t + 4 * cg;
+            rv[0] = ok ? u4[t].x + acc[t][0] : -INFINITY;
+            rv[1] = ok ? u4[t].y + acc[t][1] : -INFINITY;
+            rv[2] = ok ? u4[t].z + acc[t][2] : -INFINITY;
+            rv[3] = ok ? u4[t].w + acc[t][3] : -INFINITY;
+        }
+    }
+    wait_lgkm0();                                     // the rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+    const DrawOut none{nullptr, nullptr, nullptr, false};
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {                // static indices keep bb, pk in registers
+        if (j >= n) break;
+        float lv[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            const int c = lane * CPL + q;
+            lv[q] = (c < S::WC) ? rowb[j * S::WC + c] : -INFINITY;
+        }
+        const TilePick tp = pk[j];
+        const int tok = rescan_values<CPL>(lv, cw + lane * CPL, static_cast<int>(cw), tp.m, tp.lse,
+                                           tp.tprime, none);
+        const int rel = tok - static_cast<int>(cw), owner = rel / CPL, jj = rel - owner * CPL;
+        float mine = 0.0f;
+#pragma unroll
+        for (int q = 0; q < CPL; ++q)
+            if (q == jj) mine = lv[q];
+        const float lx = wave_bcast(mine, owner);
+        slab_finish<true>(a, bb[j], k, tok, __expf(lx - tp.lse), tp.lse);
+    }
+    __builtin_amdgcn_wave_barrier();                  // rowb may be rewritten by the next batch
 }
 
 // One position: stream launch (W2 staged once per launch; the logits stored when LOUT).
@@ -518,10 +594,10 @@ void draft_slab_select(SlabArgs a, int k) {
     }
     // the recompute's U and W1 loads go out before the W2 fragments', so both are in flight
     RecomputeIn<NT> in;
-    recompute_loads<NT, true>(a, b, k, tk, tp.tile, in);
+    recompute_loads<NT>(a, b, k, tk, tp.tile, in);
     bf16x8 w2f[NT][kKS];
     load_w2_frags<NT, kKS, kKS>(w2f, a.W2, a.V, a.r, static_cast<long long>(tp.tile) * S::WC, stg);
-    slab_recompute<NT, false, true>(a, b, k, tk, tp, w2f, in, rowv);
+    slab_recompute<NT>(a, b, k, tp, w2f, in, rowv);
 }
 
 // All positions in one launch (see the file comment). Per position k three flag rows,
@@ -545,10 +621,16 @@ void draft_slab_resident(SlabArgs a) {
     const int my_tile = slab * kSlabWaves + wave;
     const int ng = (a.B + kGrp - 1) / kGrp, npre = ng < 3 ? ng : 3;
     int* stok = reinterpret_cast<int*>(sm + tok_off<NT>());
-    // the draw's LDS lies in the W1 row slots H0 + H1, idle between streams (the U slots then
-    // hold the next position's first groups): each wave's logit row, then the picked slabs
-    float* rowv = reinterpret_cast<float*>(sm + 2 * UB) + wave * S::WC;
-    int* pslab = reinterpret_cast<int*>(sm + 2 * UB + kSlabWaves * S::WC * 4);
+    // the draw's LDS lies in the W1 row slots, idle between streams (the U slots then hold the
+    // next position's first groups): the picked slabs in H0 + H1, each wave's batch of logit
+    // rows in H2 + H3
+    static_assert(kSlabWaves * (kBatch * (S::WC + 1) + kWave) * 4 <= 2 * kHBuf, "draw LDS fits in H2 + H3");
+    int* pslab = reinterpret_cast<int*>(sm + hbuf_off<NT>(0));
+    float* rowb = reinterpret_cast<float*>(sm + hbuf_off<NT>(2)) + wave * kBatch * S::WC;
+    int* breq = reinterpret_cast<int*>(sm + hbuf_off<NT>(2) + kSlabWaves * kBatch * S::WC * 4) +
+                wave * kBatch;
+    int* dlist = reinterpret_cast<int*>(sm + hbuf_off<NT>(2) + kSlabWaves * kBatch * (S::WC + 1) * 4) +
+                 wave * kWave;
     if (tid == 0) gave_up = 0;
 
     bf16x8 w2f[NT][kKS];
@@ -631,14 +713,17 @@ void draft_slab_resident(SlabArgs a) {
             pslab[b] = static_cast<int>(load_coherent(reinterpret_cast<const unsigned long long*>(a.picks + b)));
         __syncthreads();
         if (gave_up) break;
-        for (int base = 0; base < a.B; base += kWave) {
-            const int b = base + lane;
-            unsigned long long hit = __ballot(b < a.B && pslab[min(b, a.B - 1)] == slab);
-            while (hit) {
-                const int f = __ffsll(static_cast<long long>(hit)) - 1;
-                hit &= hit - 1;
-                const int bb = base + f;
-                const unsigned long long* rec = reinterpret_cast<const unsigned long long*>(a.picks + bb);
+        // the requests picked in this slab, compacted into this wave's list (up to 64 at a
+        // time); lane j walks list entry j (its record and the slab's 8 tile partials, all
+        // lanes' loads in flight together), then this wave draws those whose tile it holds,
+        // kBatch at a time
+        auto process = [&](int m) {
+            const bool here = lane < m;
+            const int b = here ? dlist[lane] : 0;
+            TilePick tp;
+            tp.tile = -1;
+            if (here) {
+                const unsigned long long* rec = reinterpret_cast<const unsigned long long*>(a.picks + b);
                 const float2 r0 = __builtin_bit_cast(float2, load_coherent(rec));
                 const float2 r1 = __builtin_bit_cast(float2, load_coherent(rec + 1));
                 TilePick sp;
@@ -646,15 +731,52 @@ void draft_slab_resident(SlabArgs a) {
                 sp.m = r0.y;
                 sp.lse = r1.x;
                 sp.tprime = r1.y;
-                const TilePick tp = slab_walk(a, bb, sp);
-                if (tp.tile == my_tile) {
-                    RecomputeIn<NT> in;
-                    recompute_loads<NT, false>(a, bb, k, stok[bb], tp.tile, in);
-                    slab_recompute<NT, true, false>(a, bb, k, stok[bb], tp, w2f, in, rowv);
+                tp = slab_walk(a, b, sp);
+                if (tp.tile < 0 && wave == 0) {       // no tile with mass: the request is dead
+                    const long long o = static_cast<long long>(b) * a.gamma + k;
+                    store_coherent(a.x_out + o, -1);
+                    if (a.q_out) a.q_out[o] = 0.0f;
+                    if (a.lse_out) a.lse_out[o] = -INFINITY;
                 }
-                else if (tp.tile < 0 && wave == 0) slab_finish<true>(a, bb, k, -1, 0.0f, -INFINITY);
             }
+            unsigned long long hit = __ballot(here && tp.tile == my_tile);
+            while (hit) {
+                int bb[kBatch];
+                TilePick pk[kBatch];
+                int n = 0;
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    bb[j] = dlist[0];
+                    pk[j] = TilePick{my_tile, 0.0f, 0.0f, 0.0f};
+                    if (hit) {
+                        const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                        hit &= hit - 1;
+                        bb[j] = __builtin_amdgcn_readlane(b, f);
+                        pk[j].m = wave_bcast(tp.m, f);
+                        pk[j].lse = wave_bcast(tp.lse, f);
+                        pk[j].tprime = wave_bcast(tp.tprime, f);
+                        n = j + 1;
+                    }
+                }
+                batch_recompute<NT>(a, k, n, bb, pk, stok, w2f, rowb, breq);
+            }
+            __builtin_amdgcn_wave_barrier();          // dlist may be refilled
+        };
+        int m = 0;                                    // wave-uniform length of dlist
+        for (int base = 0; base < a.B; base += kWave) {
+            const int b = base + lane;
+            const unsigned long long hit = __ballot(b < a.B && pslab[min(b, a.B - 1)] == slab);
+            const int cnt = __popcll(hit);
+            if (m + cnt > kWave) {
+                process(m);
+                m = 0;
+            }
+            if ((hit >> lane) & 1ull) dlist[m + __popcll(hit & ((1ull << lane) - 1ull))] = b;
+            m += cnt;
+            wait_lgkm0();
+            __builtin_amdgcn_wave_barrier();
         }
+        if (m > 0) process(m);
         publish(2, k);
         if (k + 1 < a.gamma) prefetch_u(k + 1);
     }
@@ -721,13 +843,12 @@ bool resident_fits(int V) {
 
 }  // namespace
 
-// The persistent form: no logits output, its LDS (with the draw's logit rows and the B picked
-// slabs in H0 + H1) fits, and every slab workgroup can be on the device at once.
+// The persistent form: no logits output, its LDS (with the B picked slabs in H0 + H1) fits,
+// and every slab workgroup can be on the device at once.
 bool draft_slab_one_launch(int B, int V, bool L_out) {
     const int nt = slab_nt(V);
-    const size_t wc = 16 * static_cast<size_t>(nt);
     const bool lds_ok = slab_lds_bytes(nt, B) + kResidentExtra <= static_cast<size_t>(kLdsBytes) &&
-                        kSlabWaves * wc * 4 + 4 * static_cast<size_t>(B) <= 2 * static_cast<size_t>(kHBuf);
+                        4 * static_cast<size_t>(B) <= 2 * static_cast<size_t>(kHBuf);
     return !L_out && lds_ok && resident_fits(V);
 }
 
