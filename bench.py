@@ -49,9 +49,9 @@ MEASURED_TRAFFIC = {
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
-        bytes=4838558615.3,
+        bytes=4837692451.5,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
-        sources={"draft_slab.hip": "b508b9785aa2473032ce206d245020f44852d406b9fcc6110819c74ec1127d9e",
+        sources={"draft_slab.hip": "cc4242efcda807743f57e5afadbaacb0498195381751fe20b0850b9142e4d1b0",
                  "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
