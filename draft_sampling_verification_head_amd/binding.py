@@ -18,13 +18,14 @@ OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 PATH_NAMES = {0: "sweep", 1: "mfma", 2: "resident", 3: "slab"}
 GLOBAL, EARLY_STOP = 0, 1
+DRAFT_PER_POSITION = 1
 STS_NLL, STS_ECE = 0, 1
 
 # every symbol include/dspark.h declares
 EXPORTS = (
     "dspark_status_string", "dspark_last_error", "dspark_version",
     "dspark_markov_draft_path", "dspark_markov_draft_one_launch", "dspark_markov_draft_workspace_bytes",
-    "dspark_markov_draft",
+    "dspark_markov_draft", "dspark_markov_draft_ex",
     "dspark_verify_workspace_bytes", "dspark_verify",
     "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
     "dspark_verify_markov_workspace_bytes", "dspark_verify_markov",
@@ -46,6 +47,7 @@ _SIGS = {
     "dspark_markov_draft_one_launch": (_I, [_I, _I, _I, _I, _P, _P, _I]),
     "dspark_markov_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_markov_draft_ex": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _I]),
     "dspark_verify_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_verify": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_verify_tv_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -164,9 +166,10 @@ def markov_draft_one_launch(B: int, W1, W2, want_logits: bool = False) -> bool:
 
 
 def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=False,
-                 out=None, stream=None):
-    """dspark_markov_draft. U [B][gamma][V] fp32, W1 [V][r], W2 [r][V] (fp32 or bf16),
-    x0 [B] int32, u [B][gamma] fp32. Returns dict x, q, lse, L (None when not asked)."""
+                 per_position=False, out=None, stream=None):
+    """dspark_markov_draft (dspark_markov_draft_ex with DSPARK_DRAFT_PER_POSITION when
+    per_position). U [B][gamma][V] fp32, W1 [V][r], W2 [r][V] (fp32 or bf16), x0 [B] int32,
+    u [B][gamma] fp32. Returns dict x, q, lse, L (None when not asked)."""
     torch = _torch()
     lib = load()
     B, G, V = U.shape
@@ -187,9 +190,9 @@ def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=Fa
     L = o.get("L") if o.get("L") is not None else (torch.empty((B, G, V), dtype=torch.float32, device=dev) if want_logits else None)
     nbytes = lib.dspark_markov_draft_workspace_bytes(B, V, r, G)
     ws = workspace(nbytes, dev, "draft")
-    st = lib.dspark_markov_draft(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(x0), _ptr(u),
-                                 _ptr(x), _ptr(q), _ptr(lse), _ptr(L), _ptr(ws), ws.numel(),
-                                 _stream(stream))
+    st = lib.dspark_markov_draft_ex(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(x0), _ptr(u),
+                                    _ptr(x), _ptr(q), _ptr(lse), _ptr(L), _ptr(ws), ws.numel(),
+                                    _stream(stream), DRAFT_PER_POSITION if per_position else 0)
     _check(st, "dspark_markov_draft")
     return dict(x=x, q=q, lse=lse, L=L)
 

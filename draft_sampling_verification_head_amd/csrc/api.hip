@@ -112,10 +112,12 @@ size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma) {
            align_up(draft_slot_bytes(V, gamma));
 }
 
-int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const void* W1,
-                        const void* W2, int w_dtype, const int32_t* x0, const float* u,
-                        int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, void* ws,
-                        size_t ws_bytes, void* stream) {
+int dspark_markov_draft_ex(int B, int V, int r, int gamma, const float* U, const void* W1,
+                           const void* W2, int w_dtype, const int32_t* x0, const float* u,
+                           int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, void* ws,
+                           size_t ws_bytes, void* stream, int options) {
+    if (options & ~DSPARK_DRAFT_PER_POSITION)
+        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: unknown option bits 0x%x", options);
     if (B < 1 || V < 1 || gamma < 1 || r < 1)
         return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: B=%d V=%d r=%d gamma=%d must be >= 1",
                     B, V, r, gamma);
@@ -143,10 +145,19 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
         dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
     dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
     dc.L_out = Ld_out != nullptr;
+    dc.per_position = (options & DSPARK_DRAFT_PER_POSITION) != 0;
     dc.slots = c.take<float2>(draft_slot_bytes(V, gamma) / sizeof(float2));
     const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "markov_draft");
     return ok();
+}
+
+int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const void* W1,
+                        const void* W2, int w_dtype, const int32_t* x0, const float* u,
+                        int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, void* ws,
+                        size_t ws_bytes, void* stream) {
+    return dspark_markov_draft_ex(B, V, r, gamma, U, W1, W2, w_dtype, x0, u, x_out, q_out, lse_out,
+                                  Ld_out, ws, ws_bytes, stream, 0);
 }
 
 // ----------------------------------------------------------------------------- verify / TV

@@ -267,7 +267,7 @@ int draft_part_tiles(int V) {
 
 hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; };
-    if (draft_resident_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2))
+    if (!c.per_position && draft_resident_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2))
         return launch_draft_resident(c, st);
     if (draft_slab_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2) && al16(c.U) && (!c.L_out || al16(c.L[0])))
         return launch_draft_slab(c, st);

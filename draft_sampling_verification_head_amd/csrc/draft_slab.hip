@@ -22,12 +22,13 @@
 // result depends only on that column's operands, so the recomputed logits are bit-identical
 // to the stream's and the logits never need to be written to memory.
 //
-// Two launch shapes, which draw the same tokens bit for bit:
-//   - per position, a stream launch (draft_slab_step, which can also store the logits) and a
-//     draw launch (draft_slab_select, one wave per request, which merges the slab partials
-//     from the tile partials itself and loads the chosen tile's W2 fragments);
-//   - one persistent launch for all positions (draft_slab_resident) when the logits are not
-//     wanted and every slab workgroup fits on the device at once. W2 is loaded once per call;
+// Two launch shapes, which draw the same tokens bit for bit and store the same logits:
+//   - per position, a stream launch (draft_slab_step) and a draw launch (draft_slab_select,
+//     one wave per request, which merges the slab partials from the tile partials itself and
+//     loads the chosen tile's W2 fragments);
+//   - one persistent launch for all positions (draft_slab_resident) when every slab
+//     workgroup fits on the device at once and the caller did not ask for per-position
+//     launches. W2 is loaded once per call;
 //     each position runs in three phases separated by flag barriers (as in the single-request
 //     resident draft): the stream, which also merges each group's slab partials through LDS
 //     and publishes them; the slab picks, each workgroup for its share of the requests; the
@@ -57,7 +58,8 @@ struct SlabArgs {
     int32_t* x_out;           // [B][gamma]
     float* q_out;
     float* lse_out;
-    float* L;                 // step: logits rows of the position, L + b * L_bstride
+    float* L;                 // step: logits rows of the position, L + b * L_bstride;
+                              // resident: those of position 0, position k at L + k * V
     long long L_bstride;
     float2* part;             // [B][ntw] (max, sum exp) per request and wave tile
     float2* spart;            // resident: [B][G] the same per request and slab (8 wave tiles)
@@ -155,7 +157,7 @@ __device__ __forceinline__ void issue_group(const SlabArgs& a, int k, int g, cha
 // stores between them only make the wait longer): 2 (NT + 1) in the steady state, fewer in
 // the first groups and at the tail (after_group).
 template <int NT, bool LOUT, bool PRE>
-__device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, const bf16x8 (&w2f)[NT][kKS],
+__device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, float* L, const bf16x8 (&w2f)[NT][kKS],
                                             char* sm, const int* stok, int issued) {
     using S = Slab<NT>;
     constexpr int NL = NT + 1;                        // direct loads per wave and group
@@ -191,7 +193,7 @@ __device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, const bf16
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const long long col = cw + 16 * t + 4 * cg;
-                if (col < a.V) *reinterpret_cast<float4*>(a.L + pend_b * a.L_bstride + col) = pend_l[LOUT ? t : 0];
+                if (col < a.V) *reinterpret_cast<float4*>(L + pend_b * a.L_bstride + col) = pend_l[LOUT ? t : 0];
             }
         }
         if (lane < kGrp) a.part[static_cast<long long>(pend_b) * a.ntw + slab * kSlabWaves + wave] = pend_part;
@@ -546,7 +548,7 @@ void draft_slab_step(SlabArgs a, int k) {
     load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
     wait_lgkm0();
     __syncthreads();                                  // every wave is done with the staging area
-    slab_stream<NT, LOUT, false>(a, k, w2f, sm, stok, ng < 2 ? ng : 2);
+    slab_stream<NT, LOUT, false>(a, k, a.L, w2f, sm, stok, ng < 2 ? ng : 2);
 }
 
 // One position: draw launch, one workgroup (one wave) per request; every W2 load of the
@@ -606,7 +608,7 @@ void draft_slab_select(SlabArgs a, int k) {
 // picks the slab of its share of the requests (b = g, g + G, ...); the workgroup of a
 // picked slab walks its 8 tile partials, and the wave that holds the chosen tile in
 // registers recomputes that tile's logits and draws the token.
-template <int NT>
+template <int NT, bool LOUT>
 __global__ __launch_bounds__(kSlabThreads)
 void draft_slab_resident(SlabArgs a) {
     using S = Slab<NT>;
@@ -671,7 +673,8 @@ void draft_slab_resident(SlabArgs a) {
             stok[b] = (t >= 0 && t < a.V) ? t : -1;
         }
         __syncthreads();
-        slab_stream<NT, false, true>(a, k, w2f, sm, stok, 0);
+        slab_stream<NT, LOUT, true>(a, k, LOUT ? a.L + static_cast<long long>(k) * a.V : nullptr, w2f, sm,
+                                    stok, 0);
         // slab partials of every request for this slab, merged from the tile partials this
         // workgroup's waves stored (visible within the workgroup after the barrier)
         __builtin_amdgcn_s_waitcnt(0);
@@ -804,23 +807,36 @@ constexpr size_t kResidentExtra = 16;     // the resident launch's give-up word,
 
 struct SlabFit {
     int cus = -1;
-    int occupancy[kMaxNT + 1] = {-1, -1, -1, -1, -1, -1};
+    int occupancy[2][kMaxNT + 1] = {{-1, -1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1, -1}};
 };
 
-template <int NT>
+template <int NT, bool LOUT>
 int resident_occupancy(size_t smem) {
     int occ = 0;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_slab_resident<NT>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&draft_slab_resident<NT, LOUT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)) != hipSuccess)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, draft_slab_resident<NT>, kSlabThreads, smem) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, draft_slab_resident<NT, LOUT>, kSlabThreads, smem) !=
+        hipSuccess)
         return 0;
     return occ;
 }
 
-// Whether every slab workgroup of the resident launch can be on the device at once (queried
-// with the largest LDS the path uses, so smaller batches fit as well).
-bool resident_fits(int V) {
+template <bool LOUT>
+int resident_occupancy_nt(int nt, size_t smem) {
+    switch (nt) {
+        case 1: return resident_occupancy<1, LOUT>(smem);
+        case 2: return resident_occupancy<2, LOUT>(smem);
+        case 3: return resident_occupancy<3, LOUT>(smem);
+        case 4: return resident_occupancy<4, LOUT>(smem);
+        default: return resident_occupancy<5, LOUT>(smem);
+    }
+}
+
+// Whether every slab workgroup of the resident launch (with or without the logits output)
+// can be on the device at once (queried with the largest LDS the path uses, so smaller
+// batches fit as well).
+bool resident_fits(int V, bool L_out) {
     thread_local SlabFit cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
@@ -828,28 +844,23 @@ bool resident_fits(int V) {
     if (f.cus < 0 && hipDeviceGetAttribute(&f.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return false;
     const int nt = slab_nt(V);
-    if (f.occupancy[nt] < 0) {
+    int& occ = f.occupancy[L_out ? 1 : 0][nt];
+    if (occ < 0) {
         const size_t smem = static_cast<size_t>(kLdsBytes);
-        switch (nt) {
-            case 1: f.occupancy[nt] = resident_occupancy<1>(smem); break;
-            case 2: f.occupancy[nt] = resident_occupancy<2>(smem); break;
-            case 3: f.occupancy[nt] = resident_occupancy<3>(smem); break;
-            case 4: f.occupancy[nt] = resident_occupancy<4>(smem); break;
-            default: f.occupancy[nt] = resident_occupancy<5>(smem); break;
-        }
+        occ = L_out ? resident_occupancy_nt<true>(nt, smem) : resident_occupancy_nt<false>(nt, smem);
     }
-    return f.cus > 0 && f.occupancy[nt] >= 1 && slab_count(V) <= f.cus * f.occupancy[nt];
+    return f.cus > 0 && occ >= 1 && slab_count(V) <= f.cus * occ;
 }
 
 }  // namespace
 
-// The persistent form: no logits output, its LDS (with the B picked slabs in H0 + H1) fits,
-// and every slab workgroup can be on the device at once.
+// The persistent form: its LDS (with the B picked slabs in H0 + H1) fits, and every slab
+// workgroup can be on the device at once. It writes the logits too when they are wanted.
 bool draft_slab_one_launch(int B, int V, bool L_out) {
     const int nt = slab_nt(V);
     const bool lds_ok = slab_lds_bytes(nt, B) + kResidentExtra <= static_cast<size_t>(kLdsBytes) &&
                         4 * static_cast<size_t>(B) <= 2 * static_cast<size_t>(kHBuf);
-    return !L_out && lds_ok && resident_fits(V);
+    return lds_ok && resident_fits(V, L_out);
 }
 
 namespace {
@@ -873,13 +884,20 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
     a.spart = c.part[1] + 2 * static_cast<long long>(c.B);
     const size_t smem = slab_lds_bytes(NT, c.B);
     const dim3 grid(static_cast<unsigned>(a.G));
-    if (draft_slab_one_launch(c.B, c.V, c.L_out)) {
+    if (!c.per_position && draft_slab_one_launch(c.B, c.V, c.L_out)) {
         const int n = 3 * c.gamma * a.G;
         hipLaunchKernelGGL(clear_flags, dim3((n + 255) / 256), dim3(256), 0, st, a.flags, n);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         a.part = c.part[0];
-        hipLaunchKernelGGL(draft_slab_resident<NT>, grid, dim3(kSlabThreads), smem + kResidentExtra, st, a);
+        if (c.L_out) {
+            a.L = c.L[0];                             // the caller's [B][gamma][V]: L[k] = L[0] + k V
+            hipLaunchKernelGGL((draft_slab_resident<NT, true>), grid, dim3(kSlabThreads), smem + kResidentExtra,
+                               st, a);
+        } else {
+            hipLaunchKernelGGL((draft_slab_resident<NT, false>), grid, dim3(kSlabThreads), smem + kResidentExtra,
+                               st, a);
+        }
         return hipGetLastError();
     }
     for (int k = 0; k < c.gamma; ++k) {

@@ -21,6 +21,7 @@ struct DraftCall {
     float* L[64];             // logits rows of step k: L[k] + b * L_bstride
     long long L_bstride;
     bool L_out;               // L[k] is the caller's output (else workspace the path may skip)
+    bool per_position = false;   // no persistent launch: each position is its own launches
     float2* part[2];          // tile partials [B][draft_part_tiles(V)] of even / odd steps
     float2* slots;            // max(draft_resident_slot_bytes, draft_slab_flag_bytes) of workspace
 };

@@ -94,13 +94,14 @@ int dspark_version(void);
  *                         bf16, r <= 256 and r % 8 == 0, V % 8 == 0, V <= 163840, B <= 2048
  *                         at V > 131072 and B <= 8192 at V > 98304, 16-byte aligned W1, W2,
  *                         U and Ld_out). Logits reach memory only when Ld_out is given.
- *                         Without Ld_out, and where the batch and every slab workgroup fit
+ *                         Where the batch and every slab workgroup fit
  *                         (dspark_markov_draft_one_launch), all positions run in one launch
  *                         that holds W2 in registers throughout and separates positions by
  *                         flag barriers, with the same give-up behaviour and the same
  *                         restriction on overlapping draft calls as DSPARK_PATH_RESIDENT;
- *                         otherwise each position is one stream launch and one draw launch.
- *                         Both forms draw the same tokens bit for bit.
+ *                         otherwise, or with DSPARK_DRAFT_PER_POSITION, each position is one
+ *                         stream launch and one draw launch. Both forms draw the same tokens
+ *                         and store the same logits bit for bit.
  *   DSPARK_PATH_MFMA      one bf16 MFMA projection per position (B > 8, bf16 factors, where
  *                         the slab path does not apply).
  *   DSPARK_PATH_RESIDENT  one launch for all positions, W2 held in registers across the GPU
@@ -128,6 +129,25 @@ int dspark_markov_draft(int B, int V, int r, int gamma,
                         const int32_t* x0, const float* u,
                         int32_t* x_out, float* q_out, float* lse_out, float* Ld_out,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* Option bits of dspark_markov_draft_ex.
+ *   DSPARK_DRAFT_PER_POSITION  never the one-launch forms: every position is its own
+ *                              launches (the slab path's stream + draw launches; a single
+ *                              bf16 request takes DSPARK_PATH_SWEEP). The one-launch forms
+ *                              hold every compute unit for the whole call; per-position
+ *                              launches let kernels on other streams run between positions
+ *                              and carry no restriction on overlapping draft calls. The
+ *                              results are those of the one-launch form bit for bit on the
+ *                              slab path, and equal to within fp32 rounding order otherwise. */
+enum { DSPARK_DRAFT_PER_POSITION = 1 };
+
+/* dspark_markov_draft with option bits (0 = dspark_markov_draft); unknown bits are
+ * DSPARK_ERR_INVALID_ARG. Arguments, outputs and errors as dspark_markov_draft. */
+int dspark_markov_draft_ex(int B, int V, int r, int gamma,
+                           const float* U, const void* W1, const void* W2, int w_dtype,
+                           const int32_t* x0, const float* u,
+                           int32_t* x_out, float* q_out, float* lse_out, float* Ld_out,
+                           void* ws, size_t ws_bytes, void* stream, int options);
 
 /*
  * Lossless rejection-sampling verification.

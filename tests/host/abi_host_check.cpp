@@ -62,6 +62,11 @@ int main() {
                                      nullptr, nullptr, fake, 1 << 30, nullptr), "draft U null");
     expect_error(dspark_markov_draft(2, 8, 4, 2, ff, fake, fake, 0, fi, ff, wi, nullptr, nullptr,
                                      nullptr, fake, 8, nullptr), "draft workspace");
+    expect_error(dspark_markov_draft_ex(2, 8, 4, 2, ff, fake, fake, 0, fi, ff, wi, nullptr, nullptr,
+                                        nullptr, fake, 1 << 30, nullptr, 6), "draft option bits");
+    expect_error(dspark_markov_draft_ex(2, 8, 4, 2, ff, fake, fake, 0, fi, ff, wi, nullptr, nullptr,
+                                        nullptr, fake, 8, nullptr, DSPARK_DRAFT_PER_POSITION),
+                 "draft_ex workspace");
     // verify, TV, fused
     expect_error(dspark_verify(0, 8, 2, ff, ff, 6, nullptr, nullptr, fi, nullptr, ff, ff, wi, wi,
                                nullptr, nullptr, fake, 1 << 30, nullptr), "verify B=0");

@@ -79,7 +79,8 @@ def test_draft_path_host_rules(lib):
     assert lib.dspark_markov_draft_path(1, 151936, 256, 0, FAKE, FAKE) == 0      # fp32, B = 1
     assert lib.dspark_markov_draft_path(1, 151936, 260, 1, FAKE, FAKE) == 0      # r > 256
     assert lib.dspark_markov_draft_path(1, 151937, 256, 1, FAKE, FAKE) == 0      # V % 8 != 0
-    # one launch for all positions: never with a logits output or off the resident / slab paths
+    # one launch for all positions: only on the resident / slab paths, and only where the
+    # device holds every workgroup at once (no device here)
     f = lib.dspark_markov_draft_one_launch
     f.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int]
     assert f(64, 151936, 256, 1, FAKE, FAKE, 1) == 0
@@ -109,6 +110,21 @@ def _draft(lib, B=2, V=64, r=4, G=3, wdt=0, ws=FAKE, wsb=1 << 30, U=FAKE, x_out=
 ])
 def test_draft_rejects(lib, kw, status):
     assert _draft(lib, **kw) == status
+    assert lib.dspark_last_error()
+
+
+@cpu_only
+@pytest.mark.parametrize("options,status", [
+    (2, binding.ERR_INVALID_ARG),                     # unknown option bit
+    (-1, binding.ERR_INVALID_ARG),
+    (binding.DRAFT_PER_POSITION, binding.ERR_WORKSPACE),   # a known bit: validation goes on
+])
+def test_draft_ex_options(lib, options, status):
+    f = lib.dspark_markov_draft_ex
+    f.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 7 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int])
+    assert f(2, 64, 4, 3, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None, None, FAKE, 100, None,
+             options) == status
     assert lib.dspark_last_error()
 
 

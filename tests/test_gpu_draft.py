@@ -12,9 +12,9 @@ from parity import check_draft, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def run_draft(d, want_logits=True):
+def run_draft(d, want_logits=True, per_position=False):
     out = dspark.markov_draft(dev(d["U"]), dev(d["W1"]), dev(d["W2"]), dev(d["x0"]),
-                              dev(d["u"]), want_logits=want_logits)
+                              dev(d["u"]), want_logits=want_logits, per_position=per_position)
     torch.cuda.synchronize()
     return {k: (host(v) if v is not None else None) for k, v in out.items()}
 
@@ -75,22 +75,25 @@ def test_batched_mfma_shapes(gpu, B, V, r, G):
     (40, 151936, 256, 2),   # five, the full vocabulary
 ])
 def test_batched_slab_shapes(gpu, B, V, r, G):
-    """bf16 batches: W2 slabs in registers, draws that recompute the chosen tile. With the
-    logits output each position is a stream and a draw launch; without it one persistent
-    launch draws every position, and its tokens, probabilities and normalisers are the same
-    bit for bit."""
+    """bf16 batches: W2 slabs in registers, draws that recompute the chosen tile. One
+    persistent launch draws every position, with or without the logits output; the
+    per-position form (a stream and a draw launch per position) gives the same tokens,
+    probabilities, normalisers and logits bit for bit."""
     c = synth.custom(955 + B, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
     W1, W2 = dev(d["W1"]), dev(d["W2"])
     assert dspark.markov_draft_path(B, W1, W2) == "slab"
     assert dspark.markov_draft_one_launch(B, W1, W2)
-    assert not dspark.markov_draft_one_launch(B, W1, W2, want_logits=True)
+    assert dspark.markov_draft_one_launch(B, W1, W2, want_logits=True)
     g = run_draft(d)
     reqs = sorted({0, 1, B // 2, B - 2, B - 1})
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
                       reqs, gL=g["L"])
     assert rep.ties <= 1
     assert np.all((g["x"] >= 0) & (g["x"] < V))
+    per = run_draft(d, per_position=True)
+    for k in ("x", "q", "lse", "L"):
+        assert np.array_equal(g[k].view(np.uint8), per[k].view(np.uint8)), k
     one = run_draft(d, want_logits=False)
     for k in ("x", "q", "lse"):
         assert np.array_equal(g[k].view(np.uint8), one[k].view(np.uint8)), k
@@ -113,19 +116,29 @@ def test_single_request_bf16_shapes(gpu, V, r, G):
                       g["lse"], [0], gL=g["L"])
     assert rep.ties <= 1
     assert rep.compared + rep.ties + rep.skipped == G
+    # per-position launches instead (the vocabulary sweep): the same function to within fp32
+    # rounding order, so checked against the oracle rather than bit for bit
+    p = run_draft(d, per_position=True)
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", p["x"], p["q"],
+                      p["lse"], [0], gL=p["L"])
+    assert rep.ties <= 1
 
 
 def test_slab_logits_output_is_optional(gpu):
     """The slab path's draws do not read the logits: the same tokens, probabilities and
-    normalisers with and without the logits output (per-position launches, then the
-    persistent launch), and the stored logits match the oracle's."""
+    normalisers with and without the logits output, in both launch forms, and the stored
+    logits match the oracle's."""
     c = synth.custom(961, B=24, V=30000, r=256, gamma=4, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
     assert dspark.markov_draft_one_launch(c.B, dev(d["W1"]), dev(d["W2"]))
     a = run_draft(d, want_logits=True)
     b = run_draft(d, want_logits=False)
+    pa = run_draft(d, want_logits=True, per_position=True)
+    pb = run_draft(d, want_logits=False, per_position=True)
     for k in ("x", "q", "lse"):
-        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+        for o in (b, pa, pb):
+            assert np.array_equal(a[k].view(np.uint8), o[k].view(np.uint8)), k
+    assert np.array_equal(a["L"].view(np.uint8), pa["L"].view(np.uint8))
     check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", a["x"], a["q"], a["lse"],
                 [0, 11, 23], gL=a["L"])
 
