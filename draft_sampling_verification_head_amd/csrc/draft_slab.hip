@@ -646,7 +646,8 @@ void draft_slab_resident(SlabArgs a) {
     prefetch_u(0);
 
     auto flag_row = [&](int f, int k) { return a.flags + (static_cast<long long>(f) * a.gamma + k) * G; };
-    // every wave waits until all G flags of `row` are set; false after the spin bound
+    // wave 0 waits until all G flags of `row` are set (false after the spin bound); the other
+    // waves wait at the workgroup barrier that follows, so each workgroup polls with one wave
     auto wait_flags = [&](const unsigned long long* row) {
         for (unsigned n = 0;; ++n) {
             bool missing = false;
@@ -665,7 +666,7 @@ void draft_slab_resident(SlabArgs a) {
     int k = 0;
     for (; k < a.gamma; ++k) {
         // tokens x_{k-1} of every request: x0, or the previous position's draws
-        if (k > 0 && !wait_flags(flag_row(2, k - 1)) && lane == 0) gave_up = 1;
+        if (k > 0 && wave == 0 && !wait_flags(flag_row(2, k - 1)) && lane == 0) gave_up = 1;
         __syncthreads();                              // also: every wave is done with the draw LDS
         if (gave_up) break;
         for (int b = tid; b < a.B; b += kSlabThreads) {
@@ -694,7 +695,7 @@ void draft_slab_resident(SlabArgs a) {
         publish(0, k);
 
         // slab picks of this workgroup's requests, one wave per request
-        if (!wait_flags(flag_row(0, k)) && lane == 0) gave_up = 1;
+        if (wave == 0 && !wait_flags(flag_row(0, k)) && lane == 0) gave_up = 1;
         __syncthreads();
         if (gave_up) break;
         for (int b = slab + G * wave; b < a.B; b += G * kSlabWaves) {
@@ -711,11 +712,12 @@ void draft_slab_resident(SlabArgs a) {
         // requests picked in this slab: every wave walks the slab's 8 tile partials (written
         // by this workgroup), and the wave holding the chosen tile in registers draws. The
         // picked slabs of all requests are staged in LDS after the waves' logit rows.
-        if (!wait_flags(flag_row(1, k)) && lane == 0) gave_up = 1;
+        if (wave == 0 && !wait_flags(flag_row(1, k)) && lane == 0) gave_up = 1;
+        __syncthreads();
+        if (gave_up) break;
         for (int b = tid; b < a.B; b += kSlabThreads)
             pslab[b] = static_cast<int>(load_coherent(reinterpret_cast<const unsigned long long*>(a.picks + b)));
         __syncthreads();
-        if (gave_up) break;
         // the requests picked in this slab, compacted into this wave's list (up to 64 at a
         // time); lane j walks list entry j (its record and the slab's 8 tile partials, all
         // lanes' loads in flight together), then this wave draws those whose tile it holds,
