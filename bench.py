@@ -48,10 +48,17 @@ MEASURED_TRAFFIC = {
         sources={"draft_resident.hip": "bca35370d74d6723c8eca0d01c55009e66855f4e33f82bef3537403917327cf1",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
+    ("batched", "draft_slab_resident"): dict(
+        bytes=1515540830.5,
+        profile="profiles/draft_slab_resident_batched_B64_V151936.md",
+        sources={"draft_slab.hip": "4441872dddfba5e8ee7a963fd03058f533077cece76c65a3229092fc67f8dc5c",
+                 "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
+                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
-        bytes=4837692451.5,
+        bytes=4836163799.9,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
-        sources={"draft_slab.hip": "cc4242efcda807743f57e5afadbaacb0498195381751fe20b0850b9142e4d1b0",
+        sources={"draft_slab.hip": "4441872dddfba5e8ee7a963fd03058f533077cece76c65a3229092fc67f8dc5c",
                  "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
