@@ -65,16 +65,21 @@ MEASURED_TRAFFIC = {
 }
 
 
-def measured_traffic(workload: str, kernel: str):
-    """Counter-measured bytes per dispatch, or None if absent or the sources have changed."""
+def sources_unchanged(sources: dict) -> bool:
+    """Whether every kernel source still has the sha256 a counter figure was taken with."""
     import hashlib
-    rec = MEASURED_TRAFFIC.get((workload, kernel))
-    if rec is None:
-        return None
-    for name, digest in rec["sources"].items():
+    for name, digest in sources.items():
         with open(os.path.join(CSRC, name), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != digest:
-                return None
+                return False
+    return True
+
+
+def measured_traffic(workload: str, kernel: str):
+    """Counter-measured bytes per dispatch, or None if absent or the sources have changed."""
+    rec = MEASURED_TRAFFIC.get((workload, kernel))
+    if rec is None or not sources_unchanged(rec["sources"]):
+        return None
     return rec["bytes"]
 
 
@@ -83,7 +88,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["sts", "pipeline"], default="single")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["sts", "pipeline", "mfma"], default="single")
     ap.add_argument("--no-flush", action="store_true", help="keep the Infinity Cache warm")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -380,6 +385,92 @@ def bench_pipeline(args, torch, dspark, device):
     print(json.dumps(res), flush=True)
 
 
+# MFMA busy share of the persistent slab draft per batch size, from one rocprofv3 --pmc run of
+# `--workload mfma` (SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (GRBM_GUI_ACTIVE x
+# 1024 SIMDs), the MfmaUtil expression of rocprofiler's counter definitions). A figure holds
+# only for the kernel sources it was measured with.
+MEASURED_MFMA_BUSY = dict(
+    util={64: 6.94, 256: 13.21, 512: 15.33, 1024: 16.73},
+    profile="profiles/draft_slab_resident_mfma_sweep_V151936.md",
+    sources={"draft_slab.hip": "4441872dddfba5e8ee7a963fd03058f533077cece76c65a3229092fc67f8dc5c",
+             "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
+             "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
+             "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"})
+
+
+def bench_mfma(args, torch, dspark, device):
+    """Where the MFMA rate of the batched draft rises with the batch: the persistent slab
+    draft (W2 held in registers, no logits output) at V = 151936, r = 256, gamma = 16 for
+    B = 64, 256, 512, 1024, the Infinity Cache flushed before each call. Per call the draft
+    moves W2 once and gamma base-logit rows per request, so its arithmetic intensity is about
+    2 r / 4 = 128 flop per byte however large B is, and the attainable rate is
+    min(bf16 peak, intensity x 8 TB/s). Factors as the batched workload; U ~ N(0, 3^2),
+    tokens and uniforms drawn on the device from a fixed seed."""
+    import synth
+    c = synth.config(3)
+    w1, w2 = synth.factors(c)
+    W1, W2 = to_dev(w1, torch, device), to_dev(w2, torch, device)
+    V, r, G = c.V, c.r, c.gamma
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=device)
+    rows = []
+    for B in (64, 256, 512, 1024):
+        gen = torch.Generator(device=device).manual_seed(1000 + B)
+        U = torch.randn((B, G, V), generator=gen, device=device) * 3.0
+        x0 = torch.randint(0, V, (B,), generator=gen, device=device, dtype=torch.int32)
+        u = torch.rand((B, G), generator=gen, device=device).clamp_(max=1 - 2 ** -24)
+        out = dict(x=torch.empty((B, G), dtype=torch.int32, device=device),
+                   q=torch.empty((B, G), dtype=torch.float32, device=device),
+                   lse=torch.empty((B, G), dtype=torch.float32, device=device))
+        one = dspark.markov_draft_one_launch(B, W1, W2)
+
+        def call():
+            dspark.markov_draft(U, W1, W2, x0, u, out=out)
+
+        for _ in range(max(1, args.warmup)):
+            call()
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            flush.sum()
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        assert bool(((out["x"] >= 0) & (out["x"] < V)).all())
+        flops = 2.0 * B * r * V * G
+        moved = r * V * 2 + G * (B * V * 4 + B * r * 2 + B * 12)     # W2 once, then per position
+        tf = flops / (us * 1e-6) / 1e12
+        attain = min(MFMA_BF16_PEAK_TFLOPS, flops / moved * HBM_PEAK_GBS / 1e3)
+        row = dict(B=B, one_launch=bool(one), draft_us=us, draft_tok_s=B * G / (us * 1e-6),
+                   tflops=tf, frac_peak=tf / MFMA_BF16_PEAK_TFLOPS, flop_per_byte=flops / moved,
+                   attainable_tflops=attain, frac_attainable=tf / attain,
+                   hbm_gbs=moved / (us * 1e-6) / 1e9)
+        if MEASURED_MFMA_BUSY and sources_unchanged(MEASURED_MFMA_BUSY["sources"]):
+            row["mfma_busy_pct_counters"] = MEASURED_MFMA_BUSY["util"].get(B)
+        rows.append(row)
+        del U, x0, u, out, g
+        torch.cuda.empty_cache()
+    big = rows[-1]
+    res = dict(metric="batched Markov draft MFMA rate vs batch size (bf16 TFLOP/s)",
+               value=big["tflops"], unit="TFLOP/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=big["draft_us"] / 1e3, higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+               config=dict(workload="MFMA sweep: persistent slab draft, no logits output",
+                           V=V, r=r, gamma=G, B=[x["B"] for x in rows], mall_flush=True,
+                           graph_replay=True),
+               sweep=rows)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -394,6 +485,8 @@ def main():
         return bench_sts(args, torch, dspark, device)
     if args.workload == "pipeline":
         return bench_pipeline(args, torch, dspark, device)
+    if args.workload == "mfma":
+        return bench_mfma(args, torch, dspark, device)
     cfg = WORKLOADS[args.workload]
     verify_only = args.workload == "verify"
     c, inp = build_inputs(cfg)
