@@ -131,8 +131,28 @@ def draft_bytes_per_position(c, logits_written: bool = True) -> float:
             (c.B * c.V * 4 if logits_written else 0))
 
 
-def cpu_baseline(c, inp, seconds: float, verify_only: bool = False) -> dict:
-    """The fp64 oracle on the same step, single-threaded, repeated for about `seconds`."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def all_core_threads() -> int:
+    """Threads for the all-cores oracle leg: the cores this process may run on, capped by
+    OMP_NUM_THREADS where that is set (the CPU share of the machine)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap))) if cap and cap.isdigit() else n
+
+
+def cpu_baseline(c, inp, seconds: float, verify_only: bool = False, threads: int = 1) -> dict:
+    """The fp64 oracle on the same step, with `threads` BLAS / OpenMP threads, repeated for
+    about `seconds`."""
     from threadpoolctl import threadpool_limits
     import oracle
 
@@ -141,7 +161,7 @@ def cpu_baseline(c, inp, seconds: float, verify_only: bool = False) -> dict:
     tokens = 0
     t0 = time.perf_counter()
     steps = 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while True:
             Lt = inp["Lt"].reshape(c.B, G + 1, V)[reqs].reshape(-1, V)
             if verify_only:
@@ -163,10 +183,11 @@ def cpu_baseline(c, inp, seconds: float, verify_only: bool = False) -> dict:
             el = time.perf_counter() - t0
             if el >= seconds or el * (steps + 1) / steps > 30.0:
                 break
-    return dict(value=tokens / el, unit="tokens/s", cores=1, kind="oracle",
+    return dict(value=tokens / el, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{steps} oracle steps over requests {reqs} of the same workload "
                        f"({'verify + TV' if verify_only else 'draft + schedule + verify + TV'}, "
-                       f"fp64, one thread), {el:.1f} s")
+                       f"fp64, {threads} thread{'s' if threads > 1 else ''}), {el:.1f} s",
+                cpu=cpu_model())
 
 
 def bench_sts(args, torch, dspark, device):
@@ -382,6 +403,8 @@ def bench_pipeline(args, torch, dspark, device):
     )
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_seconds, False)
+        res["cpu_baseline_all_cores"] = cpu_baseline(c, inp, args.cpu_seconds, False,
+                                                     threads=all_core_threads())
     print(json.dumps(res), flush=True)
 
 
@@ -659,6 +682,8 @@ def main():
     res["verified_tok_s"] = verified / (ms_parts["verify_tv"] * 1e-3)
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_seconds, verify_only)
+        res["cpu_baseline_all_cores"] = cpu_baseline(c, inp, args.cpu_seconds, verify_only,
+                                                     threads=all_core_threads())
     print(json.dumps(res), flush=True)
 
 
