@@ -131,6 +131,36 @@ def draft_bytes_per_position(c, logits_written: bool = True) -> float:
             (c.B * c.V * 4 if logits_written else 0))
 
 
+def measured_peaks(torch, device) -> dict:
+    """What this GPU reaches on plain library work, beside the published peaks: a 1 GiB fp32
+    device-to-device copy (bytes read + written over its time) and a bf16 8192^3 matmul
+    (torch / hipBLASLt), each timed with HIP events over 10 calls after 3 warm-up calls."""
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * src.numel() * 4 / timed(lambda: dst.copy_(src)) / 1e9
+    del src, dst
+    n = 8192
+    x = torch.ones((n, n), dtype=torch.bfloat16, device=device)
+    y = torch.ones((n, n), dtype=torch.bfloat16, device=device)
+    mm_tflops = 2.0 * n ** 3 / timed(lambda: torch.matmul(x, y)) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    return dict(hbm_copy_gbs=copy_gbs, bf16_matmul_tflops=mm_tflops,
+                how="1 GiB fp32 copy_ (read + write bytes); bf16 8192^3 torch.matmul")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -382,6 +412,8 @@ def bench_pipeline(args, torch, dspark, device):
     roof = dict(bound="hbm", kernel=kernel, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("round", kernel),
                 bytes_per_launch=per_pos * units, positions_per_launch=units, launch_us=launch_us)
+    mp = measured_peaks(torch, device)
+    roof["measured_peak"] = dict(mp, frac_of_copy=achieved / mp["hbm_copy_gbs"])
     res = dict(
         metric=METRIC, value=(drafted + verified) / (ms_round * 1e-3), unit="tokens/s", n_gpus=1,
         steps=n, warmup=args.warmup, ms_per_step=ms_round, higher_is_better=True,
@@ -482,6 +514,9 @@ def bench_mfma(args, torch, dspark, device):
         rows.append(row)
         del U, x0, u, out, g
         torch.cuda.empty_cache()
+    mp = measured_peaks(torch, device)
+    for row in rows:
+        row["frac_of_matmul"] = row["tflops"] / mp["bf16_matmul_tflops"]
     big = rows[-1]
     res = dict(metric="batched Markov draft MFMA rate vs batch size (bf16 TFLOP/s)",
                value=big["tflops"], unit="TFLOP/s", n_gpus=1, steps=args.steps,
@@ -490,7 +525,7 @@ def bench_mfma(args, torch, dspark, device):
                config=dict(workload="MFMA sweep: persistent slab draft, no logits output",
                            V=V, r=r, gamma=G, B=[x["B"] for x in rows], mall_flush=True,
                            graph_replay=True),
-               sweep=rows)
+               sweep=rows, measured_peak=mp)
     print(json.dumps(res), flush=True)
 
 
@@ -661,6 +696,10 @@ def main():
             tflops = 2.0 * B * c.r * V * units / (launch_us * 1e-6) / 1e12
             roof["mfma"] = dict(achieved=tflops, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                 frac=tflops / MFMA_BF16_PEAK_TFLOPS)
+    mp = measured_peaks(torch, device)
+    roof["measured_peak"] = dict(mp, frac_of_copy=roof["achieved"] / mp["hbm_copy_gbs"])
+    if "mfma" in roof:
+        roof["mfma"]["frac_of_matmul"] = roof["mfma"]["achieved"] / mp["bf16_matmul_tflops"]
     what = "verify + TV labels" if verify_only else "draft + schedule + verify + TV labels"
     res = dict(
         metric=METRIC, value=value, unit="tokens/s", n_gpus=1, steps=args.steps,
