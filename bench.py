@@ -55,6 +55,13 @@ MEASURED_TRAFFIC = {
                  "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
+    # the three kernels of one dspark_verify_tv call (row_stats, verify_tv_chunks, verify_tv_select)
+    ("verify", "dspark_verify_tv"): dict(
+        bytes=10478293721.4,
+        profile="profiles/verify_tv_verify_B256_V151936.md",
+        sources={"verify.hip": "36a56d19c9cb663d607706df4e3a76946999880c0133d6dc26d0e8f086c4e270",
+                 "rows.h": "069e0045b9a59c15697218de2708ffbdb33de09773099a9e0e95cad34229983b",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
         bytes=4836163799.9,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
@@ -669,7 +676,8 @@ def main():
         roof = dict(bound="hbm",
                     kernel="dspark_verify_tv (row_stats + verify_tv_chunks + verify_tv_select)",
                     achieved=bytes_call / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
-        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS, traffic=None, bytes_per_launch=bytes_call,
+        roof.update(frac=roof["achieved"] / HBM_PEAK_GBS,
+                    traffic=measured_traffic("verify", "dspark_verify_tv"), bytes_per_launch=bytes_call,
                     launch_us=launch_us)
     else:
         path = dspark.markov_draft_path(B, t["W1"], t["W2"])
