@@ -18,21 +18,22 @@
 // (bf16 x bf16 pairs into fp32). The 8 rank-group partial sums of a column meet in LDS and
 // are added in wave order.
 //
-// Positions meet through their tile partials, with no separate barrier:
-//   - A one-block kernel fills the per-position partial slots with a sentinel before the
-//     launch.
-//   - At position k every workgroup writes its 640 logits with device-scope (sc1) stores,
-//     waits for them (s_waitcnt), then publishes its tile's (max, sum exp) into slot
-//     [k][g] with one 8-byte device-scope store.
+// Positions meet through their tile partials and one token slot, with no separate barrier:
+//   - A one-block kernel fills the per-position partial slots and token slots with a
+//     sentinel before the launch.
+//   - At position k every workgroup keeps its 640 logits in LDS (and stores them to the
+//     logits output when the caller wants it), then publishes its tile's (max, sum exp) into
+//     slot [k][g] with one 8-byte device-scope store.
 //   - Wave 0 of every workgroup polls the G slots of position k until none holds the
-//     sentinel, and then draws x_k from those partials (in tile order), rescanning the
-//     chosen 640-column tile in token order with device-scope loads.
-// Seeing a workgroup's partial therefore guarantees that its logits are visible. A
-// workgroup publishes position k+1 only after it has finished drawing x_k, so the
-// ping-pong logits rows are never overwritten while another workgroup still reads them.
-// No L2 write-back fence is used, because that costs tens of microseconds per position on
-// this part. Polling is bounded: a workgroup that gives up stops, so the launch always
-// drains, and workgroup 0 then writes the -1 sentinel into the positions it could not draw.
+//     sentinel, and picks the tile that holds the inverse-CDF point from those partials (in
+//     tile order; every workgroup reaches the same pick). The workgroup that owns the tile
+//     rescans its logits from LDS in token order and publishes (logit, token) in token slot
+//     [k]; the others poll that slot.
+// No workgroup ever reads another's logits, so nothing waits for the logits stores, and the
+// draw costs one published token instead of a read of the chosen tile. No L2 write-back
+// fence is used, because that costs tens of microseconds per position on this part. Polling
+// is bounded: a workgroup that gives up stops, so the launch always drains, and workgroup 0
+// then writes the -1 sentinel into the positions it could not draw.
 #include "common.h"
 #include "draw.h"
 #include "kernels.h"
@@ -71,17 +72,15 @@ struct ResArgs {
     int32_t* x_out;
     float* q_out;
     float* lse_out;
-    float* L[64];             // logits row of position k
+    float* L[64];             // logits row of position k (written when L_out)
+    int L_out;
     float2* slots;            // [gamma][G] tile partials, kEmpty until published
+    unsigned long long* toks; // [gamma] (logit bits << 32 | token) of each draw, kEmpty until published
 };
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t h, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
                                            __builtin_bit_cast(bf16x2, h), acc, false);
-}
-
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void store_coherent(float2* p, float2 v) {
@@ -95,13 +94,19 @@ __device__ __forceinline__ unsigned long long load_slot(const float2* p) {
                              __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Waits until every store this thread issued has been acknowledged at device scope.
-__device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void store_token(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long load_token(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __global__ __launch_bounds__(kRThreads, 1)
 void draft_resident(ResArgs a) {
     __shared__ uint4 lds[kResLds / sizeof(uint4)];         // W2 staging, then rank-group sums
     __shared__ float2 wpart[kRWaves];
+    __shared__ float tl[kResTileCols];                     // this position's logits of the tile
     __shared__ uint32_t hs[kResMaxRank / 2];               // W1[x] as bf16 pairs
     __shared__ int stok;
     __shared__ int gave_up;
@@ -198,16 +203,19 @@ void draft_resident(ResArgs a) {
         }
         const float l1 = (live && e1 < V) ? u1 + s1 : -INFINITY;
         const float l2 = (live && own2 && e2 < V) ? u2 + s2 : -INFINITY;
-        float* Lk = a.L[k];
-        if (e1 < V) store_coherent(Lk + e1, l1);
-        if (own2 && e2 < V) store_coherent(Lk + e2, l2);
+        tl[tid] = l1;
+        if (own2) tl[kRThreads + tid] = l2;
+        if (a.L_out) {
+            float* Lk = a.L[k];
+            if (e1 < V) Lk[e1] = l1;
+            if (own2 && e2 < V) Lk[e2] = l2;
+        }
         const float mw = wave_max_dpp(fmaxf(l1, l2));
         const float ew = (mw == -INFINITY) ? 0.0f
                          : ((l1 == -INFINITY ? 0.0f : __expf(l1 - mw)) +
                             (l2 == -INFINITY ? 0.0f : __expf(l2 - mw)));
         const float sw = wave_sum_dpp(ew);
         if (lane == 0) wpart[wave] = make_float2(mw, sw);
-        drain_stores();                                    // this thread's logits are visible
         __syncthreads();
         float2* slot = a.slots + static_cast<long long>(k) * a.G;
         if (tid == 0) {
@@ -248,10 +256,54 @@ void draft_resident(ResArgs a) {
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
+            int t = -1;
+            float lx = 0.0f;
+            TilePick tp;
+            tp.tile = -1;
             if (!gave_up) {
-                const DrawOut out{a.x_out + k, a.q_out ? a.q_out + k : nullptr,
-                                  a.lse_out ? a.lse_out + k : nullptr, blockIdx.x == 0};
-                const int t = draw_regs<kResTileCols, true>(V, p, Lk, a.u[k], out);
+                tp = pick_tile<kPartRegs>(p, a.u[k]);
+                if (tp.tile == static_cast<int>(blockIdx.x)) {
+                    // the chosen tile is this workgroup's: rescan its logits from LDS, in
+                    // token order (lane l owns the 10 columns from 10 l), and publish
+                    float lv[kLaneCols], e[kLaneCols];
+#pragma unroll
+                    for (int j = 0; j < kLaneCols; ++j) {
+                        lv[j] = tl[lane * kLaneCols + j];
+                        e[j] = (lv[j] == -INFINITY) ? 0.0f : __expf(lv[j] - tp.m);
+                    }
+                    t = scan_pick<kLaneCols>(e, c0 + lane * kLaneCols, tp.tprime);
+                    const int rel = t - static_cast<int>(c0);
+                    const int owner = rel / kLaneCols, jj = rel - owner * kLaneCols;
+                    float mine = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < kLaneCols; ++j)
+                        if (j == jj) mine = lv[j];
+                    lx = wave_bcast(mine, owner);
+                    if (lane == 0)
+                        store_token(a.toks + k, (static_cast<unsigned long long>(__float_as_uint(lx)) << 32) |
+                                                    static_cast<uint32_t>(t));
+                } else if (tp.tile >= 0) {
+                    // another workgroup draws: wait for its (logit, token)
+                    unsigned long long v;
+                    unsigned n2 = 0;
+                    while ((v = load_token(a.toks + k)) == kEmpty) {
+                        if (++n2 > kSpinMax) {
+                            if (lane == 0) gave_up = 1;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    t = static_cast<int>(static_cast<uint32_t>(v));
+                    lx = __uint_as_float(static_cast<uint32_t>(v >> 32));
+                }
+            }
+            if (!gave_up) {
+                if (blockIdx.x == 0 && lane == 0) {          // workgroup 0 writes the outputs
+                    const DrawOut out{a.x_out + k, a.q_out ? a.q_out + k : nullptr,
+                                      a.lse_out ? a.lse_out + k : nullptr, true};
+                    if (tp.tile < 0) put(out, -1, 0.0f, -INFINITY);
+                    else put(out, t, __expf(lx - tp.lse), tp.lse);
+                }
                 if (lane == 0) stok = t;
                 if (k + 1 < a.gamma && lane < kResMaxRank / 8) {
                     uint4 hn = make_uint4(0u, 0u, 0u, 0u);
@@ -305,8 +357,10 @@ int tiles_of(int V) { return (V + kResTileCols - 1) / kResTileCols; }
 
 }  // namespace
 
+// tile partials [gamma][G], then the token slots [gamma]
 size_t draft_resident_slot_bytes(int V, int gamma) {
-    return static_cast<size_t>(gamma) * tiles_of(V) * sizeof(float2);
+    return static_cast<size_t>(gamma) * tiles_of(V) * sizeof(float2) +
+           static_cast<size_t>(gamma) * sizeof(unsigned long long);
 }
 
 bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
@@ -328,8 +382,10 @@ hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {
     a.x0 = c.x0; a.u = c.u;
     a.x_out = c.x_out; a.q_out = c.q_out; a.lse_out = c.lse_out;
     for (int k = 0; k < c.gamma; ++k) a.L[k] = c.L[k];
+    a.L_out = c.L_out ? 1 : 0;
     a.slots = c.slots;
-    const int n = c.gamma * a.G;
+    a.toks = reinterpret_cast<unsigned long long*>(c.slots + static_cast<long long>(c.gamma) * a.G);
+    const int n = c.gamma * a.G + c.gamma;            // partial slots and token slots
     hipLaunchKernelGGL(clear_slots, dim3((n + 255) / 256), dim3(256), 0, st,
                        reinterpret_cast<unsigned long long*>(c.slots), n);
     hipError_t e = hipGetLastError();
