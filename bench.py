@@ -48,6 +48,13 @@ MEASURED_TRAFFIC = {
         sources={"draft_resident.hip": "1474f218e0755cc4687b9096a98fee447b59d18b381233080329adcd25da7d4b",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
+    # the per-position sweep of one request (bench.py --per-position)
+    ("single", "draft_step_gemv"): dict(
+        bytes=79192386.3,
+        profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
+        sources={"draft.hip": "8d2f4cb7c96b3b06c67cf019ce9feeadce6b05da7e71b20109131d26a887c15f",
+                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("batched", "draft_slab_resident"): dict(
         bytes=1515540830.5,
         profile="profiles/draft_slab_resident_batched_B64_V151936.md",
@@ -105,6 +112,9 @@ def parse():
     ap.add_argument("--rebuilt-logits", action="store_true",
                     help="verify rebuilds the draft logits from the Markov factors wherever the "
                          "draft takes the slab path, also past V = 131072")
+    ap.add_argument("--per-position", action="store_true",
+                    help="draft with DSPARK_DRAFT_PER_POSITION: launches per position instead of the "
+                         "one-launch forms (one request then takes the vocabulary sweep)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="extra eager steps with no timing (for rocprofv3 runs)")
     return ap.parse_args()
@@ -588,7 +598,8 @@ def main():
         torch.cuda.synchronize()
 
     def draft():
-        dspark.markov_draft(t["U"], t["W1"], t["W2"], t["x0"], t["u"], out=out_d)
+        dspark.markov_draft(t["U"], t["W1"], t["W2"], t["x0"], t["u"], out=out_d,
+                            per_position=args.per_position)
 
     def schedule():
         dspark.schedule(t["conf"], t["sps"], Bmax, temp=t["temp"], out=out_s)
@@ -699,8 +710,11 @@ def main():
                     timing="HIP events on the launch stream around eager calls")
     else:
         path = dspark.markov_draft_path(B, t["W1"], t["W2"])
+        if args.per_position and path == "resident":
+            path = "sweep"                    # one request drafted per position: the sweep
         per_pos = draft_bytes_per_position(c, not rebuild)   # algorithmic bytes of one position
-        one_launch = dspark.markov_draft_one_launch(B, t["W1"], t["W2"], want_logits=not rebuild)
+        one_launch = (not args.per_position and
+                      dspark.markov_draft_one_launch(B, t["W1"], t["W2"], want_logits=not rebuild))
         if one_launch:
             # one launch draws all gamma positions (W2 read once, then held in registers); the
             # timed call also holds the tiny flag-reset kernel that precedes it
@@ -737,7 +751,8 @@ def main():
                     mall_flush=not args.no_flush, graph_replay=True,
                     draft_logits=("input" if verify_only else
                                   "rebuilt by verify from the factors" if rebuild else
-                                  "written by the draft")),
+                                  "written by the draft"),
+                    draft_launches="per position" if args.per_position else "default"),
         drafted_per_step=drafted, verified_per_step=verified,
         breakdown_us={k: v * 1e3 for k, v in ms_parts.items()},
         ms_per_step_p10_p90=[float(np.percentile(ms, 10)), float(np.percentile(ms, 90))],
