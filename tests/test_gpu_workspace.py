@@ -57,3 +57,33 @@ def test_poisoned_workspaces(gpu):
         s = dspark.schedule(dev(conf), dev(sps), 64, temp=dev(synth.temperatures(G)))
         ref = oracle.schedule(conf, synth.temperatures(G), sps, 64)
         assert np.array_equal(host(s["len"]), ref["len"])
+
+
+@pytest.mark.parametrize("fill", ["zeros", "random"])
+@pytest.mark.parametrize("B,V,G,want_logits", [
+    (1, 9000, 5, True),       # the register-resident single-request draft
+    (1, 20000, 4, False),
+    (12, 9000, 3, True),      # the persistent slab draft, with and without the logits
+    (24, 20000, 4, False),
+])
+def test_one_launch_drafts_ignore_stale_slots(gpu, fill, B, V, G, want_logits):
+    """The one-launch draft forms meet through position slots in the workspace; a workspace
+    of zeros (which reads as published partials and as token 0) or of random bytes must not
+    be taken for this call's slots."""
+    lib = binding.load()
+    c = synth.custom(990 + B + G, B=B, V=V, r=16, gamma=G, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    W1, W2 = dev(d["W1"]), dev(d["W2"])
+    assert dspark.markov_draft_path(B, W1, W2) == ("resident" if B == 1 else "slab")
+    assert dspark.markov_draft_one_launch(B, W1, W2, want_logits=want_logits)
+    nbytes = lib.dspark_markov_draft_workspace_bytes(B, V, 16, G) + 4096
+    if fill == "zeros":
+        binding.workspace(nbytes, torch.device("cuda:0"), "draft").zero_()
+        torch.cuda.synchronize()
+    else:
+        _poison("draft", nbytes, 7 * B + G)
+    out = dspark.markov_draft(dev(d["U"]), W1, W2, dev(d["x0"]), dev(d["u"]), want_logits=want_logits)
+    g = {k: host(v) for k, v in out.items() if v is not None}
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
+                      range(B), gL=g.get("L"))
+    assert rep.ties <= 1
