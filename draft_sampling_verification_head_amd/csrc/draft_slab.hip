@@ -11,9 +11,10 @@
 // ranks per fragment, NT * 8 fragments), staged once through a wave-private LDS area that
 // turns rank-major rows into rank-contiguous fragments. The batch streams through the slab in
 // groups of 16 requests: U_k tiles and gathered W1 rows arrive in LDS by direct loads three
-// groups ahead, the MFMAs give the bias of 16 requests x 16 NT columns per wave, and the
-// epilogue adds U_k, optionally stores the logits, and reduces each request's columns of the
-// wave tile to (max, sum exp(l - max)), the tile partial the draw uses.
+// groups ahead, the MFMAs, their accumulators started at U_k, give the logits U_k + bias of
+// 16 requests x 16 NT columns per wave, and the epilogue optionally stores the logits and
+// reduces each request's columns of the wave tile to (max, sum exp(l - max)), the tile
+// partial the draw uses.
 //
 // Draw (one request): a two-level pick. The 8 wave-tile partials of each slab are merged in
 // tile order into a slab partial; the request's slab partials give the slab that holds the
@@ -217,9 +218,10 @@ __device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, float* L, 
         if (g + 3 < ng) issue(g + 3);
 
         const char* H = sm + hbuf_off<NT>(g & 3);
+        // the accumulators start at U_k, so the MFMAs leave the logits U_k + bias
         f32x4 acc[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{u4[t].x, u4[t].y, u4[t].z, u4[t].w};
         // B fragments one rank chunk ahead; the empty asm keeps the compiler from hoisting
         // every chunk's fragment at once, which would not fit beside the W2 fragments
         const int hl = opaque_lane(), hrq = hl & 15, hcg = hl >> 4;
@@ -250,10 +252,10 @@ __device__ __forceinline__ void slab_stream(const SlabArgs& a, int k, float* L, 
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            lv[t][0] = u4[t].x + acc[t][0];
-            lv[t][1] = u4[t].y + acc[t][1];
-            lv[t][2] = u4[t].z + acc[t][2];
-            lv[t][3] = u4[t].w + acc[t][3];
+            lv[t][0] = acc[t][0];
+            lv[t][1] = acc[t][1];
+            lv[t][2] = acc[t][2];
+            lv[t][3] = acc[t][3];
             if (!fast) {
                 const bool ok = live && cw + 16 * t + 4 * cg < a.V;
 #pragma unroll
@@ -394,9 +396,9 @@ __device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, 
     const int lane = threadIdx.x & (kWave - 1);
     const int rq = lane & 15, cg = lane >> 4;
     const long long cw = static_cast<long long>(tp.tile) * S::WC;
-    f32x4 acc[NT];
+    f32x4 acc[NT];                                   // from U_k, as in the stream
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{in.u4[t].x, in.u4[t].y, in.u4[t].z, in.u4[t].w};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
         // the W1 row of the previous token in every one of the 16 request columns
@@ -410,10 +412,10 @@ __device__ __forceinline__ void slab_recompute(const SlabArgs& a, int b, int k, 
         for (int t = 0; t < NT; ++t) {
             const bool ok = cw + 16 * t + 4 * cg < a.V;
             float* rv = rowv + 16 * t + 4 * cg;
-            rv[0] = ok ? in.u4[t].x + acc[t][0] : -INFINITY;
-            rv[1] = ok ? in.u4[t].y + acc[t][1] : -INFINITY;
-            rv[2] = ok ? in.u4[t].z + acc[t][2] : -INFINITY;
-            rv[3] = ok ? in.u4[t].w + acc[t][3] : -INFINITY;
+            rv[0] = ok ? acc[t][0] : -INFINITY;
+            rv[1] = ok ? acc[t][1] : -INFINITY;
+            rv[2] = ok ? acc[t][2] : -INFINITY;
+            rv[3] = ok ? acc[t][3] : -INFINITY;
         }
     }
     wait_lgkm0();                                     // the row is in LDS
@@ -472,9 +474,9 @@ __device__ __forceinline__ void batch_recompute(const SlabArgs& a, int k, int n,
         u4[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (rq < n && col < a.V) u4[t] = *reinterpret_cast<const float4*>(urow + col);
     }
-    f32x4 acc[NT];
+    f32x4 acc[NT];                                   // from U_k, as in the stream
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{u4[t].x, u4[t].y, u4[t].z, u4[t].w};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
         // the W1 row of request i's previous token in column i
@@ -491,10 +493,10 @@ __device__ __forceinline__ void batch_recompute(const SlabArgs& a, int k, int n,
         for (int t = 0; t < NT; ++t) {
             const bool ok = cw + 16 * t + 4 * cg < a.V;
             float* rv = rowb + rq * S::WC + 16 * t + 4 * cg;
-            rv[0] = ok ? u4[t].x + acc[t][0] : -INFINITY;
-            rv[1] = ok ? u4[t].y + acc[t][1] : -INFINITY;
-            rv[2] = ok ? u4[t].z + acc[t][2] : -INFINITY;
-            rv[3] = ok ? u4[t].w + acc[t][3] : -INFINITY;
+            rv[0] = ok ? acc[t][0] : -INFINITY;
+            rv[1] = ok ? acc[t][1] : -INFINITY;
+            rv[2] = ok ? acc[t][2] : -INFINITY;
+            rv[3] = ok ? acc[t][3] : -INFINITY;
         }
     }
     wait_lgkm0();                                     // the rows are in LDS

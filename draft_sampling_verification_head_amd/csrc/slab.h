@@ -4,10 +4,11 @@
 // A slab workgroup (8 waves) owns 128 * NT vocabulary columns; wave w owns the 16 * NT
 // columns of its "wave tile" and holds W2 for them, all ranks, in registers as A fragments
 // of v_mfma_f32_16x16x32_bf16 (W2^T: 16 columns x 32 ranks per fragment). Rows of the batch
-// stream through the slab; the bias of a row is the MFMA of these fragments with the W1 row
-// of its previous token (B operand). Column j of an MFMA result depends only on column j of
-// the B operand, so recomputing one row's tile with the same fragments in the same rank
-// order reproduces the step's logits bit for bit.
+// stream through the slab; the logits of a row are the MFMA of these fragments with the W1
+// row of its previous token (B operand), accumulated onto the row's base logits U (C
+// operand). Column j of an MFMA result depends only on column j of the B and C operands, so
+// recomputing one row's tile with the same fragments and U in the same rank order
+// reproduces the step's logits bit for bit.
 #pragma once
 
 #include "common.h"

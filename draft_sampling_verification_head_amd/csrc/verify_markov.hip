@@ -235,9 +235,17 @@ void vm_tv(VmArgs a) {
         const char* ub = sm + i * Ly::Buf;
         const char* lb = ub + Ly::UT;
         const char* H = ub + 2 * Ly::UT;
+        // this lane's chunk of tile t: the accumulators start at U, as in the slab draft
+        auto toff = [&](int t) {
+            const int c = ((t & 1) << 2) + cg;        // chunk of the tile pair t / 2
+            return (wave * Ly::NTP + (t >> 1)) * 1024 + 16 * (rr * 8 + (c ^ rr));
+        };
         f32x4 acc[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < NT; ++t) {
+            const float4 u4 = *reinterpret_cast<const float4*>(ub + toff(t));
+            acc[t] = f32x4{u4.x, u4.y, u4.z, u4.w};
+        }
         // B fragments one rank chunk ahead (request columns 8..15 repeat rows 0..7); the
         // empty asm keeps the compiler from hoisting every chunk's fragment at once, which
         // would not fit beside the W2 fragments
@@ -269,14 +277,11 @@ void vm_tv(VmArgs a) {
         float ldx_v = 0.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int c = ((t & 1) << 2) + cg;        // chunk of the tile pair t / 2
-            const int off = (wave * Ly::NTP + (t >> 1)) * 1024 + 16 * (rr * 8 + (c ^ rr));
-            const float4 u4 = *reinterpret_cast<const float4*>(ub + off);
-            const float4 t4 = *reinterpret_cast<const float4*>(lb + off);
+            const float4 t4 = *reinterpret_cast<const float4*>(lb + toff(t));
             const long long col = cw + 16 * t + 4 * cg;
             const bool ok = col < a.V;
-            const float ld[4] = {ok ? u4.x + acc[t][0] : -INFINITY, ok ? u4.y + acc[t][1] : -INFINITY,
-                                 ok ? u4.z + acc[t][2] : -INFINITY, ok ? u4.w + acc[t][3] : -INFINITY};
+            const float ld[4] = {ok ? acc[t][0] : -INFINITY, ok ? acc[t][1] : -INFINITY,
+                                 ok ? acc[t][2] : -INFINITY, ok ? acc[t][3] : -INFINITY};
             const float lt[4] = {ok ? t4.x : -INFINITY, ok ? t4.y : -INFINITY,
                                  ok ? t4.z : -INFINITY, ok ? t4.w : -INFINITY};
 #pragma unroll
@@ -407,9 +412,12 @@ void vm_tv16(VmArgs a) {
         const char* ub = sm + i * Ly::Buf + wave * NT * 1024;
         const char* lb = ub + Ly::UT;
         const char* H = sm + i * Ly::Buf + 2 * Ly::UT;
-        f32x4 acc[NT];
+        f32x4 acc[NT];                                // from U, as in the slab draft
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < NT; ++t) {
+            const float4 u4 = *reinterpret_cast<const float4*>(ub + t * 1024 + 16 * upos);
+            acc[t] = f32x4{u4.x, u4.y, u4.z, u4.w};
+        }
         const int hl = opaque_lane(), hrq = hl & 15, hcg = hl >> 4;
         auto hfrag = [&](int s) {
             const int p = (4 * s + hcg) ^ hrq;
@@ -437,12 +445,11 @@ void vm_tv16(VmArgs a) {
         float ldx_v = 0.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float4 u4 = *reinterpret_cast<const float4*>(ub + t * 1024 + 16 * upos);
             const float4 t4 = *reinterpret_cast<const float4*>(lb + t * 1024 + 16 * upos);
             const long long col = cw + 16 * t + 4 * cg;
             const bool ok = col < a.V;
-            const float ld[4] = {ok ? u4.x + acc[t][0] : -INFINITY, ok ? u4.y + acc[t][1] : -INFINITY,
-                                 ok ? u4.z + acc[t][2] : -INFINITY, ok ? u4.w + acc[t][3] : -INFINITY};
+            const float ld[4] = {ok ? acc[t][0] : -INFINITY, ok ? acc[t][1] : -INFINITY,
+                                 ok ? acc[t][2] : -INFINITY, ok ? acc[t][3] : -INFINITY};
             const float lt[4] = {ok ? t4.x : -INFINITY, ok ? t4.y : -INFINITY,
                                  ok ? t4.z : -INFINITY, ok ? t4.w : -INFINITY};
 #pragma unroll
@@ -614,9 +621,9 @@ void vm_select(SelArgs a) {
             }
             bf16x8 w2f[NT][kKS];
             load_w2_frags<NT, kKS, kKS>(w2f, a.W2, V, a.r, cw, stg);
-            f32x4 acc[NT];
+            f32x4 acc[NT];                            // from U, as in the slab draft
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < NT; ++t) acc[t] = f32x4{u4[t].x, u4[t].y, u4[t].z, u4[t].w};
 #pragma unroll
             for (int s = 0; s < kKS; ++s) {
                 {
@@ -631,8 +638,7 @@ void vm_select(SelArgs a) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const bool ok = cw + 16 * t + 4 * cg < V;
-                    const float ld[4] = {u4[t].x + acc[t][0], u4[t].y + acc[t][1],
-                                         u4[t].z + acc[t][2], u4[t].w + acc[t][3]};
+                    const float ld[4] = {acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
                     const float lt[4] = {t4[t].x, t4[t].y, t4[t].z, t4[t].w};
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
