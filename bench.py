@@ -56,10 +56,10 @@ MEASURED_TRAFFIC = {
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("batched", "draft_slab_resident"): dict(
-        bytes=1515540830.5,
+        bytes=1416251919.0,
         profile="profiles/draft_slab_resident_batched_B64_V151936.md",
-        sources={"draft_slab.hip": "4441872dddfba5e8ee7a963fd03058f533077cece76c65a3229092fc67f8dc5c",
-                 "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
+        sources={"draft_slab.hip": "b39c35f224a72a72405e8efbf383dfcaefb19a0c49feb233e055f10e86f362ac",
+                 "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the three kernels of one dspark_verify_tv call (row_stats, verify_tv_chunks, verify_tv_select)
@@ -70,10 +70,10 @@ MEASURED_TRAFFIC = {
                  "rows.h": "069e0045b9a59c15697218de2708ffbdb33de09773099a9e0e95cad34229983b",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
-        bytes=4836163799.9,
+        bytes=4835945350.4,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
-        sources={"draft_slab.hip": "4441872dddfba5e8ee7a963fd03058f533077cece76c65a3229092fc67f8dc5c",
-                 "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
+        sources={"draft_slab.hip": "b39c35f224a72a72405e8efbf383dfcaefb19a0c49feb233e055f10e86f362ac",
+                 "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
 }
@@ -460,10 +460,10 @@ def bench_pipeline(args, torch, dspark, device):
 # 1024 SIMDs), the MfmaUtil expression of rocprofiler's counter definitions). A figure holds
 # only for the kernel sources it was measured with.
 MEASURED_MFMA_BUSY = dict(
-    util={64: 6.94, 256: 13.21, 512: 15.33, 1024: 16.73},
+    util={64: 7.32, 256: 13.67, 512: 15.86, 1024: 17.29},
     profile="profiles/draft_slab_resident_mfma_sweep_V151936.md",
-    sources={"draft_slab.hip": "4441872dddfba5e8ee7a963fd03058f533077cece76c65a3229092fc67f8dc5c",
-             "slab.h": "c2214d1450bf08ba3f063ec162084d8191c68859c3ed8e9d5f2424182d5c73e7",
+    sources={"draft_slab.hip": "b39c35f224a72a72405e8efbf383dfcaefb19a0c49feb233e055f10e86f362ac",
+             "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
              "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
              "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"})
 
