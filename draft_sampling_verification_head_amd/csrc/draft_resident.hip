@@ -19,8 +19,14 @@
 // are added in wave order.
 //
 // Positions meet through their tile partials and one token slot, with no separate barrier:
-//   - A one-block kernel fills the per-position partial slots and token slots with a
-//     sentinel before the launch.
+//   - The slots are reset inside the launch. Two words follow them in the workspace: a call
+//     counter E and a ready word F. Every workgroup reads E at the start; workgroup 0 fills
+//     the partial and token slots with the sentinel while the W2 load is under way, then
+//     stores F = mix(E) (a 64-bit mixing function); no workgroup publishes a partial before it
+//     has seen that F, and workgroup 0 advances E when the launch is done, once every
+//     workgroup is known to have started (each has published its last partial). A previous
+//     call left F = mix(E - 1), so stale slots are never taken for this call's; a workspace
+//     of arbitrary bytes matches only if F happens to equal mix(E).
 //   - At position k every workgroup keeps its 640 logits in LDS (and stores them to the
 //     logits output when the caller wants it), then publishes its tile's (max, sum exp) into
 //     slot [k][g] with one 8-byte device-scope store.
@@ -76,7 +82,18 @@ struct ResArgs {
     int L_out;
     float2* slots;            // [gamma][G] tile partials, kEmpty until published
     unsigned long long* toks; // [gamma] (logit bits << 32 | token) of each draw, kEmpty until published
+    unsigned long long* epoch;   // [2]: the call counter E and the ready word F (after toks)
 };
+
+// Ready word of a call with counter e: the finaliser of the splitmix64 generator (Steele, Lea
+// and Flood, "Fast splittable pseudorandom number generators", 2014) applied to e xor a
+// constant, so that counters of all-zero or all-one bytes do not map to those bytes.
+__device__ __forceinline__ unsigned long long ready_word(unsigned long long e) {
+    unsigned long long z = e ^ 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t h, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
@@ -110,8 +127,15 @@ void draft_resident(ResArgs a) {
     __shared__ uint32_t hs[kResMaxRank / 2];               // W1[x] as bf16 pairs
     __shared__ int stok;
     __shared__ int gave_up;
+    __shared__ unsigned long long s_e0;                    // the call counter read at the start
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int V = a.V, r = a.r;
+    if (tid == 0) s_e0 = load_token(a.epoch);             // seen by every thread after a barrier
+    if (blockIdx.x == 0) {                                // reset this call's slots
+        unsigned long long* sl = reinterpret_cast<unsigned long long*>(a.slots);
+        const int n = a.gamma * a.G + a.gamma;             // partial slots, then token slots
+        for (int i = tid; i < n; i += kRThreads) store_token(sl + i, kEmpty);
+    }
     const long long c0 = static_cast<long long>(blockIdx.x) * kResTileCols;
     // epilogue columns of this thread: c0 + tid, and c0 + 512 + tid for tid < 128
     const long long e1 = c0 + tid, e2 = c0 + kRThreads + tid;
@@ -172,6 +196,12 @@ void draft_resident(ResArgs a) {
     float (*red)[kResTileCols] = reinterpret_cast<float (*)[kResTileCols]>(lds);   // reuses the staging area
 
     if (tid == 0) gave_up = 0;
+    const unsigned long long key = ready_word(s_e0);
+    if (blockIdx.x == 0) {                                // the slots are reset: publish F
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) store_token(a.epoch + 1, key);
+    }
     int tok = tok0;
     int k = 0;
     for (; k < a.gamma; ++k) {
@@ -225,7 +255,16 @@ void draft_resident(ResArgs a) {
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < kRWaves; ++i) s += tile_mass(wpart[i], m);
-            store_coherent(slot + blockIdx.x, make_float2(m, s));   // publishes the tile
+            if (k == 0) {                                 // the slots must be reset first
+                for (unsigned n = 0; load_token(a.epoch + 1) != key; ++n) {
+                    if (n > kSpinMax) {
+                        gave_up = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            if (!gave_up) store_coherent(slot + blockIdx.x, make_float2(m, s));   // publishes the tile
         }
         // U_{k+1} goes out now, so it is in flight while the partials arrive
         if (k + 1 < a.gamma) {
@@ -237,7 +276,7 @@ void draft_resident(ResArgs a) {
         if (wave == 0) {
             float2 p[kPartRegs];
             unsigned n = 0;
-            while (true) {
+            while (!gave_up) {
                 bool missing = false;
 #pragma unroll
                 for (int t = 0; t < kPartRegs; ++t) {
@@ -317,6 +356,9 @@ void draft_resident(ResArgs a) {
         if (gave_up) break;
         tok = stok;
     }
+    // every workgroup has read E: each published its last partial, which workgroup 0 saw
+    // (or the launch gave up, and E moves on all the same)
+    if (blockIdx.x == 0 && tid == 0) store_token(a.epoch, s_e0 + 1);
     if (gave_up && blockIdx.x == 0 && tid == 0) {
         for (int i = k; i < a.gamma; ++i) {
             a.x_out[i] = -1;
@@ -324,11 +366,6 @@ void draft_resident(ResArgs a) {
             if (a.lse_out) a.lse_out[i] = -INFINITY;
         }
     }
-}
-
-__global__ void clear_slots(unsigned long long* slots, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) slots[i] = kEmpty;
 }
 
 struct DeviceFit {
@@ -357,10 +394,10 @@ int tiles_of(int V) { return (V + kResTileCols - 1) / kResTileCols; }
 
 }  // namespace
 
-// tile partials [gamma][G], then the token slots [gamma]
+// tile partials [gamma][G], the token slots [gamma], then the call counter and ready word
 size_t draft_resident_slot_bytes(int V, int gamma) {
     return static_cast<size_t>(gamma) * tiles_of(V) * sizeof(float2) +
-           static_cast<size_t>(gamma) * sizeof(unsigned long long);
+           (static_cast<size_t>(gamma) + 2) * sizeof(unsigned long long);
 }
 
 bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
@@ -385,11 +422,7 @@ hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {
     a.L_out = c.L_out ? 1 : 0;
     a.slots = c.slots;
     a.toks = reinterpret_cast<unsigned long long*>(c.slots + static_cast<long long>(c.gamma) * a.G);
-    const int n = c.gamma * a.G + c.gamma;            // partial slots and token slots
-    hipLaunchKernelGGL(clear_slots, dim3((n + 255) / 256), dim3(256), 0, st,
-                       reinterpret_cast<unsigned long long*>(c.slots), n);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    a.epoch = a.toks + c.gamma;
     hipLaunchKernelGGL(draft_resident, dim3(a.G), dim3(kRThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -371,3 +371,37 @@ def test_resume_split_generation(gpu, B, V, r, G, wdt, want_logits):
         if want_logits:
             joined = np.concatenate([first["L"], second["L"]], axis=1)
             assert np.array_equal(joined.view(np.uint8), full["L"].view(np.uint8)), g1
+
+
+def test_single_request_graph_replays(gpu):
+    """The single-request resident draft captured once and replayed: the launch resets its
+    own position slots (keyed by a call counter in the workspace), so every replay, with
+    eager calls of other shapes on the same workspace between them, equals the eager call."""
+    c = synth.custom(977, B=1, V=20000, r=64, gamma=6, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    U, W1, W2, x0, u = (dev(d[k]) for k in ("U", "W1", "W2", "x0", "u"))
+    assert dspark.markov_draft_path(1, W1, W2) == "resident"
+    out = dict(x=torch.empty((1, c.gamma), dtype=torch.int32, device="cuda"),
+               q=torch.empty((1, c.gamma), dtype=torch.float32, device="cuda"),
+               lse=torch.empty((1, c.gamma), dtype=torch.float32, device="cuda"),
+               L=torch.empty((1, c.gamma, c.V), dtype=torch.float32, device="cuda"))
+    ref = run_draft(d)
+    other = synth.custom(978, B=1, V=9000, r=64, gamma=3, w_dtype="bf16", w_sigma=0.3)
+    od = synth.draft_inputs(other)
+    dspark.markov_draft(U, W1, W2, x0, u, out=out)          # workspace sized before capture
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            dspark.markov_draft(U, W1, W2, x0, u, out=out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for k in out.values():
+            k.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("x", "q", "lse", "L"):
+            assert np.array_equal(host(out[k]).view(np.uint8), ref[k].view(np.uint8)), (rep, k)
+        run_draft(od)                                        # another shape between replays

@@ -59,7 +59,7 @@ def test_poisoned_workspaces(gpu):
         assert np.array_equal(host(s["len"]), ref["len"])
 
 
-@pytest.mark.parametrize("fill", ["zeros", "random"])
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
 @pytest.mark.parametrize("B,V,G,want_logits", [
     (1, 9000, 5, True),       # the register-resident single-request draft
     (1, 20000, 4, False),
@@ -68,8 +68,8 @@ def test_poisoned_workspaces(gpu):
 ])
 def test_one_launch_drafts_ignore_stale_slots(gpu, fill, B, V, G, want_logits):
     """The one-launch draft forms meet through position slots in the workspace; a workspace
-    of zeros (which reads as published partials and as token 0) or of random bytes must not
-    be taken for this call's slots."""
+    of zeros (which reads as published partials and as token 0), of all-one bytes or of
+    random bytes must not be taken for this call's slots."""
     lib = binding.load()
     c = synth.custom(990 + B + G, B=B, V=V, r=16, gamma=G, w_dtype="bf16", w_sigma=0.3)
     d = synth.draft_inputs(c)
@@ -77,8 +77,8 @@ def test_one_launch_drafts_ignore_stale_slots(gpu, fill, B, V, G, want_logits):
     assert dspark.markov_draft_path(B, W1, W2) == ("resident" if B == 1 else "slab")
     assert dspark.markov_draft_one_launch(B, W1, W2, want_logits=want_logits)
     nbytes = lib.dspark_markov_draft_workspace_bytes(B, V, 16, G) + 4096
-    if fill == "zeros":
-        binding.workspace(nbytes, torch.device("cuda:0"), "draft").zero_()
+    if fill in ("zeros", "ones"):
+        binding.workspace(nbytes, torch.device("cuda:0"), "draft").fill_(0 if fill == "zeros" else 255)
         torch.cuda.synchronize()
     else:
         _poison("draft", nbytes, 7 * B + G)
