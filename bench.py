@@ -43,9 +43,9 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
     ("single", "draft_resident"): dict(
-        bytes=86951431.3,
+        bytes=86945882.1,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
-        sources={"draft_resident.hip": "1474f218e0755cc4687b9096a98fee447b59d18b381233080329adcd25da7d4b",
+        sources={"draft_resident.hip": "5cfbd024e5eebc35862cd5f69556d181c024d82ebd75d75508fbf4544b46bd60",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the per-position sweep of one request (bench.py --per-position)
@@ -716,8 +716,8 @@ def main():
         one_launch = (not args.per_position and
                       dspark.markov_draft_one_launch(B, t["W1"], t["W2"], want_logits=not rebuild))
         if one_launch:
-            # one launch draws all gamma positions (W2 read once, then held in registers); the
-            # timed call also holds the tiny flag-reset kernel that precedes it
+            # one launch draws all gamma positions (W2 read once, then held in registers); for
+            # the slab form the timed call also holds the tiny flag-reset kernel before it
             kernel = "draft_resident" if path == "resident" else "draft_slab_resident"
             units, launch_us = G, ms_kernel * 1e3
         else:
