@@ -65,11 +65,23 @@ struct SlabArgs {
     float2* part;             // [B][ntw] (max, sum exp) per request and wave tile
     float2* spart;            // resident: [B][G] the same per request and slab (8 wave tiles)
     unsigned long long* flags;   // resident: [3][gamma][G], kEmpty until published
+    unsigned long long* epoch;   // resident: [2] the call counter E and the ready word F
     float4* picks;            // resident: [B] (slab, max, lse, mass left in the slab)
 };
 
 constexpr unsigned kSpinMax = 1u << 20;             // bounded flag wait, about a second
 constexpr unsigned long long kEmpty = ~0ull;
+
+// Ready word of a resident call with counter e (the single-request draft uses the same word
+// in draft_resident.hip): the finaliser of the splitmix64 generator
+// (Steele, Lea and Flood, "Fast splittable pseudorandom number generators", 2014) applied to
+// e xor a constant, so that counters of all-zero or all-one bytes do not map to those bytes.
+__device__ __forceinline__ unsigned long long ready_word(unsigned long long e) {
+    unsigned long long z = e ^ 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
 
 // LDS: [U0][U1][H0][H1][U2][H2][H3][tokens]. U slot i holds group g = i (mod 3), every wave's
 // own tiles (wave-private); H slot j holds group g = j (mod 4), shared by the waves. The W2
@@ -636,11 +648,28 @@ void draft_slab_resident(SlabArgs a) {
     int* dlist = reinterpret_cast<int*>(sm + hbuf_off<NT>(2) + kSlabWaves * kBatch * (S::WC + 1) * 4) +
                  wave * kWave;
     if (tid == 0) gave_up = 0;
+    // The launch resets its own position flags (see the single-request draft): tid 0 of every
+    // workgroup reads the call counter E; workgroup 0 fills the flags with the sentinel while
+    // W2 loads and then stores the ready word F = ready_word(E); no workgroup publishes its
+    // first flag before it has seen that F; workgroup 0 advances E at the end, once every
+    // workgroup has published all its flags of the last position.
+    unsigned long long e0 = 0, key = 0;
+    if (tid == 0) {
+        e0 = load_coherent(a.epoch);
+        key = ready_word(e0);
+    }
+    if (slab == 0)
+        for (long long i = tid; i < 3ll * a.gamma * G; i += kSlabThreads) store_coherent(a.flags + i, kEmpty);
 
     bf16x8 w2f[NT][kKS];
     load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
     wait_lgkm0();
     __syncthreads();                                  // every wave is done with the staging area
+    if (slab == 0) {                                  // the flags are reset: publish F
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) store_coherent(a.epoch + 1, key);
+    }
     // U loads of the first groups of a position (they do not depend on the tokens)
     auto prefetch_u = [&](int kk) {
         for (int g = 0; g < npre; ++g) issue_group<NT, 1>(a, kk, g, sm, stok);
@@ -651,6 +680,7 @@ void draft_slab_resident(SlabArgs a) {
     // wave 0 waits until all G flags of `row` are set (false after the spin bound); the other
     // waves wait at the workgroup barrier that follows, so each workgroup polls with one wave
     auto wait_flags = [&](const unsigned long long* row) {
+        if (gave_up) return false;                    // this workgroup could not publish
         for (unsigned n = 0;; ++n) {
             bool missing = false;
             for (int i = lane; i < G; i += kWave) missing |= load_coherent(row + i) == kEmpty;
@@ -663,7 +693,18 @@ void draft_slab_resident(SlabArgs a) {
     auto publish = [&](int f, int k) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0) store_coherent(flag_row(f, k) + slab, 0ull);
+        if (tid == 0) {
+            if (f == 0 && k == 0) {                   // the flags must be reset first
+                for (unsigned n = 0; load_coherent(a.epoch + 1) != key; ++n) {
+                    if (n > kSpinMax) {
+                        gave_up = 1;
+                        return;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            store_coherent(flag_row(f, k) + slab, 0ull);
+        }
     };
     int k = 0;
     for (; k < a.gamma; ++k) {
@@ -788,6 +829,9 @@ void draft_slab_resident(SlabArgs a) {
         if (k + 1 < a.gamma) prefetch_u(k + 1);
     }
     __builtin_amdgcn_s_waitcnt(0);                    // no load in flight at exit
+    // every workgroup has read E (each published the flags workgroup 0 waited for), or the
+    // launch gave up; E moves on either way
+    if (slab == 0 && tid == 0) store_coherent(a.epoch, e0 + 1);
     if (gave_up) {                                    // this workgroup's requests: -1 from k on
         for (long long i = tid; i < static_cast<long long>(a.B) * a.gamma; i += kSlabThreads) {
             const int b = static_cast<int>(i / a.gamma), kk = static_cast<int>(i % a.gamma);
@@ -797,11 +841,6 @@ void draft_slab_resident(SlabArgs a) {
             if (a.lse_out) a.lse_out[i] = -INFINITY;
         }
     }
-}
-
-__global__ void clear_flags(unsigned long long* f, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) f[i] = kEmpty;
 }
 
 size_t slab_lds_bytes(int nt, int B) {
@@ -883,16 +922,14 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
     a.L = nullptr;
     a.L_bstride = c.L_bstride;
     a.flags = reinterpret_cast<unsigned long long*>(c.slots);
+    a.epoch = nullptr;
     // resident: the second partial buffer holds the picks [B] and the slab partials [B][G]
     a.picks = reinterpret_cast<float4*>(c.part[1]);
     a.spart = c.part[1] + 2 * static_cast<long long>(c.B);
     const size_t smem = slab_lds_bytes(NT, c.B);
     const dim3 grid(static_cast<unsigned>(a.G));
     if (!c.per_position && draft_slab_one_launch(c.B, c.V, c.L_out)) {
-        const int n = 3 * c.gamma * a.G;
-        hipLaunchKernelGGL(clear_flags, dim3((n + 255) / 256), dim3(256), 0, st, a.flags, n);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        a.epoch = a.flags + 3ll * c.gamma * a.G;      // after the flags
         a.part = c.part[0];
         if (c.L_out) {
             a.L = c.L[0];                             // the caller's [B][gamma][V]: L[k] = L[0] + k V
@@ -924,8 +961,9 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
 
 int draft_slab_tiles(int V) { return slab_count(V) * kSlabWaves; }
 
+// position flags [3][gamma][G], then the call counter and the ready word
 size_t draft_slab_flag_bytes(int V, int gamma) {
-    return 3 * static_cast<size_t>(gamma) * slab_count(V) * sizeof(unsigned long long);
+    return (3 * static_cast<size_t>(gamma) * slab_count(V) + 2) * sizeof(unsigned long long);
 }
 
 bool draft_slab_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
