@@ -56,9 +56,9 @@ MEASURED_TRAFFIC = {
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("batched", "draft_slab_resident"): dict(
-        bytes=1416251919.0,
+        bytes=1421449799.6,
         profile="profiles/draft_slab_resident_batched_B64_V151936.md",
-        sources={"draft_slab.hip": "b39c35f224a72a72405e8efbf383dfcaefb19a0c49feb233e055f10e86f362ac",
+        sources={"draft_slab.hip": "19be639ac5edace8d1f3be5b5077b08e21960b1cead6f4683dc6d9ecc1157cee",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
@@ -70,9 +70,9 @@ MEASURED_TRAFFIC = {
                  "rows.h": "069e0045b9a59c15697218de2708ffbdb33de09773099a9e0e95cad34229983b",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
-        bytes=4835945350.4,
+        bytes=4835639540.2,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
-        sources={"draft_slab.hip": "b39c35f224a72a72405e8efbf383dfcaefb19a0c49feb233e055f10e86f362ac",
+        sources={"draft_slab.hip": "19be639ac5edace8d1f3be5b5077b08e21960b1cead6f4683dc6d9ecc1157cee",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
@@ -460,9 +460,9 @@ def bench_pipeline(args, torch, dspark, device):
 # 1024 SIMDs), the MfmaUtil expression of rocprofiler's counter definitions). A figure holds
 # only for the kernel sources it was measured with.
 MEASURED_MFMA_BUSY = dict(
-    util={64: 7.32, 256: 13.67, 512: 15.86, 1024: 17.29},
+    util={64: 7.58, 256: 13.78, 512: 15.87, 1024: 17.26},
     profile="profiles/draft_slab_resident_mfma_sweep_V151936.md",
-    sources={"draft_slab.hip": "b39c35f224a72a72405e8efbf383dfcaefb19a0c49feb233e055f10e86f362ac",
+    sources={"draft_slab.hip": "19be639ac5edace8d1f3be5b5077b08e21960b1cead6f4683dc6d9ecc1157cee",
              "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
              "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
              "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"})
