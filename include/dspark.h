@@ -15,7 +15,9 @@
  *            the caller's workspace `ws` of at least `dspark_*_workspace_bytes(...)` bytes
  *            (256-byte aligned, as the HIP allocator returns). Its contents need no
  *            preparation; a call owns it until the call's work on `stream` has finished, so
- *            calls that may overlap need distinct workspaces.
+ *            calls that may overlap need distinct workspaces. (The one-launch draft forms
+ *            keep a call counter in the workspace and reset their own position slots
+ *            inside the launch; any bytes, including those of other calls, are accepted.)
  * Streams    `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue work and
  *            return without synchronising. Calls on distinct workspaces may run concurrently;
  *            the library keeps no mutable global state.
