@@ -186,6 +186,18 @@ __device__ __forceinline__ void verify_chunks_body(const RowSet& rs, int nch, co
         }
         return;
     }
+    // the acceptance test's inputs do not depend on the normalisers: wave 0 loads the drafted
+    // tokens, their uniforms and the two logits at each token before the merges below
+    int xk = 0;
+    float ltx = 0.0f, ldx = 0.0f, ua = 0.0f;
+    if (wave == 0 && lane < q.ell) {
+        xk = x[static_cast<long long>(b) * G + lane];
+        ua = u_acc[static_cast<long long>(b) * G + lane];
+        if (xk >= 0 && xk < V) {
+            ltx = rs.Lt[(q.off + lane) * V + xk];
+            ldx = rs.Ld[(static_cast<long long>(b) * G + lane) * V + xk];
+        }
+    }
     // normalisers of the verified rows: each wave merges the partials of some rows
     for (int slot = wave; slot <= q.ell; slot += kWaves) {
         const float v = merge_lse_wave(slot_part(part, b, slot, G, nch), nch);
@@ -206,12 +218,9 @@ __device__ __forceinline__ void verify_chunks_body(const RowSet& rs, int nch, co
         bool bad = false, rej = false;
         const int k = lane;
         if (k < q.ell) {
-            const int xk = x[static_cast<long long>(b) * G + k];
             if (xk < 0 || xk >= V) {
                 bad = true;
             } else {
-                const float ltx = rs.Lt[(q.off + k) * V + xk];
-                const float ldx = rs.Ld[(static_cast<long long>(b) * G + k) * V + xk];
                 const float lst = s_lt[k], lsd = s_ld[k];
                 const float lpt = (lst == -INFINITY) ? -INFINITY : ltx - lst;
                 const float lpd = (lsd == -INFINITY) ? -INFINITY : ldx - lsd;
@@ -219,7 +228,7 @@ __device__ __forceinline__ void verify_chunks_body(const RowSet& rs, int nch, co
                 if (lpd == -INFINITY)
                     acc = lpt > -INFINITY;
                 else
-                    acc = logf(clamp_uniform(u_acc[static_cast<long long>(b) * G + k])) < lpt - lpd;
+                    acc = logf(clamp_uniform(ua)) < lpt - lpd;
                 rej = !acc;
             }
         }
