@@ -64,9 +64,9 @@ MEASURED_TRAFFIC = {
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the three kernels of one dspark_verify_tv call (row_stats, verify_tv_chunks, verify_tv_select)
     ("verify", "dspark_verify_tv"): dict(
-        bytes=10478293721.4,
+        bytes=10478320250.1,
         profile="profiles/verify_tv_verify_B256_V151936.md",
-        sources={"verify.hip": "36a56d19c9cb663d607706df4e3a76946999880c0133d6dc26d0e8f086c4e270",
+        sources={"verify.hip": "8c348ebe8b99160c5e819edfd8e793181a70e5e6a7593a08dba8c5ae0d5df81f",
                  "rows.h": "069e0045b9a59c15697218de2708ffbdb33de09773099a9e0e95cad34229983b",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
