@@ -405,3 +405,44 @@ def test_single_request_graph_replays(gpu):
         for k in ("x", "q", "lse", "L"):
             assert np.array_equal(host(out[k]).view(np.uint8), ref[k].view(np.uint8)), (rep, k)
         run_draft(od)                                        # another shape between replays
+
+
+def _random_shapes(n, seed):
+    """Draft shapes drawn from a fixed seed within the slab and resident paths' caps: B = 1
+    (resident) or 9..96 (slab), V a multiple of 8 from 1024 to 163840, r a multiple of 8 up
+    to 256, gamma 1..20; the batch kept small enough for the oracle."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = 1 if g.random() < 0.3 else int(g.integers(9, 97))
+        V = int(g.integers(128, 20481)) * 8
+        r = int(g.integers(1, 33)) * 8
+        G = int(g.integers(1, 21))
+        out.append((B, V, r, G))
+    return out
+
+
+@pytest.mark.parametrize("B,V,r,G", _random_shapes(10, 2026))
+def test_random_shapes_all_forms(gpu, B, V, r, G):
+    """Seeded random shapes: the default form (one launch where it fits) with and without
+    the logits, and the per-position form, each against the oracle on sampled requests;
+    on the slab path the forms agree bit for bit."""
+    c = synth.custom(1000 + B + G, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    W1, W2 = dev(d["W1"]), dev(d["W2"])
+    path = dspark.markov_draft_path(B, W1, W2)
+    assert path == ("resident" if B == 1 else "slab")
+    a = run_draft(d, want_logits=True)
+    b = run_draft(d, want_logits=False)
+    p = run_draft(d, want_logits=True, per_position=True)
+    reqs = sorted({0, B // 2, B - 1})
+    for o in (a, p):
+        rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", o["x"], o["q"], o["lse"],
+                          reqs, gL=o["L"])
+        assert rep.ties <= 1
+    for k in ("x", "q", "lse"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+        if path == "slab":
+            assert np.array_equal(a[k].view(np.uint8), p[k].view(np.uint8)), k
+    if path == "slab":
+        assert np.array_equal(a["L"].view(np.uint8), p["L"].view(np.uint8))
