@@ -198,3 +198,34 @@ def test_lossless_first_token_chi2(gpu):
     assert np.all(host(res["n"]) >= 0)
     counts = np.bincount(y[:, 0], minlength=V).astype(float)
     assert _chi2_pvalue(counts, P[3], N) > 1e-3
+
+
+def _random_shapes(n, seed):
+    """Verify shapes drawn from a fixed seed within the entry point's caps: B 9..96 (the slab
+    draft, whose logits the rebuild reproduces bit for bit), V a multiple of 8 from 1024 to
+    163840, r a multiple of 8 up to 256, gamma 1..20, flattened or padded target rows."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(g.integers(9, 97))
+        V = int(g.integers(128, 20481)) * 8
+        r = int(g.integers(1, 33)) * 8
+        G = int(g.integers(1, 21))
+        out.append((B, V, r, G, bool(g.random() < 0.7)))
+    return out
+
+
+@pytest.mark.parametrize("B,V,r,G,flat", _random_shapes(8, 2027))
+def test_random_shapes(gpu, B, V, r, G, flat):
+    """Seeded random shapes and verify lengths: the rebuilt-logit verify against the verify
+    on the draft's own logits, and sampled requests against the oracle."""
+    c = synth.custom(1100 + B + G, B=B, V=V, r=r, gamma=G, w_dtype="bf16", w_sigma=0.3,
+                     tnoise=0.7)
+    g = np.random.default_rng(V + r)
+    lengths = g.integers(0, G + 1, size=B) if flat else None
+    if flat:
+        lengths[0], lengths[-1] = 0, G
+    inp = _inputs(c, lengths, flat)
+    D, A, M = _run(inp)
+    _compare(inp, D, A, M, B, G)
+    _oracle_check(inp, D, M, sorted({1, B // 2, B - 1}), G)
