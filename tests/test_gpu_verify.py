@@ -306,3 +306,46 @@ def test_tv_two_point_closed_form(gpu):
     inp = dict(Ld=Ld, Lt=Lt, t_off=None, length=None)
     cs = run_tv(inp)
     np.testing.assert_allclose(cs[:, 0], 1 - np.abs(qs - ss), atol=1e-6)
+
+
+def _random_shapes(n, seed):
+    """Verify shapes drawn from a fixed seed: V from 2 to 200000 (any residue mod 4), gamma
+    1..20, B up to 64 with B * gamma * V kept under 4e7 logits, flattened or padded target
+    rows, draft normalisers supplied or computed."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        V = int(np.exp(g.uniform(np.log(2), np.log(200000))))
+        G = int(g.integers(1, 21))
+        B = int(g.integers(1, max(2, min(64, 40_000_000 // (G * V)) + 1)))
+        out.append((B, V, G, bool(g.random() < 0.7), bool(g.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("B,V,G,flat,given", _random_shapes(10, 2028))
+def test_random_shapes(gpu, B, V, G, flat, given):
+    """Seeded random shapes and verify lengths: dspark_verify_tv bit for bit against
+    dspark_verify then dspark_tv_labels, and sampled requests against the oracle."""
+    c = synth.custom(1200 + V % 97, B=B, V=V, r=1, gamma=G, w_dtype="f32", tnoise=0.8)
+    g = np.random.default_rng(V + G)
+    lengths = g.integers(0, G + 1, size=B) if flat else None
+    if flat:
+        lengths[0] = G
+    inp = verify_inputs(c, lengths, flat)
+    ld_lse = None
+    if given:
+        ld_lse = dev(np.array([[oracle.softmax_row(inp["Ld"][i, k])[1] for k in range(G)]
+                               for i in range(B)], np.float32))
+    a = run_verify(inp, want_lse=True, ld_lse=ld_lse)
+    tv = run_tv(inp, lse_d=ld_lse if given else dev(a["lse_d"]), lse_t=dev(a["lse_t"]))
+    f = run_verify_tv(inp, ld_lse=ld_lse)
+    for k in ("n", "y", "lse_d", "lse_t"):
+        assert np.array_equal(a[k].view(np.uint8), f[k].view(np.uint8)), k
+    assert np.array_equal(np.isnan(tv), np.isnan(f["cstar"]))
+    fin = ~np.isnan(tv)
+    assert np.array_equal(tv[fin].view(np.uint8), f["cstar"][fin].view(np.uint8))
+    reqs = sorted({0, B // 2, B - 1})
+    rep = check_verify(inp["Ld"], inp["Lt"], inp["x"], inp["u_acc"], inp["u_fin"], inp["t_off"],
+                       inp["length"], f["n"], f["y"], reqs)
+    assert rep.accept_ties + rep.final_ties <= 1
+    check_tv(inp, f["cstar"], reqs)
