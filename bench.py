@@ -25,14 +25,16 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import synth  # noqa: E402  (seeded inputs only)
+
 METRIC = "Markov-head draft tokens/s + verified tokens/s at V=151936; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
-    "single": 2,   # single-request draft, B=1, V=151936, r=256, gamma=7 (the headline line)
-    "batched": 3,  # batched draft, B=64, V=151936, gamma=16
-    "verify": 4,   # batched verify + TV labels, B=256, V=151936, gamma=16
-    "round": 5,    # full round, B=512, V=129280, gamma=16
+    "single": synth.SINGLE,   # single-request draft, B=1, V=151936, r=256, gamma=7 (the headline line)
+    "batched": synth.BATCHED,  # batched draft, B=64, V=151936, gamma=16
+    "verify": synth.VERIFY,   # batched verify + TV labels, B=256, V=151936, gamma=16
+    "round": synth.ROUND,    # full round, B=512, V=129280, gamma=16
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
@@ -120,9 +122,9 @@ def parse():
     return ap.parse_args()
 
 
-def build_inputs(cfg: int):
+def build_inputs(seed: int):
     import synth
-    c = synth.config(cfg)
+    c = synth.config(seed)
     base = [synth.base_rows(c, b) for b in range(c.B)]
     U = np.stack([r[: c.gamma] for r in base])
     Lt = np.stack([synth.target_rows(c, b, base[b]) for b in range(c.B)]).reshape(-1, c.V)
@@ -477,7 +479,7 @@ def bench_mfma(args, torch, dspark, device):
     min(bf16 peak, intensity x 8 TB/s). Factors as the batched workload; U ~ N(0, 3^2),
     tokens and uniforms drawn on the device from a fixed seed."""
     import synth
-    c = synth.config(3)
+    c = synth.config(synth.BATCHED)
     w1, w2 = synth.factors(c)
     W1, W2 = to_dev(w1, torch, device), to_dev(w2, torch, device)
     V, r, G = c.V, c.r, c.gamma
@@ -560,9 +562,9 @@ def main():
         return bench_pipeline(args, torch, dspark, device)
     if args.workload == "mfma":
         return bench_mfma(args, torch, dspark, device)
-    cfg = WORKLOADS[args.workload]
+    seed = WORKLOADS[args.workload]
     verify_only = args.workload == "verify"
-    c, inp = build_inputs(cfg)
+    c, inp = build_inputs(seed)
     t = {k: to_dev(v, torch, device) for k, v in inp.items()}
     B, G, V = c.B, c.gamma, c.V
     Bmax = 4096

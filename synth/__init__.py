@@ -5,24 +5,25 @@ method's arithmetic (no softmax, no sampling, no acceptance test, no scheduling)
 so both the fp64 oracle and the HIP library can be fed from it without sharing
 any of the computation they are compared on.
 
-Every stream is ``numpy.random.Generator(PCG64(SeedSequence([cfg, tensor, *extra])))``.
+Every stream is ``numpy.random.Generator(PCG64(SeedSequence([seed, tensor, *extra])))``,
+where ``seed`` is the workload's seed id.
 Large per-request tensors use ``extra = [b]`` so one request's rows can be
 regenerated alone (the oracle checks sampled requests at full size that way).
 
-Shapes and distributions follow the five workloads of the hot path:
+Shapes and distributions follow the five workloads of the hot path (seed ids 1 .. 5):
 
-* cfg 1 - B=4, V=1024, r=32, gamma=4, fp32 factors. U ~ N(0, 2^2), W1, W2 ~ N(0, 0.05^2),
+* TINY - B=4, V=1024, r=32, gamma=4, fp32 factors. U ~ N(0, 2^2), W1, W2 ~ N(0, 0.05^2),
   target noise sigma = 0.5.
-* cfg 2 - B=1, V=151936, r=256, gamma=7, bf16 factors ~ N(0, 0.02^2); U ~ N(0, 3^2) with
+* SINGLE - B=1, V=151936, r=256, gamma=7, bf16 factors ~ N(0, 0.02^2); U ~ N(0, 3^2) with
   32 distinct ids per row raised by +8.
-* cfg 3 - as cfg 2 with B=64, gamma=16.
-* cfg 4 - verify only: B=256, gamma=16, V=151936; draft logits as cfg 2's U; target =
+* BATCHED - as SINGLE with B=64, gamma=16.
+* VERIFY - verify only: B=256, gamma=16, V=151936; draft logits as SINGLE's U; target =
   draft + N(0, sigma_k^2) with sigma_k from ``tests/golden/target_sigma.json``.
-* cfg 5 - full round: R=B=512, gamma=16, V=129280, r=256, bf16; confidences
+* ROUND - full round: R=B=512, gamma=16, V=129280, r=256, bf16; confidences
   Beta(8,2) * 0.97^k, temperatures 0.8 .. 1.5, SPS(B) = 1/(0.02 + 1e-5 B), Bmax=4096.
 
 The base-logit rows of a request are ``gamma + 1`` rows: the first ``gamma`` are the
-draft's U_k (cfg 4: the draft logits L_d), the last is the extra row the target
+draft's U_k (VERIFY: the draft logits L_d), the last is the extra row the target
 needs at the bonus position. Target rows are base rows plus position noise.
 """
 from __future__ import annotations
@@ -42,8 +43,8 @@ _SIGMA_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__fil
                            "tests", "golden", "target_sigma.json")
 
 
-def rng(cfg: int, tensor: int, *extra: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, tensor, *extra])))
+def rng(seed: int, tensor: int, *extra: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor, *extra])))
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -61,7 +62,7 @@ def uniforms(g: np.random.Generator, shape) -> np.ndarray:
 
 @dataclass(frozen=True)
 class Config:
-    cfg: int
+    seed: int
     name: str
     B: int
     V: int
@@ -88,34 +89,38 @@ def _sigma_table(V: int, gamma: int) -> tuple:
     return tuple(s + [s[-1]])
 
 
-def config(cfg: int) -> Config:
-    if cfg == 1:
+# seed ids of the five named workloads
+TINY, SINGLE, BATCHED, VERIFY, ROUND = 1, 2, 3, 4, 5
+
+
+def config(seed: int) -> Config:
+    if seed == TINY:
         return Config(1, "tiny fp32 full round", B=4, V=1024, r=32, gamma=4, w_dtype="f32",
                       u_sigma=2.0, w_sigma=0.05, tnoise=(0.5,) * 5)
-    if cfg == 2:
+    if seed == SINGLE:
         return Config(2, "single-request draft", B=1, V=151936, r=256, gamma=7, w_dtype="bf16",
                       u_sigma=3.0, w_sigma=0.02, boost_ids=32, boost_val=8.0,
                       tnoise=(0.5,) * 8)
-    if cfg == 3:
+    if seed == BATCHED:
         return Config(3, "batched draft", B=64, V=151936, r=256, gamma=16, w_dtype="bf16",
                       u_sigma=3.0, w_sigma=0.02, boost_ids=32, boost_val=8.0,
                       tnoise=(0.5,) * 17)
-    if cfg == 4:
+    if seed == VERIFY:
         return Config(4, "batched verify", B=256, V=151936, r=256, gamma=16, w_dtype="bf16",
                       u_sigma=3.0, w_sigma=0.02, boost_ids=32, boost_val=8.0,
                       tnoise=_sigma_table(151936, 16))
-    if cfg == 5:
+    if seed == ROUND:
         return Config(5, "full round with scheduler", B=512, V=129280, r=256, gamma=16,
                       w_dtype="bf16", u_sigma=3.0, w_sigma=0.02, boost_ids=32, boost_val=8.0,
                       tnoise=_sigma_table(129280, 16))
-    raise ValueError(f"unknown cfg {cfg}")
+    raise ValueError(f"unknown workload seed id {seed}")
 
 
-def custom(cfg: int, B: int, V: int, r: int, gamma: int, w_dtype: str = "bf16",
+def custom(seed: int, B: int, V: int, r: int, gamma: int, w_dtype: str = "bf16",
            u_sigma: float = 3.0, w_sigma: float = 0.02, boost_ids: int = 32,
            boost_val: float = 8.0, tnoise: float = 0.5) -> Config:
-    """A workload of any shape with the cfg 2 value recipe (used for ragged / edge sizes)."""
-    return Config(cfg, f"custom B={B} V={V} r={r} gamma={gamma}", B=B, V=V, r=r, gamma=gamma,
+    """A workload of any shape with the SINGLE value recipe (used for ragged / edge sizes)."""
+    return Config(seed, f"custom B={B} V={V} r={r} gamma={gamma}", B=B, V=V, r=r, gamma=gamma,
                   w_dtype=w_dtype, u_sigma=u_sigma, w_sigma=w_sigma,
                   boost_ids=min(boost_ids, V), boost_val=boost_val,
                   tnoise=(tnoise,) * (gamma + 1))
@@ -124,8 +129,8 @@ def custom(cfg: int, B: int, V: int, r: int, gamma: int, w_dtype: str = "bf16",
 # ----------------------------------------------------------------------------- factors
 def factors(c: Config):
     """W1 [V][r] and W2 [r][V]: float32 arrays for f32, uint16 bf16 bit patterns for bf16."""
-    w1 = rng(c.cfg, T_W1).standard_normal((c.V, c.r), dtype=np.float32) * np.float32(c.w_sigma)
-    w2 = rng(c.cfg, T_W2).standard_normal((c.r, c.V), dtype=np.float32) * np.float32(c.w_sigma)
+    w1 = rng(c.seed, T_W1).standard_normal((c.V, c.r), dtype=np.float32) * np.float32(c.w_sigma)
+    w2 = rng(c.seed, T_W2).standard_normal((c.r, c.V), dtype=np.float32) * np.float32(c.w_sigma)
     if c.w_dtype == "bf16":
         return f32_to_bf16_bits(w1), f32_to_bf16_bits(w2)
     return np.ascontiguousarray(w1), np.ascontiguousarray(w2)
@@ -135,9 +140,9 @@ def factors(c: Config):
 def base_rows(c: Config, b: int) -> np.ndarray:
     """Request b's gamma+1 base-logit rows, float32 [gamma+1][V]."""
     n = c.gamma + 1
-    rows = rng(c.cfg, T_U, b).standard_normal((n, c.V), dtype=np.float32) * np.float32(c.u_sigma)
+    rows = rng(c.seed, T_U, b).standard_normal((n, c.V), dtype=np.float32) * np.float32(c.u_sigma)
     if c.boost_ids:
-        g = rng(c.cfg, T_BOOST, b)
+        g = rng(c.seed, T_BOOST, b)
         for k in range(n):
             ids = g.choice(c.V, size=c.boost_ids, replace=False)
             rows[k, ids] += np.float32(c.boost_val)
@@ -149,7 +154,7 @@ def target_rows(c: Config, b: int, base: np.ndarray | None = None) -> np.ndarray
     if base is None:
         base = base_rows(c, b)
     n = c.gamma + 1
-    z = rng(c.cfg, T_TNOISE, b).standard_normal((n, c.V), dtype=np.float32)
+    z = rng(c.seed, T_TNOISE, b).standard_normal((n, c.V), dtype=np.float32)
     sig = np.asarray(c.tnoise[:n], dtype=np.float32)[:, None]
     return (base + z * sig).astype(np.float32)
 
@@ -174,21 +179,21 @@ def target_padded_all(c: Config, requests=None) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- small tensors
 def x0(c: Config) -> np.ndarray:
-    return rng(c.cfg, T_X0).integers(0, c.V, size=c.B, dtype=np.int64).astype(np.int32)
+    return rng(c.seed, T_X0).integers(0, c.V, size=c.B, dtype=np.int64).astype(np.int32)
 
 
 def draft_uniforms(c: Config) -> np.ndarray:
-    return uniforms(rng(c.cfg, T_UDRAFT), (c.B, c.gamma))
+    return uniforms(rng(c.seed, T_UDRAFT), (c.B, c.gamma))
 
 
 def verify_uniforms(c: Config):
     """(u_acc [B][gamma], u_fin [B]) fp32."""
-    return uniforms(rng(c.cfg, T_UACC), (c.B, c.gamma)), uniforms(rng(c.cfg, T_UFIN), (c.B,))
+    return uniforms(rng(c.seed, T_UACC), (c.B, c.gamma)), uniforms(rng(c.seed, T_UFIN), (c.B,))
 
 
 def token_uniforms(c: Config) -> np.ndarray:
-    """Uniforms used to draw cfg 4's draft tokens from p_d."""
-    return uniforms(rng(c.cfg, T_UX), (c.B, c.gamma))
+    """Uniforms used to draw the VERIFY workload's draft tokens from p_d."""
+    return uniforms(rng(c.seed, T_UX), (c.B, c.gamma))
 
 
 def draft_inputs(c: Config) -> dict:
@@ -199,7 +204,7 @@ def draft_inputs(c: Config) -> dict:
 # ----------------------------------------------------------------------------- scheduler
 def confidences(c: Config) -> np.ndarray:
     """c_{r,k} = Beta(8,2) * 0.97^k, k = 1..gamma, float32 [R][gamma]."""
-    g = rng(c.cfg, T_CONF)
+    g = rng(c.seed, T_CONF)
     base = g.beta(8.0, 2.0, size=(c.B, c.gamma))
     decay = 0.97 ** np.arange(1, c.gamma + 1)
     return (base * decay[None, :]).astype(np.float32)

@@ -36,7 +36,7 @@ def targets():
 def _rows(V):
     c = synth.custom(CAL_CFG[V], B=ROWS, V=V, r=1, gamma=0)
     base = np.stack([synth.base_rows(c, b)[0] for b in range(ROWS)])
-    z = np.stack([synth.rng(c.cfg, synth.T_TNOISE, b).standard_normal(V, dtype=np.float32)
+    z = np.stack([synth.rng(c.seed, synth.T_TNOISE, b).standard_normal(V, dtype=np.float32)
                   for b in range(ROWS)])
     return base, z
 
@@ -67,7 +67,7 @@ def main():
     out = dict(
         sigma=sig,
         target_mean_cstar=targets(),
-        calibration=f"{ROWS} rows per vocabulary, synth.custom(cfg={CAL_CFG}), "
+        calibration=f"{ROWS} rows per vocabulary, synth.custom(seed={CAL_CFG}), "
                     "bisection in log sigma, 24 steps",
         written_by="tests/golden/make_target_sigma.py (oracle.tv_row_pair only)",
     )

@@ -19,8 +19,8 @@ def run_draft(d, want_logits=True, per_position=False):
     return {k: (host(v) if v is not None else None) for k, v in out.items()}
 
 
-def test_cfg1_tiny_fp32_exact(gpu):
-    c = synth.config(1)
+def test_tiny_fp32_exact(gpu):
+    c = synth.config(synth.TINY)
     d = synth.draft_inputs(c)
     g = run_draft(d)
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], c.w_dtype, g["x"], g["q"],
@@ -272,8 +272,8 @@ def test_permutation_chain_closed_form(gpu):
             assert out["x"][b, k] == prev
 
 
-def test_cfg2_single_request_full(gpu):
-    c = synth.config(2)
+def test_single_request_full(gpu):
+    c = synth.config(synth.SINGLE)
     d = synth.draft_inputs(c)
     g = run_draft(d)
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], c.w_dtype, g["x"], g["q"],
@@ -282,8 +282,8 @@ def test_cfg2_single_request_full(gpu):
     assert rep.ties <= 1
 
 
-def test_cfg3_batched_sampled(gpu):
-    c = synth.config(3)
+def test_batched_draft_sampled(gpu):
+    c = synth.config(synth.BATCHED)
     d = synth.draft_inputs(c)
     g = run_draft(d)
     reqs = [0, 1, 17, 31, 32, 50, 63]

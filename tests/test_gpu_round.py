@@ -66,8 +66,8 @@ def _oracle_round_check(c, inp, g, requests):
     return rep
 
 
-def test_cfg1_round_exact(gpu):
-    c = synth.config(1)
+def test_tiny_round_exact(gpu):
+    c = synth.config(synth.TINY)
     inp = _round_inputs(c)
     inp["sps"] = synth.sps_table(64, b=1e-3)
     g = _gpu_round(c, inp, Bmax=64)
@@ -88,8 +88,8 @@ def test_cfg1_round_exact(gpu):
     assert np.max(np.abs(g["cstar"][fin] - oc[fin])) < PROB_TOL
 
 
-def test_cfg5_round_sampled(gpu):
-    c = synth.config(5)
+def test_round_workload_sampled(gpu):
+    c = synth.config(synth.ROUND)
     inp = _round_inputs(c)
     g = _gpu_round(c, inp)
     assert g["K"] == c.B + int(g["len"].sum())

@@ -28,8 +28,8 @@ def _check(conf, temp, sps, Bmax, mode):
 
 @pytest.mark.parametrize("mode", [oracle.GLOBAL, oracle.EARLY_STOP])
 @pytest.mark.parametrize("step", [0, 256])
-def test_cfg5_full(gpu, mode, step):
-    c = synth.config(5)
+def test_round_workload_full(gpu, mode, step):
+    c = synth.config(synth.ROUND)
     conf, temp, sps = synth.confidences(c), synth.temperatures(c.gamma), synth.sps_table(4096, step=step)
     g, ref = _check(conf, temp, sps, 4096, mode)
     assert np.array_equal(g["len"], ref["len"]) and g["K"][0] == ref["K"]
@@ -100,7 +100,7 @@ def test_out_of_range_inputs(gpu):
 
 
 def test_determinism(gpu):
-    c = synth.config(5)
+    c = synth.config(synth.ROUND)
     conf, temp, sps = synth.confidences(c), synth.temperatures(16), synth.sps_table(4096)
     a = run_schedule(conf, temp, sps, 4096, oracle.GLOBAL)
     b = run_schedule(conf, temp, sps, 4096, oracle.GLOBAL)

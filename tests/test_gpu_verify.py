@@ -178,8 +178,8 @@ def test_device_data_faults(gpu):
     assert out["n"][2] == -1 and out["n"][3] == -1
 
 
-def test_cfg4_batched_sampled(gpu):
-    c = synth.config(4)
+def test_batched_verify_sampled(gpu):
+    c = synth.config(synth.VERIFY)
     inp = verify_inputs(c)
     out = run_verify(inp, want_lse=True)
     reqs = [0, 3, 100, 128, 200, 255]

@@ -148,11 +148,11 @@ def test_faulty_requests(gpu):
         assert 0 <= n[b] <= G and np.all(np.isfinite(cs[b]))
 
 
-def test_cfg5_round_rebuilt_logits(gpu):
-    """The full cfg 5 round with the draft's logits never written: draft -> schedule ->
+def test_round_rebuilt_logits(gpu):
+    """The full round workload (B=512, V=129280, gamma=16) with the draft's logits never written: draft -> schedule ->
     verify_markov, against the same round verified on materialised logits, and sampled
     requests against the oracle."""
-    c = synth.config(5)
+    c = synth.config(synth.ROUND)
     base = [synth.base_rows(c, b) for b in range(c.B)]
     U = np.stack([r_[: c.gamma] for r_ in base])
     Lt_pad = np.stack([synth.target_rows(c, b, base[b]) for b in range(c.B)])

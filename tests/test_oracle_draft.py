@@ -113,7 +113,7 @@ def test_dominant_logit_wins_every_uniform():
 
 
 def test_lse_matches_scipy_and_q_is_a_probability():
-    c = synth.config(1)
+    c = synth.config(synth.TINY)
     d = synth.draft_inputs(c)
     out = oracle.markov_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], want_logits=True)
     L = out["L"]
