@@ -106,3 +106,35 @@ def test_determinism(gpu):
     b = run_schedule(conf, temp, sps, 4096, oracle.GLOBAL)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def _random_shapes(n, seed):
+    """Scheduler shapes drawn from a fixed seed within the caps: R * gamma up to 16384,
+    Bmax from R to past R * (gamma + 1), temperatures given or not, smooth or step SPS."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        G = int(g.integers(1, 65))
+        R = int(g.integers(1, 16384 // G + 1))
+        Bmax = int(g.integers(R, R * (G + 1) + 64))
+        out.append((R, G, Bmax, bool(g.random() < 0.5), int(g.integers(0, 3))))
+    return out
+
+
+@pytest.mark.parametrize("R,G,Bmax,with_temp,sps_kind", _random_shapes(10, 2029))
+def test_random_shapes(gpu, R, G, Bmax, with_temp, sps_kind):
+    """Seeded random shapes, confidences with zeros and ones mixed in, against the oracle in
+    both modes."""
+    g = np.random.default_rng(R * 131 + G)
+    conf = g.beta(4.0, 1.5, size=(R, G)).astype(np.float32)
+    conf[g.random((R, G)) < 0.05] = 0.0
+    conf[g.random((R, G)) < 0.05] = 1.0
+    temp = (0.6 + g.random(G)).astype(np.float32) if with_temp else None
+    if sps_kind == 0:
+        sps = synth.sps_table(Bmax, b=float(g.uniform(1e-6, 1e-4)))
+    elif sps_kind == 1:
+        sps = synth.sps_table(Bmax, b=float(g.uniform(1e-6, 1e-4)), step=int(g.integers(2, 513)))
+    else:
+        sps = np.sort(g.random(Bmax + 1))[::-1].astype(np.float32)
+    for mode in (oracle.GLOBAL, oracle.EARLY_STOP):
+        _check(conf, temp, sps, Bmax, mode)
