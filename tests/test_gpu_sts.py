@@ -101,3 +101,29 @@ def test_fit_on_verify_results(gpu):
     conf = synth.confidences(synth.custom(891, B=c.B, V=8, r=1, gamma=c.gamma))
     grid = np.linspace(0.25, 4.0, 31).astype(np.float32)
     check(conf, n_acc, length, grid, 15, sts.NLL)
+
+
+def _random_shapes(n, seed):
+    """STS shapes drawn from a fixed seed within the caps: N 1..70000, gamma 1..64 with
+    N * gamma kept under 1.2e6 for the oracle, 1..64 grid values, 1..16 bins, either
+    objective, full or partial verify lengths."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        G = int(g.integers(1, 65))
+        N = int(g.integers(1, min(70000, 1_200_000 // G) + 1))
+        out.append((N, G, int(g.integers(1, 65)), int(g.integers(1, 17)),
+                    [sts.NLL, sts.ECE][int(g.integers(0, 2))], bool(g.random() < 0.6)))
+    return out
+
+
+@pytest.mark.parametrize("N,G,nT,bins,objective,partial", _random_shapes(8, 2030))
+def test_random_shapes(gpu, N, G, nT, bins, objective, partial):
+    """Seeded random shapes and grids (sorted or not) against the oracle."""
+    g = np.random.default_rng(N + G)
+    T_true = g.uniform(0.5, 2.5, G)
+    conf, n_acc, length = validation_set(900 + N + G, N, G, T_true, partial)
+    grid = g.uniform(0.2, 3.5, nT).astype(np.float32)
+    if g.random() < 0.5:
+        grid = np.sort(grid)
+    check(conf, n_acc, length if partial else None, grid, bins, objective)
