@@ -19,13 +19,24 @@ Pages cited (titles as published):
 
 Functions and what pins them (all pins live in ``tests/test_oracle_*.py``):
 
+* ``inverse_cdf``, ``clamp_uniform`` - the one-uniform draw from a law in token-id order
+  (the reading for how [P3] "Semi-Autoregressive Generation"'s sample is drawn) and the
+  clamp of a host uniform into [0, 1 - 2^-24] (NaN counts as 0). Pinned by laws with exact
+  dyadic cumulative sums (boundaries, zero-mass tokens, the past-the-end fallback, an empty
+  law), a brute force in exact rationals, fixed clamp values, and planted mistakes that
+  those pins catch.
+
 * ``markov_draft`` - [P3] "Semi-Autoregressive Generation" (p_k formula, Markov bias
   B = W1[x_{k-1}] W2). Pinned by rational-weight distributions with integer CDFs, a
   one-hot Markov bias with exact expected tokens, a permutation chain, a dominant logit,
-  logsumexp against scipy and a chi-squared test of the sampler.
+  logsumexp against scipy and a chi-squared test of the sampler. Its ``forced`` option
+  (the conditional laws along a given block) is pinned by the permutation chain on an
+  arbitrary block and by equality with the plain draft on its own draws.
 * ``verify`` - [P1] "大模型推理的显存瓶颈与推测解码的演进逻辑" (rejection sampling) and [P3]
   intro (longest prefix + bonus). Pinned by p_d = p_t, zero target mass on a draft token,
-  len = 0, and chi-squared losslessness (single position and multi-round joint).
+  len = 0, and chi-squared losslessness (single position and multi-round joint). Its
+  ``n_forced`` option and ``ratio`` output are pinned by two-point laws with exact ratios,
+  residuals and bonus draws.
 * ``tv_labels`` - [P3] "Confidence-Scheduled Verification" (c* = 1 - 1/2 ||p_d - p_t||_1).
   Pinned by exact rational arithmetic, the two-point closed form, identical and disjoint
   rows, and the Monte-Carlo acceptance rate of ``verify``.

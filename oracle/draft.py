@@ -18,7 +18,8 @@ import numpy as np
 from .numerics import clamp_uniform, decode_factor, inverse_cdf, softmax_row
 
 
-def markov_draft(U, W1, W2, x0, u, w_dtype: str = "f32", requests=None, want_logits=False):
+def markov_draft(U, W1, W2, x0, u, w_dtype: str = "f32", requests=None, want_logits=False,
+                 forced=None):
     """Draft gamma tokens for each request.
 
     U  [B][gamma][V] float32 base logits; W1 [V][r], W2 [r][V] (float32, or uint16 bf16
@@ -27,6 +28,12 @@ def markov_draft(U, W1, W2, x0, u, w_dtype: str = "f32", requests=None, want_log
     other rows are left at their fill values). Returns a dict with
     x [B][gamma] int64, q [B][gamma] = p_k(x_k), lse [B][gamma], and when asked,
     L [B][gamma][V] float64 logits U_k + B_k.
+
+    ``forced`` [B][gamma] (optional) evaluates the conditional laws along a given block
+    instead of the drawn one: position k + 1 conditions on forced[b, k] rather than on the
+    token drawn at position k (p_k is a law given the prefix, so this is the same
+    definition at another prefix). x still holds the draws each position makes; with
+    forced equal to those draws the result is the unforced one.
     """
     U = np.asarray(U)
     B, G, V = U.shape
@@ -58,7 +65,7 @@ def markov_draft(U, W1, W2, x0, u, w_dtype: str = "f32", requests=None, want_log
             x[b, k] = tok
             q[b, k] = p[tok] if tok >= 0 else 0.0
             lse[b, k] = row_lse
-            prev = tok
+            prev = tok if forced is None else int(forced[b, k])
     out = dict(x=x, q=q, lse=lse)
     if L is not None:
         out["L"] = L

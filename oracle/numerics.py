@@ -24,9 +24,15 @@ def decode_factor(a: np.ndarray, w_dtype: str) -> np.ndarray:
 
 
 def clamp_uniform(u) -> float:
-    """A host uniform widened to float64 and clamped into [0, 1 - 2^-24]."""
+    """A host uniform widened to float64 and clamped into [0, 1 - 2^-24].
+
+    Values below 0 (and -0.0) give +0.0, values at or above 1 - 2^-24 give 1 - 2^-24, and a
+    NaN uniform counts as 0 (the reading for a uniform that is not a number).
+    """
     u = float(np.float32(u))
-    return min(max(u, 0.0), U_MAX)
+    if not u > 0.0:                 # negative, zero of either sign, or NaN
+        return 0.0
+    return min(u, U_MAX)
 
 
 def softmax_row(l: np.ndarray):

@@ -37,17 +37,26 @@ def _probs(row, V):
     return st
 
 
-def verify(Ld, Lt, x, u_acc, u_fin, t_off=None, length=None, requests=None):
+def verify(Ld, Lt, x, u_acc, u_fin, t_off=None, length=None, requests=None, n_forced=None):
     """Verify each request's draft block.
 
     Ld [B][gamma][V] draft logits; Lt [rows][V] flattened target logits; x [B][gamma]
     draft tokens; u_acc [B][gamma]; u_fin [B]; t_off [B+1] or None (b*(gamma+1));
-    length [B] or None (gamma). Returns dict n [B] int64, y [B][gamma+1] int64 (-1 pad).
+    length [B] or None (gamma). Returns dict n [B] int64, y [B][gamma+1] int64 (-1 pad),
+    ratio [B][gamma] = min(1, p_t(x_k) / p_d(x_k)) at each verified position (the value the
+    acceptance uniform is compared with; NaN beyond the length) and law [B] (the
+    distribution the final token was drawn from; None where no draw was made).
+
+    ``n_forced`` [B] (optional) takes the accepted count as given instead of scanning
+    (each n in [0, len]), and draws the final token and forms y for that count: the same
+    residual or bonus rule, evaluated after another acceptance path.
     """
     Ld = np.asarray(Ld)
     B, G, V = Ld.shape
     n_out = np.zeros(B, dtype=np.int64)
     y_out = np.full((B, G + 1), -1, dtype=np.int64)
+    ratio = np.full((B, G), np.nan)
+    laws = [None] * B
     todo = range(B) if requests is None else requests
     for b in todo:
         ell = G if length is None else int(length[b])
@@ -56,25 +65,30 @@ def verify(Ld, Lt, x, u_acc, u_fin, t_off=None, length=None, requests=None):
         if any(not (0 <= v < V) for v in xs):
             n_out[b] = -1
             continue
+        pd = [_probs(Ld[b, k], V)[0] for k in range(ell)]      # draft law at position k+1
+        pt = [_probs(Lt[off + k], V)[0] for k in range(ell)]   # target law at position k+1
+        for k in range(ell):
+            a, t = pd[k][xs[k]], pt[k][xs[k]]
+            ratio[b, k] = min(1.0, t / a) if a > 0 else (1.0 if t > 0 else 0.0)
         n = 0
-        while n < ell:
-            pd, _ = _probs(Ld[b, n], V)
-            pt, _ = _probs(Lt[off + n], V)
-            if accept_test(clamp_uniform(u_acc[b, n]), pd[xs[n]], pt[xs[n]]):
-                n += 1
-            else:
-                break
+        while n < ell and accept_test(clamp_uniform(u_acc[b, n]), pd[n][xs[n]], pt[n][xs[n]]):
+            n += 1
+        if n_forced is not None:
+            n = int(n_forced[b])
+            if not 0 <= n <= ell:
+                raise ValueError(f"n_forced[{b}] = {n} outside [0, {ell}]")
         uf = clamp_uniform(u_fin[b])
         if n < ell:
-            pd, _ = _probs(Ld[b, n], V)
-            pt, _ = _probs(Lt[off + n], V)
-            res = np.maximum(pt - pd, 0.0)
+            res = np.maximum(pt[n] - pd[n], 0.0)
             mass = res.sum()
-            z = inverse_cdf(res / mass, uf) if mass > 0 else inverse_cdf(pt, uf)
+            law = res / mass if mass > 0 else pt[n]
+            z = inverse_cdf(law, uf)
         else:
-            pt, _ = _probs(Lt[off + ell], V)
-            z = inverse_cdf(pt, uf) if pt.sum() > 0 else -1
+            bonus, _ = _probs(Lt[off + ell], V)
+            law = bonus if bonus.sum() > 0 else None
+            z = inverse_cdf(bonus, uf) if law is not None else -1
+        laws[b] = law
         n_out[b] = n
         y_out[b, :n] = xs[:n]
         y_out[b, n] = z
-    return dict(n=n_out, y=y_out)
+    return dict(n=n_out, y=y_out, ratio=ratio, law=laws)
