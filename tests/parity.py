@@ -1,12 +1,27 @@
 """Parity checks of GPU results against the fp64 oracle (test infrastructure).
 
-The oracle always runs on the seeded inputs only (never on a GPU result). Token decisions
-must match exactly except at sampling ties: a draw whose uniform lies within TIE of a CDF
-boundary of the oracle's own distribution, or an acceptance test with |u - min(1, p_t/p_d)|
-below TIE. A request's positions after its first tie are not compared (both sides then
-condition on different tokens), and the number of such ties is bounded by the caller.
+The oracle always runs on the seeded inputs (never on a GPU result's numbers). Every
+decision the GPU made is checked on the GPU's own path (teacher forcing), so a sampling tie
+never hides the positions after it:
+
+* draft: position k's law is the oracle's law given the GPU's tokens before k
+  (``oracle.markov_draft(..., forced=gpu tokens)``); the GPU token must be the oracle's
+  inverse-CDF draw for the same uniform, or lie within TIE of a boundary of that draw's cell
+  (a tie);
+* verify: at each position the GPU accepted, the acceptance uniform must lie below the
+  oracle's ratio min(1, p_t/p_d) (or within TIE of it); at the position it rejected, at or
+  above it (or within TIE); the final token must be the oracle's draw from the residual or
+  bonus law at the GPU's accepted count (``oracle.verify(..., n_forced=...)``), or a CDF tie.
+
+Probabilities, lse and c* are compared to PROB_TOL absolute. Each check returns a report of
+what it compared, its ties and a histogram of decision margins (the distance of the uniform to
+the nearest boundary of the decision, in the oracle's fp64 arithmetic); ``record`` appends it
+as a JSON line to the file named by DSPARK_PARITY_REPORT when that is set.
 """
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 import torch
@@ -15,6 +30,10 @@ import oracle
 
 TIE = 1e-5          # CDF / acceptance-ratio margin that counts as a tie
 PROB_TOL = 1e-4     # absolute tolerance of probabilities, lse and c*
+LOGIT_TOL = 5e-4    # absolute tolerance of logits (fp32 sums of bf16 products and fp32 U)
+
+# decade edges of the margin histogram: [0, 1e-9), [1e-9, 1e-8), ..., [1e-3, 1e-2), [1e-2, inf)
+MARGIN_EDGES = [0.0] + [10.0 ** e for e in range(-9, -1)] + [np.inf]
 
 
 def dev(a: np.ndarray, device="cuda"):
@@ -28,117 +47,198 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def is_cdf_tie(p: np.ndarray, u: float, g: int, tie: float = TIE) -> bool:
-    """GPU token g is an acceptable inverse-CDF draw for u from law p within the margin."""
+def cdf_margin(p: np.ndarray, u: float, g: int) -> float:
+    """Signed distance of u to the cell of token g under law p: >= 0 when u lies in
+    [F(g-1), F(g)) (the distance to the nearer edge), < 0 outside (minus the distance to it)."""
     if not (0 <= g < p.shape[0]) or p[g] <= 0:
-        return False
+        return -np.inf
     F = np.cumsum(p)
     lo = F[g - 1] if g > 0 else 0.0
-    return lo - tie <= u < F[g] + tie
+    hi = F[g]
+    if g == p.shape[0] - 1 or not np.any(p[g + 1:] > 0):
+        hi = np.inf                   # the last positive token also owns u past the final F
+    if lo <= u < hi:
+        return float(min(u - lo, hi - u))
+    return float(-(lo - u) if u < lo else -(u - hi))
 
 
-class DraftReport:
-    def __init__(self):
-        self.compared = 0
-        self.ties = 0
-        self.skipped = 0
+def is_cdf_tie(p: np.ndarray, u: float, g: int, tie: float = TIE) -> bool:
+    """GPU token g is an acceptable inverse-CDF draw for u from law p within the margin."""
+    return cdf_margin(p, u, g) > -tie
+
+
+class Report:
+    """What a check compared: decisions, ties, margins and the largest value errors."""
+
+    def __init__(self, name: str = ""):
+        self.name = name
+        self.compared = 0            # decisions compared (draws, accept tests, final draws)
+        self.ties = 0                # decisions that differ from the oracle's, within TIE
+        self.accept_ties = 0
+        self.final_ties = 0
+        self.requests = 0
+        self.hist = np.zeros(len(MARGIN_EDGES) - 1, dtype=np.int64)
         self.max_prob_err = 0.0
         self.max_lse_err = 0.0
         self.max_logit_err = 0.0
+        self.max_cstar_err = 0.0
+
+    # back-compatible name used by older assertions
+    @property
+    def skipped(self) -> int:
+        return 0
+
+    def margin(self, m: float):
+        m = abs(m)
+        i = int(np.searchsorted(MARGIN_EDGES, m, side="right")) - 1
+        self.hist[min(max(i, 0), len(self.hist) - 1)] += 1
+
+    def as_dict(self) -> dict:
+        return dict(name=self.name, requests=self.requests, compared=self.compared,
+                    ties=self.ties, accept_ties=self.accept_ties, final_ties=self.final_ties,
+                    tie_rate=self.ties / max(self.compared, 1),
+                    margin_hist={f"<{MARGIN_EDGES[i + 1]:.0e}": int(c)
+                                 for i, c in enumerate(self.hist)},
+                    max_prob_err=self.max_prob_err, max_lse_err=self.max_lse_err,
+                    max_logit_err=self.max_logit_err, max_cstar_err=self.max_cstar_err)
+
+    def record(self):
+        d = self.as_dict()
+        print("parity", json.dumps(d))
+        path = os.environ.get("DSPARK_PARITY_REPORT")
+        if path:
+            with open(path, "a") as f:
+                f.write(json.dumps(d) + "\n")
+        return d
 
 
-def check_draft(U, W1, W2, x0, u, w_dtype, gx, gq, glse, requests, gL=None, rep=None):
-    """Compare GPU draft outputs (numpy) with the oracle request by request."""
-    rep = rep or DraftReport()
+# backward-compatible names
+DraftReport = Report
+VerifyReport = Report
+
+
+def check_draft(U, W1, W2, x0, u, w_dtype, gx, gq, glse, requests, gL=None, rep=None,
+                group: int = 8, keep_logits=None):
+    """Compare GPU draft outputs (numpy) with the oracle on the GPU's own prefix.
+
+    Every position of every listed request is compared: the oracle evaluates position k's
+    law given the GPU's tokens before it. Returns the report. ``keep_logits`` (a dict) receives
+    the oracle's fp64 logits [1][gamma][V] of each request along the GPU's block, by b."""
+    rep = rep or Report("draft")
     B, G, V = U.shape
-    for b in requests:
-        ref = oracle.markov_draft(U[b:b + 1], W1, W2, x0[b:b + 1], u[b:b + 1], w_dtype,
-                                  want_logits=True)
-        for k in range(G):
-            o, g = int(ref["x"][0, k]), int(gx[b, k])
-            if gL is not None and o >= 0:
-                err = np.max(np.abs(gL[b, k].astype(np.float64) - ref["L"][0, k]))
-                rep.max_logit_err = max(rep.max_logit_err, float(err))
-                assert err < 5e-4, f"logits b={b} k={k} err={err}"
-            if o == g:
+    reqs = list(requests)
+    for i in range(0, len(reqs), group):
+        bs = reqs[i:i + group]
+        ref = oracle.markov_draft(U[bs], W1, W2, x0[bs], u[bs], w_dtype, want_logits=True,
+                                  forced=gx[bs])
+        for j, b in enumerate(bs):
+            rep.requests += 1
+            if keep_logits is not None:
+                keep_logits[b] = ref["L"][j:j + 1]
+            for k in range(G):
+                o, g = int(ref["x"][j, k]), int(gx[b, k])
+                if o < 0:
+                    assert g == -1, f"b={b} k={k}: oracle gives no token, gpu {g}"
+                    rep.compared += 1
+                    continue
+                if gL is not None:
+                    err = float(np.max(np.abs(gL[b, k].astype(np.float64) - ref["L"][j, k])))
+                    rep.max_logit_err = max(rep.max_logit_err, err)
+                    assert err < LOGIT_TOL, f"logits b={b} k={k} err={err}"
+                p, _ = oracle.softmax_row(ref["L"][j, k])
+                uu = oracle.clamp_uniform(u[b, k])
+                m = cdf_margin(p, uu, g)
                 rep.compared += 1
-                if o >= 0:
-                    if gq is not None:
-                        e = abs(float(gq[b, k]) - ref["q"][0, k])
-                        rep.max_prob_err = max(rep.max_prob_err, e)
-                        assert e < PROB_TOL, f"q b={b} k={k}: {gq[b, k]} vs {ref['q'][0, k]}"
-                    if glse is not None:
-                        e = abs(float(glse[b, k]) - ref["lse"][0, k])
-                        rep.max_lse_err = max(rep.max_lse_err, e)
-                        assert e < PROB_TOL * max(1.0, abs(ref["lse"][0, k])), \
-                            f"lse b={b} k={k}: {glse[b, k]} vs {ref['lse'][0, k]}"
-                continue
-            p, _ = oracle.softmax_row(ref["L"][0, k])
-            uu = oracle.clamp_uniform(u[b, k])
-            assert is_cdf_tie(p, uu, g), (
-                f"draft token mismatch b={b} k={k}: gpu {g} oracle {o} u={uu} "
-                f"F(o-1..o)={np.cumsum(p)[max(o - 1, 0)]:.8f},{np.cumsum(p)[o]:.8f}")
-            rep.ties += 1
-            rep.skipped += G - k - 1
-            break
+                rep.margin(m)
+                if o != g:
+                    F = np.cumsum(p)
+                    assert m > -TIE, (
+                        f"draft token mismatch b={b} k={k}: gpu {g} oracle {o} u={uu} "
+                        f"F(o-1..o)={F[max(o - 1, 0)]:.8f},{F[o]:.8f} margin {m:.3e}")
+                    rep.ties += 1
+                if gq is not None:
+                    e = abs(float(gq[b, k]) - p[g])
+                    rep.max_prob_err = max(rep.max_prob_err, e)
+                    assert e < PROB_TOL, f"q b={b} k={k}: {gq[b, k]} vs {p[g]}"
+                if glse is not None:
+                    e = abs(float(glse[b, k]) - ref["lse"][j, k])
+                    rep.max_lse_err = max(rep.max_lse_err, e)
+                    assert e < PROB_TOL, f"lse b={b} k={k}: {glse[b, k]} vs {ref['lse'][j, k]}"
     return rep
 
 
-def oracle_final_law(Ld, Lt, b, off, n, ell):
-    """The law the final token is drawn from, after n accepted of ell verified positions."""
-    if n < ell:
-        pd = oracle.softmax_row(Ld[b, n])
-        pt = oracle.softmax_row(Lt[off + n])
-        pd = pd[0] if pd is not None else np.zeros(Ld.shape[-1])
-        pt = pt[0] if pt is not None else np.zeros(Ld.shape[-1])
-        res = np.maximum(pt - pd, 0.0)
-        return res / res.sum() if res.sum() > 0 else pt
-    st = oracle.softmax_row(Lt[off + ell])
-    return st[0] if st is not None else None
-
-
-class VerifyReport:
-    def __init__(self):
-        self.compared = 0
-        self.accept_ties = 0
-        self.final_ties = 0
+def forced_draft_logits(U, W1, W2, x0, u, w_dtype, gx, b):
+    """The oracle's fp64 draft logits [1][gamma][V] of request b along the GPU's block."""
+    ref = oracle.markov_draft(U[b:b + 1], W1, W2, x0[b:b + 1], u[b:b + 1], w_dtype,
+                              want_logits=True, forced=gx[b:b + 1])
+    return ref["L"]
 
 
 def check_verify(Ld, Lt, x, u_acc, u_fin, t_off, length, gn, gy, requests, rep=None):
-    """Compare GPU verify outputs (numpy) with the oracle, request by request."""
-    rep = rep or VerifyReport()
+    """Compare GPU verify outputs (numpy) with the oracle on the GPU's acceptance path.
+
+    Ld [B][gamma][V] are the draft logits both sides verify (the oracle's own, fp64, when
+    they come from a draft); gn, gy the GPU's accepted counts and emitted tokens."""
+    rep = rep or Report("verify")
+    B, G, V = Ld.shape
+    for b in requests:
+        rep.requests += 1
+        ell = G if length is None else int(length[b])
+        off = b * (G + 1) if t_off is None else int(t_off[b])
+        g_n = int(gn[b])
+        args = (Ld[b:b + 1], Lt, x[b:b + 1], u_acc[b:b + 1], u_fin[b:b + 1])
+        kw = dict(t_off=np.array([off, off + ell + 1]), length=np.array([ell]))
+        assert -1 <= g_n <= ell, f"b={b}: n gpu {g_n} outside [-1, {ell}]"
+        ref = oracle.verify(*args, **kw, n_forced=np.array([max(g_n, 0)]))
+        if int(ref["n"][0]) < 0 or g_n < 0:     # an invalid draft token: the -1 sentinel
+            assert int(ref["n"][0]) == g_n, f"b={b}: n gpu {g_n} oracle {int(ref['n'][0])}"
+            assert np.all(gy[b] == -1)
+            rep.compared += 1
+            continue
+        ratio = ref["ratio"][0]
+        # acceptance decisions along the GPU's path: accepted below n, rejected at n
+        for k in range(min(g_n + 1, ell)):
+            uu = oracle.clamp_uniform(u_acc[b, k])
+            m = ratio[k] - uu                 # > 0: the oracle accepts
+            rep.compared += 1
+            rep.margin(m)
+            gpu_accepts = k < g_n
+            if (m > 0) != gpu_accepts:
+                assert abs(m) < TIE, (f"b={b} k={k}: gpu {'accepts' if gpu_accepts else 'rejects'}"
+                                      f" u={uu} ratio={ratio[k]}")
+                rep.ties += 1
+                rep.accept_ties += 1
+        assert np.array_equal(gy[b, :g_n], x[b, :g_n]), f"b={b} accepted prefix"
+        assert np.all(gy[b, g_n + 1:] == -1), f"b={b} padding"
+        gz, oz = int(gy[b, g_n]), int(ref["y"][0, g_n])
+        law = ref["law"][0]
+        rep.compared += 1
+        if law is None:
+            assert gz == -1, f"b={b}: no law to draw from, gpu {gz}"
+            continue
+        m = cdf_margin(law, oracle.clamp_uniform(u_fin[b]), gz)
+        rep.margin(m)
+        if gz != oz:
+            assert m > -TIE, f"b={b}: final token gpu {gz} oracle {oz} (n={g_n}, len={ell})"
+            rep.ties += 1
+            rep.final_ties += 1
+    return rep
+
+
+def check_cstar(Ld, Lt, t_off, length, gc, requests, rep=None, tol=PROB_TOL):
+    """c* of the listed requests against the oracle's labels (NaN pattern exact)."""
     B, G, V = Ld.shape
     for b in requests:
         ell = G if length is None else int(length[b])
         off = b * (G + 1) if t_off is None else int(t_off[b])
-        ref = oracle.verify(Ld[b:b + 1], Lt, x[b:b + 1], u_acc[b:b + 1], u_fin[b:b + 1],
-                            t_off=np.array([off, off + ell + 1]), length=np.array([ell]))
-        on, g_n = int(ref["n"][0]), int(gn[b])
-        if on != g_n:
-            m = min(on, g_n)
-            assert m >= 0, f"b={b}: n gpu {g_n} oracle {on}"
-            pd = oracle.softmax_row(Ld[b, m])[0]
-            pt = oracle.softmax_row(Lt[off + m])[0]
-            xm = int(x[b, m])
-            ratio = min(1.0, pt[xm] / pd[xm]) if pd[xm] > 0 else 1.0
-            uu = oracle.clamp_uniform(u_acc[b, m])
-            assert abs(uu - ratio) < TIE, f"b={b} k={m}: accept mismatch u={uu} ratio={ratio}"
-            assert np.array_equal(gy[b, :m], ref["y"][0, :m])
-            rep.accept_ties += 1
-            continue
-        rep.compared += 1
-        if on < 0:
-            assert np.all(gy[b] == -1)
-            continue
-        assert np.array_equal(gy[b, :on], ref["y"][0, :on]), f"b={b} accepted prefix"
-        assert np.all(gy[b, on + 1:] == -1), f"b={b} padding"
-        gz, oz = int(gy[b, on]), int(ref["y"][0, on])
-        if gz != oz:
-            law = oracle_final_law(Ld, Lt, b, off, on, ell)
-            assert law is not None and is_cdf_tie(law, oracle.clamp_uniform(u_fin[b]), gz), (
-                f"b={b}: final token gpu {gz} oracle {oz} (n={on}, len={ell})")
-            rep.final_ties += 1
-    return rep
+        ref = oracle.tv_labels(Ld[b:b + 1], Lt, t_off=np.array([off, off + ell + 1]),
+                               length=np.array([ell]))[0]
+        fin = np.isfinite(ref)
+        assert np.array_equal(fin, np.isfinite(gc[b])), f"b={b} NaN pattern"
+        err = float(np.max(np.abs(gc[b][fin] - ref[fin]))) if fin.any() else 0.0
+        if rep is not None:
+            rep.max_cstar_err = max(rep.max_cstar_err, err)
+        assert err < tol, f"b={b} c* err {err}"
 
 
 def check_schedule(conf, temp, sps, Bmax, mode, glen, gK, gtheta, ga=None):
@@ -158,12 +258,18 @@ def check_schedule(conf, temp, sps, Bmax, mode, glen, gK, gtheta, ga=None):
             lo = min(n_g, ref["n"])
             assert abs(curve[lo + 1] - curve[lo]) <= 1e-6 * abs(curve[lo]), "early-stop tie"
     assert abs(float(gtheta) - curve[n_g]) <= 1e-5 * max(1.0, abs(curve[n_g]))
-    # lengths: the selected set must be a top-n set of the oracle's ranking up to ties
+    # lengths: prefix-closed by construction; the selected set must be a top-n_g set of the
+    # oracle's a-values (every selected a at least every unselected a, up to 1e-6 relative),
+    # whether or not n_g equals the oracle's n
     a = ref["a"]
     sel = np.zeros((R, G), bool)
     for r in range(R):
         assert 0 <= glen[r] <= G
         sel[r, : glen[r]] = True
+    if sel.any() and (~sel).any():
+        lo_sel, hi_uns = a[sel].min(), a[~sel].max()
+        assert lo_sel >= hi_uns - 1e-6 * max(hi_uns, 1e-300), (
+            f"lengths are not a top-{n_g} set: min selected {lo_sel} < max unselected {hi_uns}")
     if n_g == ref["n"] and not np.array_equal(glen, ref["len"]):
         ranked = ref["ranked"]
         cut_hi = -ranked[n_g - 1][0] if n_g > 0 else np.inf

@@ -7,7 +7,7 @@ import torch
 import oracle
 import synth
 import draft_sampling_verification_head_amd as dspark
-from parity import check_draft, dev, host
+from parity import Report, check_draft, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -57,10 +57,9 @@ def test_batched_mfma_shapes(gpu, B, V, r, G):
     d = synth.draft_inputs(c)
     assert dspark.markov_draft_path(B, dev(d["W1"]), dev(d["W2"])) == "mfma"
     g = run_draft(d)
-    reqs = sorted({0, 1, B // 2, B - 2, B - 1})
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
-                      reqs, gL=g["L"])
-    assert rep.ties <= 1
+                      range(B), gL=g["L"])
+    assert rep.ties <= 1 + rep.compared // 200
     assert np.all((g["x"] >= 0) & (g["x"] < V))
 
 
@@ -86,10 +85,9 @@ def test_batched_slab_shapes(gpu, B, V, r, G):
     assert dspark.markov_draft_one_launch(B, W1, W2)
     assert dspark.markov_draft_one_launch(B, W1, W2, want_logits=True)
     g = run_draft(d)
-    reqs = sorted({0, 1, B // 2, B - 2, B - 1})
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
-                      reqs, gL=g["L"])
-    assert rep.ties <= 1
+                      range(B), gL=g["L"])
+    assert rep.ties <= 1 + rep.compared // 200
     assert np.all((g["x"] >= 0) & (g["x"] < V))
     per = run_draft(d, per_position=True)
     for k in ("x", "q", "lse", "L"):
@@ -115,7 +113,7 @@ def test_single_request_bf16_shapes(gpu, V, r, G):
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"],
                       g["lse"], [0], gL=g["L"])
     assert rep.ties <= 1
-    assert rep.compared + rep.ties + rep.skipped == G
+    assert rep.compared == G
     # per-position launches instead (the vocabulary sweep): the same function to within fp32
     # rounding order, so checked against the oracle rather than bit for bit
     p = run_draft(d, per_position=True)
@@ -278,18 +276,22 @@ def test_single_request_full(gpu):
     g = run_draft(d)
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], c.w_dtype, g["x"], g["q"],
                       g["lse"], range(c.B), gL=g["L"])
-    assert rep.compared + rep.ties + rep.skipped == c.gamma
+    assert rep.compared == c.gamma
     assert rep.ties <= 1
+    rep.record()
 
 
-def test_batched_draft_sampled(gpu):
+def test_batched_draft_all_requests(gpu):
+    """Every request and position of the batched workload (B=64, gamma=16, V=151936) against
+    the oracle on the GPU's own prefix; ties stay below 1 % of the draws."""
     c = synth.config(synth.BATCHED)
     d = synth.draft_inputs(c)
     g = run_draft(d)
-    reqs = [0, 1, 17, 31, 32, 50, 63]
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], c.w_dtype, g["x"], g["q"],
-                      g["lse"], reqs, gL=g["L"])
-    assert rep.ties <= 2
+                      g["lse"], range(c.B), gL=g["L"], rep=Report("batched draft"))
+    assert rep.compared == c.B * c.gamma
+    assert rep.ties <= 2 + rep.compared // 100
+    rep.record()
     assert np.all((g["x"] >= 0) & (g["x"] < c.V))
     assert np.all((g["q"] > 0) & (g["q"] <= 1))
 

@@ -8,7 +8,8 @@ import torch
 import oracle
 import synth
 import draft_sampling_verification_head_amd as dspark
-from parity import PROB_TOL, check_draft, check_verify, dev, host
+from parity import (PROB_TOL, Report, check_cstar, check_draft, check_verify, dev,
+                    forced_draft_logits, host)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,27 +44,24 @@ def _gpu_round(c, inp, Bmax=4096):
     return out
 
 
-def _oracle_round_check(c, inp, g, requests):
+def _oracle_round_check(c, inp, g, requests, rep=None):
+    """The schedule exactly; for each listed request the draft on the GPU's own prefix, then
+    the verify and labels of the GPU's block on the oracle's fp64 logits (teacher forcing)."""
     sched = oracle.schedule(inp["conf"], inp["temp"], inp["sps"], 4096)
     assert np.array_equal(g["len"], sched["len"]) and g["K"] == sched["K"]
     rep = check_draft(inp["U"], inp["W1"], inp["W2"], inp["x0"], inp["u"], c.w_dtype, g["x"],
-                      g["q"], g["lse"], requests, gL=g["L"])
+                      g["q"], g["lse"], requests, gL=g["L"], rep=Report("round draft"),
+                      keep_logits=(kept := {}))
+    vrep = Report("round verify")
     Lt = np.concatenate([inp["Lt_pad"][b, : sched["len"][b] + 1] for b in range(c.B)])
     for b in requests:
-        ref = oracle.markov_draft(inp["U"][b:b + 1], inp["W1"], inp["W2"], inp["x0"][b:b + 1],
-                                  inp["u"][b:b + 1], c.w_dtype, want_logits=True)
-        if not np.array_equal(ref["x"][0], g["x"][b]):
-            continue                    # a draft tie: the two chains verify different blocks
-        Ld = ref["L"]
+        Ld = kept.pop(b)
         t_off = sched["t_off"][b:b + 2]
-        vr = check_verify(Ld, Lt, ref["x"], inp["u_acc"][b:b + 1], inp["u_fin"][b:b + 1],
-                          t_off, sched["len"][b:b + 1], g["n"][b:b + 1], g["y"][b:b + 1], [0])
-        cref = oracle.tv_labels(Ld, Lt, t_off=t_off, length=sched["len"][b:b + 1])[0]
-        fin = np.isfinite(cref)
-        assert np.array_equal(fin, np.isfinite(g["cstar"][b]))
-        if fin.any():
-            assert np.max(np.abs(g["cstar"][b][fin] - cref[fin])) < PROB_TOL
-    return rep
+        check_verify(Ld, Lt, g["x"][b:b + 1], inp["u_acc"][b:b + 1], inp["u_fin"][b:b + 1],
+                     t_off, sched["len"][b:b + 1], g["n"][b:b + 1], g["y"][b:b + 1], [0],
+                     rep=vrep)
+        check_cstar(Ld, Lt, t_off, sched["len"][b:b + 1], g["cstar"][b:b + 1], [0], rep=vrep)
+    return rep, vrep
 
 
 def test_tiny_round_exact(gpu):
@@ -94,4 +92,7 @@ def test_round_workload_sampled(gpu):
     g = _gpu_round(c, inp)
     assert g["K"] == c.B + int(g["len"].sum())
     assert np.all((g["n"] >= 0) & (g["n"] <= g["len"]))
-    _oracle_round_check(c, inp, g, [0, 1, 255, 256, 400, 511])
+    rep, vrep = _oracle_round_check(c, inp, g, list(range(0, c.B, 8)))
+    assert rep.ties <= 2 + rep.compared // 100 and vrep.ties <= 2 + vrep.compared // 100
+    rep.record()
+    vrep.record()

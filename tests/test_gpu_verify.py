@@ -7,7 +7,7 @@ import torch
 import oracle
 import synth
 import draft_sampling_verification_head_amd as dspark
-from parity import PROB_TOL, check_verify, dev, host
+from parity import PROB_TOL, Report, check_cstar, check_verify, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -178,16 +178,18 @@ def test_device_data_faults(gpu):
     assert out["n"][2] == -1 and out["n"][3] == -1
 
 
-def test_batched_verify_sampled(gpu):
+def test_batched_verify_all_requests(gpu):
+    """Every request of the batched verify workload (B=256, gamma=16, V=151936): each
+    acceptance decision on the GPU's path, the final draw and every c* against the oracle."""
     c = synth.config(synth.VERIFY)
     inp = verify_inputs(c)
     out = run_verify(inp, want_lse=True)
-    reqs = [0, 3, 100, 128, 200, 255]
     rep = check_verify(inp["Ld"], inp["Lt"], inp["x"], inp["u_acc"], inp["u_fin"], None, None,
-                       out["n"], out["y"], reqs)
-    assert rep.accept_ties + rep.final_ties <= 2
+                       out["n"], out["y"], range(c.B), rep=Report("batched verify"))
+    assert rep.ties <= 2 + rep.compared // 100
     cs = run_tv(inp, lse_d=dev(out["lse_d"]), lse_t=dev(out["lse_t"]))
-    check_tv(inp, cs, reqs)
+    check_cstar(inp["Ld"], inp["Lt"], None, None, cs, range(c.B), rep=rep)
+    rep.record()
     # acceptance falls along the block as the target noise grows
     mean_c = np.nanmean(cs, axis=0)
     assert mean_c[0] > 0.8 and mean_c[-1] < 0.6
