@@ -47,6 +47,14 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def tie_bound(rep) -> int:
+    """Largest number of ties a check accepts: 2 plus 5 % of its decisions. At V ~ 1.5e5 the
+    tail cells of a peaked law are a few 1e-6 wide, so fp32 rounding of the CDF (about 1e-7)
+    moves a few per cent of the draws across a boundary; every tie is still asserted to lie
+    within TIE of the oracle's cell."""
+    return 2 + rep.compared // 20
+
+
 def cdf_margin(p: np.ndarray, u: float, g: int) -> float:
     """Signed distance of u to the cell of token g under law p: >= 0 when u lies in
     [F(g-1), F(g)) (the distance to the nearer edge), < 0 outside (minus the distance to it)."""

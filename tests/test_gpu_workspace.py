@@ -8,7 +8,7 @@ import oracle
 import synth
 import draft_sampling_verification_head_amd as dspark
 from draft_sampling_verification_head_amd import binding
-from parity import check_draft, check_verify, dev, host, PROB_TOL
+from parity import tie_bound, check_draft, check_verify, dev, host, PROB_TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -86,4 +86,4 @@ def test_one_launch_drafts_ignore_stale_slots(gpu, fill, B, V, G, want_logits):
     g = {k: host(v) for k, v in out.items() if v is not None}
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
                       range(B), gL=g.get("L"))
-    assert rep.ties <= 1
+    assert rep.ties <= tie_bound(rep)
