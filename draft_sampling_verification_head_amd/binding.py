@@ -19,12 +19,14 @@ F32, BF16 = 0, 1
 PATH_NAMES = {0: "sweep", 1: "mfma", 2: "resident", 3: "slab"}
 GLOBAL, EARLY_STOP = 0, 1
 DRAFT_PER_POSITION = 1
+DRAFT_TEST_SPIN = 256
 STS_NLL, STS_ECE = 0, 1
 
 # every symbol include/dspark.h declares
 EXPORTS = (
     "dspark_status_string", "dspark_last_error", "dspark_version",
     "dspark_markov_draft_path", "dspark_markov_draft_one_launch", "dspark_markov_draft_workspace_bytes",
+    "dspark_markov_draft_plan",
     "dspark_markov_draft", "dspark_markov_draft_ex",
     "dspark_verify_workspace_bytes", "dspark_verify",
     "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
@@ -46,6 +48,7 @@ _SIGS = {
     "dspark_markov_draft_path": (_I, [_I, _I, _I, _I, _P, _P]),
     "dspark_markov_draft_one_launch": (_I, [_I, _I, _I, _I, _P, _P, _I]),
     "dspark_markov_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "dspark_markov_draft_plan": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
     "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_markov_draft_ex": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _I]),
     "dspark_verify_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -135,14 +138,29 @@ def _need(t, name, dtype, shape, device):
 _ws_cache: dict = {}
 
 
-def workspace(nbytes: int, device, tag: str = ""):
-    """A cached uint8 device buffer of at least nbytes, reused by later calls of the same kind
-    (calls are stream-ordered on one stream, so they never overlap)."""
+def _stream_obj(stream=None):
     torch = _torch()
-    key = (str(device), tag)
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def workspace(nbytes: int, device, tag: str = "", stream=None, ws=None):
+    """The workspace of one call: the caller's ``ws`` (a uint8 device tensor, checked for size
+    and never replaced), or a cached buffer of at least nbytes per (device, stream, kind).
+    Calls of one kind on one stream are stream-ordered, so they never overlap; calls on
+    another stream get a buffer of their own. A cached buffer that must grow is replaced;
+    the old one is freed only after the work queued on its stream (record_stream), but a
+    graph captured over it would keep its address, so graph capture should pass ``ws``."""
+    torch = _torch()
+    if ws is not None:
+        if ws.dtype != torch.uint8 or ws.device != torch.device(device) or ws.numel() < nbytes:
+            raise ValueError(f"workspace must be a uint8 tensor on {device} of >= {nbytes} bytes")
+        return ws
+    s = _stream_obj(stream)
+    key = (str(device), int(s.cuda_stream), tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -165,11 +183,34 @@ def markov_draft_one_launch(B: int, W1, W2, want_logits: bool = False) -> bool:
     return bool(load().dspark_markov_draft_one_launch(B, V, r, wdt, _ptr(W1), _ptr(W2), int(want_logits)))
 
 
+def markov_draft_plan(U, W1, W2, Ld=None, per_position=False, test_spin=False):
+    """dspark_markov_draft_plan: (path name, one launch, workspace bytes) of this exact call."""
+    torch = _torch()
+    B, G, V = U.shape
+    r = W1.shape[1]
+    wdt = BF16 if W1.dtype == torch.bfloat16 else F32
+    opts = (DRAFT_PER_POSITION if per_position else 0) | (DRAFT_TEST_SPIN if test_spin else 0)
+    path, one, nb = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _check(load().dspark_markov_draft_plan(B, V, r, G, wdt, _ptr(W1), _ptr(W2), _ptr(U), _ptr(Ld), opts,
+                                           ctypes.byref(path), ctypes.byref(one), ctypes.byref(nb)),
+           "dspark_markov_draft_plan")
+    return PATH_NAMES[path.value], bool(one.value), int(nb.value)
+
+
+def draft_gave_up(ws) -> int:
+    """The give-up count of the last one-launch draft call on workspace ``ws`` (bytes 0..3);
+    synchronises with the device."""
+    torch = _torch()
+    return int(ws[:4].view(torch.int32).item())
+
+
 def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=False,
-                 per_position=False, out=None, stream=None):
+                 per_position=False, out=None, stream=None, ws=None, test_spin=False):
     """dspark_markov_draft (dspark_markov_draft_ex with DSPARK_DRAFT_PER_POSITION when
     per_position). U [B][gamma][V] fp32, W1 [V][r], W2 [r][V] (fp32 or bf16), x0 [B] int32,
-    u [B][gamma] fp32. Returns dict x, q, lse, L (None when not asked)."""
+    u [B][gamma] fp32. ``ws``: an explicit uint8 workspace (else a cached one); ``test_spin``:
+    DSPARK_DRAFT_TEST_SPIN (failure injection). Returns dict x, q, lse, L (None when not
+    asked)."""
     torch = _torch()
     lib = load()
     B, G, V = U.shape
@@ -188,17 +229,18 @@ def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=Fa
     q = o.get("q") if o.get("q") is not None else (torch.empty((B, G), dtype=torch.float32, device=dev) if want_q else None)
     lse = o.get("lse") if o.get("lse") is not None else (torch.empty((B, G), dtype=torch.float32, device=dev) if want_lse else None)
     L = o.get("L") if o.get("L") is not None else (torch.empty((B, G, V), dtype=torch.float32, device=dev) if want_logits else None)
-    nbytes = lib.dspark_markov_draft_workspace_bytes(B, V, r, G)
-    ws = workspace(nbytes, dev, "draft")
+    opts = (DRAFT_PER_POSITION if per_position else 0) | (DRAFT_TEST_SPIN if test_spin else 0)
+    _, _, nbytes = markov_draft_plan(U, W1, W2, L, per_position, test_spin)
+    ws = workspace(nbytes, dev, "draft", stream, ws)
     st = lib.dspark_markov_draft_ex(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(x0), _ptr(u),
                                     _ptr(x), _ptr(q), _ptr(lse), _ptr(L), _ptr(ws), ws.numel(),
-                                    _stream(stream), DRAFT_PER_POSITION if per_position else 0)
+                                    _stream(stream), opts)
     _check(st, "dspark_markov_draft")
     return dict(x=x, q=q, lse=lse, L=L)
 
 
 def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, want_lse=False,
-           out=None, stream=None, with_tv=False):
+           out=None, stream=None, with_tv=False, ws=None):
     """dspark_verify (dspark_verify_tv when with_tv). Ld [B][gamma][V], Lt [rows][V] fp32;
     x, u_acc [B][gamma]; u_fin [B]. Returns dict n [B], y [B][gamma+1] (and lse_d, lse_t when
     want_lse; cstar [B][gamma] when with_tv)."""
@@ -235,7 +277,7 @@ def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, wan
         cstar = o.get("cstar") if o.get("cstar") is not None else torch.empty((B, G), dtype=torch.float32, device=dev)
         _need(cstar, "cstar", torch.float32, (B, G), dev)
         nbytes = lib.dspark_verify_tv_workspace_bytes(B, V, G)
-        ws = workspace(nbytes, dev, "verify_tv")
+        ws = workspace(nbytes, dev, "verify_tv", stream, ws)
         st = lib.dspark_verify_tv(B, V, G, _ptr(Ld), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
                                   _ptr(length), _ptr(x), _ptr(ld_lse), _ptr(u_acc), _ptr(u_fin),
                                   _ptr(n), _ptr(y), _ptr(lse_d), _ptr(lse_t), _ptr(cstar),
@@ -243,7 +285,7 @@ def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, wan
         _check(st, "dspark_verify_tv")
         return dict(n=n, y=y, lse_d=lse_d, lse_t=lse_t, cstar=cstar)
     nbytes = lib.dspark_verify_workspace_bytes(B, V, G)
-    ws = workspace(nbytes, dev, "verify")
+    ws = workspace(nbytes, dev, "verify", stream, ws)
     st = lib.dspark_verify(B, V, G, _ptr(Ld), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
                            _ptr(length), _ptr(x), _ptr(ld_lse), _ptr(u_acc), _ptr(u_fin),
                            _ptr(n), _ptr(y), _ptr(lse_d), _ptr(lse_t), _ptr(ws), ws.numel(),
@@ -253,7 +295,7 @@ def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, wan
 
 
 def verify_markov(U, W1, W2, x0, x, ld_lse, Lt, u_acc, u_fin, *, t_off=None, length=None,
-                  out=None, stream=None):
+                  out=None, stream=None, ws=None):
     """dspark_verify_markov: verify + TV labels with the draft logits rebuilt from U, W1, W2
     (bf16 factors). U [B][gamma][V] fp32, x0 [B], x [B][gamma] int32, ld_lse [B][gamma] from the
     draft, Lt [rows][V] fp32, u_acc [B][gamma], u_fin [B]. Returns dict n, y, lse_t, cstar."""
@@ -287,7 +329,7 @@ def verify_markov(U, W1, W2, x0, x, ld_lse, Lt, u_acc, u_fin, *, t_off=None, len
     _need(lse_t, "lse_t", torch.float32, (B, G + 1), dev)
     _need(cstar, "cstar", torch.float32, (B, G), dev)
     nbytes = lib.dspark_verify_markov_workspace_bytes(B, V, r, G)
-    ws = workspace(nbytes, dev, "verify_markov")
+    ws = workspace(nbytes, dev, "verify_markov", stream, ws)
     st = lib.dspark_verify_markov(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), BF16, _ptr(x0), _ptr(x),
                                   _ptr(ld_lse), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
                                   _ptr(length), _ptr(u_acc), _ptr(u_fin), _ptr(n), _ptr(y),
@@ -296,7 +338,8 @@ def verify_markov(U, W1, W2, x0, x, ld_lse, Lt, u_acc, u_fin, *, t_off=None, len
     return dict(n=n, y=y, lse_t=lse_t, cstar=cstar)
 
 
-def tv_labels(Ld, Lt, *, t_off=None, length=None, lse_d=None, lse_t=None, out=None, stream=None):
+def tv_labels(Ld, Lt, *, t_off=None, length=None, lse_d=None, lse_t=None, out=None, stream=None,
+              ws=None):
     """dspark_tv_labels. Returns c* [B][gamma] (NaN beyond each request's length)."""
     torch = _torch()
     lib = load()
@@ -316,7 +359,7 @@ def tv_labels(Ld, Lt, *, t_off=None, length=None, lse_d=None, lse_t=None, out=No
         _need(lse_t, "lse_t", torch.float32, (B, G + 1), dev)
     c = out if out is not None else torch.empty((B, G), dtype=torch.float32, device=dev)
     nbytes = lib.dspark_tv_labels_workspace_bytes(B, V, G)
-    ws = workspace(nbytes, dev, "tv")
+    ws = workspace(nbytes, dev, "tv", stream, ws)
     st = lib.dspark_tv_labels(B, V, G, _ptr(Ld), _ptr(Lt), int(Lt.shape[0]), _ptr(t_off),
                               _ptr(length), _ptr(lse_d), _ptr(lse_t), _ptr(c), _ptr(ws),
                               ws.numel(), _stream(stream))
@@ -335,7 +378,8 @@ def _schedule_outputs(R, G, dev, out, want_a):
     return dict(len=length, t_off=t_off, K=K, theta=theta, a=a)
 
 
-def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None, stream=None):
+def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None, stream=None,
+             ws=None):
     """dspark_schedule. conf [R][gamma] fp32, sps [Bmax+1] fp32, temp [gamma] fp32 or None.
     Returns dict len [R], t_off [R+1], K [1], theta [1] (and a [R][gamma] when want_a)."""
     torch = _torch()
@@ -347,7 +391,7 @@ def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None,
     if temp is not None:
         _need(temp, "temp", torch.float32, (G,), dev)
     o = _schedule_outputs(R, G, dev, out, want_a)
-    ws = workspace(lib.dspark_schedule_workspace_bytes(R, G, int(Bmax)), dev, "schedule")
+    ws = workspace(lib.dspark_schedule_workspace_bytes(R, G, int(Bmax)), dev, "schedule", stream, ws)
     st = lib.dspark_schedule(R, G, _ptr(conf), _ptr(temp), _ptr(sps), int(Bmax), int(mode),
                              _ptr(o["len"]), _ptr(o["t_off"]), _ptr(o["K"]), _ptr(o["theta"]),
                              _ptr(o["a"]), _ptr(ws), ws.numel(), _stream(stream))
@@ -384,7 +428,7 @@ class ConfRing:
 
 
 def schedule_lagged(ring: ConfRing, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None,
-                    stream=None):
+                    stream=None, ws=None):
     """dspark_schedule_lagged: dspark_schedule on the confidences pushed two rounds ago."""
     torch = _torch()
     lib = load()
@@ -393,7 +437,7 @@ def schedule_lagged(ring: ConfRing, sps, Bmax, *, temp=None, mode=GLOBAL, want_a
     if temp is not None:
         _need(temp, "temp", torch.float32, (G,), dev)
     o = _schedule_outputs(R, G, dev, out, want_a)
-    ws = workspace(lib.dspark_schedule_workspace_bytes(R, G, int(Bmax)), dev, "schedule")
+    ws = workspace(lib.dspark_schedule_workspace_bytes(R, G, int(Bmax)), dev, "schedule", stream, ws)
     st = lib.dspark_schedule_lagged(R, G, _ptr(ring.buf), ring.nbytes, _ptr(temp), _ptr(sps),
                                     int(Bmax), int(mode), _ptr(o["len"]), _ptr(o["t_off"]),
                                     _ptr(o["K"]), _ptr(o["theta"]), _ptr(o["a"]), _ptr(ws),
@@ -403,7 +447,7 @@ def schedule_lagged(ring: ConfRing, sps, Bmax, *, temp=None, mode=GLOBAL, want_a
 
 
 def sts_fit(conf, n_acc, grid, *, length=None, bins=15, objective=STS_NLL, want_obj=False,
-            stream=None):
+            stream=None, ws=None):
     """dspark_sts_fit. conf [N][gamma] fp32, n_acc [N] int32 (and length [N] int32) from
     verify, grid [n_grid] fp32. Returns dict T, ece_before, ece_after [gamma] (and obj
     [gamma][n_grid] when want_obj)."""
@@ -422,7 +466,7 @@ def sts_fit(conf, n_acc, grid, *, length=None, bins=15, objective=STS_NLL, want_
     ea = torch.empty(G, dtype=torch.float32, device=dev)
     obj = torch.empty((G, nT), dtype=torch.float32, device=dev) if want_obj else None
     nbytes = lib.dspark_sts_fit_workspace_bytes(N, G, nT)
-    ws = workspace(nbytes, dev, "sts")
+    ws = workspace(nbytes, dev, "sts", stream, ws)
     st = lib.dspark_sts_fit(N, G, _ptr(conf), _ptr(n_acc), _ptr(length), _ptr(grid), nT, bins,
                             objective, _ptr(T), _ptr(eb), _ptr(ea), _ptr(obj), _ptr(ws),
                             ws.numel(), _stream(stream))

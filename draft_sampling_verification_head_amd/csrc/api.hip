@@ -104,49 +104,119 @@ int dspark_markov_draft_one_launch(int B, int V, int r, int w_dtype, const void*
     return p == DSPARK_PATH_SLAB && dspark::draft_slab_one_launch(B, V, want_logits != 0) ? 1 : 0;
 }
 
+}  // extern "C"
+
+// Draft workspace layout: a 256-byte header (bytes 0..3: the give-up count of the last
+// one-launch call), the position slots of the one-launch forms, the two tile-partial buffers
+// (every path but the single-request one), and two logits rows per request (the sweep and
+// MFMA paths, when the caller does not take the logits). A call needs only the regions of
+// the path it takes; dspark_markov_draft_workspace_bytes covers every path.
+namespace {
+
+constexpr size_t kDraftHeader = 256;
+
+struct DraftNeed {
+    size_t slots, parts, rows;
+    size_t total() const { return kDraftHeader + slots + parts + rows; }
+};
+
+DraftNeed draft_need(int B, int V, int gamma, int path, bool L_out) {
+    DraftNeed n{align_up(draft_slot_bytes(V, gamma)), 0, 0};
+    if (path != DSPARK_PATH_RESIDENT) n.parts = 2 * align_up(draft_part_count(B, V) * sizeof(float2));
+    if ((path == DSPARK_PATH_SWEEP || path == DSPARK_PATH_MFMA) && !L_out)
+        n.rows = 2 * align_up(static_cast<size_t>(B) * V * sizeof(float));
+    return n;
+}
+
+bool draft_sizes_ok(int B, int V, int r, int gamma) {
+    return B >= 1 && V >= 1 && gamma >= 1 && r >= 1 && gamma <= 64 && r <= 1024 &&
+           common_sizes_ok(B, V, gamma);
+}
+
+// The DraftCall of these arguments with every pointer but the workspace's set (the path
+// choice depends on the factors' and U's alignment, on Ld_out and on the options).
+dspark::DraftCall draft_call(int B, int V, int r, int gamma, const float* U, const void* W1,
+                             const void* W2, int w_dtype, const float* Ld_out, int options) {
+    dspark::DraftCall dc;
+    dc.B = B; dc.V = V; dc.r = r; dc.gamma = gamma; dc.w_dtype = w_dtype;
+    dc.U = U; dc.W1 = W1; dc.W2 = W2;
+    dc.L_out = Ld_out != nullptr;
+    dc.L[0] = const_cast<float*>(Ld_out);
+    dc.per_position = (options & DSPARK_DRAFT_PER_POSITION) != 0;
+    return dc;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma) {
     (void)r;
     if (B < 1 || V < 1 || gamma < 1) return 0;
-    return 2 * align_up(draft_part_count(B, V) * sizeof(float2)) +
-           2 * align_up(static_cast<size_t>(B) * V * sizeof(float)) +
-           align_up(draft_slot_bytes(V, gamma));
+    return draft_need(B, V, gamma, DSPARK_PATH_SWEEP, false).total();
+}
+
+int dspark_markov_draft_plan(int B, int V, int r, int gamma, int w_dtype, const void* W1,
+                             const void* W2, const float* U, const float* Ld_out, int options,
+                             int* path_out, int* one_launch_out, size_t* ws_bytes_out) {
+    if (options & ~(DSPARK_DRAFT_PER_POSITION | DSPARK_DRAFT_TEST_SPIN))
+        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft_plan: unknown option bits 0x%x", options);
+    if (!draft_sizes_ok(B, V, r, gamma))
+        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft_plan: B=%d V=%d r=%d gamma=%d outside caps",
+                    B, V, r, gamma);
+    if (w_dtype != DSPARK_F32 && w_dtype != DSPARK_BF16)
+        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft_plan: unknown w_dtype %d", w_dtype);
+    const dspark::DraftCall dc = draft_call(B, V, r, gamma, U, W1, W2, w_dtype, Ld_out, options);
+    bool one = false;
+    const int path = dspark::draft_path_of(dc, &one);
+    if (path_out) *path_out = path;
+    if (one_launch_out) *one_launch_out = one ? 1 : 0;
+    if (ws_bytes_out) *ws_bytes_out = draft_need(B, V, gamma, path, Ld_out != nullptr).total();
+    return ok();
 }
 
 int dspark_markov_draft_ex(int B, int V, int r, int gamma, const float* U, const void* W1,
                            const void* W2, int w_dtype, const int32_t* x0, const float* u,
                            int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, void* ws,
                            size_t ws_bytes, void* stream, int options) {
-    if (options & ~DSPARK_DRAFT_PER_POSITION)
+    if (options & ~(DSPARK_DRAFT_PER_POSITION | DSPARK_DRAFT_TEST_SPIN))
         return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: unknown option bits 0x%x", options);
     if (B < 1 || V < 1 || gamma < 1 || r < 1)
         return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: B=%d V=%d r=%d gamma=%d must be >= 1",
                     B, V, r, gamma);
-    if (gamma > 64 || r > 1024 || !common_sizes_ok(B, V, gamma))
+    if (!draft_sizes_ok(B, V, r, gamma))
         return fail(DSPARK_ERR_UNSUPPORTED, "markov_draft: gamma=%d r=%d B*gamma*V outside caps",
                     gamma, r);
     if (w_dtype != DSPARK_F32 && w_dtype != DSPARK_BF16)
         return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: unknown w_dtype %d", w_dtype);
     if (!U || !W1 || !W2 || !x0 || !u || !x_out)
         return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: a required pointer is NULL");
-    const size_t need = dspark_markov_draft_workspace_bytes(B, V, r, gamma);
-    if (!ws || ws_bytes < need)
+    dspark::DraftCall dc = draft_call(B, V, r, gamma, U, W1, W2, w_dtype, Ld_out, options);
+    const int path = dspark::draft_path_of(dc, nullptr);
+    const DraftNeed need = draft_need(B, V, gamma, path, Ld_out != nullptr);
+    if (!ws || ws_bytes < need.total())
         return fail(DSPARK_ERR_WORKSPACE, "markov_draft: workspace %zu bytes, need %zu", ws_bytes,
-                    need);
+                    need.total());
     Carver c(ws);
-    dspark::DraftCall dc;
-    dc.B = B; dc.V = V; dc.r = r; dc.gamma = gamma; dc.w_dtype = w_dtype;
-    dc.U = U; dc.W1 = W1; dc.W2 = W2; dc.x0 = x0; dc.u = u;
+    dc.status = c.take<unsigned>(kDraftHeader / sizeof(unsigned));
+    dc.slots = reinterpret_cast<float2*>(c.take<char>(need.slots));
+    float* lbuf[2] = {nullptr, nullptr};
+    if (need.parts) {
+        dc.part[0] = c.take<float2>(draft_part_count(B, V));
+        dc.part[1] = c.take<float2>(draft_part_count(B, V));
+    } else {
+        dc.part[0] = dc.part[1] = nullptr;
+    }
+    if (need.rows) {
+        lbuf[0] = c.take<float>(static_cast<size_t>(B) * V);
+        lbuf[1] = c.take<float>(static_cast<size_t>(B) * V);
+    }
+    dc.x0 = x0; dc.u = u;
     dc.x_out = x_out; dc.q_out = q_out; dc.lse_out = lse_out;
-    dc.part[0] = c.take<float2>(draft_part_count(B, V));
-    dc.part[1] = c.take<float2>(draft_part_count(B, V));
-    float* lbuf[2] = {c.take<float>(static_cast<size_t>(B) * V),
-                      c.take<float>(static_cast<size_t>(B) * V)};
     for (int k = 0; k < gamma; ++k)
         dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
     dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
-    dc.L_out = Ld_out != nullptr;
-    dc.per_position = (options & DSPARK_DRAFT_PER_POSITION) != 0;
-    dc.slots = c.take<float2>(draft_slot_bytes(V, gamma) / sizeof(float2));
+    if (options & DSPARK_DRAFT_TEST_SPIN) dc.spin = 0;
     const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "markov_draft");
     return ok();

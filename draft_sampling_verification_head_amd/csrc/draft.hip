@@ -265,13 +265,29 @@ int draft_part_tiles(int V) {
     return n > ns ? n : ns;
 }
 
-hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
+int draft_path_of(const DraftCall& c, bool* one_launch) {
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; };
-    if (!c.per_position && draft_resident_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2))
-        return launch_draft_resident(c, st);
-    if (draft_slab_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2) && al16(c.U) && (!c.L_out || al16(c.L[0])))
-        return launch_draft_slab(c, st);
-    if (draft_mfma_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2)) return launch_draft_mfma(c, st);
+    bool one = false;
+    int path = 0;                                       // DSPARK_PATH_SWEEP
+    if (!c.per_position && draft_resident_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2)) {
+        path = 2;                                       // DSPARK_PATH_RESIDENT
+        one = true;
+    } else if (draft_slab_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2) && al16(c.U) &&
+               (!c.L_out || al16(c.L[0]))) {
+        path = 3;                                       // DSPARK_PATH_SLAB
+        one = !c.per_position && draft_slab_one_launch(c.B, c.V, c.L_out);
+    } else if (draft_mfma_ok(c.B, c.V, c.r, c.w_dtype, c.W1, c.W2)) {
+        path = 1;                                       // DSPARK_PATH_MFMA
+    }
+    if (one_launch) *one_launch = one;
+    return path;
+}
+
+hipError_t launch_draft(const DraftCall& c, hipStream_t st) {
+    const int path = draft_path_of(c, nullptr);
+    if (path == 2) return launch_draft_resident(c, st);
+    if (path == 3) return launch_draft_slab(c, st);
+    if (path == 1) return launch_draft_mfma(c, st);
     StepArgs a;
     a.B = c.B; a.V = c.V; a.r = c.r; a.gamma = c.gamma; a.nblk = (c.V + kTileCols - 1) / kTileCols;
     a.U = c.U; a.W1 = c.W1; a.W2 = c.W2; a.x0 = c.x0; a.u = c.u;

@@ -62,7 +62,6 @@ constexpr int kStageLoads = kStageRows * kChunks / kWave; // uint4 loads per lan
 constexpr size_t kResLds = static_cast<size_t>(kRWaves) * kStageRows * kResTileCols * 2;
 constexpr int kPartRegs = RegTiles<kResTileCols>::value;  // partials per lane in the draw
 constexpr int kMaxTiles = kWave * kPartRegs;              // 512 workgroups at most
-constexpr unsigned kSpinMax = 1u << 20;                   // bounded wait, about a second
 constexpr unsigned long long kEmpty = ~0ull;              // sentinel: both halves NaN
 static_assert(kStageLoads * kWave == kStageRows * kChunks, "staging rounds cover whole rows");
 static_assert(kResLds >= sizeof(float) * kRWaves * kResTileCols, "sums fit in the staging area");
@@ -83,6 +82,8 @@ struct ResArgs {
     float2* slots;            // [gamma][G] tile partials, kEmpty until published
     unsigned long long* toks; // [gamma] (logit bits << 32 | token) of each draw, kEmpty until published
     unsigned long long* epoch;   // [2]: the call counter E and the ready word F (after toks)
+    unsigned* status;         // number of workgroups that gave up (reset with the slots)
+    unsigned spin;            // polls before a wait gives up
 };
 
 // Ready word of a call with counter e: the finaliser of the splitmix64 generator (Steele, Lea
@@ -135,6 +136,7 @@ void draft_resident(ResArgs a) {
         unsigned long long* sl = reinterpret_cast<unsigned long long*>(a.slots);
         const int n = a.gamma * a.G + a.gamma;             // partial slots, then token slots
         for (int i = tid; i < n; i += kRThreads) store_token(sl + i, kEmpty);
+        if (tid == 0) __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const long long c0 = static_cast<long long>(blockIdx.x) * kResTileCols;
     // epilogue columns of this thread: c0 + tid, and c0 + 512 + tid for tid < 128
@@ -257,7 +259,7 @@ void draft_resident(ResArgs a) {
             for (int i = 0; i < kRWaves; ++i) s += tile_mass(wpart[i], m);
             if (k == 0) {                                 // the slots must be reset first
                 for (unsigned n = 0; load_token(a.epoch + 1) != key; ++n) {
-                    if (n > kSpinMax) {
+                    if (n > a.spin) {
                         gave_up = 1;
                         break;
                     }
@@ -289,7 +291,7 @@ void draft_resident(ResArgs a) {
                     p[t] = (i < a.G) ? __builtin_bit_cast(float2, bits) : make_float2(-INFINITY, 0.0f);
                 }
                 if (!__any(missing)) break;
-                if (++n > kSpinMax) {
+                if (++n > a.spin) {
                     if (lane == 0) gave_up = 1;
                     break;
                 }
@@ -326,7 +328,7 @@ void draft_resident(ResArgs a) {
                     unsigned long long v;
                     unsigned n2 = 0;
                     while ((v = load_token(a.toks + k)) == kEmpty) {
-                        if (++n2 > kSpinMax) {
+                        if (++n2 > a.spin) {
                             if (lane == 0) gave_up = 1;
                             break;
                         }
@@ -359,6 +361,7 @@ void draft_resident(ResArgs a) {
     // every workgroup has read E: each published its last partial, which workgroup 0 saw
     // (or the launch gave up, and E moves on all the same)
     if (blockIdx.x == 0 && tid == 0) store_token(a.epoch, s_e0 + 1);
+    if (gave_up && tid == 0) __hip_atomic_fetch_add(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (gave_up && blockIdx.x == 0 && tid == 0) {
         for (int i = k; i < a.gamma; ++i) {
             a.x_out[i] = -1;
@@ -423,6 +426,8 @@ hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {
     a.slots = c.slots;
     a.toks = reinterpret_cast<unsigned long long*>(c.slots + static_cast<long long>(c.gamma) * a.G);
     a.epoch = a.toks + c.gamma;
+    a.status = c.status;
+    a.spin = c.spin;
     hipLaunchKernelGGL(draft_resident, dim3(a.G), dim3(kRThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -66,10 +66,11 @@ struct SlabArgs {
     float2* spart;            // resident: [B][G] the same per request and slab (8 wave tiles)
     unsigned long long* flags;   // resident: [3][gamma][G], kEmpty until published
     unsigned long long* epoch;   // resident: [2] the call counter E and the ready word F
+    unsigned* status;         // resident: number of workgroups that gave up (reset with the flags)
+    unsigned spin;            // resident: polls before a flag wait gives up
     float4* picks;            // resident: [B] (slab, max, lse, mass left in the slab)
 };
 
-constexpr unsigned kSpinMax = 1u << 20;             // bounded flag wait, about a second
 constexpr unsigned long long kEmpty = ~0ull;
 
 // Ready word of a resident call with counter e (the single-request draft uses the same word
@@ -658,8 +659,10 @@ void draft_slab_resident(SlabArgs a) {
         e0 = load_coherent(a.epoch);
         key = ready_word(e0);
     }
-    if (slab == 0)
+    if (slab == 0) {
         for (long long i = tid; i < 3ll * a.gamma * G; i += kSlabThreads) store_coherent(a.flags + i, kEmpty);
+        if (tid == 0) __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     bf16x8 w2f[NT][kKS];
     load_w2_frags<NT, 4, 1>(w2f, a.W2, a.V, a.r, cw, sm + 2 * UB + 2 * kHBuf + wave * S::Stage);
@@ -685,7 +688,7 @@ void draft_slab_resident(SlabArgs a) {
             bool missing = false;
             for (int i = lane; i < G; i += kWave) missing |= load_coherent(row + i) == kEmpty;
             if (!__any(missing)) return true;
-            if (n > kSpinMax) return false;
+            if (n > a.spin) return false;
             __builtin_amdgcn_s_sleep(1);
         }
     };
@@ -696,7 +699,7 @@ void draft_slab_resident(SlabArgs a) {
         if (tid == 0) {
             if (f == 0 && k == 0) {                   // the flags must be reset first
                 for (unsigned n = 0; load_coherent(a.epoch + 1) != key; ++n) {
-                    if (n > kSpinMax) {
+                    if (n > a.spin) {
                         gave_up = 1;
                         return;
                     }
@@ -707,11 +710,16 @@ void draft_slab_resident(SlabArgs a) {
         }
     };
     int k = 0;
+    int kfail = a.gamma;              // first position whose draws may be missing after a give-up
     for (; k < a.gamma; ++k) {
         // tokens x_{k-1} of every request: x0, or the previous position's draws
         if (k > 0 && wave == 0 && !wait_flags(flag_row(2, k - 1)) && lane == 0) gave_up = 1;
         __syncthreads();                              // also: every wave is done with the draw LDS
-        if (gave_up) break;
+        if (gave_up) {
+            // a drawer of position k - 1 may have given up before drawing it
+            kfail = k > 0 ? k - 1 : 0;
+            break;
+        }
         for (int b = tid; b < a.B; b += kSlabThreads) {
             const int t = k ? load_coherent(a.x_out + static_cast<long long>(b) * a.gamma + k - 1) : a.x0[b];
             stok[b] = (t >= 0 && t < a.V) ? t : -1;
@@ -832,10 +840,12 @@ void draft_slab_resident(SlabArgs a) {
     // every workgroup has read E (each published the flags workgroup 0 waited for), or the
     // launch gave up; E moves on either way
     if (slab == 0 && tid == 0) store_coherent(a.epoch, e0 + 1);
-    if (gave_up) {                                    // this workgroup's requests: -1 from k on
+    if (gave_up && tid == 0) __hip_atomic_fetch_add(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (gave_up) {                                    // this workgroup's requests: -1 from kfail on
+        if (kfail > k) kfail = k;
         for (long long i = tid; i < static_cast<long long>(a.B) * a.gamma; i += kSlabThreads) {
             const int b = static_cast<int>(i / a.gamma), kk = static_cast<int>(i % a.gamma);
-            if (b % G != slab || kk < k) continue;
+            if (b % G != slab || kk < kfail) continue;
             a.x_out[i] = -1;
             if (a.q_out) a.q_out[i] = 0.0f;
             if (a.lse_out) a.lse_out[i] = -INFINITY;
@@ -923,6 +933,8 @@ hipError_t launch_nt(const DraftCall& c, hipStream_t st) {
     a.L_bstride = c.L_bstride;
     a.flags = reinterpret_cast<unsigned long long*>(c.slots);
     a.epoch = nullptr;
+    a.status = c.status;
+    a.spin = c.spin;
     // resident: the second partial buffer holds the picks [B] and the slab partials [B][G]
     a.picks = reinterpret_cast<float4*>(c.part[1]);
     a.spart = c.part[1] + 2 * static_cast<long long>(c.B);

@@ -24,7 +24,13 @@ struct DraftCall {
     bool per_position = false;   // no persistent launch: each position is its own launches
     float2* part[2];          // tile partials [B][draft_part_tiles(V)] of even / odd steps
     float2* slots;            // max(draft_resident_slot_bytes, draft_slab_flag_bytes) of workspace
+    unsigned* status;         // one-launch forms: number of workgroups that gave up waiting
+    unsigned spin = 1u << 20; // polls before a one-launch form gives up (about a second)
 };
+
+// Which path (DSPARK_PATH_*) launch_draft takes for this call, and whether it runs every
+// position in one launch.
+int draft_path_of(const DraftCall& c, bool* one_launch);
 
 // Vocabulary tiles per request the partial buffers must hold (the finest tiling in use).
 int draft_part_tiles(int V);

@@ -117,15 +117,33 @@ int dspark_version(void);
  */
 enum { DSPARK_PATH_SWEEP = 0, DSPARK_PATH_MFMA = 1, DSPARK_PATH_RESIDENT = 2, DSPARK_PATH_SLAB = 3 };
 
-/* The path dspark_markov_draft takes for these arguments on the current device. */
+/* The path dspark_markov_draft takes for these arguments on the current device, assuming a
+ * 16-byte aligned U (and Ld_out) and no option bits; dspark_markov_draft_plan answers for the
+ * exact call. */
 int dspark_markov_draft_path(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
 
 /* 1 if dspark_markov_draft runs all positions in one launch for these arguments (a non-null
- * Ld_out when want_logits != 0; U 16-byte aligned) on the current device, else 0. */
+ * Ld_out when want_logits != 0), on the same assumptions as dspark_markov_draft_path. */
 int dspark_markov_draft_one_launch(int B, int V, int r, int w_dtype, const void* W1, const void* W2,
                                    int want_logits);
 
+/* Workspace of a draft call. dspark_markov_draft_workspace_bytes covers every path;
+ * dspark_markov_draft_plan gives the exact call's path, whether it runs in one launch, and the
+ * bytes that call needs (a call checks ws_bytes against that figure):
+ *   single-request one-launch path   256 + slot bytes                  (kilobytes)
+ *   slab path                        + 2 tile-partial buffers          (B * V / 16 bytes)
+ *   sweep / MFMA without Ld_out      + 2 logits rows per request       (2 * B * V * 4 bytes)
+ * Bytes 0..3 of the workspace hold, once a one-launch call has finished on its stream, a
+ * give-up count (uint32): 0 when every position was drawn, nonzero when a wait gave up (the
+ * positions not drawn then have token -1; the count may miss workgroups that gave up before
+ * the launch reset the word, but never reads 0 after a give-up). Other paths leave the word
+ * unchanged.
+ * dspark_markov_draft_plan returns DSPARK_ERR_INVALID_ARG for arguments a call would reject as
+ * sizes or dtypes; out pointers are host memory and nullable. */
 size_t dspark_markov_draft_workspace_bytes(int B, int V, int r, int gamma);
+int dspark_markov_draft_plan(int B, int V, int r, int gamma, int w_dtype, const void* W1,
+                             const void* W2, const float* U, const float* Ld_out, int options,
+                             int* path_out, int* one_launch_out, size_t* ws_bytes_out);
 int dspark_markov_draft(int B, int V, int r, int gamma,
                         const float* U, const void* W1, const void* W2, int w_dtype,
                         const int32_t* x0, const float* u,
@@ -141,7 +159,11 @@ int dspark_markov_draft(int B, int V, int r, int gamma,
  *                              and carry no restriction on overlapping draft calls. The
  *                              results are those of the one-launch form bit for bit on the
  *                              slab path, and equal to within fp32 rounding order otherwise. */
-enum { DSPARK_DRAFT_PER_POSITION = 1 };
+/*   DSPARK_DRAFT_TEST_SPIN     failure injection for tests: the one-launch forms poll each
+ *                              wait once before giving up, so a wait that is not already
+ *                              satisfied gives up (tokens -1 from that position on, the
+ *                              workspace's give-up count set). Every kernel still exits. */
+enum { DSPARK_DRAFT_PER_POSITION = 1, DSPARK_DRAFT_TEST_SPIN = 256 };
 
 /* dspark_markov_draft with option bits (0 = dspark_markov_draft); unknown bits are
  * DSPARK_ERR_INVALID_ARG. Arguments, outputs and errors as dspark_markov_draft. */
@@ -271,8 +293,10 @@ int dspark_verify_markov(int B, int V, int r, int gamma,
  *   K_out     [1]       int32 total verify tokens R + n* (nullable)
  *   theta_out [1]       fp32 Theta(n*) (nullable)
  *   a_out   [R][gamma]  fp32 prefix survival (nullable)
- * Runs as one workgroup; the ranking key keeps 32 mantissa bits of each fp64 a. The
- * workspace holds the fp64 prefix products (R * gamma * 8 bytes).
+ * Up to 64 candidates it runs as one wave; past that as three launches (keys, ranks, the Theta
+ * scan and lengths). Each candidate's ranking key keeps the sign, the exponent and 32
+ * mantissa bits of its fp64 a (44 bits), then j and r. The workspace holds per candidate the
+ * key in row order, the key in ranked order and its rank (R * gamma * 20 bytes).
  */
 size_t dspark_schedule_workspace_bytes(int R, int gamma, int Bmax);
 int dspark_schedule(int R, int gamma, const float* conf, const float* temp,

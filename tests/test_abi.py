@@ -284,3 +284,50 @@ def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.load(str(tmp_path / "nope.so"))
+
+
+def _plan(lib, B, V, r, G, wdt, W1=FAKE, W2=FAKE, U=FAKE, Ld=None, options=0):
+    path, one, nb = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_size_t(0)
+    st = lib.dspark_markov_draft_plan(B, V, r, G, wdt, W1, W2, U, Ld, options, ctypes.byref(path),
+                                      ctypes.byref(one), ctypes.byref(nb))
+    return st, path.value, one.value, nb.value
+
+
+def test_draft_plan_host_rules(lib):
+    """The plan of an exact call: its path (U and the logits output's alignment included),
+    whether it runs in one launch, and the workspace it needs, which is never more than the
+    all-path figure and drops the logits rows where the path does not use them."""
+    B, V, r, G = 64, 151936, 256, 16
+    full = lib.dspark_markov_draft_workspace_bytes(B, V, r, G)
+    st, path, one, nb = _plan(lib, B, V, r, G, 1)
+    assert st == binding.OK and path == 3 and one == 0 and nb <= full          # slab: no rows
+    assert nb < full - 2 * B * V * 4 + 4096
+    odd = ctypes.c_void_p(0x1004)
+    st, path, _, nb_m = _plan(lib, B, V, r, G, 1, U=odd)                         # U misaligned
+    assert st == binding.OK and path == 1 and nb_m == full                      # MFMA, rows in ws
+    st, path, _, nb_ml = _plan(lib, B, V, r, G, 1, U=odd, Ld=FAKE)              # logits to the caller
+    assert path == 1 and nb_ml == full - 2 * ((B * V * 4 + 255) // 256 * 256)
+    st, path, _, nb_s = _plan(lib, B, V, r, G, 0)                                # fp32: sweep
+    assert path == 0 and nb_s == full
+    st, path, _, _ = _plan(lib, B, V, r, G, 1, options=binding.DRAFT_PER_POSITION)
+    assert path == 3
+    assert _plan(lib, 0, V, r, G, 1)[0] == binding.ERR_INVALID_ARG
+    assert _plan(lib, B, V, r, 65, 1)[0] == binding.ERR_INVALID_ARG
+    assert _plan(lib, B, V, r, G, 5)[0] == binding.ERR_INVALID_ARG
+    assert _plan(lib, B, V, r, G, 1, options=2)[0] == binding.ERR_INVALID_ARG
+    st = lib.dspark_markov_draft_plan(B, V, r, G, 1, FAKE, FAKE, FAKE, None, 0, None, None, None)
+    assert st == binding.OK                                                      # outputs nullable
+
+
+@cpu_only
+def test_draft_accepts_the_planned_workspace(lib):
+    """A call checks its workspace against its own plan: the planned bytes pass the check (the
+    call then fails only at launch, here without a device), one byte less is refused."""
+    B, V, r, G = 64, 151936, 256, 16
+    _, _, _, nb = _plan(lib, B, V, r, G, 1)
+    f = lib.dspark_markov_draft_ex
+    f.argtypes = ([ctypes.c_int] * 4 + [ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 7 +
+                  [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int])
+    args = (B, V, r, G, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, None, FAKE)
+    assert f(*args, nb - 1, None, 0) == binding.ERR_WORKSPACE
+    assert f(*args, nb, None, 0) != binding.ERR_WORKSPACE

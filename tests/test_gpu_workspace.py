@@ -87,3 +87,59 @@ def test_one_launch_drafts_ignore_stale_slots(gpu, fill, B, V, G, want_logits):
     rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"], g["lse"],
                       range(B), gL=g.get("L"))
     assert rep.ties <= tie_bound(rep)
+
+
+@pytest.mark.parametrize("B,V,G", [(1, 151936, 4), (24, 20000, 4)])
+def test_one_launch_give_up_is_reported(gpu, B, V, G):
+    """Failure injection from the host (DSPARK_DRAFT_TEST_SPIN: each wait polls about once):
+    the one-launch forms give up, drain, write -1 from the first position they could not draw,
+    and count the workgroups that gave up in bytes 0..3 of the workspace. The next ordinary
+    call on the same workspace draws every position (count 0) and matches a fresh call."""
+    c = synth.custom(1300 + B, B=B, V=V, r=16, gamma=G, w_dtype="bf16", w_sigma=0.3)
+    d = synth.draft_inputs(c)
+    U, W1, W2, x0, u = dev(d["U"]), dev(d["W1"]), dev(d["W2"]), dev(d["x0"]), dev(d["u"])
+    path, one, nbytes = dspark.markov_draft_plan(U, W1, W2)
+    assert one and path == ("resident" if B == 1 else "slab")
+    ws = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda")
+    bad = dspark.markov_draft(U, W1, W2, x0, u, ws=ws, test_spin=True)
+    torch.cuda.synchronize()
+    gave = binding.draft_gave_up(ws)
+    xb = host(bad["x"])
+    assert gave >= 1, "a one-poll wait on a multi-workgroup launch should give up"
+    assert (xb == -1).any()
+    for b in range(B):                          # -1 from some position on, valid before it
+        row = xb[b]
+        k = int(np.argmax(row == -1)) if (row == -1).any() else G
+        assert np.all(row[k:] == -1) and np.all((row[:k] >= 0) & (row[:k] < V))
+    good = dspark.markov_draft(U, W1, W2, x0, u, ws=ws)
+    torch.cuda.synchronize()
+    assert binding.draft_gave_up(ws) == 0
+    fresh = dspark.markov_draft(U, W1, W2, x0, u)
+    torch.cuda.synchronize()
+    for k in ("x", "q", "lse"):
+        assert np.array_equal(host(good[k]).view(np.uint8), host(fresh[k]).view(np.uint8)), k
+
+
+def test_workspace_cache_is_per_stream_and_plan_sized(gpu):
+    """The binding keeps one cached workspace per (device, stream, kind); a call on a second
+    stream gets its own. The single-request draft's planned workspace holds no logits rows."""
+    c = synth.custom(1310, B=1, V=151936, r=256, gamma=7, w_dtype="bf16")
+    d = synth.draft_inputs(c)
+    U, W1, W2 = dev(d["U"]), dev(d["W1"]), dev(d["W2"])
+    path, one, nbytes = dspark.markov_draft_plan(U, W1, W2)
+    assert path == "resident" and one
+    lib = binding.load()
+    assert nbytes < 64 * 1024 < lib.dspark_markov_draft_workspace_bytes(1, c.V, c.r, c.gamma)
+    s2 = torch.cuda.Stream()
+    a = binding.workspace(nbytes, torch.device("cuda:0"), "draft")
+    b = binding.workspace(nbytes, torch.device("cuda:0"), "draft", s2)
+    assert a.data_ptr() != b.data_ptr()
+    x0, u = dev(d["x0"]), dev(d["u"])
+    main = torch.cuda.current_stream()
+    s2.wait_stream(main)
+    with torch.cuda.stream(s2):                 # one-launch drafts must not overlap: in turn
+        o2 = dspark.markov_draft(U, W1, W2, x0, u)
+    main.wait_stream(s2)
+    o1 = dspark.markov_draft(U, W1, W2, x0, u)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o1["x"]), host(o2["x"]))
