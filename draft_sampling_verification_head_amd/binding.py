@@ -26,7 +26,7 @@ STS_NLL, STS_ECE = 0, 1
 EXPORTS = (
     "dspark_status_string", "dspark_last_error", "dspark_version",
     "dspark_markov_draft_path", "dspark_markov_draft_one_launch", "dspark_markov_draft_workspace_bytes",
-    "dspark_markov_draft_plan",
+    "dspark_markov_draft_plan", "dspark_noalloc_scratch_bytes", "dspark_markov_draft_noalloc",
     "dspark_markov_draft", "dspark_markov_draft_ex",
     "dspark_verify_workspace_bytes", "dspark_verify",
     "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
@@ -49,6 +49,8 @@ _SIGS = {
     "dspark_markov_draft_one_launch": (_I, [_I, _I, _I, _I, _P, _P, _I]),
     "dspark_markov_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "dspark_markov_draft_plan": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
+    "dspark_noalloc_scratch_bytes": (_Z, []),
+    "dspark_markov_draft_noalloc": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I]),
     "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_markov_draft_ex": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _I]),
     "dspark_verify_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -237,6 +239,35 @@ def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=Fa
                                     _stream(stream), opts)
     _check(st, "dspark_markov_draft")
     return dict(x=x, q=q, lse=lse, L=L)
+
+
+def markov_draft_noalloc(U, W1, W2, x0, u, *, out, per_position=False, stream=None):
+    """dspark_markov_draft_noalloc: the draft with the library's static scratch instead of a
+    workspace. ``out`` holds the caller's output tensors (x required; q, lse, L optional);
+    nothing is allocated here either. Returns ``out``."""
+    torch = _torch()
+    lib = load()
+    B, G, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    wdt = {torch.float32: F32, torch.bfloat16: BF16}.get(W1.dtype)
+    if wdt is None:
+        raise TypeError("W1/W2 must be float32 or bfloat16")
+    _need(U, "U", torch.float32, (B, G, V), dev)
+    _need(W1, "W1", W1.dtype, (V, r), dev)
+    _need(W2, "W2", W1.dtype, (r, V), dev)
+    _need(x0, "x0", torch.int32, (B,), dev)
+    _need(u, "u", torch.float32, (B, G), dev)
+    _need(out["x"], "x", torch.int32, (B, G), dev)
+    for k, shape in (("q", (B, G)), ("lse", (B, G)), ("L", (B, G, V))):
+        if out.get(k) is not None:
+            _need(out[k], k, torch.float32, shape, dev)
+    st = lib.dspark_markov_draft_noalloc(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(x0),
+                                         _ptr(u), _ptr(out["x"]), _ptr(out.get("q")),
+                                         _ptr(out.get("lse")), _ptr(out.get("L")), _stream(stream),
+                                         DRAFT_PER_POSITION if per_position else 0)
+    _check(st, "dspark_markov_draft_noalloc")
+    return out
 
 
 def verify(Ld, Lt, x, u_acc, u_fin, *, t_off=None, length=None, ld_lse=None, want_lse=False,

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dspark.h"
 #include "kernels.h"
@@ -220,6 +221,69 @@ int dspark_markov_draft_ex(int B, int V, int r, int gamma, const float* U, const
     const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "markov_draft");
     return ok();
+}
+
+}  // extern "C"
+
+// Scratch of the allocation-free draft: one static device array per GPU the library runs on
+// (held until the process ends). Host code never passes the array's name to a kernel: its
+// device address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and is kept per device.
+constexpr size_t kNoAllocScratch = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, or nullptr with *err set.
+void* scratch_for_current_device(hipError_t* err) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *err = hipSuccess;
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dspark_noalloc_scratch_bytes(void) { return kNoAllocScratch; }
+
+int dspark_markov_draft_noalloc(int B, int V, int r, int gamma, const float* U, const void* W1,
+                                const void* W2, int w_dtype, const int32_t* x0, const float* u,
+                                int32_t* x_out, float* q_out, float* lse_out, float* Ld_out,
+                                void* stream, int options) {
+    size_t need = 0;
+    const int st = dspark_markov_draft_plan(B, V, r, gamma, w_dtype, W1, W2, U, Ld_out, options,
+                                            nullptr, nullptr, &need);
+    if (st != DSPARK_OK) return st;
+    if (need > kNoAllocScratch)
+        return fail(DSPARK_ERR_UNSUPPORTED,
+                    "markov_draft_noalloc: this call needs %zu bytes of scratch, the static "
+                    "scratch holds %zu (pass Ld_out, or use dspark_markov_draft with a workspace)",
+                    need, kNoAllocScratch);
+    hipError_t e = hipSuccess;
+    void* ws = scratch_for_current_device(&e);
+    if (!ws) return hip_fail(e, "markov_draft_noalloc/scratch");
+    return dspark_markov_draft_ex(B, V, r, gamma, U, W1, W2, w_dtype, x0, u, x_out, q_out, lse_out,
+                                  Ld_out, ws, kNoAllocScratch, stream, options);
 }
 
 int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const void* W1,

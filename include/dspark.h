@@ -174,6 +174,30 @@ int dspark_markov_draft_ex(int B, int V, int r, int gamma,
                            void* ws, size_t ws_bytes, void* stream, int options);
 
 /*
+ * Allocation-free draft, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). It is dspark_markov_draft_ex
+ * with the workspace taken from a static device array of dspark_noalloc_scratch_bytes()
+ * (32 MiB) that the library holds on each GPU it runs on until the process ends; it calls no
+ * allocating routine. Arguments, outputs, paths and results are those of
+ * dspark_markov_draft_ex bit for bit (the caller still passes inputs and outputs).
+ * A call whose path needs more scratch than the array holds (dspark_markov_draft_plan's
+ * ws_bytes; e.g. the sweep or MFMA path without Ld_out at large B * V) returns
+ * DSPARK_ERR_UNSUPPORTED and enqueues nothing. Every call on one GPU shares that GPU's array
+ * and finds the last call's bytes in it, which the draft accepts (its slots carry their own
+ * call counter), so nothing needs clearing; calls that overlap on one GPU (other streams,
+ * other threads) race on the array and must be ordered by the caller. The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress) with that device current;
+ * a failure there returns DSPARK_ERR_HIP. The give-up word of a one-launch call is bytes 0..3
+ * of the array.
+ */
+size_t dspark_noalloc_scratch_bytes(void);
+int dspark_markov_draft_noalloc(int B, int V, int r, int gamma,
+                                const float* U, const void* W1, const void* W2, int w_dtype,
+                                const int32_t* x0, const float* u,
+                                int32_t* x_out, float* q_out, float* lse_out, float* Ld_out,
+                                void* stream, int options);
+
+/*
  * Lossless rejection-sampling verification.
  * [P1] section "大模型推理的显存瓶颈与推测解码的演进逻辑" and [P3] intro: keep the longest accepted
  * prefix, resample at the first rejection, add a bonus token when all are kept. Rule (the
