@@ -32,6 +32,12 @@ Functions and what pins them (all pins live in ``tests/test_oracle_*.py``):
   logsumexp against scipy and a chi-squared test of the sampler. Its ``forced`` option
   (the conditional laws along a given block) is pinned by the permutation chain on an
   arbitrary block and by equality with the plain draft on its own draws.
+* ``rnn_draft`` - [P3] "Semi-Autoregressive Generation" (the RNN head: a recurrent state
+  inside the block) and [P1] "DSpark 架构设计：半自回归生成与马尔可夫修正" (its paragraph), with
+  the reading h_1 = W1[x_0], h_k = A h_{k-1} + W1[x_{k-1}], B_k = h_k W2. Pinned by A = 0
+  reproducing ``markov_draft`` bit for bit, a permutation-matrix A with one-hot W1 and
+  log-integer W2 (an integer law of the whole prefix, exact tokens and states), the A = 2I
+  chain whose context token keeps the largest weight, and forcing on its own draws.
 * ``verify`` - [P1] "大模型推理的显存瓶颈与推测解码的演进逻辑" (rejection sampling) and [P3]
   intro (longest prefix + bonus). Pinned by p_d = p_t, zero target mass on a draft token,
   len = 0, and chi-squared losslessness (single position and multi-round joint). Its
@@ -59,6 +65,7 @@ Functions and what pins them (all pins live in ``tests/test_oracle_*.py``):
 """
 from .numerics import decode_factor, clamp_uniform, softmax_row, inverse_cdf
 from .draft import markov_draft
+from .rnn import rnn_draft
 from .verify import verify, accept_test
 from .tv import tv_labels, tv_row_pair
 from .schedule import (temperature_scale, prefix_survival, schedule, brute_force_schedule,
@@ -66,7 +73,7 @@ from .schedule import (temperature_scale, prefix_survival, schedule, brute_force
 from . import sts
 
 __all__ = [
-    "decode_factor", "clamp_uniform", "softmax_row", "inverse_cdf", "markov_draft",
+    "decode_factor", "clamp_uniform", "softmax_row", "inverse_cdf", "markov_draft", "rnn_draft",
     "verify", "accept_test", "tv_labels", "tv_row_pair", "temperature_scale",
     "prefix_survival", "schedule", "brute_force_schedule", "theta_curve", "lagged_confidences",
     "lagged_schedule", "GLOBAL",

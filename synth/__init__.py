@@ -35,7 +35,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # stream ids
-T_U, T_W1, T_W2, T_X0, T_UDRAFT, T_TNOISE, T_UACC, T_UFIN, T_CONF, T_BOOST, T_UX = range(11)
+T_U, T_W1, T_W2, T_X0, T_UDRAFT, T_TNOISE, T_UACC, T_UFIN, T_CONF, T_BOOST, T_UX, T_A = range(12)
 
 U_MAX = np.float32(1.0 - 2.0 ** -24)
 
@@ -134,6 +134,13 @@ def factors(c: Config):
     if c.w_dtype == "bf16":
         return f32_to_bf16_bits(w1), f32_to_bf16_bits(w2)
     return np.ascontiguousarray(w1), np.ascontiguousarray(w2)
+
+
+def rnn_factor(c: Config, radius: float = 0.5) -> np.ndarray:
+    """The RNN head's recurrence A [r][r] ~ N(0, (radius / sqrt(r))^2): spectral radius about
+    `radius`, so the state stays of the size of a W1 row. bf16 bits or float32 as c.w_dtype."""
+    a = rng(c.seed, T_A).standard_normal((c.r, c.r), dtype=np.float32) * np.float32(radius / np.sqrt(c.r))
+    return f32_to_bf16_bits(a) if c.w_dtype == "bf16" else np.ascontiguousarray(a)
 
 
 # ----------------------------------------------------------------------------- logits
