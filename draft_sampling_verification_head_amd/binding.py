@@ -27,6 +27,7 @@ EXPORTS = (
     "dspark_status_string", "dspark_last_error", "dspark_version",
     "dspark_markov_draft_path", "dspark_markov_draft_one_launch", "dspark_markov_draft_workspace_bytes",
     "dspark_markov_draft_plan", "dspark_noalloc_scratch_bytes", "dspark_markov_draft_noalloc",
+    "dspark_rnn_draft_workspace_bytes", "dspark_rnn_draft_path", "dspark_rnn_draft",
     "dspark_markov_draft", "dspark_markov_draft_ex",
     "dspark_verify_workspace_bytes", "dspark_verify",
     "dspark_verify_tv_workspace_bytes", "dspark_verify_tv",
@@ -50,6 +51,9 @@ _SIGS = {
     "dspark_markov_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "dspark_markov_draft_plan": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]),
     "dspark_noalloc_scratch_bytes": (_Z, []),
+    "dspark_rnn_draft_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "dspark_rnn_draft_path": (_I, [_I, _I, _I, _P, _P, _P]),
+    "dspark_rnn_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_markov_draft_noalloc": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I]),
     "dspark_markov_draft": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_markov_draft_ex": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P, _I]),
@@ -239,6 +243,44 @@ def markov_draft(U, W1, W2, x0, u, *, want_q=True, want_lse=True, want_logits=Fa
                                     _stream(stream), opts)
     _check(st, "dspark_markov_draft")
     return dict(x=x, q=q, lse=lse, L=L)
+
+
+def rnn_draft_path(B: int, W1, W2, A) -> str:
+    """dspark_rnn_draft_path: "resident" (one launch) or "mfma" (launches per position)."""
+    V, r = W1.shape
+    return PATH_NAMES[load().dspark_rnn_draft_path(B, V, r, _ptr(W1), _ptr(W2), _ptr(A))]
+
+
+def rnn_draft(U, W1, W2, A, x0, u, *, want_q=True, want_lse=True, want_logits=False,
+              want_state=False, stream=None, ws=None):
+    """dspark_rnn_draft: the RNN-head draft (bf16 factors). U [B][gamma][V] fp32, W1 [V][r],
+    W2 [r][V], A [r][r] bf16, x0 [B] int32, u [B][gamma] fp32. Returns dict x, q, lse, L, h."""
+    torch = _torch()
+    lib = load()
+    B, G, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    if W1.dtype != torch.bfloat16:
+        raise TypeError("rnn_draft needs bfloat16 factors")
+    _need(U, "U", torch.float32, (B, G, V), dev)
+    _need(W1, "W1", torch.bfloat16, (V, r), dev)
+    _need(W2, "W2", torch.bfloat16, (r, V), dev)
+    _need(A, "A", torch.bfloat16, (r, r), dev)
+    _need(x0, "x0", torch.int32, (B,), dev)
+    _need(u, "u", torch.float32, (B, G), dev)
+    f32 = lambda shape: torch.empty(shape, dtype=torch.float32, device=dev)   # noqa: E731
+    x = torch.empty((B, G), dtype=torch.int32, device=dev)
+    q = f32((B, G)) if want_q else None
+    lse = f32((B, G)) if want_lse else None
+    L = f32((B, G, V)) if want_logits else None
+    h = f32((B, G, r)) if want_state else None
+    nbytes = lib.dspark_rnn_draft_workspace_bytes(B, V, r, G)
+    ws = workspace(nbytes, dev, "rnn_draft", stream, ws)
+    st = lib.dspark_rnn_draft(B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), _ptr(A), BF16, _ptr(x0), _ptr(u),
+                              _ptr(x), _ptr(q), _ptr(lse), _ptr(L), _ptr(h), _ptr(ws), ws.numel(),
+                              _stream(stream))
+    _check(st, "dspark_rnn_draft")
+    return dict(x=x, q=q, lse=lse, L=L, h=h)
 
 
 def markov_draft_noalloc(U, W1, W2, x0, u, *, out, per_position=False, stream=None):

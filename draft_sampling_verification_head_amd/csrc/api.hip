@@ -294,6 +294,80 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
                                   Ld_out, ws, ws_bytes, stream, 0);
 }
 
+// ----------------------------------------------------------------------------- RNN head
+namespace {
+
+// header, slots (single-request one-launch form), tile partials, logits rows (when the caller
+// does not take them), fp32 state ping-pong, bf16 hi / lo state rows (batched form)
+size_t rnn_ws_bytes(int B, int V, int r, int gamma) {
+    const int rp = dspark::rnn_rank_pad(r);
+    return kDraftHeader + align_up(draft_slot_bytes(V, gamma)) +
+           2 * align_up(draft_part_count(B, V) * sizeof(float2)) +
+           2 * align_up(static_cast<size_t>(B) * V * sizeof(float)) +
+           2 * align_up(static_cast<size_t>(B) * r * sizeof(float)) +
+           align_up(static_cast<size_t>(B) * 2 * rp * sizeof(uint16_t));
+}
+
+}  // namespace
+
+size_t dspark_rnn_draft_workspace_bytes(int B, int V, int r, int gamma) {
+    if (B < 1 || V < 1 || gamma < 1 || r < 1) return 0;
+    return rnn_ws_bytes(B, V, r, gamma);
+}
+
+int dspark_rnn_draft(int B, int V, int r, int gamma, const float* U, const void* W1,
+                     const void* W2, const void* A, int w_dtype, const int32_t* x0, const float* u,
+                     int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, float* h_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+    if (B < 1 || V < 1 || gamma < 1 || r < 1)
+        return fail(DSPARK_ERR_INVALID_ARG, "rnn_draft: B=%d V=%d r=%d gamma=%d must be >= 1", B, V,
+                    r, gamma);
+    if (!draft_sizes_ok(B, V, r, gamma))
+        return fail(DSPARK_ERR_UNSUPPORTED, "rnn_draft: gamma=%d r=%d B*gamma*V outside caps", gamma, r);
+    if (w_dtype != DSPARK_F32 && w_dtype != DSPARK_BF16)
+        return fail(DSPARK_ERR_INVALID_ARG, "rnn_draft: unknown w_dtype %d", w_dtype);
+    if (!U || !W1 || !W2 || !A || !x0 || !u || !x_out)
+        return fail(DSPARK_ERR_INVALID_ARG, "rnn_draft: a required pointer is NULL");
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; };
+    if (w_dtype != DSPARK_BF16 || !dspark::rnn_mfma_ok(V, r, W1, W2, A) || !al16(U))
+        return fail(DSPARK_ERR_UNSUPPORTED,
+                    "rnn_draft: needs bf16 factors, r <= 256 with r %% 8 == 0, V %% 8 == 0 and "
+                    "16-byte aligned U, W1, W2, A (w_dtype=%d r=%d V=%d)", w_dtype, r, V);
+    const size_t need = rnn_ws_bytes(B, V, r, gamma);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "rnn_draft: workspace %zu bytes, need %zu", ws_bytes, need);
+    Carver c(ws);
+    dspark::RnnCall rc;
+    dspark::DraftCall& dc = rc.d;
+    dc.B = B; dc.V = V; dc.r = r; dc.gamma = gamma; dc.w_dtype = w_dtype;
+    dc.U = U; dc.W1 = W1; dc.W2 = W2; dc.x0 = x0; dc.u = u;
+    dc.x_out = x_out; dc.q_out = q_out; dc.lse_out = lse_out;
+    dc.status = c.take<unsigned>(kDraftHeader / sizeof(unsigned));
+    dc.slots = reinterpret_cast<float2*>(c.take<char>(draft_slot_bytes(V, gamma)));
+    dc.part[0] = c.take<float2>(draft_part_count(B, V));
+    dc.part[1] = c.take<float2>(draft_part_count(B, V));
+    float* lbuf[2] = {c.take<float>(static_cast<size_t>(B) * V), c.take<float>(static_cast<size_t>(B) * V)};
+    for (int k = 0; k < gamma; ++k)
+        dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
+    dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
+    dc.L_out = Ld_out != nullptr;
+    rc.A = A;
+    rc.h_out = h_out;
+    rc.hstate[0] = c.take<float>(static_cast<size_t>(B) * r);
+    rc.hstate[1] = c.take<float>(static_cast<size_t>(B) * r);
+    rc.hrows = c.take<uint16_t>(static_cast<size_t>(B) * 2 * dspark::rnn_rank_pad(r));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = dspark::rnn_resident_ok(B, V, r, W1, W2, A) ? dspark::launch_rnn_resident(rc, st)
+                                                                     : dspark::launch_rnn_mfma(rc, st);
+    if (e != hipSuccess) return hip_fail(e, "rnn_draft");
+    return ok();
+}
+
+int dspark_rnn_draft_path(int B, int V, int r, const void* W1, const void* W2, const void* A) {
+    if (dspark::rnn_resident_ok(B, V, r, W1, W2, A)) return DSPARK_PATH_RESIDENT;
+    return DSPARK_PATH_MFMA;
+}
+
 // ----------------------------------------------------------------------------- verify / TV
 namespace {
 

@@ -53,6 +53,8 @@ struct MfmaArgs {
     const float* U;
     const uint16_t* W1;
     const uint16_t* W2;
+    const uint16_t* Hrows;    // RNN head: the state of request b as bf16 rows hi, lo at
+                              // Hrows + 2 b rp (zero beyond r); the A operand instead of W1[x]
     const int32_t* tok;       // x_{k-1}: tok[b * tok_stride]
     int tok_stride;
     float* L;                 // logits rows L + b * L_bstride
@@ -94,12 +96,17 @@ __device__ __forceinline__ float reduce_scatter32(const float (&x)[32], Op op) {
     return op(b0 ? a2[1] : a2[0], dpp_f<0xB1>(b0 ? a2[0] : a2[1]));  // quad lane ^ 1
 }
 
+// RNN = false: the Markov head (A operand = the gathered W1 rows of the previous tokens).
+// RNN = true: the RNN head's state rows, split into bf16 hi + lo parts (h = hi + lo to about
+// 2^-17 relative), each multiplied with the same W2 fragment into the same accumulators.
+template <bool RNN>
 __global__ __launch_bounds__(kThreads, 4)      // 4 waves per SIMD: two workgroups per CU
 void draft_step_mfma(MfmaArgs a) {
     extern __shared__ uint16_t sm16[];
     const int HS = a.rp + kHPad;
-    uint16_t* Hs = sm16;                              // [kMT][HS] gathered W1 rows
-    uint16_t* Ws = sm16 + kMT * HS;                   // [kWaves][kKC][kWS] W2 chunk per wave
+    uint16_t* Hs = sm16;                              // [kMT][HS] gathered W1 rows (RNN: hi)
+    uint16_t* Hl = sm16 + kMT * HS;                   // RNN: [kMT][HS] lo parts
+    uint16_t* Ws = sm16 + (RNN ? 2 : 1) * kMT * HS;   // [kWaves][kKC][kWS] W2 chunk per wave
     __shared__ float red[kWaves][kMT];
     __shared__ float rowmax[kMT];
     __shared__ int stok[kMT];
@@ -165,7 +172,17 @@ void draft_step_mfma(MfmaArgs a) {
             const int i = s / segs, c = (s % segs) * 8;
             const int t = stok[i];
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (t >= 0 && c < a.r) v = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(t) * a.r + c);
+            if (RNN) {
+                uint4 vl = make_uint4(0u, 0u, 0u, 0u);
+                if (t >= 0) {
+                    const uint16_t* hr = a.Hrows + static_cast<long long>(m0 + i) * 2 * a.rp + c;
+                    v = *reinterpret_cast<const uint4*>(hr);
+                    vl = *reinterpret_cast<const uint4*>(hr + a.rp);
+                }
+                *reinterpret_cast<uint4*>(Hl + i * HS + c) = vl;
+            } else if (t >= 0 && c < a.r) {
+                v = *reinterpret_cast<const uint4*>(a.W1 + static_cast<long long>(t) * a.r + c);
+            }
             *reinterpret_cast<uint4*>(Hs + i * HS + c) = v;
         }
     }
@@ -199,6 +216,12 @@ void draft_step_mfma(MfmaArgs a) {
                 const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Hs + (32 + l32) * HS + kofs));
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfrag, acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfrag, acc1, 0, 0, 0);
+                if (RNN) {
+                    const bf16x8 l0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Hl + l32 * HS + kofs));
+                    const bf16x8 l1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Hl + (32 + l32) * HS + kofs));
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, bfrag, acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, bfrag, acc1, 0, 0, 0);
+                }
             }
         }
     }
@@ -290,8 +313,129 @@ hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st) {
         a.tok_stride = k ? c.gamma : 1;
         a.L = c.L[k];
         a.part = c.part[k & 1];
-        hipLaunchKernelGGL(draft_step_mfma, grid, dim3(kThreads), smem, st, a);
+        a.Hrows = nullptr;
+        hipLaunchKernelGGL(draft_step_mfma<false>, grid, dim3(kThreads), smem, st, a);
         const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int k = c.gamma - 1;
+    hipLaunchKernelGGL(draft_select<kNT>, dim3((c.B + waves - 1) / waves), dim3(kSelThreads), 0, st,
+                       c.B, c.V, c.gamma, k, static_cast<const float2*>(c.part[k & 1]), a.ntiles,
+                       c.L[k], c.L_bstride, c.u, c.x_out, c.q_out, c.lse_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RNN head, batched
+// [P3] "Semi-Autoregressive Generation" (the RNN head: a recurrent state inside the block),
+// with the recurrence h_1 = W1[x_0], h_k = A h_{k-1} + W1[x_{k-1}], B_k = h_k W2.
+
+namespace {
+
+constexpr int kStateThreads = 256;      // one thread per state element (r <= 256)
+
+// One workgroup per request: h_next = (k > 0 ? A h_prev : 0) + W1[x_{k-1}] in fp32, summed
+// over j in ascending order; written as fp32 (h_next, and h_out when asked) and as the bf16
+// hi / lo rows the projection multiplies (hi = bf16(h), lo = bf16(h - hi), zero beyond r).
+// A request whose previous token is invalid is dead: its state is 0 (its logits are -inf).
+__global__ __launch_bounds__(kStateThreads)
+void rnn_state_kernel(int B, int r, int rp, int k, int gamma, const uint16_t* __restrict__ A,
+                      const uint16_t* __restrict__ W1, int V, const int32_t* __restrict__ tok,
+                      int tok_stride, const float* __restrict__ h_prev, float* __restrict__ h_next,
+                      uint16_t* __restrict__ hrows, float* __restrict__ h_out) {
+    __shared__ float hp[kMaxRank];
+    const int b = blockIdx.x, i = threadIdx.x;
+    int t = tok[static_cast<long long>(b) * tok_stride];
+    if (t < 0 || t >= V) t = -1;
+    if (k > 0 && i < r) hp[i] = h_prev[static_cast<long long>(b) * r + i];
+    __syncthreads();
+    float h = 0.0f;
+    if (i < r && t >= 0) {
+        if (k > 0) {
+            const uint16_t* Ar = A + static_cast<long long>(i) * r;
+            for (int j = 0; j < r; j += 8) {
+                const uint4 w = *reinterpret_cast<const uint4*>(Ar + j);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h = fmaf(__uint_as_float(ww[e] << 16), hp[j + 2 * e], h);
+                    h = fmaf(__uint_as_float(ww[e] & 0xffff0000u), hp[j + 2 * e + 1], h);
+                }
+            }
+        }
+        h += to_f32(W1[static_cast<long long>(t) * r + i]);
+    }
+    if (i < r) {
+        h_next[static_cast<long long>(b) * r + i] = h;
+        if (h_out) h_out[(static_cast<long long>(b) * gamma + k) * r + i] = h;
+    }
+    if (i < rp) {
+        const __bf16 hi = static_cast<__bf16>(h);
+        const __bf16 lo = static_cast<__bf16>(h - static_cast<float>(hi));
+        uint16_t* row = hrows + static_cast<long long>(b) * 2 * rp;
+        row[i] = __builtin_bit_cast(uint16_t, hi);
+        row[rp + i] = __builtin_bit_cast(uint16_t, lo);
+    }
+}
+
+}  // namespace
+
+int rnn_rank_pad(int r) {
+    int rp = (r + kKC - 1) / kKC * kKC;
+    if (rp % 8) rp += 8 - rp % 8;
+    return rp;
+}
+
+bool rnn_mfma_ok(int V, int r, const void* W1, const void* W2, const void* A) {
+    return r <= kMaxRank && (r % 8) == 0 && (V % 8) == 0 &&
+           static_cast<long long>(kMaxRank) * V < (1LL << 32) &&
+           static_cast<long long>(kMT) * 64 * V < (1LL << 32) &&
+           (reinterpret_cast<uintptr_t>(W1) % 16) == 0 && (reinterpret_cast<uintptr_t>(W2) % 16) == 0 &&
+           (reinterpret_cast<uintptr_t>(A) % 16) == 0;
+}
+
+hipError_t launch_rnn_mfma(const RnnCall& rc, hipStream_t st) {
+    const DraftCall& c = rc.d;
+    MfmaArgs a;
+    a.B = c.B; a.V = c.V; a.r = c.r; a.rp = rnn_rank_pad(c.r);
+    a.gamma = c.gamma;
+    a.ntiles = (c.V + kNT - 1) / kNT;
+    a.mgroups = (c.B + kMT - 1) / kMT;
+    a.U = c.U;
+    a.W1 = static_cast<const uint16_t*>(c.W1);
+    a.W2 = static_cast<const uint16_t*>(c.W2);
+    a.Hrows = rc.hrows;
+    a.L_bstride = c.L_bstride;
+    const unsigned grid_tiles = static_cast<unsigned>((a.ntiles + kXcds - 1) / kXcds * kXcds);
+    const dim3 grid(grid_tiles * a.mgroups);
+    const size_t smem = (2 * static_cast<size_t>(kMT) * (a.rp + kHPad) + kWaves * kKC * kWS) * sizeof(uint16_t);
+    {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(draft_step_mfma<true>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(smem));
+        if (e != hipSuccess) return e;
+    }
+    const int waves = kSelThreads / kWave;
+    for (int k = 0; k < c.gamma; ++k) {
+        if (k > 0) {
+            hipLaunchKernelGGL(draft_select<kNT>, dim3((c.B + waves - 1) / waves), dim3(kSelThreads),
+                               0, st, c.B, c.V, c.gamma, k - 1,
+                               static_cast<const float2*>(c.part[(k - 1) & 1]), a.ntiles, c.L[k - 1],
+                               c.L_bstride, c.u, c.x_out, c.q_out, c.lse_out);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        a.k = k;
+        a.tok = k ? c.x_out + (k - 1) : c.x0;
+        a.tok_stride = k ? c.gamma : 1;
+        hipLaunchKernelGGL(rnn_state_kernel, dim3(c.B), dim3(kStateThreads), 0, st, c.B, c.r, a.rp, k,
+                           c.gamma, static_cast<const uint16_t*>(rc.A), a.W1, c.V, a.tok, a.tok_stride,
+                           rc.hstate[(k + 1) & 1], rc.hstate[k & 1], rc.hrows, rc.h_out);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        a.L = c.L[k];
+        a.part = c.part[k & 1];
+        hipLaunchKernelGGL(draft_step_mfma<true>, grid, dim3(kThreads), smem, st, a);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int k = c.gamma - 1;

@@ -63,6 +63,12 @@ constexpr size_t kResLds = static_cast<size_t>(kRWaves) * kStageRows * kResTileC
 constexpr int kPartRegs = RegTiles<kResTileCols>::value;  // partials per lane in the draw
 constexpr int kMaxTiles = kWave * kPartRegs;              // 512 workgroups at most
 constexpr unsigned long long kEmpty = ~0ull;              // sentinel: both halves NaN
+// RNN head: the recurrence A, transposed into bf16 pairs (A[2p][j], A[2p+1][j]) at [j][p], sits
+// in LDS after the rank-group sums, where the W2 staging was
+constexpr size_t kRedBytes = sizeof(float) * kRWaves * kResTileCols;
+constexpr size_t kAtBytes = static_cast<size_t>(kResMaxRank) * (kResMaxRank / 2) * 4;
+constexpr size_t kResLdsRnn = kRedBytes + kAtBytes;
+static_assert(kResLdsRnn >= kResLds, "the RNN layout covers the staging area");
 static_assert(kStageLoads * kWave == kStageRows * kChunks, "staging rounds cover whole rows");
 static_assert(kResLds >= sizeof(float) * kRWaves * kResTileCols, "sums fit in the staging area");
 static_assert(kResTileCols == 640 && kRThreads + 128 == kResTileCols, "epilogue ownership");
@@ -84,6 +90,8 @@ struct ResArgs {
     unsigned long long* epoch;   // [2]: the call counter E and the ready word F (after toks)
     unsigned* status;         // number of workgroups that gave up (reset with the slots)
     unsigned spin;            // polls before a wait gives up
+    const uint16_t* A;        // RNN head: [r][r] bf16 recurrence
+    float* h_out;             // RNN head: [gamma][r] fp32 state of each position (nullable)
 };
 
 // Ready word of a call with counter e: the finaliser of the splitmix64 generator (Steele, Lea
@@ -120,12 +128,25 @@ __device__ __forceinline__ unsigned long long load_token(const unsigned long lon
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// RNN = false: the Markov head, B_k = W1[x_{k-1}] W2.
+// RNN = true: the RNN head, B_k = h_k W2 with h_1 = W1[x_0], h_k = A h_{k-1} + W1[x_{k-1}]
+// ([P3] "Semi-Autoregressive Generation": a recurrent state inside the block). Every
+// workgroup keeps h in fp32 in LDS and A (128 KB in bf16) in the LDS that the W2 staging
+// used. A h_k does not depend on the token drawn at position k, so waves 4..7 form it while
+// wave 0 waits for the position's partials; once the token is known, h_{k+1} = A h_k +
+// W1[x_k]. The products take h as bf16 hi + lo parts (h = hi + lo to about 2^-17 relative)
+// against the same W2 registers.
+template <bool RNN>
 __global__ __launch_bounds__(kRThreads, 1)
 void draft_resident(ResArgs a) {
-    __shared__ uint4 lds[kResLds / sizeof(uint4)];         // W2 staging, then rank-group sums
+    __shared__ uint4 lds[(RNN ? kResLdsRnn : kResLds) / sizeof(uint4)];   // W2 staging, then sums (+ A)
     __shared__ float2 wpart[kRWaves];
     __shared__ float tl[kResTileCols];                     // this position's logits of the tile
     __shared__ uint32_t hs[kResMaxRank / 2];               // W1[x] as bf16 pairs
+    __shared__ float hst[RNN ? kResMaxRank : 1];           // RNN: the state h_k in fp32
+    __shared__ float ah[RNN ? 2 : 1][RNN ? kResMaxRank : 1];   // RNN: A h_k, two halves of j
+    __shared__ uint32_t hhi[RNN ? kResMaxRank / 2 : 1];    // RNN: h_k as bf16 pairs, hi parts
+    __shared__ uint32_t hlo[RNN ? kResMaxRank / 2 : 1];    //                        lo parts
     __shared__ int stok;
     __shared__ int gave_up;
     __shared__ unsigned long long s_e0;                    // the call counter read at the start
@@ -172,7 +193,19 @@ void draft_resident(ResArgs a) {
             if (row < r && col < V)
                 v[rho][n] = *reinterpret_cast<const uint4*>(a.W2 + static_cast<long long>(row) * V + col);
         }
-    if (tid < kResMaxRank / 8) reinterpret_cast<uint4*>(hs)[tid] = h0;
+    if (tid < kResMaxRank / 8) {
+        reinterpret_cast<uint4*>(hs)[tid] = h0;
+        if (RNN) {                                         // h_1 = W1[x_0]: hi exact, lo zero
+            reinterpret_cast<uint4*>(hhi)[tid] = h0;
+            reinterpret_cast<uint4*>(hlo)[tid] = make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t hw[4] = {h0.x, h0.y, h0.z, h0.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hst[8 * tid + 2 * e] = __uint_as_float(hw[e] << 16);
+                hst[8 * tid + 2 * e + 1] = __uint_as_float(hw[e] & 0xffff0000u);
+            }
+        }
+    }
 #pragma unroll
     for (int rho = 0; rho < kRounds; ++rho) {
 #pragma unroll
@@ -196,6 +229,37 @@ void draft_resident(ResArgs a) {
         __syncthreads();
     }
     float (*red)[kResTileCols] = reinterpret_cast<float (*)[kResTileCols]>(lds);   // reuses the staging area
+    uint32_t* at2 = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + kRedBytes);   // RNN: A^T pairs
+    if (RNN) {
+        // A^T as bf16 pairs: at2[j * 128 + p] = (A[2p][j], A[2p+1][j]); zero beyond r. Task
+        // (p, jc) reads 8 columns of rows 2p and 2p+1; a wave's lanes take consecutive p.
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            uint4 ra[4], rb[4];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int task = tid + kRThreads * (4 * half + n);
+                const int pp = task & (kResMaxRank / 2 - 1), jc = task >> 7;
+                ra[n] = rb[n] = make_uint4(0u, 0u, 0u, 0u);
+                if (2 * pp < r && 8 * jc < r) {
+                    ra[n] = *reinterpret_cast<const uint4*>(a.A + static_cast<long long>(2 * pp) * r + 8 * jc);
+                    rb[n] = *reinterpret_cast<const uint4*>(a.A + static_cast<long long>(2 * pp + 1) * r + 8 * jc);
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int task = tid + kRThreads * (4 * half + n);
+                const int pp = task & (kResMaxRank / 2 - 1), jc = task >> 7;
+                const uint32_t wa[4] = {ra[n].x, ra[n].y, ra[n].z, ra[n].w};
+                const uint32_t wb[4] = {rb[n].x, rb[n].y, rb[n].z, rb[n].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    at2[(8 * jc + 2 * e) * (kResMaxRank / 2) + pp] = (wa[e] & 0xffffu) | (wb[e] << 16);
+                    at2[(8 * jc + 2 * e + 1) * (kResMaxRank / 2) + pp] = (wa[e] >> 16) | (wb[e] & 0xffff0000u);
+                }
+            }
+        }
+    }
 
     if (tid == 0) gave_up = 0;
     const unsigned long long key = ready_word(s_e0);
@@ -209,15 +273,23 @@ void draft_resident(ResArgs a) {
     for (; k < a.gamma; ++k) {
         // 2. projection from registers: this wave's 32 ranks of the lane's 10 columns, with
         //    h = W1[x_{k-1}] from LDS (staged before the last workgroup barrier)
-        uint32_t hv[kGroupRanks / 2];
+        if (RNN && a.h_out && blockIdx.x == 0 && tid < r) a.h_out[static_cast<long long>(k) * r + tid] = hst[tid];
+        uint32_t hv[kGroupRanks / 2], hvl[RNN ? kGroupRanks / 2 : 1];
 #pragma unroll
-        for (int m = 0; m < kGroupRanks / 2; ++m) hv[m] = hs[(kGroupRanks / 2) * wave + m];
+        for (int m = 0; m < kGroupRanks / 2; ++m) hv[m] = (RNN ? hhi : hs)[(kGroupRanks / 2) * wave + m];
+        if (RNN) {
+#pragma unroll
+            for (int m = 0; m < kGroupRanks / 2; ++m) hvl[m] = hlo[(kGroupRanks / 2) * wave + m];
+        }
         float acc[kLaneCols];
 #pragma unroll
         for (int i = 0; i < kLaneCols; ++i) {
             float s = 0.0f;
 #pragma unroll
-            for (int m = 0; m < kGroupRanks / 2; ++m) s = dot2(w[i][m], hv[m], s);
+            for (int m = 0; m < kGroupRanks / 2; ++m) {
+                s = dot2(w[i][m], hv[m], s);
+                if (RNN) s = dot2(w[i][m], hvl[m], s);
+            }
             acc[i] = s;
         }
 #pragma unroll
@@ -354,9 +426,38 @@ void draft_resident(ResArgs a) {
                 }
             }
         }
+        else if (RNN && wave >= kRWaves / 2 && k + 1 < a.gamma) {
+            // A h_k: thread (p, half) forms rows 2p, 2p+1 over j in [128 half, 128 half + 128)
+            const int t2 = tid - kRThreads / 2;
+            const int pp = t2 & (kResMaxRank / 2 - 1), jh = t2 >> 7;
+            const int j0 = jh * (kResMaxRank / 2), j1 = min(j0 + kResMaxRank / 2, r);
+            float s0 = 0.0f, s1 = 0.0f;
+            for (int j = j0; j < j1; ++j) {
+                const uint32_t wv = at2[j * (kResMaxRank / 2) + pp];
+                const float hj = hst[j];
+                s0 = fmaf(__uint_as_float(wv << 16), hj, s0);
+                s1 = fmaf(__uint_as_float(wv & 0xffff0000u), hj, s1);
+            }
+            ah[jh][2 * pp] = s0;
+            ah[jh][2 * pp + 1] = s1;
+        }
         __syncthreads();
         if (gave_up) break;
         tok = stok;
+        if (RNN && k + 1 < a.gamma) {
+            // h_{k+1} = A h_k + W1[x_k] (hs holds W1[x_k] as bf16 pairs, zero for no token)
+            if (tid < kResMaxRank) {
+                const uint32_t pr = hs[tid >> 1];
+                const float w1v = __uint_as_float((tid & 1) ? (pr & 0xffff0000u) : (pr << 16));
+                const float h = (tid < r) ? (ah[0][tid] + ah[1][tid]) + w1v : 0.0f;
+                hst[tid] = h;
+                const __bf16 hi = static_cast<__bf16>(h);
+                const __bf16 lo = static_cast<__bf16>(h - static_cast<float>(hi));
+                reinterpret_cast<uint16_t*>(hhi)[tid] = __builtin_bit_cast(uint16_t, hi);
+                reinterpret_cast<uint16_t*>(hlo)[tid] = __builtin_bit_cast(uint16_t, lo);
+            }
+            __syncthreads();
+        }
     }
     // every workgroup has read E: each published its last partial, which workgroup 0 saw
     // (or the launch gave up, and E moves on all the same)
@@ -376,6 +477,7 @@ struct DeviceFit {
     int occupancy = -1;
 };
 
+template <bool RNN>
 DeviceFit device_fit() {
     thread_local DeviceFit cache[64];
     int dev = 0;
@@ -384,7 +486,7 @@ DeviceFit device_fit() {
     if (f.cus < 0) {
         int cus = 0, occ = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, draft_resident, kRThreads, 0) !=
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, draft_resident<RNN>, kRThreads, 0) !=
                 hipSuccess)
             return DeviceFit{};
         f.cus = cus;
@@ -395,24 +497,18 @@ DeviceFit device_fit() {
 
 int tiles_of(int V) { return (V + kResTileCols - 1) / kResTileCols; }
 
-}  // namespace
-
-// tile partials [gamma][G], the token slots [gamma], then the call counter and ready word
-size_t draft_resident_slot_bytes(int V, int gamma) {
-    return static_cast<size_t>(gamma) * tiles_of(V) * sizeof(float2) +
-           (static_cast<size_t>(gamma) + 2) * sizeof(unsigned long long);
-}
-
-bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
-    if (B != 1 || w_dtype != 1 || r > kResMaxRank || (r % 8) != 0 || (V % 8) != 0) return false;
+template <bool RNN>
+bool fits(int V, int r, const void* W1, const void* W2) {
+    if (r > kResMaxRank || (r % 8) != 0 || (V % 8) != 0) return false;
     if ((reinterpret_cast<uintptr_t>(W1) % 16) != 0 || (reinterpret_cast<uintptr_t>(W2) % 16) != 0)
         return false;
-    const DeviceFit f = device_fit();
+    const DeviceFit f = device_fit<RNN>();
     const int G = tiles_of(V);
     return f.cus > 0 && f.occupancy >= 1 && G <= f.cus && G <= kMaxTiles;
 }
 
-hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {
+template <bool RNN>
+hipError_t launch(const DraftCall& c, const void* A, float* h_out, hipStream_t st) {
     ResArgs a;
     a.V = c.V; a.r = c.r; a.gamma = c.gamma;
     a.G = tiles_of(c.V);
@@ -428,8 +524,34 @@ hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {
     a.epoch = a.toks + c.gamma;
     a.status = c.status;
     a.spin = c.spin;
-    hipLaunchKernelGGL(draft_resident, dim3(a.G), dim3(kRThreads), 0, st, a);
+    a.A = static_cast<const uint16_t*>(A);
+    a.h_out = h_out;
+    hipLaunchKernelGGL(draft_resident<RNN>, dim3(a.G), dim3(kRThreads), 0, st, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// tile partials [gamma][G], the token slots [gamma], then the call counter and ready word
+size_t draft_resident_slot_bytes(int V, int gamma) {
+    return static_cast<size_t>(gamma) * tiles_of(V) * sizeof(float2) +
+           (static_cast<size_t>(gamma) + 2) * sizeof(unsigned long long);
+}
+
+bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
+    return B == 1 && w_dtype == 1 && fits<false>(V, r, W1, W2);
+}
+
+hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {
+    return launch<false>(c, nullptr, nullptr, st);
+}
+
+bool rnn_resident_ok(int B, int V, int r, const void* W1, const void* W2, const void* A) {
+    return B == 1 && (reinterpret_cast<uintptr_t>(A) % 16) == 0 && fits<true>(V, r, W1, W2);
+}
+
+hipError_t launch_rnn_resident(const RnnCall& c, hipStream_t st) {
+    return launch<true>(c.d, c.A, c.h_out, st);
 }
 
 }  // namespace dspark

@@ -56,6 +56,21 @@ int draft_resident_tile_cols();
 size_t draft_resident_slot_bytes(int V, int gamma);
 hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st);
 
+// RNN-head draft (the recurrence h_1 = W1[x_0], h_k = A h_{k-1} + W1[x_{k-1}], B_k = h_k W2):
+// the draft's arguments and workspace plus the recurrence and the state buffers.
+struct RnnCall {
+    DraftCall d;              // bf16 factors; d.slots / d.status used by the one-launch form
+    const void* A;            // [r][r] bf16
+    float* h_out;             // [B][gamma][r] fp32 states (nullable)
+    float* hstate[2];         // [B][r] fp32, ping-pong (batched form)
+    uint16_t* hrows;          // [B][2][rnn_rank_pad(r)] bf16 hi / lo rows (batched form)
+};
+int rnn_rank_pad(int r);
+bool rnn_mfma_ok(int V, int r, const void* W1, const void* W2, const void* A);
+hipError_t launch_rnn_mfma(const RnnCall& c, hipStream_t st);
+bool rnn_resident_ok(int B, int V, int r, const void* W1, const void* W2, const void* A);
+hipError_t launch_rnn_resident(const RnnCall& c, hipStream_t st);
+
 // ---------------------------------------------------------------- verify / TV
 struct RowSet {               // the draft and target rows of a verify batch
     int B, V, gamma;

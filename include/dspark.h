@@ -174,6 +174,37 @@ int dspark_markov_draft_ex(int B, int V, int r, int gamma,
                            void* ws, size_t ws_bytes, void* stream, int options);
 
 /*
+ * RNN-head sequential draft.
+ * [P3] "Semi-Autoregressive Generation": the sequential stage samples x_k ~ p_k(v) proportional
+ * to exp(U_k(v) + B_k(x_<k, v)); besides the default Markov head it names an RNN head that keeps
+ * a recurrent state inside the block. [P1] section "DSpark 架构设计：半自回归生成与马尔可夫修正"
+ * (the RNN head paragraph): an optional head whose hidden state, updated along the block,
+ * carries longer-range dependence. The pages give no update rule; this library reads it as the
+ * linear recurrence of the head's rank r
+ *     h_1 = W1[x_0],  h_k = A h_{k-1} + W1[x_{k-1}],  B_k = h_k W2,
+ * so that A = 0 is the Markov head (dspark_markov_draft, to fp32 rounding order).
+ *
+ *   U, W1, W2, x0, u, x_out, q_out, lse_out, Ld_out   as in dspark_markov_draft
+ *   A       [r][r]         recurrence, dtype w_dtype (read only)
+ *   h_out   [B][gamma][r]  fp32 state h_k each position's bias is formed from (nullable)
+ * bf16 factors only (DSPARK_BF16; DSPARK_ERR_UNSUPPORTED otherwise), r <= 256 with r % 8 == 0,
+ * V % 8 == 0, 16-byte aligned U, W1, W2 and A. The state is kept in fp32; the projection
+ * multiplies its bf16 hi and lo parts (h = hi + lo to about 2^-17 relative) with W2 and
+ * accumulates in fp32. Paths (dspark_rnn_draft_path): B = 1 where every workgroup fits runs
+ * as DSPARK_PATH_RESIDENT (one launch, W2 in registers, A in LDS; the same give-up behaviour,
+ * give-up word and restriction on overlapping draft calls); otherwise DSPARK_PATH_MFMA, three
+ * launches per position (state update, bf16 MFMA projection, draw). Sentinels as in
+ * dspark_markov_draft; a dead request's state is 0.
+ */
+size_t dspark_rnn_draft_workspace_bytes(int B, int V, int r, int gamma);
+int dspark_rnn_draft_path(int B, int V, int r, const void* W1, const void* W2, const void* A);
+int dspark_rnn_draft(int B, int V, int r, int gamma,
+                     const float* U, const void* W1, const void* W2, const void* A, int w_dtype,
+                     const int32_t* x0, const float* u,
+                     int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, float* h_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Allocation-free draft, for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc). It is dspark_markov_draft_ex
  * with the workspace taken from a static device array of dspark_noalloc_scratch_bytes()

@@ -126,19 +126,24 @@ VerifyReport = Report
 
 
 def check_draft(U, W1, W2, x0, u, w_dtype, gx, gq, glse, requests, gL=None, rep=None,
-                group: int = 8, keep_logits=None):
+                group: int = 8, keep_logits=None, oracle_fn=None):
     """Compare GPU draft outputs (numpy) with the oracle on the GPU's own prefix.
 
     Every position of every listed request is compared: the oracle evaluates position k's
     law given the GPU's tokens before it. Returns the report. ``keep_logits`` (a dict) receives
-    the oracle's fp64 logits [1][gamma][V] of each request along the GPU's block, by b."""
+    the oracle's fp64 logits [1][gamma][V] of each request along the GPU's block, by b.
+    ``oracle_fn(U, W1, W2, x0, u, w_dtype, forced)`` replaces the Markov draft (e.g. the RNN
+    head's oracle with its recurrence bound); it returns the oracle's dict with logits."""
     rep = rep or Report("draft")
     B, G, V = U.shape
     reqs = list(requests)
     for i in range(0, len(reqs), group):
         bs = reqs[i:i + group]
-        ref = oracle.markov_draft(U[bs], W1, W2, x0[bs], u[bs], w_dtype, want_logits=True,
-                                  forced=gx[bs])
+        if oracle_fn is None:
+            ref = oracle.markov_draft(U[bs], W1, W2, x0[bs], u[bs], w_dtype, want_logits=True,
+                                      forced=gx[bs])
+        else:
+            ref = oracle_fn(U[bs], W1, W2, x0[bs], u[bs], w_dtype, gx[bs])
         for j, b in enumerate(bs):
             rep.requests += 1
             if keep_logits is not None:
