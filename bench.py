@@ -119,6 +119,11 @@ def parse():
                          "one-launch forms (one request then takes the vocabulary sweep)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="extra eager steps with no timing (for rocprofv3 runs)")
+    ap.add_argument("--sub-steps", type=int, default=10,
+                    help="timed steps of each sub-record of the default run (batched draft, "
+                         "batched verify); 0 leaves them out")
+    ap.add_argument("--sub-cpu-seconds", type=float, default=3.0,
+                    help="CPU time of each sub-record's oracle baseline sample")
     return ap.parse_args()
 
 
@@ -148,6 +153,21 @@ def draft_bytes_per_position(c, logits_written: bool = True) -> float:
     sw = 2 if c.w_dtype == "bf16" else 4
     return (c.r * c.V * sw + c.B * c.V * 4 + c.B * c.r * sw + c.B * 12 +
             (c.B * c.V * 4 if logits_written else 0))
+
+
+def draft_bytes_one_launch(c, logits_written: bool = True) -> float:
+    """Algorithmic HBM bytes of a draft call that draws every position in one launch with W2
+    held on chip: W2 read once, then per position U_k, the W1 rows (or nothing more for the
+    state), the outputs and the logits row when written."""
+    sw = 2 if c.w_dtype == "bf16" else 4
+    per_pos = c.B * c.V * 4 + c.B * c.r * sw + c.B * 12 + (c.B * c.V * 4 if logits_written else 0)
+    return c.r * c.V * sw + c.gamma * per_pos
+
+
+def verify_bytes_read_once(c) -> float:
+    """Algorithmic HBM bytes of a verify + TV call: every verified draft and target row read
+    once (gamma draft rows, gamma + 1 target rows per request), plus the outputs."""
+    return c.B * (2 * c.gamma + 1) * c.V * 4 + c.B * (3 * c.gamma + 2) * 4
 
 
 def measured_peaks(torch, device) -> dict:
@@ -424,11 +444,13 @@ def bench_pipeline(args, torch, dspark, device):
     kernel = "draft_slab_resident" if one else "draft_slab_step + draft_slab_select"
     units = G if one else 1
     launch_us = draft_ms * 1e3 / (1 if one else G)
-    achieved = per_pos * units / (launch_us * 1e-6) / 1e9
+    bytes_launch = draft_bytes_one_launch(c, False) if one else per_pos
+    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
     # the same kernel on the same shapes as the round workload: its counter record applies
     roof = dict(bound="hbm", kernel=kernel, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic("round", kernel),
-                bytes_per_launch=per_pos * units, positions_per_launch=units, launch_us=launch_us)
+                bytes_per_launch=bytes_launch, positions_per_launch=units, launch_us=launch_us,
+                effective_gbs=per_pos * units / (launch_us * 1e-6) / 1e9)
     mp = measured_peaks(torch, device)
     roof["measured_peak"] = dict(mp, frac_of_copy=achieved / mp["hbm_copy_gbs"])
     res = dict(
@@ -562,8 +584,27 @@ def main():
         return bench_pipeline(args, torch, dspark, device)
     if args.workload == "mfma":
         return bench_mfma(args, torch, dspark, device)
-    seed = WORKLOADS[args.workload]
-    verify_only = args.workload == "verify"
+    mp = measured_peaks(torch, device)
+    res = run_workload(args, args.workload, torch, dspark, device, args.steps, args.cpu_seconds, mp)
+    if args.workload == "single" and args.sub_steps > 0 and not args.per_position:
+        # the same protocol on the batched shapes at V = 151936 (the draft on the slab MFMA
+        # path, and the verify + TV call), each its own record beside the headline
+        subs = {}
+        for name in ("batched", "verify"):
+            sub = run_workload(args, name, torch, dspark, device, args.sub_steps,
+                               args.sub_cpu_seconds, mp)
+            for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
+                sub.pop(k, None)
+            subs[name] = sub
+            torch.cuda.empty_cache()
+        res["sub_workloads"] = subs
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(args, workload, torch, dspark, device, steps, cpu_seconds, mp):
+    """One workload under the step protocol; returns its record (the JSON line's fields)."""
+    seed = WORKLOADS[workload]
+    verify_only = workload == "verify"
     c, inp = build_inputs(seed)
     t = {k: to_dev(v, torch, device) for k, v in inp.items()}
     B, G, V = c.B, c.gamma, c.V
@@ -688,28 +729,27 @@ def main():
     for _ in range(args.warmup):
         g_step.replay()
     torch.cuda.synchronize()
-    ms = timed(g_step, args.steps)
-    ms_parts = {name: float(np.mean(timed(g, args.steps))) for name, g in g_parts.items()}
+    ms = timed(g_step, steps)
+    ms_parts = {name: float(np.mean(timed(g, steps))) for name, g in g_parts.items()}
     # the dominant call on its own, for the roofline: draft (or verify + TV)
     dominant = "verify_tv" if verify_only else "draft"
-    ms_kernel = float(np.mean(timed_eager(parts[dominant], args.steps)))
+    ms_kernel = float(np.mean(timed_eager(parts[dominant], steps)))
     torch.cuda.synchronize()
 
     ms_step = float(np.mean(ms))
     value = (drafted + verified) / (ms_step * 1e-3)
     if verify_only:
-        # dominant work: one HBM sweep over every draft and target row, plus the final rows
-        # one sweep over every draft and target row, the final rows, then the TV pass over
-        # every (draft, target) row pair
-        bytes_call = B * (2 * G + 1) * V * 4 + B * 2 * V * 4 + B * G * 2 * V * 4
+        # the method's own work: every draft and target row read once (the one-sweep form
+        # reads nothing else but one chunk of the final row pair per request)
+        bytes_call = verify_bytes_read_once(c)
         launch_us = ms_kernel * 1e3
-        roof = dict(bound="hbm",
-                    kernel="dspark_verify_tv (row_stats + verify_tv_chunks + verify_tv_select)",
+        roof = dict(bound="hbm", kernel="dspark_verify_tv (vt_sweep + vt_select)",
                     achieved=bytes_call / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
         roof.update(frac=roof["achieved"] / HBM_PEAK_GBS,
                     traffic=measured_traffic("verify", "dspark_verify_tv"), bytes_per_launch=bytes_call,
                     launch_us=launch_us, call_us_graph=ms_parts[dominant] * 1e3,
-                    timing="HIP events on the launch stream around eager calls")
+                    timing="HIP events on the launch stream around eager calls",
+                    limiter="HBM: one pass over the rows; per-chunk waits for the row's normalisers")
     else:
         path = dspark.markov_draft_path(B, t["W1"], t["W2"])
         if args.per_position and path == "resident":
@@ -718,34 +758,45 @@ def main():
         one_launch = (not args.per_position and
                       dspark.markov_draft_one_launch(B, t["W1"], t["W2"], want_logits=not rebuild))
         if one_launch:
-            # one launch draws all gamma positions (W2 read once, then held in registers); for
-            # the slab form the timed call also holds the tiny flag-reset kernel before it
+            # one launch draws all gamma positions: W2 read once and held in registers, then
+            # per position U_k (and the logits row when written)
             kernel = "draft_resident" if path == "resident" else "draft_slab_resident"
             units, launch_us = G, ms_kernel * 1e3
+            bytes_launch = draft_bytes_one_launch(c, not rebuild)
+            limiter = ("latency: per position two cross-CU round trips (tile partials, then "
+                       "the drawn token) after a GEMV from registers" if path == "resident" else
+                       "HBM stream of U_k and three flag barriers per position")
         else:
             # one step kernel per position; the per-position time also carries the draws
             kernel = {"mfma": "draft_step_mfma + draft_select",
                       "slab": "draft_slab_step + draft_slab_select"}.get(path, "draft_step_gemv")
             units, launch_us = 1, ms_kernel * 1e3 / G
-        bytes_launch = per_pos * units
+            bytes_launch = per_pos
+            limiter = "HBM: W2 and U_k per position"
         roof = dict(bound="hbm", kernel=kernel, achieved=bytes_launch / (launch_us * 1e-6) / 1e9,
                     peak=HBM_PEAK_GBS, unit="GB/s")
+        traffic = measured_traffic(workload, kernel)
         roof.update(frac=roof["achieved"] / HBM_PEAK_GBS,
-                    traffic=measured_traffic(args.workload, kernel),
+                    traffic=traffic,
                     bytes_per_launch=bytes_launch, positions_per_launch=units,
                     launch_us=launch_us, draft_path=path, call_us_graph=ms_parts[dominant] * 1e3,
-                    timing="HIP events on the launch stream around eager calls")
+                    timing="HIP events on the launch stream around eager calls",
+                    limiter=limiter,
+                    # the per-position sweep's bytes (W2 read at every position) over the same
+                    # time: what a draft without W2 on chip would have to move
+                    effective_gbs=per_pos * units / (launch_us * 1e-6) / 1e9)
+        if traffic is not None:
+            roof["physical_gbs"] = traffic / (launch_us * 1e-6) / 1e9
         if path in ("mfma", "slab"):
             tflops = 2.0 * B * c.r * V * units / (launch_us * 1e-6) / 1e12
             roof["mfma"] = dict(achieved=tflops, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                 frac=tflops / MFMA_BF16_PEAK_TFLOPS)
-    mp = measured_peaks(torch, device)
     roof["measured_peak"] = dict(mp, frac_of_copy=roof["achieved"] / mp["hbm_copy_gbs"])
     if "mfma" in roof:
         roof["mfma"]["frac_of_matmul"] = roof["mfma"]["achieved"] / mp["bf16_matmul_tflops"]
     what = "verify + TV labels" if verify_only else "draft + schedule + verify + TV labels"
     res = dict(
-        metric=METRIC, value=value, unit="tokens/s", n_gpus=1, steps=args.steps,
+        metric=METRIC, value=value, unit="tokens/s", n_gpus=1, steps=steps,
         warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="f32", data="synthetic",
         config=dict(workload=f"{c.name}: {what} per step", B=B, V=V, r=c.r, gamma=G,
@@ -763,11 +814,12 @@ def main():
     if not verify_only:
         res["draft_tok_s"] = drafted / (ms_parts["draft"] * 1e-3)
     res["verified_tok_s"] = verified / (ms_parts["verify_tv"] * 1e-3)
-    if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(c, inp, args.cpu_seconds, verify_only)
-        res["cpu_baseline_all_cores"] = cpu_baseline(c, inp, args.cpu_seconds, verify_only,
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(c, inp, cpu_seconds, verify_only)
+        res["cpu_baseline_all_cores"] = cpu_baseline(c, inp, cpu_seconds, verify_only,
                                                      threads=all_core_threads())
-    print(json.dumps(res), flush=True)
+    del t, g_step, g_parts, out_d, out_v, flush
+    return res
 
 
 if __name__ == "__main__":

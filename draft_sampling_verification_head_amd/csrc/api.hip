@@ -428,8 +428,10 @@ int dspark_verify(int B, int V, int gamma, const float* Ld, const float* Lt, int
 
 size_t dspark_verify_tv_workspace_bytes(int B, int V, int gamma) {
     if (B < 1 || V < 1 || gamma < 1) return 0;
-    return dspark_verify_workspace_bytes(B, V, gamma) +
-           align_up(static_cast<size_t>(B) * gamma * row_chunks(V) * sizeof(float));
+    const size_t chunked = dspark_verify_workspace_bytes(B, V, gamma) +
+                           align_up(static_cast<size_t>(B) * gamma * row_chunks(V) * sizeof(float));
+    const size_t sweep = dspark::verify_sweep_bytes(B, V, gamma);
+    return chunked > sweep ? chunked : sweep;
 }
 
 int dspark_verify_tv(int B, int V, int gamma, const float* Ld, const float* Lt, int Lt_rows,
@@ -445,13 +447,20 @@ int dspark_verify_tv(int B, int V, int gamma, const float* Ld, const float* Lt, 
     if (!ws || ws_bytes < need)
         return fail(DSPARK_ERR_WORKSPACE, "verify_tv: workspace %zu bytes, need %zu", ws_bytes,
                     need);
+    dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dspark::verify_sweep_ok(V)) {                 // every row read once
+        const hipError_t e = dspark::launch_verify_sweep(rs, x, ld_lse, u_acc, u_fin, lse_d_out,
+                                                         lse_t_out, n_acc_out, y_out, cstar_out, ws,
+                                                         1u << 20, st);
+        if (e != hipSuccess) return hip_fail(e, "verify_tv/sweep");
+        return ok();
+    }
     Carver c(ws);
     float2* part = c.take<float2>(static_cast<size_t>(B) * (2 * gamma + 1) * row_chunks(V));
     float* csum = c.take<float>(static_cast<size_t>(B) * row_chunks(V));
     char* state = c.take<char>(static_cast<size_t>(B) * dspark::verify_state_bytes());
     float* psum = c.take<float>(static_cast<size_t>(B) * gamma * row_chunks(V));
-    dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
-    hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = dspark::launch_row_stats(rs, ld_lse, part, st);
     if (e != hipSuccess) return hip_fail(e, "verify_tv/row_stats");
     e = dspark::launch_verify_tv(rs, x, part, ld_lse, u_acc, u_fin, lse_d_out, lse_t_out, csum,

@@ -104,6 +104,18 @@ hipError_t launch_verify_tv(const RowSet& rs, const int32_t* x, const float2* pa
                             float* psum, int32_t* n_out, int32_t* y_out, float* cstar,
                             hipStream_t st);
 
+// Verify and TV labels in one pass over the rows (two launches: the sweep, then the draws and
+// the c* merges), with the same results as launch_row_stats + launch_verify_tv bit for bit.
+// Applies when a row has at most 64 chunks and the sweep's persistent grid fits the device.
+// `ws` holds verify_sweep_bytes(B, V, gamma) bytes (a call counter in its first word; the
+// rest needs no preparation). `spin`: polls before a wait gives up.
+size_t verify_sweep_bytes(int B, int V, int gamma);
+bool verify_sweep_ok(int V);
+hipError_t launch_verify_sweep(const RowSet& rs, const int32_t* x, const float* lse_d_in,
+                               const float* u_acc, const float* u_fin, float* lse_d_out,
+                               float* lse_t_out, int32_t* n_out, int32_t* y_out, float* cstar,
+                               void* ws, unsigned spin, hipStream_t st);
+
 // TV labels; normalisers from lse_d / lse_t when given, else merged from `part`.
 // psum: [B][gamma][nch].
 hipError_t launch_tv(const RowSet& rs, const float* lse_d, const float* lse_t,

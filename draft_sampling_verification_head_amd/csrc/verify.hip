@@ -274,35 +274,17 @@ void verify_chunks_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
                              blockIdx.x);
 }
 
+// The final draw of a request from its row's chunk masses `cs` (nch of them, in chunk order):
+// the chunk that holds u * total, then a rescan of that chunk in token order. When a residual
+// rounded to zero mass, the p_t masses of the same row are formed into `cs` and drawn from
+// instead. Returns the token (-1 when the row has no mass). Called by a whole workgroup.
 template <bool VEC4>
-__device__ __forceinline__ void verify_select_body(const RowSet& rs, int nch, const int32_t* __restrict__ x,
-                                   const float* __restrict__ u_fin, float* __restrict__ csum,
-                                   const ReqState* __restrict__ state, int32_t* __restrict__ n_out,
-                                   int32_t* __restrict__ y_out, int b) {
+__device__ __forceinline__ int final_draw(int V, int nch, FinalRow fr, float* cs, float uf) {
     __shared__ float fscr[kWaves + 1];
     __shared__ int iscr[kWaves + 1];
     __shared__ int s_found;
     __shared__ float s_tprime, s_total;
     const int tid = threadIdx.x;
-    const int G = rs.gamma, V = rs.V;
-    int32_t* y = y_out + static_cast<long long>(b) * (G + 1);
-    const ReqState st = state[b];
-    if (st.n < 0) {
-        for (int i = tid; i <= G; i += kThreads) y[i] = -1;
-        if (tid == 0) n_out[b] = -1;
-        return;
-    }
-    const ReqRows q = request_rows(rs, b);
-    const int n = st.n;
-    FinalRow fr;
-    fr.lt = rs.Lt + (q.off + n) * V;
-    fr.lse_t = st.lse_t;
-    fr.residual = st.residual;
-    fr.ld = fr.residual ? rs.Ld + (static_cast<long long>(b) * G + n) * V : nullptr;
-    fr.lse_d = st.lse_d;
-    float* cs = csum + static_cast<long long>(b) * nch;
-    const float uf = clamp_uniform(u_fin[b]);
-
     for (int pass = 0; pass < 2; ++pass) {
         // chunk totals in chunk order by one wave: lane-strided sums then a butterfly give the
         // total; the search walks the chunks in order with per-lane running sums
@@ -382,6 +364,33 @@ __device__ __forceinline__ void verify_select_body(const RowSet& rs, int nch, co
         z = block_min_int<kThreads>(hit, iscr);
         if (z == INT32_MAX) z = block_max_int<kThreads>(lastpos, iscr);
     }
+    return z;
+}
+
+template <bool VEC4>
+__device__ __forceinline__ void verify_select_body(const RowSet& rs, int nch, const int32_t* __restrict__ x,
+                                   const float* __restrict__ u_fin, float* __restrict__ csum,
+                                   const ReqState* __restrict__ state, int32_t* __restrict__ n_out,
+                                   int32_t* __restrict__ y_out, int b) {
+    const int tid = threadIdx.x;
+    const int G = rs.gamma, V = rs.V;
+    int32_t* y = y_out + static_cast<long long>(b) * (G + 1);
+    const ReqState st = state[b];
+    if (st.n < 0) {
+        for (int i = tid; i <= G; i += kThreads) y[i] = -1;
+        if (tid == 0) n_out[b] = -1;
+        return;
+    }
+    const ReqRows q = request_rows(rs, b);
+    const int n = st.n;
+    FinalRow fr;
+    fr.lt = rs.Lt + (q.off + n) * V;
+    fr.lse_t = st.lse_t;
+    fr.residual = st.residual;
+    fr.ld = fr.residual ? rs.Ld + (static_cast<long long>(b) * G + n) * V : nullptr;
+    fr.lse_d = st.lse_d;
+    const int z = final_draw<VEC4>(V, nch, fr, csum + static_cast<long long>(b) * nch,
+                                   clamp_uniform(u_fin[b]));
     for (int i = tid; i <= G; i += kThreads)
         y[i] = (i < n) ? x[static_cast<long long>(b) * G + i] : (i == n ? z : -1);
     if (tid == 0) n_out[b] = n;
@@ -498,6 +507,293 @@ void verify_tv_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
         tv_merge_body(rs, nch, psum, cstar, blockIdx.x - rs.B);
 }
 
+// ----------------------------------------------------------------------------- one sweep
+// Verify and TV labels in one pass over the rows. A unit is one verified position of a request
+// (its draft row and target row) or its bonus target row; each unit is cut into the same
+// 8192-logit chunks as above, and task (unit, chunk) keeps its chunk of both rows in registers:
+//   1. the chunk's (max, sum exp) of both rows, formed exactly as row_stats forms them, go into
+//      the unit's slot for that chunk, tagged with this call's key;
+//   2. wave 0 waits until all chunks of the unit carry the key and merges them in chunk order
+//      (the same merge as verify_chunks), giving lse_d and lse_t;
+//   3. from the registers: the chunk's sum of min(p_d, p_t) (as tv_chunks forms it) and its
+//      mass under the unit's final-draw law (the residual max(0, p_t - p_d) of a verified
+//      position, p_t of the bonus row; as chunk_mass forms them).
+// So every row is read once, and all partial results equal those of the three-kernel path bit
+// for bit. vt_select then runs the acceptance test and the final draw per request from these
+// results (reading only the drafted tokens' logits and the one chunk it rescans) and merges c*.
+//
+// The grid is persistent: every workgroup is resident at once (checked by the host), and
+// workgroup w takes tasks w, w + N, w + 2N, ... A unit's nch chunks are consecutive tasks, so
+// they belong to nch different workgroups, each of which reaches them after finishing tasks of
+// earlier units only; by induction over units every wait ends. Polling is bounded all the
+// same: a workgroup that gives up writes the call's key into the give-up word, and vt_select
+// then reports every request as faulty.
+//
+// The key is the splitmix64 finaliser (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014) of a call counter E in the workspace, xor a constant: slots left by
+// earlier calls carry earlier keys, and all-zero or all-one bytes are no key. Every sweep
+// workgroup reads E at its start; vt_select (which runs after the whole sweep) advances it.
+
+__device__ __forceinline__ unsigned long long call_key(unsigned long long e) {
+    unsigned long long z = e ^ 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ unsigned long long ld_agent(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_agent(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct SweepArgs {
+    RowSet rs;
+    int nch;
+    long long ntasks;                 // B (gamma + 1) nch
+    const float* lse_d_in;            // nullable
+    unsigned long long* slots;        // [unit][nch][4]: draft (max, sum), target (max, sum), key, -
+    float2* ulse;                     // [unit] (lse_d, lse_t)
+    float* rmass;                     // [unit][nch] mass under the unit's final-draw law
+    float* psum;                      // [b gamma + k][nch] sum of min(p_d, p_t)
+    unsigned long long* hdr;          // [0] call counter E, [1] give-up key, [2] this sweep's key
+    unsigned spin;
+};
+
+// lse of a unit's row from the lanes' chunk partials (lane i holds chunk i < nch <= 64; the
+// other lanes hold (-inf, 0)): merge_lse_wave's arithmetic on the same values.
+__device__ __forceinline__ float merge_lanes(float2 p0) {
+    const float mm = wave_max_dpp(fmaxf(-INFINITY, p0.x));
+    if (mm == -INFINITY) return -INFINITY;
+    float ss = (p0.x == -INFINITY) ? 0.0f : p0.y * __expf(p0.x - mm);
+    ss = wave_sum_dpp(ss);
+    return mm + __logf(ss);
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads)
+void vt_sweep_kernel(SweepArgs a) {
+    __shared__ float sm[2][kWaves];
+    __shared__ float fscr[kWaves + 1];
+    __shared__ float s_lse[2];
+    __shared__ int s_gave;
+    __shared__ unsigned long long s_key;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const RowSet& rs = a.rs;
+    const int G = rs.gamma, V = rs.V, nch = a.nch, G1 = G + 1;
+    if (tid == 0) {
+        s_key = call_key(ld_agent(a.hdr));
+        s_gave = 0;
+        if (blockIdx.x == 0) st_agent(a.hdr + 2, s_key);
+    }
+    __syncthreads();
+    const unsigned long long key = s_key;
+    for (long long task = blockIdx.x; task < a.ntasks; task += gridDim.x) {
+        const long long unit = task / nch;
+        const int c = static_cast<int>(task - unit * nch);
+        const int b = static_cast<int>(unit / G1), s = static_cast<int>(unit - static_cast<long long>(b) * G1);
+        const ReqRows q = request_rows(rs, b);
+        if (!q.ok || s > q.ell) continue;               // no such row: nobody waits for it
+        const bool pair = s < q.ell;
+        float t[kPer], d[kPer];
+        load_chunk<VEC4>(rs.Lt + (q.off + s) * V, c, V, t);
+        if (pair) load_chunk<VEC4>(rs.Ld + (static_cast<long long>(b) * G + s) * V, c, V, d);
+        // 1. chunk partials (row_stats' arithmetic), published with the key
+        float mt = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) mt = fmaxf(mt, t[e]);
+        float st = 0.0f;
+        if (mt != -INFINITY) {
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) st += __expf(t[e] - mt);
+        }
+        block_ms(mt, st, sm);
+        float md = -INFINITY, sd = 0.0f;
+        if (pair && !a.lse_d_in) {
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) md = fmaxf(md, d[e]);
+            if (md != -INFINITY) {
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) sd += __expf(d[e] - md);
+            }
+            block_ms(md, sd, sm);
+        }
+        unsigned long long* us = a.slots + unit * nch * 4;
+        if (tid == 0) {
+            st_agent(us + 4 * c, __builtin_bit_cast(unsigned long long, make_float2(md, sd)));
+            st_agent(us + 4 * c + 1, __builtin_bit_cast(unsigned long long, make_float2(mt, st)));
+            __builtin_amdgcn_s_waitcnt(0);              // the partials land before the key
+            st_agent(us + 4 * c + 2, key);
+        }
+        // 2. the unit's normalisers, once every chunk carries the key
+        if (wave == 0) {
+            float2 pd = make_float2(-INFINITY, 0.0f), pt = make_float2(-INFINITY, 0.0f);
+            bool ok = true;
+            if (lane < nch) {
+                for (unsigned n = 0; ld_agent(us + 4 * lane + 2) != key;) {
+                    if (++n > a.spin) {
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (ok) {
+                    pd = __builtin_bit_cast(float2, ld_agent(us + 4 * lane));
+                    pt = __builtin_bit_cast(float2, ld_agent(us + 4 * lane + 1));
+                }
+            }
+            if (__any(!ok)) {
+                if (lane == 0) {
+                    s_gave = 1;
+                    st_agent(a.hdr + 1, key);
+                }
+            }
+            const float lt = merge_lanes(pt);
+            float ld = 0.0f;
+            if (pair) ld = a.lse_d_in ? a.lse_d_in[static_cast<long long>(b) * G + s] : merge_lanes(pd);
+            if (lane == 0) {
+                s_lse[0] = ld;
+                s_lse[1] = lt;
+            }
+        }
+        __syncthreads();
+        if (s_gave) break;
+        const float lsd = s_lse[0], lst = s_lse[1];
+        if (c == 0 && tid == 0) a.ulse[unit] = make_float2(lsd, lst);
+        // 3. sum of min(p_d, p_t) (tv_chunks' arithmetic) and the final-draw mass
+        //    (chunk_mass' arithmetic) from the registers
+        if (pair) {
+            float sv = 0.0f;
+            if (lsd != -INFINITY && lst != -INFINITY) {
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) sv += __expf(fminf(d[e] - lsd, t[e] - lst));
+            }
+            sv = block_sum<kThreads>(sv, fscr);
+            if (tid == 0) a.psum[(static_cast<long long>(b) * G + s) * nch + c] = sv;
+        }
+        FinalRow fr;
+        fr.lt = nullptr;
+        fr.ld = nullptr;
+        fr.lse_t = lst;
+        fr.lse_d = pair ? lsd : 0.0f;
+        fr.residual = pair ? 1 : 0;
+        float mass = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) mass += fr.weight(t[e], pair ? d[e] : 0.0f);
+        mass = block_sum<kThreads>(mass, fscr);
+        if (tid == 0) a.rmass[unit * nch + c] = mass;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Per request (first B workgroups): the acceptance test on the unit normalisers (the same
+// test as verify_chunks on the same values), the final draw from the unit's chunk masses, the
+// outputs; the remaining workgroups merge c* as tv_merge does. A call whose sweep gave up
+// reports every request as faulty. Workgroup 0 advances the call counter last.
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads)
+void vt_select_kernel(SweepArgs a, const int32_t* __restrict__ x, const float* __restrict__ u_acc,
+                      const float* __restrict__ u_fin, float* __restrict__ lse_d_out,
+                      float* __restrict__ lse_t_out, int32_t* __restrict__ n_out,
+                      int32_t* __restrict__ y_out, float* __restrict__ cstar) {
+    __shared__ float s_lt[65], s_ld[64];
+    __shared__ int s_n, s_bad, s_gave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const RowSet& rs = a.rs;
+    const int G = rs.gamma, V = rs.V, nch = a.nch, G1 = G + 1;
+    if (tid == 0) s_gave = ld_agent(a.hdr + 1) == ld_agent(a.hdr + 2);
+    __syncthreads();
+    const bool gave = s_gave;
+    if (blockIdx.x >= static_cast<unsigned>(rs.B)) {
+        const unsigned blk = blockIdx.x - rs.B;
+        if (!gave) {
+            tv_merge_body(rs, nch, a.psum, cstar, blk);
+        } else {
+            const long long pair = static_cast<long long>(blk) * kWaves + wave;
+            if (pair < static_cast<long long>(rs.B) * G && lane == 0) cstar[pair] = qnan();
+        }
+        return;
+    }
+    const int b = blockIdx.x;
+    int32_t* y = y_out + static_cast<long long>(b) * G1;
+    const ReqRows q = request_rows(rs, b);
+    if (!q.ok || gave) {
+        for (int i = tid; i <= G; i += kThreads) {
+            y[i] = -1;
+            if (lse_t_out) lse_t_out[static_cast<long long>(b) * G1 + i] = qnan();
+            if (lse_d_out && i < G) lse_d_out[static_cast<long long>(b) * G + i] = qnan();
+        }
+        if (tid == 0) n_out[b] = -1;
+    } else {
+        int xk = 0;
+        float ltx = 0.0f, ldx = 0.0f, ua = 0.0f;
+        if (wave == 0 && lane < q.ell) {
+            xk = x[static_cast<long long>(b) * G + lane];
+            ua = u_acc[static_cast<long long>(b) * G + lane];
+            if (xk >= 0 && xk < V) {
+                ltx = rs.Lt[(q.off + lane) * V + xk];
+                ldx = rs.Ld[(static_cast<long long>(b) * G + lane) * V + xk];
+            }
+        }
+        const float2* ul = a.ulse + static_cast<long long>(b) * G1;
+        for (int i = tid; i <= q.ell; i += kThreads) {
+            s_lt[i] = ul[i].y;
+            if (i < q.ell) s_ld[i] = a.lse_d_in ? a.lse_d_in[static_cast<long long>(b) * G + i] : ul[i].x;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            bool bad = false, rej = false;
+            const int k = lane;
+            if (k < q.ell) {
+                if (xk < 0 || xk >= V) {
+                    bad = true;
+                } else {
+                    const float lst = s_lt[k], lsd = s_ld[k];
+                    const float lpt = (lst == -INFINITY) ? -INFINITY : ltx - lst;
+                    const float lpd = (lsd == -INFINITY) ? -INFINITY : ldx - lsd;
+                    bool acc;
+                    if (lpd == -INFINITY)
+                        acc = lpt > -INFINITY;
+                    else
+                        acc = logf(clamp_uniform(ua)) < lpt - lpd;
+                    rej = !acc;
+                }
+            }
+            const unsigned long long badm = __ballot(bad);
+            const unsigned long long rejm = __ballot(rej);
+            if (lane == 0) {
+                s_bad = badm != 0ull;
+                s_n = rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : q.ell;
+            }
+        }
+        __syncthreads();
+        const int n = s_n;
+        for (int i = tid; i <= G; i += kThreads) {
+            if (lse_t_out) lse_t_out[static_cast<long long>(b) * G1 + i] = (i <= q.ell) ? s_lt[i] : qnan();
+            if (lse_d_out && i < G) lse_d_out[static_cast<long long>(b) * G + i] = (i < q.ell) ? s_ld[i] : qnan();
+        }
+        if (s_bad) {
+            for (int i = tid; i <= G; i += kThreads) y[i] = -1;
+            if (tid == 0) n_out[b] = -1;
+        } else {
+            FinalRow fr;
+            fr.lt = rs.Lt + (q.off + n) * V;
+            fr.lse_t = s_lt[n];
+            fr.residual = n < q.ell;
+            fr.ld = fr.residual ? rs.Ld + (static_cast<long long>(b) * G + n) * V : nullptr;
+            fr.lse_d = fr.residual ? s_ld[n] : 0.0f;
+            const int z = final_draw<VEC4>(V, nch, fr, a.rmass + (static_cast<long long>(b) * G1 + n) * nch,
+                                           clamp_uniform(u_fin[b]));
+            for (int i = tid; i <= G; i += kThreads)
+                y[i] = (i < n) ? x[static_cast<long long>(b) * G + i] : (i == n ? z : -1);
+            if (tid == 0) n_out[b] = n;
+        }
+    }
+    if (b == 0 && tid == 0) st_agent(a.hdr, ld_agent(a.hdr) + 1);   // the next call's key
+}
+
 }  // namespace
 
 int verify_chunk_elems() { return kChunk; }
@@ -558,6 +854,88 @@ hipError_t launch_verify_tv(const RowSet& rs, const int32_t* x, const float2* pa
     const unsigned nmerge = static_cast<unsigned>((pairs + kWaves - 1) / kWaves);
     DSPARK_LAUNCH_VEC4(verify_tv_select_kernel, dim3(static_cast<unsigned>(rs.B) + nmerge), rs, nch,
                        x, u_fin, csum, rstate, n_out, y_out, psum, cstar);
+    return hipGetLastError();
+}
+
+// ---- one-sweep verify + TV
+namespace {
+
+struct SweepFit {
+    int cus = -1;
+    int occ[2] = {-1, -1};
+};
+
+// Resident workgroups of vt_sweep_kernel on the current device (0 if unknown).
+int sweep_capacity(bool vec4) {
+    thread_local SweepFit cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    SweepFit& f = cache[dev];
+    if (f.cus < 0 && hipDeviceGetAttribute(&f.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    int& occ = f.occ[vec4 ? 1 : 0];
+    if (occ < 0) {
+        int o = 0;
+        const hipError_t e = vec4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, vt_sweep_kernel<true>, kThreads, 0)
+                                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, vt_sweep_kernel<false>, kThreads, 0);
+        occ = (e == hipSuccess) ? o : 0;
+    }
+    return f.cus > 0 ? f.cus * occ : 0;
+}
+
+}  // namespace
+
+size_t verify_sweep_bytes(int B, int V, int gamma) {
+    const size_t nch = static_cast<size_t>(nchunks(V));
+    const size_t units = static_cast<size_t>(B) * (gamma + 1);
+    auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+    return 256 + al(units * nch * 4 * sizeof(unsigned long long)) + al(units * sizeof(float2)) +
+           al(units * nch * sizeof(float)) + al(static_cast<size_t>(B) * gamma * nch * sizeof(float));
+}
+
+bool verify_sweep_ok(int V) {
+    return nchunks(V) <= kWave && sweep_capacity(true) >= nchunks(V) && sweep_capacity(false) >= nchunks(V);
+}
+
+hipError_t launch_verify_sweep(const RowSet& rs, const int32_t* x, const float* lse_d_in,
+                               const float* u_acc, const float* u_fin, float* lse_d_out,
+                               float* lse_t_out, int32_t* n_out, int32_t* y_out, float* cstar,
+                               void* ws, unsigned spin, hipStream_t st) {
+    SweepArgs a;
+    a.rs = rs;
+    a.nch = nchunks(rs.V);
+    a.ntasks = static_cast<long long>(rs.B) * (rs.gamma + 1) * a.nch;
+    a.lse_d_in = lse_d_in;
+    a.spin = spin;
+    char* p = static_cast<char*>(ws);
+    auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+    const size_t units = static_cast<size_t>(rs.B) * (rs.gamma + 1);
+    a.hdr = reinterpret_cast<unsigned long long*>(p);
+    p += 256;
+    a.slots = reinterpret_cast<unsigned long long*>(p);
+    p += al(units * a.nch * 4 * sizeof(unsigned long long));
+    a.ulse = reinterpret_cast<float2*>(p);
+    p += al(units * sizeof(float2));
+    a.rmass = reinterpret_cast<float*>(p);
+    p += al(units * a.nch * sizeof(float));
+    a.psum = reinterpret_cast<float*>(p);
+    const bool v4 = rows_vec4(rs);
+    const long long cap = sweep_capacity(v4);
+    const unsigned grid = static_cast<unsigned>(a.ntasks < cap ? a.ntasks : cap);
+    if (v4)
+        hipLaunchKernelGGL(vt_sweep_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(vt_sweep_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long pairs = static_cast<long long>(rs.B) * rs.gamma;
+    const dim3 g2(static_cast<unsigned>(rs.B + (pairs + kWaves - 1) / kWaves));
+    if (v4)
+        hipLaunchKernelGGL(vt_select_kernel<true>, g2, dim3(kThreads), 0, st, a, x, u_acc, u_fin, lse_d_out,
+                           lse_t_out, n_out, y_out, cstar);
+    else
+        hipLaunchKernelGGL(vt_select_kernel<false>, g2, dim3(kThreads), 0, st, a, x, u_acc, u_fin, lse_d_out,
+                           lse_t_out, n_out, y_out, cstar);
     return hipGetLastError();
 }
 

@@ -158,6 +158,78 @@ def test_verify_tv_matches_separate_calls(gpu, B, V, G, flat, given):
     check_tv(inp, f["cstar"], range(B))
 
 
+@pytest.mark.parametrize("B,V,G,flat,given", [
+    (2, 600000, 2, True, False),    # 74 chunks per row: past the one-sweep form, the chunked kernels
+    (3, 524288, 2, False, True),    # exactly 64 chunks: the one-sweep form at its cap
+])
+def test_verify_tv_at_the_sweep_cap(gpu, B, V, G, flat, given):
+    """Both implementations of dspark_verify_tv (one sweep up to 64 chunks per row, the chunked
+    kernels beyond) match the separate calls bit for bit and the oracle."""
+    test_verify_tv_matches_separate_calls(gpu, B, V, G, flat, given)
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_verify_tv_sweep_workspace_and_graph_replays(gpu, fill):
+    """The one-sweep form tags its chunk slots with a key derived from a call counter in the
+    workspace: a workspace of zeros, of all-one bytes or of random bytes, calls in a row, and
+    replays of a captured call all give the separate calls' results bit for bit."""
+    from draft_sampling_verification_head_amd import binding
+    c = synth.custom(960, B=6, V=40000, r=1, gamma=5, w_dtype="f32", tnoise=0.8)
+    g = np.random.default_rng(960)
+    lengths = g.integers(0, c.gamma + 1, size=c.B)
+    lengths[0] = c.gamma
+    inp = verify_inputs(c, lengths, True)
+    a = run_verify(inp, want_lse=True)
+    tv = run_tv(inp, lse_d=dev(a["lse_d"]), lse_t=dev(a["lse_t"]))
+    lib = binding.load()
+    ws = torch.empty(lib.dspark_verify_tv_workspace_bytes(c.B, c.V, c.gamma), dtype=torch.uint8,
+                     device="cuda")
+    if fill == "zeros":
+        ws.zero_()
+    elif fill == "ones":
+        ws.fill_(255)
+    else:
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda",
+                               generator=torch.Generator(device="cuda").manual_seed(7)))
+    t = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    out = {k: torch.empty_like(dev(a[k])) for k in ("n", "y", "lse_d", "lse_t")}
+    out["cstar"] = torch.empty((c.B, c.gamma), dtype=torch.float32, device="cuda")
+
+    def call():
+        dspark.verify(t["Ld"], t["Lt"], t["x"], t["u_acc"], t["u_fin"], t_off=t["t_off"],
+                      length=t["length"], want_lse=True, with_tv=True, out=out, ws=ws)
+
+    def check():
+        torch.cuda.synchronize()
+        for k in ("n", "y", "lse_d", "lse_t"):
+            assert np.array_equal(host(out[k]).view(np.uint8), a[k].view(np.uint8)), k
+        cs = host(out["cstar"])
+        assert np.array_equal(np.isnan(cs), np.isnan(tv))
+        fin = ~np.isnan(tv)
+        assert np.array_equal(cs[fin], tv[fin])
+        for v in out.values():
+            v.fill_(-3)
+        torch.cuda.synchronize()
+
+    for _ in range(3):
+        call()
+        check()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call()                                      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    check()
+    with torch.cuda.graph(graph, stream=s):
+        call()
+    for _ in range(4):
+        graph.replay()
+        check()
+        call()                                      # eager calls between the replays
+        check()
+
+
 def test_device_data_faults(gpu):
     c = synth.custom(947, B=4, V=700, r=1, gamma=3, w_dtype="f32")
     lengths = np.array([3, 2, 1, 3])
