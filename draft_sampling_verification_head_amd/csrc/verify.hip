@@ -573,7 +573,7 @@ __device__ __forceinline__ float merge_lanes(float2 p0) {
 }
 
 template <bool VEC4>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kThreads, 4)      // four workgroups per CU
 void vt_sweep_kernel(SweepArgs a) {
     __shared__ float sm[2][kWaves];
     __shared__ float fscr[kWaves + 1];
