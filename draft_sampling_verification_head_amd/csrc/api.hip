@@ -449,6 +449,13 @@ int dspark_verify_tv(int B, int V, int gamma, const float* Ld, const float* Lt, 
                     need);
     dspark::RowSet rs{B, V, gamma, Ld, Lt, Lt_rows, t_off, len};
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dspark::verify_sweep_ok(V) && dspark::verify_small_ok(rs)) {   // one launch
+        const hipError_t e = dspark::launch_verify_small(rs, x, ld_lse, u_acc, u_fin, lse_d_out,
+                                                         lse_t_out, n_acc_out, y_out, cstar_out, ws,
+                                                         1u << 20, st);
+        if (e != hipSuccess) return hip_fail(e, "verify_tv/small");
+        return ok();
+    }
     if (dspark::verify_sweep_ok(V)) {                 // every row read once
         const hipError_t e = dspark::launch_verify_sweep(rs, x, ld_lse, u_acc, u_fin, lse_d_out,
                                                          lse_t_out, n_acc_out, y_out, cstar_out, ws,

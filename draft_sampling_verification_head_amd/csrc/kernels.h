@@ -111,6 +111,13 @@ hipError_t launch_verify_tv(const RowSet& rs, const int32_t* x, const float2* pa
 // rest needs no preparation). `spin`: polls before a wait gives up.
 size_t verify_sweep_bytes(int B, int V, int gamma);
 bool verify_sweep_ok(int V);
+// The same in one launch, one workgroup per (row, chunk) task, where every task fits the
+// device at once (small batches); the same workspace layout header and results.
+bool verify_small_ok(const RowSet& rs);
+hipError_t launch_verify_small(const RowSet& rs, const int32_t* x, const float* lse_d_in,
+                               const float* u_acc, const float* u_fin, float* lse_d_out,
+                               float* lse_t_out, int32_t* n_out, int32_t* y_out, float* cstar,
+                               void* ws, unsigned spin, hipStream_t st);
 hipError_t launch_verify_sweep(const RowSet& rs, const int32_t* x, const float* lse_d_in,
                                const float* u_acc, const float* u_fin, float* lse_d_out,
                                float* lse_t_out, int32_t* n_out, int32_t* y_out, float* cstar,

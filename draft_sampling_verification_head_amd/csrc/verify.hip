@@ -794,6 +794,421 @@ void vt_select_kernel(SweepArgs a, const int32_t* __restrict__ x, const float* _
     if (b == 0 && tid == 0) st_agent(a.hdr, ld_agent(a.hdr) + 1);   // the next call's key
 }
 
+// ----------------------------------------------------------------------------- one launch
+// Verify and TV labels of a small batch in one launch: one workgroup per task (unit, chunk),
+// every workgroup resident at once (the host checks), and every hand-over between workgroups
+// a key-tagged slot instead of a kernel boundary. A task
+//   1. forms its chunk's partials and waits for its unit's normalisers, as vt_sweep does;
+//   2. publishes its chunk's sum of min(p_d, p_t), its mass under the unit's final-draw law and
+//      its p_t mass (for a residual that rounds to zero), and, if its chunk holds the drafted
+//      token, the acceptance decision (as verify_chunks forms it; chunk 0 flags a token outside
+//      [0, V));
+//   3. chunk 0 of a verified position merges c* (as tv_merge); every task of the unit that the
+//      decisions make the final one waits for that unit's masses, finds the chunk that holds
+//      u * total (as final_draw), and that chunk's task rescans its own registers in token order
+//      (through LDS, in final_draw's layout and order) and writes n and y.
+// Every result equals the chunked kernels' bit for bit. Chunk 0 of request 0's first unit
+// waits at the end until every live task has published, then advances the call counter.
+// Polling is bounded: a workgroup that gives up writes the call's key into the give-up word
+// (the outputs of such a call are not defined).
+
+// Hand-over words of the one-launch form: 32 bits of this call's tag beside a 32-bit value,
+// stored and loaded as one 64-bit word, so a word is valid on its own and no store needs to
+// wait for another. The tag is the low half of the call counter xor a constant: consecutive
+// calls differ, and all-zero or all-one words carry no call's tag.
+__device__ __forceinline__ unsigned call_tag(unsigned long long e) {
+    return static_cast<unsigned>(e) ^ 0x9e3779b9u;
+}
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
+    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, unsigned v) {
+    return (static_cast<unsigned long long>(tag) << 32) | v;
+}
+__device__ __forceinline__ bool has_tag(unsigned long long w, unsigned tag) {
+    return static_cast<unsigned>(w >> 32) == tag;
+}
+__device__ __forceinline__ float tagged_f(unsigned long long w) {
+    return __uint_as_float(static_cast<unsigned>(w));
+}
+
+constexpr int kSmallMaxTasks = 768;                 // one-launch form: tasks per call at most
+
+struct SmallArgs {
+    RowSet rs;
+    int nch;
+    long long ntasks;
+    const float* lse_d_in;
+    const int32_t* x;
+    const float* u_acc;
+    const float* u_fin;
+    float* lse_d_out;
+    float* lse_t_out;
+    int32_t* n_out;
+    int32_t* y_out;
+    float* cstar;
+    unsigned long long* slots;        // [unit][nch][4] tagged: draft max, sum; target max, sum
+    unsigned long long* mslots;       // [unit][nch][4] tagged: sum min, final mass, p_t mass, -
+    unsigned long long* flags;        // [B][gamma] tagged acceptance codes: 1 keep, 2 reject, 3 bad token
+    unsigned long long* hdr;          // [0] call counter E, [1] give-up key
+    unsigned spin;
+};
+
+// Polls until every lane's word is tagged (lanes with p == nullptr are ready); false after
+// the spin bound. The whole wave calls it.
+__device__ __forceinline__ bool poll_tagged(const unsigned long long* p, unsigned long long& v,
+                                            unsigned tag, unsigned spin) {
+    bool done = p == nullptr;
+    for (unsigned n = 0;;) {
+        if (!done) {
+            v = ld_agent(p);
+            done = has_tag(v, tag);
+        }
+        if (__all(done)) return true;
+        if (++n > spin) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads, 2)
+void vt_small_kernel(SmallArgs a) {
+    __shared__ float sm[2][kWaves];
+    __shared__ float fscr[kWaves + 1];
+    __shared__ int iscr[kWaves + 1];
+    __shared__ float s_lse[2];
+    __shared__ int s_gave, s_n, s_bad, s_found, s_residual;
+    __shared__ float s_tprime;
+    __shared__ unsigned s_tag;
+    __shared__ float wl[kChunk];                     // the rescan's weights in token order
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const RowSet& rs = a.rs;
+    const int G = rs.gamma, V = rs.V, nch = a.nch, G1 = G + 1;
+    const long long task = blockIdx.x;
+    const long long unit = task / nch;
+    const int c = static_cast<int>(task - unit * nch);
+    const int b = static_cast<int>(unit / G1), s = static_cast<int>(unit - static_cast<long long>(b) * G1);
+    const ReqRows q = request_rows(rs, b);
+    const bool anchor = b == 0 && s == 0 && c == 0;
+    int32_t* y = a.y_out + static_cast<long long>(b) * G1;
+    if (!q.ok) {                                     // a faulty request: its first task reports it
+        if (s == 0 && c == 0) {
+            for (int i = tid; i <= G; i += kThreads) {
+                y[i] = -1;
+                if (a.lse_t_out) a.lse_t_out[static_cast<long long>(b) * G1 + i] = qnan();
+                if (i < G) {
+                    if (a.lse_d_out) a.lse_d_out[static_cast<long long>(b) * G + i] = qnan();
+                    a.cstar[static_cast<long long>(b) * G + i] = qnan();
+                }
+            }
+            if (tid == 0) a.n_out[b] = -1;
+        }
+        if (!anchor) return;
+    }
+    const bool live = q.ok && s <= q.ell;
+    const bool pair = live && s < q.ell;
+    float t[kPer], d[kPer];
+    float lsd = 0.0f, lst = 0.0f;
+    unsigned long long* us = a.slots + unit * nch * 4;
+    unsigned long long* ms = a.mslots + unit * nch * 4;
+    if (live) {
+        load_chunk<VEC4>(rs.Lt + (q.off + s) * V, c, V, t);
+        if (pair) load_chunk<VEC4>(rs.Ld + (static_cast<long long>(b) * G + s) * V, c, V, d);
+    }
+    // the call's tag, read while the chunk is on its way (the anchor counts on every task
+    // having read it before it publishes)
+    if (tid == 0) {
+        s_tag = call_tag(ld_agent(a.hdr));
+        s_gave = 0;
+    }
+    __syncthreads();
+    const unsigned tag = s_tag;
+    if (live) {
+        // 1. partials, published as tagged words; the unit's normalisers
+        float mt = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) mt = fmaxf(mt, t[e]);
+        float st = 0.0f;
+        if (mt != -INFINITY) {
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) st += __expf(t[e] - mt);
+        }
+        block_ms(mt, st, sm);
+        float md = -INFINITY, sd = 0.0f;
+        if (pair && !a.lse_d_in) {
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) md = fmaxf(md, d[e]);
+            if (md != -INFINITY) {
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) sd += __expf(d[e] - md);
+            }
+            block_ms(md, sd, sm);
+        }
+        if (tid < 4) {
+            const float v = tid == 0 ? md : tid == 1 ? sd : tid == 2 ? mt : st;
+            st_agent(us + 4 * c + tid, tagged(tag, v));
+        }
+        if (wave == 0) {
+            // lane i reads chunk i's four words
+            float2 pd = make_float2(-INFINITY, 0.0f), pt = make_float2(-INFINITY, 0.0f);
+            bool ok = true;
+            if (lane < nch) {
+                unsigned long long w[4];
+                for (unsigned n = 0;;) {
+                    bool all = true;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        w[j] = ld_agent(us + 4 * lane + j);
+                        all &= has_tag(w[j], tag);
+                    }
+                    if (all) break;
+                    if (++n > a.spin) {
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (ok) {
+                    pd = make_float2(tagged_f(w[0]), tagged_f(w[1]));
+                    pt = make_float2(tagged_f(w[2]), tagged_f(w[3]));
+                }
+            }
+            if (__any(!ok) && lane == 0) {
+                s_gave = 1;
+                st_agent(a.hdr + 1, static_cast<unsigned long long>(tag));
+            }
+            const float lt = merge_lanes(pt);
+            float ld = 0.0f;
+            if (pair) ld = a.lse_d_in ? a.lse_d_in[static_cast<long long>(b) * G + s] : merge_lanes(pd);
+            if (lane == 0) {
+                s_lse[0] = ld;
+                s_lse[1] = lt;
+            }
+        }
+        __syncthreads();
+        lsd = s_lse[0];
+        lst = s_lse[1];
+    }
+    if (live && !s_gave) {
+        // 2. the chunk's sums, published; the acceptance decision of its drafted token
+        float sv = 0.0f;
+        if (pair && lsd != -INFINITY && lst != -INFINITY) {
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) sv += __expf(fminf(d[e] - lsd, t[e] - lst));
+        }
+        if (pair) sv = block_sum<kThreads>(sv, fscr);
+        FinalRow fr;
+        fr.lt = nullptr;
+        fr.ld = nullptr;
+        fr.lse_t = lst;
+        fr.lse_d = pair ? lsd : 0.0f;
+        fr.residual = pair ? 1 : 0;
+        float mass = 0.0f, ptm = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) mass += fr.weight(t[e], pair ? d[e] : 0.0f);
+        mass = block_sum<kThreads>(mass, fscr);
+        if (pair) {
+            fr.residual = 0;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) ptm += fr.weight(t[e], 0.0f);
+            ptm = block_sum<kThreads>(ptm, fscr);
+        }
+        if (tid < 3) st_agent(ms + 4 * c + tid, tagged(tag, tid == 0 ? sv : tid == 1 ? mass : ptm));
+        if (pair) {
+            const int xk = a.x[static_cast<long long>(b) * G + s];
+            const long long base = static_cast<long long>(c) * kChunk;
+            unsigned long long* fl = a.flags + static_cast<long long>(b) * G + s;
+            if (xk < 0 || xk >= V) {
+                if (c == 0 && tid == 0) st_agent(fl, tagged(tag, 3u));
+            } else if (xk >= base && xk < base + kChunk) {
+                const int rel = static_cast<int>(xk - base);
+                if (tid == ((rel >> 2) & (kThreads - 1))) {
+                    const int ei = 4 * (rel >> 10) + (rel & 3);
+                    float ltx = 0.0f, ldx = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < kPer; ++e)
+                        if (e == ei) {
+                            ltx = t[e];
+                            ldx = d[e];
+                        }
+                    const float lpt = (lst == -INFINITY) ? -INFINITY : ltx - lst;
+                    const float lpd = (lsd == -INFINITY) ? -INFINITY : ldx - lsd;
+                    bool acc;
+                    if (lpd == -INFINITY)
+                        acc = lpt > -INFINITY;
+                    else
+                        acc = logf(clamp_uniform(a.u_acc[static_cast<long long>(b) * G + s])) < lpt - lpd;
+                    st_agent(fl, tagged(tag, acc ? 1u : 2u));
+                }
+            }
+        }
+        // normalisers out (chunk 0 of each unit; the bonus unit also fills what lies beyond)
+        if (c == 0) {
+            if (tid == 0) {
+                if (a.lse_t_out) a.lse_t_out[static_cast<long long>(b) * G1 + s] = lst;
+                if (pair && a.lse_d_out) a.lse_d_out[static_cast<long long>(b) * G + s] = lsd;
+            }
+            if (!pair) {
+                for (int i = s + 1 + tid; i <= G; i += kThreads)
+                    if (a.lse_t_out) a.lse_t_out[static_cast<long long>(b) * G1 + i] = qnan();
+                for (int i = s + tid; i < G; i += kThreads) {
+                    if (a.lse_d_out) a.lse_d_out[static_cast<long long>(b) * G + i] = qnan();
+                    a.cstar[static_cast<long long>(b) * G + i] = qnan();
+                }
+            }
+        }
+        // 3. one poll for the request's acceptance codes and the unit's chunk sums
+        if (wave == 0) {
+            unsigned long long fv = 0, w0 = 0, w1 = 0, w2 = 0;
+            bool ok = poll_tagged(lane < q.ell ? a.flags + static_cast<long long>(b) * G + lane : nullptr,
+                                  fv, tag, a.spin);
+            ok = ok && poll_tagged(lane < nch ? ms + 4 * lane : nullptr, w0, tag, a.spin);
+            ok = ok && poll_tagged(lane < nch ? ms + 4 * lane + 1 : nullptr, w1, tag, a.spin);
+            ok = ok && poll_tagged(lane < nch ? ms + 4 * lane + 2 : nullptr, w2, tag, a.spin);
+            const unsigned code = static_cast<unsigned>(fv) & 3u;
+            const bool bad = ok && lane < q.ell && code == 3u;
+            const bool rej = ok && lane < q.ell && code == 2u;
+            const unsigned long long badm = __ballot(bad), rejm = __ballot(rej);
+            const int n = rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : q.ell;
+            // c* of a verified position (chunk 0): tv_merge's sum over the chunks
+            float ps = (ok && lane < nch) ? tagged_f(w0) : 0.0f;
+            ps = wave_sum_dpp(ps);
+            if (pair && c == 0 && ok && lane == 0) a.cstar[static_cast<long long>(b) * G + s] = ps;
+            // the final draw's search when this unit is the final one (final_draw's search)
+            int found = -1;
+            float tprime = INFINITY;
+            bool residual = pair;
+            if (ok && badm == 0ull && s == n) {
+                float mv = (lane < nch) ? tagged_f(w1) : 0.0f;
+                const float pv = (lane < nch) ? tagged_f(w2) : 0.0f;
+                const float uf = clamp_uniform(a.u_fin[b]);
+                for (int pass = 0; pass < 2; ++pass) {
+                    const float v = (lane < nch) ? mv : 0.0f;
+                    const float tot = wave_sum_dpp(v);
+                    const float target = uf * tot;
+                    found = -1;
+                    tprime = INFINITY;
+                    const float incl = wave_incl_scan_dpp(v);
+                    const float excl = wave_shr1_dpp(incl);
+                    const unsigned long long hit = __ballot((lane < nch) && (v > 0.0f) && (incl > target));
+                    if (hit) {
+                        const int f = __ffsll(static_cast<long long>(hit)) - 1;
+                        found = f;
+                        tprime = target - (0.0f + wave_bcast(excl, f));
+                    }
+                    if (found < 0 && tot > 0.0f) {
+                        const int last = (lane < nch && v > 0.0f) ? lane : -1;
+                        found = wave_max_int_dpp(last);
+                        tprime = INFINITY;
+                    }
+                    if (tot > 0.0f || !residual) break;
+                    residual = false;                 // residual rounded to zero: p_t instead
+                    mv = pv;
+                }
+            }
+            if (lane == 0) {
+                if (!ok) {
+                    s_gave = 1;
+                    st_agent(a.hdr + 1, static_cast<unsigned long long>(tag));
+                }
+                s_bad = badm != 0ull;
+                s_n = n;
+                s_found = found;
+                s_tprime = tprime;
+                s_residual = residual ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        const int n = s_n;
+        if (!s_gave && s_bad && !pair && c == 0) {    // a drafted token outside [0, V)
+            for (int i = tid; i <= G; i += kThreads) y[i] = -1;
+            if (tid == 0) a.n_out[b] = -1;
+        }
+        const int found = s_found;
+        if (!s_gave && !s_bad && s == n && (found == c || (found < 0 && c == 0))) {
+            int z = -1;
+            if (found == c) {
+                // the rescan: weights into LDS in token order, then final_draw's layout and order
+                FinalRow fw;
+                fw.lt = nullptr;
+                fw.ld = nullptr;
+                fw.lse_t = lst;
+                fw.lse_d = pair ? lsd : 0.0f;
+                fw.residual = s_residual;
+#pragma unroll
+                for (int g = 0; g < kPer / 4; ++g)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const int e = 4 * g + w;
+                        wl[4 * (tid + kThreads * g) + w] = fw.weight(t[e], fw.residual ? d[e] : 0.0f);
+                    }
+                __syncthreads();
+                float wv[kPer];
+                float local = 0.0f;
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) {
+                    wv[e] = wl[kPer * tid + e];
+                    local += wv[e];
+                }
+                float tot;
+                const float ex = block_excl_scan<kThreads>(local, fscr, &tot);
+                const float tprime = s_tprime;
+                const long long v0 = static_cast<long long>(c) * kChunk + static_cast<long long>(kPer) * tid;
+                int hit = INT32_MAX, lastpos = -1;
+                float run = ex;
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) {
+                    run += wv[e];
+                    if (wv[e] > 0.0f) {
+                        lastpos = static_cast<int>(v0 + e);
+                        if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(v0 + e);
+                    }
+                }
+                z = block_min_int<kThreads>(hit, iscr);
+                if (z == INT32_MAX) z = block_max_int<kThreads>(lastpos, iscr);
+            }
+            for (int i = tid; i <= G; i += kThreads)
+                y[i] = (i < n) ? a.x[static_cast<long long>(b) * G + i] : (i == n ? z : -1);
+            if (tid == 0) a.n_out[b] = n;
+        }
+    }
+    // the anchor: once every live task has published its partials, the next call's counter
+    if (anchor) {
+        if (wave == 0) {
+            // lane l watches tasks l, l + 64, ...: all of its words are loaded together per round
+            constexpr int kPerLane = kSmallMaxTasks / kWave;
+            bool watch[kPerLane];
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) {
+                const long long tk = lane + static_cast<long long>(kWave) * j;
+                watch[j] = false;
+                if (tk < a.ntasks) {
+                    const long long u2 = tk / nch;
+                    const int b2 = static_cast<int>(u2 / G1), s2 = static_cast<int>(u2 - static_cast<long long>(b2) * G1);
+                    const ReqRows q2 = request_rows(rs, b2);
+                    watch[j] = q2.ok && s2 <= q2.ell;
+                }
+            }
+            for (unsigned n2 = 0;; ++n2) {
+                unsigned long long w[kPerLane];
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j)
+                    w[j] = watch[j] ? ld_agent(a.slots + (lane + static_cast<long long>(kWave) * j) * 4 + 3) : 0ull;
+                bool miss = false;
+#pragma unroll
+                for (int j = 0; j < kPerLane; ++j) {
+                    if (watch[j] && has_tag(w[j], tag)) watch[j] = false;
+                    miss |= watch[j];
+                }
+                if (!__any(miss) || n2 > a.spin) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        if (tid == 0) st_agent(a.hdr, ld_agent(a.hdr) + 1);
+    }
+}
+
 }  // namespace
 
 int verify_chunk_elems() { return kChunk; }
@@ -889,12 +1304,70 @@ size_t verify_sweep_bytes(int B, int V, int gamma) {
     const size_t nch = static_cast<size_t>(nchunks(V));
     const size_t units = static_cast<size_t>(B) * (gamma + 1);
     auto al = [](size_t n) { return (n + 255) / 256 * 256; };
-    return 256 + al(units * nch * 4 * sizeof(unsigned long long)) + al(units * sizeof(float2)) +
-           al(units * nch * sizeof(float)) + al(static_cast<size_t>(B) * gamma * nch * sizeof(float));
+    const size_t sweep = 256 + al(units * nch * 4 * sizeof(unsigned long long)) + al(units * sizeof(float2)) +
+                         al(units * nch * sizeof(float)) + al(static_cast<size_t>(B) * gamma * nch * sizeof(float));
+    const size_t small = 256 + 2 * al(units * nch * 4 * sizeof(unsigned long long)) +
+                         al(static_cast<size_t>(B) * gamma * sizeof(unsigned long long));
+    return sweep > small ? sweep : small;
+}
+
+// Resident workgroups of vt_small_kernel on the current device (0 if unknown).
+int small_capacity(bool vec4) {
+    thread_local SweepFit cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    SweepFit& f = cache[dev];
+    if (f.cus < 0 && hipDeviceGetAttribute(&f.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    int& occ = f.occ[vec4 ? 1 : 0];
+    if (occ < 0) {
+        int o = 0;
+        const hipError_t e = vec4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, vt_small_kernel<true>, kThreads, 0)
+                                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, vt_small_kernel<false>, kThreads, 0);
+        occ = (e == hipSuccess) ? o : 0;
+    }
+    return f.cus > 0 ? f.cus * occ : 0;
 }
 
 bool verify_sweep_ok(int V) {
     return nchunks(V) <= kWave && sweep_capacity(true) >= nchunks(V) && sweep_capacity(false) >= nchunks(V);
+}
+
+bool verify_small_ok(const RowSet& rs) {
+    const int nch = nchunks(rs.V);
+    const long long ntasks = static_cast<long long>(rs.B) * (rs.gamma + 1) * nch;
+    return nch <= kWave && ntasks <= kSmallMaxTasks && ntasks <= small_capacity(rows_vec4(rs));
+}
+
+hipError_t launch_verify_small(const RowSet& rs, const int32_t* x, const float* lse_d_in,
+                               const float* u_acc, const float* u_fin, float* lse_d_out,
+                               float* lse_t_out, int32_t* n_out, int32_t* y_out, float* cstar,
+                               void* ws, unsigned spin, hipStream_t st) {
+    SmallArgs a;
+    a.rs = rs;
+    a.nch = nchunks(rs.V);
+    a.ntasks = static_cast<long long>(rs.B) * (rs.gamma + 1) * a.nch;
+    a.lse_d_in = lse_d_in;
+    a.x = x; a.u_acc = u_acc; a.u_fin = u_fin;
+    a.lse_d_out = lse_d_out; a.lse_t_out = lse_t_out; a.n_out = n_out; a.y_out = y_out;
+    a.cstar = cstar;
+    a.spin = spin;
+    char* p = static_cast<char*>(ws);
+    auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+    const size_t units = static_cast<size_t>(rs.B) * (rs.gamma + 1);
+    a.hdr = reinterpret_cast<unsigned long long*>(p);
+    p += 256;
+    a.slots = reinterpret_cast<unsigned long long*>(p);
+    p += al(units * a.nch * 4 * sizeof(unsigned long long));
+    a.mslots = reinterpret_cast<unsigned long long*>(p);
+    p += al(units * a.nch * 4 * sizeof(unsigned long long));
+    a.flags = reinterpret_cast<unsigned long long*>(p);
+    const bool v4 = rows_vec4(rs);
+    if (v4)
+        hipLaunchKernelGGL(vt_small_kernel<true>, dim3(static_cast<unsigned>(a.ntasks)), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(vt_small_kernel<false>, dim3(static_cast<unsigned>(a.ntasks)), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_verify_sweep(const RowSet& rs, const int32_t* x, const float* lse_d_in,

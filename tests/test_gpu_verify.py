@@ -160,7 +160,9 @@ def test_verify_tv_matches_separate_calls(gpu, B, V, G, flat, given):
 
 @pytest.mark.parametrize("B,V,G,flat,given", [
     (2, 600000, 2, True, False),    # 74 chunks per row: past the one-sweep form, the chunked kernels
-    (3, 524288, 2, False, True),    # exactly 64 chunks: the one-sweep form at its cap
+    (3, 524288, 2, False, True),    # exactly 64 chunks: the persistent sweep (576 tasks)
+    (64, 40000, 5, True, False),    # 1920 tasks: the persistent sweep
+    (2, 40000, 5, False, True),     # 60 tasks: the one-launch form
 ])
 def test_verify_tv_at_the_sweep_cap(gpu, B, V, G, flat, given):
     """Both implementations of dspark_verify_tv (one sweep up to 64 chunks per row, the chunked
