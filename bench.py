@@ -45,36 +45,36 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
     ("single", "draft_resident"): dict(
-        bytes=86945882.1,
+        bytes=86944749.3,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
-        sources={"draft_resident.hip": "5cfbd024e5eebc35862cd5f69556d181c024d82ebd75d75508fbf4544b46bd60",
+        sources={"draft_resident.hip": "1205812310a76addccb39045c3db6b8512183917bf4df61dec9c0498bcaf3033",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the per-position sweep of one request (bench.py --per-position)
     ("single", "draft_step_gemv"): dict(
-        bytes=79192386.3,
+        bytes=79191939.8,
         profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
-        sources={"draft.hip": "8d2f4cb7c96b3b06c67cf019ce9feeadce6b05da7e71b20109131d26a887c15f",
+        sources={"draft.hip": "48a48f93317cfc1a63460cbe3d00ebf91bb049d6b29ba4e96aeab52653667d8d",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("batched", "draft_slab_resident"): dict(
-        bytes=1421449799.6,
+        bytes=1421492055.2,
         profile="profiles/draft_slab_resident_batched_B64_V151936.md",
-        sources={"draft_slab.hip": "19be639ac5edace8d1f3be5b5077b08e21960b1cead6f4683dc6d9ecc1157cee",
+        sources={"draft_slab.hip": "21b13026391fbfdf5bd1eb540df939c58901b0a9cb5ba32671181343b05300f5",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
-    # the three kernels of one dspark_verify_tv call (row_stats, verify_tv_chunks, verify_tv_select)
+    # the two kernels of one dspark_verify_tv call on the sweep path (vt_sweep, vt_select)
     ("verify", "dspark_verify_tv"): dict(
-        bytes=10478320250.1,
+        bytes=5427108003.4,
         profile="profiles/verify_tv_verify_B256_V151936.md",
-        sources={"verify.hip": "8c348ebe8b99160c5e819edfd8e793181a70e5e6a7593a08dba8c5ae0d5df81f",
+        sources={"verify.hip": "03f4a54e05cdae3bcc343aeb19175fb7ad829bb663b0a229845cfaf40c72e96e",
                  "rows.h": "069e0045b9a59c15697218de2708ffbdb33de09773099a9e0e95cad34229983b",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
-        bytes=4835639540.2,
+        bytes=4835563051.9,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
-        sources={"draft_slab.hip": "19be639ac5edace8d1f3be5b5077b08e21960b1cead6f4683dc6d9ecc1157cee",
+        sources={"draft_slab.hip": "21b13026391fbfdf5bd1eb540df939c58901b0a9cb5ba32671181343b05300f5",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
@@ -750,6 +750,8 @@ def run_workload(args, workload, torch, dspark, device, steps, cpu_seconds, mp):
                     launch_us=launch_us, call_us_graph=ms_parts[dominant] * 1e3,
                     timing="HIP events on the launch stream around eager calls",
                     limiter="HBM: one pass over the rows; per-chunk waits for the row's normalisers")
+        if roof["traffic"] is not None:
+            roof["physical_gbs"] = roof["traffic"] / (launch_us * 1e-6) / 1e9
     else:
         path = dspark.markov_draft_path(B, t["W1"], t["W2"])
         if args.per_position and path == "resident":
