@@ -33,61 +33,187 @@ namespace {
 using namespace rows;
 
 
-// Chunk c of a row in the sweep layout: thread t holds float4 granules t + kThreads*g.
+// Chunk c of a row in the sweep layout: thread t holds float4 granules t + kThreads*g. The
+// chunk's base is wave-uniform and the lane offsets are 32-bit, so each load takes a scalar base
+// and one offset register.
 template <bool VEC4>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int c, int V,
                                            float (&x)[kPer]) {
     const long long base = static_cast<long long>(c) * kChunk;
-    const int t = threadIdx.x;
+    const unsigned t = threadIdx.x;
+    const long long left = static_cast<long long>(V) - base;
+    const unsigned lim = static_cast<unsigned>(left < kChunk ? left : kChunk);   // logits in the chunk
     if (VEC4) {
         const float4* r4 = reinterpret_cast<const float4*>(row + base);
 #pragma unroll
         for (int g = 0; g < kPer / 4; ++g) {
-            const long long i = static_cast<long long>(t) + kThreads * g;
+            const unsigned i = t + kThreads * g;
             float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-            if (base + 4 * i < V) v = r4[i];        // V % 4 == 0: a granule is in or out
+            if (4 * i < lim) v = r4[i];             // V % 4 == 0: a granule is in or out
             x[4 * g] = v.x; x[4 * g + 1] = v.y; x[4 * g + 2] = v.z; x[4 * g + 3] = v.w;
         }
     } else {
+        const float* r = row + base;
 #pragma unroll
         for (int g = 0; g < kPer / 4; ++g)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const long long v = base + 4 * (static_cast<long long>(t) + kThreads * g) + w;
-                x[4 * g + w] = (v < V) ? row[v] : -INFINITY;
+                const unsigned v = 4 * (t + kThreads * g) + w;
+                x[4 * g + w] = (v < lim) ? r[v] : -INFINITY;
             }
     }
 }
 
-// (max, sum exp(x - max)) pairs; the combination is symmetric, so butterflies are exact.
-__device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s2) {
-    const float mm = fmaxf(m, m2);
-    if (mm == -INFINITY) {
-        m = -INFINITY;
-        s = 0.0f;
-        return;
-    }
-    s = s * __expf(m - mm) + s2 * __expf(m2 - mm);
-    m = mm;
+// Within a chunk every probability is formed from the chunk's own maximum M: the term
+// e = exp(x - M) gives both the chunk's (max, sum exp) partial and, once the row's lse is known,
+// the probability p = e * exp(M - lse). So one exponential per logit serves the normalisers, the
+// TV sums and the final-draw masses, and every kernel that forms a probability of a chunk forms
+// the same value.
+
+// The maximum of a chunk held kPer values per thread (the same in every thread): within each
+// wave by DPP, then over the waves. red holds kWaves floats, not written again before a later
+// barrier.
+__device__ __forceinline__ float chunk_max(const float (&x)[kPer], float* red) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    float ml = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) ml = fmaxf(ml, x[e]);
+    ml = wave_max_dpp(ml);
+    if (lane == 0) red[wave] = ml;
+    __syncthreads();
+    float mm = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, red[w]);
+    return mm;
 }
 
-__device__ __forceinline__ void block_ms(float& m, float& s, float (*sm)[kWaves]) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
-        ms_combine(m, s, m2, s2);
-    }
+// Two chunks' maxima at once (one barrier); red holds [2][kWaves] floats.
+__device__ __forceinline__ void chunk_max2(const float (&x)[kPer], const float (&y)[kPer],
+                                           float& mx, float& my, float (*red)[kWaves]) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    float ax = -INFINITY, ay = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        ax = fmaxf(ax, x[e]);
+        ay = fmaxf(ay, y[e]);
+    }
+    ax = wave_max_dpp(ax);
+    ay = wave_max_dpp(ay);
     if (lane == 0) {
-        sm[0][wave] = m;
-        sm[1][wave] = s;
+        red[0][wave] = ax;
+        red[1][wave] = ay;
     }
     __syncthreads();
-    m = sm[0][0];
-    s = sm[1][0];
+    mx = red[0][0];
+    my = red[1][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) ms_combine(m, s, sm[0][w], sm[1][w]);
+    for (int w = 1; w < kWaves; ++w) {
+        mx = fmaxf(mx, red[0][w]);
+        my = fmaxf(my, red[1][w]);
+    }
+}
+
+// e = exp(x - m) of one logit; a chunk whose max is -inf has no mass (e = 0).
+__device__ __forceinline__ float chunk_e(float x, float m) {
+    return (m == -INFINITY) ? 0.0f : __expf(x - m);
+}
+
+// The factor exp(M - lse) that turns a chunk's terms into probabilities; 0 for a row (or chunk)
+// with no mass.
+__device__ __forceinline__ float chunk_scale(float m, float lse) {
+    return (m == -INFINITY || lse == -INFINITY) ? 0.0f : __expf(m - lse);
+}
+
+// (max, sum exp(x - max)) of one chunk: the chunk's max, then its terms, summed within each
+// wave by DPP and over the waves in wave order. With KEEP the terms replace x. red holds
+// [2][kWaves] floats, not written again before a later barrier.
+template <bool KEEP>
+__device__ __forceinline__ void chunk_ms(float (&x)[kPer], float& m, float& s,
+                                         float (*red)[kWaves]) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const float mm = chunk_max(x, red[0]);
+    float sl = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const float v = chunk_e(x[e], mm);
+        sl += v;
+        if (KEEP) x[e] = v;
+    }
+    sl = wave_sum_dpp(sl);
+    if (lane == 0) red[1][wave] = sl;
     __syncthreads();
+    float ss = red[1][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) ss += red[1][w];
+    m = mm;
+    s = ss;
+}
+
+// chunk_ms of two rows at once (per row the same arithmetic), one pair of barriers for both;
+// red holds [4][kWaves] floats.
+template <bool KEEP>
+__device__ __forceinline__ void chunk_ms2(float (&x)[kPer], float (&y)[kPer], float& mx,
+                                          float& sx, float& my, float& sy, float (*red)[kWaves]) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    float mmx, mmy;
+    chunk_max2(x, y, mmx, mmy, red);
+    float lx = 0.0f, ly = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const float vx = chunk_e(x[e], mmx), vy = chunk_e(y[e], mmy);
+        lx += vx;
+        ly += vy;
+        if (KEEP) {
+            x[e] = vx;
+            y[e] = vy;
+        }
+    }
+    lx = wave_sum_dpp(lx);
+    ly = wave_sum_dpp(ly);
+    if (lane == 0) {
+        red[2][wave] = lx;
+        red[3][wave] = ly;
+    }
+    __syncthreads();
+    float ssx = red[2][0], ssy = red[3][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        ssx += red[2][w];
+        ssy += red[3][w];
+    }
+    mx = mmx;
+    sx = ssx;
+    my = mmy;
+    sy = ssy;
+}
+
+// Workgroup sums of N per-thread values at once: within each wave by DPP, then over the waves
+// in wave order, one barrier for all N. scratch holds N kWaves floats, not written again before
+// a later barrier. Every chunk-level sum of a probability (TV sums, final-draw masses) goes
+// through here, so each kernel that forms such a sum forms the same value.
+template <int N>
+__device__ __forceinline__ void chunk_sums(float (&v)[N], float* scratch) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = wave_sum_dpp(v[j]);
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) scratch[j * kWaves + wave] = v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        float t = scratch[j * kWaves];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) t += scratch[j * kWaves + w];
+        v[j] = t;
+    }
+}
+
+__device__ __forceinline__ float chunk_sum(float x, float* scratch) {
+    float v[1] = {x};
+    chunk_sums<1>(v, scratch);
+    return v[0];
 }
 
 // ----------------------------------------------------------------------------- row_stats
@@ -115,42 +241,60 @@ void row_stats_kernel(RowSet rs, int nch, const float* __restrict__ lse_d_in,
     if (!valid) return;
     float x[kPer];
     load_chunk<VEC4>(row, c, rs.V, x);
-    float m = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) m = fmaxf(m, x[e]);
-    float s = 0.0f;
-    if (m != -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) s += __expf(x[e] - m);
-    }
-    block_ms(m, s, sm);
+    float m, s;
+    chunk_ms<false>(x, m, s, sm);
     if (threadIdx.x == 0) part[rowid * nch + c] = make_float2(m, s);
 }
 
 // ----------------------------------------------------------------------------- verify
-// Weights of the final draw: p_t (bonus, or residual with zero mass) or max(0, p_t - p_d).
+// The final draw's row: its weights are p_t (bonus, or residual with zero mass) or
+// max(0, p_t - p_d), formed per chunk from the chunk's terms (see chunk_ms).
 struct FinalRow {
     const float* lt;
     const float* ld;
     float lse_t, lse_d;
     int residual;
+    float sct, scd;                 // this chunk's exp(M - lse) of the target and draft rows
 
-    __device__ __forceinline__ float weight(float lt_v, float ld_v) const {
-        const float pt = (lse_t == -INFINITY) ? 0.0f : __expf(lt_v - lse_t);
+    // the scales of a chunk whose target and draft maxima are mt and md
+    __device__ __forceinline__ void at_chunk(float mt, float md) {
+        sct = chunk_scale(mt, lse_t);
+        scd = residual ? chunk_scale(md, lse_d) : 0.0f;
+    }
+    // the weight of a logit pair from its chunk terms e_t, e_d
+    __device__ __forceinline__ float weight(float et, float ed) const {
+        const float pt = et * sct;
         if (!residual) return pt;
-        const float pd = (lse_d == -INFINITY) ? 0.0f : __expf(ld_v - lse_d);
-        return fmaxf(pt - pd, 0.0f);
+        return fmaxf(pt - ed * scd, 0.0f);
     }
 };
 
+// A chunk's terms in place and the scales of fr at that chunk (the chunk's maxima by block
+// reductions). red holds [2][kWaves] floats.
+__device__ __forceinline__ void chunk_terms(FinalRow& fr, float (&t)[kPer], float (&d)[kPer],
+                                            float (*red)[kWaves]) {
+    float mt, md = -INFINITY;
+    if (fr.residual)
+        chunk_max2(t, d, mt, md, red);
+    else
+        mt = chunk_max(t, red[0]);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        t[e] = chunk_e(t[e], mt);
+        d[e] = fr.residual ? chunk_e(d[e], md) : 0.0f;
+    }
+    fr.at_chunk(mt, md);
+}
+
 template <bool VEC4>
-__device__ __forceinline__ float chunk_mass(const FinalRow& fr, int c, int V) {
+__device__ __forceinline__ float chunk_mass(FinalRow fr, int c, int V, float (*red)[kWaves]) {
     float t[kPer], d[kPer];
     load_chunk<VEC4>(fr.lt, c, V, t);
     if (fr.residual) load_chunk<VEC4>(fr.ld, c, V, d);
+    chunk_terms(fr, t, d, red);
     float s = 0.0f;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) s += fr.weight(t[e], fr.residual ? d[e] : 0.0f);
+    for (int e = 0; e < kPer; ++e) s += fr.weight(t[e], d[e]);
     return s;
 }
 
@@ -168,6 +312,7 @@ __device__ __forceinline__ void verify_chunks_body(const RowSet& rs, int nch, co
                                    float* __restrict__ lse_t_out, float* __restrict__ csum,
                                    ReqState* __restrict__ state, unsigned blk) {
     __shared__ float fscr[kWaves + 1];
+    __shared__ float red[2][kWaves];
     __shared__ float s_lt[65], s_ld[64];
     __shared__ int s_n, s_bad;
 
@@ -259,7 +404,7 @@ __device__ __forceinline__ void verify_chunks_body(const RowSet& rs, int nch, co
     fr.residual = n < q.ell;
     fr.ld = fr.residual ? rs.Ld + (static_cast<long long>(b) * G + n) * V : nullptr;
     fr.lse_d = fr.residual ? s_ld[n] : 0.0f;
-    const float s = block_sum<kThreads>(chunk_mass<VEC4>(fr, c, V), fscr);
+    const float s = chunk_sum(chunk_mass<VEC4>(fr, c, V, red), fscr);
     if (tid == 0) csum[static_cast<long long>(b) * nch + c] = s;
 }
 
@@ -281,6 +426,7 @@ void verify_chunks_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
 template <bool VEC4>
 __device__ __forceinline__ int final_draw(int V, int nch, FinalRow fr, float* cs, float uf) {
     __shared__ float fscr[kWaves + 1];
+    __shared__ float red[2][kWaves];
     __shared__ int iscr[kWaves + 1];
     __shared__ int s_found;
     __shared__ float s_tprime, s_total;
@@ -327,7 +473,7 @@ __device__ __forceinline__ int final_draw(int V, int nch, FinalRow fr, float* cs
         // residual mass rounded to zero: draw from p_t of the same target row instead
         fr.residual = 0;
         for (int i = 0; i < nch; ++i) {
-            const float s = block_sum<kThreads>(chunk_mass<VEC4>(fr, i, V), fscr);
+            const float s = chunk_sum(chunk_mass<VEC4>(fr, i, V, red), fscr);
             if (tid == 0) cs[i] = s;
         }
         __syncthreads();
@@ -339,11 +485,12 @@ __device__ __forceinline__ int final_draw(int V, int nch, FinalRow fr, float* cs
         float t[kPer], d[kPer];
         load_chunk_contig<VEC4>(fr.lt, found, V, t);
         if (fr.residual) load_chunk_contig<VEC4>(fr.ld, found, V, d);
+        chunk_terms(fr, t, d, red);
         float w[kPer];
         float local = 0.0f;
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
-            w[e] = fr.weight(t[e], fr.residual ? d[e] : 0.0f);
+            w[e] = fr.weight(t[e], d[e]);
             local += w[e];
         }
         float tot;
@@ -412,6 +559,7 @@ __device__ __forceinline__ void tv_chunks_body(const RowSet& rs, int nch, const 
                                const float* __restrict__ lse_t, const float2* __restrict__ part,
                                float* __restrict__ psum, unsigned blk) {
     __shared__ float fscr[kWaves + 1];
+    __shared__ float red[2][kWaves];
     __shared__ float s_lse[2];
     const int G = rs.gamma, V = rs.V, tid = threadIdx.x;
     const int c = static_cast<int>(blk % static_cast<unsigned>(nch));
@@ -437,10 +585,13 @@ __device__ __forceinline__ void tv_chunks_body(const RowSet& rs, int nch, const 
         float ld[kPer], lt[kPer];
         load_chunk<VEC4>(rs.Ld + pair * V, c, V, ld);
         load_chunk<VEC4>(rs.Lt + (q.off + k) * V, c, V, lt);
+        float md, mt;
+        chunk_max2(ld, lt, md, mt, red);
+        const float scd = chunk_scale(md, a), sct = chunk_scale(mt, cc);
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) s += __expf(fminf(ld[e] - a, lt[e] - cc));
+        for (int e = 0; e < kPer; ++e) s += fminf(chunk_e(ld[e], md) * scd, chunk_e(lt[e], mt) * sct);
     }
-    s = block_sum<kThreads>(s, fscr);
+    s = chunk_sum(s, fscr);
     if (tid == 0) psum[pair * nch + c] = s;
 }
 
@@ -522,10 +673,11 @@ void verify_tv_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
 // for bit. vt_select then runs the acceptance test and the final draw per request from these
 // results (reading only the drafted tokens' logits and the one chunk it rescans) and merges c*.
 //
-// The grid is persistent: every workgroup is resident at once (checked by the host), and
-// workgroup w takes tasks w, w + N, w + 2N, ... A unit's nch chunks are consecutive tasks, so
-// they belong to nch different workgroups, each of which reaches them after finishing tasks of
-// earlier units only; by induction over units every wait ends. Polling is bounded all the
+// The grid is persistent: every workgroup is resident at once (checked by the host). It is
+// split into groups of N >= nch workgroups, each group sweeping a contiguous range of units,
+// and workgroup w of a group takes the group's tasks w, w + N, w + 2N, ... A unit's nch chunks
+// are consecutive tasks, so they belong to nch different workgroups, each of which reaches them
+// after finishing tasks of earlier units only; by induction over units every wait ends. Polling is bounded all the
 // same: a workgroup that gives up writes the call's key into the give-up word, and vt_select
 // then reports every request as faulty.
 //
@@ -560,6 +712,8 @@ struct SweepArgs {
     float* psum;                      // [b gamma + k][nch] sum of min(p_d, p_t)
     unsigned long long* hdr;          // [0] call counter E, [1] give-up key, [2] this sweep's key
     unsigned spin;
+    long long units;                  // B (gamma + 1)
+    int groups;                       // workgroup groups, each sweeping its own range of units
 };
 
 // lse of a unit's row from the lanes' chunk partials (lane i holds chunk i < nch <= 64; the
@@ -575,8 +729,8 @@ __device__ __forceinline__ float merge_lanes(float2 p0) {
 template <bool VEC4>
 __global__ __launch_bounds__(kThreads, 4)      // four workgroups per CU
 void vt_sweep_kernel(SweepArgs a) {
-    __shared__ float sm[2][kWaves];
-    __shared__ float fscr[kWaves + 1];
+    __shared__ float sm[4][kWaves];
+    __shared__ float fscr[2 * (kWaves + 1)];
     __shared__ float s_lse[2];
     __shared__ int s_gave;
     __shared__ unsigned long long s_key;
@@ -590,7 +744,13 @@ void vt_sweep_kernel(SweepArgs a) {
     }
     __syncthreads();
     const unsigned long long key = s_key;
-    for (long long task = blockIdx.x; task < a.ntasks; task += gridDim.x) {
+    // group grp of the workgroups sweeps units [u0, u1), its workgroups taking its tasks
+    // round-robin; a unit's waits then involve the workgroups of one group only
+    const unsigned per = gridDim.x / static_cast<unsigned>(a.groups);
+    const unsigned grp = blockIdx.x / per;
+    const long long u0 = a.units * grp / a.groups, u1 = a.units * (grp + 1) / a.groups;
+    for (long long lt = blockIdx.x - grp * per; lt < (u1 - u0) * nch; lt += per) {
+        const long long task = u0 * nch + lt;
         const long long unit = task / nch;
         const int c = static_cast<int>(task - unit * nch);
         const int b = static_cast<int>(unit / G1), s = static_cast<int>(unit - static_cast<long long>(b) * G1);
@@ -601,25 +761,13 @@ void vt_sweep_kernel(SweepArgs a) {
         load_chunk<VEC4>(rs.Lt + (q.off + s) * V, c, V, t);
         if (pair) load_chunk<VEC4>(rs.Ld + (static_cast<long long>(b) * G + s) * V, c, V, d);
         // 1. chunk partials (row_stats' arithmetic), published with the key
-        float mt = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) mt = fmaxf(mt, t[e]);
-        float st = 0.0f;
-        if (mt != -INFINITY) {
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) st += __expf(t[e] - mt);
-        }
-        block_ms(mt, st, sm);
-        float md = -INFINITY, sd = 0.0f;
-        if (pair && !a.lse_d_in) {
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) md = fmaxf(md, d[e]);
-            if (md != -INFINITY) {
-#pragma unroll
-                for (int e = 0; e < kPer; ++e) sd += __expf(d[e] - md);
-            }
-            block_ms(md, sd, sm);
-        }
+        // (the registers then hold the chunk's terms exp(x - M); a pair forms both rows'
+        // terms, also when the draft's lse is given)
+        float mt, st, md = -INFINITY, sd = 0.0f;
+        if (pair)
+            chunk_ms2<true>(t, d, mt, st, md, sd, sm);
+        else
+            chunk_ms<true>(t, mt, st, sm);
         unsigned long long* us = a.slots + unit * nch * 4;
         if (tid == 0) {
             st_agent(us + 4 * c, __builtin_bit_cast(unsigned long long, make_float2(md, sd)));
@@ -663,26 +811,28 @@ void vt_sweep_kernel(SweepArgs a) {
         const float lsd = s_lse[0], lst = s_lse[1];
         if (c == 0 && tid == 0) a.ulse[unit] = make_float2(lsd, lst);
         // 3. sum of min(p_d, p_t) (tv_chunks' arithmetic) and the final-draw mass
-        //    (chunk_mass' arithmetic) from the registers
+        //    (chunk_mass' arithmetic) from the chunk's terms in the registers
+        const float sct = chunk_scale(mt, lst);
+        float sv = 0.0f, mass = 0.0f;
         if (pair) {
-            float sv = 0.0f;
-            if (lsd != -INFINITY && lst != -INFINITY) {
+            // (a row with no mass has scale 0, so the sum is 0 as tv_chunks leaves it)
+            const float scd = chunk_scale(md, lsd);
 #pragma unroll
-                for (int e = 0; e < kPer; ++e) sv += __expf(fminf(d[e] - lsd, t[e] - lst));
+            for (int e = 0; e < kPer; ++e) {
+                const float pt = t[e] * sct, pd = d[e] * scd;
+                sv += fminf(pd, pt);
+                mass += fmaxf(pt - pd, 0.0f);
             }
-            sv = block_sum<kThreads>(sv, fscr);
+            float v2[2] = {sv, mass};
+            chunk_sums<2>(v2, fscr);
+            sv = v2[0];
+            mass = v2[1];
             if (tid == 0) a.psum[(static_cast<long long>(b) * G + s) * nch + c] = sv;
-        }
-        FinalRow fr;
-        fr.lt = nullptr;
-        fr.ld = nullptr;
-        fr.lse_t = lst;
-        fr.lse_d = pair ? lsd : 0.0f;
-        fr.residual = pair ? 1 : 0;
-        float mass = 0.0f;
+        } else {
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) mass += fr.weight(t[e], pair ? d[e] : 0.0f);
-        mass = block_sum<kThreads>(mass, fscr);
+            for (int e = 0; e < kPer; ++e) mass += t[e] * sct;
+            mass = chunk_sum(mass, fscr);
+        }
         if (tid == 0) a.rmass[unit * nch + c] = mass;
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -873,8 +1023,8 @@ __device__ __forceinline__ bool poll_tagged(const unsigned long long* p, unsigne
 template <bool VEC4>
 __global__ __launch_bounds__(kThreads, 2)
 void vt_small_kernel(SmallArgs a) {
-    __shared__ float sm[2][kWaves];
-    __shared__ float fscr[kWaves + 1];
+    __shared__ float sm[4][kWaves];
+    __shared__ float fscr[3 * kWaves + 1];
     __shared__ int iscr[kWaves + 1];
     __shared__ float s_lse[2];
     __shared__ int s_gave, s_n, s_bad, s_found, s_residual;
@@ -923,27 +1073,17 @@ void vt_small_kernel(SmallArgs a) {
     }
     __syncthreads();
     const unsigned tag = s_tag;
+    float cmt = -INFINITY, cmd = -INFINITY;          // the chunk's maxima (target, draft)
     if (live) {
-        // 1. partials, published as tagged words; the unit's normalisers
-        float mt = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) mt = fmaxf(mt, t[e]);
-        float st = 0.0f;
-        if (mt != -INFINITY) {
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) st += __expf(t[e] - mt);
-        }
-        block_ms(mt, st, sm);
-        float md = -INFINITY, sd = 0.0f;
-        if (pair && !a.lse_d_in) {
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) md = fmaxf(md, d[e]);
-            if (md != -INFINITY) {
-#pragma unroll
-                for (int e = 0; e < kPer; ++e) sd += __expf(d[e] - md);
-            }
-            block_ms(md, sd, sm);
-        }
+        // 1. partials, published as tagged words; the unit's normalisers (a pair forms both
+        //    rows' partials, also when the draft's lse is given: its terms need the max)
+        float mt, st, md = -INFINITY, sd = 0.0f;
+        if (pair)
+            chunk_ms2<false>(t, d, mt, st, md, sd, sm);
+        else
+            chunk_ms<false>(t, mt, st, sm);
+        cmt = mt;
+        cmd = md;
         if (tid < 4) {
             const float v = tid == 0 ? md : tid == 1 ? sd : tid == 2 ? mt : st;
             st_agent(us + 4 * c + tid, tagged(tag, v));
@@ -991,28 +1131,27 @@ void vt_small_kernel(SmallArgs a) {
     }
     if (live && !s_gave) {
         // 2. the chunk's sums, published; the acceptance decision of its drafted token
-        float sv = 0.0f;
-        if (pair && lsd != -INFINITY && lst != -INFINITY) {
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) sv += __expf(fminf(d[e] - lsd, t[e] - lst));
-        }
-        if (pair) sv = block_sum<kThreads>(sv, fscr);
-        FinalRow fr;
-        fr.lt = nullptr;
-        fr.ld = nullptr;
-        fr.lse_t = lst;
-        fr.lse_d = pair ? lsd : 0.0f;
-        fr.residual = pair ? 1 : 0;
-        float mass = 0.0f, ptm = 0.0f;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) mass += fr.weight(t[e], pair ? d[e] : 0.0f);
-        mass = block_sum<kThreads>(mass, fscr);
+        // (from the chunk's terms: sum of min(p_d, p_t), the final-draw mass, p_t's mass)
+        const float sct = chunk_scale(cmt, lst);
+        float sv = 0.0f, mass = 0.0f, ptm = 0.0f;
         if (pair) {
-            fr.residual = 0;
+            const float scd = chunk_scale(cmd, lsd);
 #pragma unroll
-            for (int e = 0; e < kPer; ++e) ptm += fr.weight(t[e], 0.0f);
-            ptm = block_sum<kThreads>(ptm, fscr);
+            for (int e = 0; e < kPer; ++e) {
+                const float pt = chunk_e(t[e], cmt) * sct, pd = chunk_e(d[e], cmd) * scd;
+                sv += fminf(pd, pt);
+                mass += fmaxf(pt - pd, 0.0f);
+                ptm += pt;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) mass += chunk_e(t[e], cmt) * sct;
         }
+        float v3[3] = {sv, mass, ptm};
+        chunk_sums<3>(v3, fscr);
+        sv = v3[0];
+        mass = v3[1];
+        ptm = v3[2];
         if (tid < 3) st_agent(ms + 4 * c + tid, tagged(tag, tid == 0 ? sv : tid == 1 ? mass : ptm));
         if (pair) {
             const int xk = a.x[static_cast<long long>(b) * G + s];
@@ -1135,12 +1274,14 @@ void vt_small_kernel(SmallArgs a) {
                 fw.lse_t = lst;
                 fw.lse_d = pair ? lsd : 0.0f;
                 fw.residual = s_residual;
+                fw.at_chunk(cmt, cmd);
 #pragma unroll
                 for (int g = 0; g < kPer / 4; ++g)
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         const int e = 4 * g + w;
-                        wl[4 * (tid + kThreads * g) + w] = fw.weight(t[e], fw.residual ? d[e] : 0.0f);
+                        wl[4 * (tid + kThreads * g) + w] =
+                            fw.weight(chunk_e(t[e], cmt), fw.residual ? chunk_e(d[e], cmd) : 0.0f);
                     }
                 __syncthreads();
                 float wv[kPer];
@@ -1394,7 +1535,12 @@ hipError_t launch_verify_sweep(const RowSet& rs, const int32_t* x, const float* 
     a.psum = reinterpret_cast<float*>(p);
     const bool v4 = rows_vec4(rs);
     const long long cap = sweep_capacity(v4);
-    const unsigned grid = static_cast<unsigned>(a.ntasks < cap ? a.ntasks : cap);
+    a.units = static_cast<long long>(units);
+    // two groups when each still has a workgroup per chunk of a row and the sweep takes
+    // several rounds of tasks
+    a.groups = (cap / 2 >= a.nch && a.ntasks >= 2 * cap) ? 2 : 1;
+    unsigned grid = static_cast<unsigned>(a.ntasks < cap ? a.ntasks : cap);
+    grid = grid / a.groups * a.groups;
     if (v4)
         hipLaunchKernelGGL(vt_sweep_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a);
     else
