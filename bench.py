@@ -66,9 +66,9 @@ MEASURED_TRAFFIC = {
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the two kernels of one dspark_verify_tv call on the sweep path (vt_sweep, vt_select)
     ("verify", "dspark_verify_tv"): dict(
-        bytes=5287520990.5,
+        bytes=5286748767.6,
         profile="profiles/verify_tv_verify_B256_V151936.md",
-        sources={"verify.hip": "5a4ee497e9b17212df82fb74c9ba717c1577c12588b87776b36451b7776e6bec",
+        sources={"verify.hip": "99cd80b7f65f69eb92ba582a9ce10ce4870b5070caec8936cca3ab9333186687",
                  "rows.h": "069e0045b9a59c15697218de2708ffbdb33de09773099a9e0e95cad34229983b",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(

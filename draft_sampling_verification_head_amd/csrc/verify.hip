@@ -113,10 +113,15 @@ __device__ __forceinline__ void chunk_max2(const float (&x)[kPer], const float (
     }
 }
 
-// e = exp(x - m) of one logit; a chunk whose max is -inf has no mass (e = 0).
-__device__ __forceinline__ float chunk_e(float x, float m) {
-    return (m == -INFINITY) ? 0.0f : __expf(x - m);
+// e = exp(x - m) of a logit x of a chunk whose max is m, as 2^(x log2(e) - m log2(e)) with
+// one fused multiply-add. A chunk whose max is -inf holds only -inf logits: there m log2(e)
+// is taken as 0, and every term is 2^-inf = 0.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float chunk_ml2(float m) { return (m == -INFINITY) ? 0.0f : m * kLog2e; }
+__device__ __forceinline__ float chunk_e2(float x, float ml2) {
+    return __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -ml2));
 }
+__device__ __forceinline__ float chunk_e(float x, float m) { return chunk_e2(x, chunk_ml2(m)); }
 
 // The factor exp(M - lse) that turns a chunk's terms into probabilities; 0 for a row (or chunk)
 // with no mass.
@@ -132,10 +137,11 @@ __device__ __forceinline__ void chunk_ms(float (&x)[kPer], float& m, float& s,
                                          float (*red)[kWaves]) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const float mm = chunk_max(x, red[0]);
+    const float ml2 = chunk_ml2(mm);
     float sl = 0.0f;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-        const float v = chunk_e(x[e], mm);
+        const float v = chunk_e2(x[e], ml2);
         sl += v;
         if (KEEP) x[e] = v;
     }
@@ -157,10 +163,11 @@ __device__ __forceinline__ void chunk_ms2(float (&x)[kPer], float (&y)[kPer], fl
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     float mmx, mmy;
     chunk_max2(x, y, mmx, mmy, red);
+    const float lx2 = chunk_ml2(mmx), ly2 = chunk_ml2(mmy);
     float lx = 0.0f, ly = 0.0f;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-        const float vx = chunk_e(x[e], mmx), vy = chunk_e(y[e], mmy);
+        const float vx = chunk_e2(x[e], lx2), vy = chunk_e2(y[e], ly2);
         lx += vx;
         ly += vy;
         if (KEEP) {
@@ -278,10 +285,11 @@ __device__ __forceinline__ void chunk_terms(FinalRow& fr, float (&t)[kPer], floa
         chunk_max2(t, d, mt, md, red);
     else
         mt = chunk_max(t, red[0]);
+    const float t2 = chunk_ml2(mt), d2 = chunk_ml2(md);
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-        t[e] = chunk_e(t[e], mt);
-        d[e] = fr.residual ? chunk_e(d[e], md) : 0.0f;
+        t[e] = chunk_e2(t[e], t2);
+        d[e] = fr.residual ? chunk_e2(d[e], d2) : 0.0f;
     }
     fr.at_chunk(mt, md);
 }
@@ -588,8 +596,9 @@ __device__ __forceinline__ void tv_chunks_body(const RowSet& rs, int nch, const 
         float md, mt;
         chunk_max2(ld, lt, md, mt, red);
         const float scd = chunk_scale(md, a), sct = chunk_scale(mt, cc);
+        const float d2 = chunk_ml2(md), t2 = chunk_ml2(mt);
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) s += fminf(chunk_e(ld[e], md) * scd, chunk_e(lt[e], mt) * sct);
+        for (int e = 0; e < kPer; ++e) s += fminf(chunk_e2(ld[e], d2) * scd, chunk_e2(lt[e], t2) * sct);
     }
     s = chunk_sum(s, fscr);
     if (tid == 0) psum[pair * nch + c] = s;

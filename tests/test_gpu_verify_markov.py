@@ -58,7 +58,11 @@ def _final_law(L, Lt, b, off, n, ell):
 
 def _compare(inp, D, A, M, B, G):
     """Identical acceptance decisions and normalisers; final tokens equal up to CDF ties;
-    labels equal up to summation order."""
+    labels equal up to summation order. The two paths form the final-draw weights from
+    different exponentials (per 8192-logit chunk from the read rows, per slab tile from the
+    rebuilt logits), so a final draw may fall on either side of a cell edge: each such
+    difference must be a CDF tie of the token the rebuilt path drew, and their number stays
+    within the harness's tie bound over the B final draws."""
     assert np.array_equal(A["n"], M["n"])
     assert np.array_equal(A["lse_t"].view(np.uint8), M["lse_t"].view(np.uint8))
     ties = 0
@@ -75,7 +79,7 @@ def _compare(inp, D, A, M, B, G):
             law = _final_law(D["L"], inp["Lt"], b, off, n, ell)
             assert is_cdf_tie(law, oracle.clamp_uniform(inp["u_fin"][b]), int(M["y"][b, n]))
             ties += 1
-    assert ties <= 1
+    assert ties <= 2 + B // 20
     fin = np.isfinite(A["cstar"])
     assert np.array_equal(fin, np.isfinite(M["cstar"]))
     if fin.any():
