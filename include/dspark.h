@@ -283,11 +283,17 @@ int dspark_tv_labels(int B, int V, int gamma,
 
 /*
  * Verify and TV labels in one call: the same results as dspark_verify followed by
- * dspark_tv_labels on the same rows, in fewer launches (the TV chunk sums run beside the
- * acceptance pass, the TV merges beside the final draws). Arguments as in dspark_verify,
- * plus cstar_out [B][gamma] fp32 (required) as in dspark_tv_labels. The normalisers of
- * both come from the same row partials, so c* equals what dspark_tv_labels computes from
- * this call's lse_d / lse_t.
+ * dspark_tv_labels on the same rows, bit for bit. Arguments as in dspark_verify, plus
+ * cstar_out [B][gamma] fp32 (required) as in dspark_tv_labels. The normalisers of both come
+ * from the same row partials, so c* equals what dspark_tv_labels computes from this call's
+ * lse_d / lse_t.
+ * Rows of at most 64 chunks of 8192 logits (V <= 524288) are read once: a persistent pass
+ * keeps each chunk of a row pair in registers until the row's normalisers are known (two
+ * launches), or for at most 768 (row, chunk) tasks a single launch that also draws the
+ * final token. Longer rows take two passes (normalisers, then acceptance data and TV sums).
+ * Every path forms a probability from its chunk's maximum M as exp(x - M) * exp(M - lse).
+ * The one-pass forms need every workgroup of the launch resident at once and must not
+ * overlap another call on the same workspace.
  */
 size_t dspark_verify_tv_workspace_bytes(int B, int V, int gamma);
 int dspark_verify_tv(int B, int V, int gamma,
