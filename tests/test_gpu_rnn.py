@@ -133,3 +133,48 @@ def test_rnn_sentinels_and_rejects(gpu):
     e = _inputs(f)
     with pytest.raises(TypeError):
         dspark.rnn_draft(dev(e["U"]), dev(e["W1"]), dev(e["W2"]), dev(e["A"]), dev(e["x0"]), dev(e["u"]))
+
+
+def test_rnn_joint_law_chi_squared(gpu):
+    """2^18 requests from one context, two positions (the batched kernels): the pairs
+    (x_1, x_2) follow p_1(x_1) p_2(x_2 | x_1), where p_2's bias comes from the state
+    h_2 = A W1[x_0] + W1[x_1]; chi-squared over the 256 cells, small cells pooled. The law is
+    the oracle's, with x_1 forced to each value in turn."""
+    import scipy.stats
+    N, V, r, G = 1 << 18, 16, 8, 2
+    g = np.random.default_rng(45)
+    U2 = (0.7 * g.standard_normal((G, V))).astype(np.float32)
+    W1 = synth.f32_to_bf16_bits((0.8 * g.standard_normal((V, r))).astype(np.float32))
+    W2 = synth.f32_to_bf16_bits((0.8 * g.standard_normal((r, V))).astype(np.float32))
+    A = synth.f32_to_bf16_bits((0.5 * g.standard_normal((r, r))).astype(np.float32))
+    x0 = 5
+    P = np.zeros((V, V))
+    for x1 in range(V):
+        ref = oracle.rnn_draft(U2[None], W1, W2, A, np.array([x0]), np.full((1, G), 0.5, np.float32),
+                               "bf16", want_logits=True, forced=np.array([[x1, 0]]))
+        P[x1] = oracle.softmax_row(ref["L"][0, 0])[0][x1] * oracle.softmax_row(ref["L"][0, 1])[0]
+    assert abs(P.sum() - 1.0) < 1e-12
+    U = torch.from_numpy(U2).cuda().expand(N, G, V).contiguous()
+    u = torch.from_numpy(synth.uniforms(synth.rng(935, 0), (N, G))).cuda()
+    assert dspark.rnn_draft_path(N, dev(W1), dev(W2), dev(A)) == "mfma"
+    out = dspark.rnn_draft(U, dev(W1), dev(W2), dev(A), torch.full((N,), x0, dtype=torch.int32,
+                                                                  device="cuda"), u,
+                           want_q=False, want_lse=False)
+    x = host(out["x"]).astype(np.int64)
+    assert x.min() >= 0 and x.max() < V
+    counts = np.bincount(x[:, 0] * V + x[:, 1], minlength=V * V).astype(float)
+    expected = N * P.ravel()
+    keep = expected >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    exp = np.append(expected[keep], expected[~keep].sum())
+    assert scipy.stats.chisquare(obs, exp).pvalue > 1e-3
+    # the Markov head's law differs: without A h_1 the same counts are far from it
+    Pm = np.zeros((V, V))
+    for x1 in range(V):
+        ref = oracle.markov_draft(U2[None], W1, W2, np.array([x0]), np.full((1, G), 0.5, np.float32),
+                                  "bf16", want_logits=True, forced=np.array([[x1, 0]]))
+        Pm[x1] = oracle.softmax_row(ref["L"][0, 0])[0][x1] * oracle.softmax_row(ref["L"][0, 1])[0]
+    em = N * Pm.ravel()
+    km = em >= 5
+    assert scipy.stats.chisquare(np.append(counts[km], counts[~km].sum()),
+                                 np.append(em[km], em[~km].sum())).pvalue < 1e-6
