@@ -662,9 +662,19 @@ def run_workload(args, workload, torch, dspark, device, steps, cpu_seconds, mp):
 
     parts = dict(verify_tv=verify) if verify_only else dict(draft=draft, schedule=schedule,
                                                            verify_tv=verify)
+    # the schedule does not read this step's draft: where the draft takes the single-request
+    # launch and the schedule fits one wave, the step runs both in that launch
+    fused = (not verify_only and not args.per_position and
+             dspark.markov_draft_schedule_fused(B, t["W1"], t["W2"], B, G))
+
+    def draft_schedule():
+        dspark.markov_draft_schedule(t["U"], t["W1"], t["W2"], t["x0"], t["u"], t["sps"], Bmax,
+                                     conf=t["conf"], temp=t["temp"], out=out_d, out_sched=out_s)
+
+    step_fns = [draft_schedule, verify] if fused else list(parts.values())
 
     def step():
-        for fn in parts.values():
+        for fn in step_fns:
             fn()
 
     for _ in range(max(1, args.warmup)):
@@ -807,7 +817,9 @@ def run_workload(args, workload, torch, dspark, device, steps, cpu_seconds, mp):
                     draft_logits=("input" if verify_only else
                                   "rebuilt by verify from the factors" if rebuild else
                                   "written by the draft"),
-                    draft_launches="per position" if args.per_position else "default"),
+                    draft_launches="per position" if args.per_position else "default",
+                    schedule=("none" if verify_only else
+                              "in the draft's launch" if fused else "its own launch")),
         drafted_per_step=drafted, verified_per_step=verified,
         breakdown_us={k: v * 1e3 for k, v in ms_parts.items()},
         ms_per_step_p10_p90=[float(np.percentile(ms, 10)), float(np.percentile(ms, 90))],

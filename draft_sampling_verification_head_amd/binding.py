@@ -34,6 +34,8 @@ EXPORTS = (
     "dspark_verify_markov_workspace_bytes", "dspark_verify_markov",
     "dspark_tv_labels_workspace_bytes", "dspark_tv_labels",
     "dspark_schedule_workspace_bytes", "dspark_schedule",
+    "dspark_markov_draft_schedule_workspace_bytes", "dspark_markov_draft_schedule_fused",
+    "dspark_markov_draft_schedule",
     "dspark_conf_ring_bytes", "dspark_conf_ring_init", "dspark_conf_ring_push", "dspark_schedule_lagged",
     "dspark_sts_fit_workspace_bytes", "dspark_sts_fit",
 )
@@ -68,6 +70,11 @@ _SIGS = {
     "dspark_tv_labels": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "dspark_schedule_workspace_bytes": (_Z, [_I, _I, _I]),
     "dspark_schedule": (_I, [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "dspark_markov_draft_schedule_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "dspark_markov_draft_schedule_fused": (_I, [_I, _I, _I, _I, _I, _P, _P, _I]),
+    "dspark_markov_draft_schedule": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+                                          _I, _P, _P, _Z, _P, _P, _I, _I, _P, _P, _P, _P, _P,
+                                          _P, _Z, _P]),
     "dspark_conf_ring_bytes": (_Z, [_I, _I]),
     "dspark_conf_ring_init": (_I, [_I, _I, _P, _Z, _P]),
     "dspark_conf_ring_push": (_I, [_I, _I, _P, _Z, _P, _P]),
@@ -447,7 +454,8 @@ def _schedule_outputs(R, G, dev, out, want_a):
     t_off = o.get("t_off") if o.get("t_off") is not None else torch.empty((R + 1,), dtype=torch.int32, device=dev)
     K = o.get("K") if o.get("K") is not None else torch.empty((1,), dtype=torch.int32, device=dev)
     theta = o.get("theta") if o.get("theta") is not None else torch.empty((1,), dtype=torch.float32, device=dev)
-    a = torch.empty((R, G), dtype=torch.float32, device=dev) if want_a else None
+    a = o.get("a") if o.get("a") is not None else (torch.empty((R, G), dtype=torch.float32, device=dev)
+                                                   if want_a else None)
     return dict(len=length, t_off=t_off, K=K, theta=theta, a=a)
 
 
@@ -470,6 +478,64 @@ def schedule(conf, sps, Bmax, *, temp=None, mode=GLOBAL, want_a=False, out=None,
                              _ptr(o["a"]), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "dspark_schedule")
     return o
+
+
+def markov_draft_schedule_fused(B: int, W1, W2, R: int, gamma: int) -> bool:
+    """dspark_markov_draft_schedule_fused: whether markov_draft_schedule runs the schedule in
+    the draft's launch."""
+    torch = _torch()
+    V, r = W1.shape
+    wdt = {torch.float32: F32, torch.bfloat16: BF16}[W1.dtype]
+    return bool(load().dspark_markov_draft_schedule_fused(B, V, r, gamma, wdt, _ptr(W1), _ptr(W2), R))
+
+
+def markov_draft_schedule(U, W1, W2, x0, u, sps, Bmax, *, conf=None, ring=None, temp=None,
+                          mode=GLOBAL, want_q=True, want_lse=True, want_logits=False,
+                          want_a=False, out=None, out_sched=None, stream=None, ws=None):
+    """dspark_markov_draft_schedule: the draft of markov_draft and the schedule of schedule
+    (conf [R][gamma]) or schedule_lagged (ring, a ConfRing) in one call. Returns (draft dict,
+    schedule dict) as those two calls return them."""
+    torch = _torch()
+    lib = load()
+    B, G, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    wdt = {torch.float32: F32, torch.bfloat16: BF16}.get(W1.dtype)
+    if wdt is None:
+        raise TypeError("W1/W2 must be float32 or bfloat16")
+    _need(U, "U", torch.float32, (B, G, V), dev)
+    _need(W1, "W1", W1.dtype, (V, r), dev)
+    _need(W2, "W2", W1.dtype, (r, V), dev)
+    _need(x0, "x0", torch.int32, (B,), dev)
+    _need(u, "u", torch.float32, (B, G), dev)
+    if (conf is None) == (ring is None):
+        raise ValueError("give exactly one of conf and ring")
+    if ring is not None:
+        R = ring.R
+        if ring.gamma != G:
+            raise ValueError("the ring's gamma differs from the draft's")
+    else:
+        R = conf.shape[0]
+        _need(conf, "conf", torch.float32, (R, G), dev)
+    _need(sps, "sps", torch.float32, (Bmax + 1,), dev)
+    if temp is not None:
+        _need(temp, "temp", torch.float32, (G,), dev)
+    o = out or {}
+    x = o.get("x") if o.get("x") is not None else torch.empty((B, G), dtype=torch.int32, device=dev)
+    q = o.get("q") if o.get("q") is not None else (torch.empty((B, G), dtype=torch.float32, device=dev) if want_q else None)
+    lse = o.get("lse") if o.get("lse") is not None else (torch.empty((B, G), dtype=torch.float32, device=dev) if want_lse else None)
+    L = o.get("L") if o.get("L") is not None else (torch.empty((B, G, V), dtype=torch.float32, device=dev) if want_logits else None)
+    so = _schedule_outputs(R, G, dev, out_sched, want_a)
+    nbytes = lib.dspark_markov_draft_schedule_workspace_bytes(B, V, r, G, R, int(Bmax))
+    ws = workspace(nbytes, dev, "draft_schedule", stream, ws)
+    st = lib.dspark_markov_draft_schedule(
+        B, V, r, G, _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(x0), _ptr(u), _ptr(x), _ptr(q),
+        _ptr(lse), _ptr(L), R, _ptr(conf), _ptr(ring.buf if ring is not None else None),
+        ring.nbytes if ring is not None else 0, _ptr(temp), _ptr(sps), int(Bmax), int(mode),
+        _ptr(so["len"]), _ptr(so["t_off"]), _ptr(so["K"]), _ptr(so["theta"]), _ptr(so["a"]),
+        _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "dspark_markov_draft_schedule")
+    return dict(x=x, q=q, lse=lse, L=L), so
 
 
 class ConfRing:

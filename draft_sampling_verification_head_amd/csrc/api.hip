@@ -11,6 +11,7 @@
 
 #include "../../include/dspark.h"
 #include "kernels.h"
+#include "schedule_small.h"
 
 namespace {
 
@@ -176,27 +177,34 @@ int dspark_markov_draft_plan(int B, int V, int r, int gamma, int w_dtype, const 
     return ok();
 }
 
-int dspark_markov_draft_ex(int B, int V, int r, int gamma, const float* U, const void* W1,
-                           const void* W2, int w_dtype, const int32_t* x0, const float* u,
-                           int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, void* ws,
-                           size_t ws_bytes, void* stream, int options) {
+}  // extern "C"
+
+namespace {
+
+// The draft of dspark_markov_draft_ex; with a one-wave schedule job that the single-request
+// launch can take, that launch also runs the job (*job_taken set), else the job is left to
+// the caller.
+int draft_run(const char* who, int B, int V, int r, int gamma, const float* U, const void* W1,
+              const void* W2, int w_dtype, const int32_t* x0, const float* u, int32_t* x_out,
+              float* q_out, float* lse_out, float* Ld_out, void* ws, size_t ws_bytes, void* stream,
+              int options, const dspark::sched::SmallJob* job, bool* job_taken) {
     if (options & ~(DSPARK_DRAFT_PER_POSITION | DSPARK_DRAFT_TEST_SPIN))
-        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: unknown option bits 0x%x", options);
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: unknown option bits 0x%x", who, options);
     if (B < 1 || V < 1 || gamma < 1 || r < 1)
-        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: B=%d V=%d r=%d gamma=%d must be >= 1",
-                    B, V, r, gamma);
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: B=%d V=%d r=%d gamma=%d must be >= 1",
+                    who, B, V, r, gamma);
     if (!draft_sizes_ok(B, V, r, gamma))
-        return fail(DSPARK_ERR_UNSUPPORTED, "markov_draft: gamma=%d r=%d B*gamma*V outside caps",
-                    gamma, r);
+        return fail(DSPARK_ERR_UNSUPPORTED, "%s: gamma=%d r=%d B*gamma*V outside caps",
+                    who, gamma, r);
     if (w_dtype != DSPARK_F32 && w_dtype != DSPARK_BF16)
-        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: unknown w_dtype %d", w_dtype);
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: unknown w_dtype %d", who, w_dtype);
     if (!U || !W1 || !W2 || !x0 || !u || !x_out)
-        return fail(DSPARK_ERR_INVALID_ARG, "markov_draft: a required pointer is NULL");
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: a required pointer is NULL", who);
     dspark::DraftCall dc = draft_call(B, V, r, gamma, U, W1, W2, w_dtype, Ld_out, options);
     const int path = dspark::draft_path_of(dc, nullptr);
     const DraftNeed need = draft_need(B, V, gamma, path, Ld_out != nullptr);
     if (!ws || ws_bytes < need.total())
-        return fail(DSPARK_ERR_WORKSPACE, "markov_draft: workspace %zu bytes, need %zu", ws_bytes,
+        return fail(DSPARK_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes,
                     need.total());
     Carver c(ws);
     dc.status = c.take<unsigned>(kDraftHeader / sizeof(unsigned));
@@ -218,9 +226,26 @@ int dspark_markov_draft_ex(int B, int V, int r, int gamma, const float* U, const
         dc.L[k] = Ld_out ? Ld_out + static_cast<long long>(k) * V : lbuf[k & 1];
     dc.L_bstride = Ld_out ? static_cast<long long>(gamma) * V : V;
     if (options & DSPARK_DRAFT_TEST_SPIN) dc.spin = 0;
+    if (job && path == DSPARK_PATH_RESIDENT && dspark::draft_resident_takes_job(V)) {
+        dc.job = job;
+        *job_taken = true;
+    }
     const hipError_t e = dspark::launch_draft(dc, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "markov_draft");
+    if (e != hipSuccess) return hip_fail(e, who);
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_markov_draft_ex(int B, int V, int r, int gamma, const float* U, const void* W1,
+                           const void* W2, int w_dtype, const int32_t* x0, const float* u,
+                           int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, void* ws,
+                           size_t ws_bytes, void* stream, int options) {
+    bool taken = false;
+    return draft_run("markov_draft", B, V, r, gamma, U, W1, W2, w_dtype, x0, u, x_out, q_out,
+                     lse_out, Ld_out, ws, ws_bytes, stream, options, nullptr, &taken);
 }
 
 }  // extern "C"
@@ -571,10 +596,8 @@ namespace {
 
 // Shared checks and launch of dspark_schedule / dspark_schedule_lagged (ring_n: the ring's
 // counter, conf then the base of its slots).
-int schedule_call(const char* who, int R, int gamma, const float* conf, const long long* ring_n,
-                  const float* temp, const float* sps, int Bmax, int mode, int32_t* len_out,
-                  int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out, void* ws,
-                  size_t ws_bytes, void* stream) {
+int schedule_check(const char* who, int R, int gamma, const float* conf, const float* sps,
+                   int Bmax, int mode, const int32_t* len_out) {
     if (R < 1 || gamma < 1)
         return fail(DSPARK_ERR_INVALID_ARG, "%s: R=%d gamma=%d must be >= 1", who, R, gamma);
     if (gamma > 64 || static_cast<long long>(R) * gamma > dspark::schedule_max_candidates())
@@ -587,6 +610,15 @@ int schedule_call(const char* who, int R, int gamma, const float* conf, const lo
         return fail(DSPARK_ERR_INVALID_ARG, "%s: unknown mode %d", who, mode);
     if (!conf || !sps || !len_out)
         return fail(DSPARK_ERR_INVALID_ARG, "%s: conf / sps / len_out is NULL", who);
+    return DSPARK_OK;
+}
+
+int schedule_call(const char* who, int R, int gamma, const float* conf, const long long* ring_n,
+                  const float* temp, const float* sps, int Bmax, int mode, int32_t* len_out,
+                  int32_t* t_off_out, int32_t* K_out, float* theta_out, float* a_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+    const int st = schedule_check(who, R, gamma, conf, sps, Bmax, mode, len_out);
+    if (st != DSPARK_OK) return st;
     const size_t need = dspark_schedule_workspace_bytes(R, gamma, Bmax);
     if (!ws || ws_bytes < need)
         return fail(DSPARK_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
@@ -666,6 +698,58 @@ int dspark_schedule_lagged(int R, int gamma, const void* ring, size_t ring_bytes
     return schedule_call("schedule_lagged", R, gamma, ring_slots(ring), ring_counter(ring), temp, sps,
                          Bmax, mode, len_out, t_off_out, K_out, theta_out, a_out, ws, ws_bytes,
                          stream);
+}
+
+// ----------------------------------------------------------------------------- draft + schedule
+size_t dspark_markov_draft_schedule_workspace_bytes(int B, int V, int r, int gamma, int R, int Bmax) {
+    const size_t d = dspark_markov_draft_workspace_bytes(B, V, r, gamma);
+    const size_t s = dspark_schedule_workspace_bytes(R, gamma, Bmax);
+    if (!d || !s) return 0;
+    return align_up(d) + s;
+}
+
+int dspark_markov_draft_schedule_fused(int B, int V, int r, int gamma, int w_dtype, const void* W1,
+                                       const void* W2, int R) {
+    if (R < 1 || gamma < 1 || static_cast<long long>(R) * gamma > dspark::sched::kSmallCand) return 0;
+    return dspark_markov_draft_path(B, V, r, w_dtype, W1, W2) == DSPARK_PATH_RESIDENT &&
+                   dspark::draft_resident_takes_job(V)
+               ? 1
+               : 0;
+}
+
+int dspark_markov_draft_schedule(int B, int V, int r, int gamma, const float* U, const void* W1,
+                                 const void* W2, int w_dtype, const int32_t* x0, const float* u,
+                                 int32_t* x_out, float* q_out, float* lse_out, float* Ld_out, int R,
+                                 const float* conf, const void* ring, size_t ring_bytes,
+                                 const float* temp, const float* sps, int Bmax, int mode,
+                                 int32_t* len_out, int32_t* t_off_out, int32_t* K_out,
+                                 float* theta_out, float* a_out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    const char* who = "markov_draft_schedule";
+    const float* cf = conf;
+    const long long* ring_n = nullptr;
+    if (ring) {
+        const int st = check_ring(who, R, gamma, ring, ring_bytes);
+        if (st != DSPARK_OK) return st;
+        cf = ring_slots(ring);
+        ring_n = ring_counter(ring);
+    }
+    int st = schedule_check(who, R, gamma, cf, sps, Bmax, mode, len_out);
+    if (st != DSPARK_OK) return st;
+    const size_t need = dspark_markov_draft_schedule_workspace_bytes(B, V, r, gamma, R, Bmax);
+    if (!need) return fail(DSPARK_ERR_INVALID_ARG, "%s: B=%d V=%d gamma=%d must be >= 1", who, B, V, gamma);
+    if (!ws || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+    const size_t dbytes = align_up(dspark_markov_draft_workspace_bytes(B, V, r, gamma));
+    const dspark::sched::SmallJob job{R, gamma, cf, ring_n, temp, sps, Bmax, mode,
+                                      len_out, t_off_out, K_out, theta_out, a_out};
+    const bool small = static_cast<long long>(R) * gamma <= dspark::sched::kSmallCand;
+    bool taken = false;
+    st = draft_run(who, B, V, r, gamma, U, W1, W2, w_dtype, x0, u, x_out, q_out, lse_out, Ld_out, ws,
+                   dbytes, stream, 0, small ? &job : nullptr, &taken);
+    if (st != DSPARK_OK || taken) return st;
+    return schedule_call(who, R, gamma, cf, ring_n, temp, sps, Bmax, mode, len_out, t_off_out, K_out,
+                         theta_out, a_out, static_cast<char*>(ws) + dbytes, ws_bytes - dbytes, stream);
 }
 
 // ----------------------------------------------------------------------------- STS fit

@@ -43,6 +43,7 @@
 #include "common.h"
 #include "draw.h"
 #include "kernels.h"
+#include "schedule_small.h"
 
 namespace dspark {
 
@@ -92,6 +93,8 @@ struct ResArgs {
     unsigned spin;            // polls before a wait gives up
     const uint16_t* A;        // RNN head: [r][r] bf16 recurrence
     float* h_out;             // RNN head: [gamma][r] fp32 state of each position (nullable)
+    sched::SmallJob job;      // with_job: the schedule run by workgroup G, beside the draft
+    int with_job;
 };
 
 // Ready word of a call with counter e: the finaliser of the splitmix64 generator (Steele, Lea
@@ -150,6 +153,14 @@ void draft_resident(ResArgs a) {
     __shared__ int stok;
     __shared__ int gave_up;
     __shared__ unsigned long long s_e0;                    // the call counter read at the start
+    if (a.with_job && blockIdx.x == static_cast<unsigned>(a.G)) {
+        // the extra workgroup: the schedule, by its first wave, on LDS the draft leaves alone
+        // (this workgroup drafts nothing and takes no part in the position slots)
+        if (threadIdx.x < kWave)
+            sched::schedule_small<false>(a.job, reinterpret_cast<double*>(lds),
+                                         reinterpret_cast<double*>(lds) + sched::kSmallCand);
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int V = a.V, r = a.r;
     if (tid == 0) s_e0 = load_token(a.epoch);             // seen by every thread after a barrier
@@ -526,7 +537,9 @@ hipError_t launch(const DraftCall& c, const void* A, float* h_out, hipStream_t s
     a.spin = c.spin;
     a.A = static_cast<const uint16_t*>(A);
     a.h_out = h_out;
-    hipLaunchKernelGGL(draft_resident<RNN>, dim3(a.G), dim3(kRThreads), 0, st, a);
+    a.with_job = (!RNN && c.job) ? 1 : 0;
+    if (a.with_job) a.job = *c.job;
+    hipLaunchKernelGGL(draft_resident<RNN>, dim3(a.G + a.with_job), dim3(kRThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -540,6 +553,12 @@ size_t draft_resident_slot_bytes(int V, int gamma) {
 
 bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {
     return B == 1 && w_dtype == 1 && fits<false>(V, r, W1, W2);
+}
+
+bool draft_resident_takes_job(int V) {
+    const DeviceFit f = device_fit<false>();
+    return f.cus > 0 && f.occupancy >= 1 &&
+           static_cast<long long>(tiles_of(V)) + 1 <= static_cast<long long>(f.cus) * f.occupancy;
 }
 
 hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st) {

@@ -8,6 +8,8 @@
 namespace dspark {
 
 // ---------------------------------------------------------------- draft
+namespace sched { struct SmallJob; }
+
 struct DraftCall {
     int B, V, r, gamma, w_dtype;
     const float* U;
@@ -26,6 +28,9 @@ struct DraftCall {
     float2* slots;            // max(draft_resident_slot_bytes, draft_slab_flag_bytes) of workspace
     unsigned* status;         // one-launch forms: number of workgroups that gave up waiting
     unsigned spin = 1u << 20; // polls before a one-launch form gives up (about a second)
+    // a one-wave schedule the single-request launch runs in one extra workgroup (the caller
+    // checks draft_resident_takes_job first); null: none
+    const sched::SmallJob* job = nullptr;
 };
 
 // Which path (DSPARK_PATH_*) launch_draft takes for this call, and whether it runs every
@@ -54,6 +59,9 @@ hipError_t launch_draft_slab(const DraftCall& c, hipStream_t st);
 bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2);
 int draft_resident_tile_cols();
 size_t draft_resident_slot_bytes(int V, int gamma);
+// Whether the single-request launch at this V can add one workgroup for a schedule job (every
+// workgroup of the launch resident at once, the draft's included).
+bool draft_resident_takes_job(int V);
 hipError_t launch_draft_resident(const DraftCall& c, hipStream_t st);
 
 // RNN-head draft (the recurrence h_1 = W1[x_0], h_k = A h_{k-1} + W1[x_{k-1}], B_k = h_k W2):

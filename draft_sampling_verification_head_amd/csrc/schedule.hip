@@ -25,144 +25,20 @@
 // The slot is resolved on the device, so a captured round needs no host round trip.
 #include "common.h"
 #include "kernels.h"
+#include "schedule_small.h"
 
 namespace dspark {
 
 namespace {
 
+using namespace sched;
+
 constexpr int kMaxCand = 16384;            // 128 KB of keys in LDS
-constexpr unsigned long long kMask44 = (1ull << 44) - 1ull;
-
-// The confidences a schedule reads: `conf`, or with a ring counter the lagged ring slot.
-__device__ __forceinline__ const float* lagged(const float* conf, const long long* ring_n, int R, int G) {
-    if (!ring_n) return conf;
-    const long long n = *ring_n;
-    return conf + ((n + 1) % 3) * static_cast<long long>(R) * G;   // (n - 2) mod 3 for n >= 0
-}
-
-__device__ __forceinline__ double scaled_conf(float c, const float* temp, int j) {
-    const double cd = static_cast<double>(c);
-    if (!(cd > 0.0)) return 0.0;          // also NaN
-    if (cd >= 1.0) return 1.0;
-    if (!temp) return cd;
-    double T = static_cast<double>(temp[j]);
-    if (!(T > 0.0)) T = 1.0;
-    return 1.0 / (1.0 + pow((1.0 - cd) / cd, 1.0 / T));
-}
-
-__device__ __forceinline__ unsigned long long make_key(double a, int j, int r) {
-    const unsigned long long q = static_cast<unsigned long long>(__double_as_longlong(a)) >> 20;
-    return (((~q) & kMask44) << 20) | (static_cast<unsigned long long>(j) << 14) |
-           static_cast<unsigned long long>(r);
-}
-
-__device__ __forceinline__ double key_value(unsigned long long key) {
-    const unsigned long long q = (~(key >> 20)) & kMask44;
-    return __longlong_as_double(static_cast<long long>(q << 20));
-}
-
-struct Best {
-    double theta;
-    int n;
-};
-
-__device__ __forceinline__ Best better(Best a, Best b) {
-    // larger Theta wins; equal Theta -> smaller n. NaN Theta never wins.
-    if (b.theta > a.theta || (b.theta == a.theta && b.n < a.n) || (a.theta != a.theta)) return b;
-    return a;
-}
-
-// One wave for up to 64 candidates (a few short requests): every candidate sits in a lane,
-// ranks come from comparing against all keys (read out with v_readlane), and everything
-// else is a wave-level scan or reduction. The SPS entries the search reads do not depend on
-// the data, so they are loaded together with the confidences.
-constexpr int kSmallCand = kWave;
-
 __global__ __launch_bounds__(kWave)
-void schedule_small_kernel(int R, int G, const float* __restrict__ conf_in,
-                           const long long* __restrict__ ring_n,
-                           const float* __restrict__ temp, const float* __restrict__ sps,
-                           int Bmax, int mode, int32_t* __restrict__ len_out,
-                           int32_t* __restrict__ t_off_out, int32_t* __restrict__ K_out,
-                           float* __restrict__ theta_out, float* __restrict__ a_out) {
-    const float* conf = lagged(conf_in, ring_n, R, G);
+void schedule_small_kernel(SmallJob job) {
     __shared__ double cs[kSmallCand];
     __shared__ double sorted[kSmallCand];
-    const int lane = threadIdx.x;
-    const int N = R * G;
-    const int nmax = min(N, Bmax - R);
-    // loads: the candidate's confidence and SPS(R + lane + 1), SPS(R) for n = 0
-    const float c = (lane < N) ? conf[lane] : 0.0f;
-    const double sps_next = (lane < nmax) ? static_cast<double>(sps[R + lane + 1]) : 0.0;
-    const double sps0 = static_cast<double>(sps[R]);
-    cs[lane] = (lane < N) ? scaled_conf(c, temp, lane % G) : 0.0;
-    __syncthreads();
-    // prefix products in position order, one lane per request (same order as the oracle)
-    if (lane < R) {
-        double a = 1.0;
-        for (int j = 0; j < G; ++j) {
-            a *= cs[lane * G + j];
-            cs[lane * G + j] = a;
-        }
-    }
-    __syncthreads();
-    const double a = (lane < N) ? cs[lane] : 0.0;
-    if (a_out && lane < N) a_out[lane] = static_cast<float>(a);
-    const int r = lane / G, j = lane - r * G;
-    const unsigned long long key = (lane < N) ? make_key(a, j, r) : ~0ull;
-    // rank = number of smaller keys (keys are distinct: they carry j and r)
-    int rank = 0;
-    for (int i = 0; i < N; ++i) {
-        const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(key), i);
-        const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(key >> 32), i);
-        rank += ((static_cast<unsigned long long>(hi) << 32 | lo) < key) ? 1 : 0;
-    }
-    if (lane < N) sorted[rank] = key_value(key);
-    __syncthreads();
-    // S(n) for n = lane + 1: inclusive sum of the ranked values (lane-order fp64 scan)
-    double S = (lane < N) ? sorted[lane] : 0.0;
-    S = wave_incl_scan(S);
-    // Theta(0) and Theta(lane + 1); GLOBAL = smallest argmax, EARLY_STOP = first drop
-    const double th0 = static_cast<double>(R) * sps0;
-    const bool valid = lane < nmax;
-    const double th = valid ? (static_cast<double>(R) + S) * sps_next : -INFINITY;
-    double th_prev = __shfl_up(th, 1, kWave);
-    if (lane == 0) th_prev = th0;
-    const unsigned long long drop = __ballot(valid && th <= th_prev);
-    Best best{th0, 0};
-    Best mine{th, lane + 1};
-    if (valid) best = better(best, mine);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        Best other{__shfl_xor(best.theta, o, kWave), __shfl_xor(best.n, o, kWave)};
-        best = better(best, other);
-    }
-    int nstar;
-    if (mode == 1)
-        nstar = drop ? (__ffsll(static_cast<long long>(drop)) - 1) : nmax;
-    else
-        nstar = best.n;
-    const double S_star = (nstar == 0) ? 0.0 : __shfl(S, nstar - 1, kWave);
-    const double sps_star = (nstar == 0) ? sps0 : __shfl(sps_next, nstar - 1, kWave);
-    // lengths: candidates ranked before n*, counted per request
-    const bool kept = lane < N && rank < nstar;
-    const unsigned long long keptm = __ballot(kept);
-    int len = 0;
-    if (lane < R) {
-        const unsigned long long blockm = ((G == 64) ? ~0ull : ((1ull << G) - 1ull)) << (lane * G);
-        len = __popcll(keptm & blockm);
-        len_out[lane] = len;
-    }
-    if (t_off_out) {
-        const int v = (lane < R) ? len + 1 : 0;
-        const int incl = wave_incl_scan(v);
-        if (lane < R) t_off_out[lane] = incl - v;
-        if (lane == R - 1) t_off_out[R] = incl;
-    }
-    if (lane == 0) {
-        if (K_out) *K_out = R + nstar;
-        if (theta_out) *theta_out = static_cast<float>((static_cast<double>(R) + S_star) * sps_star);
-    }
+    schedule_small<true>(job, cs, sorted);
 }
 
 // ---------------------------------------------------------------- many candidates
@@ -429,8 +305,9 @@ hipError_t launch_schedule(int R, int gamma, const float* conf, const long long*
                            int32_t* len_out, int32_t* t_off_out, int32_t* K_out, float* theta_out,
                            float* a_out, double* a_ws, hipStream_t st) {
     if (R * gamma <= kSmallCand) {
-        hipLaunchKernelGGL(schedule_small_kernel, dim3(1), dim3(kWave), 0, st, R, gamma, conf, ring_n,
-                           temp, sps, Bmax, mode, len_out, t_off_out, K_out, theta_out, a_out);
+        const SmallJob job{R, gamma, conf, ring_n, temp, sps, Bmax, mode, len_out, t_off_out, K_out,
+                           theta_out, a_out};
+        hipLaunchKernelGGL(schedule_small_kernel, dim3(1), dim3(kWave), 0, st, job);
         return hipGetLastError();
     }
     const int N = R * gamma;

@@ -366,6 +366,32 @@ int dspark_schedule(int R, int gamma, const float* conf, const float* temp,
                     float* a_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The draft and the schedule in one call, for callers whose schedule does not depend on this
+ * draft (the two-step-lag schedule of [P1] section "硬件感知与置信度自适应调度机制", which
+ * takes the scheduler off the step's critical path): the results of dspark_markov_draft
+ * followed by dspark_schedule (ring NULL) or dspark_schedule_lagged (ring given; conf is then
+ * ignored), bit for bit. gamma is the block length of both; R the schedule's request count.
+ * When the draft takes the single-request one-launch form (DSPARK_PATH_RESIDENT) and
+ * R * gamma <= 64, the schedule runs in one extra workgroup of the draft's launch, on a
+ * compute unit the draft leaves idle (dspark_markov_draft_schedule_fused tells whether a call
+ * does); otherwise the schedule is launched after the draft. Argument rules and errors are
+ * those of the two calls. Workspace: dspark_markov_draft_schedule_workspace_bytes (the draft's
+ * worst-case workspace, then the schedule's).
+ */
+size_t dspark_markov_draft_schedule_workspace_bytes(int B, int V, int r, int gamma, int R, int Bmax);
+int dspark_markov_draft_schedule_fused(int B, int V, int r, int gamma, int w_dtype, const void* W1,
+                                       const void* W2, int R);
+int dspark_markov_draft_schedule(int B, int V, int r, int gamma,
+                                 const float* U, const void* W1, const void* W2, int w_dtype,
+                                 const int32_t* x0, const float* u,
+                                 int32_t* x_out, float* q_out, float* lse_out, float* Ld_out,
+                                 int R, const float* conf, const void* ring, size_t ring_bytes,
+                                 const float* temp, const float* sps, int Bmax, int mode,
+                                 int32_t* len_out, int32_t* t_off_out, int32_t* K_out,
+                                 float* theta_out, float* a_out,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Two-step-lag schedule.
  * [P1] section "硬件感知与置信度自适应调度机制" (the asynchronous adaptation): the verify
  * lengths of step t are decided from the confidences predicted at step t - 2, which cannot

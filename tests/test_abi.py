@@ -331,3 +331,54 @@ def test_draft_accepts_the_planned_workspace(lib):
     args = (B, V, r, G, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, None, FAKE)
     assert f(*args, nb - 1, None, 0) == binding.ERR_WORKSPACE
     assert f(*args, nb, None, 0) != binding.ERR_WORKSPACE
+
+
+def _draft_schedule_fn(lib):
+    f = lib.dspark_markov_draft_schedule
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    f.argtypes = ([I] * 4 + [P] * 3 + [I] + [P] * 6 + [I, P, P, Z, P, P, I, I] + [P] * 5 + [P, Z, P])
+    return f
+
+
+def test_draft_schedule_workspace_and_fusion_rules(lib):
+    """The fused call's workspace is the draft's worst case, aligned, then the schedule's; the
+    schedule rides in the draft's launch only for the single-request path and <= 64
+    candidates (and never where no device answers the residency query)."""
+    B, V, r, G, R, Bmax = 1, 151936, 256, 7, 1, 4096
+    d = lib.dspark_markov_draft_workspace_bytes(B, V, r, G)
+    s = lib.dspark_schedule_workspace_bytes(R, G, Bmax)
+    got = lib.dspark_markov_draft_schedule_workspace_bytes(B, V, r, G, R, Bmax)
+    assert got == -(-d // 256) * 256 + s
+    assert lib.dspark_markov_draft_schedule_workspace_bytes(0, V, r, G, R, Bmax) == 0
+    assert lib.dspark_markov_draft_schedule_workspace_bytes(B, V, r, G, 0, Bmax) == 0
+    f = lib.dspark_markov_draft_schedule_fused
+    f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p] * 2 + [ctypes.c_int]
+    assert f(64, V, r, 16, 1, FAKE, FAKE, 64) == 0        # slab path
+    assert f(1, V, r, 16, 1, FAKE, FAKE, 5) == 0          # 80 candidates
+    assert f(1, V, r, 16, 1, FAKE, FAKE, 0) == 0
+    if _no_gpu():
+        assert f(1, V, r, 7, 1, FAKE, FAKE, 1) == 0       # no device: no residency answer
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(conf=None), binding.ERR_INVALID_ARG),            # neither conf nor ring
+    (dict(R=0), binding.ERR_INVALID_ARG),
+    (dict(mode=7), binding.ERR_INVALID_ARG),
+    (dict(Bmax=0), binding.ERR_INVALID_ARG),               # Bmax < R
+    (dict(len_out=None), binding.ERR_INVALID_ARG),
+    (dict(ring=ctypes.c_void_p(0x1004), ring_bytes=1 << 20), binding.ERR_INVALID_ARG),   # misaligned
+    (dict(ring=FAKE, ring_bytes=8), binding.ERR_WORKSPACE),    # ring too small
+    (dict(ws=None), binding.ERR_WORKSPACE),
+    (dict(wsb=100), binding.ERR_WORKSPACE),
+])
+def test_draft_schedule_rejects(lib, kw, status):
+    a = dict(B=1, V=64, r=8, G=3, R=1, conf=FAKE, ring=None, ring_bytes=0, Bmax=64, mode=0,
+             len_out=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    f = _draft_schedule_fn(lib)
+    st = f(a["B"], a["V"], a["r"], a["G"], FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, None,
+           a["R"], a["conf"], a["ring"], a["ring_bytes"], None, FAKE, a["Bmax"], a["mode"],
+           a["len_out"], None, None, None, None, a["ws"], a["wsb"], None)
+    assert st == status
+    assert lib.dspark_last_error()
