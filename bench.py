@@ -45,9 +45,9 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
     ("single", "draft_resident"): dict(
-        bytes=86944749.3,
+        bytes=86970802.0,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
-        sources={"draft_resident.hip": "1205812310a76addccb39045c3db6b8512183917bf4df61dec9c0498bcaf3033",
+        sources={"draft_resident.hip": "500b1242842057d21c694c44ac4e4209d0ec2877d60bbbf6267bdf417e640ae1",
                  "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the per-position sweep of one request (bench.py --per-position)
