@@ -1013,17 +1013,26 @@ struct SmallArgs {
     unsigned spin;
 };
 
-// Polls until every lane's word is tagged (lanes with p == nullptr are ready); false after
-// the spin bound. The whole wave calls it.
-__device__ __forceinline__ bool poll_tagged(const unsigned long long* p, unsigned long long& v,
-                                            unsigned tag, unsigned spin) {
-    bool done = p == nullptr;
+// Polls until each of every lane's N words carries the tag (a null pointer counts as ready);
+// false after the spin bound. Every round loads the lane's untagged words together, so the
+// wait costs the round trips of the slowest word. The whole wave calls it.
+template <int N>
+__device__ __forceinline__ bool poll_tagged_n(const unsigned long long* const (&p)[N],
+                                              unsigned long long (&v)[N], unsigned tag, unsigned spin) {
+    bool done[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) done[j] = p[j] == nullptr;
     for (unsigned n = 0;;) {
-        if (!done) {
-            v = ld_agent(p);
-            done = has_tag(v, tag);
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            if (!done[j]) v[j] = ld_agent(p[j]);
+        bool all = true;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            done[j] = done[j] || has_tag(v[j], tag);
+            all = all && done[j];
         }
-        if (__all(done)) return true;
+        if (__all(all)) return true;
         if (++n > spin) return false;
         __builtin_amdgcn_s_sleep(1);
     }
@@ -1207,12 +1216,13 @@ void vt_small_kernel(SmallArgs a) {
         }
         // 3. one poll for the request's acceptance codes and the unit's chunk sums
         if (wave == 0) {
-            unsigned long long fv = 0, w0 = 0, w1 = 0, w2 = 0;
-            bool ok = poll_tagged(lane < q.ell ? a.flags + static_cast<long long>(b) * G + lane : nullptr,
-                                  fv, tag, a.spin);
-            ok = ok && poll_tagged(lane < nch ? ms + 4 * lane : nullptr, w0, tag, a.spin);
-            ok = ok && poll_tagged(lane < nch ? ms + 4 * lane + 1 : nullptr, w1, tag, a.spin);
-            ok = ok && poll_tagged(lane < nch ? ms + 4 * lane + 2 : nullptr, w2, tag, a.spin);
+            const unsigned long long* const pw[4] = {
+                lane < q.ell ? a.flags + static_cast<long long>(b) * G + lane : nullptr,
+                lane < nch ? ms + 4 * lane : nullptr, lane < nch ? ms + 4 * lane + 1 : nullptr,
+                lane < nch ? ms + 4 * lane + 2 : nullptr};
+            unsigned long long wv4[4] = {0, 0, 0, 0};
+            const bool ok = poll_tagged_n<4>(pw, wv4, tag, a.spin);
+            const unsigned long long fv = wv4[0], w0 = wv4[1], w1 = wv4[2], w2 = wv4[3];
             const unsigned code = static_cast<unsigned>(fv) & 3u;
             const bool bad = ok && lane < q.ell && code == 3u;
             const bool rej = ok && lane < q.ell && code == 2u;
