@@ -56,6 +56,7 @@ __device__ __forceinline__ void load_chunk_contig(const float* __restrict__ row,
 // first, then the scaled sums in lane-strided order and a fixed-order wave sum); the same
 // value in every lane.
 __device__ __forceinline__ float merge_lse_wave(const float2* __restrict__ P, int nch) {
+#pragma clang fp contract(off)          // each product and sum rounds on its own at every call site
     const int lane = threadIdx.x & (kWave - 1);
     float mm = -INFINITY;
     float2 p0 = make_float2(-INFINITY, 0.0f);

@@ -26,6 +26,12 @@
 #include "kernels.h"
 #include "rows.h"
 
+// Every product and sum below rounds on its own (fused only where written as fmaf), so the
+// verify's forms (one launch, sweep, chunked kernels) form each probability, mass and running
+// sum with the same roundings whatever the contraction choices at each site: they agree bit
+// for bit by construction.
+#pragma clang fp contract(off)
+
 namespace dspark {
 
 namespace {
@@ -294,6 +300,58 @@ __device__ __forceinline__ void chunk_terms(FinalRow& fr, float (&t)[kPer], floa
     fr.at_chunk(mt, md);
 }
 
+// The draw inside one chunk. Thread i holds the weights w of the kPer tokens v0, v0 + 1, ...
+// (the threads' runs follow token order). Returns the first token whose running sum exceeds
+// tprime or, when rounding leaves tprime at or past the chunk's sum, the last token of positive
+// weight (-1 if there is none). The running sum adds a thread's own weights in order to the sum
+// of the runs before it: the runs' sums are scanned across the wave by DPP and the wave totals
+// added in wave order. fscr holds kWaves floats and iscr 2 * kWaves ints; a caller syncs before
+// it reuses them. Called by the whole workgroup.
+__device__ __forceinline__ int chunk_pick(const float (&w)[kPer], float tprime, int v0, float* fscr,
+                                          int* iscr) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    float local = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) local += w[e];
+    const float incl = wave_incl_scan_dpp(local);
+    const float excl = wave_shr1_dpp(incl);
+    if (lane == kWave - 1) fscr[wave] = incl;
+    __syncthreads();
+    float run = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWaves - 1; ++j)
+        if (j < wave) run += fscr[j];
+    run += excl;
+    // bit e of pos: token v0 + e has weight; of past: it has weight and the running sum up to
+    // it exceeds tprime (bit masks rather than branches)
+    unsigned pos = 0u, past = 0u;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        run += w[e];
+        const unsigned bit = 1u << e;
+        pos |= (w[e] > 0.0f) ? bit : 0u;
+        past |= (run > tprime) ? bit : 0u;
+    }
+    past &= pos;
+    int hit = past ? v0 + __builtin_ctz(past) : INT32_MAX;
+    int last = pos ? v0 + 31 - __builtin_clz(pos) : -1;
+    static_assert(kPer == 32, "one bit per token of a thread's run");
+    hit = wave_min_int_dpp(hit);
+    last = wave_max_int_dpp(last);
+    if (lane == 0) {
+        iscr[wave] = hit;
+        iscr[kWaves + wave] = last;
+    }
+    __syncthreads();
+    int h = iscr[0], l = iscr[kWaves];
+#pragma unroll
+    for (int j = 1; j < kWaves; ++j) {
+        h = min(h, iscr[j]);
+        l = max(l, iscr[kWaves + j]);
+    }
+    return h != INT32_MAX ? h : l;
+}
+
 template <bool VEC4>
 __device__ __forceinline__ float chunk_mass(FinalRow fr, int c, int V, float (*red)[kWaves]) {
     float t[kPer], d[kPer];
@@ -435,7 +493,7 @@ template <bool VEC4>
 __device__ __forceinline__ int final_draw(int V, int nch, FinalRow fr, float* cs, float uf) {
     __shared__ float fscr[kWaves + 1];
     __shared__ float red[2][kWaves];
-    __shared__ int iscr[kWaves + 1];
+    __shared__ int iscr[2 * kWaves];
     __shared__ int s_found;
     __shared__ float s_tprime, s_total;
     const int tid = threadIdx.x;
@@ -495,29 +553,9 @@ __device__ __forceinline__ int final_draw(int V, int nch, FinalRow fr, float* cs
         if (fr.residual) load_chunk_contig<VEC4>(fr.ld, found, V, d);
         chunk_terms(fr, t, d, red);
         float w[kPer];
-        float local = 0.0f;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            w[e] = fr.weight(t[e], d[e]);
-            local += w[e];
-        }
-        float tot;
-        const float ex = block_excl_scan<kThreads>(local, fscr, &tot);
-        const float tprime = s_tprime;
-        const long long v0 =
-            static_cast<long long>(found) * kChunk + static_cast<long long>(kPer) * tid;
-        int hit = INT32_MAX, lastpos = -1;
-        float run = ex;
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            run += w[e];
-            if (w[e] > 0.0f) {
-                lastpos = static_cast<int>(v0 + e);
-                if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(v0 + e);
-            }
-        }
-        z = block_min_int<kThreads>(hit, iscr);
-        if (z == INT32_MAX) z = block_max_int<kThreads>(lastpos, iscr);
+        for (int e = 0; e < kPer; ++e) w[e] = fr.weight(t[e], d[e]);
+        z = chunk_pick(w, s_tprime, found * kChunk + kPer * tid, fscr, iscr);
     }
     return z;
 }
@@ -766,6 +804,8 @@ void vt_sweep_kernel(SweepArgs a) {
         const ReqRows q = request_rows(rs, b);
         if (!q.ok || s > q.ell) continue;               // no such row: nobody waits for it
         const bool pair = s < q.ell;
+        // the draft's given normaliser, loaded ahead of the chunk (it is needed right after the wait)
+        const float lsdi = (pair && a.lse_d_in) ? a.lse_d_in[static_cast<long long>(b) * G + s] : 0.0f;
         float t[kPer], d[kPer];
         load_chunk<VEC4>(rs.Lt + (q.off + s) * V, c, V, t);
         if (pair) load_chunk<VEC4>(rs.Ld + (static_cast<long long>(b) * G + s) * V, c, V, d);
@@ -809,7 +849,7 @@ void vt_sweep_kernel(SweepArgs a) {
             }
             const float lt = merge_lanes(pt);
             float ld = 0.0f;
-            if (pair) ld = a.lse_d_in ? a.lse_d_in[static_cast<long long>(b) * G + s] : merge_lanes(pd);
+            if (pair) ld = a.lse_d_in ? lsdi : merge_lanes(pd);
             if (lane == 0) {
                 s_lse[0] = ld;
                 s_lse[1] = lt;
@@ -1043,12 +1083,14 @@ __global__ __launch_bounds__(kThreads, 2)
 void vt_small_kernel(SmallArgs a) {
     __shared__ float sm[4][kWaves];
     __shared__ float fscr[3 * kWaves + 1];
-    __shared__ int iscr[kWaves + 1];
+    __shared__ int iscr[2 * kWaves];
     __shared__ float s_lse[2];
     __shared__ int s_gave, s_n, s_bad, s_found, s_residual;
     __shared__ float s_tprime;
     __shared__ unsigned s_tag;
-    __shared__ float wl[kChunk];                     // the rescan's weights in token order
+    // the rescan's weights in token order, 4 words of padding after every 32 (one thread's
+    // run), so the row-wise writes and the run-wise reads both spread over the banks
+    __shared__ float4 wl[(kChunk + kChunk / 8) / 4];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const RowSet& rs = a.rs;
     const int G = rs.gamma, V = rs.V, nch = a.nch, G1 = G + 1;
@@ -1079,9 +1121,29 @@ void vt_small_kernel(SmallArgs a) {
     float lsd = 0.0f, lst = 0.0f;
     unsigned long long* us = a.slots + unit * nch * 4;
     unsigned long long* ms = a.mslots + unit * nch * 4;
+    // the later steps' inputs, loaded ahead of the chunk: the drafted token, its uniform and the
+    // draft's given normaliser; the final draw's uniform and the request's drafted tokens
+    int xk = -1, xr = -1;
+    float ua = 0.0f, lsdi = 0.0f, uf = 0.0f;
+    if (live) {
+        if (pair) {
+            xk = a.x[static_cast<long long>(b) * G + s];
+            ua = a.u_acc[static_cast<long long>(b) * G + s];
+            if (a.lse_d_in) lsdi = a.lse_d_in[static_cast<long long>(b) * G + s];
+        }
+        uf = a.u_fin[b];
+        if (tid < G) xr = a.x[static_cast<long long>(b) * G + tid];
+    }
+    const long long base = static_cast<long long>(c) * kChunk;
+    const bool owner = pair && xk >= 0 && xk < V && xk >= base && xk < base + kChunk;
+    float ltx = 0.0f, ldx = 0.0f;                    // the two logits at the drafted token
     if (live) {
         load_chunk<VEC4>(rs.Lt + (q.off + s) * V, c, V, t);
         if (pair) load_chunk<VEC4>(rs.Ld + (static_cast<long long>(b) * G + s) * V, c, V, d);
+        if (owner && tid == 0) {
+            ltx = rs.Lt[(q.off + s) * V + xk];
+            ldx = rs.Ld[(static_cast<long long>(b) * G + s) * V + xk];
+        }
     }
     // the call's tag, read while the chunk is on its way (the anchor counts on every task
     // having read it before it publishes)
@@ -1094,12 +1156,13 @@ void vt_small_kernel(SmallArgs a) {
     float cmt = -INFINITY, cmd = -INFINITY;          // the chunk's maxima (target, draft)
     if (live) {
         // 1. partials, published as tagged words; the unit's normalisers (a pair forms both
-        //    rows' partials, also when the draft's lse is given: its terms need the max)
+        //    rows' partials, also when the draft's lse is given: its terms need the max). The
+        //    chunk's terms replace its logits.
         float mt, st, md = -INFINITY, sd = 0.0f;
         if (pair)
-            chunk_ms2<false>(t, d, mt, st, md, sd, sm);
+            chunk_ms2<true>(t, d, mt, st, md, sd, sm);
         else
-            chunk_ms<false>(t, mt, st, sm);
+            chunk_ms<true>(t, mt, st, sm);
         cmt = mt;
         cmd = md;
         if (tid < 4) {
@@ -1137,7 +1200,7 @@ void vt_small_kernel(SmallArgs a) {
             }
             const float lt = merge_lanes(pt);
             float ld = 0.0f;
-            if (pair) ld = a.lse_d_in ? a.lse_d_in[static_cast<long long>(b) * G + s] : merge_lanes(pd);
+            if (pair) ld = a.lse_d_in ? lsdi : merge_lanes(pd);
             if (lane == 0) {
                 s_lse[0] = ld;
                 s_lse[1] = lt;
@@ -1156,14 +1219,14 @@ void vt_small_kernel(SmallArgs a) {
             const float scd = chunk_scale(cmd, lsd);
 #pragma unroll
             for (int e = 0; e < kPer; ++e) {
-                const float pt = chunk_e(t[e], cmt) * sct, pd = chunk_e(d[e], cmd) * scd;
+                const float pt = t[e] * sct, pd = d[e] * scd;
                 sv += fminf(pd, pt);
                 mass += fmaxf(pt - pd, 0.0f);
                 ptm += pt;
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < kPer; ++e) mass += chunk_e(t[e], cmt) * sct;
+            for (int e = 0; e < kPer; ++e) mass += t[e] * sct;
         }
         float v3[3] = {sv, mass, ptm};
         chunk_sums<3>(v3, fscr);
@@ -1172,31 +1235,18 @@ void vt_small_kernel(SmallArgs a) {
         ptm = v3[2];
         if (tid < 3) st_agent(ms + 4 * c + tid, tagged(tag, tid == 0 ? sv : tid == 1 ? mass : ptm));
         if (pair) {
-            const int xk = a.x[static_cast<long long>(b) * G + s];
-            const long long base = static_cast<long long>(c) * kChunk;
             unsigned long long* fl = a.flags + static_cast<long long>(b) * G + s;
             if (xk < 0 || xk >= V) {
                 if (c == 0 && tid == 0) st_agent(fl, tagged(tag, 3u));
-            } else if (xk >= base && xk < base + kChunk) {
-                const int rel = static_cast<int>(xk - base);
-                if (tid == ((rel >> 2) & (kThreads - 1))) {
-                    const int ei = 4 * (rel >> 10) + (rel & 3);
-                    float ltx = 0.0f, ldx = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < kPer; ++e)
-                        if (e == ei) {
-                            ltx = t[e];
-                            ldx = d[e];
-                        }
-                    const float lpt = (lst == -INFINITY) ? -INFINITY : ltx - lst;
-                    const float lpd = (lsd == -INFINITY) ? -INFINITY : ldx - lsd;
-                    bool acc;
-                    if (lpd == -INFINITY)
-                        acc = lpt > -INFINITY;
-                    else
-                        acc = logf(clamp_uniform(a.u_acc[static_cast<long long>(b) * G + s])) < lpt - lpd;
-                    st_agent(fl, tagged(tag, acc ? 1u : 2u));
-                }
+            } else if (owner && tid == 0) {
+                const float lpt = (lst == -INFINITY) ? -INFINITY : ltx - lst;
+                const float lpd = (lsd == -INFINITY) ? -INFINITY : ldx - lsd;
+                bool acc;
+                if (lpd == -INFINITY)
+                    acc = lpt > -INFINITY;
+                else
+                    acc = logf(clamp_uniform(ua)) < lpt - lpd;
+                st_agent(fl, tagged(tag, acc ? 1u : 2u));
             }
         }
         // normalisers out (chunk 0 of each unit; the bonus unit also fills what lies beyond)
@@ -1239,11 +1289,11 @@ void vt_small_kernel(SmallArgs a) {
             if (ok && badm == 0ull && s == n) {
                 float mv = (lane < nch) ? tagged_f(w1) : 0.0f;
                 const float pv = (lane < nch) ? tagged_f(w2) : 0.0f;
-                const float uf = clamp_uniform(a.u_fin[b]);
+                const float ufc = clamp_uniform(uf);
                 for (int pass = 0; pass < 2; ++pass) {
                     const float v = (lane < nch) ? mv : 0.0f;
                     const float tot = wave_sum_dpp(v);
-                    const float target = uf * tot;
+                    const float target = ufc * tot;
                     found = -1;
                     tprime = INFINITY;
                     const float incl = wave_incl_scan_dpp(v);
@@ -1294,41 +1344,32 @@ void vt_small_kernel(SmallArgs a) {
                 fw.lse_d = pair ? lsd : 0.0f;
                 fw.residual = s_residual;
                 fw.at_chunk(cmt, cmd);
+                // token row r (tokens 4 r .. 4 r + 3) goes to padded vector r + r / 8; the run
+                // of thread i starts at vector 9 i
+                const bool rd = fw.residual;
 #pragma unroll
-                for (int g = 0; g < kPer / 4; ++g)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const int e = 4 * g + w;
-                        wl[4 * (tid + kThreads * g) + w] =
-                            fw.weight(chunk_e(t[e], cmt), fw.residual ? chunk_e(d[e], cmd) : 0.0f);
-                    }
+                for (int g = 0; g < kPer / 4; ++g) {
+                    const int e = 4 * g, r = tid + kThreads * g;
+                    wl[r + (r >> 3)] = make_float4(fw.weight(t[e], rd ? d[e] : 0.0f),
+                                                   fw.weight(t[e + 1], rd ? d[e + 1] : 0.0f),
+                                                   fw.weight(t[e + 2], rd ? d[e + 2] : 0.0f),
+                                                   fw.weight(t[e + 3], rd ? d[e + 3] : 0.0f));
+                }
                 __syncthreads();
                 float wv[kPer];
-                float local = 0.0f;
 #pragma unroll
-                for (int e = 0; e < kPer; ++e) {
-                    wv[e] = wl[kPer * tid + e];
-                    local += wv[e];
+                for (int g = 0; g < kPer / 4; ++g) {
+                    const float4 v = wl[(kPer / 4 + 1) * tid + g];
+                    wv[4 * g] = v.x;
+                    wv[4 * g + 1] = v.y;
+                    wv[4 * g + 2] = v.z;
+                    wv[4 * g + 3] = v.w;
                 }
-                float tot;
-                const float ex = block_excl_scan<kThreads>(local, fscr, &tot);
-                const float tprime = s_tprime;
-                const long long v0 = static_cast<long long>(c) * kChunk + static_cast<long long>(kPer) * tid;
-                int hit = INT32_MAX, lastpos = -1;
-                float run = ex;
-#pragma unroll
-                for (int e = 0; e < kPer; ++e) {
-                    run += wv[e];
-                    if (wv[e] > 0.0f) {
-                        lastpos = static_cast<int>(v0 + e);
-                        if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(v0 + e);
-                    }
-                }
-                z = block_min_int<kThreads>(hit, iscr);
-                if (z == INT32_MAX) z = block_max_int<kThreads>(lastpos, iscr);
+                z = chunk_pick(wv, s_tprime, c * kChunk + kPer * tid, fscr, iscr);
             }
+            // gamma <= 64 < kThreads: thread i writes y[i] (its drafted token was loaded above)
             for (int i = tid; i <= G; i += kThreads)
-                y[i] = (i < n) ? a.x[static_cast<long long>(b) * G + i] : (i == n ? z : -1);
+                y[i] = (i < n) ? (i == tid ? xr : a.x[static_cast<long long>(b) * G + i]) : (i == n ? z : -1);
             if (tid == 0) a.n_out[b] = n;
         }
     }
