@@ -30,11 +30,15 @@
 //   - At position k every workgroup keeps its 640 logits in LDS (and stores them to the
 //     logits output when the caller wants it), then publishes its tile's (max, sum exp) into
 //     slot [k][g] with one 8-byte device-scope store.
-//   - Wave 0 of every workgroup polls the G slots of position k until none holds the
-//     sentinel, and picks the tile that holds the inverse-CDF point from those partials (in
-//     tile order; every workgroup reaches the same pick). The workgroup that owns the tile
-//     rescans its logits from LDS in token order and publishes (logit, token) in token slot
-//     [k]; the others poll that slot.
+//   - Wave 0 of workgroup 0 polls the G slots of position k until none holds the sentinel,
+//     picks the tile that holds the inverse-CDF point from those partials (in tile order),
+//     and publishes the pick (tile, global max, remaining mass) in two pick words. Wave 0 of
+//     every other workgroup polls the pick words and token slot [k] together. The workgroup
+//     that owns the picked tile rescans its logits from LDS in token order and publishes
+//     (logit, token) in token slot [k]; the others take the token from there.
+//   A single poller of the partials keeps the polling light: when every workgroup polled the
+//   G partial slots, the loads queued and each of the two round trips took several times the
+//   latency of one store seen by one poller; the pick costs one light hop more.
 // No workgroup ever reads another's logits, so nothing waits for the logits stores, and the
 // draw costs one published token instead of a read of the chosen tile. No L2 write-back
 // fence is used, because that costs tens of microseconds per position on this part. Polling
@@ -88,7 +92,9 @@ struct ResArgs {
     int L_out;
     float2* slots;            // [gamma][G] tile partials, kEmpty until published
     unsigned long long* toks; // [gamma] (logit bits << 32 | token) of each draw, kEmpty until published
-    unsigned long long* epoch;   // [2]: the call counter E and the ready word F (after toks)
+    unsigned long long* picks;   // [gamma][2] (max bits << 32 | tile + 1), (remaining mass bits << 32 |
+                                 // tile + 1) of each pick (tile + 1 = 0: no mass), kEmpty until published
+    unsigned long long* epoch;   // [2]: the call counter E and the ready word F (after the picks)
     unsigned* status;         // number of workgroups that gave up (reset with the slots)
     unsigned spin;            // polls before a wait gives up
     const uint16_t* A;        // RNN head: [r][r] bf16 recurrence
@@ -150,6 +156,7 @@ void draft_resident(ResArgs a) {
     __shared__ float ah[RNN ? 2 : 1][RNN ? kResMaxRank : 1];   // RNN: A h_k, two halves of j
     __shared__ uint32_t hhi[RNN ? kResMaxRank / 2 : 1];    // RNN: h_k as bf16 pairs, hi parts
     __shared__ uint32_t hlo[RNN ? kResMaxRank / 2 : 1];    //                        lo parts
+    __shared__ unsigned long long ptile[kMaxTiles];       // workgroup 0: the position's tile partials
     __shared__ int stok;
     __shared__ int gave_up;
     __shared__ unsigned long long s_e0;                    // the call counter read at the start
@@ -166,7 +173,7 @@ void draft_resident(ResArgs a) {
     if (tid == 0) s_e0 = load_token(a.epoch);             // seen by every thread after a barrier
     if (blockIdx.x == 0) {                                // reset this call's slots
         unsigned long long* sl = reinterpret_cast<unsigned long long*>(a.slots);
-        const int n = a.gamma * a.G + a.gamma;             // partial slots, then token slots
+        const int n = a.gamma * a.G + 3 * a.gamma;         // partial slots, token slots, pick words
         for (int i = tid; i < n; i += kRThreads) store_token(sl + i, kEmpty);
         if (tid == 0) __hip_atomic_store(a.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -357,38 +364,61 @@ void draft_resident(ResArgs a) {
             u1 = (e1 < V) ? a.U[o + e1] : 0.0f;
             u2 = (own2 && e2 < V) ? a.U[o + e2] : 0.0f;
         }
-        // 4. wave 0: wait for every tile partial of position k, draw x_k, stage W1[x_k]
+        // 4. wave 0: draw x_k (workgroup 0 picks the tile, its owner rescans it), stage W1[x_k]
         if (wave == 0) {
-            float2 p[kPartRegs];
-            unsigned n = 0;
-            while (!gave_up) {
-                bool missing = false;
-#pragma unroll
-                for (int t = 0; t < kPartRegs; ++t) {
-                    const int i = lane * kPartRegs + t;
-                    unsigned long long bits = 0ull;
-                    if (i < a.G) {
-                        bits = load_slot(slot + i);
-                        missing |= bits == kEmpty;
-                    }
-                    p[t] = (i < a.G) ? __builtin_bit_cast(float2, bits) : make_float2(-INFINITY, 0.0f);
-                }
-                if (!__any(missing)) break;
-                if (++n > a.spin) {
-                    if (lane == 0) gave_up = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
             int t = -1;
             float lx = 0.0f;
             TilePick tp;
             tp.tile = -1;
-            if (!gave_up) {
-                tp = pick_tile<kPartRegs>(p, a.u[k]);
-                if (tp.tile == static_cast<int>(blockIdx.x)) {
-                    // the chosen tile is this workgroup's: rescan its logits from LDS, in
-                    // token order (lane l owns the 10 columns from 10 l), and publish
+            tp.m = tp.lse = -INFINITY;
+            tp.tprime = INFINITY;
+            bool known = false;                           // the pick is known here
+            unsigned long long* pk = a.picks + 2 * k;
+            if (blockIdx.x == 0) {
+                // load j of lane l reads tile 64 j + l, so each load covers 512 contiguous
+                // bytes (a round costs one request per line, and their count sets its latency);
+                // LDS then hands lane l the tiles [4 l, 4 l + 4) that the pick takes
+                unsigned long long q[kPartRegs];
+                unsigned n = 0;
+                while (!gave_up) {
+                    bool missing = false;
+#pragma unroll
+                    for (int j = 0; j < kPartRegs; ++j) {
+                        const int i = kWave * j + lane;
+                        q[j] = (i < a.G) ? load_slot(slot + i) : 0ull;
+                        missing |= (i < a.G) && q[j] == kEmpty;
+                    }
+                    if (!__any(missing)) break;
+                    if (++n > a.spin) {
+                        if (lane == 0) gave_up = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+#pragma unroll
+                for (int j = 0; j < kPartRegs; ++j) ptile[kWave * j + lane] = q[j];
+                __builtin_amdgcn_wave_barrier();          // the wave's LDS writes before its reads
+                float2 p[kPartRegs];
+#pragma unroll
+                for (int t = 0; t < kPartRegs; ++t) {
+                    const int i = lane * kPartRegs + t;
+                    p[t] = (i < a.G) ? __builtin_bit_cast(float2, ptile[i]) : make_float2(-INFINITY, 0.0f);
+                }
+                if (!gave_up) {
+                    tp = pick_tile<kPartRegs>(p, a.u[k]);
+                    known = true;
+                    if (lane == 0) {
+                        const unsigned long long id = static_cast<uint32_t>(tp.tile + 1);
+                        store_token(pk, (static_cast<unsigned long long>(__float_as_uint(tp.m)) << 32) | id);
+                        store_token(pk + 1, (static_cast<unsigned long long>(__float_as_uint(tp.tprime)) << 32) | id);
+                    }
+                }
+            }
+            // every workgroup: the token from its slot, or, in the owner of the picked tile, from a
+            // rescan of its logits in LDS in token order (lane l owns the 10 columns from 10 l)
+            bool have = known && tp.tile < 0;             // no mass: no token
+            for (unsigned n2 = 0; !gave_up && !have;) {
+                if (known && tp.tile == static_cast<int>(blockIdx.x)) {
                     float lv[kLaneCols], e[kLaneCols];
 #pragma unroll
                     for (int j = 0; j < kLaneCols; ++j) {
@@ -406,20 +436,35 @@ void draft_resident(ResArgs a) {
                     if (lane == 0)
                         store_token(a.toks + k, (static_cast<unsigned long long>(__float_as_uint(lx)) << 32) |
                                                     static_cast<uint32_t>(t));
-                } else if (tp.tile >= 0) {
-                    // another workgroup draws: wait for its (logit, token)
-                    unsigned long long v;
-                    unsigned n2 = 0;
-                    while ((v = load_token(a.toks + k)) == kEmpty) {
-                        if (++n2 > a.spin) {
-                            if (lane == 0) gave_up = 1;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
+                    have = true;
+                    break;
+                }
+                // one round: the pick words (until known) and the token slot, loaded together
+                unsigned long long w0 = 0ull, w1 = 0ull;
+                if (!known) {
+                    w0 = load_token(pk);
+                    w1 = load_token(pk + 1);
+                }
+                const unsigned long long v = load_token(a.toks + k);
+                if (v != kEmpty) {
                     t = static_cast<int>(static_cast<uint32_t>(v));
                     lx = __uint_as_float(static_cast<uint32_t>(v >> 32));
+                    have = true;
+                    break;
                 }
+                if (!known && w0 != kEmpty && w1 != kEmpty) {
+                    tp.tile = static_cast<int>(static_cast<uint32_t>(w0)) - 1;
+                    tp.m = __uint_as_float(static_cast<uint32_t>(w0 >> 32));
+                    tp.tprime = __uint_as_float(static_cast<uint32_t>(w1 >> 32));
+                    known = true;
+                    have = tp.tile < 0;
+                    continue;                             // the owner rescans at once
+                }
+                if (++n2 > a.spin) {
+                    if (lane == 0) gave_up = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
             if (!gave_up) {
                 if (blockIdx.x == 0 && lane == 0) {          // workgroup 0 writes the outputs
@@ -532,7 +577,8 @@ hipError_t launch(const DraftCall& c, const void* A, float* h_out, hipStream_t s
     a.L_out = c.L_out ? 1 : 0;
     a.slots = c.slots;
     a.toks = reinterpret_cast<unsigned long long*>(c.slots + static_cast<long long>(c.gamma) * a.G);
-    a.epoch = a.toks + c.gamma;
+    a.picks = a.toks + c.gamma;
+    a.epoch = a.picks + 2 * c.gamma;
     a.status = c.status;
     a.spin = c.spin;
     a.A = static_cast<const uint16_t*>(A);
@@ -545,10 +591,11 @@ hipError_t launch(const DraftCall& c, const void* A, float* h_out, hipStream_t s
 
 }  // namespace
 
-// tile partials [gamma][G], the token slots [gamma], then the call counter and ready word
+// tile partials [gamma][G], the token slots [gamma], the pick words [gamma][2], then the call
+// counter and ready word
 size_t draft_resident_slot_bytes(int V, int gamma) {
     return static_cast<size_t>(gamma) * tiles_of(V) * sizeof(float2) +
-           (static_cast<size_t>(gamma) + 2) * sizeof(unsigned long long);
+           (3 * static_cast<size_t>(gamma) + 2) * sizeof(unsigned long long);
 }
 
 bool draft_resident_ok(int B, int V, int r, int w_dtype, const void* W1, const void* W2) {

@@ -69,15 +69,19 @@ __device__ __forceinline__ int scan_pick(const float (&e)[CPL], long long c0, fl
     for (int j = 0; j < CPL; ++j) local += e[j];
     const float incl = wave_incl_scan_dpp(local);
     float run = wave_shr1_dpp(incl);
-    int hit = INT32_MAX, lastpos = -1;
+    // bit j of pos: column c0 + j has weight; of past: it has weight and the running weight up
+    // to it exceeds tprime (bit masks rather than branches)
+    static_assert(CPL <= 32, "one bit per column of a lane");
+    unsigned pos = 0u, past = 0u;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         run += e[j];
-        if (e[j] > 0.0f) {
-            lastpos = static_cast<int>(c0 + j);
-            if (hit == INT32_MAX && run > tprime) hit = static_cast<int>(c0 + j);
-        }
+        pos |= (e[j] > 0.0f) ? (1u << j) : 0u;
+        past |= (run > tprime) ? (1u << j) : 0u;
     }
+    past &= pos;
+    const int hit = past ? static_cast<int>(c0) + __builtin_ctz(past) : INT32_MAX;
+    const int lastpos = pos ? static_cast<int>(c0) + 31 - __builtin_clz(pos) : -1;
     const int tok = wave_min_int_dpp(hit);
     return tok == INT32_MAX ? wave_max_int_dpp(lastpos) : tok;
 }
