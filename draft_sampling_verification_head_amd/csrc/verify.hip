@@ -710,9 +710,10 @@ void verify_tv_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
 // (its draft row and target row) or its bonus target row; each unit is cut into the same
 // 8192-logit chunks as above, and task (unit, chunk) keeps its chunk of both rows in registers:
 //   1. the chunk's (max, sum exp) of both rows, formed exactly as row_stats forms them, go into
-//      the unit's slot for that chunk, tagged with this call's key;
-//   2. wave 0 waits until all chunks of the unit carry the key and merges them in chunk order
-//      (the same merge as verify_chunks), giving lse_d and lse_t;
+//      the unit's slot for that chunk as four words tagged with this call's tag;
+//   2. wave 0 waits until all chunks of the unit carry the tag (one round loads every word of
+//      the unit, polled every few hundred cycles so the polls do not crowd the rows' loads) and
+//      merges them in chunk order (the same merge as verify_chunks), giving lse_d and lse_t;
 //   3. from the registers: the chunk's sum of min(p_d, p_t) (as tv_chunks forms it) and its
 //      mass under the unit's final-draw law (the residual max(0, p_t - p_d) of a verified
 //      position, p_t of the bonus row; as chunk_mass forms them).
@@ -729,9 +730,9 @@ void verify_tv_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
 // then reports every request as faulty.
 //
 // The key is the splitmix64 finaliser (Steele, Lea and Flood, "Fast splittable pseudorandom
-// number generators", 2014) of a call counter E in the workspace, xor a constant: slots left by
-// earlier calls carry earlier keys, and all-zero or all-one bytes are no key. Every sweep
-// workgroup reads E at its start; vt_select (which runs after the whole sweep) advances it.
+// number generators", 2014) of a call counter E in the workspace, xor a constant, and the tag
+// is call_tag(E): slots left by earlier calls carry earlier tags. Every sweep workgroup reads E
+// at its start; vt_select (which runs after the whole sweep) advances it.
 
 __device__ __forceinline__ unsigned long long call_key(unsigned long long e) {
     unsigned long long z = e ^ 0x9e3779b97f4a7c15ull;
@@ -748,12 +749,32 @@ __device__ __forceinline__ void st_agent(unsigned long long* p, unsigned long lo
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Hand-over words between workgroups: 32 bits of this call's tag beside a 32-bit value,
+// stored and loaded as one 64-bit word, so a word is valid on its own and no store needs to
+// wait for another. The tag is the low half of the call counter xor a constant: consecutive
+// calls differ, and all-zero or all-one words carry no call's tag.
+__device__ __forceinline__ unsigned call_tag(unsigned long long e) {
+    return static_cast<unsigned>(e) ^ 0x9e3779b9u;
+}
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
+    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, unsigned v) {
+    return (static_cast<unsigned long long>(tag) << 32) | v;
+}
+__device__ __forceinline__ bool has_tag(unsigned long long w, unsigned tag) {
+    return static_cast<unsigned>(w >> 32) == tag;
+}
+__device__ __forceinline__ float tagged_f(unsigned long long w) {
+    return __uint_as_float(static_cast<unsigned>(w));
+}
+
 struct SweepArgs {
     RowSet rs;
     int nch;
     long long ntasks;                 // B (gamma + 1) nch
     const float* lse_d_in;            // nullable
-    unsigned long long* slots;        // [unit][nch][4]: draft (max, sum), target (max, sum), key, -
+    unsigned long long* slots;        // [unit][nch][4] tagged: draft max, sum; target max, sum
     float2* ulse;                     // [unit] (lse_d, lse_t)
     float* rmass;                     // [unit][nch] mass under the unit's final-draw law
     float* psum;                      // [b gamma + k][nch] sum of min(p_d, p_t)
@@ -781,16 +802,20 @@ void vt_sweep_kernel(SweepArgs a) {
     __shared__ float s_lse[2];
     __shared__ int s_gave;
     __shared__ unsigned long long s_key;
+    __shared__ unsigned s_tag;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const RowSet& rs = a.rs;
     const int G = rs.gamma, V = rs.V, nch = a.nch, G1 = G + 1;
     if (tid == 0) {
-        s_key = call_key(ld_agent(a.hdr));
+        const unsigned long long e = ld_agent(a.hdr);
+        s_key = call_key(e);
+        s_tag = call_tag(e);
         s_gave = 0;
         if (blockIdx.x == 0) st_agent(a.hdr + 2, s_key);
     }
     __syncthreads();
     const unsigned long long key = s_key;
+    const unsigned tag = s_tag;
     // group grp of the workgroups sweeps units [u0, u1), its workgroups taking its tasks
     // round-robin; a unit's waits then involve the workgroups of one group only
     const unsigned per = gridDim.x / static_cast<unsigned>(a.groups);
@@ -809,7 +834,7 @@ void vt_sweep_kernel(SweepArgs a) {
         float t[kPer], d[kPer];
         load_chunk<VEC4>(rs.Lt + (q.off + s) * V, c, V, t);
         if (pair) load_chunk<VEC4>(rs.Ld + (static_cast<long long>(b) * G + s) * V, c, V, d);
-        // 1. chunk partials (row_stats' arithmetic), published with the key
+        // 1. chunk partials (row_stats' arithmetic), published as tagged words
         // (the registers then hold the chunk's terms exp(x - M); a pair forms both rows'
         // terms, also when the draft's lse is given)
         float mt, st, md = -INFINITY, sd = 0.0f;
@@ -818,27 +843,33 @@ void vt_sweep_kernel(SweepArgs a) {
         else
             chunk_ms<true>(t, mt, st, sm);
         unsigned long long* us = a.slots + unit * nch * 4;
-        if (tid == 0) {
-            st_agent(us + 4 * c, __builtin_bit_cast(unsigned long long, make_float2(md, sd)));
-            st_agent(us + 4 * c + 1, __builtin_bit_cast(unsigned long long, make_float2(mt, st)));
-            __builtin_amdgcn_s_waitcnt(0);              // the partials land before the key
-            st_agent(us + 4 * c + 2, key);
+        if (tid < 4) {
+            const float v = tid == 0 ? md : tid == 1 ? sd : tid == 2 ? mt : st;
+            st_agent(us + 4 * c + tid, tagged(tag, v));
         }
-        // 2. the unit's normalisers, once every chunk carries the key
+        // 2. the unit's normalisers, once every chunk's words carry the tag
         if (wave == 0) {
             float2 pd = make_float2(-INFINITY, 0.0f), pt = make_float2(-INFINITY, 0.0f);
             bool ok = true;
             if (lane < nch) {
-                for (unsigned n = 0; ld_agent(us + 4 * lane + 2) != key;) {
+                unsigned long long w[4];
+                for (unsigned n = 0;;) {
+                    bool all = true;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        w[j] = ld_agent(us + 4 * lane + j);
+                        all &= has_tag(w[j], tag);
+                    }
+                    if (all) break;
                     if (++n > a.spin) {
                         ok = false;
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(1);
+                    __builtin_amdgcn_s_sleep(16);
                 }
                 if (ok) {
-                    pd = __builtin_bit_cast(float2, ld_agent(us + 4 * lane));
-                    pt = __builtin_bit_cast(float2, ld_agent(us + 4 * lane + 1));
+                    pd = make_float2(tagged_f(w[0]), tagged_f(w[1]));
+                    pt = make_float2(tagged_f(w[2]), tagged_f(w[3]));
                 }
             }
             if (__any(!ok)) {
@@ -1011,25 +1042,6 @@ void vt_select_kernel(SweepArgs a, const int32_t* __restrict__ x, const float* _
 // Polling is bounded: a workgroup that gives up writes the call's key into the give-up word
 // (the outputs of such a call are not defined).
 
-// Hand-over words of the one-launch form: 32 bits of this call's tag beside a 32-bit value,
-// stored and loaded as one 64-bit word, so a word is valid on its own and no store needs to
-// wait for another. The tag is the low half of the call counter xor a constant: consecutive
-// calls differ, and all-zero or all-one words carry no call's tag.
-__device__ __forceinline__ unsigned call_tag(unsigned long long e) {
-    return static_cast<unsigned>(e) ^ 0x9e3779b9u;
-}
-__device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
-    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
-}
-__device__ __forceinline__ unsigned long long tagged(unsigned tag, unsigned v) {
-    return (static_cast<unsigned long long>(tag) << 32) | v;
-}
-__device__ __forceinline__ bool has_tag(unsigned long long w, unsigned tag) {
-    return static_cast<unsigned>(w >> 32) == tag;
-}
-__device__ __forceinline__ float tagged_f(unsigned long long w) {
-    return __uint_as_float(static_cast<unsigned>(w));
-}
 
 constexpr int kSmallMaxTasks = 768;                 // one-launch form: tasks per call at most
 
