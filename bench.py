@@ -45,38 +45,38 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
     ("single", "draft_resident"): dict(
-        bytes=86970802.0,
+        bytes=86697211.5,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
-        sources={"draft_resident.hip": "500b1242842057d21c694c44ac4e4209d0ec2877d60bbbf6267bdf417e640ae1",
-                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
+        sources={"draft_resident.hip": "3b10cd99634f60bcf455ad08b5b56544542e0f32a11f7d72e767f4bb9f507202",
+                 "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the per-position sweep of one request (bench.py --per-position)
     ("single", "draft_step_gemv"): dict(
-        bytes=79191939.8,
+        bytes=79190294.5,
         profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
         sources={"draft.hip": "48a48f93317cfc1a63460cbe3d00ebf91bb049d6b29ba4e96aeab52653667d8d",
-                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
+                 "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("batched", "draft_slab_resident"): dict(
-        bytes=1421492055.2,
+        bytes=1446169785.6,
         profile="profiles/draft_slab_resident_batched_B64_V151936.md",
         sources={"draft_slab.hip": "21b13026391fbfdf5bd1eb540df939c58901b0a9cb5ba32671181343b05300f5",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
-                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
+                 "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the two kernels of one dspark_verify_tv call on the sweep path (vt_sweep, vt_select)
     ("verify", "dspark_verify_tv"): dict(
-        bytes=5286748767.6,
+        bytes=5262739029.8,
         profile="profiles/verify_tv_verify_B256_V151936.md",
-        sources={"verify.hip": "99cd80b7f65f69eb92ba582a9ce10ce4870b5070caec8936cca3ab9333186687",
-                 "rows.h": "069e0045b9a59c15697218de2708ffbdb33de09773099a9e0e95cad34229983b",
+        sources={"verify.hip": "2f3a3106333ccf4251e793eeaeb3a9d810cdaa08b22d88429b09244e9b6f1bc7",
+                 "rows.h": "034bd45b0d847736581802a52cbc1a69584399aadbae0696fe836fb20b4fd3e8",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
-        bytes=4835563051.9,
+        bytes=4835578158.7,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
         sources={"draft_slab.hip": "21b13026391fbfdf5bd1eb540df939c58901b0a9cb5ba32671181343b05300f5",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
-                 "draw.h": "43a8e1c1813a52d9afa9b7e05469d4ab43e1fc94f9fc81e6a04f463aa99ef44e",
+                 "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
 }
 
@@ -775,8 +775,9 @@ def run_workload(args, workload, torch, dspark, device, steps, cpu_seconds, mp):
             kernel = "draft_resident" if path == "resident" else "draft_slab_resident"
             units, launch_us = G, ms_kernel * 1e3
             bytes_launch = draft_bytes_one_launch(c, not rebuild)
-            limiter = ("latency: per position two cross-CU round trips (tile partials, then "
-                       "the drawn token) after a GEMV from registers" if path == "resident" else
+            limiter = ("latency: per position three cross-CU hand-overs (tile partials to one "
+                       "poller, the pick to the tile's owner, the token to all) after a GEMV "
+                       "from registers" if path == "resident" else
                        "HBM stream of U_k and three flag barriers per position")
         else:
             # one step kernel per position; the per-position time also carries the draws
