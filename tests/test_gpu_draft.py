@@ -226,6 +226,25 @@ def test_single_request_bf16_permutation_chain(gpu):
         assert out["x"][0, k] == prev
 
 
+def test_single_request_pick_in_first_and_last_tile(gpu):
+    """The single-request draft's draw when the picked tile is workgroup 0's own (the
+    workgroup that gathers the tile partials then also rescans) and when it is the last,
+    ragged tile: a +20 boost puts almost all of a position's mass on token 5 (tile 0) or on
+    token V - 1 (the third tile of V = 1288), alternately."""
+    c = synth.custom(947, B=1, V=1288, r=64, gamma=8, w_dtype="bf16", w_sigma=0.02)
+    d = synth.draft_inputs(c)
+    d["U"] = (0.1 * np.random.default_rng(947).standard_normal(d["U"].shape)).astype(np.float32)
+    want = [5 if k % 2 == 0 else c.V - 1 for k in range(c.gamma)]
+    for k, tok in enumerate(want):
+        d["U"][0, k, tok] += 20.0
+    assert dspark.markov_draft_path(1, dev(d["W1"]), dev(d["W2"])) == "resident"
+    g = run_draft(d)
+    assert g["x"][0].tolist() == want
+    rep = check_draft(d["U"], d["W1"], d["W2"], d["x0"], d["u"], "bf16", g["x"], g["q"],
+                      g["lse"], [0], gL=g["L"])
+    assert rep.ties == 0 and rep.compared == c.gamma
+
+
 def test_single_request_bf16_sentinels(gpu):
     c = synth.custom(936, B=1, V=3000, r=32, gamma=5)
     d = synth.draft_inputs(c)
