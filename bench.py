@@ -672,8 +672,22 @@ def run_workload(args, workload, torch, dspark, device, steps, cpu_seconds, mp):
                                      conf=t["conf"], temp=t["temp"], out=out_d, out_sched=out_s)
 
     step_fns = [draft_schedule, verify] if fused else list(parts.values())
+    # otherwise the schedule runs on a second stream beside the draft: the persistent draft
+    # holds one compute unit per vocabulary slab, and the schedule's few workgroups take
+    # compute units it leaves free (18 of 256 at V = 151936)
+    overlap = not fused and not verify_only
+    side = torch.cuda.Stream(device=device) if overlap else None
 
     def step():
+        if overlap:
+            main = torch.cuda.current_stream()
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                schedule()
+            draft()
+            main.wait_stream(side)
+            verify()
+            return
         for fn in step_fns:
             fn()
 
@@ -820,7 +834,8 @@ def run_workload(args, workload, torch, dspark, device, steps, cpu_seconds, mp):
                                   "written by the draft"),
                     draft_launches="per position" if args.per_position else "default",
                     schedule=("none" if verify_only else
-                              "in the draft's launch" if fused else "its own launch")),
+                              "in the draft's launch" if fused else
+                              "its own launches, on a second stream beside the draft")),
         drafted_per_step=drafted, verified_per_step=verified,
         breakdown_us={k: v * 1e3 for k, v in ms_parts.items()},
         ms_per_step_p10_p90=[float(np.percentile(ms, 10)), float(np.percentile(ms, 90))],
