@@ -86,6 +86,20 @@ MEASURED_TRAFFIC = {
 }
 
 
+# VALU instructions of one STS fit (sts_prep + sts_stats + sts_pick; SQ_INSTS_VALU summed over
+# the dispatches of one call on the STS workload), kept while the sources are unchanged.
+MEASURED_VALU = {
+    ("sts", "sts_fit"): dict(
+        instructions=48075857,
+        profile="profiles/sts_fit_N65536_G16.md",
+        sources={"sts.hip": "8cdd95471ed406ac1976ff6097aee3b0dd081e8f0996f73329b1b2e5a2080cc7",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
+}
+# VALU issue peak of the chip: 256 CUs x 4 SIMDs, one wave64 instruction per SIMD every 4
+# cycles (16 lanes; fp32 and fp64 adds, multiplies and FMAs alike), at 2.4 GHz.
+VALU_PEAK_GINSTR = 256 * 4 * 2.4 / 4
+
+
 def sources_unchanged(sources: dict) -> bool:
     """Whether every kernel source still has the sha256 a counter figure was taken with."""
     import hashlib
@@ -291,13 +305,30 @@ def bench_sts(args, torch, dspark, device):
         b.record()
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the method's work: every observed pair at every grid temperature and at T = 1
+    obs = 0
+    for k in range(G):
+        obs += int(np.sum((k < n_acc) | ((k == n_acc) & (n_acc < G))))
+    evals = obs * (nT + 1)
+    rec = MEASURED_VALU[("sts", "sts_fit")]
+    instr = rec["instructions"] if rec["instructions"] and sources_unchanged(rec["sources"]) else None
+    achieved = None if instr is None else instr / (ms * 1e-3) / 1e9
+    roofline = dict(bound="alu", kernel="sts_fit (sts_prep + sts_stats + sts_pick)",
+                    achieved=achieved, peak=VALU_PEAK_GINSTR, unit="G VALU instr/s",
+                    frac=None if achieved is None else achieved / VALU_PEAK_GINSTR, traffic=None,
+                    evaluations_per_call=evals,
+                    lane_instr_per_evaluation=None if instr is None else instr * 64 / evals,
+                    evaluations_per_s=evals / (ms * 1e-3),
+                    timing="HIP events around each call (three launches)",
+                    instructions=f"SQ_INSTS_VALU of one call, {rec['profile']}")
     res = dict(metric="STS per-position temperature fit: validation pairs per second",
                value=N * G / (ms * 1e-3), unit="pairs/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="f64", data="synthetic",
                config=dict(workload="STS fit", N=N, gamma=G, grid=nT, bins=bins, objective="nll"),
                T=[round(float(v), 4) for v in out["T"].cpu()],
-               ece_before=float(out["ece_before"].mean()), ece_after=float(out["ece_after"].mean()))
+               ece_before=float(out["ece_before"].mean()), ece_after=float(out["ece_after"].mean()),
+               roofline=roofline)
     if args.cpu_seconds > 0:
         import time
         from threadpoolctl import threadpool_limits

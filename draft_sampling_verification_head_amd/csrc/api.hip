@@ -756,8 +756,8 @@ int dspark_markov_draft_schedule(int B, int V, int r, int gamma, const float* U,
 size_t dspark_sts_fit_workspace_bytes(int N, int gamma, int n_grid) {
     if (N < 1 || gamma < 1 || n_grid < 1) return 0;
     const size_t cells = static_cast<size_t>(N) * gamma;
-    return align_up(cells * sizeof(float)) + align_up(cells) +
-           align_up(dspark::sts_stats_bytes(gamma, n_grid));
+    return align_up(cells * sizeof(double)) + align_up(cells) +
+           align_up(dspark::sts_stats_bytes(N, gamma, n_grid));
 }
 
 int dspark_sts_fit(int N, int gamma, const float* conf, const int32_t* n_acc, const int32_t* len,
@@ -780,11 +780,12 @@ int dspark_sts_fit(int N, int gamma, const float* conf, const int32_t* n_acc, co
         return fail(DSPARK_ERR_WORKSPACE, "sts_fit: workspace %zu bytes, need %zu", ws_bytes, need);
     Carver c(ws);
     const size_t cells = static_cast<size_t>(N) * gamma;
-    float* ct = c.take<float>(cells);
+    double* gt = c.take<double>(cells);
     int8_t* ot = c.take<int8_t>(cells);
-    double* stats = c.take<double>(dspark::sts_stats_bytes(gamma, n_grid) / sizeof(double));
+    auto* part = c.take<unsigned long long>(dspark::sts_stats_bytes(N, gamma, n_grid) /
+                                            sizeof(unsigned long long));
     const hipError_t e = dspark::launch_sts_fit(N, gamma, conf, n_acc, len, grid, n_grid, bins,
-                                                objective, ct, ot, stats, T_out, ece_before,
+                                                objective, gt, ot, part, T_out, ece_before,
                                                 ece_after, obj_out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "sts_fit");
     return ok();

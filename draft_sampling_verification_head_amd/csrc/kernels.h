@@ -178,10 +178,10 @@ hipError_t launch_conf_ring_push(long long* ring_n, float* slots, const float* c
 
 // ---------------------------------------------------------------- STS fit
 int sts_max_bins();
-size_t sts_stats_bytes(int gamma, int n_grid);
+size_t sts_stats_bytes(int N, int gamma, int n_grid);
 hipError_t launch_sts_fit(int N, int G, const float* conf, const int32_t* n_acc,
                           const int32_t* len, const float* grid, int nT, int bins, int objective,
-                          float* ct, int8_t* ot, double* stats, float* T_out, float* ece_before,
-                          float* ece_after, float* obj_out, hipStream_t st);
+                          double* gt, int8_t* ot, unsigned long long* part, float* T_out,
+                          float* ece_before, float* ece_after, float* obj_out, hipStream_t st);
 
 }  // namespace dspark

@@ -444,7 +444,8 @@ int dspark_schedule_lagged(int R, int gamma, const void* ring, size_t ring_bytes
  *   obj_out [gamma][n_grid] fp32 the objective at every grid value (nullable)
  * Outcomes: positions k < n_acc were accepted, position n_acc was rejected when
  * n_acc < len, later positions were not observed. Calibrated score:
- * sigmoid(logit(c) / T) in fp64. Caps: 1 <= N, N * gamma < 2^31, 1 <= gamma <= 64,
+ * sigmoid(logit(c) / T) in fp64; the ECE's per-bin sums of (outcome - score) add each term
+ * rounded to 2^-30 as an exact integer, so results are bitwise reproducible. Caps: 1 <= N, N * gamma < 2^31, 1 <= gamma <= 64,
  * 1 <= n_grid <= 4096.
  */
 enum { DSPARK_STS_NLL = 0, DSPARK_STS_ECE = 1 };

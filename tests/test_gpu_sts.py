@@ -9,6 +9,10 @@ import synth
 import draft_sampling_verification_head_amd as dspark
 from parity import dev, host
 
+
+def lib():
+    return dspark.binding.load()
+
 pytestmark = pytest.mark.gpu
 
 
@@ -81,6 +85,46 @@ def test_nothing_observed(gpu):
     n_acc = np.full(10, -1, np.int32)
     g = run(conf, n_acc, None, np.array([0.5, 1.0, 2.0], np.float32), 15, sts.NLL)
     assert np.all(g["T"] == 0.5) and np.all(g["ece_before"] == 0) and np.all(g["ece_after"] == 0)
+
+
+def test_edge_scores_and_temperatures(gpu):
+    """Scores at and past the edges (0, 1, negative, above 1, NaN, the float just below 1) and
+    grid values that count as 1 (0, negative, NaN), an infinite temperature (every interior
+    score 0.5) and a tiny one (hard 0 / 1 scores), against the oracle with both objectives."""
+    g = np.random.default_rng(77)
+    N, G = 3000, 3
+    conf = g.beta(6, 2, size=(N, G)).astype(np.float32)
+    edge = np.array([0.0, 1.0, -0.5, 1.5, np.nan, np.float32(1) - np.float32(2 ** -24), 1e-30, 0.5],
+                    np.float32)
+    conf[: edge.size * 40] = np.repeat(edge, 40)[:, None]
+    n_acc = g.integers(0, G + 1, size=N).astype(np.int32)
+    grid = np.array([0.5, 1.0, 2.0, np.inf, 0.0, -1.0, np.nan, 1e-30, 3.0], np.float32)
+    for objective in (sts.NLL, sts.ECE):
+        check(conf, n_acc, None, grid, 15, objective)
+
+
+def test_bitwise_reruns_and_poisoned_workspace(gpu):
+    """Two calls on workspaces filled with zeros and with random bytes give the same bits
+    (every partial is written before it is read, and every sum has a fixed order or is
+    exact), with both objectives and with more than one slice of samples per position."""
+    g = np.random.default_rng(31)
+    N, G = 40000, 5
+    conf, n_acc, length = validation_set(31, N, G, np.linspace(0.7, 2.0, G), True)
+    grid = np.linspace(0.3, 3.0, 19).astype(np.float32)              # 20 temperatures: groups of 5
+    nbytes = lib().dspark_sts_fit_workspace_bytes(N, G, grid.size)
+    for objective in (sts.NLL, sts.ECE):
+        outs = []
+        for fill in ("zeros", "random"):
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+            if fill == "random":
+                ws.copy_(torch.from_numpy(g.integers(0, 256, nbytes, dtype=np.uint8)))
+            out = dspark.sts_fit(dev(conf), dev(n_acc), dev(grid), length=dev(length),
+                                 objective=objective, want_obj=True, ws=ws)
+            torch.cuda.synchronize()
+            outs.append({k: host(v) for k, v in out.items()})
+        for k in outs[0]:
+            assert outs[0][k].tobytes() == outs[1][k].tobytes(), k
+    check(conf, n_acc, length, grid, 15, sts.ECE)
 
 
 def test_fit_on_verify_results(gpu):
