@@ -37,7 +37,7 @@
  *            B*gamma*V < 2^40;
  *            scheduler R*gamma <= 16384 and R <= Bmax <= 2^20.
  * Results    Deterministic: two calls on the same inputs give bit-identical outputs (no float
- *            atomics; every reduction has a fixed order).
+ *            atomics; every reduction has a fixed order or is an exact integer sum).
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -109,7 +109,8 @@ int dspark_version(void);
  *   DSPARK_PATH_RESIDENT  one launch for all positions, W2 held in registers across the GPU
  *                         (B = 1, bf16, r <= 256 and r % 8 == 0, V % 8 == 0, 16-byte aligned
  *                         factors, ceil(V / 640) <= compute units). Its workgroups must all be
- *                         resident at once and meet at a grid barrier after every position.
+ *                         resident at once: after every position each waits for the token
+ *                         that all of their partial sums decide.
  *                         If other work keeps compute units busy for about a second, a
  *                         barrier gives up, and the positions not yet drawn get token -1,
  *                         q = 0 and lse = -inf. Draft calls on other streams of the same
