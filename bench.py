@@ -76,6 +76,21 @@ MEASURED_TRAFFIC = {
         sources={"verify.hip": "2f3a3106333ccf4251e793eeaeb3a9d810cdaa08b22d88429b09244e9b6f1bc7",
                  "rows.h": "034bd45b0d847736581802a52cbc1a69584399aadbae0696fe836fb20b4fd3e8",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
+    # one RNN-head draft call (bench.py --workload rnn): the one-launch form, and the
+    # per-position form summed over its launches (rnn_state once, then per position
+    # draft_step_mfma<true> and rnn_select_kernel)
+    ("rnn_single", "draft_resident<true>"): dict(
+        bytes=85624927.6,
+        profile="profiles/rnn_draft_B1_B64_V151936.md",
+        sources={"draft_resident.hip": "3b10cd99634f60bcf455ad08b5b56544542e0f32a11f7d72e767f4bb9f507202",
+                 "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
+    ("rnn_batched", "rnn_mfma"): dict(
+        bytes=2559845665.8,
+        profile="profiles/rnn_draft_B1_B64_V151936.md",
+        sources={"draft_mfma.hip": "574c0084782453dbb56f6417a98d3ebace902c5086dd80af19406b4574a5982e",
+                 "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
+                 "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
         bytes=4835578158.7,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
@@ -123,7 +138,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["sts", "pipeline", "mfma"], default="single")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["sts", "pipeline", "mfma", "rnn"],
+                    default="single")
     ap.add_argument("--no-flush", action="store_true", help="keep the Infinity Cache warm")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
@@ -343,6 +359,98 @@ def bench_sts(args, torch, dspark, device):
         res["cpu_baseline"] = dict(value=fits * N * G / el, unit="pairs/s", cores=1, kind="oracle",
                                    sample=f"{fits} fp64 oracle fits of the same {N} x {G} pairs "
                                           f"and {nT} temperatures, one thread, {el:.1f} s")
+    print(json.dumps(res), flush=True)
+
+
+def bench_rnn(args, torch, dspark, device):
+    """The RNN head's draft (h_1 = W1[x_0], h_k = A h_{k-1} + W1[x_{k-1}], B_k = h_k W2) on
+    the single-request shapes (B = 1, V = 151936, r = 256, gamma = 7: one launch with W2 in
+    registers and A in LDS) and the batched shapes (B = 64, gamma = 16: per position an MFMA
+    projection launch, whose extra workgroups form A h_k meanwhile, and a draw launch that
+    adds the drawn token's W1 row to finish h_{k+1}). Factors, base logits, context tokens and
+    uniforms are those of the Markov workloads, A ~ N(0, (0.5 / sqrt(r))^2). Each call is
+    launched directly and timed with HIP events, the Infinity Cache flushed before it.
+    Algorithmic bytes per call: the one-launch form reads W2 and A once, then per position
+    U_k and the W1 rows; the per-position form reads W2 at every position and writes the
+    logits rows the draw reads, plus the state rows (hi and lo bf16) and A."""
+    import synth
+    from oracle import rnn as oracle_rnn
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=device)
+    recs = {}
+    for name, preset in (("single", synth.SINGLE), ("batched", synth.BATCHED)):
+        c = synth.config(preset)
+        B, V, r, G = c.B, c.V, c.r, c.gamma
+        w1, w2 = synth.factors(c)
+        a = synth.rnn_factor(c)
+        U_h = np.stack([synth.base_rows(c, b)[:G] for b in range(B)])
+        x0_h, u_h = synth.x0(c), synth.draft_uniforms(c)
+        W1, W2, A, U, x0, u = (to_dev(x, torch, device) for x in (w1, w2, a, U_h, x0_h, u_h))
+        path = dspark.rnn_draft_path(B, W1, W2, A)
+
+        def call():
+            return dspark.rnn_draft(U, W1, W2, A, x0, u)
+
+        for _ in range(max(1, args.warmup)):
+            out = call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            flush.sum()
+            e0.record()
+            out = call()
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+        x = out["x"].cpu().numpy()
+        assert ((x >= 0) & (x < V)).all()
+        if path == "resident":
+            moved = r * V * 2 + r * r * 2 + G * (B * V * 4 + B * r * 2 + B * 12)
+            limiter = ("latency: W2 and A loaded once, then per position three cross-CU "
+                       "hand-overs (as the Markov head's one-launch draft)")
+        else:
+            moved = G * (draft_bytes_per_position(c, True) + B * r * 2 * 2 + r * r * 2)
+            limiter = "HBM: W2, U_k and the logits rows per position"
+        achieved = moved / (us * 1e-6) / 1e9
+        key = ("rnn_single", "draft_resident<true>") if path == "resident" else ("rnn_batched", "rnn_mfma")
+        traffic = measured_traffic(*key)
+        recs[name] = dict(B=B, V=V, r=r, gamma=G, path=path, draft_us=us,
+                          draft_tok_s=B * G / (us * 1e-6),
+                          roofline=dict(bound="hbm", kernel=("draft_resident<true>" if path == "resident" else
+                                                              "draft_step_mfma<true> + rnn_select per position"),
+                                        achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                                        frac=achieved / HBM_PEAK_GBS, traffic=traffic,
+                                        physical_gbs=None if traffic is None else traffic / (us * 1e-6) / 1e9,
+                                        bytes_per_call=moved, limiter=limiter,
+                                        timing="HIP events around each call, median"))
+        if name == "single" and args.cpu_seconds > 0:
+            import time
+            from threadpoolctl import threadpool_limits
+            n, t0 = 0, time.perf_counter()
+            with threadpool_limits(limits=1):
+                while True:
+                    oracle_rnn.rnn_draft(U_h, w1, w2, a, x0_h, u_h, w_dtype="bf16")
+                    n += 1
+                    el = time.perf_counter() - t0
+                    if el >= args.cpu_seconds:
+                        break
+            recs[name]["cpu_baseline"] = dict(
+                value=n * B * G / el, unit="draft tokens/s", cores=1, kind="oracle",
+                sample=f"{n} fp64 oracle drafts of the single-request workload "
+                       f"({B} x {G} tokens at V = {V}), one thread, {el:.1f} s")
+        del U, W1, W2, A, x0, u, out
+        torch.cuda.empty_cache()
+    one = recs["single"]
+    res = dict(metric="RNN-head draft tokens/s at V=151936", value=one["draft_tok_s"],
+               unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=one["draft_us"] / 1e3, higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16", data="synthetic",
+               config=dict(workload="RNN-head draft, single request", B=1, V=one["V"], r=one["r"],
+                           gamma=one["gamma"], factors="bf16", mall_flush=True, launch="direct"),
+               roofline=one["roofline"], path=one["path"],
+               sub_workloads=dict(batched=recs["batched"]))
+    if "cpu_baseline" in one:
+        res["cpu_baseline"] = one["cpu_baseline"]
     print(json.dumps(res), flush=True)
 
 
@@ -620,6 +728,8 @@ def main():
         return bench_pipeline(args, torch, dspark, device)
     if args.workload == "mfma":
         return bench_mfma(args, torch, dspark, device)
+    if args.workload == "rnn":
+        return bench_rnn(args, torch, dspark, device)
     mp = measured_peaks(torch, device)
     res = run_workload(args, args.workload, torch, dspark, device, args.steps, args.cpu_seconds, mp)
     if args.workload == "single" and args.sub_steps > 0 and not args.per_position:

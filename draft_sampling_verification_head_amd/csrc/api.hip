@@ -323,13 +323,13 @@ int dspark_markov_draft(int B, int V, int r, int gamma, const float* U, const vo
 namespace {
 
 // header, slots (single-request one-launch form), tile partials, logits rows (when the caller
-// does not take them), fp32 state ping-pong, bf16 hi / lo state rows (batched form)
+// does not take them), fp32 state ping-pong and A h_k, bf16 hi / lo state rows (batched form)
 size_t rnn_ws_bytes(int B, int V, int r, int gamma) {
     const int rp = dspark::rnn_rank_pad(r);
     return kDraftHeader + align_up(draft_slot_bytes(V, gamma)) +
            2 * align_up(draft_part_count(B, V) * sizeof(float2)) +
            2 * align_up(static_cast<size_t>(B) * V * sizeof(float)) +
-           2 * align_up(static_cast<size_t>(B) * r * sizeof(float)) +
+           3 * align_up(static_cast<size_t>(B) * r * sizeof(float)) +
            align_up(static_cast<size_t>(B) * 2 * rp * sizeof(uint16_t));
 }
 
@@ -381,6 +381,7 @@ int dspark_rnn_draft(int B, int V, int r, int gamma, const float* U, const void*
     rc.hstate[0] = c.take<float>(static_cast<size_t>(B) * r);
     rc.hstate[1] = c.take<float>(static_cast<size_t>(B) * r);
     rc.hrows = c.take<uint16_t>(static_cast<size_t>(B) * 2 * dspark::rnn_rank_pad(r));
+    rc.ah = c.take<float>(static_cast<size_t>(B) * r);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = dspark::rnn_resident_ok(B, V, r, W1, W2, A) ? dspark::launch_rnn_resident(rc, st)
                                                                      : dspark::launch_rnn_mfma(rc, st);

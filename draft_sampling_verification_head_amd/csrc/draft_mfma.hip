@@ -60,6 +60,11 @@ struct MfmaArgs {
     float* L;                 // logits rows L + b * L_bstride
     long long L_bstride;
     float2* part;             // [B][ntiles] (max, sum exp) per request and tile
+    // RNN head: workgroups from mv0 on (one per request) form A h_k while the tiles run
+    const uint16_t* A;        // [r][r] bf16
+    const float* hcur;        // [B][r] fp32 state h_k
+    float* Ah;                // [B][r] fp32 A h_k, for the draw launch to finish h_{k+1}
+    unsigned mv0;             // first matvec workgroup (the grid's end when there is none)
 };
 
 // Row of accumulator element v of half-tile h, for the lane half hf = lane / 32.
@@ -99,10 +104,37 @@ __device__ __forceinline__ float reduce_scatter32(const float (&x)[32], Op op) {
 // RNN = false: the Markov head (A operand = the gathered W1 rows of the previous tokens).
 // RNN = true: the RNN head's state rows, split into bf16 hi + lo parts (h = hi + lo to about
 // 2^-17 relative), each multiplied with the same W2 fragment into the same accumulators.
+// A h_k of request b in fp32, row i summed over j in ascending order from 0 (the sum
+// rnn_state_kernel forms before adding the W1 row). hp: r floats of LDS.
+__device__ void rnn_matvec(const MfmaArgs& a, int b, float* hp) {
+    const int i = threadIdx.x, r = a.r;
+    if (i < r) hp[i] = a.hcur[static_cast<long long>(b) * r + i];
+    __syncthreads();
+    if (i >= r) return;
+    const uint16_t* Ar = a.A + static_cast<long long>(i) * r;
+    float h = 0.0f;
+    for (int j = 0; j < r; j += 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(Ar + j);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h = fmaf(__uint_as_float(ww[e] << 16), hp[j + 2 * e], h);
+            h = fmaf(__uint_as_float(ww[e] & 0xffff0000u), hp[j + 2 * e + 1], h);
+        }
+    }
+    a.Ah[static_cast<long long>(b) * r + i] = h;
+}
+
 template <bool RNN>
 __global__ __launch_bounds__(kThreads, 4)      // 4 waves per SIMD: two workgroups per CU
 void draft_step_mfma(MfmaArgs a) {
     extern __shared__ uint16_t sm16[];
+    if constexpr (RNN) {
+        if (blockIdx.x >= a.mv0) {
+            rnn_matvec(a, static_cast<int>(blockIdx.x - a.mv0), reinterpret_cast<float*>(sm16));
+            return;
+        }
+    }
     const int HS = a.rp + kHPad;
     uint16_t* Hs = sm16;                              // [kMT][HS] gathered W1 rows (RNN: hi)
     uint16_t* Hl = sm16 + kMT * HS;                   // RNN: [kMT][HS] lo parts
@@ -314,6 +346,10 @@ hipError_t launch_draft_mfma(const DraftCall& c, hipStream_t st) {
         a.L = c.L[k];
         a.part = c.part[k & 1];
         a.Hrows = nullptr;
+        a.A = nullptr;
+        a.hcur = nullptr;
+        a.Ah = nullptr;
+        a.mv0 = grid.x;
         hipLaunchKernelGGL(draft_step_mfma<false>, grid, dim3(kThreads), smem, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -377,6 +413,48 @@ void rnn_state_kernel(int B, int r, int rp, int k, int gamma, const uint16_t* __
     }
 }
 
+// Draw of position k for every request (one wave per request, as draft_select), then, when
+// a later position follows, the request's next state h_{k+1} = A h_k + W1[x_k]: A h_k comes
+// from the matvec workgroups of position k's projection launch, and the W1 row of the token
+// just drawn is added to it, so the state equals rnn_state_kernel's bit for bit. It is
+// written as rnn_state_kernel writes it (fp32, h_out, bf16 hi / lo rows); a dead request's
+// state is 0.
+__global__ __launch_bounds__(kSelThreads)
+void rnn_select_kernel(int B, int V, int r, int rp, int gamma, int k,
+                       const float2* __restrict__ part, int nblk, const float* __restrict__ L,
+                       long long L_bstride, const float* __restrict__ u, int32_t* __restrict__ x_out,
+                       float* __restrict__ q_out, float* __restrict__ lse_out,
+                       const float* __restrict__ Ah, const uint16_t* __restrict__ W1,
+                       float* __restrict__ h_next, uint16_t* __restrict__ hrows,
+                       float* __restrict__ h_out) {
+    const int b = blockIdx.x * (kSelThreads / kWave) + threadIdx.x / kWave;
+    if (b >= B) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long o = static_cast<long long>(b) * gamma + k;
+    const DrawOut out{x_out + o, q_out ? q_out + o : nullptr, lse_out ? lse_out + o : nullptr,
+                      true};
+    int t = draw_wave<kNT>(V, part + static_cast<long long>(b) * nblk, nblk, L + b * L_bstride,
+                           u[o], out);
+    if (k + 1 >= gamma) return;
+    if (t < 0 || t >= V) t = -1;
+    uint16_t* row = hrows + static_cast<long long>(b) * 2 * rp;
+    for (int i = lane; i < rp; i += kWave) {
+        float h = 0.0f;
+        if (i < r && t >= 0) {
+            h = Ah[static_cast<long long>(b) * r + i];
+            h += to_f32(W1[static_cast<long long>(t) * r + i]);
+        }
+        if (i < r) {
+            h_next[static_cast<long long>(b) * r + i] = h;
+            if (h_out) h_out[(static_cast<long long>(b) * gamma + k + 1) * r + i] = h;
+        }
+        const __bf16 hi = static_cast<__bf16>(h);
+        const __bf16 lo = static_cast<__bf16>(h - static_cast<float>(hi));
+        row[i] = __builtin_bit_cast(uint16_t, hi);
+        row[rp + i] = __builtin_bit_cast(uint16_t, lo);
+    }
+}
+
 }  // namespace
 
 int rnn_rank_pad(int r) {
@@ -414,35 +492,35 @@ hipError_t launch_rnn_mfma(const RnnCall& rc, hipStream_t st) {
                                                  static_cast<int>(smem));
         if (e != hipSuccess) return e;
     }
+    a.A = static_cast<const uint16_t*>(rc.A);
+    a.Ah = rc.ah;
+    // h_1 = W1[x_0]; afterwards each draw launch finishes the next state (rnn_select_kernel)
+    hipLaunchKernelGGL(rnn_state_kernel, dim3(c.B), dim3(kStateThreads), 0, st, c.B, c.r, a.rp, 0,
+                       c.gamma, static_cast<const uint16_t*>(rc.A), a.W1, c.V, c.x0, 1,
+                       rc.hstate[1], rc.hstate[0], rc.hrows, rc.h_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int waves = kSelThreads / kWave;
     for (int k = 0; k < c.gamma; ++k) {
-        if (k > 0) {
-            hipLaunchKernelGGL(draft_select<kNT>, dim3((c.B + waves - 1) / waves), dim3(kSelThreads),
-                               0, st, c.B, c.V, c.gamma, k - 1,
-                               static_cast<const float2*>(c.part[(k - 1) & 1]), a.ntiles, c.L[k - 1],
-                               c.L_bstride, c.u, c.x_out, c.q_out, c.lse_out);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
         a.k = k;
         a.tok = k ? c.x_out + (k - 1) : c.x0;
         a.tok_stride = k ? c.gamma : 1;
-        hipLaunchKernelGGL(rnn_state_kernel, dim3(c.B), dim3(kStateThreads), 0, st, c.B, c.r, a.rp, k,
-                           c.gamma, static_cast<const uint16_t*>(rc.A), a.W1, c.V, a.tok, a.tok_stride,
-                           rc.hstate[(k + 1) & 1], rc.hstate[k & 1], rc.hrows, rc.h_out);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         a.L = c.L[k];
         a.part = c.part[k & 1];
-        hipLaunchKernelGGL(draft_step_mfma<true>, grid, dim3(kThreads), smem, st, a);
+        a.hcur = rc.hstate[k & 1];
+        a.mv0 = grid.x;
+        const dim3 g(grid.x + (k + 1 < c.gamma ? static_cast<unsigned>(c.B) : 0u));
+        hipLaunchKernelGGL(draft_step_mfma<true>, g, dim3(kThreads), smem, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(rnn_select_kernel, dim3((c.B + waves - 1) / waves), dim3(kSelThreads), 0, st,
+                           c.B, c.V, c.r, a.rp, c.gamma, k, static_cast<const float2*>(c.part[k & 1]),
+                           a.ntiles, c.L[k], c.L_bstride, c.u, c.x_out, c.q_out, c.lse_out, rc.ah,
+                           a.W1, rc.hstate[(k + 1) & 1], rc.hrows, rc.h_out);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int k = c.gamma - 1;
-    hipLaunchKernelGGL(draft_select<kNT>, dim3((c.B + waves - 1) / waves), dim3(kSelThreads), 0, st,
-                       c.B, c.V, c.gamma, k, static_cast<const float2*>(c.part[k & 1]), a.ntiles,
-                       c.L[k], c.L_bstride, c.u, c.x_out, c.q_out, c.lse_out);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace dspark

@@ -72,6 +72,7 @@ struct RnnCall {
     float* h_out;             // [B][gamma][r] fp32 states (nullable)
     float* hstate[2];         // [B][r] fp32, ping-pong (batched form)
     uint16_t* hrows;          // [B][2][rnn_rank_pad(r)] bf16 hi / lo rows (batched form)
+    float* ah;                // [B][r] fp32 A h_k (batched form)
 };
 int rnn_rank_pad(int r);
 bool rnn_mfma_ok(int V, int r, const void* W1, const void* W2, const void* A);
