@@ -50,20 +50,20 @@ CSRC = os.path.join(ROOT, "draft_sampling_verification_head_amd", "csrc")
 # A figure holds only for the kernel sources it was measured with.
 MEASURED_TRAFFIC = {
     ("single", "draft_resident"): dict(
-        bytes=86697211.5,
+        bytes=86696716.7,
         profile="profiles/draft_resident_single_request_B1_V151936.md",
         sources={"draft_resident.hip": "3b10cd99634f60bcf455ad08b5b56544542e0f32a11f7d72e767f4bb9f507202",
                  "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the per-position sweep of one request (bench.py --per-position)
     ("single", "draft_step_gemv"): dict(
-        bytes=79190294.5,
+        bytes=79190153.7,
         profile="profiles/draft_step_gemv_single_request_B1_V151936.md",
         sources={"draft.hip": "48a48f93317cfc1a63460cbe3d00ebf91bb049d6b29ba4e96aeab52653667d8d",
                  "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("batched", "draft_slab_resident"): dict(
-        bytes=1446169785.6,
+        bytes=1446072095.4,
         profile="profiles/draft_slab_resident_batched_B64_V151936.md",
         sources={"draft_slab.hip": "21b13026391fbfdf5bd1eb540df939c58901b0a9cb5ba32671181343b05300f5",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",
@@ -71,9 +71,9 @@ MEASURED_TRAFFIC = {
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # the two kernels of one dspark_verify_tv call on the sweep path (vt_sweep, vt_select)
     ("verify", "dspark_verify_tv"): dict(
-        bytes=5262739029.8,
+        bytes=5221276587.5,
         profile="profiles/verify_tv_verify_B256_V151936.md",
-        sources={"verify.hip": "2f3a3106333ccf4251e793eeaeb3a9d810cdaa08b22d88429b09244e9b6f1bc7",
+        sources={"verify.hip": "efe611bd18c839ca90d544abe373e633178acc100ea6dd2072766ba3e22300bd",
                  "rows.h": "034bd45b0d847736581802a52cbc1a69584399aadbae0696fe836fb20b4fd3e8",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     # one RNN-head draft call (bench.py --workload rnn): the one-launch form, and the
@@ -92,7 +92,7 @@ MEASURED_TRAFFIC = {
                  "draw.h": "f0ce56704c0ecddfcb12c94b365cb76428c1d65276c0e1114289aa0f5b04a122",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
     ("round", "draft_slab_resident"): dict(
-        bytes=4835578158.7,
+        bytes=4835505781.0,
         profile="profiles/draft_slab_resident_round_B512_V129280.md",
         sources={"draft_slab.hip": "21b13026391fbfdf5bd1eb540df939c58901b0a9cb5ba32671181343b05300f5",
                  "slab.h": "30a5c0d57967acb7597dbfd00d25a931686c28c32d439bbb8511f3ca1f0fa765",

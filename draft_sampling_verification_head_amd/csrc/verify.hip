@@ -722,8 +722,9 @@ void verify_tv_select_kernel(RowSet rs, int nch, const int32_t* __restrict__ x,
 // results (reading only the drafted tokens' logits and the one chunk it rescans) and merges c*.
 //
 // The grid is persistent: every workgroup is resident at once (checked by the host). It is
-// split into groups of N >= nch workgroups, each group sweeping a contiguous range of units,
-// and workgroup w of a group takes the group's tasks w, w + N, w + 2N, ... A unit's nch chunks
+// split into groups of N >= nch workgroups, each group sweeping a contiguous range of units
+// (the verified rows only, when the lengths are given and B <= kLiveMax), and workgroup w of
+// a group takes the group's tasks w, w + N, w + 2N, ... A unit's nch chunks
 // are consecutive tasks, so they belong to nch different workgroups, each of which reaches them
 // after finishing tasks of earlier units only; by induction over units every wait ends. Polling is bounded all the
 // same: a workgroup that gives up writes the call's key into the give-up word, and vt_select
@@ -782,7 +783,13 @@ struct SweepArgs {
     unsigned spin;
     long long units;                  // B (gamma + 1)
     int groups;                       // workgroup groups, each sweeping its own range of units
+    int compact;                      // 1: the tasks cover the verified rows only (B <= kLiveMax)
 };
+
+// Requests whose verified rows the sweep can index through LDS: with per-request lengths, the
+// tasks then cover only the rows that exist (len + 1 target and len draft rows per valid
+// request), so a workgroup never meets runs of absent rows that others do not.
+constexpr int kLiveMax = 4096;
 
 // lse of a unit's row from the lanes' chunk partials (lane i holds chunk i < nch <= 64; the
 // other lanes hold (-inf, 0)): merge_lse_wave's arithmetic on the same values.
@@ -803,6 +810,8 @@ void vt_sweep_kernel(SweepArgs a) {
     __shared__ int s_gave;
     __shared__ unsigned long long s_key;
     __shared__ unsigned s_tag;
+    __shared__ int s_cum[kLiveMax];                  // compact: verified rows of requests <= b
+    __shared__ int s_wsum[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const RowSet& rs = a.rs;
     const int G = rs.gamma, V = rs.V, nch = a.nch, G1 = G + 1;
@@ -813,6 +822,32 @@ void vt_sweep_kernel(SweepArgs a) {
         s_gave = 0;
         if (blockIdx.x == 0) st_agent(a.hdr + 2, s_key);
     }
+    // compact: inclusive scan over the requests of their verified rows (0 for a faulty one)
+    long long units = a.units;
+    if (a.compact) {
+        int carry = 0;
+        for (int b0 = 0; b0 < rs.B; b0 += kThreads) {
+            const int b = b0 + tid;
+            int v = 0;
+            if (b < rs.B) {
+                const ReqRows q = request_rows(rs, b);
+                v = q.ok ? q.ell + 1 : 0;
+            }
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int w = __shfl_up(v, o, kWave);
+                if (lane >= o) v += w;
+            }
+            if (lane == kWave - 1) s_wsum[wave] = v;
+            __syncthreads();
+            int before = carry;
+            for (int w = 0; w < wave; ++w) before += s_wsum[w];
+            if (b < rs.B) s_cum[b] = before + v;
+            for (int w = 0; w < kWaves; ++w) carry += s_wsum[w];
+            __syncthreads();
+        }
+        units = carry;
+    }
     __syncthreads();
     const unsigned long long key = s_key;
     const unsigned tag = s_tag;
@@ -820,12 +855,23 @@ void vt_sweep_kernel(SweepArgs a) {
     // round-robin; a unit's waits then involve the workgroups of one group only
     const unsigned per = gridDim.x / static_cast<unsigned>(a.groups);
     const unsigned grp = blockIdx.x / per;
-    const long long u0 = a.units * grp / a.groups, u1 = a.units * (grp + 1) / a.groups;
+    const long long u0 = units * grp / a.groups, u1 = units * (grp + 1) / a.groups;
+    int bcur = 0;                                    // compact: request of the current task
     for (long long lt = blockIdx.x - grp * per; lt < (u1 - u0) * nch; lt += per) {
         const long long task = u0 * nch + lt;
-        const long long unit = task / nch;
-        const int c = static_cast<int>(task - unit * nch);
-        const int b = static_cast<int>(unit / G1), s = static_cast<int>(unit - static_cast<long long>(b) * G1);
+        const long long lu = task / nch;
+        const int c = static_cast<int>(task - lu * nch);
+        int b, s;
+        if (a.compact) {
+            // tasks of a workgroup come in increasing order, so the request only moves forward
+            while (s_cum[bcur] <= lu) ++bcur;
+            b = bcur;
+            s = static_cast<int>(lu - (b ? s_cum[b - 1] : 0));
+        } else {
+            b = static_cast<int>(lu / G1);
+            s = static_cast<int>(lu - static_cast<long long>(b) * G1);
+        }
+        const long long unit = static_cast<long long>(b) * G1 + s;
         const ReqRows q = request_rows(rs, b);
         if (!q.ok || s > q.ell) continue;               // no such row: nobody waits for it
         const bool pair = s < q.ell;
@@ -1611,6 +1657,7 @@ hipError_t launch_verify_sweep(const RowSet& rs, const int32_t* x, const float* 
     // two groups when each still has a workgroup per chunk of a row and the sweep takes
     // several rounds of tasks
     a.groups = (cap / 2 >= a.nch && a.ntasks >= 2 * cap) ? 2 : 1;
+    a.compact = (rs.len != nullptr && rs.B <= kLiveMax) ? 1 : 0;
     unsigned grid = static_cast<unsigned>(a.ntasks < cap ? a.ntasks : cap);
     grid = grid / a.groups * a.groups;
     if (v4)

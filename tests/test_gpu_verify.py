@@ -170,6 +170,36 @@ def test_verify_tv_at_the_sweep_cap(gpu, B, V, G, flat, given):
     test_verify_tv_matches_separate_calls(gpu, B, V, G, flat, given)
 
 
+def test_verify_tv_sweep_over_verified_rows_only(gpu):
+    """With lengths given, the persistent sweep's tasks run over the verified rows only: empty
+    requests (length 0: one target row), full ones, ragged ones and requests with an invalid
+    length (no rows at all) in the padded layout. The results equal the separate calls bit for
+    bit, the invalid requests come back as faults, and the others match the oracle."""
+    B, V, G = 40, 40000, 5
+    c = synth.custom(977, B=B, V=V, r=1, gamma=G, w_dtype="f32", tnoise=0.8)
+    g = np.random.default_rng(977)
+    lengths = g.integers(0, G + 1, size=B)
+    lengths[:4] = [0, G, 0, G]
+    bad = [7, 21]
+    inp = verify_inputs(c, lengths, flat=False)
+    inp["length"][bad[0]] = G + 3
+    inp["length"][bad[1]] = -2
+    a = run_verify(inp, want_lse=True)
+    tv = run_tv(inp, lse_d=dev(a["lse_d"]), lse_t=dev(a["lse_t"]))
+    f = run_verify_tv(inp)
+    for k in ("n", "y", "lse_d", "lse_t"):
+        assert np.array_equal(a[k].view(np.uint8), f[k].view(np.uint8)), k
+    assert np.array_equal(np.isnan(tv), np.isnan(f["cstar"]))
+    fin = ~np.isnan(tv)
+    assert np.array_equal(tv[fin], f["cstar"][fin])
+    assert all(f["n"][b] == -1 and np.all(f["y"][b] == -1) for b in bad)
+    good = [b for b in range(B) if b not in bad]
+    rep = check_verify(inp["Ld"], inp["Lt"], inp["x"], inp["u_acc"], inp["u_fin"], inp["t_off"],
+                       inp["length"], f["n"], f["y"], good)
+    assert rep.ties <= tie_bound(rep)
+    check_tv(inp, f["cstar"], good)
+
+
 @pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
 def test_verify_tv_sweep_workspace_and_graph_replays(gpu, fill):
     """The one-sweep form tags its chunk slots with a key derived from a call counter in the
