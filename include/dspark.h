@@ -193,8 +193,9 @@ int dspark_markov_draft_ex(int B, int V, int r, int gamma,
  * multiplies its bf16 hi and lo parts (h = hi + lo to about 2^-17 relative) with W2 and
  * accumulates in fp32. Paths (dspark_rnn_draft_path): B = 1 where every workgroup fits runs
  * as DSPARK_PATH_RESIDENT (one launch, W2 in registers, A in LDS; the same give-up behaviour,
- * give-up word and restriction on overlapping draft calls); otherwise DSPARK_PATH_MFMA, three
- * launches per position (state update, bf16 MFMA projection, draw). Sentinels as in
+ * give-up word and restriction on overlapping draft calls); otherwise DSPARK_PATH_MFMA: one
+ * launch for h_1, then two per position (the bf16 MFMA projection, whose extra workgroups
+ * form A h_k meanwhile, and the draw, which adds the drawn token's W1 row). Sentinels as in
  * dspark_markov_draft; a dead request's state is 0.
  */
 size_t dspark_rnn_draft_workspace_bytes(int B, int V, int r, int gamma);
