@@ -105,9 +105,9 @@ MEASURED_TRAFFIC = {
 # the dispatches of one call on the STS workload), kept while the sources are unchanged.
 MEASURED_VALU = {
     ("sts", "sts_fit"): dict(
-        instructions=48075857,
+        instructions=47677714,
         profile="profiles/sts_fit_N65536_G16.md",
-        sources={"sts.hip": "8cdd95471ed406ac1976ff6097aee3b0dd081e8f0996f73329b1b2e5a2080cc7",
+        sources={"sts.hip": "071d3440ddd427b45792a33fe2c331c76fdf1be42a193ee2da7f1df25c289e5d",
                  "common.h": "97b949bdb612b911538ef35847a6ba82a3dffe9004498e237d6935e1c1330f84"}),
 }
 # VALU issue peak of the chip: 256 CUs x 4 SIMDs, one wave64 instruction per SIMD every 4

@@ -12,9 +12,9 @@
 // accepted, position n_i was rejected when n_i < len_i, later positions were not observed.
 // The calibrated score is sigmoid(logit(c) / T) = 1 / (1 + exp(g / T)) with the log-odds
 // complement g = log((1 - c) / c), in fp64. Three launches:
-//   sts_prep   - g (+inf for c <= 0 or NaN, -inf for c >= 1, so that the same expression
-//                gives the scores 0 and 1 there) and the outcome of every pair, one
-//                contiguous column per position;
+//   sts_prep   - the outcome of every pair and, for the observed ones, g (+inf for c <= 0
+//                or NaN, -inf for c >= 1, so that the same expression gives the scores 0
+//                and 1 there), one contiguous column per position;
 //   sts_stats  - one workgroup per (position, five or four grid temperatures, slice of
 //                the samples). Each wave packs the observed samples of its 64-sample chunks
 //                into an LDS queue, in sample order, and evaluates full waves of them at the
@@ -66,12 +66,13 @@ StsShape sts_shape(int N, int G, int nT) {
 }
 
 // One workgroup per tile of T = 256 / gamma samples (one score per thread): the tile's
-// scores are read in their [N][gamma] order, turned into (g, outcome) and transposed through
-// LDS, so both the reads and the column writes are contiguous.
+// scores and outcomes are read in their [N][gamma] order and transposed through LDS, then
+// written as contiguous columns; g is formed in the second pass and only for observed pairs
+// (the sweep reads no other), so the late positions, mostly unobserved, skip the logarithm.
 __global__ __launch_bounds__(kStsThreads)
 void sts_prep(int N, int G, const float* __restrict__ conf, const int32_t* __restrict__ n_acc,
               const int32_t* __restrict__ len, double* __restrict__ gt, int8_t* __restrict__ ot) {
-    __shared__ double lg[kStsThreads + 64];               // [position][T + 1], padded rows
+    __shared__ float lc[kStsThreads + 64];                // [position][T + 1], padded rows
     __shared__ int8_t lo[kStsThreads + 64];
     const int T = kStsThreads / G;                         // G <= 64, so T >= 4
     const long long s0 = static_cast<long long>(blockIdx.x) * T;
@@ -87,12 +88,7 @@ void sts_prep(int N, int G, const float* __restrict__ conf, const int32_t* __res
                 if (k < n) o = 1;
                 else if (k == n && n < ell) o = 0;
             }
-            const double c = static_cast<double>(conf[s * G + k]);
-            double g;
-            if (!(c > 0.0)) g = INFINITY;                 // also NaN: score 0 at every T
-            else if (c >= 1.0) g = -INFINITY;             // score 1 at every T
-            else g = log((1.0 - c) / c);
-            lg[k * (T + 1) + j] = g;
+            lc[k * (T + 1) + j] = conf[s * G + k];
             lo[k * (T + 1) + j] = o;
         }
     }
@@ -101,8 +97,16 @@ void sts_prep(int N, int G, const float* __restrict__ conf, const int32_t* __res
         const int k = tid / T, j = tid - k * T;
         const long long s = s0 + j;
         if (s < N) {
-            gt[static_cast<long long>(k) * N + s] = lg[k * (T + 1) + j];
-            ot[static_cast<long long>(k) * N + s] = lo[k * (T + 1) + j];
+            const int8_t o = lo[k * (T + 1) + j];
+            double g = 0.0;                                // unobserved: never read
+            if (o >= 0) {
+                const double c = static_cast<double>(lc[k * (T + 1) + j]);
+                if (!(c > 0.0)) g = INFINITY;             // also NaN: score 0 at every T
+                else if (c >= 1.0) g = -INFINITY;         // score 1 at every T
+                else g = log((1.0 - c) / c);
+            }
+            gt[static_cast<long long>(k) * N + s] = g;
+            ot[static_cast<long long>(k) * N + s] = o;
         }
     }
 }
